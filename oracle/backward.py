@@ -1,0 +1,94 @@
+"""Backward of the block (LayerNorm backward, e5m2 dZ, dgrad, wgrad), fp64.
+
+Test infrastructure only (see the package docstring).
+
+Sources:
+  * [LoKA] section III-C (Trainer Integration): the low-precision linear is a
+    drop-in for a standard Linear with its own autograd function routing the
+    forward and the backward separately, so the backward is the exact
+    gradient of the forward's definition;
+  * [LoKA] section III-C and Table VI: rowwise recipes for the backward GEMMs
+    (the "RW" recipe, with "RW GW HP" keeping wgrad in high precision as the
+    alternative);
+  * [GEM] "Mixed Ultra-Low-Precision Training": e5m2-range gradients,
+    scale factors along each GEMM's own contraction (K) dimension.
+
+Reading R8 (the training-step configuration names dY, dX = dY.W^T and
+dW = X^T.dY "plus LayerNorm backward" without saying where the LayerNorm
+sits): dY is the gradient at the LayerNorm output Y; the LayerNorm backward
+turns it into dZ, the gradient at the GEMM output; dZ is what both GEMMs
+consume.  Per row m, with yhat = (z - mu) * rstd and g = dY * gamma:
+    dZ     = rstd * (g - mean_n g - yhat * mean_n (g * yhat))
+    dgamma = sum_m dY * yhat,   dbeta = sum_m dY,   dbias = sum_m dZ
+dZ is rounded to fp32 (the precision the quantizer is defined on) and:
+  * dgrad: dX = dequant( q_row(dZ, e5m2) . q_row(W, e4m3)^T ), where the
+    rows of W[K,N] are its k index, so W's scale is per k, amax over n;
+  * wgrad: dW = dequant( q_col(X, e4m3)^T . q_col(dZ, e5m2) ), scales per
+    column of X (per k) and of dZ (per n), amax over the M rows -- both
+    operands scaled along the contraction;
+  * dW stays fp32-or-wider (returned in fp64 here), dX is rounded to bf16.
+The literal reading (dY already is dZ, no LayerNorm) is `no_ln=True`.
+"""
+
+import numpy as np
+
+from .codec import E4M3, E5M2, bf16_to_f64, decode_fp8, f32, f64_to_bf16
+from .forward import gemm_ln_forward, _vec
+from .quant import quantize, ROW, COL
+
+
+def layernorm_backward(dy, z, mu, rstd, gamma):
+    """Exact fp64 LayerNorm backward for y = gamma*(z-mu)*rstd + beta with
+    rstd = 1/sqrt(var + eps): returns (dz, dgamma, dbeta)."""
+    yhat = (z - mu[:, None]) * rstd[:, None]
+    g = dy * gamma[None, :]
+    mg = g.mean(axis=1)
+    mgy = (g * yhat).mean(axis=1)
+    dz = rstd[:, None] * (g - mg[:, None] - yhat * mgy[:, None])
+    return dz, (dy * yhat).sum(axis=0), dy.sum(axis=0)
+
+
+def dgrad(dz32, w):
+    """dX = dequant(q_row(dZ) . q_row(W)^T): dz32 [M,N] fp32-exact, w [K,N]."""
+    q_dz, s_dz = quantize(dz32, ROW, E5M2)
+    q_w, s_w = quantize(w, ROW, E4M3)
+    acc = decode_fp8(q_dz, E5M2) @ decode_fp8(q_w, E4M3).T
+    dx = acc * np.asarray(s_dz, np.float64)[:, None] * np.asarray(s_w, np.float64)[None, :]
+    return dx, q_dz, s_dz, q_w, s_w
+
+
+def wgrad(x, dz32):
+    """dW = dequant(q_col(X)^T . q_col(dZ)): x [M,K], dz32 [M,N]."""
+    q_x, s_x = quantize(x, COL, E4M3)
+    q_dz, s_dz = quantize(dz32, COL, E5M2)
+    acc = decode_fp8(q_x, E4M3).T @ decode_fp8(q_dz, E5M2)
+    dw = acc * np.asarray(s_x, np.float64)[:, None] * np.asarray(s_dz, np.float64)[None, :]
+    return dw, q_x, s_x, q_dz, s_dz
+
+
+def gemm_ln_backward(x_bits, w_bits, dy_bits, bias_bits=None, gamma_bits=None, beta_bits=None,
+                     eps=1e-5, no_ln=False):
+    """Backward of the rowwise-recipe forward for bf16 inputs.
+
+    Returns a dict with dz (fp64), dz32 (its fp32 rounding), the e5m2 row
+    codes/scales of dz32, dx (fp64) and dx_bits (bf16), dw (fp64), dgamma,
+    dbeta, dbias (fp64; dgamma/dbeta are None when no_ln)."""
+    x = bf16_to_f64(x_bits)
+    w = bf16_to_f64(w_bits)
+    dy = bf16_to_f64(dy_bits)
+    N = w.shape[1]
+    if no_ln:
+        dz, dgamma, dbeta = dy, None, None
+    else:
+        fwd = gemm_ln_forward(x_bits, w_bits, bias_bits, gamma_bits, beta_bits, eps, recipe="row")
+        dz, dgamma, dbeta = layernorm_backward(dy, fwd["z"], fwd["mean"], fwd["rstd"],
+                                               _vec(gamma_bits, N, 1.0))
+    dz32 = f32(dz).astype(np.float64)
+    dx, q_dz, s_dz, q_wr, s_wr = dgrad(dz32, w)
+    dw, q_xc, s_xc, q_dzc, s_dzc = wgrad(x, dz32)
+    return {
+        "dz": dz, "dz32": dz32, "q_dz": q_dz, "s_dz": s_dz, "q_wr": q_wr, "s_wr": s_wr,
+        "dx": dx, "dx_bits": f64_to_bf16(dx), "dw": dw,
+        "q_xc": q_xc, "s_xc": s_xc, "q_dzc": q_dzc, "s_dzc": s_dzc,
+        "dgamma": dgamma, "dbeta": dbeta, "dbias": dz.sum(axis=0),
+    }
