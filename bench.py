@@ -1,0 +1,257 @@
+"""Benchmark of the FP8 GEMM + LayerNorm block on one MI355X.
+
+One step = one loka_gemm_fp8_ln call on the rowwise workload (X[16384,512]
+bf16 Student-t(3) with outlier columns, W[512,512] pre-quantized per column,
+bias, LayerNorm over 512): the X amax and e4m3 cast, the FP8 MFMA GEMM and
+the dequant + bias + LayerNorm epilogue, all in one kernel.  The weight is
+quantized once per step of training, outside the activation path (reported
+separately as `weight_quant_us`).  Inputs are resident in HBM; 16 rotating
+input/output sets (537 MB) keep the 256 MB Infinity Cache from serving them.
+Launches are replayed from a HIP graph so host launch cost does not enter.
+
+Prints one JSON line.  `roofline` is for the fused forward kernel (HBM
+bound: 254 FLOP/B against a ridge of 625); `cpu_baseline` is the NumPy
+oracle on this host's cores.  Other workloads of the block (tensor recipe,
+MX, backward, grouped) are timed the same way and reported under `rows`.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FP8 quant+GEMM+LayerNorm TFLOP/s and % FP8 MFMA peak (M=16384,K=N=512)"
+PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+ROTATE = 16
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-rows", action="store_true", help="skip the other workloads")
+    p.add_argument("--only", default=None, help="time one workload only (for profiling): fwd|tensor|mx|bwd|grouped")
+    return p.parse_args()
+
+
+def fwd_bytes(M, K, N, mx=False):
+    """Algorithmic HBM bytes of one fused forward: read X (bf16) once, the
+    weight codes and scales, bias/gamma/beta; write Y (bf16) once."""
+    sw = N * (K // 32) if mx else N * 4
+    return 2 * M * K + N * K + sw + 3 * 2 * N + 2 * M * N
+
+
+def timed_graph(torch, launches, steps, warmup, stream):
+    """Capture `launches` (callables enqueuing on `stream`) into one graph,
+    replay it until `steps` launches ran; returns (seconds, launches run)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for f in launches:  # eager warm-up (kernel attribute set-up happens here)
+            f()
+    stream.synchronize()
+    with torch.cuda.graph(g, stream=stream):
+        for f in launches:
+            f()
+    reps_w = max(1, warmup // len(launches))
+    reps = max(1, steps // len(launches))
+    for _ in range(reps_w):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / 1e3, reps * len(launches)
+
+
+def dev_bf16(torch, bits):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).cuda()
+
+
+def bench_forward(torch, lk, case, x_mode, steps, warmup, stream):
+    """Time loka_gemm_fp8_ln over ROTATE buffer sets; returns a dict."""
+    M, K, N = case["M"], case["K"], case["N"]
+    w = dev_bf16(torch, case["w"])
+    wmode = {"row": "col", "tensor": "tensor", "mx32_row": "mx32_col"}[x_mode]
+    qw, sw, _ = lk.loka_quant_fp8(w, mode=wmode, transpose_out=True, stream=stream)
+    x0 = dev_bf16(torch, case["x"])
+    vec = [dev_bf16(torch, case[k]) for k in ("bias", "gamma", "beta")]
+    launches = []
+    for i in range(ROTATE):
+        x = x0 if i == 0 else x0.clone()
+        f, _ = lk.loka_gemm_fp8_ln(x, qw, sw, *vec, x_mode=x_mode, stream=stream, prepare=True)
+        launches.append(f)
+    torch.cuda.synchronize()
+    secs, n = timed_graph(torch, launches, steps, warmup, stream)
+    per = secs / n
+    flops = 2.0 * M * N * K
+    nbytes = fwd_bytes(M, K, N, mx=x_mode == "mx32_row")
+    # the weight quantization (once per training step), same rotation
+    import ctypes
+    a = lk.QuantArgs(rows=K, cols=N, ld=N, mode=lk.MODES[wmode])
+    nb = lk.library().loka_quant_workspace_size(ctypes.byref(a))
+    wsq = torch.empty(max(nb, 16), dtype=torch.uint8, device="cuda")
+    wq = []
+    for i in range(ROTATE):
+        wi = w if i == 0 else w.clone()
+        qwi, swi = torch.empty_like(qw), torch.empty_like(sw)
+        wq.append(lambda wi=wi, qwi=qwi, swi=swi: lk.loka_quant_fp8(
+            wi, mode=wmode, transpose_out=True, codes=qwi, scales=swi, stream=stream, workspace=wsq))
+    wsecs, wn = timed_graph(torch, wq, min(steps, 800), min(warmup, 80), stream)
+    return {"us": per * 1e6, "tflops": flops / per / 1e12, "gbs": nbytes / per / 1e9, "bytes": nbytes,
+            "flops": flops, "weight_quant_us": wsecs / wn * 1e6}
+
+
+def bench_backward(torch, lk, case, steps, warmup, stream):
+    M, K, N = case["M"], case["K"], case["N"]
+    x, w, dy = dev_bf16(torch, case["x"]), dev_bf16(torch, case["w"]), dev_bf16(torch, case["dy"])
+    bias, gamma, beta = (dev_bf16(torch, case[k]) for k in ("bias", "gamma", "beta"))
+    qw, sw, _ = lk.loka_quant_fp8(w, mode="col", transpose_out=True, stream=stream)
+    qwr, swr, _ = lk.loka_quant_fp8(w, mode="row", stream=stream)
+    f = lk.loka_gemm_fp8_ln(x, qw, sw, bias, gamma, beta, want_stats=True, want_qx=True, stream=stream)
+    ctx = {"qx": f["qx"], "sx": f["sx"], "mean": f["mean"], "rstd": f["rstd"], "qw": qw, "sw": sw}
+    launches = []
+    for i in range(4):
+        dyi = dy if i == 0 else dy.clone()
+        fn, _ = lk.loka_gemm_fp8_bwd(dyi, x, qwr, swr, ctx=ctx, bias=bias, gamma=gamma, stream=stream, prepare=True)
+        launches.append(fn)
+    torch.cuda.synchronize()
+    secs, n = timed_graph(torch, launches, max(40, steps // 20), max(8, warmup // 20), stream)
+    per = secs / n
+    flops = 2.0 * M * N * K * 3  # recomputed Z, dgrad, wgrad
+    nbytes = 2 * M * N + M * K + 2 * M * K + 2 * M * K + 4 * K * N  # dY, qX, X, dX, dW (minimum)
+    return {"us": per * 1e6, "tflops": flops / per / 1e12, "gbs_min_bytes": nbytes / per / 1e9}
+
+
+def bench_grouped(torch, lk, groups, steps, warmup, stream):
+    dg = []
+    flops = 0.0
+    nbytes = 0
+    for g in groups:
+        qw, sw, _ = lk.loka_quant_fp8(dev_bf16(torch, g["w"]), mode="col", transpose_out=True, stream=stream)
+        dg.append({"x": dev_bf16(torch, g["x"]), "qw": qw, "sw": sw, "bias": dev_bf16(torch, g["bias"]),
+                   "gamma": dev_bf16(torch, g["gamma"]), "beta": dev_bf16(torch, g["beta"])})
+        flops += 2.0 * g["M"] * g["N"] * g["K"]
+        nbytes += fwd_bytes(g["M"], g["K"], g["N"])
+    fn, _ = lk.loka_grouped_gemm_fp8_ln(dg, stream=stream, prepare=True)
+    torch.cuda.synchronize()
+    secs, n = timed_graph(torch, [fn], max(20, steps // 40), max(4, warmup // 40), stream)
+    per = secs / n
+    return {"us": per * 1e6, "tflops": flops / per / 1e12, "gbs": nbytes / per / 1e9, "bytes": nbytes,
+            "flops": flops}
+
+
+def cpu_baseline(case):
+    """The NumPy oracle, untuned, on one host thread: the full rowwise
+    forward (quantize X and W, fp64 GEMM, LayerNorm, bf16 rounding)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import forward
+    M, K, N = case["M"], case["K"], case["N"]
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            forward.gemm_ln_forward(case["x"], case["w"], case["bias"], case["gamma"], case["beta"], recipe="row")
+            reps += 1
+            if time.perf_counter() - t0 > 8.0:
+                break
+        dt = (time.perf_counter() - t0) / reps
+    return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full rowwise forward(s) of M={M},K={K},N={N} on one host thread, "
+                      f"{dt:.2f} s each"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import fp8_precision_gemm_amd as lk
+    from synth import workloads
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    stream = torch.cuda.Stream()
+    case = workloads.outlier_case(dy=True)
+    rows = {}
+    only = args.only
+    main_res = None
+    if only in (None, "fwd"):
+        main_res = bench_forward(torch, lk, case, "row", args.steps, args.warmup, stream)
+        print(f"[bench] rowwise forward: {main_res['us']:.2f} us/launch", file=sys.stderr, flush=True)
+    if not args.no_rows and only in (None, "tensor"):
+        r = bench_forward(torch, lk, workloads.tensor_case(), "tensor", args.steps, args.warmup, stream)
+        rows["tensor_fwd_512x256x256"] = {k: round(v, 3) for k, v in r.items()}
+        print(f"[bench] tensor forward: {r['us']:.2f} us", file=sys.stderr, flush=True)
+    if not args.no_rows and only in (None, "mx"):
+        r = bench_forward(torch, lk, workloads.mx_case(), "mx32_row", max(200, args.steps // 4),
+                          max(20, args.warmup // 4), stream)
+        rows["mx_fwd_65536x1024x256"] = {k: round(v, 3) for k, v in r.items()}
+        rows["mx_fwd_65536x1024x256"]["hbm_frac"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
+        print(f"[bench] mx forward: {r['us']:.2f} us", file=sys.stderr, flush=True)
+    if not args.no_rows and only in (None, "bwd"):
+        r = bench_backward(torch, lk, case, args.steps, args.warmup, stream)
+        rows["bwd_16384x512x512"] = {k: round(v, 3) for k, v in r.items()}
+        print(f"[bench] backward: {r['us']:.2f} us", file=sys.stderr, flush=True)
+    if not args.no_rows and only in (None, "grouped"):
+        r = bench_grouped(torch, lk, workloads.grouped_case(), args.steps, args.warmup, stream)
+        rows["grouped_64x8192"] = {k: round(v, 3) for k, v in r.items()}
+        rows["grouped_64x8192"]["hbm_frac"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
+        print(f"[bench] grouped: {r['us']:.2f} us", file=sys.stderr, flush=True)
+    if main_res is None:
+        print(json.dumps({"rows": rows}))
+        return
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(case)
+    ms = main_res["us"] / 1e3
+    out = {
+        "metric": METRIC,
+        "value": round(main_res["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": "rowwise FP8 GEMM + LayerNorm forward, X[16384,512] Student-t(3) with 5 outlier "
+                               "columns x50, W[512,512] per-column e4m3, LayerNorm over 512",
+                   "M": 16384, "K": 512, "N": 512, "x_scaling": "row", "w_scaling": "col", "fmt": "e4m3"},
+        "pct_fp8_peak": round(100 * main_res["tflops"] / PEAK_FP8_TFLOPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(main_res["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(main_res["gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "k_fwd<row> (fused X quant + FP8 MFMA GEMM + LayerNorm)",
+                     "algorithmic_bytes_per_launch": main_res["bytes"],
+                     "avg_launch_us": round(main_res["us"], 3)},
+        "weight_quant_us": round(main_res["weight_quant_us"], 3),
+        "value_incl_weight_quant": round(main_res["flops"] / ((main_res["us"] + main_res["weight_quant_us"]) * 1e-6)
+                                         / 1e12, 2),
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

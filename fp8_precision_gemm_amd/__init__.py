@@ -1,0 +1,326 @@
+"""Python binding of liblokafp8.so (the FP8 GEMM + LayerNorm block for MI355X).
+
+Argument marshalling only: every step of the block runs in the library's
+HIP kernels.  PyTorch provides device memory and the current stream.  The
+functions carry the C ABI's names (see include/loka_fp8.h for the full
+contract and the page passages each call follows).  If the library is not
+built, importing works but every call raises: there is no fallback path.
+"""
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LokaError", "library", "library_path", "abi_version",
+    "loka_quant_fp8", "loka_gemm_fp8_ln", "loka_gemm_fp8_bwd", "loka_grouped_gemm_fp8_ln",
+    "QuantArgs", "FwdArgs", "BwdArgs", "GroupDesc", "GroupedArgs",
+    "E4M3", "E5M2", "MODES", "STATUS",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "liblokafp8.so")
+
+E4M3, E5M2 = 0, 1
+FMTS = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
+MODES = {"tensor": 0, "row": 1, "col": 2, "mx32_row": 3, "mx32_col": 4}
+STATUS = {0: "LOKA_OK", 1: "LOKA_ERR_INVALID_ARG", 2: "LOKA_ERR_UNSUPPORTED", 3: "LOKA_ERR_ALIGNMENT",
+          4: "LOKA_ERR_WORKSPACE", 5: "LOKA_ERR_HIP"}
+BWD_NO_LN = 1
+
+c_i64, c_i32, c_f32, c_vp, c_sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class QuantArgs(ctypes.Structure):
+    _fields_ = [("rows", c_i64), ("cols", c_i64), ("ld", c_i64), ("src_dtype", c_i32), ("fmt", c_i32),
+                ("mode", c_i32), ("transpose_out", c_i32), ("src", c_vp), ("codes", c_vp), ("scales", c_vp),
+                ("amax", c_vp), ("workspace", c_vp), ("workspace_bytes", c_sz)]
+
+
+class FwdArgs(ctypes.Structure):
+    _fields_ = [("M", c_i64), ("N", c_i64), ("K", c_i64), ("x_mode", c_i32), ("flags", c_i32), ("eps", c_f32),
+                ("x", c_vp), ("qw", c_vp), ("sw", c_vp), ("bias", c_vp), ("gamma", c_vp), ("beta", c_vp),
+                ("y", c_vp), ("z", c_vp), ("mean", c_vp), ("rstd", c_vp), ("qx_out", c_vp), ("sx_out", c_vp),
+                ("workspace", c_vp), ("workspace_bytes", c_sz)]
+
+
+class BwdArgs(ctypes.Structure):
+    _fields_ = [("M", c_i64), ("N", c_i64), ("K", c_i64), ("flags", c_i32), ("reserved", c_i32),
+                ("dy", c_vp), ("qx", c_vp), ("sx", c_vp), ("mean", c_vp), ("rstd", c_vp), ("qw", c_vp),
+                ("sw", c_vp), ("bias", c_vp), ("gamma", c_vp), ("x", c_vp), ("qw_row", c_vp), ("sw_row", c_vp),
+                ("dx", c_vp), ("dw", c_vp), ("dgamma", c_vp), ("dbeta", c_vp), ("dbias", c_vp), ("dz", c_vp),
+                ("dz_codes", c_vp), ("dz_scales", c_vp), ("workspace", c_vp), ("workspace_bytes", c_sz)]
+
+
+class GroupDesc(ctypes.Structure):
+    _fields_ = [("M", c_i64), ("N", c_i64), ("K", c_i64), ("x", c_vp), ("qw", c_vp), ("sw", c_vp), ("bias", c_vp),
+                ("gamma", c_vp), ("beta", c_vp), ("y", c_vp), ("z", c_vp)]
+
+
+class GroupedArgs(ctypes.Structure):
+    _fields_ = [("num_groups", c_i32), ("x_mode", c_i32), ("eps", c_f32), ("reserved", c_i32),
+                ("groups", ctypes.POINTER(GroupDesc)), ("workspace", c_vp), ("workspace_bytes", c_sz)]
+
+
+class LokaError(RuntimeError):
+    def __init__(self, status, detail):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+_lib = None
+
+
+def library():
+    """The loaded liblokafp8.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is missing: build it with "
+                               "`python -m fp8_precision_gemm_amd.build` (no fallback exists)")
+        lib = ctypes.CDLL(library_path)
+        for name, argt in [("loka_quant_fp8", QuantArgs), ("loka_gemm_fp8_ln", FwdArgs),
+                           ("loka_gemm_fp8_bwd", BwdArgs), ("loka_grouped_gemm_fp8_ln", GroupedArgs)]:
+            f = getattr(lib, name)
+            f.argtypes = [ctypes.POINTER(argt), c_vp]
+            f.restype = c_i32
+        for name, argt in [("loka_quant_workspace_size", QuantArgs), ("loka_gemm_fp8_ln_workspace_size", FwdArgs),
+                           ("loka_gemm_fp8_bwd_workspace_size", BwdArgs), ("loka_grouped_workspace_size", GroupedArgs)]:
+            f = getattr(lib, name)
+            f.argtypes = [ctypes.POINTER(argt)]
+            f.restype = c_sz
+        lib.loka_last_error.restype = ctypes.c_char_p
+        lib.loka_status_string.restype = ctypes.c_char_p
+        lib.loka_status_string.argtypes = [c_i32]
+        lib.loka_abi_version.restype = c_i32
+        _lib = lib
+    return _lib
+
+
+def abi_version():
+    return library().loka_abi_version()
+
+
+def _check(status):
+    if status != 0:
+        raise LokaError(status, library().loka_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _workspace(nbytes, device, given=None):
+    if nbytes == 0:
+        return None
+    if given is not None:
+        return given
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _need(t, dtype, shape, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def loka_quant_fp8(src, fmt="e4m3", mode="row", transpose_out=False, codes=None, scales=None, amax=None,
+                   want_amax=False, workspace=None, stream=None):
+    """Quantize a 2-D bf16/fp32 CUDA tensor.  Returns (codes, scales, amax)."""
+    if src.dim() != 2 or src.stride(1) != 1:
+        raise ValueError("src must be 2-D with unit column stride")
+    rows, cols = src.shape
+    m = MODES[mode]
+    f = FMTS[fmt]
+    dev = src.device
+    if codes is None:
+        codes = torch.empty((cols, rows) if transpose_out else (rows, cols), dtype=torch.uint8, device=dev)
+    if scales is None:
+        if m == 0:
+            scales = torch.empty(1, dtype=torch.float32, device=dev)
+        elif m == 1:
+            scales = torch.empty(rows, dtype=torch.float32, device=dev)
+        elif m == 2:
+            scales = torch.empty(cols, dtype=torch.float32, device=dev)
+        elif m == 3:
+            scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+        else:
+            scales = torch.empty((cols, rows // 32), dtype=torch.uint8, device=dev)
+    if want_amax and amax is None and m <= 2:
+        amax = torch.empty(scales.shape, dtype=torch.float32, device=dev)
+    a = QuantArgs(rows=rows, cols=cols, ld=src.stride(0) if rows > 1 else cols,
+                  src_dtype=0 if src.dtype == torch.bfloat16 else 1, fmt=f, mode=m,
+                  transpose_out=1 if transpose_out else 0, src=_ptr(src), codes=_ptr(codes), scales=_ptr(scales),
+                  amax=_ptr(amax))
+    if src.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("src must be bfloat16 or float32")
+    lib = library()
+    nb = lib.loka_quant_workspace_size(ctypes.byref(a))
+    ws = _workspace(nb, dev, workspace)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = nb if ws is None else ws.numel()
+    _check(lib.loka_quant_fp8(ctypes.byref(a), _stream(stream)))
+    return codes, scales, amax
+
+
+def _fwd_args(x, qw, sw, bias, gamma, beta, eps, x_mode, y, z, mean, rstd, qx_out, sx_out):
+    M, K = x.shape
+    N = qw.shape[0]
+    return FwdArgs(M=M, N=N, K=K, x_mode=MODES[x_mode], flags=0, eps=eps, x=_ptr(x), qw=_ptr(qw), sw=_ptr(sw),
+                   bias=_ptr(bias), gamma=_ptr(gamma), beta=_ptr(beta), y=_ptr(y), z=_ptr(z), mean=_ptr(mean),
+                   rstd=_ptr(rstd), qx_out=_ptr(qx_out), sx_out=_ptr(sx_out))
+
+
+def loka_gemm_fp8_ln(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e-5, x_mode="row", y=None, want_z=False,
+                     want_stats=False, want_qx=False, workspace=None, stream=None, prepare=False):
+    """Y = LayerNorm(dequant(q(X) . q(W)) + bias) for bf16 X [M, K] and the
+    pre-quantized weight qw [N, K] (e4m3) with scales sw.
+
+    Returns a dict with y and the requested optional outputs.  With
+    prepare=True returns (launch, outputs) where launch() enqueues the call
+    again with the same arguments (for timing loops)."""
+    M, K = x.shape
+    N = qw.shape[0]
+    dev = x.device
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(qw, torch.uint8, (N, K), "qw")
+    for v, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta")):
+        if v is not None:
+            _need(v, torch.bfloat16, (N,), nm)
+    out = {"y": y if y is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)}
+    if want_z:
+        out["z"] = torch.empty((M, N), dtype=torch.float32, device=dev)
+    if want_stats:
+        out["mean"] = torch.empty(M, dtype=torch.float32, device=dev)
+        out["rstd"] = torch.empty(M, dtype=torch.float32, device=dev)
+    if want_qx:
+        out["qx"] = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        if x_mode == "tensor":
+            out["sx"] = torch.empty(1, dtype=torch.float32, device=dev)
+        elif x_mode == "row":
+            out["sx"] = torch.empty(M, dtype=torch.float32, device=dev)
+        else:
+            out["sx"] = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    a = _fwd_args(x, qw, sw, bias, gamma, beta, eps, x_mode, out["y"], out.get("z"), out.get("mean"),
+                  out.get("rstd"), out.get("qx"), out.get("sx"))
+    lib = library()
+    nb = lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(a))
+    ws = _workspace(nb, dev, workspace)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = nb if ws is None else ws.numel()
+    keep = (x, qw, sw, bias, gamma, beta, ws, out)
+    st = _stream(stream)
+    fn = lib.loka_gemm_fp8_ln
+    ref = ctypes.byref(a)
+
+    def launch():
+        _check(fn(ref, st))
+        return keep
+
+    if prepare:
+        return launch, out
+    launch()
+    return out
+
+
+def loka_gemm_fp8_bwd(dy, x, qw_row, sw_row, ctx=None, bias=None, gamma=None, no_ln=False, want_dz=False,
+                      want_dz_codes=False, want_dgamma=True, want_dbias=True, workspace=None, stream=None,
+                      prepare=False):
+    """Backward of loka_gemm_fp8_ln (row recipe).
+
+    ctx: dict with qx [M,K] uint8, sx [M], mean [M], rstd [M], qw [N,K], sw [N]
+    (the forward's qx/sx outputs, statistics and weight); unused with no_ln.
+    Returns a dict with dx, dw and the requested outputs."""
+    M, N = dy.shape
+    K = x.shape[1]
+    dev = dy.device
+    _need(dy, torch.bfloat16, (M, N), "dy")
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(qw_row, torch.uint8, (K, N), "qw_row")
+    ctx = ctx or {}
+    out = {"dx": torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+           "dw": torch.empty((K, N), dtype=torch.float32, device=dev)}
+    if want_dgamma and not no_ln:
+        out["dgamma"] = torch.empty(N, dtype=torch.float32, device=dev)
+        out["dbeta"] = torch.empty(N, dtype=torch.float32, device=dev)
+    if want_dbias:
+        out["dbias"] = torch.empty(N, dtype=torch.float32, device=dev)
+    if want_dz:
+        out["dz"] = torch.empty((M, N), dtype=torch.float32, device=dev)
+    if want_dz_codes:
+        out["dz_codes"] = torch.empty((M, N), dtype=torch.uint8, device=dev)
+        out["dz_scales"] = torch.empty(M, dtype=torch.float32, device=dev)
+    a = BwdArgs(M=M, N=N, K=K, flags=BWD_NO_LN if no_ln else 0, reserved=0, dy=_ptr(dy), qx=_ptr(ctx.get("qx")),
+                sx=_ptr(ctx.get("sx")), mean=_ptr(ctx.get("mean")), rstd=_ptr(ctx.get("rstd")),
+                qw=_ptr(ctx.get("qw")), sw=_ptr(ctx.get("sw")), bias=_ptr(bias), gamma=_ptr(gamma), x=_ptr(x),
+                qw_row=_ptr(qw_row), sw_row=_ptr(sw_row), dx=_ptr(out["dx"]), dw=_ptr(out["dw"]),
+                dgamma=_ptr(out.get("dgamma")), dbeta=_ptr(out.get("dbeta")), dbias=_ptr(out.get("dbias")),
+                dz=_ptr(out.get("dz")), dz_codes=_ptr(out.get("dz_codes")), dz_scales=_ptr(out.get("dz_scales")))
+    lib = library()
+    nb = lib.loka_gemm_fp8_bwd_workspace_size(ctypes.byref(a))
+    ws = _workspace(nb, dev, workspace)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = nb if ws is None else ws.numel()
+    keep = (dy, x, qw_row, sw_row, ctx, bias, gamma, ws, out)
+    st = _stream(stream)
+    fn = lib.loka_gemm_fp8_bwd
+    ref = ctypes.byref(a)
+
+    def launch():
+        _check(fn(ref, st))
+        return keep
+
+    if prepare:
+        return launch, out
+    launch()
+    return out
+
+
+def loka_grouped_gemm_fp8_ln(groups, eps=1e-5, want_z=False, workspace=None, stream=None, prepare=False):
+    """groups: list of dicts with x [M,K] bf16, qw [N,K] uint8, sw [N] fp32 and
+    optional bias/gamma/beta bf16 [N].  Returns one output dict per group."""
+    outs, keep = [], []
+    descs = (GroupDesc * max(1, len(groups)))()
+    for i, g in enumerate(groups):
+        x, qw = g["x"], g["qw"]
+        M, K = x.shape
+        N = qw.shape[0]
+        _need(x, torch.bfloat16, (M, K), f"groups[{i}].x")
+        _need(qw, torch.uint8, (N, K), f"groups[{i}].qw")
+        o = {"y": torch.empty((M, N), dtype=torch.bfloat16, device=x.device)}
+        if want_z:
+            o["z"] = torch.empty((M, N), dtype=torch.float32, device=x.device)
+        outs.append(o)
+        keep.append((g, o))
+        descs[i] = GroupDesc(M=M, N=N, K=K, x=_ptr(x), qw=_ptr(qw), sw=_ptr(g["sw"]), bias=_ptr(g.get("bias")),
+                             gamma=_ptr(g.get("gamma")), beta=_ptr(g.get("beta")), y=_ptr(o["y"]), z=_ptr(o.get("z")))
+    a = GroupedArgs(num_groups=len(groups), x_mode=MODES["row"], eps=eps, reserved=0, groups=descs)
+    lib = library()
+    nb = lib.loka_grouped_workspace_size(ctypes.byref(a))
+    dev = groups[0]["x"].device if groups else torch.device("cuda")
+    ws = _workspace(nb, dev, workspace)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = nb if ws is None else ws.numel()
+    keep.append((descs, ws))
+    st = _stream(stream)
+    fn = lib.loka_grouped_gemm_fp8_ln
+    ref = ctypes.byref(a)
+
+    def launch():
+        _check(fn(ref, st))
+        return keep
+
+    if prepare:
+        return launch, outs
+    launch()
+    return outs

@@ -1,0 +1,240 @@
+// C ABI of liblokafp8.so: argument validation, workspace sizing and dispatch
+// to the gfx950 kernels.  The contract of each entry point (with the page
+// passages it follows) is in include/loka_fp8.h.  Validation runs before any
+// HIP call, so every error path is reachable without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/loka_fp8.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+loka_status fail(loka_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+loka_status fail(loka_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+loka_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) {
+    g_last_error[0] = '\0';
+    return LOKA_OK;
+  }
+  return fail(LOKA_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE(cond, st, ...) \
+  do {                         \
+    if (!(cond)) return fail(st, __VA_ARGS__); \
+  } while (0)
+
+#define REQUIRE_ALIGNED(ptr) \
+  REQUIRE((ptr) == nullptr || aligned16(ptr), LOKA_ERR_ALIGNMENT, "%s is not 16-byte aligned", #ptr)
+
+loka_status check_workspace(size_t need, const void* ws, size_t have) {
+  if (need == 0) return LOKA_OK;
+  REQUIRE(ws != nullptr, LOKA_ERR_WORKSPACE, "workspace is NULL but %zu bytes are required", need);
+  REQUIRE(have >= need, LOKA_ERR_WORKSPACE, "workspace_bytes %zu < required %zu", have, need);
+  REQUIRE(aligned16(ws), LOKA_ERR_ALIGNMENT, "workspace is not 16-byte aligned");
+  return LOKA_OK;
+}
+
+// Shape checks shared by the forward, backward and grouped entry points.
+loka_status check_fwd_shape(int64_t M, int64_t N, int64_t K, int x_mode) {
+  REQUIRE(M >= 0 && N >= 0 && K >= 0, LOKA_ERR_INVALID_ARG, "negative size (M=%lld N=%lld K=%lld)", (long long)M,
+          (long long)N, (long long)K);
+  REQUIRE(N % 64 == 0 && N >= 64 && N <= 1024, LOKA_ERR_UNSUPPORTED,
+          "N=%lld: the fused LayerNorm needs N %% 64 == 0 and 64 <= N <= 1024", (long long)N);
+  REQUIRE(K >= 16 && K <= 2048 && K % 16 == 0, LOKA_ERR_UNSUPPORTED, "K=%lld: need K %% 16 == 0, 16 <= K <= 2048",
+          (long long)K);
+  REQUIRE(x_mode != LOKA_SCALE_MX32_ROW || K % 32 == 0, LOKA_ERR_UNSUPPORTED, "MX32 needs K %% 32 == 0 (K=%lld)",
+          (long long)K);
+  REQUIRE(M <= ((int64_t)1 << 31) - 64, LOKA_ERR_UNSUPPORTED, "M=%lld too large", (long long)M);
+  return LOKA_OK;
+}
+
+loka_status check_eps(float eps) {
+  REQUIRE(std::isfinite(eps) && eps >= 0.0f, LOKA_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  return LOKA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int loka_abi_version(void) { return LOKA_ABI_VERSION; }
+
+const char* loka_status_string(loka_status s) {
+  switch (s) {
+    case LOKA_OK: return "LOKA_OK";
+    case LOKA_ERR_INVALID_ARG: return "LOKA_ERR_INVALID_ARG";
+    case LOKA_ERR_UNSUPPORTED: return "LOKA_ERR_UNSUPPORTED";
+    case LOKA_ERR_ALIGNMENT: return "LOKA_ERR_ALIGNMENT";
+    case LOKA_ERR_WORKSPACE: return "LOKA_ERR_WORKSPACE";
+    case LOKA_ERR_HIP: return "LOKA_ERR_HIP";
+  }
+  return "LOKA_ERR_UNKNOWN";
+}
+
+const char* loka_last_error(void) { return g_last_error; }
+
+// ---------------------------------------------------------------------------
+size_t loka_quant_workspace_size(const loka_quant_args* a) {
+  if (a == nullptr || a->rows < 0 || a->cols < 0 || a->mode < 0 || a->mode > 4) return 0;
+  if (a->rows == 0 || a->cols == 0) return 0;
+  return (size_t)loka::quant_plan(a->rows, a->cols, a->mode).ws_floats * sizeof(float);
+}
+
+loka_status loka_quant_fp8(const loka_quant_args* a, void* stream) {
+  REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
+  REQUIRE(a->rows >= 0 && a->cols >= 0, LOKA_ERR_INVALID_ARG, "negative rows/cols");
+  REQUIRE(a->ld >= a->cols, LOKA_ERR_INVALID_ARG, "ld %lld < cols %lld", (long long)a->ld, (long long)a->cols);
+  REQUIRE(a->src_dtype == LOKA_DTYPE_BF16 || a->src_dtype == LOKA_DTYPE_F32, LOKA_ERR_INVALID_ARG, "bad src_dtype %d",
+          a->src_dtype);
+  REQUIRE(a->fmt == LOKA_E4M3 || a->fmt == LOKA_E5M2, LOKA_ERR_INVALID_ARG, "bad fmt %d", a->fmt);
+  REQUIRE(a->mode >= LOKA_SCALE_TENSOR && a->mode <= LOKA_SCALE_MX32_COL, LOKA_ERR_INVALID_ARG, "bad mode %d", a->mode);
+  REQUIRE(a->transpose_out == 0 || a->transpose_out == 1, LOKA_ERR_INVALID_ARG, "transpose_out must be 0 or 1");
+  const bool mx = a->mode == LOKA_SCALE_MX32_ROW || a->mode == LOKA_SCALE_MX32_COL;
+  REQUIRE(!(mx && a->amax != nullptr), LOKA_ERR_INVALID_ARG, "amax output is not defined for MX modes");
+  REQUIRE(a->cols % 16 == 0, LOKA_ERR_UNSUPPORTED, "cols %% 16 != 0");
+  REQUIRE(a->ld % 8 == 0, LOKA_ERR_ALIGNMENT, "ld %% 8 != 0");
+  REQUIRE(a->mode != LOKA_SCALE_MX32_ROW || a->cols % 32 == 0, LOKA_ERR_UNSUPPORTED, "MX32_ROW needs cols %% 32 == 0");
+  REQUIRE(a->mode != LOKA_SCALE_MX32_COL || a->rows % 32 == 0, LOKA_ERR_UNSUPPORTED, "MX32_COL needs rows %% 32 == 0");
+  REQUIRE(!a->transpose_out || a->rows % 16 == 0, LOKA_ERR_UNSUPPORTED, "transpose_out needs rows %% 16 == 0");
+  const bool empty = a->rows == 0 || a->cols == 0;
+  if (!empty) {
+    REQUIRE(a->src && a->codes && a->scales, LOKA_ERR_INVALID_ARG, "src, codes and scales are required");
+  }
+  REQUIRE_ALIGNED(a->src);
+  REQUIRE_ALIGNED(a->codes);
+  REQUIRE_ALIGNED(a->scales);
+  REQUIRE_ALIGNED(a->amax);
+  loka_status st = check_workspace(loka_quant_workspace_size(a), a->workspace, a->workspace_bytes);
+  if (st != LOKA_OK) return st;
+  if (empty) return LOKA_OK;
+  loka::QuantLaunch q{};
+  q.src = a->src; q.rows = a->rows; q.cols = a->cols; q.ld = a->ld;
+  q.src_dtype = a->src_dtype; q.fmt = a->fmt; q.mode = a->mode; q.transpose_out = a->transpose_out;
+  q.codes = a->codes; q.scales = a->scales; q.amax_out = a->amax; q.workspace = a->workspace;
+  return hip_status(loka::launch_quant(q, static_cast<hipStream_t>(stream)), "loka_quant_fp8");
+}
+
+// ---------------------------------------------------------------------------
+size_t loka_gemm_fp8_ln_workspace_size(const loka_fwd_args* a) {
+  if (a == nullptr || a->M <= 0 || a->K <= 0) return 0;
+  return loka::fwd_workspace_bytes(a->M, a->N, a->K, a->x_mode);
+}
+
+loka_status loka_gemm_fp8_ln(const loka_fwd_args* a, void* stream) {
+  REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
+  REQUIRE(a->x_mode == LOKA_SCALE_TENSOR || a->x_mode == LOKA_SCALE_ROW || a->x_mode == LOKA_SCALE_MX32_ROW,
+          LOKA_ERR_INVALID_ARG, "x_mode must be TENSOR, ROW or MX32_ROW (got %d)", a->x_mode);
+  REQUIRE(a->flags == 0, LOKA_ERR_INVALID_ARG, "flags must be 0");
+  loka_status st = check_fwd_shape(a->M, a->N, a->K, a->x_mode);
+  if (st != LOKA_OK) return st;
+  if ((st = check_eps(a->eps)) != LOKA_OK) return st;
+  if (a->M > 0) REQUIRE(a->x && a->qw && a->sw && a->y, LOKA_ERR_INVALID_ARG, "x, qw, sw and y are required");
+  REQUIRE_ALIGNED(a->x); REQUIRE_ALIGNED(a->qw); REQUIRE_ALIGNED(a->sw); REQUIRE_ALIGNED(a->bias);
+  REQUIRE_ALIGNED(a->gamma); REQUIRE_ALIGNED(a->beta); REQUIRE_ALIGNED(a->y); REQUIRE_ALIGNED(a->z);
+  REQUIRE_ALIGNED(a->mean); REQUIRE_ALIGNED(a->rstd); REQUIRE_ALIGNED(a->qx_out); REQUIRE_ALIGNED(a->sx_out);
+  if ((st = check_workspace(loka_gemm_fp8_ln_workspace_size(a), a->workspace, a->workspace_bytes)) != LOKA_OK) return st;
+  if (a->M == 0) return LOKA_OK;
+  loka::FwdLaunch f{};
+  f.M = a->M; f.N = a->N; f.K = a->K; f.x_mode = a->x_mode; f.eps = a->eps;
+  f.x = a->x; f.qw = a->qw; f.sw = a->sw; f.bias = a->bias; f.gamma = a->gamma; f.beta = a->beta;
+  f.y = a->y; f.z = a->z; f.mean = a->mean; f.rstd = a->rstd; f.qx_out = a->qx_out; f.sx_out = a->sx_out;
+  f.workspace = a->workspace;
+  return hip_status(loka::launch_fwd(f, static_cast<hipStream_t>(stream)), "loka_gemm_fp8_ln");
+}
+
+// ---------------------------------------------------------------------------
+size_t loka_gemm_fp8_bwd_workspace_size(const loka_bwd_args* a) {
+  if (a == nullptr || a->M <= 0 || a->N <= 0 || a->K <= 0) return 0;
+  return loka::bwd_workspace_bytes(a->M, a->N, a->K);
+}
+
+loka_status loka_gemm_fp8_bwd(const loka_bwd_args* a, void* stream) {
+  REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
+  REQUIRE(a->flags == 0 || a->flags == LOKA_BWD_NO_LN, LOKA_ERR_INVALID_ARG, "unknown flags %d", a->flags);
+  loka_status st = check_fwd_shape(a->M, a->N, a->K, LOKA_SCALE_ROW);
+  if (st != LOKA_OK) return st;
+  REQUIRE(a->K % 64 == 0 && a->K <= 1024, LOKA_ERR_UNSUPPORTED, "backward needs K %% 64 == 0 and K <= 1024");
+  REQUIRE(a->M % 16 == 0, LOKA_ERR_UNSUPPORTED, "backward needs M %% 16 == 0");
+  const bool no_ln = (a->flags & LOKA_BWD_NO_LN) != 0;
+  if (a->M > 0) {
+    REQUIRE(a->dy && a->x && a->qw_row && a->sw_row && a->dx && a->dw, LOKA_ERR_INVALID_ARG,
+            "dy, x, qw_row, sw_row, dx and dw are required");
+    if (!no_ln)
+      REQUIRE(a->qx && a->sx && a->mean && a->rstd && a->qw && a->sw, LOKA_ERR_INVALID_ARG,
+              "the forward context (qx, sx, mean, rstd, qw, sw) is required");
+  }
+  REQUIRE(!(no_ln && (a->dgamma || a->dbeta)), LOKA_ERR_INVALID_ARG, "dgamma/dbeta are undefined without LayerNorm");
+  REQUIRE_ALIGNED(a->dy); REQUIRE_ALIGNED(a->qx); REQUIRE_ALIGNED(a->sx); REQUIRE_ALIGNED(a->mean);
+  REQUIRE_ALIGNED(a->rstd); REQUIRE_ALIGNED(a->qw); REQUIRE_ALIGNED(a->sw); REQUIRE_ALIGNED(a->bias);
+  REQUIRE_ALIGNED(a->gamma); REQUIRE_ALIGNED(a->x); REQUIRE_ALIGNED(a->qw_row); REQUIRE_ALIGNED(a->sw_row);
+  REQUIRE_ALIGNED(a->dx); REQUIRE_ALIGNED(a->dw); REQUIRE_ALIGNED(a->dgamma); REQUIRE_ALIGNED(a->dbeta);
+  REQUIRE_ALIGNED(a->dbias); REQUIRE_ALIGNED(a->dz); REQUIRE_ALIGNED(a->dz_codes); REQUIRE_ALIGNED(a->dz_scales);
+  if ((st = check_workspace(loka_gemm_fp8_bwd_workspace_size(a), a->workspace, a->workspace_bytes)) != LOKA_OK)
+    return st;
+  if (a->M == 0) return LOKA_OK;
+  loka::BwdLaunch b{};
+  b.M = a->M; b.N = a->N; b.K = a->K; b.no_ln = no_ln ? 1 : 0;
+  b.dy = a->dy; b.qx = a->qx; b.sx = a->sx; b.mean = a->mean; b.rstd = a->rstd; b.qw = a->qw; b.sw = a->sw;
+  b.bias = a->bias; b.gamma = a->gamma; b.x = a->x; b.qw_row = a->qw_row; b.sw_row = a->sw_row;
+  b.dx = a->dx; b.dw = a->dw; b.dgamma = a->dgamma; b.dbeta = a->dbeta; b.dbias = a->dbias;
+  b.dz = a->dz; b.dz_codes = a->dz_codes; b.dz_scales = a->dz_scales; b.workspace = a->workspace;
+  return hip_status(loka::launch_bwd(b, static_cast<hipStream_t>(stream)), "loka_gemm_fp8_bwd");
+}
+
+// ---------------------------------------------------------------------------
+static_assert(sizeof(loka_group_desc) == sizeof(loka::GroupDev), "group descriptor layouts differ");
+
+size_t loka_grouped_workspace_size(const loka_grouped_args* a) {
+  if (a == nullptr || a->num_groups <= 0) return 0;
+  return loka::grouped_workspace_bytes(a->num_groups, reinterpret_cast<const loka::GroupDev*>(a->groups));
+}
+
+loka_status loka_grouped_gemm_fp8_ln(const loka_grouped_args* a, void* stream) {
+  REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
+  REQUIRE(a->num_groups >= 0, LOKA_ERR_INVALID_ARG, "num_groups < 0");
+  REQUIRE(a->x_mode == LOKA_SCALE_ROW, LOKA_ERR_UNSUPPORTED, "grouped launch supports x_mode ROW only");
+  loka_status st = check_eps(a->eps);
+  if (st != LOKA_OK) return st;
+  if (a->num_groups == 0) return LOKA_OK;
+  REQUIRE(a->groups != nullptr, LOKA_ERR_INVALID_ARG, "groups is NULL");
+  int64_t tiles = 0;
+  for (int i = 0; i < a->num_groups; ++i) {
+    const loka_group_desc& g = a->groups[i];
+    st = check_fwd_shape(g.M, g.N, g.K, LOKA_SCALE_ROW);
+    if (st != LOKA_OK) return fail(st, "group %d: %s", i, std::string(g_last_error).c_str());
+    if (g.M > 0)
+      REQUIRE(g.x && g.qw && g.sw && g.y, LOKA_ERR_INVALID_ARG, "group %d: x, qw, sw and y are required", i);
+    REQUIRE(aligned16(g.x) && aligned16(g.qw) && aligned16(g.sw) && aligned16(g.bias) && aligned16(g.gamma) &&
+                aligned16(g.beta) && aligned16(g.y) && aligned16(g.z),
+            LOKA_ERR_ALIGNMENT, "group %d: a pointer is not 16-byte aligned", i);
+    tiles += (g.M + 63) / 64;
+  }
+  REQUIRE(tiles < ((int64_t)1 << 31), LOKA_ERR_UNSUPPORTED, "too many tiles");
+  if ((st = check_workspace(loka_grouped_workspace_size(a), a->workspace, a->workspace_bytes)) != LOKA_OK) return st;
+  loka::GroupedLaunch gl{};
+  gl.num_groups = a->num_groups;
+  gl.eps = a->eps;
+  gl.groups = reinterpret_cast<const loka::GroupDev*>(a->groups);
+  gl.workspace = a->workspace;
+  return hip_status(loka::launch_grouped(gl, static_cast<hipStream_t>(stream)), "loka_grouped_gemm_fp8_ln");
+}
+
+}  // extern "C"

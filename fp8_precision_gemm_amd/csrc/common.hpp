@@ -1,0 +1,156 @@
+// Device helpers shared by the gfx950 kernels of liblokafp8: bf16 and FP8
+// conversions, scale arithmetic, wavefront reductions and the FP8 MFMA.
+//
+// Numerics (stated once; every kernel follows them):
+//  * tensor/row/column scales: s = amax / FMAX and r = FMAX / amax, both IEEE
+//    fp32 divisions (correctly rounded: the library is built without fast
+//    math), r clamped to the largest finite fp32, amax == 0 -> s = r = 1.
+//  * cast: t = x * r (one fp32 multiply), clamped to +-FMAX, then the
+//    hardware RNE convert (v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32).  The clamp
+//    makes saturation explicit; the convert rounds to nearest even with
+//    gradual underflow, which was checked bit for bit against exact
+//    round-to-nearest-even on every bf16 value and the FP8 grid midpoints.
+//  * MX32: E8M0 exponent e = clamp(floor(log2 amax) - emax_elem, -127, 127)
+//    read from the fp32 exponent field (leading-zero count for subnormal
+//    amax), as the GEM page's bit-manipulation scale derivation does;
+//    x * 2^-e is one exact fp32 multiply.
+//
+// MFMA operand layout (v_mfma_scale_f32_16x16x128_f8f6f4): lane l supplies
+// operand row (l % 16) and, with g = l / 16, the K bytes [16g, 16g+16) and
+// [64+16g, 64+16g+16) of the 128-wide K chunk (the hardware's own K order,
+// in which the E8M0 scale held by lane group G covers K block [32G, 32G+32)).
+// The result lane l holds D[4*(l/16) + j][l % 16], j = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace loka {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kE5M2Max = 57344.0f;
+constexpr float kFltMax = 3.40282346638528859812e+38f;
+
+template <int FMT>
+struct Fp8Traits;
+template <>
+struct Fp8Traits<0> {  // OCP e4m3
+  static constexpr float fmax = kE4M3Max;
+  static constexpr int emax_elem = 8;
+};
+template <>
+struct Fp8Traits<1> {  // OCP e5m2
+  static constexpr float fmax = kE5M2Max;
+  static constexpr int emax_elem = 15;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t two) { return __uint_as_float(two << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t two) { return __uint_as_float(two & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Two fp32 -> two FP8 codes (saturating RNE), in bits [0,16) of the result
+// merged into `old` at word HI (false: bits 0-15, true: bits 16-31).
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t cvt_pk(float a, float b, uint32_t old) {
+  constexpr float m = Fp8Traits<FMT>::fmax;
+  a = fminf(fmaxf(a, -m), m);
+  b = fminf(fmaxf(b, -m), m);
+  if (FMT == 0) return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, (int)old, HI);
+}
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt4(float a, float b, float c, float d) {
+  uint32_t lo = cvt_pk<FMT, false>(a, b, 0u);
+  return cvt_pk<FMT, true>(c, d, lo);
+}
+
+struct ScalePair {
+  float s;  // dequantization scale (stored)
+  float r;  // quantization multiplier
+};
+template <int FMT>
+__device__ __forceinline__ ScalePair scales_from_amax(float amax) {
+  ScalePair p;
+  if (amax == 0.0f) {
+    p.s = 1.0f;
+    p.r = 1.0f;
+  } else {
+    p.s = amax / Fp8Traits<FMT>::fmax;
+    p.r = fminf(Fp8Traits<FMT>::fmax / amax, kFltMax);
+  }
+  return p;
+}
+
+// E8M0 code of an fp32 block amax (>= 0, finite).
+template <int FMT>
+__device__ __forceinline__ int e8m0_from_amax(float amax) {
+  uint32_t u = __float_as_uint(amax);
+  if (u == 0u) return 0;
+  int ef = (int)(u >> 23);
+  int flog2 = ef != 0 ? ef - 127 : (31 - __clz((int)(u & 0x7FFFFFu))) - 149;
+  int e = flog2 - Fp8Traits<FMT>::emax_elem;
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  return e + 127;
+}
+// 2^-(code-127) as an fp32 multiplier; exact for every code an fp32 amax can
+// produce (the exponent stays within [-119, 127]).
+__device__ __forceinline__ float e8m0_inv_multiplier(int code) {
+  int neg = 127 - code;  // -e
+  return __uint_as_float((uint32_t)(neg + 127) << 23);
+}
+
+// Wavefront (64-lane) reductions.
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+// Reduction over the 4 lane groups that share l % 16 (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float group4_sum(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+// FP8 MFMA, fp32 accumulate.  FA/FB: 0 = e4m3, 1 = e5m2 (the instruction's
+// cbsz / blgp format selectors).  Scale operands 0 select the unscaled form.
+template <int FA, int FB>
+__device__ __forceinline__ v4f mfma_fp8(const v8i& a, const v8i& b, v4f c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, 0, 0, 0);
+}
+// MX form: sa / sb are the E8M0 codes this lane supplies.
+__device__ __forceinline__ v4f mfma_mx_e4m3(const v8i& a, const v8i& b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// Load one MFMA operand fragment: 16 bytes at p + 16g and 16 bytes at
+// p + 64 + 16g, each half only when it lies below `limit` bytes (else 0).
+__device__ __forceinline__ v8i load_frag(const uint8_t* p, int g, int kc, int limit) {
+  v8i f;
+  int o0 = kc + 16 * g, o1 = kc + 64 + 16 * g;
+  uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+  if (o0 < limit) a = *reinterpret_cast<const uint4*>(p + o0);
+  if (o1 < limit) b = *reinterpret_cast<const uint4*>(p + o1);
+  f[0] = (int)a.x; f[1] = (int)a.y; f[2] = (int)a.z; f[3] = (int)a.w;
+  f[4] = (int)b.x; f[5] = (int)b.y; f[6] = (int)b.z; f[7] = (int)b.w;
+  return f;
+}
+
+}  // namespace loka

@@ -1,0 +1,519 @@
+// Backward of the fused FP8 GEMM + LayerNorm (loka_gemm_fp8_bwd) on gfx950.
+//
+// Source: LoKA section III-C (Trainer Integration): the FP8 linear is a
+// drop-in for a standard Linear whose own autograd function routes the
+// backward separately, so this is the exact gradient of the forward's
+// definition with rowwise recipes (Table VI's RW recipe); GEM "Mixed
+// Ultra-Low-Precision Training": gradients in the e5m2 range, scale factors
+// along each GEMM's own contraction dimension.
+//
+// Launches (all on the caller's stream):
+//  1. k_bwd_main, one workgroup per 64 rows:
+//       recompute Z = dequant(qX . qW) + b from the forward's codes (MFMA),
+//       LayerNorm backward in fp32 registers (two row reductions),
+//       dZ -> e5m2 row codes in LDS (+ optional dz / codes / scales out),
+//       dgrad MFMA  dX = q(dZ) . q_row(W)^T  -> bf16,
+//       per-workgroup column partials of dgamma, dbeta, dbias and max|dZ|.
+//  2. column amax + cast of X (e4m3, transposed to [K, M]);
+//     cast of dZ (e5m2, transposed to [N, M]) with the maxima from step 1.
+//  3. k_wgrad: split-M FP8 MFMA, fp32 partials per M slice.
+//  4. k_finalize: fixed-order sums of the partials (deterministic), scales.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace loka {
+
+QuantPlan quant_plan(int64_t rows, int64_t cols, int mode);
+hipError_t launch_cast_col_with_partials(const void* src, int src_dtype, int fmt, int64_t rows, int64_t cols,
+                                         int64_t ld, const float* partials, int64_t np, uint8_t* codes_t,
+                                         float* scales, hipStream_t s);
+
+namespace {
+
+constexpr int kMT = 4;           // 64 rows per workgroup
+constexpr int kBM = 16 * kMT;
+constexpr int kWgSplitRows = 1024;  // M rows per wgrad slice
+
+struct BwdBlock {
+  int64_t M;
+  int N, K;
+  const uint16_t* dy;
+  const uint8_t* qx;
+  const float* sx;
+  const float* mean;
+  const float* rstd;
+  const uint8_t* qw;
+  const float* sw;
+  const uint16_t* bias;
+  const uint16_t* gamma;
+  const uint8_t* qw_row;
+  const float* sw_row;
+  uint16_t* dx;
+  float* dz;  // fp32 [M, N] (user buffer or workspace): always written
+  uint8_t* dz_codes;
+  float* dz_scales;
+  float* part;  // [4][nblocks][N]: dgamma, dbeta, dbias, max|dZ|
+  int nblocks;
+};
+
+__device__ __forceinline__ void ld4_bf16(const uint16_t* p, float def, float o[4]) {
+  if (p == nullptr) {
+    o[0] = o[1] = o[2] = o[3] = def;
+    return;
+  }
+  uint2 u = *reinterpret_cast<const uint2*>(p);
+  o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x); o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
+}
+
+// Sum / max over the 16 lanes sharing l / 16 (lanes with the same 4 columns).
+__device__ __forceinline__ float col16_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float col16_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+template <int NTMAX, int KTMAX, int NO_LN>
+__global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int K = p.K, N = p.N;
+  const int ldk = K + 16, ldn = N + 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.x * kBM;
+
+  uint8_t* xs = smem;                                  // qX rows [BM][K+16]
+  uint8_t* ds = xs + (size_t)kBM * ldk;                // dZ codes [BM][N+16]
+  float* red0 = reinterpret_cast<float*>(ds + (size_t)kBM * ldn);
+  float* red1 = red0 + 4 * kBM;
+  float* rsc = red1 + 4 * kBM;                         // dZ row scales [BM]
+
+  const int nt = N / 64;
+  const int nb = wave * nt * 16;
+  v4f acc[NTMAX][kMT];  // holds Z, then dZ
+
+  if (!NO_LN) {
+    // stage the forward's X codes in LDS
+    const int k16 = K / 16;
+    for (int u = tid; u < kBM * k16; u += 256) {
+      const int lr = u / k16, c = (u - lr * k16) * 16;
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (m0 + lr < p.M) v = *reinterpret_cast<const uint4*>(p.qx + (m0 + lr) * K + c);
+      *reinterpret_cast<uint4*>(xs + lr * ldk + c) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NTMAX; ++t)
+#pragma unroll
+      for (int i = 0; i < kMT; ++i) acc[t][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int kc = 0; kc < K; kc += 128) {
+      v8i xf[kMT];
+#pragma unroll
+      for (int i = 0; i < kMT; ++i) xf[i] = load_frag(xs + (16 * i + r) * ldk, g, kc, K);
+#pragma unroll
+      for (int t = 0; t < NTMAX; ++t) {
+        if (t < nt) {
+          const v8i wf = load_frag(p.qw + (int64_t)(nb + 16 * t + r) * K, g, kc, K);
+#pragma unroll
+          for (int i = 0; i < kMT; ++i) acc[t][i] = mfma_fp8<0, 0>(wf, xf[i], acc[t][i]);
+        }
+      }
+    }
+  }
+
+  // per-row constants of this lane's rows m = m0 + 16 i + r
+  float mu[kMT], rs[kMT], sxv[kMT];
+  bool rowok[kMT];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) {
+    const int64_t m = m0 + 16 * i + r;
+    rowok[i] = m < p.M;
+    mu[i] = (!NO_LN && rowok[i]) ? p.mean[m] : 0.0f;
+    rs[i] = (!NO_LN && rowok[i]) ? p.rstd[m] : 0.0f;
+    sxv[i] = (!NO_LN && rowok[i]) ? p.sx[m] : 0.0f;
+  }
+
+  // g = dY * gamma, yhat; row sums of g and g * yhat.  acc <- yhat, dyg[] <- g
+  // (the dY values are re-read below; they stay in L1/L2)
+  float s1[kMT], s2[kMT];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) s1[i] = s2[i] = 0.0f;
+  float colg[NTMAX][4], colb[NTMAX][4];  // dgamma, dbeta partials (over this lane's rows)
+#pragma unroll
+  for (int t = 0; t < NTMAX; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) colg[t][j] = colb[t][j] = 0.0f;
+
+#pragma unroll
+  for (int t = 0; t < NTMAX; ++t) {
+    if (t < nt) {
+      const int n0 = nb + 16 * t + 4 * g;
+      float swv[4], bv[4], gm[4];
+      if (!NO_LN) {
+        float4 s4 = *reinterpret_cast<const float4*>(p.sw + n0);
+        swv[0] = s4.x; swv[1] = s4.y; swv[2] = s4.z; swv[3] = s4.w;
+        ld4_bf16(p.bias ? p.bias + n0 : nullptr, 0.0f, bv);
+        ld4_bf16(p.gamma ? p.gamma + n0 : nullptr, 1.0f, gm);
+      }
+#pragma unroll
+      for (int i = 0; i < kMT; ++i) {
+        const int64_t m = m0 + 16 * i + r;
+        float dyv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (rowok[i]) ld4_bf16(p.dy + m * N + n0, 0.0f, dyv);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (NO_LN) {
+            acc[t][i][j] = dyv[j];  // dZ = dY
+          } else {
+            const float z = acc[t][i][j] * sxv[i] * swv[j] + bv[j];
+            const float yh = (z - mu[i]) * rs[i];
+            const float gg = dyv[j] * gm[j];
+            acc[t][i][j] = yh;
+            s1[i] += gg;
+            s2[i] += gg * yh;
+            colg[t][j] += dyv[j] * yh;
+            colb[t][j] += dyv[j];
+          }
+        }
+      }
+    }
+  }
+
+  if (!NO_LN) {
+#pragma unroll
+    for (int i = 0; i < kMT; ++i) {
+      s1[i] = group4_sum(s1[i]);
+      s2[i] = group4_sum(s2[i]);
+      if (g == 0) {
+        red0[wave * kBM + 16 * i + r] = s1[i];
+        red1[wave * kBM + 16 * i + r] = s2[i];
+      }
+    }
+    __syncthreads();
+    const float invn = 1.0f / (float)N;
+#pragma unroll
+    for (int i = 0; i < kMT; ++i) {
+      const int rr = 16 * i + r;
+      s1[i] = (red0[rr] + red0[kBM + rr] + red0[2 * kBM + rr] + red0[3 * kBM + rr]) * invn;  // mean g
+      s2[i] = (red1[rr] + red1[kBM + rr] + red1[2 * kBM + rr] + red1[3 * kBM + rr]) * invn;  // mean g*yhat
+    }
+    // dZ = rstd * (g - mean g - yhat * mean(g yhat))
+#pragma unroll
+    for (int t = 0; t < NTMAX; ++t) {
+      if (t < nt) {
+        const int n0 = nb + 16 * t + 4 * g;
+        float gm[4];
+        ld4_bf16(p.gamma ? p.gamma + n0 : nullptr, 1.0f, gm);
+#pragma unroll
+        for (int i = 0; i < kMT; ++i) {
+          const int64_t m = m0 + 16 * i + r;
+          float dyv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+          if (rowok[i]) ld4_bf16(p.dy + m * N + n0, 0.0f, dyv);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float gg = dyv[j] * gm[j];
+            acc[t][i][j] = rowok[i] ? rs[i] * (gg - s1[i] - acc[t][i][j] * s2[i]) : 0.0f;
+          }
+        }
+      }
+    }
+  }
+
+  // row amax of dZ -> e5m2 scales; column partials; dZ out; codes -> LDS
+  float am[kMT];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) am[i] = 0.0f;
+#pragma unroll
+  for (int t = 0; t < NTMAX; ++t)
+    if (t < nt)
+#pragma unroll
+      for (int i = 0; i < kMT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) am[i] = fmaxf(am[i], fabsf(acc[t][i][j]));
+  __syncthreads();  // red0/red1 reads above are complete before reuse
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) {
+    am[i] = fmaxf(am[i], __shfl_xor(am[i], 16, 64));
+    am[i] = fmaxf(am[i], __shfl_xor(am[i], 32, 64));
+    if (g == 0) red0[wave * kBM + 16 * i + r] = am[i];
+  }
+  __syncthreads();
+  float rq[kMT];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) {
+    const int rr = 16 * i + r;
+    const float a = fmaxf(fmaxf(red0[rr], red0[kBM + rr]), fmaxf(red0[2 * kBM + rr], red0[3 * kBM + rr]));
+    ScalePair sp = scales_from_amax<1>(a);
+    rq[i] = sp.r;
+    if (wave == 0 && g == 0) {
+      rsc[rr] = sp.s;
+      if (p.dz_scales && rowok[i]) p.dz_scales[m0 + rr] = sp.s;
+    }
+  }
+
+  const int nblk = blockIdx.x;
+#pragma unroll
+  for (int t = 0; t < NTMAX; ++t) {
+    if (t < nt) {
+      const int n0 = nb + 16 * t + 4 * g;
+      float cdb[4] = {0.0f, 0.0f, 0.0f, 0.0f}, cmx[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int i = 0; i < kMT; ++i) {
+        const int lr = 16 * i + r;
+        const int64_t m = m0 + lr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          cdb[j] += acc[t][i][j];
+          cmx[j] = fmaxf(cmx[j], fabsf(acc[t][i][j]));
+        }
+        const uint32_t q = cvt4<1>(acc[t][i][0] * rq[i], acc[t][i][1] * rq[i], acc[t][i][2] * rq[i],
+                                   acc[t][i][3] * rq[i]);
+        *reinterpret_cast<uint32_t*>(ds + lr * ldn + n0) = q;
+        if (rowok[i]) {
+          *reinterpret_cast<float4*>(p.dz + m * N + n0) =
+              make_float4(acc[t][i][0], acc[t][i][1], acc[t][i][2], acc[t][i][3]);
+          if (p.dz_codes) *reinterpret_cast<uint32_t*>(p.dz_codes + m * N + n0) = q;
+        }
+      }
+      // reduce over the 16 lanes (rows) sharing these 4 columns
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float a = col16_sum(colg[t][j]);
+        const float b = col16_sum(colb[t][j]);
+        const float c = col16_sum(cdb[j]);
+        const float d = col16_max(cmx[j]);
+        if (r == 0) {
+          const size_t o = (size_t)nblk * N + n0 + j;
+          const size_t plane = (size_t)p.nblocks * N;
+          p.part[o] = a;
+          p.part[plane + o] = b;
+          p.part[2 * plane + o] = c;
+          p.part[3 * plane + o] = d;
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // dgrad: D[k][m] = sum_n Wr[k][n] dZq[m][n];  wave w owns k columns [w K/4, (w+1) K/4)
+  const int kt = K / 64;
+  const int kb0 = wave * kt * 16;
+  v4f dacc[KTMAX][kMT];
+#pragma unroll
+  for (int t = 0; t < KTMAX; ++t)
+#pragma unroll
+    for (int i = 0; i < kMT; ++i) dacc[t][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int nc = 0; nc < N; nc += 128) {
+    v8i df[kMT];
+#pragma unroll
+    for (int i = 0; i < kMT; ++i) df[i] = load_frag(ds + (16 * i + r) * ldn, g, nc, N);
+#pragma unroll
+    for (int t = 0; t < KTMAX; ++t) {
+      if (t < kt) {
+        const v8i wf = load_frag(p.qw_row + (int64_t)(kb0 + 16 * t + r) * N, g, nc, N);
+#pragma unroll
+        for (int i = 0; i < kMT; ++i) dacc[t][i] = mfma_fp8<0, 1>(wf, df[i], dacc[t][i]);
+      }
+    }
+  }
+  float dsv[kMT];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) dsv[i] = rsc[16 * i + r];
+#pragma unroll
+  for (int t = 0; t < KTMAX; ++t) {
+    if (t < kt) {
+      const int k0 = kb0 + 16 * t + 4 * g;
+      const float4 s4 = *reinterpret_cast<const float4*>(p.sw_row + k0);
+      const float swr[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+      for (int i = 0; i < kMT; ++i) {
+        const int64_t m = m0 + 16 * i + r;
+        if (m < p.M) {
+          float o[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) o[j] = dacc[t][i][j] * dsv[i] * swr[j];
+          *reinterpret_cast<uint2*>(p.dx + m * K + k0) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+        }
+      }
+    }
+  }
+}
+
+// wgrad partials: part[s][k][n] = sum over m in slice s of Xc^T[k][m] * dZc^T[n][m]
+// (codes only).  Workgroup tile 128 (n) x 128 (k); wavefront (wn, wk) in 2 x 2
+// owns 64 x 64 = 4 x 4 MFMA tiles.  A = dZc^T rows n (e5m2), B = Xc^T rows k
+// (e4m3), so lane (r, g) holds D[n = 16a + 4g + j][k = 16b + r].
+__global__ __launch_bounds__(256) void k_wgrad(const uint8_t* dzt, const uint8_t* xt, int64_t M, int N, int K,
+                                               int64_t rows_per_split, float* part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  const int n0 = blockIdx.x * 128 + (wave & 1) * 64;
+  const int k0 = blockIdx.y * 128 + (wave >> 1) * 64;
+  const int64_t ms = (int64_t)blockIdx.z * rows_per_split;
+  int64_t me = ms + rows_per_split;
+  if (me > M) me = M;
+  v4f acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  const bool nin = n0 < N, kin = k0 < K;
+  if (nin && kin) {
+    const int lim = (int)(me - ms);
+    for (int mc = 0; mc < lim; mc += 128) {
+      v8i af[4], bf[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) af[a] = load_frag(dzt + (int64_t)(n0 + 16 * a + r) * M + ms, g, mc, lim);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bf[b] = load_frag(xt + (int64_t)(k0 + 16 * b + r) * M + ms, g, mc, lim);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = mfma_fp8<1, 0>(af[a], bf[b], acc[a][b]);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int n = n0 + 16 * a + 4 * g, k = k0 + 16 * b + r;
+        *reinterpret_cast<float4*>(part + ((int64_t)blockIdx.z * K + k) * N + n) =
+            make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+      }
+  }
+}
+
+// dW[k][n] = (sum_s part[s][k][n]) * sxc[k] * sdzc[n]; column vectors from the
+// per-workgroup partials.  Fixed summation order => deterministic.
+__global__ __launch_bounds__(256) void k_finalize(const float* wpart, int nsplit, const float* sxc, const float* sdzc,
+                                                  int K, int N, float* dw, const float* cpart, int nblocks,
+                                                  float* dgamma, float* dbeta, float* dbias) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t kn = (int64_t)K * N;
+  if (i < kn) {
+    float s = 0.0f;
+    for (int sp = 0; sp < nsplit; ++sp) s += wpart[(int64_t)sp * kn + i];
+    const int k = (int)(i / N), n = (int)(i - (int64_t)k * N);
+    dw[i] = s * sxc[k] * sdzc[n];
+  } else if (i < kn + N) {
+    const int n = (int)(i - kn);
+    const size_t plane = (size_t)nblocks * N;
+    float a = 0.0f, b = 0.0f, c = 0.0f;
+    for (int bl = 0; bl < nblocks; ++bl) {
+      a += cpart[(size_t)bl * N + n];
+      b += cpart[plane + (size_t)bl * N + n];
+      c += cpart[2 * plane + (size_t)bl * N + n];
+    }
+    if (dgamma) dgamma[n] = a;
+    if (dbeta) dbeta[n] = b;
+    if (dbias) dbias[n] = c;
+  }
+}
+
+size_t bwd_lds_bytes(int K, int N) {
+  return (size_t)kBM * (K + 16) + (size_t)kBM * (N + 16) + (size_t)(2 * 4 * kBM + kBM) * 4;
+}
+
+struct BwdWs {
+  size_t part, dz, xt, sxc, xcolp, dzt, sdzc, wpart, total;
+  int nblocks, nsplit;
+  int64_t xnp;
+};
+BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K) {
+  BwdWs w{};
+  auto al = [](size_t b) { return (b + 255) / 256 * 256; };
+  w.nblocks = (int)((M + kBM - 1) / kBM);
+  w.nsplit = (int)((M + kWgSplitRows - 1) / kWgSplitRows);
+  if (w.nsplit < 1) w.nsplit = 1;
+  QuantPlan xq = quant_plan(M, K, 2);
+  w.xnp = xq.np;
+  size_t o = 0;
+  w.part = o; o += al((size_t)4 * w.nblocks * N * 4);
+  w.dz = o; o += al((size_t)M * N * 4);
+  w.xt = o; o += al((size_t)M * K);
+  w.sxc = o; o += al((size_t)K * 4);
+  w.xcolp = o; o += al((size_t)xq.ws_floats * 4);
+  w.dzt = o; o += al((size_t)M * N);
+  w.sdzc = o; o += al((size_t)N * 4);
+  w.wpart = o; o += al((size_t)w.nsplit * K * N * 4);
+  w.total = o;
+  return w;
+}
+
+template <int NTMAX, int KTMAX>
+hipError_t launch_main_t(const BwdBlock& p, int no_ln, hipStream_t s) {
+  const size_t lds = bwd_lds_bytes(p.K, p.N);
+  const dim3 grid((unsigned)p.nblocks);
+  if (no_ln) {
+    auto kern = k_bwd_main<NTMAX, KTMAX, 1>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, p);
+  } else {
+    auto kern = k_bwd_main<NTMAX, KTMAX, 0>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int64_t M, int64_t N, int64_t K) { return bwd_ws_layout(M, N, K).total; }
+
+hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
+  if (a.M == 0) return hipSuccess;
+  const BwdWs w = bwd_ws_layout(a.M, a.N, a.K);
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  BwdBlock p;
+  p.M = a.M; p.N = (int)a.N; p.K = (int)a.K;
+  p.dy = static_cast<const uint16_t*>(a.dy);
+  p.qx = a.qx; p.sx = a.sx; p.mean = a.mean; p.rstd = a.rstd;
+  p.qw = a.qw; p.sw = a.sw;
+  p.bias = static_cast<const uint16_t*>(a.bias);
+  p.gamma = static_cast<const uint16_t*>(a.gamma);
+  p.qw_row = a.qw_row; p.sw_row = a.sw_row;
+  p.dx = static_cast<uint16_t*>(a.dx);
+  p.dz = a.dz ? a.dz : reinterpret_cast<float*>(ws + w.dz);
+  p.dz_codes = a.dz_codes; p.dz_scales = a.dz_scales;
+  p.part = reinterpret_cast<float*>(ws + w.part);
+  p.nblocks = w.nblocks;
+
+  hipError_t e;
+  const int nt = (int)a.N / 64, kt = (int)a.K / 64;
+  if (nt <= 8 && kt <= 8) e = launch_main_t<8, 8>(p, a.no_ln, s);
+  else if (nt <= 8) e = launch_main_t<8, 16>(p, a.no_ln, s);
+  else if (kt <= 8) e = launch_main_t<16, 8>(p, a.no_ln, s);
+  else e = launch_main_t<16, 16>(p, a.no_ln, s);
+  if (e != hipSuccess) return e;
+
+  // column quantization of X (e4m3) and dZ (e5m2), both transposed to [*, M]
+  uint8_t* xt = ws + w.xt;
+  float* sxc = reinterpret_cast<float*>(ws + w.sxc);
+  uint8_t* dzt = ws + w.dzt;
+  float* sdzc = reinterpret_cast<float*>(ws + w.sdzc);
+  QuantLaunch xq{};
+  xq.src = a.x; xq.rows = a.M; xq.cols = a.K; xq.ld = a.K; xq.src_dtype = 0; xq.fmt = 0; xq.mode = 2;
+  xq.transpose_out = 1; xq.codes = xt; xq.scales = sxc; xq.amax_out = nullptr; xq.workspace = ws + w.xcolp;
+  e = launch_quant(xq, s);
+  if (e != hipSuccess) return e;
+  const float* dzmax = p.part + (size_t)3 * w.nblocks * a.N;
+  e = launch_cast_col_with_partials(p.dz, 1, 1, a.M, a.N, a.N, dzmax, w.nblocks, dzt, sdzc, s);
+  if (e != hipSuccess) return e;
+
+  float* wpart = reinterpret_cast<float*>(ws + w.wpart);
+  dim3 g((unsigned)((a.N + 127) / 128), (unsigned)((a.K + 127) / 128), (unsigned)w.nsplit);
+  hipLaunchKernelGGL(k_wgrad, g, dim3(256), 0, s, dzt, xt, a.M, (int)a.N, (int)a.K, (int64_t)kWgSplitRows, wpart);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t tot = a.K * a.N + a.N;
+  hipLaunchKernelGGL(k_finalize, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, wpart, w.nsplit, sxc, sdzc,
+                     (int)a.K, (int)a.N, a.dw, p.part, w.nblocks, a.dgamma, a.dbeta, a.dbias);
+  return hipGetLastError();
+}
+
+}  // namespace loka

@@ -1,0 +1,103 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Arguments arrive here already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace loka {
+
+// ---- quantization --------------------------------------------------------
+struct QuantLaunch {
+  const void* src;
+  int64_t rows, cols, ld;
+  int src_dtype;  // 0 bf16, 1 fp32
+  int fmt;        // 0 e4m3, 1 e5m2
+  int mode;       // loka_scaling
+  int transpose_out;
+  uint8_t* codes;
+  void* scales;
+  float* amax_out;
+  void* workspace;
+};
+struct QuantPlan {
+  int64_t np = 0;         // number of partial maxima (tensor/col) or rows (row)
+  int64_t rpc = 0;        // rows per chunk (col)
+  int64_t ws_floats = 0;  // workspace floats
+};
+QuantPlan quant_plan(int64_t rows, int64_t cols, int mode);
+hipError_t launch_quant(const QuantLaunch& a, hipStream_t s);
+
+// ---- forward -------------------------------------------------------------
+struct FwdLaunch {
+  int64_t M, N, K;
+  int x_mode;  // 0 tensor, 1 row, 3 mx32
+  float eps;
+  const void* x;
+  const uint8_t* qw;
+  const void* sw;
+  const void* bias;
+  const void* gamma;
+  const void* beta;
+  void* y;
+  float* z;
+  float* mean;
+  float* rstd;
+  uint8_t* qx_out;
+  void* sx_out;
+  void* workspace;
+};
+size_t fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int x_mode);
+hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s);
+
+// ---- backward ------------------------------------------------------------
+struct BwdLaunch {
+  int64_t M, N, K;
+  int no_ln;
+  const void* dy;
+  const uint8_t* qx;
+  const float* sx;
+  const float* mean;
+  const float* rstd;
+  const uint8_t* qw;
+  const float* sw;
+  const void* bias;
+  const void* gamma;
+  const void* x;
+  const uint8_t* qw_row;
+  const float* sw_row;
+  void* dx;
+  float* dw;
+  float* dgamma;
+  float* dbeta;
+  float* dbias;
+  float* dz;
+  uint8_t* dz_codes;
+  float* dz_scales;
+  void* workspace;
+};
+size_t bwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
+hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s);
+
+// ---- grouped -------------------------------------------------------------
+struct GroupDev {  // one group as the device sees it (copied into the workspace)
+  int64_t M, N, K;
+  const void* x;
+  const uint8_t* qw;
+  const float* sw;
+  const void* bias;
+  const void* gamma;
+  const void* beta;
+  void* y;
+  float* z;
+};
+struct GroupedLaunch {
+  int num_groups;
+  float eps;
+  const GroupDev* groups;  // host array
+  void* workspace;         // device
+};
+size_t grouped_workspace_bytes(int num_groups, const GroupDev* groups);
+hipError_t launch_grouped(const GroupedLaunch& a, hipStream_t s);
+
+}  // namespace loka

@@ -1,0 +1,369 @@
+// Standalone amax -> scale -> saturating RNE cast (loka_quant_fp8) on gfx950.
+//
+// Source: LoKA section II-C (quantization is a first-order cost of an FP8
+// linear) and section III-C (tensorwise / rowwise / blockwise recipes); GEM
+// "Low Precision Flash Attention" (MX block scales along K, E8M0 from a
+// max-abs reduction by bit manipulation) and "Mixed Ultra-Low-Precision
+// Training" (weights quantized once, separately from the activations).
+//
+// Pass 1 (amax):  tensor -> per-block partial maxima; row -> one wavefront
+//                 per row; column -> per row-chunk partial maxima.
+// Pass 2 (cast):  64 x 64 tiles, 256 threads, each thread 16 consecutive
+//                 elements of one row; the group multipliers come from pass 1
+//                 (MX blocks are reduced inside the tile).  Transposed output
+//                 goes through LDS so both the loads and the stores are
+//                 coalesced.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace loka {
+namespace {
+
+constexpr int kTile = 64;
+
+template <int DT>
+__device__ __forceinline__ void load16(const void* base, int64_t off, bool ok, float v[16]) {
+  if (!ok) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    return;
+  }
+  if (DT == 0) {
+    const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    uint4 a = p[0], b = p[1];
+    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float4 f = p[i];
+      v[4 * i] = f.x; v[4 * i + 1] = f.y; v[4 * i + 2] = f.z; v[4 * i + 3] = f.w;
+    }
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, int64_t off, float v[8]) {
+  if (DT == 0) {
+    uint4 a = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+    uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(w[i]);
+      v[2 * i + 1] = bf16_hi(w[i]);
+    }
+  } else {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+}
+
+// ---- pass 1 ---------------------------------------------------------------
+
+// Partial max |x| of the whole array: block b covers 8-element units
+// b, b + gridDim.x, ... (unit u = row u / c8, columns 8 * (u % c8) ...).
+template <int DT>
+__global__ __launch_bounds__(256) void k_amax_tensor(const void* src, int64_t rows, int64_t cols, int64_t ld,
+                                                     float* partials) {
+  __shared__ float red[4];
+  const int64_t c8 = cols / 8;
+  const int64_t units = rows * c8;
+  float m = 0.0f;
+  for (int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x; u < units; u += (int64_t)gridDim.x * 256) {
+    int64_t r = u / c8, c = (u - r * c8) * 8;
+    float v[8];
+    load8<DT>(src, r * ld + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partials[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// One wavefront per row: amax[r] = max_c |x[r, c]|.
+template <int DT>
+__global__ __launch_bounds__(256) void k_amax_row(const void* src, int64_t rows, int64_t cols, int64_t ld,
+                                                  float* amax) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  float m = 0.0f;
+  for (int64_t c = (int64_t)lane * 8; c < cols; c += 512) {
+    float v[8];
+    load8<DT>(src, r * ld + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+  }
+  m = wave_max(m);
+  if (lane == 0) amax[r] = m;
+}
+
+// partials[chunk][c] = max over rows [chunk * rpc, (chunk + 1) * rpc) of |x[r, c]|.
+// Block: 64 threads x 8 columns = 512 columns; grid (ceil(cols/512), nchunks).
+template <int DT>
+__global__ __launch_bounds__(64) void k_amax_col(const void* src, int64_t rows, int64_t cols, int64_t ld,
+                                                 int64_t rpc, float* partials) {
+  const int64_t c = ((int64_t)blockIdx.x * 64 + threadIdx.x) * 8;
+  if (c >= cols) return;
+  const int64_t r0 = (int64_t)blockIdx.y * rpc;
+  const int64_t r1 = r0 + rpc < rows ? r0 + rpc : rows;
+  float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int64_t r = r0; r < r1; ++r) {
+    float v[8];
+    load8<DT>(src, r * ld + c, v);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
+  }
+  float4* out = reinterpret_cast<float4*>(partials + (int64_t)blockIdx.y * cols + c);
+  out[0] = make_float4(m[0], m[1], m[2], m[3]);
+  out[1] = make_float4(m[4], m[5], m[6], m[7]);
+}
+
+// ---- pass 2 ---------------------------------------------------------------
+
+struct CastParams {
+  const void* src;
+  int64_t rows, cols, ld;
+  uint8_t* codes;
+  void* scales;
+  float* amax_out;
+  const float* amax_in;  // tensor: partials[np]; row: amax[rows]; col: partials[np][cols]
+  int64_t np;
+};
+
+// Tile (blockIdx.y, blockIdx.x) covers rows [64 by, +64), cols [64 bx, +64).
+// Thread t: tile row t / 4, tile columns 16 (t % 4) .. +16.
+template <int DT, int FMT, int MODE, int TRANS>
+__global__ __launch_bounds__(256) void k_cast_tile(CastParams p) {
+  __shared__ float r_col[kTile];             // COL: multiplier per tile column
+  __shared__ float red[4];
+  __shared__ float colmax[kTile][kTile + 1];  // MX32_COL: |x| staging
+  __shared__ int e8_col[2][kTile];            // MX32_COL: E8M0 per (row block, column)
+  __shared__ uint8_t tcodes[kTile][kTile + 4];  // transposed output staging
+
+  const int t = threadIdx.x;
+  const int tr = t >> 2, tc = (t & 3) * 16;
+  const int64_t row = (int64_t)blockIdx.y * kTile + tr;
+  const int64_t col0 = (int64_t)blockIdx.x * kTile + tc;
+  const bool ok = row < p.rows && col0 < p.cols;
+
+  float v[16];
+  load16<DT>(p.src, row * p.ld + col0, ok, v);
+
+  float mult[16];
+  if (MODE == 0) {  // tensor: reduce the partial maxima
+    float m = 0.0f;
+    for (int64_t i = t; i < p.np; i += 256) m = fmaxf(m, p.amax_in[i]);
+    m = wave_max(m);
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    ScalePair sp = scales_from_amax<FMT>(m);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
+      static_cast<float*>(p.scales)[0] = sp.s;
+      if (p.amax_out) p.amax_out[0] = m;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mult[i] = sp.r;
+  } else if (MODE == 1) {  // row
+    float a = row < p.rows ? p.amax_in[row] : 0.0f;
+    ScalePair sp = scales_from_amax<FMT>(a);
+    if (blockIdx.x == 0 && (t & 3) == 0 && row < p.rows) {
+      static_cast<float*>(p.scales)[row] = sp.s;
+      if (p.amax_out) p.amax_out[row] = a;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mult[i] = sp.r;
+  } else if (MODE == 2) {  // column: reduce partials per tile column
+    if (t < kTile) {
+      int64_t c = (int64_t)blockIdx.x * kTile + t;
+      float m = 0.0f;
+      if (c < p.cols)
+        for (int64_t k = 0; k < p.np; ++k) m = fmaxf(m, p.amax_in[k * p.cols + c]);
+      ScalePair sp = scales_from_amax<FMT>(m);
+      r_col[t] = sp.r;
+      if (blockIdx.y == 0 && c < p.cols) {
+        static_cast<float*>(p.scales)[c] = sp.s;
+        if (p.amax_out) p.amax_out[c] = m;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mult[i] = r_col[tc + i];
+  } else if (MODE == 3) {  // MX32 along rows: this thread's 16 columns are half a block
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));  // partner thread holds the other half
+    int e8 = e8m0_from_amax<FMT>(m);
+    float mu = e8m0_inv_multiplier(e8);
+    if ((t & 1) == 0 && ok) {
+      int64_t nb = p.cols / 32;
+      static_cast<uint8_t*>(p.scales)[row * nb + col0 / 32] = (uint8_t)e8;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mult[i] = mu;
+  } else {  // MX32 down columns: 32-row blocks of each column, via LDS
+#pragma unroll
+    for (int i = 0; i < 16; ++i) colmax[tr][tc + i] = fabsf(v[i]);
+    __syncthreads();
+    if (t < 2 * kTile) {
+      int c = t & (kTile - 1), b = t >> 6;
+      float m = 0.0f;
+      for (int i = 0; i < 32; ++i) m = fmaxf(m, colmax[32 * b + i][c]);
+      int e8 = e8m0_from_amax<FMT>(m);
+      e8_col[b][c] = e8;
+      int64_t gc = (int64_t)blockIdx.x * kTile + c;
+      int64_t grb = (int64_t)blockIdx.y * 2 + b;  // global row block
+      if (gc < p.cols && grb * 32 < p.rows) static_cast<uint8_t*>(p.scales)[gc * (p.rows / 32) + grb] = (uint8_t)e8;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mult[i] = e8m0_inv_multiplier(e8_col[tr >> 5][tc + i]);
+  }
+
+  uint32_t w[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    w[q] = cvt4<FMT>(v[4 * q] * mult[4 * q], v[4 * q + 1] * mult[4 * q + 1], v[4 * q + 2] * mult[4 * q + 2],
+                     v[4 * q + 3] * mult[4 * q + 3]);
+
+  if (!TRANS) {
+    if (ok) *reinterpret_cast<uint4*>(p.codes + row * p.cols + col0) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) tcodes[tr][tc + 4 * q + b] = (uint8_t)(w[q] >> (8 * b));
+    __syncthreads();
+    // thread t: tile column t / 4, tile rows 16 (t % 4) .. +16
+    const int oc = t >> 2, orow = (t & 3) * 16;
+    const int64_t gc = (int64_t)blockIdx.x * kTile + oc;
+    const int64_t gr = (int64_t)blockIdx.y * kTile + orow;
+    if (gc < p.cols && gr < p.rows) {
+      uint32_t o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        o[q] = (uint32_t)tcodes[orow + 4 * q][oc] | ((uint32_t)tcodes[orow + 4 * q + 1][oc] << 8) |
+               ((uint32_t)tcodes[orow + 4 * q + 2][oc] << 16) | ((uint32_t)tcodes[orow + 4 * q + 3][oc] << 24);
+      *reinterpret_cast<uint4*>(p.codes + gc * p.rows + gr) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+template <int DT, int FMT, int MODE>
+void launch_cast(const CastParams& cp, int trans, hipStream_t s) {
+  dim3 grid((unsigned)((cp.cols + kTile - 1) / kTile), (unsigned)((cp.rows + kTile - 1) / kTile));
+  if (trans)
+    hipLaunchKernelGGL((k_cast_tile<DT, FMT, MODE, 1>), grid, dim3(256), 0, s, cp);
+  else
+    hipLaunchKernelGGL((k_cast_tile<DT, FMT, MODE, 0>), grid, dim3(256), 0, s, cp);
+}
+
+template <int DT, int FMT>
+void dispatch_cast(const CastParams& cp, int mode, int trans, hipStream_t s) {
+  switch (mode) {
+    case 0: launch_cast<DT, FMT, 0>(cp, trans, s); break;
+    case 1: launch_cast<DT, FMT, 1>(cp, trans, s); break;
+    case 2: launch_cast<DT, FMT, 2>(cp, trans, s); break;
+    case 3: launch_cast<DT, FMT, 3>(cp, trans, s); break;
+    default: launch_cast<DT, FMT, 4>(cp, trans, s); break;
+  }
+}
+
+}  // namespace
+
+QuantPlan quant_plan(int64_t rows, int64_t cols, int mode) {
+  QuantPlan q{};
+  if (mode == 0) {
+    int64_t units = rows * (cols / 8);
+    int64_t nb = (units + 256 * 16 - 1) / (256 * 16);
+    q.np = nb < 1 ? 1 : (nb > 1024 ? 1024 : nb);
+    q.ws_floats = q.np;
+  } else if (mode == 1) {
+    q.np = rows;
+    q.ws_floats = rows;
+  } else if (mode == 2) {
+    int64_t rpc = 64;
+    int64_t nch = (rows + rpc - 1) / rpc;
+    if (nch > 256) {  // keep the per-column reduction in pass 2 short
+      nch = 256;
+      rpc = (rows + nch - 1) / nch;
+      nch = (rows + rpc - 1) / rpc;
+    }
+    if (nch < 1) nch = 1;
+    q.np = nch;
+    q.rpc = rpc;
+    q.ws_floats = nch * cols;
+  }
+  return q;
+}
+
+hipError_t launch_quant(const QuantLaunch& a, hipStream_t s) {
+  if (a.rows == 0 || a.cols == 0) return hipSuccess;
+  QuantPlan q = quant_plan(a.rows, a.cols, a.mode);
+  float* ws = static_cast<float*>(a.workspace);
+  CastParams cp{a.src, a.rows, a.cols, a.ld, a.codes, a.scales, a.amax_out, ws, q.np};
+  const bool f32 = a.src_dtype == 1;
+  if (a.mode == 0) {
+    if (f32) hipLaunchKernelGGL(k_amax_tensor<1>, dim3((unsigned)q.np), dim3(256), 0, s, a.src, a.rows, a.cols, a.ld, ws);
+    else hipLaunchKernelGGL(k_amax_tensor<0>, dim3((unsigned)q.np), dim3(256), 0, s, a.src, a.rows, a.cols, a.ld, ws);
+  } else if (a.mode == 1) {
+    dim3 g((unsigned)((a.rows + 3) / 4));
+    if (f32) hipLaunchKernelGGL(k_amax_row<1>, g, dim3(256), 0, s, a.src, a.rows, a.cols, a.ld, ws);
+    else hipLaunchKernelGGL(k_amax_row<0>, g, dim3(256), 0, s, a.src, a.rows, a.cols, a.ld, ws);
+  } else if (a.mode == 2) {
+    dim3 g((unsigned)((a.cols + 511) / 512), (unsigned)q.np);
+    if (f32) hipLaunchKernelGGL(k_amax_col<1>, g, dim3(64), 0, s, a.src, a.rows, a.cols, a.ld, q.rpc, ws);
+    else hipLaunchKernelGGL(k_amax_col<0>, g, dim3(64), 0, s, a.src, a.rows, a.cols, a.ld, q.rpc, ws);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (f32) {
+    if (a.fmt == 0) dispatch_cast<1, 0>(cp, a.mode, a.transpose_out, s);
+    else dispatch_cast<1, 1>(cp, a.mode, a.transpose_out, s);
+  } else {
+    if (a.fmt == 0) dispatch_cast<0, 0>(cp, a.mode, a.transpose_out, s);
+    else dispatch_cast<0, 1>(cp, a.mode, a.transpose_out, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace loka
+
+namespace loka {
+
+// Tensor-mode amax partials of a bf16 array (used by the tensor-recipe forward).
+hipError_t launch_amax_tensor_partials(const void* src, int64_t rows, int64_t cols, int64_t ld, float* partials,
+                                       hipStream_t s) {
+  QuantPlan q = quant_plan(rows, cols, 0);
+  hipLaunchKernelGGL(k_amax_tensor<0>, dim3((unsigned)q.np), dim3(256), 0, s, src, rows, cols, ld, partials);
+  return hipGetLastError();
+}
+
+// Column cast with precomputed partial column maxima (np x cols), used by the
+// backward for dZ whose column maxima come out of the fused LN-backward kernel.
+hipError_t launch_cast_col_with_partials(const void* src, int src_dtype, int fmt, int64_t rows, int64_t cols,
+                                         int64_t ld, const float* partials, int64_t np, uint8_t* codes_t,
+                                         float* scales, hipStream_t s) {
+  CastParams cp{src, rows, cols, ld, codes_t, scales, nullptr, partials, np};
+  if (src_dtype == 1) {
+    if (fmt == 0) launch_cast<1, 0, 2>(cp, 1, s);
+    else launch_cast<1, 1, 2>(cp, 1, s);
+  } else {
+    if (fmt == 0) launch_cast<0, 0, 2>(cp, 1, s);
+    else launch_cast<0, 1, 2>(cp, 1, s);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace loka

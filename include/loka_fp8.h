@@ -1,0 +1,310 @@
+/*
+ * loka_fp8.h -- C ABI of liblokafp8.so: the FP8 "small GEMM followed by
+ * normalization" block on AMD Instinct MI355X (gfx950).
+ *
+ * The block (sources, by page title and section):
+ *   - "LoKA: Low-precision Kernel Applications for Recommendation Models At
+ *     Scale", section I and section III-B: recommendation models are
+ *     dominated by small GEMMs followed immediately by a normalization, and
+ *     the LayerNorm must run in higher precision after dequantization;
+ *     section III-B2 (Block-wise Normalization, Case 1): with a large batch
+ *     and a small output dimension the whole output row fits in one block
+ *     of the GEMM, so the normalization is fused into its epilogue;
+ *     section III-B1 (No Bias): a missing bias is a first-class mode;
+ *     section III-C (Dispatch): the FP8 linear is a drop-in for a standard
+ *     Linear, with tensorwise / rowwise / blockwise recipes and separate
+ *     forward and backward routing; unsupported sites stay in high
+ *     precision.
+ *   - "GEM Training: How Meta Doubled the Efficiency of Its LLM-Scale Ads
+ *     Foundation Model", "Low Precision Flash Attention" and "Mixed
+ *     Ultra-Low-Precision Training": MXFP8 block scales along each GEMM's K
+ *     dimension, E8M0 scales derived by bit manipulation from a max-abs
+ *     reduction; weights quantized once per step, separately from the
+ *     activations.
+ *
+ * Conventions for every entry point:
+ *   - All tensors are row-major and dense unless an `ld` says otherwise.
+ *     bf16 tensors are passed as raw 16-bit patterns (void*).  FP8 codes are
+ *     OCP e4m3 ("e4m3fn", max 448) or e5m2 (max 57344) bytes.
+ *   - Every pointer is a DEVICE pointer except `loka_grouped_args::groups`
+ *     (host array).  The caller allocates and owns every buffer, including
+ *     the workspace; the library never allocates or frees memory and keeps
+ *     no global state, so calls are thread-safe.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream).  Nothing synchronizes the host.
+ *   - Arguments are validated before anything is enqueued.  On any error
+ *     nothing is enqueued and outputs are untouched.  LOKA_ERR_UNSUPPORTED
+ *     marks a shape or mode combination this library does not run (the
+ *     caller's cue to fall back to bf16).  A HIP launch failure returns
+ *     LOKA_ERR_HIP; loka_last_error() then holds the HIP error text
+ *     (thread-local).
+ *   - Base pointers must be 16-byte aligned (LOKA_ERR_ALIGNMENT otherwise).
+ *
+ * Quantization arithmetic (identical in every entry point):
+ *   tensor / row / column scaling: amax = max |x| over the group; the
+ *   stored dequantization scale is s = RN32(amax / FMAX), the multiplier
+ *   r = RN32(FMAX / amax) (saturating at the largest fp32), amax == 0 gives
+ *   s = r = 1; code = satRNE_fp8(RN32(x * r)): round to nearest even, values
+ *   past +-FMAX clamp to the +-FMAX code, -0 encodes as 0x80.
+ *   MX32: one E8M0 scale per 32 consecutive elements,
+ *   e = clamp(floor(log2 amax) - emax_elem, -127, 127) with emax_elem 8
+ *   (e4m3) / 15 (e5m2), stored as e + 127 (amax == 0 -> 0);
+ *   code = satRNE_fp8(x * 2^-e).
+ *   Non-finite inputs are outside the contract (results unspecified).
+ */
+#ifndef LOKA_FP8_H
+#define LOKA_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LOKA_ABI_VERSION 1
+
+typedef enum {
+  LOKA_OK = 0,
+  LOKA_ERR_INVALID_ARG = 1, /* null required pointer, negative size, bad enum */
+  LOKA_ERR_UNSUPPORTED = 2, /* valid request this library does not run      */
+  LOKA_ERR_ALIGNMENT = 3,   /* a base pointer is not 16-byte aligned        */
+  LOKA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required   */
+  LOKA_ERR_HIP = 5          /* a HIP call failed; see loka_last_error()     */
+} loka_status;
+
+typedef enum { LOKA_E4M3 = 0, LOKA_E5M2 = 1 } loka_fp8_fmt;
+
+typedef enum {
+  LOKA_SCALE_TENSOR = 0,  /* one fp32 scale for the whole array                 */
+  LOKA_SCALE_ROW = 1,     /* one fp32 scale per row (amax along the row)        */
+  LOKA_SCALE_COL = 2,     /* one fp32 scale per column (amax down the column)   */
+  LOKA_SCALE_MX32_ROW = 3,/* one E8M0 per 32 consecutive elements along a row   */
+  LOKA_SCALE_MX32_COL = 4 /* one E8M0 per 32 consecutive elements down a column */
+} loka_scaling;
+
+typedef enum { LOKA_DTYPE_BF16 = 0, LOKA_DTYPE_F32 = 1 } loka_dtype;
+
+/* ------------------------------------------------------------------------
+ * loka_quant_fp8: amax -> scale -> saturating RNE cast of a 2-D array.
+ *
+ * Source: LoKA section II-C (quantization overhead is a first-order cost
+ * of the FP8 linear) and section III-C (tensorwise / rowwise / blockwise
+ * recipes); GEM "Low Precision Flash Attention" (MX block scales along K,
+ * E8M0 by bit manipulation) and "Mixed Ultra-Low-Precision Training"
+ * (weights quantized separately from activations).
+ *
+ *   src      [rows, cols] with row stride `ld` elements (ld >= cols),
+ *            bf16 or fp32 (src_dtype).
+ *   codes    transpose_out == 0: [rows, cols] (row stride cols);
+ *            transpose_out == 1: [cols, rows] (row stride rows): the
+ *            codes of src^T, with `rows` contiguous -- the MFMA operand
+ *            layout when `rows` is the caller's contraction dimension (a
+ *            weight W[K, N] for the forward, X or dZ for the wgrad).
+ *   scales   TENSOR: float[1]; ROW: float[rows]; COL: float[cols];
+ *            MX32_ROW: uint8[rows][cols/32]; MX32_COL: uint8[cols][rows/32].
+ *            (The scale layout does not depend on transpose_out.)
+ *   amax     optional float out, same count as the fp32 scales
+ *            (TENSOR/ROW/COL only; must be NULL for MX).
+ *   workspace device scratch of loka_quant_workspace_size() bytes
+ *            (may be NULL when that size is 0).
+ * Requirements: rows, cols >= 0; cols % 16 == 0; MX32_ROW: cols % 32 == 0;
+ * MX32_COL: rows % 32 == 0; transpose_out requires rows % 16 == 0.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t rows, cols, ld;
+  int32_t src_dtype;     /* loka_dtype   */
+  int32_t fmt;           /* loka_fp8_fmt */
+  int32_t mode;          /* loka_scaling */
+  int32_t transpose_out; /* 0 or 1       */
+  const void* src;
+  uint8_t* codes;
+  void* scales;
+  float* amax;
+  void* workspace;
+  size_t workspace_bytes;
+} loka_quant_args;
+
+size_t loka_quant_workspace_size(const loka_quant_args* args);
+loka_status loka_quant_fp8(const loka_quant_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * loka_gemm_fp8_ln: Y = LayerNorm(dequant(q(X) . q(W)) + bias), fused.
+ *
+ * Source: LoKA section III-B2 (normalization fused into the GEMM epilogue
+ * while the output tile is on chip; Case 1, the whole row in one block),
+ * section III-B (dequantize before the LayerNorm, which runs in high
+ * precision), section III-B1 (No Bias); GEM "Mixed Ultra-Low-Precision
+ * Training" (activation quantization fused into the neighbouring kernel
+ * instead of a separate pass).
+ *
+ *   X       bf16 [M, K]; quantized inside the kernel per x_mode, e4m3.
+ *   qw, sw  the weight, quantized beforehand with loka_quant_fp8 on
+ *           W [K, N] with transpose_out = 1 (codes [N, K], e4m3):
+ *             x_mode TENSOR   -> W mode TENSOR,  sw float[1]
+ *             x_mode ROW      -> W mode COL,     sw float[N]
+ *             x_mode MX32_ROW -> W mode MX32_COL, sw uint8[N][K/32]
+ *   bias, gamma, beta  bf16 [N] or NULL (NULL = 0, 1, 0; NULL bias is the
+ *           No-Bias mode).
+ *   Z[m,n]  = acc[m,n] * s_x[m] * s_w[n] + bias[n]   (MX: the E8M0 scales
+ *           multiply each 32-wide K block inside the MFMA), acc the fp32
+ *           FP8 MFMA sum.
+ *   Y       = gamma * (Z - mean_n Z) / sqrt(var_n Z + eps) + beta, bf16 RNE
+ *           (population variance, two-pass, fp32).
+ *   Optional outputs (NULL to skip): z fp32 [M, N]; mean, rstd fp32 [M];
+ *   qx_out e4m3 [M, K] and sx_out (float[1] | float[M] | uint8[M][K/32]):
+ *   the quantized X, bit-identical to loka_quant_fp8's, for the backward.
+ *   workspace: loka_gemm_fp8_ln_workspace_size() bytes (TENSOR needs the
+ *   amax partials; 0 otherwise).
+ * Requirements: M >= 0; N % 64 == 0 and 64 <= N <= 1024 (else
+ * UNSUPPORTED: the row must fit one workgroup); K % 16 == 0 (MX: % 32),
+ * 16 <= K <= 2048.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t M, N, K;
+  int32_t x_mode; /* LOKA_SCALE_TENSOR, LOKA_SCALE_ROW or LOKA_SCALE_MX32_ROW */
+  int32_t flags;  /* reserved, must be 0 */
+  float eps;
+  const void* x;
+  const uint8_t* qw;
+  const void* sw;
+  const void* bias;
+  const void* gamma;
+  const void* beta;
+  void* y;
+  float* z;
+  float* mean;
+  float* rstd;
+  uint8_t* qx_out;
+  void* sx_out;
+  void* workspace;
+  size_t workspace_bytes;
+} loka_fwd_args;
+
+size_t loka_gemm_fp8_ln_workspace_size(const loka_fwd_args* args);
+loka_status loka_gemm_fp8_ln(const loka_fwd_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * loka_gemm_fp8_bwd: the backward of loka_gemm_fp8_ln (x_mode ROW).
+ *
+ * Source: LoKA section III-C (Trainer Integration: a custom autograd
+ * function routes forward and backward separately; rowwise recipes, with
+ * Table VI's RW recipe for the gradients); GEM "Mixed Ultra-Low-Precision
+ * Training" (gradients in the e5m2 range, scales along each GEMM's own
+ * contraction dimension).
+ *
+ * dY is the gradient at Y.  Per row, with yhat = (Z - mean) * rstd and
+ * g = dY * gamma:
+ *   dZ     = rstd * (g - mean_n g - yhat * mean_n(g * yhat))   (fp32)
+ *   dgamma = sum_m dY * yhat,  dbeta = sum_m dY,  dbias = sum_m dZ
+ *   dgrad: dX = dequant(q_row(dZ, e5m2) . q_row(W, e4m3)^T)   bf16 [M, K]
+ *          (W's rows are its k index: scales per k, amax over n)
+ *   wgrad: dW = dequant(q_col(X, e4m3)^T . q_col(dZ, e5m2))   fp32 [K, N]
+ *          (scales per column of X and of dZ, amax over the M rows)
+ * With flags & LOKA_BWD_NO_LN, dY already is dZ (no LayerNorm); mean,
+ * rstd, gamma, qx, sx, qw, sw, bias are then unused and may be NULL, and
+ * dgamma/dbeta must be NULL.
+ *
+ *   ctx from the forward: qx e4m3 [M, K] + sx float[M] (its qx_out/sx_out),
+ *     mean, rstd float[M], qw [N, K] + sw float[N] (its weight), bias and
+ *     gamma bf16 [N] or NULL.  Z is recomputed from qx, qw in the kernel.
+ *   x       bf16 [M, K] (column-quantized here for wgrad).
+ *   qw_row, sw_row: W [K, N] quantized with loka_quant_fp8 mode ROW, e4m3,
+ *     transpose_out 0 (codes [K, N], scales float[K]).
+ *   Outputs: dx bf16 [M, K]; dw fp32 [K, N]; dgamma, dbeta, dbias fp32 [N]
+ *     or NULL; optional dz fp32 [M, N]; optional dz_codes e5m2 [M, N] and
+ *     dz_scales float[M] (the dgrad operand, for parity checks).
+ *   All reductions over M are deterministic (fixed-order two-stage sums).
+ * Requirements: as loka_gemm_fp8_ln with x_mode ROW, plus K % 64 == 0,
+ *   K <= 1024 and M % 16 == 0.
+ * ---------------------------------------------------------------------- */
+#define LOKA_BWD_NO_LN 1
+
+typedef struct {
+  int64_t M, N, K;
+  int32_t flags;
+  int32_t reserved;
+  const void* dy;
+  const uint8_t* qx;
+  const float* sx;
+  const float* mean;
+  const float* rstd;
+  const uint8_t* qw;
+  const float* sw;
+  const void* bias;
+  const void* gamma;
+  const void* x;
+  const uint8_t* qw_row;
+  const float* sw_row;
+  void* dx;
+  float* dw;
+  float* dgamma;
+  float* dbeta;
+  float* dbias;
+  float* dz;
+  uint8_t* dz_codes;
+  float* dz_scales;
+  void* workspace;
+  size_t workspace_bytes;
+} loka_bwd_args;
+
+size_t loka_gemm_fp8_bwd_workspace_size(const loka_bwd_args* args);
+loka_status loka_gemm_fp8_bwd(const loka_bwd_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * loka_grouped_gemm_fp8_ln: many independent loka_gemm_fp8_ln problems
+ * (x_mode ROW) in one launch.
+ *
+ * Source: LoKA section I (wide ensembles of small layers); GEM
+ * "Generalized Dot-Product Attention" (tile lists precomputed on the CPU,
+ * empty tiles skipped) and "Expert Parallelism" (one expert per rank).
+ *
+ *   groups  HOST array of num_groups descriptors; each is one forward with
+ *           the same meaning and requirements as loka_fwd_args (x_mode
+ *           ROW): x bf16 [M,K], qw [N,K] + sw float[N] from
+ *           loka_quant_fp8(COL, transpose_out=1), bias/gamma/beta bf16 [N]
+ *           or NULL, y bf16 [M,N], optional z fp32 [M,N].
+ *   workspace device memory of loka_grouped_workspace_size() bytes: the
+ *           library copies the descriptors and the tile table into it with
+ *           an asynchronous host-to-device copy on `stream`, so it must not
+ *           be reused until the launch has completed.
+ * Each group's output is bit-identical to a single loka_gemm_fp8_ln call
+ * with the same inputs.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t M, N, K;
+  const void* x;
+  const uint8_t* qw;
+  const float* sw;
+  const void* bias;
+  const void* gamma;
+  const void* beta;
+  void* y;
+  float* z;
+} loka_group_desc;
+
+typedef struct {
+  int32_t num_groups;
+  int32_t x_mode; /* LOKA_SCALE_ROW */
+  float eps;
+  int32_t reserved;
+  const loka_group_desc* groups;
+  void* workspace;
+  size_t workspace_bytes;
+} loka_grouped_args;
+
+size_t loka_grouped_workspace_size(const loka_grouped_args* args);
+loka_status loka_grouped_gemm_fp8_ln(const loka_grouped_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Helpers.
+ * ---------------------------------------------------------------------- */
+const char* loka_status_string(loka_status s); /* static text, never NULL */
+const char* loka_last_error(void);            /* thread-local detail of the last failing call */
+int loka_abi_version(void);                   /* LOKA_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOKA_FP8_H */

@@ -1,0 +1,193 @@
+"""The C ABI on the CPU: the library loads, exports every function that
+include/loka_fp8.h declares, and rejects every invalid call before it
+touches the GPU (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import fp8_precision_gemm_amd as lk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "loka_fp8.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(lk.library_path):
+        from fp8_precision_gemm_amd import build
+        build.build()
+    return lk.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(loka_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("loka_quant_fp8", "loka_gemm_fp8_ln", "loka_gemm_fp8_bwd", "loka_grouped_gemm_fp8_ln"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", lk.library_path], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (loka_[a-z0-9_]+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_helpers(lib):
+    assert lib.loka_abi_version() == 1
+    for code, name in lk.STATUS.items():
+        assert lib.loka_status_string(code).decode() == name
+
+
+def test_struct_layouts_match_header():
+    """Field order and count of the ctypes mirrors against the header's structs."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for cname, py in [("loka_quant_args", lk.QuantArgs), ("loka_fwd_args", lk.FwdArgs),
+                      ("loka_bwd_args", lk.BwdArgs), ("loka_group_desc", lk.GroupDesc),
+                      ("loka_grouped_args", lk.GroupedArgs)]:
+        body = re.search(r"typedef struct \{([^{}]*)\}\s*" + cname + ";", text).group(1)
+        fields = []
+        for decl in body.split(";"):
+            decl = decl.strip()
+            if not decl:
+                continue
+            names = decl.split()[-1] if "," not in decl else None
+            if names is None:  # "int64_t rows, cols, ld"
+                first, *rest = decl.split(",")
+                fields.append(first.split()[-1].lstrip("*"))
+                fields += [r.strip().lstrip("*") for r in rest]
+            else:
+                fields.append(names.lstrip("*"))
+        assert [f for f, _ in py._fields_] == fields, cname
+
+
+FAKE = 0x100000  # an aligned, never-dereferenced address: validation fails first
+
+
+def _fwd(**kw):
+    a = lk.FwdArgs(M=128, N=256, K=256, x_mode=1, flags=0, eps=1e-5, x=FAKE, qw=FAKE, sw=FAKE, y=FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _call(lib, fn, a):
+    return getattr(lib, fn)(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=100), 2), (dict(N=2048), 2), (dict(N=0), 2), (dict(K=20), 2), (dict(K=4096), 2),
+    (dict(M=-1), 1), (dict(x_mode=2), 1), (dict(x_mode=9), 1), (dict(flags=1), 1),
+    (dict(eps=float("nan")), 1), (dict(eps=-1.0), 1),
+    (dict(x=None), 1), (dict(qw=None), 1), (dict(sw=None), 1), (dict(y=None), 1),
+    (dict(x=FAKE + 8), 3), (dict(bias=FAKE + 2), 3), (dict(z=FAKE + 4), 3),
+    (dict(x_mode=3, K=48), 2),
+    (dict(x_mode=0), 4),  # tensor recipe needs the amax workspace
+])
+def test_forward_validation(lib, kw, status):
+    a = _fwd(**kw)
+    assert _call(lib, "loka_gemm_fp8_ln", a) == status
+    assert lib.loka_last_error().decode()
+
+
+def test_forward_empty_batch_is_a_noop(lib):
+    assert _call(lib, "loka_gemm_fp8_ln", _fwd(M=0, x=None, qw=None, sw=None, y=None)) == 0
+
+
+def test_forward_workspace_sizes(lib):
+    a = _fwd(x_mode=0)
+    need = lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(a))
+    assert need > 0
+    a.workspace = FAKE
+    a.workspace_bytes = need - 4
+    assert _call(lib, "loka_gemm_fp8_ln", a) == 4
+    a.workspace = FAKE + 4
+    a.workspace_bytes = need
+    assert _call(lib, "loka_gemm_fp8_ln", a) == 3
+    assert lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(_fwd(x_mode=1))) == 0
+
+
+def _quant(**kw):
+    a = lk.QuantArgs(rows=64, cols=64, ld=64, src_dtype=0, fmt=0, mode=1, transpose_out=0, src=FAKE, codes=FAKE,
+                     scales=FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), 1), (dict(ld=32), 1), (dict(src_dtype=2), 1), (dict(fmt=3), 1), (dict(mode=5), 1),
+    (dict(transpose_out=2), 1), (dict(cols=40, ld=40), 2), (dict(mode=3, cols=48, ld=48), 2),
+    (dict(mode=4, rows=48), 2), (dict(transpose_out=1, rows=40), 2), (dict(ld=68), 3),
+    (dict(src=None), 1), (dict(codes=None), 1), (dict(scales=None), 1), (dict(mode=3, amax=FAKE), 1),
+    (dict(codes=FAKE + 1), 3), (dict(mode=0), 4), (dict(mode=2), 4),
+])
+def test_quant_validation(lib, kw, status):
+    assert _call(lib, "loka_quant_fp8", _quant(**kw)) == status
+
+
+def test_quant_empty_is_a_noop(lib):
+    assert _call(lib, "loka_quant_fp8", _quant(rows=0, src=None, codes=None, scales=None)) == 0
+    assert lib.loka_quant_workspace_size(ctypes.byref(_quant(mode=3))) == 0
+    assert lib.loka_quant_workspace_size(ctypes.byref(_quant(mode=2))) > 0
+
+
+def _bwd(**kw):
+    a = lk.BwdArgs(M=128, N=256, K=256, flags=0, dy=FAKE, qx=FAKE, sx=FAKE, mean=FAKE, rstd=FAKE, qw=FAKE, sw=FAKE,
+                   x=FAKE, qw_row=FAKE, sw_row=FAKE, dx=FAKE, dw=FAKE)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(flags=2), 1), (dict(K=96), 2), (dict(K=2048), 2), (dict(M=24), 2), (dict(N=96), 2),
+    (dict(dy=None), 1), (dict(dw=None), 1), (dict(mean=None), 1), (dict(qx=None), 1),
+    (dict(flags=1, dgamma=FAKE), 1), (dict(dz=FAKE + 4), 3),
+    ({}, 4),  # the backward always needs its workspace
+])
+def test_backward_validation(lib, kw, status):
+    assert _call(lib, "loka_gemm_fp8_bwd", _bwd(**kw)) == status
+
+
+def test_backward_literal_reading_needs_no_context(lib):
+    a = _bwd(flags=1, qx=None, sx=None, mean=None, rstd=None, qw=None, sw=None)
+    assert _call(lib, "loka_gemm_fp8_bwd", a) == 4  # past the context checks, stops at the workspace
+
+
+def test_grouped_validation(lib):
+    descs = (lk.GroupDesc * 2)()
+    descs[0] = lk.GroupDesc(M=64, N=128, K=128, x=FAKE, qw=FAKE, sw=FAKE, y=FAKE)
+    descs[1] = lk.GroupDesc(M=64, N=96, K=128, x=FAKE, qw=FAKE, sw=FAKE, y=FAKE)
+    a = lk.GroupedArgs(num_groups=2, x_mode=1, eps=1e-5, groups=descs)
+    assert lib.loka_grouped_gemm_fp8_ln(ctypes.byref(a), None) == 2
+    assert "group 1" in lib.loka_last_error().decode()
+    descs[1].N = 128
+    descs[1].y = FAKE + 2
+    assert lib.loka_grouped_gemm_fp8_ln(ctypes.byref(a), None) == 3
+    descs[1].y = FAKE
+    assert lib.loka_grouped_gemm_fp8_ln(ctypes.byref(a), None) == 4
+    a.x_mode = 0
+    assert lib.loka_grouped_gemm_fp8_ln(ctypes.byref(a), None) == 2
+    a.x_mode = 1
+    a.num_groups = 0
+    assert lib.loka_grouped_gemm_fp8_ln(ctypes.byref(a), None) == 0
+
+
+def test_product_path_refuses_without_library(monkeypatch, tmp_path):
+    """No fallback: a missing library is an error, not a silent CPU path."""
+    monkeypatch.setattr(lk, "library_path", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(lk, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        lk.library()

@@ -1,0 +1,148 @@
+"""loka_gemm_fp8_ln on the GPU against the oracle.
+
+Full-size cases use the three forward workloads (tensor recipe 512x256x256,
+rowwise 16384x512x512 on outlier activations, MX 65536x1024x256 on
+log-normal rows) in the launch configuration the benchmark times; the
+oracle computes sampled rows there (rows are independent under the row and
+MX recipes; the tensor case is small enough to check whole).  Smaller cases
+span several tiles with ragged M, K not a multiple of 128, No-Bias and
+default gamma/beta, and degenerate rows."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import codec, forward, quant
+from synth.workloads import forward_case, mx_case, outlier_case, tensor_case, to_bf16_bits
+from tests.gpu_helpers import bf16_dev, check_y, check_z, host, row_sigma, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+W_MODE = {"tensor": "tensor", "row": "col", "mx32_row": "mx32_col"}
+RECIPE = {"tensor": "tensor", "row": "row", "mx32_row": "mx32"}
+
+
+def run_gpu(lib, c, x_mode, eps=1e-5, no_bias=False, no_affine=False):
+    x = bf16_dev(c["x"])
+    w = bf16_dev(c["w"])
+    qw, sw, _ = lib.loka_quant_fp8(w, fmt="e4m3", mode=W_MODE[x_mode], transpose_out=True)
+    out = lib.loka_gemm_fp8_ln(x, qw, sw, bias=None if no_bias else bf16_dev(c["bias"]),
+                               gamma=None if no_affine else bf16_dev(c["gamma"]),
+                               beta=None if no_affine else bf16_dev(c["beta"]), eps=eps, x_mode=x_mode,
+                               want_z=True, want_stats=True, want_qx=True)
+    torch.cuda.synchronize()
+    res = {k: host(v) for k, v in out.items()}
+    res["qw"], res["sw"] = host(qw), host(sw)
+    return res
+
+
+def oracle_rows(c, x_mode, rows, eps=1e-5, no_bias=False, no_affine=False):
+    xs = c["x"][rows] if rows is not None else c["x"]
+    return forward.gemm_ln_forward(xs, c["w"], None if no_bias else c["bias"],
+                                   None if no_affine else c["gamma"], None if no_affine else c["beta"],
+                                   eps=eps, recipe=RECIPE[x_mode])
+
+
+def compare(g, o, rows, x_mode, label):
+    sel = slice(None) if rows is None else rows
+    np.testing.assert_array_equal(g["qx"][sel], o["qx"], err_msg=f"{label}: X codes")
+    if x_mode == "row":
+        np.testing.assert_array_equal(g["sx"][sel].view(np.uint32), o["sx"].astype(np.float32).view(np.uint32))
+    elif x_mode == "mx32_row":
+        np.testing.assert_array_equal(g["sx"][sel], o["sx"])
+    else:
+        np.testing.assert_array_equal(g["sx"].view(np.uint32), o["sx"].astype(np.float32).view(np.uint32))
+    # the weight's codes (transposed) and scales
+    np.testing.assert_array_equal(g["qw"].T, o["qw"], err_msg=f"{label}: W codes")
+    if x_mode == "mx32_row":
+        np.testing.assert_array_equal(g["sw"], o["sw"])
+    else:
+        np.testing.assert_array_equal(g["sw"].view(np.uint32), o["sw"].astype(np.float32).view(np.uint32))
+    sigma = row_sigma(o["z"])
+    ez = check_z(g["z"][sel], o["z"], sigma, label)
+    ey = check_y(g["y"][sel], o["y"], label)
+    np.testing.assert_allclose(g["mean"][sel], o["mean"], rtol=0, atol=1e-3 * sigma.max())
+    np.testing.assert_allclose(g["rstd"][sel], o["rstd"], rtol=2e-3)
+    print(f"{label}: Z err {ez:.2e}  Y max abs err {ey:.2e}")
+    return ez
+
+
+def test_tensor_recipe_full(lib):
+    c = tensor_case()
+    g = run_gpu(lib, c, "tensor")
+    o = oracle_rows(c, "tensor", None)
+    compare(g, o, None, "tensor", "tensor 512x256x256")
+
+
+def test_rowwise_outliers_full_size(lib):
+    c = outlier_case()
+    g = run_gpu(lib, c, "row")
+    rows = sample_rows(c["M"], 1024)
+    o = oracle_rows(c, "row", rows)
+    compare(g, o, rows, "row", "row 16384x512x512")
+
+
+def test_mx_full_size(lib):
+    c = mx_case()
+    g = run_gpu(lib, c, "mx32_row")
+    rows = sample_rows(c["M"], 512)
+    o = oracle_rows(c, "mx32_row", rows)
+    compare(g, o, rows, "mx32_row", "mx 65536x1024x256")
+
+
+@pytest.mark.parametrize("x_mode", ["tensor", "row", "mx32_row"])
+@pytest.mark.parametrize("M,K,N", [(1000, 192, 192), (130, 160, 384), (64, 1024, 128), (1, 64, 64),
+                                   (257, 2048, 128), (200, 512, 1024)])
+def test_ragged_shapes(lib, x_mode, M, K, N):
+    c = forward_case(M, K, N, seed=M + K + N, x_dist="student_t3_outliers", gamma_var=0.1, beta_var=0.1)
+    g = run_gpu(lib, c, x_mode)
+    o = oracle_rows(c, x_mode, None)
+    compare(g, o, None, x_mode, f"{x_mode} {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("x_mode", ["row", "mx32_row"])
+def test_no_bias_default_affine_and_degenerate_rows(lib, x_mode):
+    c = forward_case(192, 256, 256, seed=7)
+    x = codec.bf16_to_f64(c["x"])
+    x[3] = 0.0               # zero row: Z = 0 -> y = beta
+    x[4] = 1.0               # constant row
+    x[5] *= 2.0 ** -120      # tiny amax (r saturates / E8M0 clamps)
+    x[6] *= 2.0 ** 100
+    c["x"] = to_bf16_bits(x)
+    g = run_gpu(lib, c, x_mode, no_bias=True, no_affine=True)
+    o = oracle_rows(c, x_mode, None, no_bias=True, no_affine=True)
+    compare(g, o, None, x_mode, f"{x_mode} no-bias")
+    assert np.all(g["y"][3] == 0)
+
+
+def test_power_of_two_row_rescaling_on_gpu(lib):
+    """Rows scaled by 2**j, j >= 0, with no bias and eps = 0: the codes are
+    identical, the row scales exactly 2**j times larger, Z exactly 2**j
+    times larger and Y bit-identical -- on the GPU alone (every scaling by a
+    power of two is exact in the kernel's fp32 arithmetic)."""
+    c = forward_case(256, 512, 512, seed=11, x_dist="student_t3_outliers")
+    x = codec.bf16_to_f64(c["x"])
+    j = np.arange(256) % 17
+    c2 = dict(c, x=to_bf16_bits(np.ldexp(x, j[:, None])))
+    g1 = run_gpu(lib, c, "row", eps=0.0, no_bias=True)
+    g2 = run_gpu(lib, c2, "row", eps=0.0, no_bias=True)
+    np.testing.assert_array_equal(g1["qx"], g2["qx"])
+    np.testing.assert_array_equal(np.ldexp(g1["sx"].astype(np.float64), j), g2["sx"].astype(np.float64))
+    np.testing.assert_array_equal(np.ldexp(g1["z"].astype(np.float64), j[:, None]), g2["z"].astype(np.float64))
+    np.testing.assert_array_equal(g1["y"], g2["y"])
+
+
+def test_deterministic_and_stream_async(lib):
+    c = outlier_case(M=4096)
+    a = run_gpu(lib, c, "row")
+    b = run_gpu(lib, c, "row")
+    for k in ("y", "z", "qx", "sx", "mean", "rstd"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+    # on a side stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        x = bf16_dev(c["x"])
+        qw, sw, _ = lib.loka_quant_fp8(bf16_dev(c["w"]), mode="col", transpose_out=True)
+        out = lib.loka_gemm_fp8_ln(x, qw, sw, bf16_dev(c["bias"]), bf16_dev(c["gamma"]), bf16_dev(c["beta"]))
+    s.synchronize()
+    np.testing.assert_array_equal(host(out["y"]), a["y"])
