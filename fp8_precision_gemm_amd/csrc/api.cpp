@@ -220,6 +220,8 @@ loka_status loka_grouped_gemm_fp8_ln(const loka_grouped_args* a, void* stream) {
     const loka_group_desc& g = a->groups[i];
     st = check_fwd_shape(g.M, g.N, g.K, LOKA_SCALE_ROW);
     if (st != LOKA_OK) return fail(st, "group %d: %s", i, std::string(g_last_error).c_str());
+    REQUIRE(g.N <= 512, LOKA_ERR_UNSUPPORTED, "group %d: the grouped launch supports N <= 512 (N=%lld)", i,
+            (long long)g.N);
     if (g.M > 0)
       REQUIRE(g.x && g.qw && g.sw && g.y, LOKA_ERR_INVALID_ARG, "group %d: x, qw, sw and y are required", i);
     REQUIRE(aligned16(g.x) && aligned16(g.qw) && aligned16(g.sw) && aligned16(g.bias) && aligned16(g.gamma) &&

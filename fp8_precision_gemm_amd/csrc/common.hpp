@@ -111,7 +111,30 @@ __device__ __forceinline__ float e8m0_inv_multiplier(int code) {
   return __uint_as_float((uint32_t)(neg + 127) << 23);
 }
 
-// Wavefront (64-lane) reductions.
+// DPP max of v with the value of another lane (dpp control CTRL); rows
+// outside ROW_MASK keep their own value.
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_max(float v) {
+  const int iv = __float_as_int(v);
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(iv, iv, CTRL, ROW_MASK, 0xF, false)));
+}
+// Max over each quad of lanes (4 consecutive lanes).
+__device__ __forceinline__ float quad_max(float v) {
+  v = dpp_max<0xB1>(v);  // quad_perm [1,0,3,2]
+  return dpp_max<0x4E>(v);  // quad_perm [2,3,0,1]
+}
+// Max over the whole wavefront, returned uniformly (DPP within rows of 16,
+// row broadcasts across rows, then lane 63 read back).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  v = quad_max(v);
+  v = dpp_max<0x124>(v);        // row_ror:4
+  v = dpp_max<0x128>(v);        // row_ror:8
+  v = dpp_max<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_max<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Wavefront (64-lane) reductions through LDS permutes.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

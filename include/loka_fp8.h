@@ -269,7 +269,8 @@ loka_status loka_gemm_fp8_bwd(const loka_bwd_args* args, void* stream);
  *           an asynchronous host-to-device copy on `stream`, so it must not
  *           be reused until the launch has completed.
  * Each group's output is bit-identical to a single loka_gemm_fp8_ln call
- * with the same inputs.
+ * with the same inputs.  Requirements: as loka_gemm_fp8_ln, with N <= 512
+ * for every group (LOKA_ERR_UNSUPPORTED otherwise).
  * ---------------------------------------------------------------------- */
 typedef struct {
   int64_t M, N, K;
