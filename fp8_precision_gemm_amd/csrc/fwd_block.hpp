@@ -233,9 +233,21 @@ __device__ __forceinline__ void mma_step(v4f (&acc)[NT][MT], const v8i (&wf)[NT]
                             : mfma_fp8<0, 0>(wf[t], xf[i], acc[t][i]);
 }
 
+// Per-column vectors of one 16-column tile for this lane's 4 columns,
+// requested at kernel start: dequantization scales, bias, gamma, beta.
+struct ColVec {
+  float4 sw;
+  uint2 b, ga, be;
+};
+
+__device__ __forceinline__ void unpack4(uint2 u, float o[4]) {
+  o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x); o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
+}
+
 // One workgroup (8 wavefronts): BM = 16*MT rows, all N columns (N <= 128*NTW).
-// MODE: 0 tensor, 1 row, 3 mx32.
-template <int MODE, int NTW, int MT>
+// MODE: 0 tensor, 1 row, 3 mx32.  ALLV: N is a multiple of 128, so every
+// wavefront's NTW tiles are real (no clamped duplicates to mask out).
+template <int MODE, int NTW, int MT, bool ALLV>
 __device__ __forceinline__ void fwd_block(const FwdBlock& p, int64_t m0, uint8_t* smem) {
   constexpr int BM = 16 * MT;
   const int K = p.K, N = p.N;
@@ -250,7 +262,7 @@ __device__ __forceinline__ void fwd_block(const FwdBlock& p, int64_t m0, uint8_t
   uint8_t* xe8 = reinterpret_cast<uint8_t*>(rs + BM);
   float* red0 = reinterpret_cast<float*>(xe8 + ((size_t)BM * kb + 15) / 16 * 16);
   float* red1 = red0 + kWaves * BM;
-  float* wgs = red1 + kWaves * BM;  // workgroup scalars: [0] s_w bound, [1] |b| bound, [8+w], [16+w] partials
+  float* wgs = red1 + kWaves * BM;  // workgroup scalars: [8+w], [16+w] per-wavefront column maxima
 
   // this wavefront's column tiles: w, w+8, ... (clamped beyond T, discarded)
   const int r = lane & 15, g = lane >> 4;
@@ -262,29 +274,27 @@ __device__ __forceinline__ void fwd_block(const FwdBlock& p, int64_t m0, uint8_t
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
     const int t = wave + kWaves * j;
-    tvalid[j] = t < T;
-    tile[j] = t < T ? t : T - 1;
+    tvalid[j] = ALLV || t < T;
+    tile[j] = (ALLV || t < T) ? t : T - 1;
     wrow[j] = p.qw + (int64_t)(16 * tile[j] + r) * K;
     srow[j] = MODE == 3 ? sw8 + (int64_t)(16 * tile[j] + r) * kb : nullptr;
   }
+  // the first two weight chunks and every per-column vector are requested
+  // before the activations are touched
   const int nfull = K >> 7;
   v8i wa[NTW], wb[NTW];
   int sa[NTW], sb[NTW];
   if (nfull > 0) load_w<MODE, NTW, true>(wa, sa, wrow, srow, g, 0, K, kb);
-
-  // row-magnitude bound for the variance rescale: |z| <= s_x * 448^2 K max(s_w) + max|b|
-  if (MODE != 3) {
-    float swm = 0.0f, bm = 0.0f;
-    for (int n = tid; n < N; n += kThreads) {
-      swm = fmaxf(swm, MODE == 1 ? static_cast<const float*>(p.sw)[n] : static_cast<const float*>(p.sw)[0]);
-      if (p.bias) bm = fmaxf(bm, fabsf(__uint_as_float((uint32_t)p.bias[n] << 16)));
-    }
-    swm = wave_max_dpp(swm);
-    bm = wave_max_dpp(bm);
-    if (lane == 0) {
-      wgs[8 + wave] = swm;
-      wgs[16 + wave] = bm;
-    }
+  if (nfull > 1) load_w<MODE, NTW, true>(wb, sb, wrow, srow, g, 128, K, kb);
+  ColVec cv[NTW];
+  const uint2 ones = make_uint2(0x3F803F80u, 0x3F803F80u), zeros = make_uint2(0u, 0u);
+#pragma unroll
+  for (int j = 0; j < NTW; ++j) {
+    const int n0 = 16 * tile[j] + 4 * g;
+    if (MODE == 1) cv[j].sw = *reinterpret_cast<const float4*>(static_cast<const float*>(p.sw) + n0);
+    cv[j].b = p.bias ? *reinterpret_cast<const uint2*>(p.bias + n0) : zeros;
+    cv[j].ga = p.gamma ? *reinterpret_cast<const uint2*>(p.gamma + n0) : ones;
+    cv[j].be = p.beta ? *reinterpret_cast<const uint2*>(p.beta + n0) : zeros;
   }
 
   // ---- 1. quantize ----------------------------------------------------------
@@ -292,15 +302,6 @@ __device__ __forceinline__ void fwd_block(const FwdBlock& p, int64_t m0, uint8_t
   else if (K <= 1024) quantize_rows<MODE, 2, MT>(p, m0, wave, lane, xs, rs, xe8);
   else quantize_rows<MODE, 4, MT>(p, m0, wave, lane, xs, rs, xe8);
   __syncthreads();
-  if (MODE != 3 && tid == 0) {
-    float swm = 0.0f, bm = 0.0f;
-    for (int w = 0; w < kWaves; ++w) {
-      swm = fmaxf(swm, wgs[8 + w]);
-      bm = fmaxf(bm, wgs[16 + w]);
-    }
-    wgs[0] = swm * (448.0f * 448.0f) * (float)K;
-    wgs[1] = bm;
-  }
 
   // optional: the quantized X (bit-identical to loka_quant_fp8) for the backward
   if (p.qx_out != nullptr) {
@@ -330,14 +331,14 @@ __device__ __forceinline__ void fwd_block(const FwdBlock& p, int64_t m0, uint8_t
   for (int j = 0; j < NTW; ++j)
 #pragma unroll
     for (int i = 0; i < MT; ++i) acc[j][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  // full 128-deep chunks, the next chunk's weight fragments in flight while
-  // the current ones feed the MFMAs (two register sets, alternating)
+  // full 128-deep chunks from two alternating register sets; a set is
+  // refilled with the chunk after next as soon as its MFMAs are issued
   for (int c = 0; c < nfull; c += 2) {
-    if (c + 1 < nfull) load_w<MODE, NTW, true>(wb, sb, wrow, srow, g, (c + 1) << 7, K, kb);
     mma_step<MODE, NTW, MT>(acc, wa, sa, xs, xe8, ldk, kb, r, g, c << 7, K);
-    if (c + 1 >= nfull) break;
     if (c + 2 < nfull) load_w<MODE, NTW, true>(wa, sa, wrow, srow, g, (c + 2) << 7, K, kb);
+    if (c + 1 >= nfull) break;
     mma_step<MODE, NTW, MT>(acc, wb, sb, xs, xe8, ldk, kb, r, g, (c + 1) << 7, K);
+    if (c + 3 < nfull) load_w<MODE, NTW, true>(wb, sb, wrow, srow, g, (c + 3) << 7, K, kb);
   }
   if (K & 127) {  // tail chunk: fragments past K read as zero
     const int kc = nfull << 7;
@@ -353,28 +354,45 @@ __device__ __forceinline__ void fwd_block(const FwdBlock& p, int64_t m0, uint8_t
   float psum[MT], pmax[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) psum[i] = pmax[i] = 0.0f;
+  float swm = 0.0f, bm = 0.0f;  // this lane's column maxima of s_w and |b| (variance-rescale bound)
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
-    const int n0 = 16 * tile[j] + 4 * g;
     float swv[4], bv[4];
     if (MODE == 1) {
-      const float4 s4 = *reinterpret_cast<const float4*>(static_cast<const float*>(p.sw) + n0);
-      swv[0] = s4.x; swv[1] = s4.y; swv[2] = s4.z; swv[3] = s4.w;
+      swv[0] = cv[j].sw.x; swv[1] = cv[j].sw.y; swv[2] = cv[j].sw.z; swv[3] = cv[j].sw.w;
     } else {
       const float s0 = MODE == 0 ? static_cast<const float*>(p.sw)[0] : 1.0f;
       swv[0] = swv[1] = swv[2] = swv[3] = s0;
     }
-    load4_bf16(p.bias ? p.bias + n0 : nullptr, 0.0f, bv);
-    const float vm = tvalid[j] ? 1.0f : 0.0f;
+    unpack4(cv[j].b, bv);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      swm = fmaxf(swm, swv[q]);
+      bm = fmaxf(bm, fabsf(bv[q]));
+    }
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float zz = MODE == 3 ? acc[j][i][q] + bv[q] : fmaf(acc[j][i][q], sxv[i] * swv[q], bv[q]);
         acc[j][i][q] = zz;
-        psum[i] = fmaf(zz, vm, psum[i]);
-        if (MODE == 3) pmax[i] = fmaxf(pmax[i], fabsf(zz) * vm);
+        if (ALLV) {
+          psum[i] += zz;
+          if (MODE == 3) pmax[i] = fmaxf(pmax[i], fabsf(zz));
+        } else {
+          const float vm = tvalid[j] ? 1.0f : 0.0f;
+          psum[i] = fmaf(zz, vm, psum[i]);
+          if (MODE == 3) pmax[i] = fmaxf(pmax[i], fabsf(zz) * vm);
+        }
       }
+    }
+  }
+  if (MODE != 3) {
+    swm = wave_max_dpp(swm);
+    bm = wave_max_dpp(bm);
+    if (lane == 0) {
+      wgs[8 + wave] = swm;
+      wgs[16 + wave] = bm;
     }
   }
   const float invn = 1.0f / (float)N;
@@ -391,6 +409,17 @@ __device__ __forceinline__ void fwd_block(const FwdBlock& p, int64_t m0, uint8_t
     }
   }
   __syncthreads();
+  // |z| <= s_x * 448^2 K max_n s_w + max_n |b| bounds a row's values (tensor/row
+  // recipes); MX rows use their actual maximum
+  float bound_w = 0.0f, bound_b = 0.0f;
+  if (MODE != 3) {
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      bound_w = fmaxf(bound_w, wgs[8 + w]);
+      bound_b = fmaxf(bound_b, wgs[16 + w]);
+    }
+    bound_w *= (448.0f * 448.0f) * (float)K;
+  }
   float mu[MT], cs[MT];
   bool scaled = false;
 #pragma unroll
@@ -403,17 +432,17 @@ __device__ __forceinline__ void fwd_block(const FwdBlock& p, int64_t m0, uint8_t
       if (MODE == 3) mx = fmaxf(mx, red1[w * BM + rr]);
     }
     mu[i] = s * invn;
-    cs[i] = row_rescale(MODE == 3 ? mx : sxv[i] * wgs[0] + wgs[1]);
+    cs[i] = row_rescale(MODE == 3 ? mx : sxv[i] * bound_w + bound_b);
     scaled |= cs[i] != 1.0f;
   }
-  __syncthreads();  // red0 is reused below
+  __syncthreads();  // red0/red1 are reused below
   float psq[MT];
 #pragma unroll
   for (int i = 0; i < MT; ++i) psq[i] = 0.0f;
   if (__any(scaled)) {  // rows too large to square in fp32 (rare)
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
-      const float vm = tvalid[j] ? 1.0f : 0.0f;
+      const float vm = (ALLV || tvalid[j]) ? 1.0f : 0.0f;
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
@@ -425,12 +454,12 @@ __device__ __forceinline__ void fwd_block(const FwdBlock& p, int64_t m0, uint8_t
   } else {
 #pragma unroll
     for (int j = 0; j < NTW; ++j) {
-      const float vm = tvalid[j] ? 1.0f : 0.0f;
 #pragma unroll
       for (int i = 0; i < MT; ++i)
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const float d = (acc[j][i][q] - mu[i]) * vm;
+          float d = acc[j][i][q] - mu[i];
+          if (!ALLV) d *= tvalid[j] ? 1.0f : 0.0f;
           psq[i] = fmaf(d, d, psq[i]);
         }
     }
@@ -466,19 +495,26 @@ __device__ __forceinline__ void fwd_block(const FwdBlock& p, int64_t m0, uint8_t
   for (int j = 0; j < NTW; ++j) {
     const int n0 = 16 * tile[j] + 4 * g;
     float gv[4], bv[4];
-    load4_bf16(p.gamma ? p.gamma + n0 : nullptr, 1.0f, gv);
-    load4_bf16(p.beta ? p.beta + n0 : nullptr, 0.0f, bv);
+    unpack4(cv[j].ga, gv);
+    unpack4(cv[j].be, bv);
 #pragma unroll
     for (int i = 0; i < MT; ++i) {
       float o[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = fmaf((acc[j][i][q] - mu[i]) * rsd[i], gv[q], bv[q]);
-      if (tvalid[j])
+      if (ALLV || tvalid[j])
         *reinterpret_cast<uint2*>(xs + (16 * i + r) * ldy + 2 * n0) = make_uint2(pack_bf16_hw(o[0], o[1]),
                                                                               pack_bf16_hw(o[2], o[3]));
-      if (p.z != nullptr && tvalid[j]) {
+    }
+  }
+  if (p.z != nullptr) {  // optional fp32 pre-norm output
+#pragma unroll
+    for (int j = 0; j < NTW; ++j) {
+      const int n0 = 16 * tile[j] + 4 * g;
+#pragma unroll
+      for (int i = 0; i < MT; ++i) {
         const int64_t m = m0 + 16 * i + r;
-        if (m < p.M)
+        if ((ALLV || tvalid[j]) && m < p.M)
           *reinterpret_cast<float4*>(p.z + m * N + n0) =
               make_float4(acc[j][i][0], acc[j][i][1], acc[j][i][2], acc[j][i][3]);
       }

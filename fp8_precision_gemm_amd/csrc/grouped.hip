@@ -40,10 +40,10 @@ __global__ __launch_bounds__(kThreads) void k_grouped(const GroupDev* groups, co
   p.eps = eps; p.x_r = 1.0f; p.x_s = 1.0f;
   const int64_t m0 = (int64_t)(b - tile_start[lo]) * (16 * kMT);
   switch ((p.N + 127) / 128) {  // column tiles per wavefront
-    case 1: fwd_block<1, 1, kMT>(p, m0, smem); break;
-    case 2: fwd_block<1, 2, kMT>(p, m0, smem); break;
-    case 3: fwd_block<1, 3, kMT>(p, m0, smem); break;
-    case 4: fwd_block<1, 4, kMT>(p, m0, smem); break;
+    case 1: fwd_block<1, 1, kMT, false>(p, m0, smem); break;
+    case 2: fwd_block<1, 2, kMT, false>(p, m0, smem); break;
+    case 3: fwd_block<1, 3, kMT, false>(p, m0, smem); break;
+    case 4: fwd_block<1, 4, kMT, false>(p, m0, smem); break;
     default: break;
   }
 }
