@@ -30,6 +30,9 @@ METRIC = "FP8 quant+GEMM+LayerNorm TFLOP/s and % FP8 MFMA peak (M=16384,K=N=512)
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 ROTATE = 16
+# The fused rowwise forward's sources and the committed counter summary of its HBM traffic.
+FWD_SOURCES = ["common.hpp", "launch.hpp", "fwd_block.hpp", "fwd_row.hip"]
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_fwd_row_16384x512x512_hbm_counters.md")
 
 
 def parse():
@@ -39,7 +42,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-rows", action="store_true", help="skip the other workloads")
-    p.add_argument("--only", default=None, help="time one workload only (for profiling): fwd|tensor|mx|bwd|grouped")
+    p.add_argument("--only", default=None,
+                   help="comma list of workloads to time (for profiling): fwd,tensor,mx,bwd,grouped,copy")
     return p.parse_args()
 
 
@@ -48,6 +52,26 @@ def fwd_bytes(M, K, N, mx=False):
     weight codes and scales, bias/gamma/beta; write Y (bf16) once."""
     sw = N * (K // 32) if mx else N * 4
     return 2 * M * K + N * K + sw + 3 * 2 * N + 2 * M * N
+
+
+def measured_traffic():
+    """HBM bytes per launch of the fused rowwise forward, as FETCH_SIZE +
+    WRITE_SIZE (each calibrated against a 16 MiB copy) recorded in the
+    committed counter summary -- or None when the kernel's sources no longer
+    hash to the value recorded with the counters."""
+    import hashlib
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and " " not in line.split(": ")[0])
+    h = hashlib.sha256()
+    for f in FWD_SOURCES:
+        with open(os.path.join(ROOT, "fp8_precision_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if fields.get("kernel_source_sha256_16", "").strip() != h.hexdigest()[:16]:
+        return None
+    return int(fields["traffic_bytes_per_launch"])
 
 
 def timed_graph(torch, launches, steps, warmup, stream):
@@ -156,6 +180,19 @@ def bench_grouped(torch, lk, groups, steps, warmup, stream):
             "flops": flops}
 
 
+def bench_copy(torch, steps, warmup, stream):
+    """A plain device copy of a 16 MiB buffer (torch's copy kernel): the
+    calibration reference for the HBM byte counters (it must read and write
+    exactly 16 MiB per launch)."""
+    nbytes = 16 << 20
+    src = [torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_() for _ in range(ROTATE)]
+    dst = [torch.empty_like(t) for t in src]
+    launches = [lambda a=a, b=b: b.copy_(a) for a, b in zip(src, dst)]
+    secs, n = timed_graph(torch, launches, steps, warmup, stream)
+    per = secs / n
+    return {"us": per * 1e6, "gbs": 2 * nbytes / per / 1e9, "bytes_read": nbytes, "bytes_written": nbytes}
+
+
 def cpu_baseline(case):
     """The NumPy oracle, untuned, on one host thread: the full rowwise
     forward (quantize X and W, fp64 GEMM, LayerNorm, bf16 rounding)."""
@@ -168,7 +205,7 @@ def cpu_baseline(case):
         while True:
             forward.gemm_ln_forward(case["x"], case["w"], case["bias"], case["gamma"], case["beta"], recipe="row")
             reps += 1
-            if time.perf_counter() - t0 > 8.0:
+            if time.perf_counter() - t0 > 12.0:
                 break
         dt = (time.perf_counter() - t0) / reps
     return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
@@ -192,30 +229,35 @@ def main():
     stream = torch.cuda.Stream()
     case = workloads.outlier_case(dy=True)
     rows = {}
-    only = args.only
+    only = None if args.only is None else set(args.only.split(","))
+    want = lambda name: only is None or name in only
     main_res = None
-    if only in (None, "fwd"):
+    if want("fwd"):
         main_res = bench_forward(torch, lk, case, "row", args.steps, args.warmup, stream)
         print(f"[bench] rowwise forward: {main_res['us']:.2f} us/launch", file=sys.stderr, flush=True)
-    if not args.no_rows and only in (None, "tensor"):
+    if not args.no_rows and want("tensor"):
         r = bench_forward(torch, lk, workloads.tensor_case(), "tensor", args.steps, args.warmup, stream)
         rows["tensor_fwd_512x256x256"] = {k: round(v, 3) for k, v in r.items()}
         print(f"[bench] tensor forward: {r['us']:.2f} us", file=sys.stderr, flush=True)
-    if not args.no_rows and only in (None, "mx"):
+    if not args.no_rows and want("mx"):
         r = bench_forward(torch, lk, workloads.mx_case(), "mx32_row", max(200, args.steps // 4),
                           max(20, args.warmup // 4), stream)
         rows["mx_fwd_65536x1024x256"] = {k: round(v, 3) for k, v in r.items()}
         rows["mx_fwd_65536x1024x256"]["hbm_frac"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
         print(f"[bench] mx forward: {r['us']:.2f} us", file=sys.stderr, flush=True)
-    if not args.no_rows and only in (None, "bwd"):
+    if not args.no_rows and want("bwd"):
         r = bench_backward(torch, lk, case, args.steps, args.warmup, stream)
         rows["bwd_16384x512x512"] = {k: round(v, 3) for k, v in r.items()}
         print(f"[bench] backward: {r['us']:.2f} us", file=sys.stderr, flush=True)
-    if not args.no_rows and only in (None, "grouped"):
+    if not args.no_rows and want("grouped"):
         r = bench_grouped(torch, lk, workloads.grouped_case(), args.steps, args.warmup, stream)
         rows["grouped_64x8192"] = {k: round(v, 3) for k, v in r.items()}
         rows["grouped_64x8192"]["hbm_frac"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
         print(f"[bench] grouped: {r['us']:.2f} us", file=sys.stderr, flush=True)
+    if only is not None and "copy" in only:
+        r = bench_copy(torch, args.steps, args.warmup, stream)
+        rows["copy_16MiB"] = {k: round(v, 3) for k, v in r.items()}
+        print(f"[bench] copy 16 MiB: {r['us']:.2f} us", file=sys.stderr, flush=True)
     if main_res is None:
         print(json.dumps({"rows": rows}))
         return
@@ -240,7 +282,8 @@ def main():
                    "M": 16384, "K": 512, "N": 512, "x_scaling": "row", "w_scaling": "col", "fmt": "e4m3"},
         "pct_fp8_peak": round(100 * main_res["tflops"] / PEAK_FP8_TFLOPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(main_res["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(main_res["gbs"] / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(main_res["gbs"] / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
+                     "traffic_unit": "bytes/launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "kernel": "k_fwd<row> (fused X quant + FP8 MFMA GEMM + LayerNorm)",
                      "algorithmic_bytes_per_launch": main_res["bytes"],
                      "avg_launch_us": round(main_res["us"], 3)},
