@@ -80,16 +80,13 @@ struct ScalePair {
   float s;  // dequantization scale (stored)
   float r;  // quantization multiplier
 };
+// Branch-free: amax == 0 divides FMAX by itself, giving s = r = 1 exactly.
 template <int FMT>
 __device__ __forceinline__ ScalePair scales_from_amax(float amax) {
+  const float a = amax == 0.0f ? Fp8Traits<FMT>::fmax : amax;
   ScalePair p;
-  if (amax == 0.0f) {
-    p.s = 1.0f;
-    p.r = 1.0f;
-  } else {
-    p.s = amax / Fp8Traits<FMT>::fmax;
-    p.r = fminf(Fp8Traits<FMT>::fmax / amax, kFltMax);
-  }
+  p.s = a / Fp8Traits<FMT>::fmax;
+  p.r = fminf(Fp8Traits<FMT>::fmax / a, kFltMax);
   return p;
 }
 
@@ -112,13 +109,20 @@ __device__ __forceinline__ float e8m0_inv_multiplier(int code) {
 }
 
 // DPP max of v with the value of another lane (dpp control CTRL); rows
-// outside ROW_MASK keep their own value.
+// outside ROW_MASK keep their own value.  Only for non-negative values
+// (amaxes, scales, +0): their fp32 order is the unsigned order of their
+// bits, so the max is one v_max_u32 with the DPP operand folded in (an fp32
+// max would first canonicalize the moved value).
 template <int CTRL, int ROW_MASK = 0xF>
 __device__ __forceinline__ float dpp_max(float v) {
-  const int iv = __float_as_int(v);
-  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(iv, iv, CTRL, ROW_MASK, 0xF, false)));
+  const uint32_t iv = __float_as_uint(v);
+  // all rows written: bound_ctrl with the max identity 0 lets the move fold
+  // into the max; rows masked off must keep their own value instead
+  const uint32_t ov = ROW_MASK == 0xF ? (uint32_t)__builtin_amdgcn_update_dpp(0, (int)iv, CTRL, 0xF, 0xF, true)
+                                      : (uint32_t)__builtin_amdgcn_update_dpp((int)iv, (int)iv, CTRL, ROW_MASK, 0xF, false);
+  return __uint_as_float(iv > ov ? iv : ov);
 }
-// Max over each quad of lanes (4 consecutive lanes).
+// Max over each quad of lanes (4 consecutive lanes); non-negative values.
 __device__ __forceinline__ float quad_max(float v) {
   v = dpp_max<0xB1>(v);  // quad_perm [1,0,3,2]
   return dpp_max<0x4E>(v);  // quad_perm [2,3,0,1]

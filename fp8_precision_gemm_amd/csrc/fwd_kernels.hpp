@@ -1,0 +1,112 @@
+// Kernels and launch logic of loka_gemm_fp8_ln for one scaling recipe, all
+// column counts: the weight-resident persistent kernel (fwd_resident.hpp)
+// when the FP8 weight fits in the workgroup's registers (K*N <= 256 KiB,
+// N <= 512), otherwise one workgroup per 64-row (32 for N > 512) tile of
+// the general block (fwd_block.hpp).  Each recipe's translation unit
+// (fwd_tensor.hip, fwd_row.hip, fwd_mx.hip) instantiates launch_mode<MODE>.
+#pragma once
+
+#include "fwd_block.hpp"
+#include "fwd_resident.hpp"
+
+namespace loka {
+namespace fwd {
+namespace {
+
+template <int MODE, int NTW, bool ALLV>
+__global__ __launch_bounds__(kThreads) void k_fwd(FwdBlock p, const float* partials, int np) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  if (MODE == 0) {
+    __shared__ float red8[kWaves];
+    ScalePair sp = reduce_tensor_scale<0>(partials, np, red8);
+    p.x_r = sp.r;
+    p.x_s = sp.s;
+  }
+  fwd_block<MODE, NTW, Shape<NTW>::MT, ALLV>(p, (int64_t)blockIdx.x * (16 * Shape<NTW>::MT), smem);
+}
+
+template <int MODE, int NTW, bool ALLV>
+hipError_t launch_t(const FwdBlock& p, const float* partials, int np, hipStream_t s) {
+  constexpr int BM = 16 * Shape<NTW>::MT;
+  const unsigned grid = (unsigned)((p.M + BM - 1) / BM);
+  const size_t lds = fwd_lds_bytes(BM, p.K, p.N);
+  auto kern = k_fwd<MODE, NTW, ALLV>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, s, p, partials, np);
+  return hipGetLastError();
+}
+
+
+template <int MODE, int NT, bool OPT, bool FULL>
+__global__ __launch_bounds__(kThreads) void k_fwd_res(FwdBlock p, const float* partials, int np) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  if (MODE == 0) {
+    __shared__ float red8[kWaves];
+    ScalePair sp = reduce_tensor_scale<0>(partials, np, red8);
+    p.x_r = sp.r;
+    p.x_s = sp.s;
+  }
+  // a contiguous, balanced range of 16-row tiles per workgroup
+  const int64_t T = (p.M + kResRows - 1) / kResRows, G = gridDim.x, b = blockIdx.x;
+  ResBlock<MODE, NT, OPT, FULL> blk(p, b * T / G, (b + 1) * T / G, smem);
+  blk.run();
+}
+
+template <int MODE, int NT>
+hipError_t launch_res_t(const FwdBlock& p, const float* partials, int np, int grid, hipStream_t s) {
+  const size_t lds = (size_t)res_lds(NT, p.N).total;
+  const bool opt = p.z != nullptr || p.mean != nullptr || p.rstd != nullptr || p.qx_out != nullptr ||
+                   p.sx_out != nullptr;
+  // whole column tiles per wavefront and whole 256-column pieces per lane
+  const bool full = p.N == 128 * NT && p.K == 256 * Res<NT>::KQ;
+  auto kern = opt ? (full ? k_fwd_res<MODE, NT, true, true> : k_fwd_res<MODE, NT, true, false>)
+                  : (full ? k_fwd_res<MODE, NT, false, true> : k_fwd_res<MODE, NT, false, false>);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, s, p, partials, np);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Workgroups for the weight-resident kernel: one per compute unit (each
+// holds a full copy of the weight), fewer when there are fewer tiles.
+inline hipError_t res_grid(int64_t M, int* grid) {
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const int64_t T = (M + kResRows - 1) / kResRows;
+  *grid = (int)(T < cus ? T : cus);
+  return hipSuccess;
+}
+
+template <int MODE>
+hipError_t launch_mode(const FwdBlock& p, const float* partials, int np, hipStream_t s) {
+  if (res_fits(p.K, p.N)) {
+    int grid = 0;
+    hipError_t e = res_grid(p.M, &grid);
+    if (e != hipSuccess) return e;
+    switch (res_nt(p.N)) {
+      case 1: return launch_res_t<MODE, 1>(p, partials, np, grid, s);
+      case 2: return launch_res_t<MODE, 2>(p, partials, np, grid, s);
+      case 3: return launch_res_t<MODE, 3>(p, partials, np, grid, s);
+      case 4: return launch_res_t<MODE, 4>(p, partials, np, grid, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch ((p.N + 127) / 128) {  // column tiles per wavefront
+#define LOKA_CASE(V) \
+  case V:            \
+    return p.N % 128 == 0 ? launch_t<MODE, V, true>(p, partials, np, s) : launch_t<MODE, V, false>(p, partials, np, s);
+    LOKA_CASE(1) LOKA_CASE(2) LOKA_CASE(3) LOKA_CASE(4) LOKA_CASE(5) LOKA_CASE(6) LOKA_CASE(7) LOKA_CASE(8)
+#undef LOKA_CASE
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fwd
+}  // namespace loka

@@ -1,0 +1,678 @@
+// The weight-resident fused forward: one persistent workgroup per compute
+// unit holds the whole FP8 weight in registers and streams row tiles of X
+// through it.
+//
+// Source: LoKA section III-B2 (Block-wise Normalization, Case 1): with a
+// large batch and a small output dimension a whole output row lives in one
+// block of the GEMM, so the LayerNorm runs in the GEMM epilogue while the
+// tile is still on chip; section III-B (the GEMM output is dequantized and
+// normalized in high precision); section III-B1 (No Bias).  GEM "Mixed
+// Ultra-Low-Precision Training": the activation cast is fused into the
+// neighbouring kernel instead of taking an extra pass over HBM; "Low
+// Precision Flash Attention": MX block scales along K.
+//
+// Shape of the work.  In the recommendation shapes (M >> K, N <= 512) the
+// weight is small (K*N <= 256 KiB of e4m3 codes) and X and Y dominate the
+// bytes.  A workgroup of 8 wavefronts splits the N columns into 8 slices of
+// 16*NT columns; wavefront w keeps the W^T rows of its slice for all of K in
+// VGPRs (NT x KC MFMA A-fragments, at most 128 registers per lane), loaded
+// once per workgroup: each wavefront's slice is one contiguous run of W^T,
+// read with 1 KiB coalesced loads and rearranged into fragment order through
+// a private LDS staging area, one 128-deep chunk at a time.  The workgroup
+// then walks a contiguous range of 16-row tiles.  Per tile:
+//   * X rows are requested D tiles ahead into registers: each wavefront owns
+//     2 rows, 32 lanes per row, 16 B per lane per 256 columns, so HBM reads
+//     stay in flight across the loop;
+//   * each wavefront quantizes its 2 rows of the next tile into one of two
+//     LDS code buffers: the two rows' max-abs reductions (DPP within rows of
+//     16 lanes, a permlane swap across them) and their scale divisions run
+//     side by side in the two halves of the wavefront;
+//   * v_mfma_scale_f32_16x16x128_f8f6f4 multiplies the resident W^T
+//     fragments (A) by the tile's codes read from LDS (B);
+//   * epilogue: dequant + bias in registers, each wavefront's row sum and
+//     centred sum of squares over its slice, one LDS exchange and barrier,
+//     the slices' statistics combined exactly (sum of the slices' centred
+//     sums plus the between-slice term, Chan, Golub and LeVeque's pairwise
+//     update), then gamma/beta and bf16 stores straight from registers.
+// One barrier per tile; X is read once and Y written once.
+//
+// Column order inside a slice.  The 16 rows of MFMA tile t are mapped to
+// columns so that lane group g (lanes 16g..16g+15) ends up holding 4*nv
+// consecutive output columns of its row (nv = the slice's valid tiles):
+// tile t, A-row 4a+b <-> column c0 + 4*nv*a + 4t + b.  Y is then written with
+// 8- or 16-byte stores and the per-column vectors are contiguous float4s.
+//
+// Cast without a clamp (tensor and row recipes).  With r = RN32(448/amax)
+// every |x*r| is at most 448*(1 + 2^-23); the hardware convert rounds
+// everything up to the 448/480 midpoint (464) to the 448 code, so the
+// saturation the format definition asks for is already what it produces.
+// MX scaling can reach 512*2^e before the cast and keeps the clamp.
+#pragma once
+
+#include "common.hpp"
+#include "fwd_block.hpp"
+#include "launch.hpp"
+
+namespace loka {
+namespace fwd {
+
+constexpr int kResRows = 16;  // rows per tile
+constexpr int kWst = 144;     // weight staging row stride (bytes): 128-byte chunk + 16 pad
+
+// Per-wavefront tile count NT (N <= 128*NT) fixes the K capacity: NT*KC
+// fragments of 8 VGPRs stay within 128 registers.
+template <int NT>
+struct Res {
+  static constexpr int KC = NT <= 2 ? 8 : (NT == 3 ? 5 : 4);  // 128-deep K chunks held
+  static constexpr int KQ = (KC * 128 + 255) / 256;           // 16-byte X loads per lane (32 lanes per row)
+  static constexpr int D = KQ <= 2 ? 3 : 2;                    // tiles of X requested ahead
+  static constexpr int LDX = KC * 128 + 16;                    // LDS code row stride (bytes)
+  static constexpr int KP = (KC + 3) / 4;                     // E8M0 words per lane group
+  static constexpr int XE = 16 * KP;                           // E8M0 bytes per LDS row ([g][KP words])
+};
+
+__host__ __device__ constexpr int res_nt(int N) { return (N + 127) / 128; }
+__host__ __device__ constexpr int res_kc(int nt) { return nt <= 2 ? 8 : (nt == 3 ? 5 : 4); }
+// Does (K, N) fit the weight-resident kernel?
+__host__ __device__ constexpr bool res_fits(int K, int N) {
+  return N >= 16 && N <= 512 && N % 16 == 0 && K >= 16 && K % 16 == 0 && (K + 127) / 128 <= res_kc(res_nt(N));
+}
+
+// LDS carve-up (bytes, every part 16-byte aligned):
+//   codes [2][16][LDX] u8 | xe8 [2][16][XE] u8 | rs [2][16] f32 |
+//   red [2][16][8] float2 | cvec [4][N] f32 (s_w, bias, gamma, beta) |
+//   wmx [3][8] f32 | wst [8][16*NT][kWst] u8 (weight staging, set-up only)
+struct ResLds {
+  int codes, xe8, rs, red, cvec, wmx, wst, total;
+};
+__host__ __device__ inline ResLds res_lds(int nt, int N) {
+  const int kc = res_kc(nt), ldx = kc * 128 + 16, xe = 16 * ((kc + 3) / 4);
+  ResLds l;
+  l.codes = 0;
+  l.xe8 = l.codes + 2 * kResRows * ldx;
+  l.rs = l.xe8 + ((2 * kResRows * xe + 15) / 16) * 16;
+  l.red = l.rs + 2 * kResRows * 4;
+  l.cvec = l.red + 2 * kResRows * 8 * 8;
+  l.wmx = l.cvec + 4 * N * 4;
+  l.wst = l.wmx + 32 * 4;
+  l.total = l.wst + 8 * 16 * nt * kWst;
+  return l;
+}
+
+// Max over each 32-lane half of the wavefront, returned in every lane of
+// that half: quads and rows of 16 by DPP, then the two rows of a half
+// exchanged by v_permlane16_swap.  Non-negative values only.
+__device__ __forceinline__ float half_max(float v) {
+  v = quad_max(v);
+  v = dpp_max<0x124>(v);  // row_ror:4
+  v = dpp_max<0x128>(v);  // row_ror:8
+  const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(max((uint32_t)s[0], (uint32_t)s[1]));  // non-negative: unsigned order
+}
+// Sum over the 4 lanes l, l^16, l^32, l^48 (the lanes holding one output
+// row of a 16x16 MFMA tile), returned in all four.
+__device__ __forceinline__ float sum4(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// 8 bf16 (one 16-byte piece) -> fp32
+__device__ __forceinline__ void unpack8(const uint4& u, float v[8]) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_lo(w[i]);
+    v[2 * i + 1] = bf16_hi(w[i]);
+  }
+}
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+// Largest sign-cleared bf16 bit pattern of 8 finite bf16 values (= the bits of max |x|).
+__device__ __forceinline__ uint32_t absmax_bits8(const uint4& u) {
+  const u16x2 a = __builtin_bit_cast(u16x2, u.x & 0x7FFF7FFFu), b = __builtin_bit_cast(u16x2, u.y & 0x7FFF7FFFu);
+  const u16x2 c = __builtin_bit_cast(u16x2, u.z & 0x7FFF7FFFu), d = __builtin_bit_cast(u16x2, u.w & 0x7FFF7FFFu);
+  const u16x2 mx = __builtin_elementwise_max(__builtin_elementwise_max(a, b), __builtin_elementwise_max(c, d));
+  return max((uint32_t)mx.x, (uint32_t)mx.y);
+}
+
+// MX MFMA with both E8M0 operands taken from byte `sel` (0..3) of packed
+// scale words (the instruction's op_sel byte select; sel is a constant
+// after unrolling).
+__device__ __forceinline__ v4f mfma_mx_sel(int sel, const v8i& a, const v8i& b, v4f c, uint32_t sa, uint32_t sb) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, (int)sa, 0, (int)sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 1, (int)sa, 1, (int)sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 2, (int)sa, 2, (int)sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 3, (int)sa, 3, (int)sb);
+  }
+}
+
+// OPT: the optional outputs (fp32 Z, mean/rstd, the X codes and scales) are
+// requested; the variant without them carries none of their branches.
+// FULL: N = 128*NT and K = 256*KQ, so every wavefront owns NT whole column
+// tiles and every lane a whole share of each row: no partial-shape guards.
+template <int MODE, int NT, bool OPT, bool FULL>
+struct ResBlock {
+  using R = Res<NT>;
+  static constexpr int KC = R::KC, KQ = R::KQ, D = R::D, LDX = R::LDX, XE = R::XE, KP = R::KP;
+
+  const FwdBlock& p;
+  int64_t tb, te;  // tile range [tb, te)
+  int K, N, kcv, kb, T16, nv, c0, tid, lane, wave, r, g, hrow, hl;
+  uint8_t* codes;
+  uint8_t* xe8;
+  float* rs;
+  float2* red;
+  float* cvec;
+  float* wmx;
+  uint8_t* wst;
+  float bw, bb;   // bound on |z|: row factor (tensor/row: 448^2 K max s_w; MX: 448^2 K 2^(ew_max-127)), max |bias|
+  float inv_nw;   // 1 / (columns of this wavefront's slice)
+
+  v8i wf[NT][KC];
+  uint32_t wsc[NT][KP];
+  uint4 xr[D][KQ];
+  v4f acc[NT];
+  float cs;       // this lane's row rescale factor (power of two)
+  bool scaled;    // some row of this wavefront's tile needs cs != 1
+  // set-up values in flight: this thread's column (tid < N) and the MX scale bytes
+  float cv_sw;
+  uint16_t cv_b, cv_g, cv_be;
+  uint8_t wse[NT][KC];
+
+  __device__ __forceinline__ bool tv(int t) const { return FULL || t < nv; }  // column tile t of the slice is real
+  __device__ __forceinline__ bool kv(int k) const { return FULL || k < K; }   // column k of X is real
+
+  __device__ __forceinline__ ResBlock(const FwdBlock& p_, int64_t tb_, int64_t te_, uint8_t* smem)
+      : p(p_), tb(tb_), te(te_) {
+    K = p.K;
+    N = p.N;
+    kcv = FULL ? KC : (K + 127) >> 7;
+    kb = K >> 5;
+    T16 = N >> 4;
+    tid = threadIdx.x;
+    lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    r = lane & 15;
+    g = lane >> 4;
+    hrow = 2 * wave + (lane >> 5);  // the tile row this lane quantizes
+    hl = lane & 31;                  // its lane within that row's half
+    nv = FULL ? NT : min(max(T16 - wave * NT, 0), NT);
+    c0 = 16 * NT * wave;
+    inv_nw = nv > 0 ? 1.0f / (float)(16 * nv) : 0.0f;
+    const ResLds l = res_lds(NT, N);
+    codes = smem + l.codes;
+    xe8 = smem + l.xe8;
+    rs = reinterpret_cast<float*>(smem + l.rs);
+    red = reinterpret_cast<float2*>(smem + l.red);
+    cvec = reinterpret_cast<float*>(smem + l.cvec);
+    wmx = reinterpret_cast<float*>(smem + l.wmx);
+    wst = smem + l.wst + wave * (16 * NT * kWst);
+  }
+
+  // ---- X row of tile `t` for this lane into register slot S: elements
+  // 256q + 8*hl .. +8 (row clamped to M-1 and columns to K-8: the duplicates
+  // never change a max and are never stored)
+  template <int S>
+  __device__ __forceinline__ void load_x(int64_t t) {
+    if (t >= te) return;
+    int64_t m = t * kResRows + hrow;
+    m = m < p.M ? m : p.M - 1;
+    const uint16_t* xrow = p.x + m * K;
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+      int k = q * 256 + hl * 8;
+      if (!FULL) k = k < K ? k : K - 8;
+      xr[S][q] = *reinterpret_cast<const uint4*>(xrow + k);
+    }
+  }
+
+  // ---- quantize register slot S (tile t) into code buffer `buf`.  Values
+  // are unpacked 8 at a time; with more than two 16-byte pieces per lane
+  // the row max-abs is taken on the packed bf16 bit patterns instead
+  // (|x| ordering equals the ordering of the sign-cleared bits).  Per-row
+  // values go to LDS from every lane of the half (same address, same value)
+  // so that the FULL variant has no divergent branch.
+  template <int S>
+  __device__ __forceinline__ void quantize(int64_t t, int buf) {
+    const int64_t m = t * kResRows + hrow;
+    // past this workgroup's range the tile is a stale slot: LDS only, never
+    // the optional global outputs (those rows belong to another workgroup)
+    const bool out_ok = OPT && t < te && m < p.M;
+    uint8_t* crow = codes + (buf * kResRows + hrow) * LDX;
+    if (MODE == 3) {
+      // block of piece q: 8q + hl/4, stored at LDS slot (g = (hl/4)%4, c = 2q + hl/16)
+      uint8_t* erow = xe8 + (buf * kResRows + hrow) * XE + ((hl >> 2) & 3) * (4 * KP) + (hl >> 4);
+      float emax = 0.0f;
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) {
+        float v[8];
+        unpack8(xr[S][q], v);
+        float a = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+        a = quad_max(a);  // a 32-element block is held by 4 consecutive lanes
+        const int e8 = e8m0_from_amax<0>(a);
+        const float mu = e8m0_inv_multiplier(e8);
+        const int k = q * 256 + hl * 8;
+        if (kv(k)) {
+          emax = fmaxf(emax, (float)e8);
+          erow[2 * q] = (uint8_t)e8;  // the quad's 4 lanes write the same byte
+          if (out_ok && p.sx_out != nullptr && (hl & 3) == 0)
+            static_cast<uint8_t*>(p.sx_out)[m * kb + (k >> 5)] = (uint8_t)e8;
+          const uint32_t lo = cvt4<0>(v[0] * mu, v[1] * mu, v[2] * mu, v[3] * mu);
+          const uint32_t hi = cvt4<0>(v[4] * mu, v[5] * mu, v[6] * mu, v[7] * mu);
+          *reinterpret_cast<uint2*>(crow + k) = make_uint2(lo, hi);
+          if (out_ok && p.qx_out != nullptr) *reinterpret_cast<uint2*>(p.qx_out + m * K + k) = make_uint2(lo, hi);
+        }
+      }
+      emax = half_max(emax);
+      rs[buf * kResRows + hrow] = emax;
+      return;
+    }
+    float rmul;
+    if (MODE == 1) {
+      float a = 0.0f;
+      if (KQ <= 2) {
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) {
+          float v[8];
+          unpack8(xr[S][q], v);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a = fmaxf(a, fabsf(v[i]));
+        }
+      } else {
+        uint32_t mb = 0;
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) mb = max(mb, absmax_bits8(xr[S][q]));
+        a = __uint_as_float(mb << 16);
+      }
+      a = half_max(a);
+      const ScalePair sp = scales_from_amax<0>(a);  // both rows' divisions in one pass
+      rs[buf * kResRows + hrow] = sp.s;
+      if (out_ok && p.sx_out != nullptr && hl == 0) static_cast<float*>(p.sx_out)[m] = sp.s;
+      rmul = sp.r;
+    } else {
+      rmul = p.x_r;
+    }
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+      const int k = q * 256 + hl * 8;
+      if (kv(k)) {
+        float v[8];
+        unpack8(xr[S][q], v);
+        // the first convert of each word leaves bits 16-31 of its `old`
+        // operand (here the input word) for the second one to overwrite
+        uint32_t lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[0] * rmul, v[1] * rmul, (int)xr[S][q].x, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(v[2] * rmul, v[3] * rmul, (int)lo, true);
+        uint32_t hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[4] * rmul, v[5] * rmul, (int)xr[S][q].z, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(v[6] * rmul, v[7] * rmul, (int)hi, true);
+        *reinterpret_cast<uint2*>(crow + k) = make_uint2(lo, hi);
+        if (out_ok && p.qx_out != nullptr) *reinterpret_cast<uint2*>(p.qx_out + m * K + k) = make_uint2(lo, hi);
+      }
+    }
+  }
+
+  // ---- set-up, part 1: request the weight slice (coalesced, into the
+  // fragment registers as raw storage), its MX scale bytes and this
+  // thread's column vectors; nothing here waits for a load
+  __device__ __forceinline__ void request_weights() {
+    // raw piece q of chunk c: slice row 8q + lane/8, bytes c*128 + 16*(lane%8)
+    const int sub = lane >> 3, off = (lane & 7) * 16;
+    const uint8_t* base = p.qw + (int64_t)(c0 + sub) * K + off;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+#pragma unroll
+      for (int q = 0; q < 2 * NT; ++q) {
+        uint4 u = make_uint4(0, 0, 0, 0);
+        if (FULL || (q < 2 * nv && c < kcv && c * 128 + off < K))
+          u = *reinterpret_cast<const uint4*>(base + (int64_t)(8 * q) * K + c * 128);
+        const int t = q >> 1, h = (q & 1) * 4;
+        wf[t][c][h] = (int)u.x; wf[t][c][h + 1] = (int)u.y; wf[t][c][h + 2] = (int)u.z; wf[t][c][h + 3] = (int)u.w;
+      }
+    }
+    if (MODE == 3) {
+      const uint8_t* sw8 = static_cast<const uint8_t*>(p.sw);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int col = c0 + 4 * nv * (r >> 2) + 4 * t + (r & 3);
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          const int blk = 4 * c + g;
+          wse[t][c] = (tv(t) && (FULL || blk < kb)) ? sw8[(int64_t)col * kb + blk] : (uint8_t)127;
+        }
+      }
+    }
+    if (tid < N) {
+      cv_sw = MODE == 1 ? static_cast<const float*>(p.sw)[tid] : (MODE == 0 ? static_cast<const float*>(p.sw)[0] : 1.0f);
+      cv_b = p.bias ? p.bias[tid] : (uint16_t)0;
+      cv_g = p.gamma ? p.gamma[tid] : (uint16_t)0x3F80;
+      cv_be = p.beta ? p.beta[tid] : (uint16_t)0;
+    }
+  }
+
+  // ---- set-up, part 2: weight fragments through the staging area, MX
+  // scale words, column vectors into LDS with their maxima, LDS padding
+  __device__ __forceinline__ void stage_weights() {
+    const int sub = lane >> 3, off = (lane & 7) * 16;
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (!FULL && c >= kcv) break;
+#pragma unroll
+      for (int q = 0; q < 2 * NT; ++q) {
+        if (FULL || q < 2 * nv) {
+          const int t = q >> 1, h = (q & 1) * 4;
+          *reinterpret_cast<uint4*>(wst + (8 * q + sub) * kWst + off) =
+              make_uint4((uint32_t)wf[t][c][h], (uint32_t)wf[t][c][h + 1], (uint32_t)wf[t][c][h + 2],
+                         (uint32_t)wf[t][c][h + 3]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        v8i f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = 0;
+        if (tv(t)) {
+          const uint8_t* src = wst + (4 * nv * (r >> 2) + 4 * t + (r & 3)) * kWst + 16 * g;
+          const uint4 a = *reinterpret_cast<const uint4*>(src);
+          const uint4 b = *reinterpret_cast<const uint4*>(src + 64);
+          f[0] = (int)a.x; f[1] = (int)a.y; f[2] = (int)a.z; f[3] = (int)a.w;
+          f[4] = (int)b.x; f[5] = (int)b.y; f[6] = (int)b.z; f[7] = (int)b.w;
+        }
+        wf[t][c] = f;
+      }
+    }
+    float msw = 0.0f, mb = 0.0f, ewm = 0.0f;
+    if (MODE == 3) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+#pragma unroll
+        for (int q = 0; q < KP; ++q) wsc[t][q] = 0;
+#pragma unroll
+        for (int c = 0; c < KC; ++c) {
+          wsc[t][c >> 2] |= (uint32_t)wse[t][c] << (8 * (c & 3));
+          if (tv(t) && (FULL || 4 * c + g < kb)) ewm = fmaxf(ewm, (float)wse[t][c]);
+        }
+      }
+    }
+    if (tid < N) {
+      const float b = bf16_lo(cv_b);
+      cvec[tid] = cv_sw;
+      cvec[N + tid] = b;
+      cvec[2 * N + tid] = bf16_lo(cv_g);
+      cvec[3 * N + tid] = bf16_lo(cv_be);
+      msw = cv_sw;
+      mb = fabsf(b);
+    }
+    msw = wave_max_dpp(msw);
+    mb = wave_max_dpp(mb);
+    ewm = wave_max_dpp(ewm);
+    if (lane == 0) {
+      wmx[wave] = msw;
+      wmx[8 + wave] = mb;
+      wmx[16 + wave] = ewm;
+    }
+    // zero the code rows past K (up to the last chunk) and give the padded
+    // MX blocks a unit scale, in both buffers
+    if (!FULL) {
+      const int padb = kcv * 128 - K;  // multiple of 16
+      if (padb > 0) {
+        const int per = padb >> 4;
+        for (int u = tid; u < 2 * kResRows * per; u += kThreads) {
+          const int row = u / per, o = K + 16 * (u - row * per);
+          *reinterpret_cast<uint4*>(codes + row * LDX + o) = make_uint4(0, 0, 0, 0);
+        }
+      }
+      if (MODE == 3) {
+        for (int u = tid; u < 2 * kResRows * XE; u += kThreads) {
+          const int sl = u % XE, c = sl % (4 * KP);  // LDS slot (g, c) holds block 4c+g
+          if (4 * c + sl / (4 * KP) >= kb) xe8[u] = 127;
+        }
+      }
+    }
+  }
+
+  // after the set-up barrier
+  __device__ __forceinline__ void read_bounds() {
+    float msw = 0.0f, mb = 0.0f, ewm = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      msw = fmaxf(msw, wmx[w]);
+      mb = fmaxf(mb, wmx[8 + w]);
+      ewm = fmaxf(ewm, wmx[16 + w]);
+    }
+    const float kk = (448.0f * 448.0f) * (float)K;
+    // launch constants: kept in scalar registers
+    bw = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(MODE == 3 ? ldexpf(kk, (int)ewm - 127) : kk * msw)));
+    bb = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mb)));
+  }
+
+  // ---- GEMM of the tile in code buffer `buf`
+  __device__ __forceinline__ void mma(int buf) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint8_t* brow = codes + (buf * kResRows + r) * LDX + 16 * g;
+    const uint32_t* erow = reinterpret_cast<const uint32_t*>(xe8 + (buf * kResRows + r) * XE + g * (4 * KP));
+    uint32_t xsw[KP];
+    if (MODE == 3) {
+#pragma unroll
+      for (int q = 0; q < KP; ++q) xsw[q] = erow[q];
+    }
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+      if (!FULL && c >= kcv) break;
+      const uint4 a = *reinterpret_cast<const uint4*>(brow + c * 128);
+      const uint4 b = *reinterpret_cast<const uint4*>(brow + c * 128 + 64);
+      v8i xf;
+      xf[0] = (int)a.x; xf[1] = (int)a.y; xf[2] = (int)a.z; xf[3] = (int)a.w;
+      xf[4] = (int)b.x; xf[5] = (int)b.y; xf[6] = (int)b.z; xf[7] = (int)b.w;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        if (MODE == 3)
+          acc[t] = mfma_mx_sel(c & 3, wf[t][c], xf, acc[t], wsc[t][c >> 2], xsw[c >> 2]);
+        else
+          acc[t] = mfma_fp8<0, 0>(wf[t][c], xf, acc[t]);
+      }
+      // keep at most two chunks of B fragments in flight (with 8 chunks the
+      // scheduler would otherwise hoist every LDS read and spill)
+      if (KC > 4 && (c & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // ---- epilogue, part 1: z = dequant(acc) + b in place; this slice's row
+  // sum and centred sum of squares to LDS
+  __device__ __forceinline__ void epilogue_stats(int buf) {
+    const float rsv = rs[buf * kResRows + r];
+    const float sx = MODE == 1 ? rsv : (MODE == 0 ? p.x_s : 1.0f);
+    const float bound = MODE == 3 ? ldexpf(bw, (int)rsv - 127) + bb : sx * bw + bb;
+    cs = row_rescale(bound);
+    scaled = __builtin_amdgcn_ballot_w64(cs != 1.0f) != 0;
+    const float* cb = cvec + c0 + 4 * nv * g;
+    float s = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if (tv(t)) {
+        const float4 sw4 = *reinterpret_cast<const float4*>(cb + 4 * t);
+        const float4 b4 = *reinterpret_cast<const float4*>(cb + N + 4 * t);
+        const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float z = MODE == 3 ? acc[t][j] + bv[j] : fmaf(acc[t][j], sx * swv[j], bv[j]);
+          acc[t][j] = z;
+          s += z;
+        }
+      }
+    }
+    s = sum4(s);
+    const float mw = s * inv_nw;
+    float q = 0.0f;
+    if (!scaled) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (tv(t))
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float d = acc[t][j] - mw;
+            q = fmaf(d, d, q);
+          }
+    } else {  // rows too large to square in fp32 (rare): deviations scaled by cs first
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (tv(t))
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float d = (acc[t][j] - mw) * cs;
+            q = fmaf(d, d, q);
+          }
+    }
+    q = sum4(q);
+    red[(buf * kResRows + r) * kWaves + wave] = make_float2(s, q);  // the row's 4 lanes write the same pair
+  }
+
+  // ---- epilogue, part 2 (after the barrier): combine the slices, normalize, store
+  __device__ __forceinline__ void epilogue_out(int buf, int64_t t) {
+    const float4* rw4 = reinterpret_cast<const float4*>(red + (buf * kResRows + r) * kWaves);
+    float sw_[kWaves], qw_[kWaves];
+#pragma unroll
+    for (int i = 0; i < kWaves / 2; ++i) {
+      const float4 u = rw4[i];
+      sw_[2 * i] = u.x; qw_[2 * i] = u.y; sw_[2 * i + 1] = u.z; qw_[2 * i + 1] = u.w;
+    }
+    float S = 0.0f, Q = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      S += sw_[w];
+      Q += qw_[w];
+    }
+    const float invn = 1.0f / (float)N;
+    const float mean = S * invn;
+    // between-slice term: sum_w (s_w - n_w mean)^2 / n_w, with the
+    // deviations scaled by cs first on the (rare) rescaled path, like the
+    // within-slice sums
+    float B = 0.0f;
+    const float dsc = scaled ? cs : 1.0f;
+    if (FULL || N == 128 * NT) {  // every slice has 16*NT columns
+      const float ns = (float)(16 * NT);
+      if (!scaled) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float d = fmaf(-ns, mean, sw_[w]);
+          B = fmaf(d, d, B);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float d = fmaf(-ns, mean, sw_[w]) * dsc;
+          B = fmaf(d, d, B);
+        }
+      }
+      B *= 1.0f / ns;
+    } else {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int nw = 16 * min(max(T16 - w * NT, 0), NT);
+        if (nw > 0) {
+          const float d = fmaf(-(float)nw, mean, sw_[w]) * dsc;
+          B = fmaf(d * (1.0f / (float)nw), d, B);
+        }
+      }
+    }
+    const float rstd = !scaled ? __builtin_amdgcn_rsqf(fmaf(Q + B, invn, p.eps))
+                               : cs * __builtin_amdgcn_rsqf(fmaf(Q + B, invn, p.eps * cs * cs));
+    const int64_t m = t * kResRows + r;
+    if (m >= p.M) return;
+    if (OPT && wave == 0 && g == 0) {
+      if (p.mean) p.mean[m] = mean;
+      if (p.rstd) p.rstd[m] = rstd;
+    }
+    const float nmr = -mean * rstd;
+    const int cl = c0 + 4 * nv * g;  // this lane's first column
+    const float* gb = cvec + 2 * N + cl;
+    uint32_t packed[NT][2];
+#pragma unroll
+    for (int t2 = 0; t2 < NT; ++t2) {
+      packed[t2][0] = packed[t2][1] = 0u;
+      if (tv(t2)) {
+        const float4 ga = *reinterpret_cast<const float4*>(gb + 4 * t2);
+        const float4 be = *reinterpret_cast<const float4*>(gb + N + 4 * t2);
+        const float gv[4] = {ga.x, ga.y, ga.z, ga.w}, bv[4] = {be.x, be.y, be.z, be.w};
+        float o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o[j] = fmaf(fmaf(acc[t2][j], rstd, nmr), gv[j], bv[j]);
+        packed[t2][0] = pack_bf16_hw(o[0], o[1]);
+        packed[t2][1] = pack_bf16_hw(o[2], o[3]);
+        if (OPT && p.z != nullptr)
+          *reinterpret_cast<float4*>(p.z + m * N + cl + 4 * t2) =
+              make_float4(acc[t2][0], acc[t2][1], acc[t2][2], acc[t2][3]);
+      }
+    }
+    uint16_t* yrow = p.y + m * N + cl;
+    if ((nv & 1) == 0) {  // 16-byte aligned pairs of tiles
+#pragma unroll
+      for (int t2 = 0; t2 + 1 < NT; t2 += 2)
+        if (tv(t2))
+          *reinterpret_cast<uint4*>(yrow + 4 * t2) =
+              make_uint4(packed[t2][0], packed[t2][1], packed[t2 + 1][0], packed[t2 + 1][1]);
+    } else {
+#pragma unroll
+      for (int t2 = 0; t2 < NT; ++t2)
+        if (tv(t2)) *reinterpret_cast<uint2*>(yrow + 4 * t2) = make_uint2(packed[t2][0], packed[t2][1]);
+    }
+  }
+
+  // MFMAs of the current tile interleaved with the VALU work of quantizing
+  // the next one (the MFMAs run on the matrix core while the quantization
+  // issues): one MFMA, then a few VALU instructions, repeatedly
+  __device__ __forceinline__ void interleave_hint() {
+#pragma unroll
+    for (int i = 0; i < NT * KC; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+    }
+  }
+
+  // one tile of the loop: GEMM of tile j (buffer j&1) alongside the
+  // quantization of tile j+1 (from slot S1 = (j+1) % D; past the range it
+  // quantizes a stale slot into the unused buffer), then tile j+1+D is
+  // requested into that slot
+  template <int S1>
+  __device__ __forceinline__ void step(int64_t j) {
+    const int buf = (int)(j & 1);
+    const int64_t t = tb + j;
+    mma(buf);
+    quantize<S1>(t + 1, buf ^ 1);
+    if (FULL && !OPT) interleave_hint();
+    load_x<S1>(t + 1 + D);
+    epilogue_stats(buf);
+    __syncthreads();
+    epilogue_out(buf, t);
+  }
+
+  __device__ __forceinline__ void run() {
+    if (tb >= te) return;
+    if (OPT && MODE == 0 && p.sx_out != nullptr && tb == 0 && tid == 0) static_cast<float*>(p.sx_out)[0] = p.x_s;
+    // requests first: X tiles (HBM), the weight slice (L2-resident after
+    // its first reader), the column vectors; then the work that waits
+    load_x<0>(tb);
+    if (D > 1) load_x<(1 % D)>(tb + 1);
+    if (D > 2) load_x<(2 % D)>(tb + 2);
+    request_weights();
+    quantize<0>(tb, 0);
+    load_x<0>(tb + D);
+    stage_weights();
+    __syncthreads();
+    read_bounds();
+    const int64_t n = te - tb;
+    for (int64_t j = 0; j < n; j += D) {
+      step<1 % D>(j);
+      if (j + 1 >= n) break;
+      step<2 % D>(j + 1);
+      if (D == 2 || j + 2 >= n) continue;
+      step<0>(j + 2);
+    }
+  }
+};
+
+}  // namespace fwd
+}  // namespace loka
