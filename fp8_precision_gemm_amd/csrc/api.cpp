@@ -215,19 +215,23 @@ loka_status loka_grouped_gemm_fp8_ln(const loka_grouped_args* a, void* stream) {
   if (st != LOKA_OK) return st;
   if (a->num_groups == 0) return LOKA_OK;
   REQUIRE(a->groups != nullptr, LOKA_ERR_INVALID_ARG, "groups is NULL");
+  REQUIRE(a->num_groups <= loka::grouped_max_groups(), LOKA_ERR_UNSUPPORTED, "num_groups %d > %d", a->num_groups,
+          loka::grouped_max_groups());
   int64_t tiles = 0;
   for (int i = 0; i < a->num_groups; ++i) {
     const loka_group_desc& g = a->groups[i];
     st = check_fwd_shape(g.M, g.N, g.K, LOKA_SCALE_ROW);
     if (st != LOKA_OK) return fail(st, "group %d: %s", i, std::string(g_last_error).c_str());
-    REQUIRE(g.N <= 512, LOKA_ERR_UNSUPPORTED, "group %d: the grouped launch supports N <= 512 (N=%lld)", i,
-            (long long)g.N);
+    REQUIRE(loka::fwd_weight_resident(g.N, g.K), LOKA_ERR_UNSUPPORTED,
+            "group %d: the grouped launch needs N <= 512 and K <= 1024 (N <= 256), 640 (N <= 384) or 512 "
+            "(N <= 512); got N=%lld K=%lld",
+            i, (long long)g.N, (long long)g.K);
     if (g.M > 0)
       REQUIRE(g.x && g.qw && g.sw && g.y, LOKA_ERR_INVALID_ARG, "group %d: x, qw, sw and y are required", i);
     REQUIRE(aligned16(g.x) && aligned16(g.qw) && aligned16(g.sw) && aligned16(g.bias) && aligned16(g.gamma) &&
                 aligned16(g.beta) && aligned16(g.y) && aligned16(g.z),
             LOKA_ERR_ALIGNMENT, "group %d: a pointer is not 16-byte aligned", i);
-    tiles += (g.M + 63) / 64;
+    tiles += (g.M + 15) / 16;
   }
   REQUIRE(tiles < ((int64_t)1 << 31), LOKA_ERR_UNSUPPORTED, "too many tiles");
   if ((st = check_workspace(loka_grouped_workspace_size(a), a->workspace, a->workspace_bytes)) != LOKA_OK) return st;

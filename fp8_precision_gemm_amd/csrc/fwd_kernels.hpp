@@ -59,8 +59,8 @@ hipError_t launch_res_t(const FwdBlock& p, const float* partials, int np, int gr
   const size_t lds = (size_t)res_lds(NT, p.N).total;
   const bool opt = p.z != nullptr || p.mean != nullptr || p.rstd != nullptr || p.qx_out != nullptr ||
                    p.sx_out != nullptr;
-  // whole column tiles per wavefront and whole 256-column pieces per lane
-  const bool full = p.N == 128 * NT && p.K == 256 * Res<NT>::KQ;
+  // whole column tiles per wavefront, whole 256-column pieces per lane, whole 16-row tiles
+  const bool full = p.N == 128 * NT && p.K == 256 * Res<NT>::KQ && p.M % kResRows == 0;
   auto kern = opt ? (full ? k_fwd_res<MODE, NT, true, true> : k_fwd_res<MODE, NT, true, false>)
                   : (full ? k_fwd_res<MODE, NT, false, true> : k_fwd_res<MODE, NT, false, false>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -65,7 +65,7 @@ template <int NT>
 struct Res {
   static constexpr int KC = NT <= 2 ? 8 : (NT == 3 ? 5 : 4);  // 128-deep K chunks held
   static constexpr int KQ = (KC * 128 + 255) / 256;           // 16-byte X loads per lane (32 lanes per row)
-  static constexpr int D = KQ <= 2 ? 3 : 2;                    // tiles of X requested ahead
+  static constexpr int D = 2;                                  // tiles of X requested ahead
   static constexpr int LDX = KC * 128 + 16;                    // LDS code row stride (bytes)
   static constexpr int KP = (KC + 3) / 4;                     // E8M0 words per lane group
   static constexpr int XE = 16 * KP;                           // E8M0 bytes per LDS row ([g][KP words])
@@ -150,8 +150,9 @@ __device__ __forceinline__ v4f mfma_mx_sel(int sel, const v8i& a, const v8i& b, 
 
 // OPT: the optional outputs (fp32 Z, mean/rstd, the X codes and scales) are
 // requested; the variant without them carries none of their branches.
-// FULL: N = 128*NT and K = 256*KQ, so every wavefront owns NT whole column
-// tiles and every lane a whole share of each row: no partial-shape guards.
+// FULL: N = 128*NT, K = 256*KQ and M a multiple of 16, so every wavefront
+// owns NT whole column tiles, every lane a whole share of each row and every
+// tile 16 real rows: no partial-shape guards.
 template <int MODE, int NT, bool OPT, bool FULL>
 struct ResBlock {
   using R = Res<NT>;
@@ -173,9 +174,11 @@ struct ResBlock {
   v8i wf[NT][KC];
   uint32_t wsc[NT][KP];
   uint4 xr[D][KQ];
-  v4f acc[NT];
-  float cs;       // this lane's row rescale factor (power of two)
-  bool scaled;    // some row of this wavefront's tile needs cs != 1
+  // two accumulator sets: the GEMM of tile j fills one while the epilogue
+  // of tile j-1 reads the other
+  v4f acc0[NT], acc1[NT];
+  float cs0, cs1;   // per set: this lane's row rescale factor (power of two)
+  bool sc0, sc1;    // per set: some row of the wavefront's tile needs cs != 1
   // set-up values in flight: this thread's column (tid < N) and the MX scale bytes
   float cv_sw;
   uint16_t cv_b, cv_g, cv_be;
@@ -449,7 +452,7 @@ struct ResBlock {
   }
 
   // ---- GEMM of the tile in code buffer `buf`
-  __device__ __forceinline__ void mma(int buf) {
+  __device__ __forceinline__ void mma(int buf, v4f (&acc)[NT]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
     const uint8_t* brow = codes + (buf * kResRows + r) * LDX + 16 * g;
@@ -482,7 +485,7 @@ struct ResBlock {
 
   // ---- epilogue, part 1: z = dequant(acc) + b in place; this slice's row
   // sum and centred sum of squares to LDS
-  __device__ __forceinline__ void epilogue_stats(int buf) {
+  __device__ __forceinline__ void epilogue_stats(int buf, v4f (&acc)[NT], float& cs, bool& scaled) {
     const float rsv = rs[buf * kResRows + r];
     const float sx = MODE == 1 ? rsv : (MODE == 0 ? p.x_s : 1.0f);
     const float bound = MODE == 3 ? ldexpf(bw, (int)rsv - 127) + bb : sx * bw + bb;
@@ -531,7 +534,7 @@ struct ResBlock {
   }
 
   // ---- epilogue, part 2 (after the barrier): combine the slices, normalize, store
-  __device__ __forceinline__ void epilogue_out(int buf, int64_t t) {
+  __device__ __forceinline__ void epilogue_out(int buf, int64_t t, const v4f (&acc)[NT], float cs, bool scaled) {
     const float4* rw4 = reinterpret_cast<const float4*>(red + (buf * kResRows + r) * kWaves);
     float sw_[kWaves], qw_[kWaves];
 #pragma unroll
@@ -581,7 +584,7 @@ struct ResBlock {
     const float rstd = !scaled ? __builtin_amdgcn_rsqf(fmaf(Q + B, invn, p.eps))
                                : cs * __builtin_amdgcn_rsqf(fmaf(Q + B, invn, p.eps * cs * cs));
     const int64_t m = t * kResRows + r;
-    if (m >= p.M) return;
+    if (!FULL && m >= p.M) return;
     if (OPT && wave == 0 && g == 0) {
       if (p.mean) p.mean[m] = mean;
       if (p.rstd) p.rstd[m] = rstd;
@@ -621,56 +624,70 @@ struct ResBlock {
     }
   }
 
-  // MFMAs of the current tile interleaved with the VALU work of quantizing
-  // the next one (the MFMAs run on the matrix core while the quantization
-  // issues): one MFMA, then a few VALU instructions, repeatedly
+  // MFMAs of the current tile interleaved with the VALU work around them
+  // (the previous tile's normalization and stores, the next tile's
+  // quantization): one MFMA, then a few VALU instructions, repeatedly
   __device__ __forceinline__ void interleave_hint() {
 #pragma unroll
     for (int i = 0; i < NT * KC; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
     }
   }
 
-  // one tile of the loop: GEMM of tile j (buffer j&1) alongside the
-  // quantization of tile j+1 (from slot S1 = (j+1) % D; past the range it
-  // quantizes a stale slot into the unused buffer), then tile j+1+D is
-  // requested into that slot
-  template <int S1>
+  // one tile of the loop (j >= 1): GEMM of tile j into set A alongside the
+  // normalization and stores of tile j-1 (set !A) and the quantization of
+  // tile j+1 (slot S1 = (j+1) % D; past the range it quantizes a stale slot
+  // into the unused buffer); then tile j+1+D is requested into that slot and
+  // tile j's statistics go to LDS
+  template <int S1, int A>
   __device__ __forceinline__ void step(int64_t j) {
     const int buf = (int)(j & 1);
     const int64_t t = tb + j;
-    mma(buf);
+    v4f (&cur)[NT] = A ? acc1 : acc0;
+    v4f (&prev)[NT] = A ? acc0 : acc1;
+    mma(buf, cur);
+    epilogue_out(buf ^ 1, t - 1, prev, A ? cs0 : cs1, A ? sc0 : sc1);
     quantize<S1>(t + 1, buf ^ 1);
     if (FULL && !OPT) interleave_hint();
     load_x<S1>(t + 1 + D);
-    epilogue_stats(buf);
+    epilogue_stats(buf, cur, A ? cs1 : cs0, A ? sc1 : sc0);
     __syncthreads();
-    epilogue_out(buf, t);
   }
 
   __device__ __forceinline__ void run() {
     if (tb >= te) return;
     if (OPT && MODE == 0 && p.sx_out != nullptr && tb == 0 && tid == 0) static_cast<float*>(p.sx_out)[0] = p.x_s;
-    // requests first: X tiles (HBM), the weight slice (L2-resident after
-    // its first reader), the column vectors; then the work that waits
+    // requests first, in the order they are needed (load completions are
+    // counted in issue order): X tile 0 (HBM), the weight slice (L2-resident
+    // after its first reader) and the column vectors, then X tile 1
     load_x<0>(tb);
-    if (D > 1) load_x<(1 % D)>(tb + 1);
-    if (D > 2) load_x<(2 % D)>(tb + 2);
     request_weights();
+    load_x<1>(tb + 1);
     quantize<0>(tb, 0);
     load_x<0>(tb + D);
     stage_weights();
     __syncthreads();
     read_bounds();
+    // tile 0: GEMM alongside the quantization of tile 1
+    mma(0, acc0);
+    quantize<1>(tb + 1, 1);
+    if (FULL && !OPT) interleave_hint();
+    load_x<1>(tb + 1 + D);
+    epilogue_stats(0, acc0, cs0, sc0);
+    __syncthreads();
     const int64_t n = te - tb;
-    for (int64_t j = 0; j < n; j += D) {
-      step<1 % D>(j);
-      if (j + 1 >= n) break;
-      step<2 % D>(j + 1);
-      if (D == 2 || j + 2 >= n) continue;
-      step<0>(j + 2);
+    int64_t j = 1;
+    while (j < n) {
+      step<0, 1>(j);
+      if (++j >= n) break;
+      step<1, 0>(j);
+      ++j;
     }
+    // the last tile's normalization and stores
+    const int64_t l = n - 1;
+    if (l & 1) epilogue_out(1, tb + l, acc1, cs1, sc1);
+    else epilogue_out(0, tb + l, acc0, cs0, sc0);
   }
 };
 

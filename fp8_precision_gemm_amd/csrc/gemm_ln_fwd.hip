@@ -2,6 +2,7 @@
 // fused kernel of the requested recipe (fwd_tensor.hip, fwd_row.hip,
 // fwd_mx.hip hold the kernels; fwd_block.hpp the shared block body).
 #include "fwd_block.hpp"
+#include "fwd_resident.hpp"
 
 namespace loka {
 
@@ -13,6 +14,8 @@ hipError_t launch_tensor(const FwdBlock& p, const float* partials, int np, hipSt
 hipError_t launch_row(const FwdBlock& p, const float* partials, int np, hipStream_t s);
 hipError_t launch_mx(const FwdBlock& p, const float* partials, int np, hipStream_t s);
 }  // namespace fwd
+
+bool fwd_weight_resident(int64_t N, int64_t K) { return N <= 512 && K <= 2048 && fwd::res_fits((int)K, (int)N); }
 
 size_t fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int x_mode) {
   (void)N;

@@ -1,93 +1,240 @@
 // loka_grouped_gemm_fp8_ln: many independent rowwise forwards in one launch.
 //
 // Source: LoKA section I (wide ensembles of small layers); GEM "Generalized
-// Dot-Product Attention" (tile lists precomputed on the CPU, empty tiles
-// skipped) and "Expert Parallelism" (one expert per rank).  Each workgroup
-// finds its group by binary search in the host-built tile table and runs
-// the same block body as the single forward, so every group's output is
-// bit-identical to a single loka_gemm_fp8_ln call.
-#include "fwd_block.hpp"
+// Dot-Product Attention" (tile lists precomputed instead of discovered by
+// every block, empty tiles skipped) and "Expert Parallelism" (one expert per
+// rank).
+//
+// Launches on the caller's stream:
+//  1. k_grouped_plan (one workgroup) reads the group descriptors and writes
+//     the plan into the workspace, per shape class (column tiles per
+//     wavefront NT = ceil(N/128), and whether the shape is the guard-free
+//     FULL case): the first global 16-row tile of every group of the class
+//     (exclusive prefix sums of ceil(M_g/16), other classes counting as
+//     empty) and the first tile of every persistent workgroup, chosen so
+//     that each workgroup gets an equal share of the estimated cost (bytes
+//     moved per tile, 32(K_g+N_g), plus a fixed per-tile term).
+//  2. per class present, k_grouped_res<NT, FULL> (one persistent workgroup
+//     per compute unit) walks its contiguous range of the class's tiles
+//     group by group; for each group it loads that group's weight into
+//     registers and runs exactly the weight-resident block of the single
+//     forward (fwd_resident.hpp) over its tiles of that group.  The per-tile
+//     arithmetic is the same as a single loka_gemm_fp8_ln call's, so every
+//     group's output is bit-identical to one.  (One kernel per class keeps
+//     each kernel's registers to one block variant.)
+#include "fwd_resident.hpp"
 
 namespace loka {
 namespace fwd {
 namespace {
 
-constexpr int kMT = 4;  // 64-row tiles (groups have N <= 512: at most 4 column tiles per wavefront)
+constexpr int kPlanThreads = 1024;
+constexpr int kMaxGroups = 2048;
 
-// tile_start[g] = first workgroup of group g (prefix sums of ceil(M_g / 64)),
-// tile_start[num_groups] = grid size.
-__global__ __launch_bounds__(kThreads) void k_grouped(const GroupDev* groups, const int* tile_start, int num_groups,
-                                                 float eps) {
+// estimated cost of one 16-row tile: bytes of X read and Y written, plus a
+// fixed term for the per-tile reductions and synchronization
+__host__ __device__ inline int64_t tile_cost(int64_t K, int64_t N) { return 32 * (K + N) + 2048; }
+
+constexpr int kClasses = 8;       // NT in 1..4, FULL or not
+constexpr int kMaxGrid = 1024;    // workgroups per class launch
+
+// shape class of a group: 2 (NT - 1) + FULL (the same test as the single forward's)
+__host__ __device__ inline int group_class(int64_t M, int64_t N, int64_t K) {
+  const int nt = res_nt((int)N);
+  const int kq = nt == 1 ? Res<1>::KQ : nt == 2 ? Res<2>::KQ : nt == 3 ? Res<3>::KQ : Res<4>::KQ;
+  const bool full = N == 128 * nt && K == 256 * kq && M % kResRows == 0;
+  return 2 * (nt - 1) + (full ? 1 : 0);
+}
+
+// plan of class c: tile_pre[c][G+1], wg_start[c][kMaxGrid+1]; grid[c] workgroups
+__global__ __launch_bounds__(kPlanThreads) void k_grouped_plan(const GroupDev* groups, int G, int cus,
+                                                                 int* tile_pre, int* wg_start) {
+  __shared__ int64_t cpre[kMaxGroups + 1];   // exclusive prefix of group costs
+  __shared__ int tpre[kMaxGroups + 1];       // exclusive prefix of group tiles
+  __shared__ int64_t ccost[kMaxGroups];      // per-tile cost of each group
+  __shared__ int64_t sc[kPlanThreads];
+  __shared__ int st[kPlanThreads];
+  const int tid = threadIdx.x;
+  for (int cls = 0; cls < kClasses; ++cls) {
+    int64_t carry_c = 0;
+    int carry_t = 0;
+    for (int base = 0; base < G; base += kPlanThreads) {
+      const int i = base + tid;
+      int tiles = 0;
+      int64_t cost = 0;
+      if (i < G) {
+        const GroupDev& gd = groups[i];
+        ccost[i] = tile_cost(gd.K, gd.N);
+        if (group_class(gd.M, gd.N, gd.K) == cls) {
+          tiles = (int)((gd.M + kResRows - 1) / kResRows);
+          cost = (int64_t)tiles * ccost[i];
+        }
+      }
+      sc[tid] = cost;
+      st[tid] = tiles;
+      __syncthreads();
+      for (int o = 1; o < kPlanThreads; o <<= 1) {  // inclusive scan (Hillis-Steele)
+        const int64_t a = tid >= o ? sc[tid - o] : 0;
+        const int b = tid >= o ? st[tid - o] : 0;
+        __syncthreads();
+        sc[tid] += a;
+        st[tid] += b;
+        __syncthreads();
+      }
+      if (i < G) {
+        cpre[i] = carry_c + sc[tid] - cost;
+        tpre[i] = carry_t + st[tid] - tiles;
+      }
+      carry_c += sc[kPlanThreads - 1];
+      carry_t += st[kPlanThreads - 1];
+      __syncthreads();
+    }
+    if (tid == 0) {
+      cpre[G] = carry_c;
+      tpre[G] = carry_t;
+    }
+    __syncthreads();
+    int* tp = tile_pre + cls * (G + 1);
+    int* ws = wg_start + cls * (kMaxGrid + 1);
+    for (int i = tid; i <= G; i += kPlanThreads) tp[i] = tpre[i];
+    // workgroup b starts at the first tile whose starting cost is >= b*C/grid
+    const int64_t C = cpre[G];
+    const int grid = (int)(tpre[G] < cus ? tpre[G] : cus);
+    for (int b = tid; b <= grid; b += kPlanThreads) {
+      int start;
+      if (b == grid) {
+        start = tpre[G];
+      } else {
+        const int64_t x = (C / grid) * b + ((C % grid) * b) / grid;
+        int lo = 0, hi = G - 1;  // last group with cpre[g] <= x
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (cpre[mid] <= x) lo = mid;
+          else hi = mid - 1;
+        }
+        const int tiles_g = tpre[lo + 1] - tpre[lo];
+        int64_t j = tiles_g == 0 ? 0 : (x - cpre[lo] + ccost[lo] - 1) / ccost[lo];
+        if (j > tiles_g) j = tiles_g;
+        start = tpre[lo] + (int)j;
+      }
+      ws[b] = start;
+    }
+    __syncthreads();  // cpre/tpre are rebuilt for the next class
+  }
+}
+
+template <bool OPT, int NT, bool FULL>
+__global__ __launch_bounds__(kThreads) void k_grouped_res(const GroupDev* groups, const int* tile_pre,
+                                                          const int* wg_start, int G, float eps) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int b = blockIdx.x;
-  int lo = 0, hi = num_groups - 1;  // last group with tile_start <= b (skips empty groups)
+  int t = wg_start[blockIdx.x];
+  const int tend = wg_start[blockIdx.x + 1];
+  int lo = 0, hi = G - 1;  // last group with tile_pre[g] <= t
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (tile_start[mid] <= b) lo = mid;
+    if (tile_pre[mid] <= t) lo = mid;
     else hi = mid - 1;
   }
-  const GroupDev gd = groups[lo];
-  FwdBlock p;
-  p.M = gd.M; p.N = (int)gd.N; p.K = (int)gd.K;
-  p.x = static_cast<const uint16_t*>(gd.x);
-  p.qw = gd.qw; p.sw = gd.sw;
-  p.bias = static_cast<const uint16_t*>(gd.bias);
-  p.gamma = static_cast<const uint16_t*>(gd.gamma);
-  p.beta = static_cast<const uint16_t*>(gd.beta);
-  p.y = static_cast<uint16_t*>(gd.y);
-  p.z = gd.z;
-  p.mean = nullptr; p.rstd = nullptr; p.qx_out = nullptr; p.sx_out = nullptr;
-  p.eps = eps; p.x_r = 1.0f; p.x_s = 1.0f;
-  const int64_t m0 = (int64_t)(b - tile_start[lo]) * (16 * kMT);
-  switch ((p.N + 127) / 128) {  // column tiles per wavefront
-    case 1: fwd_block<1, 1, kMT, false>(p, m0, smem); break;
-    case 2: fwd_block<1, 2, kMT, false>(p, m0, smem); break;
-    case 3: fwd_block<1, 3, kMT, false>(p, m0, smem); break;
-    case 4: fwd_block<1, 4, kMT, false>(p, m0, smem); break;
-    default: break;
+  int g = lo;
+  while (t < tend) {
+    while (tile_pre[g + 1] <= t) ++g;  // past finished groups and those of other classes
+    const int seg_end = min(tend, tile_pre[g + 1]);
+    const GroupDev gd = groups[g];
+    FwdBlock p;
+    p.M = gd.M; p.N = (int)gd.N; p.K = (int)gd.K;
+    p.x = static_cast<const uint16_t*>(gd.x);
+    p.qw = gd.qw; p.sw = gd.sw;
+    p.bias = static_cast<const uint16_t*>(gd.bias);
+    p.gamma = static_cast<const uint16_t*>(gd.gamma);
+    p.beta = static_cast<const uint16_t*>(gd.beta);
+    p.y = static_cast<uint16_t*>(gd.y);
+    p.z = gd.z;
+    p.mean = nullptr; p.rstd = nullptr; p.qx_out = nullptr; p.sx_out = nullptr;
+    p.eps = eps; p.x_r = 1.0f; p.x_s = 1.0f;
+    ResBlock<1, NT, OPT, FULL> blk(p, t - tile_pre[g], seg_end - tile_pre[g], smem);
+    blk.run();
+    __syncthreads();  // the next group's set-up rewrites the LDS
+    t = seg_end;
   }
+}
+
+template <bool OPT, int NT, bool FULL>
+hipError_t launch_class(const GroupDev* dg, const int* tp, const int* ws, int G, int grid, size_t lds, float eps,
+                        hipStream_t s) {
+  auto kern = k_grouped_res<OPT, NT, FULL>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, s, dg, tp, ws, G, eps);
+  return hipGetLastError();
 }
 
 }  // namespace
 }  // namespace fwd
 
+int grouped_max_groups() { return fwd::kMaxGroups; }
+
+// workspace: [ descriptors | tile_pre [8][G+1] | wg_start [8][1025] ]
 size_t grouped_workspace_bytes(int num_groups, const GroupDev* groups) {
   (void)groups;
-  size_t b = (size_t)num_groups * sizeof(GroupDev);
-  b = (b + 255) / 256 * 256;
-  b += (size_t)(num_groups + 1) * sizeof(int);
+  size_t b = ((size_t)num_groups * sizeof(GroupDev) + 255) / 256 * 256;
+  b += ((size_t)fwd::kClasses * (num_groups + 1) * sizeof(int) + 255) / 256 * 256;
+  b += (size_t)fwd::kClasses * (fwd::kMaxGrid + 1) * sizeof(int);
   return b;
 }
 
 hipError_t launch_grouped(const GroupedLaunch& a, hipStream_t s) {
-  constexpr int BM = 16 * fwd::kMT;
-  // host-built tile table: prefix sums of ceil(M_g / BM); empty groups get no tiles
-  int* starts = new int[a.num_groups + 1];
-  int total = 0;
-  size_t lds = 0;
-  for (int gi = 0; gi < a.num_groups; ++gi) {
-    starts[gi] = total;
-    total += (int)((a.groups[gi].M + BM - 1) / BM);
-    const size_t l = fwd::fwd_lds_bytes(BM, (int)a.groups[gi].K, (int)a.groups[gi].N);
-    if (l > lds) lds = l;
+  const int G = a.num_groups;
+  int64_t tiles[fwd::kClasses] = {0};
+  size_t lds[fwd::kClasses] = {0};
+  bool opt = false;
+  for (int gi = 0; gi < G; ++gi) {
+    const GroupDev& gd = a.groups[gi];
+    const int c = fwd::group_class(gd.M, gd.N, gd.K);
+    tiles[c] += (gd.M + fwd::kResRows - 1) / fwd::kResRows;
+    const size_t l = (size_t)fwd::res_lds(fwd::res_nt((int)gd.N), (int)gd.N).total;
+    if (l > lds[c]) lds[c] = l;
+    if (gd.z != nullptr) opt = true;
   }
-  starts[a.num_groups] = total;
-  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
-  const size_t gbytes = ((size_t)a.num_groups * sizeof(GroupDev) + 255) / 256 * 256;
-  GroupDev* dgroups = reinterpret_cast<GroupDev*>(ws);
-  int* dstarts = reinterpret_cast<int*>(ws + gbytes);
-  // pageable host sources: the runtime stages them before these calls return
-  hipError_t e = hipMemcpyAsync(dgroups, a.groups, (size_t)a.num_groups * sizeof(GroupDev), hipMemcpyHostToDevice, s);
-  if (e == hipSuccess)
-    e = hipMemcpyAsync(dstarts, starts, (size_t)(a.num_groups + 1) * sizeof(int), hipMemcpyHostToDevice, s);
-  delete[] starts;
-  if (e != hipSuccess) return e;
+  int64_t total = 0;
+  for (int c = 0; c < fwd::kClasses; ++c) total += tiles[c];
   if (total == 0) return hipSuccess;
-  e = hipFuncSetAttribute(reinterpret_cast<const void*>(fwd::k_grouped), hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds);
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  const size_t gbytes = ((size_t)G * sizeof(GroupDev) + 255) / 256 * 256;
+  const size_t tbytes = ((size_t)fwd::kClasses * (G + 1) * sizeof(int) + 255) / 256 * 256;
+  GroupDev* dgroups = reinterpret_cast<GroupDev*>(ws);
+  int* tile_pre = reinterpret_cast<int*>(ws + gbytes);
+  int* wg_start = reinterpret_cast<int*>(ws + gbytes + tbytes);
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(fwd::k_grouped, dim3((unsigned)total), dim3(fwd::kThreads), lds, s, dgroups, dstarts, a.num_groups, a.eps);
-  return hipGetLastError();
+  if (cus > fwd::kMaxGrid) cus = fwd::kMaxGrid;
+  // the caller's descriptor array is the copy's source (it must stay valid
+  // until the copy has run)
+  e = hipMemcpyAsync(dgroups, a.groups, (size_t)G * sizeof(GroupDev), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(fwd::k_grouped_plan, dim3(1), dim3(fwd::kPlanThreads), 0, s, dgroups, G, cus, tile_pre,
+                     wg_start);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int c = 0; c < fwd::kClasses && e == hipSuccess; ++c) {
+    if (tiles[c] == 0) continue;
+    const int grid = (int)(tiles[c] < cus ? tiles[c] : cus);
+    const int* tp = tile_pre + c * (G + 1);
+    const int* wsc = wg_start + c * (fwd::kMaxGrid + 1);
+#define LOKA_CLASS(C, NT, FULL)                                                                              \
+  case C:                                                                                                   \
+    e = opt ? fwd::launch_class<true, NT, FULL>(dgroups, tp, wsc, G, grid, lds[c], a.eps, s)                \
+            : fwd::launch_class<false, NT, FULL>(dgroups, tp, wsc, G, grid, lds[c], a.eps, s);              \
+    break;
+    switch (c) {
+      LOKA_CLASS(0, 1, false) LOKA_CLASS(1, 1, true) LOKA_CLASS(2, 2, false) LOKA_CLASS(3, 2, true)
+      LOKA_CLASS(4, 3, false) LOKA_CLASS(5, 3, true) LOKA_CLASS(6, 4, false) LOKA_CLASS(7, 4, true)
+      default: break;
+    }
+#undef LOKA_CLASS
+  }
+  return e;
 }
 
 }  // namespace loka

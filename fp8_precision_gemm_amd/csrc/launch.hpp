@@ -98,6 +98,10 @@ struct GroupedLaunch {
   void* workspace;         // device
 };
 size_t grouped_workspace_bytes(int num_groups, const GroupDev* groups);
+int grouped_max_groups();
+// Does a forward of this shape fit the weight-resident kernel (K*N <= 256 KiB
+// of codes held in registers, N <= 512)?  Every group of a grouped launch must.
+bool fwd_weight_resident(int64_t N, int64_t K);
 hipError_t launch_grouped(const GroupedLaunch& a, hipStream_t s);
 
 }  // namespace loka

@@ -268,9 +268,16 @@ loka_status loka_gemm_fp8_bwd(const loka_bwd_args* args, void* stream);
  *           library copies the descriptors and the tile table into it with
  *           an asynchronous host-to-device copy on `stream`, so it must not
  *           be reused until the launch has completed.
+ *   The workspace also receives the launch plan (each group's first tile
+ *   and each workgroup's share), computed on the device from the copied
+ *   descriptors.  For graph capture the host array must stay valid and
+ *   unchanged for every replay.
  * Each group's output is bit-identical to a single loka_gemm_fp8_ln call
- * with the same inputs.  Requirements: as loka_gemm_fp8_ln, with N <= 512
- * for every group (LOKA_ERR_UNSUPPORTED otherwise).
+ * with the same inputs.  Requirements: as loka_gemm_fp8_ln, with
+ * num_groups <= 2048 and every group's weight small enough to stay in
+ * registers: N <= 512 and K <= 1024 (N <= 256), 640 (N <= 384) or 512
+ * (N <= 512); LOKA_ERR_UNSUPPORTED otherwise (run such groups as single
+ * calls).
  * ---------------------------------------------------------------------- */
 typedef struct {
   int64_t M, N, K;
