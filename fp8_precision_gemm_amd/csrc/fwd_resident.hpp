@@ -65,7 +65,12 @@ template <int NT>
 struct Res {
   static constexpr int KC = NT <= 2 ? 8 : (NT == 3 ? 5 : 4);  // 128-deep K chunks held
   static constexpr int KQ = (KC * 128 + 255) / 256;           // 16-byte X loads per lane (32 lanes per row)
-  static constexpr int D = 2;                                  // tiles of X requested ahead
+  // software pipeline (two accumulator sets: the next tile's GEMM overlaps
+  // the previous tile's normalization) where the registers allow it, i.e.
+  // with at most 4 resident K chunks; deeper K runs the steps one after
+  // another with one slot of X in flight
+  static constexpr bool PIPE = KC <= 4;
+  static constexpr int D = PIPE ? 2 : 1;                       // tiles of X requested ahead
   static constexpr int LDX = KC * 128 + 16;                    // LDS code row stride (bytes)
   static constexpr int KP = (KC + 3) / 4;                     // E8M0 words per lane group
   static constexpr int XE = 16 * KP;                           // E8M0 bytes per LDS row ([g][KP words])
@@ -157,6 +162,7 @@ template <int MODE, int NT, bool OPT, bool FULL>
 struct ResBlock {
   using R = Res<NT>;
   static constexpr int KC = R::KC, KQ = R::KQ, D = R::D, LDX = R::LDX, XE = R::XE, KP = R::KP;
+  static constexpr bool PIPE = R::PIPE;
 
   const FwdBlock& p;
   int64_t tb, te;  // tile range [tb, te)
@@ -655,6 +661,20 @@ struct ResBlock {
     __syncthreads();
   }
 
+  // one tile without the pipeline (deep K): GEMM of tile j, quantization of
+  // tile j+1 from the single slot, request of tile j+2, statistics, barrier,
+  // normalization and stores
+  __device__ __forceinline__ void step_seq(int64_t j) {
+    const int buf = (int)(j & 1);
+    const int64_t t = tb + j;
+    mma(buf, acc0);
+    quantize<0>(t + 1, buf ^ 1);
+    load_x<0>(t + 2);
+    epilogue_stats(buf, acc0, cs0, sc0);
+    __syncthreads();
+    epilogue_out(buf, t, acc0, cs0, sc0);
+  }
+
   __device__ __forceinline__ void run() {
     if (tb >= te) return;
     if (OPT && MODE == 0 && p.sx_out != nullptr && tb == 0 && tid == 0) static_cast<float*>(p.sx_out)[0] = p.x_s;
@@ -663,17 +683,21 @@ struct ResBlock {
     // after its first reader) and the column vectors, then X tile 1
     load_x<0>(tb);
     request_weights();
-    load_x<1>(tb + 1);
+    if (PIPE) load_x<(1 % D)>(tb + 1);
     quantize<0>(tb, 0);
     load_x<0>(tb + D);
     stage_weights();
     __syncthreads();
     read_bounds();
+    if (!PIPE) {
+      for (int64_t j = 0; j < te - tb; ++j) step_seq(j);
+      return;
+    }
     // tile 0: GEMM alongside the quantization of tile 1
     mma(0, acc0);
-    quantize<1>(tb + 1, 1);
+    quantize<(1 % D)>(tb + 1, 1);
     if (FULL && !OPT) interleave_hint();
-    load_x<1>(tb + 1 + D);
+    load_x<(1 % D)>(tb + 1 + D);
     epilogue_stats(0, acc0, cs0, sc0);
     __syncthreads();
     const int64_t n = te - tb;
@@ -681,7 +705,7 @@ struct ResBlock {
     while (j < n) {
       step<0, 1>(j);
       if (++j >= n) break;
-      step<1, 0>(j);
+      step<(1 % D), 0>(j);
       ++j;
     }
     // the last tile's normalization and stores
