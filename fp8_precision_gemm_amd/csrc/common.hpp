@@ -180,4 +180,26 @@ __device__ __forceinline__ v8i load_frag(const uint8_t* p, int g, int kc, int li
   return f;
 }
 
+// Fragment-interleaved layout of an [R][C] byte matrix (R a multiple of 16,
+// C padded with zeros to a multiple of 128), internal to the backward: the
+// 16 x 128 block (R/16, C/128) is 2 KiB holding its eight 16-byte column
+// pieces one after another, each piece being the 16 rows' bytes side by
+// side.  An MFMA operand fragment (lane (r, g) reading pieces g and g+4 of
+// row r) then reads 256 contiguous bytes per 16 lanes instead of 16 scattered
+// rows.
+__host__ __device__ inline size_t ilv_offset(int64_t row, int64_t col, int64_t nch) {
+  return ((size_t)((row >> 4) * nch + (col >> 7)) * 8 + (size_t)((col & 127) >> 4)) * 256 + (size_t)(row & 15) * 16 +
+         (size_t)(col & 15);
+}
+// Fragment of row tile rt (rows 16 rt .. +16), 128-column chunk c.
+__device__ __forceinline__ v8i load_frag_ilv(const uint8_t* base, int64_t rt, int64_t c, int64_t nch, int r, int g) {
+  const uint8_t* b = base + (size_t)(rt * nch + c) * 2048 + r * 16;
+  const uint4 x = *reinterpret_cast<const uint4*>(b + g * 256);
+  const uint4 y = *reinterpret_cast<const uint4*>(b + (4 + g) * 256);
+  v8i f;
+  f[0] = (int)x.x; f[1] = (int)x.y; f[2] = (int)x.z; f[3] = (int)x.w;
+  f[4] = (int)y.x; f[5] = (int)y.y; f[6] = (int)y.z; f[7] = (int)y.w;
+  return f;
+}
+
 }  // namespace loka

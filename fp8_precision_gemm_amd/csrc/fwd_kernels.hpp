@@ -39,7 +39,7 @@ hipError_t launch_t(const FwdBlock& p, const float* partials, int np, hipStream_
 }
 
 
-template <int MODE, int NT, bool OPT, bool FULL>
+template <int MODE, int NT, int KC, bool OPT, bool FULL>
 __global__ __launch_bounds__(kThreads) void k_fwd_res(FwdBlock p, const float* partials, int np) {
   extern __shared__ __align__(16) uint8_t smem[];
   if (MODE == 0) {
@@ -50,19 +50,18 @@ __global__ __launch_bounds__(kThreads) void k_fwd_res(FwdBlock p, const float* p
   }
   // a contiguous, balanced range of 16-row tiles per workgroup
   const int64_t T = (p.M + kResRows - 1) / kResRows, G = gridDim.x, b = blockIdx.x;
-  ResBlock<MODE, NT, OPT, FULL> blk(p, b * T / G, (b + 1) * T / G, smem);
+  ResBlock<MODE, NT, KC, OPT, FULL> blk(p, b * T / G, (b + 1) * T / G, smem);
   blk.run();
 }
 
-template <int MODE, int NT>
+template <int MODE, int NT, int KC>
 hipError_t launch_res_t(const FwdBlock& p, const float* partials, int np, int grid, hipStream_t s) {
-  const size_t lds = (size_t)res_lds(NT, p.N).total;
+  const size_t lds = (size_t)res_lds(NT, KC, p.N).total;
   const bool opt = p.z != nullptr || p.mean != nullptr || p.rstd != nullptr || p.qx_out != nullptr ||
                    p.sx_out != nullptr;
-  // whole column tiles per wavefront, whole 256-column pieces per lane, whole 16-row tiles
-  const bool full = p.N == 128 * NT && p.K == 256 * Res<NT>::KQ && p.M % kResRows == 0;
-  auto kern = opt ? (full ? k_fwd_res<MODE, NT, true, true> : k_fwd_res<MODE, NT, true, false>)
-                  : (full ? k_fwd_res<MODE, NT, false, true> : k_fwd_res<MODE, NT, false, false>);
+  const bool full = res_full(p.M, p.N, p.K, NT, KC);
+  auto kern = opt ? (full ? k_fwd_res<MODE, NT, KC, true, true> : k_fwd_res<MODE, NT, KC, true, false>)
+                  : (full ? k_fwd_res<MODE, NT, KC, false, true> : k_fwd_res<MODE, NT, KC, false, false>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -90,11 +89,19 @@ hipError_t launch_mode(const FwdBlock& p, const float* partials, int np, hipStre
     int grid = 0;
     hipError_t e = res_grid(p.M, &grid);
     if (e != hipSuccess) return e;
-    switch (res_nt(p.N)) {
-      case 1: return launch_res_t<MODE, 1>(p, partials, np, grid, s);
-      case 2: return launch_res_t<MODE, 2>(p, partials, np, grid, s);
-      case 3: return launch_res_t<MODE, 3>(p, partials, np, grid, s);
-      case 4: return launch_res_t<MODE, 4>(p, partials, np, grid, s);
+    const int nt = res_nt(p.N);
+    switch (res_shape(nt, res_kc(nt, p.K))) {
+      case 0: return launch_res_t<MODE, 1, 2>(p, partials, np, grid, s);
+      case 1: return launch_res_t<MODE, 1, 4>(p, partials, np, grid, s);
+      case 2: return launch_res_t<MODE, 1, 8>(p, partials, np, grid, s);
+      case 3: return launch_res_t<MODE, 2, 2>(p, partials, np, grid, s);
+      case 4: return launch_res_t<MODE, 2, 4>(p, partials, np, grid, s);
+      case 5: return launch_res_t<MODE, 2, 8>(p, partials, np, grid, s);
+      case 6: return launch_res_t<MODE, 3, 2>(p, partials, np, grid, s);
+      case 7: return launch_res_t<MODE, 3, 4>(p, partials, np, grid, s);
+      case 8: return launch_res_t<MODE, 3, 5>(p, partials, np, grid, s);
+      case 9: return launch_res_t<MODE, 4, 2>(p, partials, np, grid, s);
+      case 10: return launch_res_t<MODE, 4, 4>(p, partials, np, grid, s);
       default: return hipErrorInvalidValue;
     }
   }

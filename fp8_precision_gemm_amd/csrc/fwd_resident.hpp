@@ -59,17 +59,18 @@ namespace fwd {
 constexpr int kResRows = 16;  // rows per tile
 constexpr int kWst = 144;     // weight staging row stride (bytes): 128-byte chunk + 16 pad
 
-// Per-wavefront tile count NT (N <= 128*NT) fixes the K capacity: NT*KC
-// fragments of 8 VGPRs stay within 128 registers.
-template <int NT>
+// Shapes: NT column tiles per wavefront (N <= 128*NT) and KC resident 128-deep
+// K chunks (K <= 128*KC); NT*KC fragments of 8 VGPRs stay within 128
+// registers.  Instantiated chunk counts: 2, 4 and the per-NT maximum (8, 8,
+// 5, 4), so a small K keeps a small weight footprint.
+template <int NT, int KC>
 struct Res {
-  static constexpr int KC = NT <= 2 ? 8 : (NT == 3 ? 5 : 4);  // 128-deep K chunks held
   static constexpr int KQ = (KC * 128 + 255) / 256;           // 16-byte X loads per lane (32 lanes per row)
   // software pipeline (two accumulator sets: the next tile's GEMM overlaps
-  // the previous tile's normalization) where the registers allow it, i.e.
-  // with at most 4 resident K chunks; deeper K runs the steps one after
-  // another with one slot of X in flight
-  static constexpr bool PIPE = KC <= 4;
+  // the previous tile's normalization) where the registers allow it; the
+  // largest weights run the steps one after another with one slot of X in
+  // flight
+  static constexpr bool PIPE = NT * KC <= 12 || (NT == 4 && KC == 4);
   static constexpr int D = PIPE ? 2 : 1;                       // tiles of X requested ahead
   static constexpr int LDX = KC * 128 + 16;                    // LDS code row stride (bytes)
   static constexpr int KP = (KC + 3) / 4;                     // E8M0 words per lane group
@@ -77,10 +78,27 @@ struct Res {
 };
 
 __host__ __device__ constexpr int res_nt(int N) { return (N + 127) / 128; }
-__host__ __device__ constexpr int res_kc(int nt) { return nt <= 2 ? 8 : (nt == 3 ? 5 : 4); }
+__host__ __device__ constexpr int res_kc_max(int nt) { return nt <= 2 ? 8 : (nt == 3 ? 5 : 4); }
+// the instantiated chunk count for K: 2, 4, else the maximum
+__host__ __device__ constexpr int res_kc(int nt, int K) {
+  return (K + 127) / 128 <= 2 ? 2 : ((K + 127) / 128 <= 4 ? 4 : res_kc_max(nt));
+}
 // Does (K, N) fit the weight-resident kernel?
 __host__ __device__ constexpr bool res_fits(int K, int N) {
-  return N >= 16 && N <= 512 && N % 16 == 0 && K >= 16 && K % 16 == 0 && (K + 127) / 128 <= res_kc(res_nt(N));
+  return N >= 16 && N <= 512 && N % 16 == 0 && K >= 16 && K % 16 == 0 && (K + 127) / 128 <= res_kc_max(res_nt(N));
+}
+// FULL shape (no partial-shape guards): whole column tiles per wavefront,
+// whole 256-column pieces per lane, whole 16-row tiles
+__host__ __device__ constexpr bool res_full(int64_t M, int N, int K, int nt, int kc) {
+  return N == 128 * nt && K == 256 * ((kc * 128 + 255) / 256) && M % 16 == 0;
+}
+// the instantiated (NT, KC) pairs, numbered 0..10
+constexpr int kResShapes = 11;
+__host__ __device__ constexpr int res_shape(int nt, int kc) {
+  return nt == 1 ? (kc == 2 ? 0 : kc == 4 ? 1 : 2)
+       : nt == 2 ? (kc == 2 ? 3 : kc == 4 ? 4 : 5)
+       : nt == 3 ? (kc == 2 ? 6 : kc == 4 ? 7 : 8)
+                 : (kc == 2 ? 9 : 10);
 }
 
 // LDS carve-up (bytes, every part 16-byte aligned):
@@ -90,8 +108,8 @@ __host__ __device__ constexpr bool res_fits(int K, int N) {
 struct ResLds {
   int codes, xe8, rs, red, cvec, wmx, wst, total;
 };
-__host__ __device__ inline ResLds res_lds(int nt, int N) {
-  const int kc = res_kc(nt), ldx = kc * 128 + 16, xe = 16 * ((kc + 3) / 4);
+__host__ __device__ inline ResLds res_lds(int nt, int kc, int N) {
+  const int ldx = kc * 128 + 16, xe = 16 * ((kc + 3) / 4);
   ResLds l;
   l.codes = 0;
   l.xe8 = l.codes + 2 * kResRows * ldx;
@@ -158,10 +176,10 @@ __device__ __forceinline__ v4f mfma_mx_sel(int sel, const v8i& a, const v8i& b, 
 // FULL: N = 128*NT, K = 256*KQ and M a multiple of 16, so every wavefront
 // owns NT whole column tiles, every lane a whole share of each row and every
 // tile 16 real rows: no partial-shape guards.
-template <int MODE, int NT, bool OPT, bool FULL>
+template <int MODE, int NT, int KC, bool OPT, bool FULL>
 struct ResBlock {
-  using R = Res<NT>;
-  static constexpr int KC = R::KC, KQ = R::KQ, D = R::D, LDX = R::LDX, XE = R::XE, KP = R::KP;
+  using R = Res<NT, KC>;
+  static constexpr int KQ = R::KQ, D = R::D, LDX = R::LDX, XE = R::XE, KP = R::KP;
   static constexpr bool PIPE = R::PIPE;
 
   const FwdBlock& p;
@@ -210,7 +228,7 @@ struct ResBlock {
     nv = FULL ? NT : min(max(T16 - wave * NT, 0), NT);
     c0 = 16 * NT * wave;
     inv_nw = nv > 0 ? 1.0f / (float)(16 * nv) : 0.0f;
-    const ResLds l = res_lds(NT, N);
+    const ResLds l = res_lds(NT, KC, N);
     codes = smem + l.codes;
     xe8 = smem + l.xe8;
     rs = reinterpret_cast<float*>(smem + l.rs);

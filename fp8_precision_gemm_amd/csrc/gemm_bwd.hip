@@ -17,7 +17,13 @@
 //  2. column amax + cast of X (e4m3, transposed to [K, M]);
 //     cast of dZ (e5m2, transposed to [N, M]) with the maxima from step 1.
 //  3. k_wgrad: split-M FP8 MFMA, fp32 partials per M slice.
-//  4. k_finalize: fixed-order sums of the partials (deterministic), scales.
+//  4. k_finalize: fixed-order sums of the partials (deterministic), scales;
+//     k_col_vectors: dgamma, dbeta, dbias from the column partials.
+// Every FP8 operand the kernels read as MFMA fragments straight from memory
+// (both weights, the transposed X and dZ codes) is first laid out in the
+// fragment-interleaved order of ilv_offset(), so each 16-lane fragment load
+// reads 256 contiguous bytes (k_relayout does it for the weights; the
+// transposing casts write it directly).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -26,13 +32,25 @@ namespace loka {
 QuantPlan quant_plan(int64_t rows, int64_t cols, int mode);
 hipError_t launch_cast_col_with_partials(const void* src, int src_dtype, int fmt, int64_t rows, int64_t cols,
                                          int64_t ld, const float* partials, int64_t np, uint8_t* codes_t,
-                                         float* scales, hipStream_t s);
+                                         float* scales, float* mult, hipStream_t s);
 
 namespace {
 
 constexpr int kMT = 4;           // 64 rows per workgroup
 constexpr int kBM = 16 * kMT;
 constexpr int kWgSplitRows = 1024;  // M rows per wgrad slice
+
+// [R][C] row-major bytes -> fragment-interleaved (C padded to 128 with zeros).
+// One thread per 16-byte piece.
+__global__ __launch_bounds__(256) void k_relayout(const uint8_t* src, int R, int C, uint8_t* dst) {
+  const int64_t nch = (C + 127) / 128, pieces = nch * 8;
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= (int64_t)R * pieces) return;
+  const int64_t row = u / pieces, col = (u - row * pieces) * 16;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (col < C) v = *reinterpret_cast<const uint4*>(src + row * C + col);
+  *reinterpret_cast<uint4*>(dst + ilv_offset(row, col, nch)) = v;
+}
 
 struct BwdBlock {
   int64_t M;
@@ -48,6 +66,8 @@ struct BwdBlock {
   const uint16_t* gamma;
   const uint8_t* qw_row;
   const float* sw_row;
+  const uint8_t* qwi;     // qw [N][K] interleaved (K padded to 128)
+  const uint8_t* qwri;    // qw_row [K][N] interleaved (N padded to 128)
   uint16_t* dx;
   float* dz;  // fp32 [M, N] (user buffer or workspace): always written
   uint8_t* dz_codes;
@@ -117,7 +137,7 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
 #pragma unroll
       for (int t = 0; t < NTMAX; ++t) {
         if (t < nt) {
-          const v8i wf = load_frag(p.qw + (int64_t)(nb + 16 * t + r) * K, g, kc, K);
+          const v8i wf = load_frag_ilv(p.qwi, nb / 16 + t, kc >> 7, (K + 127) >> 7, r, g);
 #pragma unroll
           for (int i = 0; i < kMT; ++i) acc[t][i] = mfma_fp8<0, 0>(wf, xf[i], acc[t][i]);
         }
@@ -314,7 +334,7 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
 #pragma unroll
     for (int t = 0; t < KTMAX; ++t) {
       if (t < kt) {
-        const v8i wf = load_frag(p.qw_row + (int64_t)(kb0 + 16 * t + r) * N, g, nc, N);
+        const v8i wf = load_frag_ilv(p.qwri, kb0 / 16 + t, nc >> 7, (N + 127) >> 7, r, g);
 #pragma unroll
         for (int i = 0; i < kMT; ++i) dacc[t][i] = mfma_fp8<0, 1>(wf, df[i], dacc[t][i]);
       }
@@ -346,34 +366,47 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
 // wgrad partials: part[s][k][n] = sum over m in slice s of Xc^T[k][m] * dZc^T[n][m]
 // (codes only).  Workgroup tile 128 (n) x 128 (k); wavefront (wn, wk) in 2 x 2
 // owns 64 x 64 = 4 x 4 MFMA tiles.  A = dZc^T rows n (e5m2), B = Xc^T rows k
-// (e4m3), so lane (r, g) holds D[n = 16a + 4g + j][k = 16b + r].
+// (e4m3), both fragment-interleaved with M padded to 128 (zero codes), so
+// lane (r, g) holds D[n = 16a + 4g + j][k = 16b + r].  Slice s covers the
+// 128-row chunks [s * chunks_per_split, +chunks_per_split).
 __global__ __launch_bounds__(256) void k_wgrad(const uint8_t* dzt, const uint8_t* xt, int64_t M, int N, int K,
-                                               int64_t rows_per_split, float* part) {
+                                               int64_t chunks_per_split, float* part) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 128 + (wave & 1) * 64;
   const int k0 = blockIdx.y * 128 + (wave >> 1) * 64;
-  const int64_t ms = (int64_t)blockIdx.z * rows_per_split;
-  int64_t me = ms + rows_per_split;
-  if (me > M) me = M;
+  const int64_t nch = (M + 127) / 128;
+  const int64_t cs = (int64_t)blockIdx.z * chunks_per_split;
+  int64_t ce = cs + chunks_per_split;
+  if (ce > nch) ce = nch;
   v4f acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   const bool nin = n0 < N, kin = k0 < K;
-  if (nin && kin) {
-    const int lim = (int)(me - ms);
-    for (int mc = 0; mc < lim; mc += 128) {
-      v8i af[4], bf[4];
+  if (nin && kin && cs < ce) {
+    // the next 128-row chunk's fragments are requested before this chunk's MFMAs
+    v8i af[4], bf[4], an[4], bn[4];
 #pragma unroll
-      for (int a = 0; a < 4; ++a) af[a] = load_frag(dzt + (int64_t)(n0 + 16 * a + r) * M + ms, g, mc, lim);
+    for (int a = 0; a < 4; ++a) af[a] = load_frag_ilv(dzt, n0 / 16 + a, cs, nch, r, g);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) bf[b] = load_frag(xt + (int64_t)(k0 + 16 * b + r) * M + ms, g, mc, lim);
+    for (int b = 0; b < 4; ++b) bf[b] = load_frag_ilv(xt, k0 / 16 + b, cs, nch, r, g);
+    for (int64_t c = cs; c < ce; ++c) {
+      const int64_t cn = c + 1 < ce ? c + 1 : c;  // past the end: a harmless reload of this chunk
+#pragma unroll
+      for (int a = 0; a < 4; ++a) an[a] = load_frag_ilv(dzt, n0 / 16 + a, cn, nch, r, g);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) bn[b] = load_frag_ilv(xt, k0 / 16 + b, cn, nch, r, g);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = mfma_fp8<1, 0>(af[a], bf[b], acc[a][b]);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        af[a] = an[a];
+        bf[a] = bn[a];
+      }
     }
 #pragma unroll
     for (int a = 0; a < 4; ++a)
@@ -386,11 +419,10 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint8_t* dzt, const uint8_t
   }
 }
 
-// dW[k][n] = (sum_s part[s][k][n]) * sxc[k] * sdzc[n]; column vectors from the
-// per-workgroup partials.  Fixed summation order => deterministic.
+// dW[k][n] = (sum_s part[s][k][n]) * sxc[k] * sdzc[n].  Fixed summation
+// order => deterministic.
 __global__ __launch_bounds__(256) void k_finalize(const float* wpart, int nsplit, const float* sxc, const float* sdzc,
-                                                  int K, int N, float* dw, const float* cpart, int nblocks,
-                                                  float* dgamma, float* dbeta, float* dbias) {
+                                                  int K, int N, float* dw) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t kn = (int64_t)K * N;
   if (i < kn) {
@@ -398,14 +430,45 @@ __global__ __launch_bounds__(256) void k_finalize(const float* wpart, int nsplit
     for (int sp = 0; sp < nsplit; ++sp) s += wpart[(int64_t)sp * kn + i];
     const int k = (int)(i / N), n = (int)(i - (int64_t)k * N);
     dw[i] = s * sxc[k] * sdzc[n];
-  } else if (i < kn + N) {
-    const int n = (int)(i - kn);
-    const size_t plane = (size_t)nblocks * N;
-    float a = 0.0f, b = 0.0f, c = 0.0f;
-    for (int bl = 0; bl < nblocks; ++bl) {
-      a += cpart[(size_t)bl * N + n];
-      b += cpart[plane + (size_t)bl * N + n];
-      c += cpart[2 * plane + (size_t)bl * N + n];
+  }
+}
+
+// dgamma, dbeta, dbias from the per-workgroup column partials: block of 256
+// threads = 16 columns x 16 subsets of the workgroups (strided, 2 in flight),
+// then the subset sums in a fixed order => deterministic.
+__global__ __launch_bounds__(256) void k_col_vectors(const float* cpart, int nblocks, int N, float* dgamma,
+                                                     float* dbeta, float* dbias) {
+  __shared__ float red[3][16][16];
+  const int cl = threadIdx.x & 15, part = threadIdx.x >> 4;
+  const int n = blockIdx.x * 16 + cl;
+  const size_t plane = (size_t)nblocks * N;
+  float a = 0.0f, b = 0.0f, c = 0.0f;
+  if (n < N) {
+    int bl = part;
+    for (; bl + 16 < nblocks; bl += 32) {
+      const size_t o0 = (size_t)bl * N + n, o1 = (size_t)(bl + 16) * N + n;
+      const float a0 = cpart[o0], b0 = cpart[plane + o0], c0 = cpart[2 * plane + o0];
+      const float a1 = cpart[o1], b1 = cpart[plane + o1], c1 = cpart[2 * plane + o1];
+      a += a0; b += b0; c += c0;
+      a += a1; b += b1; c += c1;
+    }
+    for (; bl < nblocks; bl += 16) {
+      const size_t o = (size_t)bl * N + n;
+      a += cpart[o];
+      b += cpart[plane + o];
+      c += cpart[2 * plane + o];
+    }
+  }
+  red[0][part][cl] = a;
+  red[1][part][cl] = b;
+  red[2][part][cl] = c;
+  __syncthreads();
+  if (part == 0 && n < N) {
+#pragma unroll
+    for (int i = 1; i < 16; ++i) {
+      a += red[0][i][cl];
+      b += red[1][i][cl];
+      c += red[2][i][cl];
     }
     if (dgamma) dgamma[n] = a;
     if (dbeta) dbeta[n] = b;
@@ -418,7 +481,7 @@ size_t bwd_lds_bytes(int K, int N) {
 }
 
 struct BwdWs {
-  size_t part, dz, xt, sxc, xcolp, dzt, sdzc, wpart, total;
+  size_t part, dz, xt, sxc, xcolp, dzt, sdzc, dzmult, qwi, qwri, wpart, total;
   int nblocks, nsplit;
   int64_t xnp;
 };
@@ -433,11 +496,15 @@ BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K) {
   size_t o = 0;
   w.part = o; o += al((size_t)4 * w.nblocks * N * 4);
   w.dz = o; o += al((size_t)M * N * 4);
-  w.xt = o; o += al((size_t)M * K);
+  const int64_t mpad = (M + 127) / 128 * 128;
+  w.xt = o; o += al((size_t)mpad * K);
   w.sxc = o; o += al((size_t)K * 4);
   w.xcolp = o; o += al((size_t)xq.ws_floats * 4);
-  w.dzt = o; o += al((size_t)M * N);
+  w.dzt = o; o += al((size_t)mpad * N);
   w.sdzc = o; o += al((size_t)N * 4);
+  w.dzmult = o; o += al((size_t)N * 4);
+  w.qwi = o; o += al((size_t)N * ((K + 127) / 128 * 128));
+  w.qwri = o; o += al((size_t)K * ((N + 127) / 128 * 128));
   w.wpart = o; o += al((size_t)w.nsplit * K * N * 4);
   w.total = o;
   return w;
@@ -482,8 +549,19 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
   p.dz_codes = a.dz_codes; p.dz_scales = a.dz_scales;
   p.part = reinterpret_cast<float*>(ws + w.part);
   p.nblocks = w.nblocks;
+  p.qwi = ws + w.qwi;
+  p.qwri = ws + w.qwri;
 
   hipError_t e;
+  {  // both weights into the fragment-interleaved order
+    const int64_t kp = (a.K + 127) / 128 * 8, np_ = (a.N + 127) / 128 * 8;
+    if (!a.no_ln)
+      hipLaunchKernelGGL(k_relayout, dim3((unsigned)((a.N * kp + 255) / 256)), dim3(256), 0, s, a.qw, (int)a.N,
+                         (int)a.K, ws + w.qwi);
+    hipLaunchKernelGGL(k_relayout, dim3((unsigned)((a.K * np_ + 255) / 256)), dim3(256), 0, s, a.qw_row, (int)a.K,
+                       (int)a.N, ws + w.qwri);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   const int nt = (int)a.N / 64, kt = (int)a.K / 64;
   if (nt <= 8 && kt <= 8) e = launch_main_t<8, 8>(p, a.no_ln, s);
   else if (nt <= 8) e = launch_main_t<8, 16>(p, a.no_ln, s);
@@ -498,21 +576,27 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
   float* sdzc = reinterpret_cast<float*>(ws + w.sdzc);
   QuantLaunch xq{};
   xq.src = a.x; xq.rows = a.M; xq.cols = a.K; xq.ld = a.K; xq.src_dtype = 0; xq.fmt = 0; xq.mode = 2;
-  xq.transpose_out = 1; xq.codes = xt; xq.scales = sxc; xq.amax_out = nullptr; xq.workspace = ws + w.xcolp;
+  xq.transpose_out = 2; xq.codes = xt; xq.scales = sxc; xq.amax_out = nullptr; xq.workspace = ws + w.xcolp;
   e = launch_quant(xq, s);
   if (e != hipSuccess) return e;
   const float* dzmax = p.part + (size_t)3 * w.nblocks * a.N;
-  e = launch_cast_col_with_partials(p.dz, 1, 1, a.M, a.N, a.N, dzmax, w.nblocks, dzt, sdzc, s);
+  e = launch_cast_col_with_partials(p.dz, 1, 1, a.M, a.N, a.N, dzmax, w.nblocks, dzt, sdzc,
+                                    reinterpret_cast<float*>(ws + w.dzmult), s);
   if (e != hipSuccess) return e;
 
   float* wpart = reinterpret_cast<float*>(ws + w.wpart);
   dim3 g((unsigned)((a.N + 127) / 128), (unsigned)((a.K + 127) / 128), (unsigned)w.nsplit);
-  hipLaunchKernelGGL(k_wgrad, g, dim3(256), 0, s, dzt, xt, a.M, (int)a.N, (int)a.K, (int64_t)kWgSplitRows, wpart);
+  hipLaunchKernelGGL(k_wgrad, g, dim3(256), 0, s, dzt, xt, a.M, (int)a.N, (int)a.K, (int64_t)(kWgSplitRows / 128),
+                     wpart);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t tot = a.K * a.N + a.N;
+  const int64_t tot = a.K * a.N;
   hipLaunchKernelGGL(k_finalize, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, wpart, w.nsplit, sxc, sdzc,
-                     (int)a.K, (int)a.N, a.dw, p.part, w.nblocks, a.dgamma, a.dbeta, a.dbias);
+                     (int)a.K, (int)a.N, a.dw);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (a.dgamma || a.dbeta || a.dbias)
+    hipLaunchKernelGGL(k_col_vectors, dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, p.part, w.nblocks, (int)a.N,
+                       a.dgamma, a.dbeta, a.dbias);
   return hipGetLastError();
 }
 

@@ -35,15 +35,18 @@ constexpr int kMaxGroups = 2048;
 // fixed term for the per-tile reductions and synchronization
 __host__ __device__ inline int64_t tile_cost(int64_t K, int64_t N) { return 32 * (K + N) + 2048; }
 
-constexpr int kClasses = 8;       // NT in 1..4, FULL or not
+constexpr int kClasses = 2 * kResShapes;  // (NT, KC) shape x FULL or not
 constexpr int kMaxGrid = 1024;    // workgroups per class launch
 
-// shape class of a group: 2 (NT - 1) + FULL (the same test as the single forward's)
+// Resident chunk count of a group: 4 for K <= 512, else the maximum.  Fewer
+// classes mean fewer launches (each pays a weight prologue and a drain);
+// the chunk count only sizes the registers, the per-tile arithmetic over
+// ceil(K/128) chunks is the single forward's whatever it is.
+__host__ __device__ inline int group_kc(int nt, int K) { return (K + 127) / 128 <= 4 ? 4 : res_kc_max(nt); }
+// shape class of a group: 2 res_shape(NT, KC) + FULL
 __host__ __device__ inline int group_class(int64_t M, int64_t N, int64_t K) {
-  const int nt = res_nt((int)N);
-  const int kq = nt == 1 ? Res<1>::KQ : nt == 2 ? Res<2>::KQ : nt == 3 ? Res<3>::KQ : Res<4>::KQ;
-  const bool full = N == 128 * nt && K == 256 * kq && M % kResRows == 0;
-  return 2 * (nt - 1) + (full ? 1 : 0);
+  const int nt = res_nt((int)N), kc = group_kc(nt, (int)K);
+  return 2 * res_shape(nt, kc) + (res_full(M, (int)N, (int)K, nt, kc) ? 1 : 0);
 }
 
 // plan of class c: tile_pre[c][G+1], wg_start[c][kMaxGrid+1]; grid[c] workgroups
@@ -123,7 +126,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_grouped_plan(const GroupDev* g
   }
 }
 
-template <bool OPT, int NT, bool FULL>
+template <bool OPT, int NT, int KC, bool FULL>
 __global__ __launch_bounds__(kThreads) void k_grouped_res(const GroupDev* groups, const int* tile_pre,
                                                           const int* wg_start, int G, float eps) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -151,17 +154,17 @@ __global__ __launch_bounds__(kThreads) void k_grouped_res(const GroupDev* groups
     p.z = gd.z;
     p.mean = nullptr; p.rstd = nullptr; p.qx_out = nullptr; p.sx_out = nullptr;
     p.eps = eps; p.x_r = 1.0f; p.x_s = 1.0f;
-    ResBlock<1, NT, OPT, FULL> blk(p, t - tile_pre[g], seg_end - tile_pre[g], smem);
+    ResBlock<1, NT, KC, OPT, FULL> blk(p, t - tile_pre[g], seg_end - tile_pre[g], smem);
     blk.run();
     __syncthreads();  // the next group's set-up rewrites the LDS
     t = seg_end;
   }
 }
 
-template <bool OPT, int NT, bool FULL>
+template <bool OPT, int NT, int KC, bool FULL>
 hipError_t launch_class(const GroupDev* dg, const int* tp, const int* ws, int G, int grid, size_t lds, float eps,
                         hipStream_t s) {
-  auto kern = k_grouped_res<OPT, NT, FULL>;
+  auto kern = k_grouped_res<OPT, NT, KC, FULL>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -192,7 +195,8 @@ hipError_t launch_grouped(const GroupedLaunch& a, hipStream_t s) {
     const GroupDev& gd = a.groups[gi];
     const int c = fwd::group_class(gd.M, gd.N, gd.K);
     tiles[c] += (gd.M + fwd::kResRows - 1) / fwd::kResRows;
-    const size_t l = (size_t)fwd::res_lds(fwd::res_nt((int)gd.N), (int)gd.N).total;
+    const int nt = fwd::res_nt((int)gd.N);
+    const size_t l = (size_t)fwd::res_lds(nt, fwd::group_kc(nt, (int)gd.K), (int)gd.N).total;
     if (l > lds[c]) lds[c] = l;
     if (gd.z != nullptr) opt = true;
   }
@@ -222,14 +226,18 @@ hipError_t launch_grouped(const GroupedLaunch& a, hipStream_t s) {
     const int grid = (int)(tiles[c] < cus ? tiles[c] : cus);
     const int* tp = tile_pre + c * (G + 1);
     const int* wsc = wg_start + c * (fwd::kMaxGrid + 1);
-#define LOKA_CLASS(C, NT, FULL)                                                                              \
-  case C:                                                                                                   \
-    e = opt ? fwd::launch_class<true, NT, FULL>(dgroups, tp, wsc, G, grid, lds[c], a.eps, s)                \
-            : fwd::launch_class<false, NT, FULL>(dgroups, tp, wsc, G, grid, lds[c], a.eps, s);              \
+#define LOKA_CLASS(S, NT, KC)                                                                                \
+  case 2 * S:                                                                                               \
+    e = opt ? fwd::launch_class<true, NT, KC, false>(dgroups, tp, wsc, G, grid, lds[c], a.eps, s)           \
+            : fwd::launch_class<false, NT, KC, false>(dgroups, tp, wsc, G, grid, lds[c], a.eps, s);         \
+    break;                                                                                                  \
+  case 2 * S + 1:                                                                                           \
+    e = opt ? fwd::launch_class<true, NT, KC, true>(dgroups, tp, wsc, G, grid, lds[c], a.eps, s)            \
+            : fwd::launch_class<false, NT, KC, true>(dgroups, tp, wsc, G, grid, lds[c], a.eps, s);          \
     break;
     switch (c) {
-      LOKA_CLASS(0, 1, false) LOKA_CLASS(1, 1, true) LOKA_CLASS(2, 2, false) LOKA_CLASS(3, 2, true)
-      LOKA_CLASS(4, 3, false) LOKA_CLASS(5, 3, true) LOKA_CLASS(6, 4, false) LOKA_CLASS(7, 4, true)
+      LOKA_CLASS(1, 1, 4) LOKA_CLASS(2, 1, 8) LOKA_CLASS(4, 2, 4) LOKA_CLASS(5, 2, 8) LOKA_CLASS(7, 3, 4)
+      LOKA_CLASS(8, 3, 5) LOKA_CLASS(10, 4, 4)
       default: break;
     }
 #undef LOKA_CLASS

@@ -108,24 +108,76 @@ __global__ __launch_bounds__(256) void k_amax_row(const void* src, int64_t rows,
 }
 
 // partials[chunk][c] = max over rows [chunk * rpc, (chunk + 1) * rpc) of |x[r, c]|.
-// Block: 64 threads x 8 columns = 512 columns; grid (ceil(cols/512), nchunks).
+// Block: 4 wavefronts x 64 lanes x 8 columns = 512 columns; the wavefronts
+// take every 4th row of the chunk, 4 rows in flight each, and combine in LDS.
+// Grid (ceil(cols/512), nchunks).
 template <int DT>
-__global__ __launch_bounds__(64) void k_amax_col(const void* src, int64_t rows, int64_t cols, int64_t ld,
-                                                 int64_t rpc, float* partials) {
-  const int64_t c = ((int64_t)blockIdx.x * 64 + threadIdx.x) * 8;
-  if (c >= cols) return;
+__global__ __launch_bounds__(256) void k_amax_col(const void* src, int64_t rows, int64_t cols, int64_t ld,
+                                                  int64_t rpc, float* partials) {
+  __shared__ float red[4][512];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t c = ((int64_t)blockIdx.x * 64 + lane) * 8;
   const int64_t r0 = (int64_t)blockIdx.y * rpc;
   const int64_t r1 = r0 + rpc < rows ? r0 + rpc : rows;
   float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int64_t r = r0; r < r1; ++r) {
-    float v[8];
-    load8<DT>(src, r * ld + c, v);
+  if (c < cols) {
+    int64_t r = r0 + wave;
+    for (; r + 12 < r1; r += 16) {
+      float v[4][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
+      for (int u = 0; u < 4; ++u) load8<DT>(src, (r + 4 * u) * ld + c, v[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[u][i]));
+    }
+    for (; r < r1; r += 4) {
+      float v[8];
+      load8<DT>(src, r * ld + c, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
+    }
   }
-  float4* out = reinterpret_cast<float4*>(partials + (int64_t)blockIdx.y * cols + c);
-  out[0] = make_float4(m[0], m[1], m[2], m[3]);
-  out[1] = make_float4(m[4], m[5], m[6], m[7]);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[wave][lane * 8 + i] = m[i];
+  __syncthreads();
+  for (int u = threadIdx.x; u < 512; u += 256) {
+    const int64_t cc = (int64_t)blockIdx.x * 512 + u;
+    if (cc < cols)
+      partials[(int64_t)blockIdx.y * cols + cc] = fmaxf(fmaxf(red[0][u], red[1][u]), fmaxf(red[2][u], red[3][u]));
+  }
+}
+
+// Column scales from the row-chunk partial maxima, once per column: block of
+// 256 threads = 16 columns x 16 strided subsets of the np partials (4 loads
+// in flight each).  Writes the stored scale s, the multiplier r (for the
+// cast) and optionally amax.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_col_scales(const float* partials, int64_t np, int64_t cols, float* scales,
+                                                    float* mult, float* amax_out) {
+  __shared__ float red[16][16];
+  const int cl = threadIdx.x & 15, part = threadIdx.x >> 4;
+  const int64_t c = (int64_t)blockIdx.x * 16 + cl;
+  float m = 0.0f;
+  if (c < cols) {
+    int64_t k = part;
+    for (; k + 48 < np; k += 64) {
+      const float a = partials[k * cols + c], b = partials[(k + 16) * cols + c];
+      const float d = partials[(k + 32) * cols + c], e = partials[(k + 48) * cols + c];
+      m = fmaxf(m, fmaxf(fmaxf(a, b), fmaxf(d, e)));
+    }
+    for (; k < np; k += 16) m = fmaxf(m, partials[k * cols + c]);
+  }
+  red[part][cl] = m;
+  __syncthreads();
+  if (part == 0 && c < cols) {
+#pragma unroll
+    for (int i = 1; i < 16; ++i) m = fmaxf(m, red[i][cl]);
+    const ScalePair sp = scales_from_amax<FMT>(m);
+    scales[c] = sp.s;
+    mult[c] = sp.r;
+    if (amax_out) amax_out[c] = m;
+  }
 }
 
 // ---- pass 2 ---------------------------------------------------------------
@@ -136,7 +188,7 @@ struct CastParams {
   uint8_t* codes;
   void* scales;
   float* amax_out;
-  const float* amax_in;  // tensor: partials[np]; row: amax[rows]; col: partials[np][cols]
+  const float* amax_in;  // tensor: partials[np]; row: amax[rows]; col: multipliers[cols]
   int64_t np;
 };
 
@@ -183,18 +235,10 @@ __global__ __launch_bounds__(256) void k_cast_tile(CastParams p) {
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i) mult[i] = sp.r;
-  } else if (MODE == 2) {  // column: reduce partials per tile column
+  } else if (MODE == 2) {  // column: the multipliers from k_col_scales
     if (t < kTile) {
-      int64_t c = (int64_t)blockIdx.x * kTile + t;
-      float m = 0.0f;
-      if (c < p.cols)
-        for (int64_t k = 0; k < p.np; ++k) m = fmaxf(m, p.amax_in[k * p.cols + c]);
-      ScalePair sp = scales_from_amax<FMT>(m);
-      r_col[t] = sp.r;
-      if (blockIdx.y == 0 && c < p.cols) {
-        static_cast<float*>(p.scales)[c] = sp.s;
-        if (p.amax_out) p.amax_out[c] = m;
-      }
+      const int64_t c = (int64_t)blockIdx.x * kTile + t;
+      r_col[t] = c < p.cols ? p.amax_in[c] : 1.0f;
     }
     __syncthreads();
 #pragma unroll
@@ -237,7 +281,7 @@ __global__ __launch_bounds__(256) void k_cast_tile(CastParams p) {
     w[q] = cvt4<FMT>(v[4 * q] * mult[4 * q], v[4 * q + 1] * mult[4 * q + 1], v[4 * q + 2] * mult[4 * q + 2],
                      v[4 * q + 3] * mult[4 * q + 3]);
 
-  if (!TRANS) {
+  if (TRANS == 0) {
     if (ok) *reinterpret_cast<uint4*>(p.codes + row * p.cols + col0) = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
 #pragma unroll
@@ -249,21 +293,30 @@ __global__ __launch_bounds__(256) void k_cast_tile(CastParams p) {
     const int oc = t >> 2, orow = (t & 3) * 16;
     const int64_t gc = (int64_t)blockIdx.x * kTile + oc;
     const int64_t gr = (int64_t)blockIdx.y * kTile + orow;
-    if (gc < p.cols && gr < p.rows) {
+    // TRANS 2: fragment-interleaved [cols][rows padded to 128]; the rows past
+    // `rows` (up to the padding) are written as zero codes
+    const int64_t nch = (p.rows + 127) / 128;
+    if (gc < p.cols && gr < (TRANS == 2 ? nch * 128 : p.rows)) {
       uint32_t o[4];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         o[q] = (uint32_t)tcodes[orow + 4 * q][oc] | ((uint32_t)tcodes[orow + 4 * q + 1][oc] << 8) |
                ((uint32_t)tcodes[orow + 4 * q + 2][oc] << 16) | ((uint32_t)tcodes[orow + 4 * q + 3][oc] << 24);
-      *reinterpret_cast<uint4*>(p.codes + gc * p.rows + gr) = make_uint4(o[0], o[1], o[2], o[3]);
+      uint8_t* dst = TRANS == 2 ? p.codes + ilv_offset(gc, gr, nch) : p.codes + gc * p.rows + gr;
+      *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
 }
 
+// trans: 0 plain, 1 transposed row-major, 2 transposed fragment-interleaved
+// (internal; the row count is covered up to the next multiple of 128)
 template <int DT, int FMT, int MODE>
 void launch_cast(const CastParams& cp, int trans, hipStream_t s) {
-  dim3 grid((unsigned)((cp.cols + kTile - 1) / kTile), (unsigned)((cp.rows + kTile - 1) / kTile));
-  if (trans)
+  const int64_t rows = trans == 2 ? (cp.rows + 127) / 128 * 128 : cp.rows;
+  dim3 grid((unsigned)((cp.cols + kTile - 1) / kTile), (unsigned)((rows + kTile - 1) / kTile));
+  if (trans == 2)
+    hipLaunchKernelGGL((k_cast_tile<DT, FMT, MODE, 2>), grid, dim3(256), 0, s, cp);
+  else if (trans == 1)
     hipLaunchKernelGGL((k_cast_tile<DT, FMT, MODE, 1>), grid, dim3(256), 0, s, cp);
   else
     hipLaunchKernelGGL((k_cast_tile<DT, FMT, MODE, 0>), grid, dim3(256), 0, s, cp);
@@ -303,7 +356,7 @@ QuantPlan quant_plan(int64_t rows, int64_t cols, int mode) {
     if (nch < 1) nch = 1;
     q.np = nch;
     q.rpc = rpc;
-    q.ws_floats = nch * cols;
+    q.ws_floats = nch * cols + cols;  // partials, then the column multipliers
   }
   return q;
 }
@@ -323,8 +376,17 @@ hipError_t launch_quant(const QuantLaunch& a, hipStream_t s) {
     else hipLaunchKernelGGL(k_amax_row<0>, g, dim3(256), 0, s, a.src, a.rows, a.cols, a.ld, ws);
   } else if (a.mode == 2) {
     dim3 g((unsigned)((a.cols + 511) / 512), (unsigned)q.np);
-    if (f32) hipLaunchKernelGGL(k_amax_col<1>, g, dim3(64), 0, s, a.src, a.rows, a.cols, a.ld, q.rpc, ws);
-    else hipLaunchKernelGGL(k_amax_col<0>, g, dim3(64), 0, s, a.src, a.rows, a.cols, a.ld, q.rpc, ws);
+    if (f32) hipLaunchKernelGGL(k_amax_col<1>, g, dim3(256), 0, s, a.src, a.rows, a.cols, a.ld, q.rpc, ws);
+    else hipLaunchKernelGGL(k_amax_col<0>, g, dim3(256), 0, s, a.src, a.rows, a.cols, a.ld, q.rpc, ws);
+    float* mult = ws + q.np * a.cols;
+    dim3 gs((unsigned)((a.cols + 15) / 16));
+    if (a.fmt == 0)
+      hipLaunchKernelGGL(k_col_scales<0>, gs, dim3(256), 0, s, ws, q.np, a.cols, static_cast<float*>(a.scales), mult,
+                         a.amax_out);
+    else
+      hipLaunchKernelGGL(k_col_scales<1>, gs, dim3(256), 0, s, ws, q.np, a.cols, static_cast<float*>(a.scales), mult,
+                         a.amax_out);
+    cp.amax_in = mult;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -352,16 +414,21 @@ hipError_t launch_amax_tensor_partials(const void* src, int64_t rows, int64_t co
 
 // Column cast with precomputed partial column maxima (np x cols), used by the
 // backward for dZ whose column maxima come out of the fused LN-backward kernel.
+// mult: cols floats of scratch for the multipliers.  Output: codes transposed
+// to [cols][rows] in the fragment-interleaved layout (rows padded to 128).
 hipError_t launch_cast_col_with_partials(const void* src, int src_dtype, int fmt, int64_t rows, int64_t cols,
                                          int64_t ld, const float* partials, int64_t np, uint8_t* codes_t,
-                                         float* scales, hipStream_t s) {
-  CastParams cp{src, rows, cols, ld, codes_t, scales, nullptr, partials, np};
+                                         float* scales, float* mult, hipStream_t s) {
+  dim3 gs((unsigned)((cols + 15) / 16));
+  if (fmt == 0) hipLaunchKernelGGL(k_col_scales<0>, gs, dim3(256), 0, s, partials, np, cols, scales, mult, nullptr);
+  else hipLaunchKernelGGL(k_col_scales<1>, gs, dim3(256), 0, s, partials, np, cols, scales, mult, nullptr);
+  CastParams cp{src, rows, cols, ld, codes_t, scales, nullptr, mult, np};
   if (src_dtype == 1) {
-    if (fmt == 0) launch_cast<1, 0, 2>(cp, 1, s);
-    else launch_cast<1, 1, 2>(cp, 1, s);
+    if (fmt == 0) launch_cast<1, 0, 2>(cp, 2, s);
+    else launch_cast<1, 1, 2>(cp, 2, s);
   } else {
-    if (fmt == 0) launch_cast<0, 0, 2>(cp, 1, s);
-    else launch_cast<0, 1, 2>(cp, 1, s);
+    if (fmt == 0) launch_cast<0, 0, 2>(cp, 2, s);
+    else launch_cast<0, 1, 2>(cp, 2, s);
   }
   return hipGetLastError();
 }
