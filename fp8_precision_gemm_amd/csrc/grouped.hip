@@ -6,7 +6,10 @@
 // rank).
 //
 // Launches on the caller's stream:
-//  1. k_grouped_plan (one workgroup) reads the group descriptors and writes
+//  1. The plan: normally computed on the host and passed by value to each
+//     class launch (GroupPlan, at most 256 groups per class and 256
+//     workgroups); for larger problems k_grouped_plan (one workgroup) reads
+//     the group descriptors and writes
 //     the plan into the workspace, per shape class (column tiles per
 //     wavefront NT = ceil(N/128), and whether the shape is the guard-free
 //     FULL case): the first global 16-row tile of every group of the class
@@ -48,6 +51,18 @@ __host__ __device__ inline int group_class(int64_t M, int64_t N, int64_t K) {
   const int nt = res_nt((int)N), kc = group_kc(nt, (int)K);
   return 2 * res_shape(nt, kc) + (res_full(M, (int)N, (int)K, nt, kc) ? 1 : 0);
 }
+
+// The plan of one class as a kernel argument (by value, so a captured graph
+// replays it without any host copy): the class's groups, their exclusive
+// prefix of 16-row tiles, and each workgroup's first tile.
+constexpr int kPlanGroups = 256;
+struct GroupPlan {
+  int ngroups;
+  int grid;
+  int gid[kPlanGroups];
+  int tile_pre[kPlanGroups + 1];
+  int wg_start[kPlanGroups + 1];
+};
 
 // plan of class c: tile_pre[c][G+1], wg_start[c][kMaxGrid+1]; grid[c] workgroups
 __global__ __launch_bounds__(kPlanThreads) void k_grouped_plan(const GroupDev* groups, int G, int cus,
@@ -161,6 +176,51 @@ __global__ __launch_bounds__(kThreads) void k_grouped_res(const GroupDev* groups
   }
 }
 
+// the same walk, with the plan as an argument (group index through gid)
+template <bool OPT, int NT, int KC, bool FULL>
+__global__ __launch_bounds__(kThreads) void k_grouped_res_arg(const GroupDev* groups, GroupPlan plan, float eps) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  int t = plan.wg_start[blockIdx.x];
+  const int tend = plan.wg_start[blockIdx.x + 1];
+  int lo = 0, hi = plan.ngroups - 1;  // last class group with tile_pre <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (plan.tile_pre[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  int q = lo;
+  while (t < tend) {
+    while (plan.tile_pre[q + 1] <= t) ++q;  // past finished and empty groups
+    const int seg_end = min(tend, plan.tile_pre[q + 1]);
+    const GroupDev gd = groups[plan.gid[q]];
+    FwdBlock p;
+    p.M = gd.M; p.N = (int)gd.N; p.K = (int)gd.K;
+    p.x = static_cast<const uint16_t*>(gd.x);
+    p.qw = gd.qw; p.sw = gd.sw;
+    p.bias = static_cast<const uint16_t*>(gd.bias);
+    p.gamma = static_cast<const uint16_t*>(gd.gamma);
+    p.beta = static_cast<const uint16_t*>(gd.beta);
+    p.y = static_cast<uint16_t*>(gd.y);
+    p.z = gd.z;
+    p.mean = nullptr; p.rstd = nullptr; p.qx_out = nullptr; p.sx_out = nullptr;
+    p.eps = eps; p.x_r = 1.0f; p.x_s = 1.0f;
+    ResBlock<1, NT, KC, OPT, FULL> blk(p, t - plan.tile_pre[q], seg_end - plan.tile_pre[q], smem);
+    blk.run();
+    __syncthreads();  // the next group's set-up rewrites the LDS
+    t = seg_end;
+  }
+}
+
+template <bool OPT, int NT, int KC, bool FULL>
+hipError_t launch_class_arg(const GroupDev* dg, const GroupPlan& plan, size_t lds, float eps, hipStream_t s) {
+  auto kern = k_grouped_res_arg<OPT, NT, KC, FULL>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)plan.grid), dim3(kThreads), lds, s, dg, plan, eps);
+  return hipGetLastError();
+}
+
 template <bool OPT, int NT, int KC, bool FULL>
 hipError_t launch_class(const GroupDev* dg, const int* tp, const int* ws, int G, int grid, size_t lds, float eps,
                         hipStream_t s) {
@@ -218,6 +278,71 @@ hipError_t launch_grouped(const GroupedLaunch& a, hipStream_t s) {
   // until the copy has run)
   e = hipMemcpyAsync(dgroups, a.groups, (size_t)G * sizeof(GroupDev), hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return e;
+  // host plans (passed by value) when every class fits GroupPlan
+  int ngc[fwd::kClasses] = {0};
+  for (int gi = 0; gi < G; ++gi) {
+    const GroupDev& gd = a.groups[gi];
+    ++ngc[fwd::group_class(gd.M, gd.N, gd.K)];
+  }
+  bool host_plan = cus <= fwd::kPlanGroups;
+  for (int c = 0; c < fwd::kClasses; ++c) host_plan = host_plan && ngc[c] <= fwd::kPlanGroups;
+  if (host_plan) {
+    for (int c = 0; c < fwd::kClasses && e == hipSuccess; ++c) {
+      if (tiles[c] == 0) continue;
+      fwd::GroupPlan plan;
+      plan.ngroups = 0;
+      int64_t cost_pre[fwd::kPlanGroups + 1];
+      int64_t ccost[fwd::kPlanGroups];
+      int64_t tp = 0, cp = 0;
+      for (int gi = 0; gi < G; ++gi) {
+        const GroupDev& gd = a.groups[gi];
+        if (fwd::group_class(gd.M, gd.N, gd.K) != c) continue;
+        const int q = plan.ngroups++;
+        plan.gid[q] = gi;
+        plan.tile_pre[q] = (int)tp;
+        cost_pre[q] = cp;
+        ccost[q] = fwd::tile_cost(gd.K, gd.N);
+        const int64_t tl = (gd.M + fwd::kResRows - 1) / fwd::kResRows;
+        tp += tl;
+        cp += tl * ccost[q];
+      }
+      const int ng = plan.ngroups;
+      plan.tile_pre[ng] = (int)tp;
+      cost_pre[ng] = cp;
+      const int grid = (int)(tp < cus ? tp : cus);
+      plan.grid = grid;
+      // workgroup b starts at the first tile whose starting cost is >= b*C/grid
+      for (int b = 0; b <= grid; ++b) {
+        if (b == grid) {
+          plan.wg_start[b] = (int)tp;
+          continue;
+        }
+        const int64_t x = (cp / grid) * b + ((cp % grid) * b) / grid;
+        int q = 0;
+        while (q + 1 < ng && cost_pre[q + 1] <= x) ++q;
+        const int64_t tq = plan.tile_pre[q + 1] - plan.tile_pre[q];
+        int64_t j = tq == 0 ? 0 : (x - cost_pre[q] + ccost[q] - 1) / ccost[q];
+        if (j > tq) j = tq;
+        plan.wg_start[b] = plan.tile_pre[q] + (int)j;
+      }
+#define LOKA_CLASS(S, NT, KC)                                                                     \
+  case 2 * S:                                                                                    \
+    e = opt ? fwd::launch_class_arg<true, NT, KC, false>(dgroups, plan, lds[c], a.eps, s)        \
+            : fwd::launch_class_arg<false, NT, KC, false>(dgroups, plan, lds[c], a.eps, s);      \
+    break;                                                                                       \
+  case 2 * S + 1:                                                                                \
+    e = opt ? fwd::launch_class_arg<true, NT, KC, true>(dgroups, plan, lds[c], a.eps, s)         \
+            : fwd::launch_class_arg<false, NT, KC, true>(dgroups, plan, lds[c], a.eps, s);       \
+    break;
+      switch (c) {
+        LOKA_CLASS(1, 1, 4) LOKA_CLASS(2, 1, 8) LOKA_CLASS(4, 2, 4) LOKA_CLASS(5, 2, 8) LOKA_CLASS(7, 3, 4)
+        LOKA_CLASS(8, 3, 5) LOKA_CLASS(10, 4, 4)
+        default: break;
+      }
+#undef LOKA_CLASS
+    }
+    return e;
+  }
   hipLaunchKernelGGL(fwd::k_grouped_plan, dim3(1), dim3(fwd::kPlanThreads), 0, s, dgroups, G, cus, tile_pre,
                      wg_start);
   if ((e = hipGetLastError()) != hipSuccess) return e;

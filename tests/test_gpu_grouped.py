@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from oracle import forward
-from synth.workloads import grouped_case
+from synth.workloads import forward_case, grouped_case
 from tests.gpu_helpers import bf16_dev, check_y, check_z, host, row_sigma, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -59,3 +59,30 @@ def test_grouped_ragged_and_empty_groups(lib):
         ref = forward.gemm_ln_forward(g["x"], g["w"], g["bias"], g["gamma"], g["beta"])
         check_z(host(o["z"]), ref["z"], row_sigma(ref["z"]), f"group {i}")
         check_y(host(o["y"]), ref["y"], f"group {i}")
+
+
+def test_grouped_many_groups_device_plan(lib):
+    """More than 256 groups in one shape class: the launch plan is built on
+    the device instead of being passed by value.  Every group (empty and
+    ragged ones included) must equal a single call bit for bit, and a few
+    are checked against the oracle."""
+    groups = []
+    for i in range(300):  # one shape class (K = N = 128), ragged and empty M
+        m = (0, 1, 16, 17, 48)[i % 5]
+        c = forward_case(max(m, 1), 128, 128, seed=1000 + i)
+        groups.append(c if m > 0 else dict(c, M=0, x=c["x"][:0]))
+    dg = prepare(lib, groups)
+    outs = lib.loka_grouped_gemm_fp8_ln(dg, want_z=True)
+    torch.cuda.synchronize()
+    for i, (g, d, o) in enumerate(zip(groups, dg, outs)):
+        if g["x"].shape[0] == 0:
+            assert o["y"].numel() == 0
+            continue
+        s = lib.loka_gemm_fp8_ln(d["x"], d["qw"], d["sw"], d["bias"], d["gamma"], d["beta"], want_z=True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(s["y"]), host(o["y"]), err_msg=f"group {i}")
+        np.testing.assert_array_equal(host(s["z"]), host(o["z"]), err_msg=f"group {i}")
+        if i % 50 == 3:
+            ref = forward.gemm_ln_forward(g["x"], g["w"], g["bias"], g["gamma"], g["beta"])
+            check_z(host(o["z"]), ref["z"], row_sigma(ref["z"]), f"group {i}")
+            check_y(host(o["y"]), ref["y"], f"group {i}")
