@@ -71,7 +71,9 @@ struct Res {
   // largest weights run the steps one after another with one slot of X in
   // flight
   static constexpr bool PIPE = NT * KC <= 12 || (NT == 4 && KC == 4);
-  static constexpr int D = PIPE ? 2 : 1;                       // tiles of X requested ahead
+  // tiles of X requested ahead: small weights run short steps, so they
+  // keep four tiles in flight (the registers are there)
+  static constexpr int D = !PIPE ? 1 : (NT * KC <= 8 ? 4 : 2);
   static constexpr int LDX = KC * 128 + 16;                    // LDS code row stride (bytes)
   static constexpr int KP = (KC + 3) / 4;                     // E8M0 words per lane group
   static constexpr int XE = 16 * KP;                           // E8M0 bytes per LDS row ([g][KP words])
@@ -701,7 +703,9 @@ struct ResBlock {
     // after its first reader) and the column vectors, then X tile 1
     load_x<0>(tb);
     request_weights();
-    if (PIPE) load_x<(1 % D)>(tb + 1);
+    if (D > 1) load_x<(1 % D)>(tb + 1);
+    if (D > 2) load_x<(2 % D)>(tb + 2);
+    if (D > 3) load_x<(3 % D)>(tb + 3);
     quantize<0>(tb, 0);
     load_x<0>(tb + D);
     stage_weights();
@@ -719,12 +723,26 @@ struct ResBlock {
     epilogue_stats(0, acc0, cs0, sc0);
     __syncthreads();
     const int64_t n = te - tb;
+    // step j quantizes tile j+1 from slot (j+1) % D and fills accumulator set j % 2
     int64_t j = 1;
-    while (j < n) {
-      step<0, 1>(j);
-      if (++j >= n) break;
-      step<(1 % D), 0>(j);
-      ++j;
+    if (D == 2) {
+      while (j < n) {
+        step<0, 1>(j);
+        if (++j >= n) break;
+        step<(1 % D), 0>(j);
+        ++j;
+      }
+    } else {
+      while (j < n) {
+        step<(2 % D), 1>(j);
+        if (++j >= n) break;
+        step<(3 % D), 0>(j);
+        if (++j >= n) break;
+        step<0, 1>(j);
+        if (++j >= n) break;
+        step<(1 % D), 0>(j);
+        ++j;
+      }
     }
     // the last tile's normalization and stores
     const int64_t l = n - 1;
