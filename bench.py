@@ -31,7 +31,7 @@ PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 ROTATE = 16
 # The fused rowwise forward's sources and the committed counter summary of its HBM traffic.
-FWD_SOURCES = ["common.hpp", "launch.hpp", "fwd_block.hpp", "fwd_row.hip"]
+FWD_SOURCES = ["common.hpp", "launch.hpp", "fwd_block.hpp", "fwd_resident.hpp", "fwd_kernels.hpp", "fwd_row.hip"]
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_fwd_row_16384x512x512_hbm_counters.md")
 
 
@@ -284,7 +284,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(main_res["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(main_res["gbs"] / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
                      "traffic_unit": "bytes/launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "kernel": "k_fwd<row> (fused X quant + FP8 MFMA GEMM + LayerNorm)",
+                     "kernel": "k_fwd_res<row> (weight-resident fused X quant + FP8 MFMA GEMM + LayerNorm)",
                      "algorithmic_bytes_per_launch": main_res["bytes"],
                      "avg_launch_us": round(main_res["us"], 3)},
         "weight_quant_us": round(main_res["weight_quant_us"], 3),
