@@ -5,7 +5,9 @@ bf16 Student-t(3) with outlier columns, W[512,512] pre-quantized per column,
 bias, LayerNorm over 512): the X amax and e4m3 cast, the FP8 MFMA GEMM and
 the dequant + bias + LayerNorm epilogue, all in one kernel.  The weight is
 quantized once per step of training, outside the activation path (reported
-separately as `weight_quant_us`).  Inputs are resident in HBM; 16 rotating
+separately as `weight_quant_us`), straight into the packed layout the kernel
+reads; the same call with a row-major weight (rearranged inside the call) is
+reported under `rows`.  Inputs are resident in HBM; 16 rotating
 input/output sets (537 MB) keep the 256 MB Infinity Cache from serving them.
 Launches are replayed from a HIP graph so host launch cost does not enter.
 
@@ -107,22 +109,27 @@ def dev_bf16(torch, bits):
     return t.view(torch.bfloat16).cuda()
 
 
-def bench_forward(torch, lk, case, x_mode, steps, warmup, stream):
-    """Time loka_gemm_fp8_ln over ROTATE buffer sets; returns a dict."""
+def bench_forward(torch, lk, case, x_mode, steps, warmup, stream, packed=True):
+    """Time loka_gemm_fp8_ln over ROTATE buffer sets; returns a dict.  The
+    weight is quantized straight into the packed layout the kernel reads
+    (packed=False: row-major [N, K] codes, rearranged inside every call)."""
     M, K, N = case["M"], case["K"], case["N"]
     w = dev_bf16(torch, case["w"])
     wmode = {"row": "col", "tensor": "tensor", "mx32_row": "mx32_col"}[x_mode]
-    qw, sw, _ = lk.loka_quant_fp8(w, mode=wmode, transpose_out=True, stream=stream)
+    layout = "packed" if packed else True
+    qw, sw, _ = lk.loka_quant_fp8(w, mode=wmode, transpose_out=layout, stream=stream)
     x0 = dev_bf16(torch, case["x"])
     vec = [dev_bf16(torch, case[k]) for k in ("bias", "gamma", "beta")]
     launches = []
     for i in range(ROTATE):
         x = x0 if i == 0 else x0.clone()
-        f, _ = lk.loka_gemm_fp8_ln(x, qw, sw, *vec, x_mode=x_mode, stream=stream, prepare=True)
+        f, _ = lk.loka_gemm_fp8_ln(x, qw, sw, *vec, x_mode=x_mode, stream=stream, prepare=True, w_packed=packed)
         launches.append(f)
     torch.cuda.synchronize()
     secs, n = timed_graph(torch, launches, steps, warmup, stream)
     per = secs / n
+    if not packed:
+        return {"us": per * 1e6}
     flops = 2.0 * M * N * K
     nbytes = fwd_bytes(M, K, N, mx=x_mode == "mx32_row")
     # the weight quantization (once per training step), same rotation
@@ -135,7 +142,7 @@ def bench_forward(torch, lk, case, x_mode, steps, warmup, stream):
         wi = w if i == 0 else w.clone()
         qwi, swi = torch.empty_like(qw), torch.empty_like(sw)
         wq.append(lambda wi=wi, qwi=qwi, swi=swi: lk.loka_quant_fp8(
-            wi, mode=wmode, transpose_out=True, codes=qwi, scales=swi, stream=stream, workspace=wsq))
+            wi, mode=wmode, transpose_out=layout, codes=qwi, scales=swi, stream=stream, workspace=wsq))
     wsecs, wn = timed_graph(torch, wq, min(steps, 800), min(warmup, 80), stream)
     return {"us": per * 1e6, "tflops": flops / per / 1e12, "gbs": nbytes / per / 1e9, "bytes": nbytes,
             "flops": flops, "weight_quant_us": wsecs / wn * 1e6}
@@ -167,12 +174,12 @@ def bench_grouped(torch, lk, groups, steps, warmup, stream):
     flops = 0.0
     nbytes = 0
     for g in groups:
-        qw, sw, _ = lk.loka_quant_fp8(dev_bf16(torch, g["w"]), mode="col", transpose_out=True, stream=stream)
+        qw, sw, _ = lk.loka_quant_fp8(dev_bf16(torch, g["w"]), mode="col", transpose_out="packed", stream=stream)
         dg.append({"x": dev_bf16(torch, g["x"]), "qw": qw, "sw": sw, "bias": dev_bf16(torch, g["bias"]),
                    "gamma": dev_bf16(torch, g["gamma"]), "beta": dev_bf16(torch, g["beta"])})
         flops += 2.0 * g["M"] * g["N"] * g["K"]
         nbytes += fwd_bytes(g["M"], g["K"], g["N"])
-    fn, _ = lk.loka_grouped_gemm_fp8_ln(dg, stream=stream, prepare=True)
+    fn, _ = lk.loka_grouped_gemm_fp8_ln(dg, stream=stream, prepare=True, w_packed=True)
     torch.cuda.synchronize()
     secs, n = timed_graph(torch, [fn], max(20, steps // 40), max(4, warmup // 40), stream)
     per = secs / n
@@ -235,6 +242,11 @@ def main():
     if want("fwd"):
         main_res = bench_forward(torch, lk, case, "row", args.steps, args.warmup, stream)
         print(f"[bench] rowwise forward: {main_res['us']:.2f} us/launch", file=sys.stderr, flush=True)
+        if not args.no_rows:
+            r = bench_forward(torch, lk, case, "row", max(200, args.steps // 4), max(20, args.warmup // 4), stream,
+                              packed=False)
+            rows["fwd_16384x512x512_rowmajor_weight"] = {"us": round(r["us"], 3)}
+            print(f"[bench] rowwise forward, row-major weight: {r['us']:.2f} us", file=sys.stderr, flush=True)
     if not args.no_rows and want("tensor"):
         r = bench_forward(torch, lk, workloads.tensor_case(), "tensor", args.steps, args.warmup, stream)
         rows["tensor_fwd_512x256x256"] = {k: round(v, 3) for k, v in r.items()}
@@ -279,7 +291,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": "rowwise FP8 GEMM + LayerNorm forward, X[16384,512] Student-t(3) with 5 outlier "
                                "columns x50, W[512,512] per-column e4m3, LayerNorm over 512",
-                   "M": 16384, "K": 512, "N": 512, "x_scaling": "row", "w_scaling": "col", "fmt": "e4m3"},
+                   "M": 16384, "K": 512, "N": 512, "x_scaling": "row", "w_scaling": "col", "fmt": "e4m3",
+                   "w_layout": "packed (fragment-interleaved e4m3 codes from loka_quant_fp8)"},
         "pct_fp8_peak": round(100 * main_res["tflops"] / PEAK_FP8_TFLOPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(main_res["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(main_res["gbs"] / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),

@@ -28,6 +28,7 @@ MODES = {"tensor": 0, "row": 1, "col": 2, "mx32_row": 3, "mx32_col": 4}
 STATUS = {0: "LOKA_OK", 1: "LOKA_ERR_INVALID_ARG", 2: "LOKA_ERR_UNSUPPORTED", 3: "LOKA_ERR_ALIGNMENT",
           4: "LOKA_ERR_WORKSPACE", 5: "LOKA_ERR_HIP"}
 BWD_NO_LN = 1
+FWD_W_PACKED = 1
 
 c_i64, c_i32, c_f32, c_vp, c_sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -59,7 +60,7 @@ class GroupDesc(ctypes.Structure):
 
 
 class GroupedArgs(ctypes.Structure):
-    _fields_ = [("num_groups", c_i32), ("x_mode", c_i32), ("eps", c_f32), ("reserved", c_i32),
+    _fields_ = [("num_groups", c_i32), ("x_mode", c_i32), ("eps", c_f32), ("flags", c_i32),
                 ("groups", ctypes.POINTER(GroupDesc)), ("workspace", c_vp), ("workspace_bytes", c_sz)]
 
 
@@ -134,17 +135,30 @@ def _need(t, dtype, shape, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def packed_shape(rows, cols):
+    """Shape of the codes of a [rows, cols] source quantized with
+    transpose_out="packed": cols rows of ceil(rows/128)*128 bytes (the
+    fragment-interleaved layout; not row-major)."""
+    return (cols, (rows + 127) // 128 * 128)
+
+
 def loka_quant_fp8(src, fmt="e4m3", mode="row", transpose_out=False, codes=None, scales=None, amax=None,
                    want_amax=False, workspace=None, stream=None):
-    """Quantize a 2-D bf16/fp32 CUDA tensor.  Returns (codes, scales, amax)."""
+    """Quantize a 2-D bf16/fp32 CUDA tensor.  Returns (codes, scales, amax).
+
+    transpose_out: False (codes [rows, cols]), True (codes of src^T, [cols,
+    rows]) or "packed" (codes of src^T in the fragment-interleaved layout
+    that loka_gemm_fp8_ln(w_packed=True) reads; shape packed_shape(rows, cols))."""
     if src.dim() != 2 or src.stride(1) != 1:
         raise ValueError("src must be 2-D with unit column stride")
     rows, cols = src.shape
     m = MODES[mode]
     f = FMTS[fmt]
     dev = src.device
+    trans = 2 if transpose_out == "packed" else (1 if transpose_out else 0)
     if codes is None:
-        codes = torch.empty((cols, rows) if transpose_out else (rows, cols), dtype=torch.uint8, device=dev)
+        shape = packed_shape(rows, cols) if trans == 2 else ((cols, rows) if trans else (rows, cols))
+        codes = torch.empty(shape, dtype=torch.uint8, device=dev)
     if scales is None:
         if m == 0:
             scales = torch.empty(1, dtype=torch.float32, device=dev)
@@ -160,7 +174,7 @@ def loka_quant_fp8(src, fmt="e4m3", mode="row", transpose_out=False, codes=None,
         amax = torch.empty(scales.shape, dtype=torch.float32, device=dev)
     a = QuantArgs(rows=rows, cols=cols, ld=src.stride(0) if rows > 1 else cols,
                   src_dtype=0 if src.dtype == torch.bfloat16 else 1, fmt=f, mode=m,
-                  transpose_out=1 if transpose_out else 0, src=_ptr(src), codes=_ptr(codes), scales=_ptr(scales),
+                  transpose_out=trans, src=_ptr(src), codes=_ptr(codes), scales=_ptr(scales),
                   amax=_ptr(amax))
     if src.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("src must be bfloat16 or float32")
@@ -173,18 +187,19 @@ def loka_quant_fp8(src, fmt="e4m3", mode="row", transpose_out=False, codes=None,
     return codes, scales, amax
 
 
-def _fwd_args(x, qw, sw, bias, gamma, beta, eps, x_mode, y, z, mean, rstd, qx_out, sx_out):
+def _fwd_args(x, qw, sw, bias, gamma, beta, eps, x_mode, y, z, mean, rstd, qx_out, sx_out, w_packed=False):
     M, K = x.shape
     N = qw.shape[0]
-    return FwdArgs(M=M, N=N, K=K, x_mode=MODES[x_mode], flags=0, eps=eps, x=_ptr(x), qw=_ptr(qw), sw=_ptr(sw),
+    return FwdArgs(M=M, N=N, K=K, x_mode=MODES[x_mode], flags=FWD_W_PACKED if w_packed else 0, eps=eps, x=_ptr(x), qw=_ptr(qw), sw=_ptr(sw),
                    bias=_ptr(bias), gamma=_ptr(gamma), beta=_ptr(beta), y=_ptr(y), z=_ptr(z), mean=_ptr(mean),
                    rstd=_ptr(rstd), qx_out=_ptr(qx_out), sx_out=_ptr(sx_out))
 
 
 def loka_gemm_fp8_ln(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e-5, x_mode="row", y=None, want_z=False,
-                     want_stats=False, want_qx=False, workspace=None, stream=None, prepare=False):
+                     want_stats=False, want_qx=False, workspace=None, stream=None, prepare=False, w_packed=False):
     """Y = LayerNorm(dequant(q(X) . q(W)) + bias) for bf16 X [M, K] and the
-    pre-quantized weight qw [N, K] (e4m3) with scales sw.
+    pre-quantized weight qw [N, K] (e4m3) with scales sw; with w_packed=True
+    qw is in the packed layout (loka_quant_fp8(transpose_out="packed")).
 
     Returns a dict with y and the requested optional outputs.  With
     prepare=True returns (launch, outputs) where launch() enqueues the call
@@ -193,7 +208,7 @@ def loka_gemm_fp8_ln(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e-5, x_mo
     N = qw.shape[0]
     dev = x.device
     _need(x, torch.bfloat16, (M, K), "x")
-    _need(qw, torch.uint8, (N, K), "qw")
+    _need(qw, torch.uint8, packed_shape(K, N) if w_packed else (N, K), "qw")
     for v, nm in ((bias, "bias"), (gamma, "gamma"), (beta, "beta")):
         if v is not None:
             _need(v, torch.bfloat16, (N,), nm)
@@ -212,7 +227,7 @@ def loka_gemm_fp8_ln(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e-5, x_mo
         else:
             out["sx"] = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
     a = _fwd_args(x, qw, sw, bias, gamma, beta, eps, x_mode, out["y"], out.get("z"), out.get("mean"),
-                  out.get("rstd"), out.get("qx"), out.get("sx"))
+                  out.get("rstd"), out.get("qx"), out.get("sx"), w_packed)
     lib = library()
     nb = lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(a))
     ws = _workspace(nb, dev, workspace)
@@ -286,9 +301,11 @@ def loka_gemm_fp8_bwd(dy, x, qw_row, sw_row, ctx=None, bias=None, gamma=None, no
     return out
 
 
-def loka_grouped_gemm_fp8_ln(groups, eps=1e-5, want_z=False, workspace=None, stream=None, prepare=False):
-    """groups: list of dicts with x [M,K] bf16, qw [N,K] uint8, sw [N] fp32 and
-    optional bias/gamma/beta bf16 [N].  Returns one output dict per group."""
+def loka_grouped_gemm_fp8_ln(groups, eps=1e-5, want_z=False, workspace=None, stream=None, prepare=False,
+                             w_packed=False):
+    """groups: list of dicts with x [M,K] bf16, qw [N,K] uint8 (packed layout
+    with w_packed=True), sw [N] fp32 and optional bias/gamma/beta bf16 [N].
+    Returns one output dict per group."""
     outs, keep = [], []
     descs = (GroupDesc * max(1, len(groups)))()
     for i, g in enumerate(groups):
@@ -296,7 +313,7 @@ def loka_grouped_gemm_fp8_ln(groups, eps=1e-5, want_z=False, workspace=None, str
         M, K = x.shape
         N = qw.shape[0]
         _need(x, torch.bfloat16, (M, K), f"groups[{i}].x")
-        _need(qw, torch.uint8, (N, K), f"groups[{i}].qw")
+        _need(qw, torch.uint8, packed_shape(K, N) if w_packed else (N, K), f"groups[{i}].qw")
         o = {"y": torch.empty((M, N), dtype=torch.bfloat16, device=x.device)}
         if want_z:
             o["z"] = torch.empty((M, N), dtype=torch.float32, device=x.device)
@@ -304,7 +321,8 @@ def loka_grouped_gemm_fp8_ln(groups, eps=1e-5, want_z=False, workspace=None, str
         keep.append((g, o))
         descs[i] = GroupDesc(M=M, N=N, K=K, x=_ptr(x), qw=_ptr(qw), sw=_ptr(g["sw"]), bias=_ptr(g.get("bias")),
                              gamma=_ptr(g.get("gamma")), beta=_ptr(g.get("beta")), y=_ptr(o["y"]), z=_ptr(o.get("z")))
-    a = GroupedArgs(num_groups=len(groups), x_mode=MODES["row"], eps=eps, reserved=0, groups=descs)
+    a = GroupedArgs(num_groups=len(groups), x_mode=MODES["row"], eps=eps, flags=FWD_W_PACKED if w_packed else 0,
+                    groups=descs)
     lib = library()
     nb = lib.loka_grouped_workspace_size(ctypes.byref(a))
     dev = groups[0]["x"].device if groups else torch.device("cuda")

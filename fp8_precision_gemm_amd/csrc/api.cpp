@@ -106,7 +106,7 @@ loka_status loka_quant_fp8(const loka_quant_args* a, void* stream) {
           a->src_dtype);
   REQUIRE(a->fmt == LOKA_E4M3 || a->fmt == LOKA_E5M2, LOKA_ERR_INVALID_ARG, "bad fmt %d", a->fmt);
   REQUIRE(a->mode >= LOKA_SCALE_TENSOR && a->mode <= LOKA_SCALE_MX32_COL, LOKA_ERR_INVALID_ARG, "bad mode %d", a->mode);
-  REQUIRE(a->transpose_out == 0 || a->transpose_out == 1, LOKA_ERR_INVALID_ARG, "transpose_out must be 0 or 1");
+  REQUIRE(a->transpose_out >= 0 && a->transpose_out <= 2, LOKA_ERR_INVALID_ARG, "transpose_out must be 0, 1 or 2");
   const bool mx = a->mode == LOKA_SCALE_MX32_ROW || a->mode == LOKA_SCALE_MX32_COL;
   REQUIRE(!(mx && a->amax != nullptr), LOKA_ERR_INVALID_ARG, "amax output is not defined for MX modes");
   REQUIRE(a->cols % 16 == 0, LOKA_ERR_UNSUPPORTED, "cols %% 16 != 0");
@@ -135,16 +135,21 @@ loka_status loka_quant_fp8(const loka_quant_args* a, void* stream) {
 // ---------------------------------------------------------------------------
 size_t loka_gemm_fp8_ln_workspace_size(const loka_fwd_args* a) {
   if (a == nullptr || a->M <= 0 || a->K <= 0) return 0;
-  return loka::fwd_workspace_bytes(a->M, a->N, a->K, a->x_mode);
+  return loka::fwd_workspace_bytes(a->M, a->N, a->K, a->x_mode, (a->flags & LOKA_FWD_W_PACKED) != 0);
 }
 
 loka_status loka_gemm_fp8_ln(const loka_fwd_args* a, void* stream) {
   REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
   REQUIRE(a->x_mode == LOKA_SCALE_TENSOR || a->x_mode == LOKA_SCALE_ROW || a->x_mode == LOKA_SCALE_MX32_ROW,
           LOKA_ERR_INVALID_ARG, "x_mode must be TENSOR, ROW or MX32_ROW (got %d)", a->x_mode);
-  REQUIRE(a->flags == 0, LOKA_ERR_INVALID_ARG, "flags must be 0");
+  REQUIRE((a->flags & ~LOKA_FWD_W_PACKED) == 0, LOKA_ERR_INVALID_ARG, "unknown flags %d", a->flags);
+  const bool packed = (a->flags & LOKA_FWD_W_PACKED) != 0;
   loka_status st = check_fwd_shape(a->M, a->N, a->K, a->x_mode);
   if (st != LOKA_OK) return st;
+  REQUIRE(!packed || loka::fwd_weight_resident(a->N, a->K), LOKA_ERR_UNSUPPORTED,
+          "LOKA_FWD_W_PACKED needs the weight-resident shapes: N <= 512 and K <= 1024 (N <= 256), 640 (N <= 384) "
+          "or 512 (N <= 512); got N=%lld K=%lld",
+          (long long)a->N, (long long)a->K);
   if ((st = check_eps(a->eps)) != LOKA_OK) return st;
   if (a->M > 0) REQUIRE(a->x && a->qw && a->sw && a->y, LOKA_ERR_INVALID_ARG, "x, qw, sw and y are required");
   REQUIRE_ALIGNED(a->x); REQUIRE_ALIGNED(a->qw); REQUIRE_ALIGNED(a->sw); REQUIRE_ALIGNED(a->bias);
@@ -157,6 +162,7 @@ loka_status loka_gemm_fp8_ln(const loka_fwd_args* a, void* stream) {
   f.x = a->x; f.qw = a->qw; f.sw = a->sw; f.bias = a->bias; f.gamma = a->gamma; f.beta = a->beta;
   f.y = a->y; f.z = a->z; f.mean = a->mean; f.rstd = a->rstd; f.qx_out = a->qx_out; f.sx_out = a->sx_out;
   f.workspace = a->workspace;
+  f.w_packed = packed;
   return hip_status(loka::launch_fwd(f, static_cast<hipStream_t>(stream)), "loka_gemm_fp8_ln");
 }
 
@@ -204,13 +210,15 @@ static_assert(sizeof(loka_group_desc) == sizeof(loka::GroupDev), "group descript
 
 size_t loka_grouped_workspace_size(const loka_grouped_args* a) {
   if (a == nullptr || a->num_groups <= 0) return 0;
-  return loka::grouped_workspace_bytes(a->num_groups, reinterpret_cast<const loka::GroupDev*>(a->groups));
+  return loka::grouped_workspace_bytes(a->num_groups, reinterpret_cast<const loka::GroupDev*>(a->groups),
+                                       (a->flags & LOKA_FWD_W_PACKED) != 0);
 }
 
 loka_status loka_grouped_gemm_fp8_ln(const loka_grouped_args* a, void* stream) {
   REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
   REQUIRE(a->num_groups >= 0, LOKA_ERR_INVALID_ARG, "num_groups < 0");
   REQUIRE(a->x_mode == LOKA_SCALE_ROW, LOKA_ERR_UNSUPPORTED, "grouped launch supports x_mode ROW only");
+  REQUIRE((a->flags & ~LOKA_FWD_W_PACKED) == 0, LOKA_ERR_INVALID_ARG, "unknown flags %d", a->flags);
   loka_status st = check_eps(a->eps);
   if (st != LOKA_OK) return st;
   if (a->num_groups == 0) return LOKA_OK;
@@ -240,6 +248,7 @@ loka_status loka_grouped_gemm_fp8_ln(const loka_grouped_args* a, void* stream) {
   gl.eps = a->eps;
   gl.groups = reinterpret_cast<const loka::GroupDev*>(a->groups);
   gl.workspace = a->workspace;
+  gl.w_packed = (a->flags & LOKA_FWD_W_PACKED) != 0;
   return hip_status(loka::launch_grouped(gl, static_cast<hipStream_t>(stream)), "loka_grouped_gemm_fp8_ln");
 }
 

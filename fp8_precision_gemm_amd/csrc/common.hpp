@@ -29,10 +29,14 @@ namespace loka {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 
 constexpr float kE4M3Max = 448.0f;
 constexpr float kE5M2Max = 57344.0f;
 constexpr float kFltMax = 3.40282346638528859812e+38f;
+// Fourth word of a raw buffer resource on gfx9-family parts (32-bit data
+// format, no swizzle): loads at offsets past the record count return zeros.
+constexpr int kBufferWord3 = 0x00020000;
 
 template <int FMT>
 struct Fp8Traits;

@@ -16,10 +16,11 @@
 // bytes.  A workgroup of 8 wavefronts splits the N columns into 8 slices of
 // 16*NT columns; wavefront w keeps the W^T rows of its slice for all of K in
 // VGPRs (NT x KC MFMA A-fragments, at most 128 registers per lane), loaded
-// once per workgroup: each wavefront's slice is one contiguous run of W^T,
-// read with 1 KiB coalesced loads and rearranged into fragment order through
-// a private LDS staging area, one 128-deep chunk at a time.  The workgroup
-// then walks a contiguous range of 16-row tiles.  Per tile:
+// once per workgroup straight into the fragment registers: W^T is stored in
+// the fragment-interleaved layout (ilv_offset: per 16 columns and 128-deep K
+// chunk one 2 KiB block in exactly the order the 64 lanes hold it), so each
+// fragment is two 1 KiB coalesced loads with no rearrangement on chip.  The
+// workgroup then walks a contiguous range of 16-row tiles.  Per tile:
 //   * X rows are requested D tiles ahead into registers: each wavefront owns
 //     2 rows, 32 lanes per row, 16 B per lane per 256 columns, so HBM reads
 //     stay in flight across the loop;
@@ -36,11 +37,10 @@
 //     update), then gamma/beta and bf16 stores straight from registers.
 // One barrier per tile; X is read once and Y written once.
 //
-// Column order inside a slice.  The 16 rows of MFMA tile t are mapped to
-// columns so that lane group g (lanes 16g..16g+15) ends up holding 4*nv
-// consecutive output columns of its row (nv = the slice's valid tiles):
-// tile t, A-row 4a+b <-> column c0 + 4*nv*a + 4t + b.  Y is then written with
-// 8- or 16-byte stores and the per-column vectors are contiguous float4s.
+// Column order.  MFMA tile t of wavefront w covers the 16 output columns
+// 16(w NT + t) .. +16 in order, so its A-row i is column c0 + 16t + i and
+// lane (r, g) ends up holding columns c0 + 16t + 4g .. +4 of row r: 8-byte Y
+// stores and float4 reads of the per-column vectors.
 //
 // Cast without a clamp (tensor and row recipes).  With r = RN32(448/amax)
 // every |x*r| is at most 448*(1 + 2^-23); the hardware convert rounds
@@ -57,7 +57,6 @@ namespace loka {
 namespace fwd {
 
 constexpr int kResRows = 16;  // rows per tile
-constexpr int kWst = 144;     // weight staging row stride (bytes): 128-byte chunk + 16 pad
 
 // Shapes: NT column tiles per wavefront (N <= 128*NT) and KC resident 128-deep
 // K chunks (K <= 128*KC); NT*KC fragments of 8 VGPRs stay within 128
@@ -106,10 +105,11 @@ __host__ __device__ constexpr int res_shape(int nt, int kc) {
 // LDS carve-up (bytes, every part 16-byte aligned):
 //   codes [2][16][LDX] u8 | xe8 [2][16][XE] u8 | rs [2][16] f32 |
 //   red [2][16][8] float2 | cvec [4][N] f32 (s_w, bias, gamma, beta) |
-//   wmx [3][8] f32 | wst [8][16*NT][kWst] u8 (weight staging, set-up only)
+//   wmx [3][8] f32 | ystg [8][16][32*NT + 16] (each wavefront's Y block)
 struct ResLds {
-  int codes, xe8, rs, red, cvec, wmx, wst, total;
+  int codes, xe8, rs, red, cvec, wmx, ystg, total;
 };
+__host__ __device__ constexpr int res_yst(int nt) { return 32 * nt + 16; }  // Y staging row stride (bytes)
 __host__ __device__ inline ResLds res_lds(int nt, int kc, int N) {
   const int ldx = kc * 128 + 16, xe = 16 * ((kc + 3) / 4);
   ResLds l;
@@ -119,8 +119,8 @@ __host__ __device__ inline ResLds res_lds(int nt, int kc, int N) {
   l.red = l.rs + 2 * kResRows * 4;
   l.cvec = l.red + 2 * kResRows * 8 * 8;
   l.wmx = l.cvec + 4 * N * 4;
-  l.wst = l.wmx + 32 * 4;
-  l.total = l.wst + 8 * 16 * nt * kWst;
+  l.ystg = l.wmx + 32 * 4;
+  l.total = l.ystg + kWaves * kResRows * res_yst(nt);
   return l;
 }
 
@@ -193,7 +193,7 @@ struct ResBlock {
   float2* red;
   float* cvec;
   float* wmx;
-  uint8_t* wst;
+  uint8_t* ystg;  // this wavefront's Y staging block [16][res_yst(NT)]
   float bw, bb;   // bound on |z|: row factor (tensor/row: 448^2 K max s_w; MX: 448^2 K 2^(ew_max-127)), max |bias|
   float inv_nw;   // 1 / (columns of this wavefront's slice)
 
@@ -203,8 +203,7 @@ struct ResBlock {
   // two accumulator sets: the GEMM of tile j fills one while the epilogue
   // of tile j-1 reads the other
   v4f acc0[NT], acc1[NT];
-  float cs0, cs1;   // per set: this lane's row rescale factor (power of two)
-  bool sc0, sc1;    // per set: some row of the wavefront's tile needs cs != 1
+  float cs0, cs1;   // per set: this lane's row rescale factor (power of two, 1 for ordinary rows)
   // set-up values in flight: this thread's column (tid < N) and the MX scale bytes
   float cv_sw;
   uint16_t cv_b, cv_g, cv_be;
@@ -237,23 +236,28 @@ struct ResBlock {
     red = reinterpret_cast<float2*>(smem + l.red);
     cvec = reinterpret_cast<float*>(smem + l.cvec);
     wmx = reinterpret_cast<float*>(smem + l.wmx);
-    wst = smem + l.wst + wave * (16 * NT * kWst);
+    ystg = smem + l.ystg + wave * (kResRows * res_yst(NT));
   }
 
   // ---- X row of tile `t` for this lane into register slot S: elements
-  // 256q + 8*hl .. +8 (row clamped to M-1 and columns to K-8: the duplicates
-  // never change a max and are never stored)
+  // 256q + 8*hl .. +8.  The tile is read through a bounds-checked buffer
+  // that covers only its rows inside both M and the workgroup's range, so
+  // rows past M and tiles past the range read as zeros without a branch (a
+  // zero never changes a max, and such rows are never stored); columns are
+  // clamped to K-8 (duplicates, never stored either).
   template <int S>
   __device__ __forceinline__ void load_x(int64_t t) {
-    if (t >= te) return;
-    int64_t m = t * kResRows + hrow;
-    m = m < p.M ? m : p.M - 1;
-    const uint16_t* xrow = p.x + m * K;
+    const int64_t row0 = min(t * kResRows, p.M);
+    const int64_t left = min(min(te * kResRows, p.M) - row0, (int64_t)kResRows);
+    const int bytes = left > 0 ? (int)left * K * 2 : 0;
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x + row0 * K), (short)0, bytes, kBufferWord3);
+    const uint32_t rb = (uint32_t)hrow * (uint32_t)(2 * K);
 #pragma unroll
     for (int q = 0; q < KQ; ++q) {
       int k = q * 256 + hl * 8;
       if (!FULL) k = k < K ? k : K - 8;
-      xr[S][q] = *reinterpret_cast<const uint4*>(xrow + k);
+      xr[S][q] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, rb + 2 * (uint32_t)k, 0, 0));
     }
   }
 
@@ -343,29 +347,40 @@ struct ResBlock {
     }
   }
 
-  // ---- set-up, part 1: request the weight slice (coalesced, into the
-  // fragment registers as raw storage), its MX scale bytes and this
-  // thread's column vectors; nothing here waits for a load
+  // ---- set-up, part 1: this thread's column vectors and the MX scale
+  // bytes, then the weight slice straight into the fragment registers
+  // (fragment-interleaved W^T: lane l reads bytes 16l of both 1 KiB halves
+  // of each 2 KiB block; chunks in the order the GEMM uses them).  Nothing
+  // here waits for a load; the vectors come first so that staging them does
+  // not wait for the weight.
   __device__ __forceinline__ void request_weights() {
-    // raw piece q of chunk c: slice row 8q + lane/8, bytes c*128 + 16*(lane%8)
-    const int sub = lane >> 3, off = (lane & 7) * 16;
-    const uint8_t* base = p.qw + (int64_t)(c0 + sub) * K + off;
+    request_vectors();
+    const int64_t nch = (K + 127) >> 7;
+    const uint8_t* base = p.qw + (int64_t)(wave * NT) * nch * 2048 + lane * 16;
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
 #pragma unroll
-      for (int q = 0; q < 2 * NT; ++q) {
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (FULL || (q < 2 * nv && c < kcv && c * 128 + off < K))
-          u = *reinterpret_cast<const uint4*>(base + (int64_t)(8 * q) * K + c * 128);
-        const int t = q >> 1, h = (q & 1) * 4;
-        wf[t][c][h] = (int)u.x; wf[t][c][h + 1] = (int)u.y; wf[t][c][h + 2] = (int)u.z; wf[t][c][h + 3] = (int)u.w;
+      for (int t = 0; t < NT; ++t) {
+        uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
+        if (FULL || (tv(t) && c < kcv)) {
+          const uint8_t* blk = base + ((int64_t)t * nch + c) * 2048;
+          a = *reinterpret_cast<const uint4*>(blk);
+          b = *reinterpret_cast<const uint4*>(blk + 1024);
+        }
+        v8i f;
+        f[0] = (int)a.x; f[1] = (int)a.y; f[2] = (int)a.z; f[3] = (int)a.w;
+        f[4] = (int)b.x; f[5] = (int)b.y; f[6] = (int)b.z; f[7] = (int)b.w;
+        wf[t][c] = f;
       }
     }
+  }
+
+  __device__ __forceinline__ void request_vectors() {
     if (MODE == 3) {
       const uint8_t* sw8 = static_cast<const uint8_t*>(p.sw);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const int col = c0 + 4 * nv * (r >> 2) + 4 * t + (r & 3);
+        const int col = c0 + 16 * t + r;
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
           const int blk = 4 * c + g;
@@ -381,37 +396,9 @@ struct ResBlock {
     }
   }
 
-  // ---- set-up, part 2: weight fragments through the staging area, MX
-  // scale words, column vectors into LDS with their maxima, LDS padding
-  __device__ __forceinline__ void stage_weights() {
-    const int sub = lane >> 3, off = (lane & 7) * 16;
-#pragma unroll
-    for (int c = 0; c < KC; ++c) {
-      if (!FULL && c >= kcv) break;
-#pragma unroll
-      for (int q = 0; q < 2 * NT; ++q) {
-        if (FULL || q < 2 * nv) {
-          const int t = q >> 1, h = (q & 1) * 4;
-          *reinterpret_cast<uint4*>(wst + (8 * q + sub) * kWst + off) =
-              make_uint4((uint32_t)wf[t][c][h], (uint32_t)wf[t][c][h + 1], (uint32_t)wf[t][c][h + 2],
-                         (uint32_t)wf[t][c][h + 3]);
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        v8i f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) f[i] = 0;
-        if (tv(t)) {
-          const uint8_t* src = wst + (4 * nv * (r >> 2) + 4 * t + (r & 3)) * kWst + 16 * g;
-          const uint4 a = *reinterpret_cast<const uint4*>(src);
-          const uint4 b = *reinterpret_cast<const uint4*>(src + 64);
-          f[0] = (int)a.x; f[1] = (int)a.y; f[2] = (int)a.z; f[3] = (int)a.w;
-          f[4] = (int)b.x; f[5] = (int)b.y; f[6] = (int)b.z; f[7] = (int)b.w;
-        }
-        wf[t][c] = f;
-      }
-    }
+  // ---- set-up, part 2: MX scale words, column vectors into LDS with their
+  // maxima, LDS padding
+  __device__ __forceinline__ void stage_vectors() {
     float msw = 0.0f, mb = 0.0f, ewm = 0.0f;
     if (MODE == 3) {
 #pragma unroll
@@ -511,19 +498,18 @@ struct ResBlock {
 
   // ---- epilogue, part 1: z = dequant(acc) + b in place; this slice's row
   // sum and centred sum of squares to LDS
-  __device__ __forceinline__ void epilogue_stats(int buf, v4f (&acc)[NT], float& cs, bool& scaled) {
+  __device__ __forceinline__ void epilogue_stats(int buf, v4f (&acc)[NT], float& cs) {
     const float rsv = rs[buf * kResRows + r];
     const float sx = MODE == 1 ? rsv : (MODE == 0 ? p.x_s : 1.0f);
     const float bound = MODE == 3 ? ldexpf(bw, (int)rsv - 127) + bb : sx * bw + bb;
     cs = row_rescale(bound);
-    scaled = __builtin_amdgcn_ballot_w64(cs != 1.0f) != 0;
-    const float* cb = cvec + c0 + 4 * nv * g;
+    const float* cb = cvec + c0 + 4 * g;
     float s = 0.0f;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (tv(t)) {
-        const float4 sw4 = *reinterpret_cast<const float4*>(cb + 4 * t);
-        const float4 b4 = *reinterpret_cast<const float4*>(cb + N + 4 * t);
+        const float4 sw4 = *reinterpret_cast<const float4*>(cb + 16 * t);
+        const float4 b4 = *reinterpret_cast<const float4*>(cb + N + 16 * t);
         const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -535,32 +521,25 @@ struct ResBlock {
     }
     s = sum4(s);
     const float mw = s * inv_nw;
+    // deviations scaled by cs before squaring (rows too large to square in
+    // fp32); one fma rounds (z - mw) * cs once, which for cs = 1 is z - mw
+    // and otherwise its exact power-of-two scaling: no branch on the rare case
+    const float nmc = -mw * cs;
     float q = 0.0f;
-    if (!scaled) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-        if (tv(t))
+    for (int t = 0; t < NT; ++t)
+      if (tv(t))
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float d = acc[t][j] - mw;
-            q = fmaf(d, d, q);
-          }
-    } else {  // rows too large to square in fp32 (rare): deviations scaled by cs first
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        if (tv(t))
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float d = (acc[t][j] - mw) * cs;
-            q = fmaf(d, d, q);
-          }
-    }
+        for (int j = 0; j < 4; ++j) {
+          const float d = fmaf(acc[t][j], cs, nmc);
+          q = fmaf(d, d, q);
+        }
     q = sum4(q);
     red[(buf * kResRows + r) * kWaves + wave] = make_float2(s, q);  // the row's 4 lanes write the same pair
   }
 
   // ---- epilogue, part 2 (after the barrier): combine the slices, normalize, store
-  __device__ __forceinline__ void epilogue_out(int buf, int64_t t, const v4f (&acc)[NT], float cs, bool scaled) {
+  __device__ __forceinline__ void epilogue_out(int buf, int64_t t, const v4f (&acc)[NT], float cs) {
     const float4* rw4 = reinterpret_cast<const float4*>(red + (buf * kResRows + r) * kWaves);
     float sw_[kWaves], qw_[kWaves];
 #pragma unroll
@@ -577,22 +556,21 @@ struct ResBlock {
     const float invn = 1.0f / (float)N;
     const float mean = S * invn;
     // between-slice term: sum_w (s_w - n_w mean)^2 / n_w, with the
-    // deviations scaled by cs first on the (rare) rescaled path, like the
-    // within-slice sums
+    // deviations scaled by cs like the within-slice sums (cs = 1: unscaled)
     float B = 0.0f;
-    const float dsc = scaled ? cs : 1.0f;
     if (FULL || N == 128 * NT) {  // every slice has 16*NT columns
       const float ns = (float)(16 * NT);
-      if (!scaled) {
+      if ((NT & (NT - 1)) == 0) {  // ns and cs powers of two: -ns*mean*cs is exact
+        const float nsm = -ns * mean * cs;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          const float d = fmaf(-ns, mean, sw_[w]);
+          const float d = fmaf(sw_[w], cs, nsm);
           B = fmaf(d, d, B);
         }
       } else {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-          const float d = fmaf(-ns, mean, sw_[w]) * dsc;
+          const float d = fmaf(-ns, mean, sw_[w]) * cs;
           B = fmaf(d, d, B);
         }
       }
@@ -602,51 +580,58 @@ struct ResBlock {
       for (int w = 0; w < kWaves; ++w) {
         const int nw = 16 * min(max(T16 - w * NT, 0), NT);
         if (nw > 0) {
-          const float d = fmaf(-(float)nw, mean, sw_[w]) * dsc;
+          const float d = fmaf(-(float)nw, mean, sw_[w]) * cs;
           B = fmaf(d * (1.0f / (float)nw), d, B);
         }
       }
     }
-    const float rstd = !scaled ? __builtin_amdgcn_rsqf(fmaf(Q + B, invn, p.eps))
-                               : cs * __builtin_amdgcn_rsqf(fmaf(Q + B, invn, p.eps * cs * cs));
+    // variance of the scaled deviations is var * cs^2: rstd = cs / sqrt(var cs^2 + eps cs^2)
+    const float rstd = cs * __builtin_amdgcn_rsqf(fmaf(Q + B, invn, p.eps * cs * cs));
     const int64_t m = t * kResRows + r;
-    if (!FULL && m >= p.M) return;
-    if (OPT && wave == 0 && g == 0) {
+    const bool row_ok = FULL || m < p.M;
+    if (OPT && row_ok && wave == 0 && g == 0) {
       if (p.mean) p.mean[m] = mean;
       if (p.rstd) p.rstd[m] = rstd;
     }
     const float nmr = -mean * rstd;
-    const int cl = c0 + 4 * nv * g;  // this lane's first column
+    const int cl = c0 + 4 * g;  // this lane's first column (tile t adds 16t)
     const float* gb = cvec + 2 * N + cl;
-    uint32_t packed[NT][2];
+    constexpr int YST = res_yst(NT);
 #pragma unroll
     for (int t2 = 0; t2 < NT; ++t2) {
-      packed[t2][0] = packed[t2][1] = 0u;
       if (tv(t2)) {
-        const float4 ga = *reinterpret_cast<const float4*>(gb + 4 * t2);
-        const float4 be = *reinterpret_cast<const float4*>(gb + N + 4 * t2);
+        const float4 ga = *reinterpret_cast<const float4*>(gb + 16 * t2);
+        const float4 be = *reinterpret_cast<const float4*>(gb + N + 16 * t2);
         const float gv[4] = {ga.x, ga.y, ga.z, ga.w}, bv[4] = {be.x, be.y, be.z, be.w};
         float o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = fmaf(fmaf(acc[t2][j], rstd, nmr), gv[j], bv[j]);
-        packed[t2][0] = pack_bf16_hw(o[0], o[1]);
-        packed[t2][1] = pack_bf16_hw(o[2], o[3]);
-        if (OPT && p.z != nullptr)
-          *reinterpret_cast<float4*>(p.z + m * N + cl + 4 * t2) =
+        *reinterpret_cast<uint2*>(ystg + r * YST + (16 * t2 + 4 * g) * 2) =
+            make_uint2(pack_bf16_hw(o[0], o[1]), pack_bf16_hw(o[2], o[3]));
+        if (OPT && p.z != nullptr && row_ok)
+          *reinterpret_cast<float4*>(p.z + m * N + cl + 16 * t2) =
               make_float4(acc[t2][0], acc[t2][1], acc[t2][2], acc[t2][3]);
       }
     }
-    uint16_t* yrow = p.y + m * N + cl;
-    if ((nv & 1) == 0) {  // 16-byte aligned pairs of tiles
+    // The wavefront's 16 x 16*NT block of Y goes out from the staging rows in
+    // 16-byte pieces, consecutive lanes along a row: each store instruction
+    // writes whole 32*NT-byte row segments (for NT = 4, eight 128-byte
+    // lines), as non-temporal (streaming) stores: Y is not read again here,
+    // and streaming it keeps the write-back of one launch from holding up
+    // the next launch's loads.  LDS operations of one wavefront complete in
+    // order, so the reads see the writes above and the next tile's writes
+    // come after them.
+    constexpr int CPR = 2 * NT, TOT = kResRows * CPR;  // 16-byte pieces per row / per block
 #pragma unroll
-      for (int t2 = 0; t2 + 1 < NT; t2 += 2)
-        if (tv(t2))
-          *reinterpret_cast<uint4*>(yrow + 4 * t2) =
-              make_uint4(packed[t2][0], packed[t2][1], packed[t2 + 1][0], packed[t2 + 1][1]);
-    } else {
-#pragma unroll
-      for (int t2 = 0; t2 < NT; ++t2)
-        if (tv(t2)) *reinterpret_cast<uint2*>(yrow + 4 * t2) = make_uint2(packed[t2][0], packed[t2][1]);
+    for (int i = 0; i < (TOT + 63) / 64; ++i) {
+      const int u = lane + 64 * i;
+      if (TOT % 64 == 0 || u < TOT) {
+        const int row = u / CPR, ch = u - row * CPR;
+        const uint4 v = *reinterpret_cast<const uint4*>(ystg + row * YST + ch * 16);
+        const int64_t mm = t * kResRows + row;
+        if (FULL || (mm < p.M && ch < 2 * nv))
+          __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p.y + mm * N + c0 + ch * 8));
+      }
     }
   }
 
@@ -673,11 +658,11 @@ struct ResBlock {
     v4f (&cur)[NT] = A ? acc1 : acc0;
     v4f (&prev)[NT] = A ? acc0 : acc1;
     mma(buf, cur);
-    epilogue_out(buf ^ 1, t - 1, prev, A ? cs0 : cs1, A ? sc0 : sc1);
+    epilogue_out(buf ^ 1, t - 1, prev, A ? cs0 : cs1);
     quantize<S1>(t + 1, buf ^ 1);
     if (FULL && !OPT) interleave_hint();
     load_x<S1>(t + 1 + D);
-    epilogue_stats(buf, cur, A ? cs1 : cs0, A ? sc1 : sc0);
+    epilogue_stats(buf, cur, A ? cs1 : cs0);
     __syncthreads();
   }
 
@@ -690,9 +675,9 @@ struct ResBlock {
     mma(buf, acc0);
     quantize<0>(t + 1, buf ^ 1);
     load_x<0>(t + 2);
-    epilogue_stats(buf, acc0, cs0, sc0);
+    epilogue_stats(buf, acc0, cs0);
     __syncthreads();
-    epilogue_out(buf, t, acc0, cs0, sc0);
+    epilogue_out(buf, t, acc0, cs0);
   }
 
   __device__ __forceinline__ void run() {
@@ -708,7 +693,7 @@ struct ResBlock {
     if (D > 3) load_x<(3 % D)>(tb + 3);
     quantize<0>(tb, 0);
     load_x<0>(tb + D);
-    stage_weights();
+    stage_vectors();
     __syncthreads();
     read_bounds();
     if (!PIPE) {
@@ -720,7 +705,7 @@ struct ResBlock {
     quantize<(1 % D)>(tb + 1, 1);
     if (FULL && !OPT) interleave_hint();
     load_x<(1 % D)>(tb + 1 + D);
-    epilogue_stats(0, acc0, cs0, sc0);
+    epilogue_stats(0, acc0, cs0);
     __syncthreads();
     const int64_t n = te - tb;
     // step j quantizes tile j+1 from slot (j+1) % D and fills accumulator set j % 2
@@ -746,8 +731,8 @@ struct ResBlock {
     }
     // the last tile's normalization and stores
     const int64_t l = n - 1;
-    if (l & 1) epilogue_out(1, tb + l, acc1, cs1, sc1);
-    else epilogue_out(0, tb + l, acc0, cs0, sc0);
+    if (l & 1) epilogue_out(1, tb + l, acc1, cs1);
+    else epilogue_out(0, tb + l, acc0, cs0);
   }
 };
 

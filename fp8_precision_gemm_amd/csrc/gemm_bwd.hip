@@ -22,7 +22,7 @@
 // Every FP8 operand the kernels read as MFMA fragments straight from memory
 // (both weights, the transposed X and dZ codes) is first laid out in the
 // fragment-interleaved order of ilv_offset(), so each 16-lane fragment load
-// reads 256 contiguous bytes (k_relayout does it for the weights; the
+// reads 256 contiguous bytes (launch_relayout does it for the weights; the
 // transposing casts write it directly).
 #include "common.hpp"
 #include "launch.hpp"
@@ -39,18 +39,6 @@ namespace {
 constexpr int kMT = 4;           // 64 rows per workgroup
 constexpr int kBM = 16 * kMT;
 constexpr int kWgSplitRows = 1024;  // M rows per wgrad slice
-
-// [R][C] row-major bytes -> fragment-interleaved (C padded to 128 with zeros).
-// One thread per 16-byte piece.
-__global__ __launch_bounds__(256) void k_relayout(const uint8_t* src, int R, int C, uint8_t* dst) {
-  const int64_t nch = (C + 127) / 128, pieces = nch * 8;
-  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (u >= (int64_t)R * pieces) return;
-  const int64_t row = u / pieces, col = (u - row * pieces) * 16;
-  uint4 v = make_uint4(0, 0, 0, 0);
-  if (col < C) v = *reinterpret_cast<const uint4*>(src + row * C + col);
-  *reinterpret_cast<uint4*>(dst + ilv_offset(row, col, nch)) = v;
-}
 
 struct BwdBlock {
   int64_t M;
@@ -554,13 +542,8 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
 
   hipError_t e;
   {  // both weights into the fragment-interleaved order
-    const int64_t kp = (a.K + 127) / 128 * 8, np_ = (a.N + 127) / 128 * 8;
-    if (!a.no_ln)
-      hipLaunchKernelGGL(k_relayout, dim3((unsigned)((a.N * kp + 255) / 256)), dim3(256), 0, s, a.qw, (int)a.N,
-                         (int)a.K, ws + w.qwi);
-    hipLaunchKernelGGL(k_relayout, dim3((unsigned)((a.K * np_ + 255) / 256)), dim3(256), 0, s, a.qw_row, (int)a.K,
-                       (int)a.N, ws + w.qwri);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!a.no_ln && (e = launch_relayout(a.qw, a.N, a.K, ws + w.qwi, s)) != hipSuccess) return e;
+    if ((e = launch_relayout(a.qw_row, a.K, a.N, ws + w.qwri, s)) != hipSuccess) return e;
   }
   const int nt = (int)a.N / 64, kt = (int)a.K / 64;
   if (nt <= 8 && kt <= 8) e = launch_main_t<8, 8>(p, a.no_ln, s);

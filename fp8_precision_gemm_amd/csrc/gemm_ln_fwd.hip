@@ -17,10 +17,39 @@ hipError_t launch_mx(const FwdBlock& p, const float* partials, int np, hipStream
 
 bool fwd_weight_resident(int64_t N, int64_t K) { return N <= 512 && K <= 2048 && fwd::res_fits((int)K, (int)N); }
 
-size_t fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int x_mode) {
-  (void)N;
-  if (x_mode != 0) return 0;
-  return (size_t)quant_plan(M, K, 0).np * sizeof(float);
+namespace {
+
+// [R][C] row-major bytes -> fragment-interleaved (C padded to 128 with zeros).
+// One thread per 16-byte piece of the destination, in destination order.
+__global__ __launch_bounds__(256) void k_relayout(const uint8_t* src, int64_t R, int64_t C, uint8_t* dst) {
+  const int64_t nch = (C + 127) / 128, pieces = nch * 8;
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= R * pieces) return;
+  const int64_t row = u / pieces, col = (u - row * pieces) * 16;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (col < C) v = *reinterpret_cast<const uint4*>(src + row * C + col);
+  *reinterpret_cast<uint4*>(dst + ilv_offset(row, col, nch)) = v;
+}
+
+size_t align256(size_t b) { return (b + 255) / 256 * 256; }
+
+size_t partial_bytes(int64_t M, int64_t K, int x_mode) {
+  return x_mode == 0 ? align256((size_t)quant_plan(M, K, 0).np * sizeof(float)) : 0;
+}
+
+}  // namespace
+
+hipError_t launch_relayout(const uint8_t* src, int64_t R, int64_t C, uint8_t* dst, hipStream_t s) {
+  const int64_t n = R * ((C + 127) / 128) * 8;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_relayout, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, src, R, C, dst);
+  return hipGetLastError();
+}
+
+size_t fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int x_mode, bool w_packed) {
+  size_t b = partial_bytes(M, K, x_mode);
+  if (!w_packed && fwd_weight_resident(N, K)) b += ilv_bytes(N, K);
+  return b;
 }
 
 hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s) {
@@ -35,6 +64,13 @@ hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s) {
   p.y = static_cast<uint16_t*>(a.y);
   p.z = a.z; p.mean = a.mean; p.rstd = a.rstd; p.qx_out = a.qx_out; p.sx_out = a.sx_out;
   p.eps = a.eps; p.x_r = 1.0f; p.x_s = 1.0f;
+  if (!a.w_packed && fwd_weight_resident(a.N, a.K)) {
+    // the resident kernel reads the weight fragment-interleaved
+    uint8_t* wi = static_cast<uint8_t*>(a.workspace) + partial_bytes(a.M, a.K, a.x_mode);
+    hipError_t e = launch_relayout(a.qw, a.N, a.K, wi, s);
+    if (e != hipSuccess) return e;
+    p.qw = wi;
+  }
   if (a.x_mode == 0) {
     float* partials = static_cast<float*>(a.workspace);
     const int np = (int)quant_plan(a.M, a.K, 0).np;

@@ -17,7 +17,10 @@
 //     empty) and the first tile of every persistent workgroup, chosen so
 //     that each workgroup gets an equal share of the estimated cost (bytes
 //     moved per tile, 32(K_g+N_g), plus a fixed per-tile term).
-//  2. per class present, k_grouped_res<NT, FULL> (one persistent workgroup
+//  2. without packed weights, k_relayout_groups rearranges every group's
+//     row-major weight into the fragment-interleaved layout the resident
+//     block reads (group g at g * stride in the workspace);
+//  3. per class present, k_grouped_res<NT, FULL> (one persistent workgroup
 //     per compute unit) walks its contiguous range of the class's tiles
 //     group by group; for each group it loads that group's weight into
 //     registers and runs exactly the weight-resident block of the single
@@ -33,6 +36,29 @@ namespace {
 
 constexpr int kPlanThreads = 1024;
 constexpr int kMaxGroups = 2048;
+
+// Where the groups' fragment-interleaved weights are: the descriptors' own
+// qw (base == nullptr) or the workspace copy of group g at base + g*stride.
+struct WeightSrc {
+  const uint8_t* base;
+  int64_t stride;
+};
+__device__ __forceinline__ const uint8_t* group_weight(const WeightSrc& w, const GroupDev& gd, int g) {
+  return w.base != nullptr ? w.base + (int64_t)g * w.stride : gd.qw;
+}
+
+// Every group's [N][K] weight codes -> fragment-interleaved at dst + g*stride
+// (grid.y = group, one thread per 16-byte destination piece).
+__global__ __launch_bounds__(256) void k_relayout_groups(const GroupDev* groups, uint8_t* dst, int64_t stride) {
+  const GroupDev gd = groups[blockIdx.y];
+  const int64_t nch = (gd.K + 127) / 128, pieces = nch * 8;
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= gd.N * pieces) return;
+  const int64_t row = u / pieces, col = (u - row * pieces) * 16;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (col < gd.K) v = *reinterpret_cast<const uint4*>(gd.qw + row * gd.K + col);
+  *reinterpret_cast<uint4*>(dst + (int64_t)blockIdx.y * stride + ilv_offset(row, col, nch)) = v;
+}
 
 // estimated cost of one 16-row tile: bytes of X read and Y written, plus a
 // fixed term for the per-tile reductions and synchronization
@@ -143,7 +169,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_grouped_plan(const GroupDev* g
 
 template <bool OPT, int NT, int KC, bool FULL>
 __global__ __launch_bounds__(kThreads) void k_grouped_res(const GroupDev* groups, const int* tile_pre,
-                                                          const int* wg_start, int G, float eps) {
+                                                          const int* wg_start, int G, float eps, WeightSrc wsrc) {
   extern __shared__ __align__(16) uint8_t smem[];
   int t = wg_start[blockIdx.x];
   const int tend = wg_start[blockIdx.x + 1];
@@ -161,7 +187,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped_res(const GroupDev* groups
     FwdBlock p;
     p.M = gd.M; p.N = (int)gd.N; p.K = (int)gd.K;
     p.x = static_cast<const uint16_t*>(gd.x);
-    p.qw = gd.qw; p.sw = gd.sw;
+    p.qw = group_weight(wsrc, gd, g); p.sw = gd.sw;
     p.bias = static_cast<const uint16_t*>(gd.bias);
     p.gamma = static_cast<const uint16_t*>(gd.gamma);
     p.beta = static_cast<const uint16_t*>(gd.beta);
@@ -178,7 +204,8 @@ __global__ __launch_bounds__(kThreads) void k_grouped_res(const GroupDev* groups
 
 // the same walk, with the plan as an argument (group index through gid)
 template <bool OPT, int NT, int KC, bool FULL>
-__global__ __launch_bounds__(kThreads) void k_grouped_res_arg(const GroupDev* groups, GroupPlan plan, float eps) {
+__global__ __launch_bounds__(kThreads) void k_grouped_res_arg(const GroupDev* groups, GroupPlan plan, float eps,
+                                                              WeightSrc wsrc) {
   extern __shared__ __align__(16) uint8_t smem[];
   int t = plan.wg_start[blockIdx.x];
   const int tend = plan.wg_start[blockIdx.x + 1];
@@ -196,7 +223,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped_res_arg(const GroupDev* gr
     FwdBlock p;
     p.M = gd.M; p.N = (int)gd.N; p.K = (int)gd.K;
     p.x = static_cast<const uint16_t*>(gd.x);
-    p.qw = gd.qw; p.sw = gd.sw;
+    p.qw = group_weight(wsrc, gd, plan.gid[q]); p.sw = gd.sw;
     p.bias = static_cast<const uint16_t*>(gd.bias);
     p.gamma = static_cast<const uint16_t*>(gd.gamma);
     p.beta = static_cast<const uint16_t*>(gd.beta);
@@ -212,23 +239,24 @@ __global__ __launch_bounds__(kThreads) void k_grouped_res_arg(const GroupDev* gr
 }
 
 template <bool OPT, int NT, int KC, bool FULL>
-hipError_t launch_class_arg(const GroupDev* dg, const GroupPlan& plan, size_t lds, float eps, hipStream_t s) {
+hipError_t launch_class_arg(const GroupDev* dg, const GroupPlan& plan, size_t lds, float eps, WeightSrc w,
+                            hipStream_t s) {
   auto kern = k_grouped_res_arg<OPT, NT, KC, FULL>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)plan.grid), dim3(kThreads), lds, s, dg, plan, eps);
+  hipLaunchKernelGGL(kern, dim3((unsigned)plan.grid), dim3(kThreads), lds, s, dg, plan, eps, w);
   return hipGetLastError();
 }
 
 template <bool OPT, int NT, int KC, bool FULL>
 hipError_t launch_class(const GroupDev* dg, const int* tp, const int* ws, int G, int grid, size_t lds, float eps,
-                        hipStream_t s) {
+                        WeightSrc w, hipStream_t s) {
   auto kern = k_grouped_res<OPT, NT, KC, FULL>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, s, dg, tp, ws, G, eps);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, s, dg, tp, ws, G, eps, w);
   return hipGetLastError();
 }
 
@@ -237,12 +265,29 @@ hipError_t launch_class(const GroupDev* dg, const int* tp, const int* ws, int G,
 
 int grouped_max_groups() { return fwd::kMaxGroups; }
 
-// workspace: [ descriptors | tile_pre [8][G+1] | wg_start [8][1025] ]
-size_t grouped_workspace_bytes(int num_groups, const GroupDev* groups) {
-  (void)groups;
+namespace {
+// stride of the packed weight copies: the largest group's, 256-byte aligned
+size_t packed_stride(int num_groups, const GroupDev* groups) {
+  size_t m = 0;
+  for (int i = 0; i < num_groups; ++i) {
+    const size_t b = ilv_bytes(groups[i].N, groups[i].K);
+    if (b > m) m = b;
+  }
+  return (m + 255) / 256 * 256;
+}
+size_t plan_bytes(int num_groups) {
   size_t b = ((size_t)num_groups * sizeof(GroupDev) + 255) / 256 * 256;
   b += ((size_t)fwd::kClasses * (num_groups + 1) * sizeof(int) + 255) / 256 * 256;
-  b += (size_t)fwd::kClasses * (fwd::kMaxGrid + 1) * sizeof(int);
+  b += ((size_t)fwd::kClasses * (fwd::kMaxGrid + 1) * sizeof(int) + 255) / 256 * 256;
+  return b;
+}
+}  // namespace
+
+// workspace: [ descriptors | tile_pre [classes][G+1] | wg_start [classes][kMaxGrid+1] |
+//              packed weights [G][stride] (without LOKA_FWD_W_PACKED) ]
+size_t grouped_workspace_bytes(int num_groups, const GroupDev* groups, bool w_packed) {
+  size_t b = plan_bytes(num_groups);
+  if (!w_packed) b += (size_t)num_groups * packed_stride(num_groups, groups);
   return b;
 }
 
@@ -278,6 +323,20 @@ hipError_t launch_grouped(const GroupedLaunch& a, hipStream_t s) {
   // until the copy has run)
   e = hipMemcpyAsync(dgroups, a.groups, (size_t)G * sizeof(GroupDev), hipMemcpyHostToDevice, s);
   if (e != hipSuccess) return e;
+  fwd::WeightSrc wsrc{nullptr, 0};
+  if (!a.w_packed) {
+    const size_t stride = packed_stride(G, a.groups);
+    int64_t pieces = 0;
+    for (int gi = 0; gi < G; ++gi) {
+      const int64_t pc = a.groups[gi].N * ((a.groups[gi].K + 127) / 128) * 8;
+      if (pc > pieces) pieces = pc;
+    }
+    uint8_t* wpk = ws + plan_bytes(G);
+    hipLaunchKernelGGL(fwd::k_relayout_groups, dim3((unsigned)((pieces + 255) / 256), (unsigned)G), dim3(256), 0, s,
+                       dgroups, wpk, (int64_t)stride);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    wsrc = fwd::WeightSrc{wpk, (int64_t)stride};
+  }
   // host plans (passed by value) when every class fits GroupPlan
   int ngc[fwd::kClasses] = {0};
   for (int gi = 0; gi < G; ++gi) {
@@ -327,12 +386,12 @@ hipError_t launch_grouped(const GroupedLaunch& a, hipStream_t s) {
       }
 #define LOKA_CLASS(S, NT, KC)                                                                     \
   case 2 * S:                                                                                    \
-    e = opt ? fwd::launch_class_arg<true, NT, KC, false>(dgroups, plan, lds[c], a.eps, s)        \
-            : fwd::launch_class_arg<false, NT, KC, false>(dgroups, plan, lds[c], a.eps, s);      \
+    e = opt ? fwd::launch_class_arg<true, NT, KC, false>(dgroups, plan, lds[c], a.eps, wsrc, s)        \
+            : fwd::launch_class_arg<false, NT, KC, false>(dgroups, plan, lds[c], a.eps, wsrc, s);      \
     break;                                                                                       \
   case 2 * S + 1:                                                                                \
-    e = opt ? fwd::launch_class_arg<true, NT, KC, true>(dgroups, plan, lds[c], a.eps, s)         \
-            : fwd::launch_class_arg<false, NT, KC, true>(dgroups, plan, lds[c], a.eps, s);       \
+    e = opt ? fwd::launch_class_arg<true, NT, KC, true>(dgroups, plan, lds[c], a.eps, wsrc, s)         \
+            : fwd::launch_class_arg<false, NT, KC, true>(dgroups, plan, lds[c], a.eps, wsrc, s);       \
     break;
       switch (c) {
         LOKA_CLASS(1, 1, 4) LOKA_CLASS(2, 1, 8) LOKA_CLASS(4, 2, 4) LOKA_CLASS(5, 2, 8) LOKA_CLASS(7, 3, 4)
@@ -353,12 +412,12 @@ hipError_t launch_grouped(const GroupedLaunch& a, hipStream_t s) {
     const int* wsc = wg_start + c * (fwd::kMaxGrid + 1);
 #define LOKA_CLASS(S, NT, KC)                                                                                \
   case 2 * S:                                                                                               \
-    e = opt ? fwd::launch_class<true, NT, KC, false>(dgroups, tp, wsc, G, grid, lds[c], a.eps, s)           \
-            : fwd::launch_class<false, NT, KC, false>(dgroups, tp, wsc, G, grid, lds[c], a.eps, s);         \
+    e = opt ? fwd::launch_class<true, NT, KC, false>(dgroups, tp, wsc, G, grid, lds[c], a.eps, wsrc, s)           \
+            : fwd::launch_class<false, NT, KC, false>(dgroups, tp, wsc, G, grid, lds[c], a.eps, wsrc, s);         \
     break;                                                                                                  \
   case 2 * S + 1:                                                                                           \
-    e = opt ? fwd::launch_class<true, NT, KC, true>(dgroups, tp, wsc, G, grid, lds[c], a.eps, s)            \
-            : fwd::launch_class<false, NT, KC, true>(dgroups, tp, wsc, G, grid, lds[c], a.eps, s);          \
+    e = opt ? fwd::launch_class<true, NT, KC, true>(dgroups, tp, wsc, G, grid, lds[c], a.eps, wsrc, s)            \
+            : fwd::launch_class<false, NT, KC, true>(dgroups, tp, wsc, G, grid, lds[c], a.eps, wsrc, s);          \
     break;
     switch (c) {
       LOKA_CLASS(1, 1, 4) LOKA_CLASS(2, 1, 8) LOKA_CLASS(4, 2, 4) LOKA_CLASS(5, 2, 8) LOKA_CLASS(7, 3, 4)

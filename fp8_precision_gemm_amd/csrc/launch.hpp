@@ -46,8 +46,17 @@ struct FwdLaunch {
   uint8_t* qx_out;
   void* sx_out;
   void* workspace;
+  bool w_packed;  // qw already in the fragment-interleaved layout
 };
-size_t fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int x_mode);
+// Workspace of one forward: the tensor recipe's amax partials, then (for
+// the weight-resident kernel with a row-major weight) the weight rearranged
+// into the fragment-interleaved layout.
+size_t fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int x_mode, bool w_packed);
+// Bytes of a [R][C] code array in the fragment-interleaved layout (C padded
+// to a multiple of 128).
+inline size_t ilv_bytes(int64_t R, int64_t C) { return (size_t)R * (size_t)((C + 127) / 128 * 128); }
+// [R][C] row-major codes (R % 16 == 0, C % 16 == 0) -> fragment-interleaved.
+hipError_t launch_relayout(const uint8_t* src, int64_t R, int64_t C, uint8_t* dst, hipStream_t s);
 hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s);
 
 // ---- backward ------------------------------------------------------------
@@ -96,8 +105,9 @@ struct GroupedLaunch {
   float eps;
   const GroupDev* groups;  // host array
   void* workspace;         // device
+  bool w_packed;           // every group's qw already fragment-interleaved
 };
-size_t grouped_workspace_bytes(int num_groups, const GroupDev* groups);
+size_t grouped_workspace_bytes(int num_groups, const GroupDev* groups, bool w_packed);
 int grouped_max_groups();
 // Does a forward of this shape fit the weight-resident kernel (K*N <= 256 KiB
 // of codes held in registers, N <= 512)?  Every group of a grouped launch must.

@@ -100,7 +100,17 @@ typedef enum { LOKA_DTYPE_BF16 = 0, LOKA_DTYPE_F32 = 1 } loka_dtype;
  *            transpose_out == 1: [cols, rows] (row stride rows): the
  *            codes of src^T, with `rows` contiguous -- the MFMA operand
  *            layout when `rows` is the caller's contraction dimension (a
- *            weight W[K, N] for the forward, X or dZ for the wgrad).
+ *            weight W[K, N] for the forward, X or dZ for the wgrad);
+ *            transpose_out == 2: the codes of src^T in the fragment-
+ *            interleaved ("packed") layout, cols * ceil(rows/128)*128
+ *            bytes: for every 16 consecutive columns j0..j0+15 of src and
+ *            every 128-row chunk c (rows past `rows` are zero codes) one
+ *            2 KiB block at ((j0/16) * ceil(rows/128) + c) * 2048, whose
+ *            byte 256 p + 16 i + b is src^T[j0 + i][128 c + 16 p + b]
+ *            (p = 0..7, i = 0..15, b = 0..15).  Lane l = i + 16 g of a
+ *            64-wide MFMA fragment load then reads bytes 16 l of each
+ *            1 KiB half: the weight layout loka_gemm_fp8_ln and the
+ *            grouped launch read with LOKA_FWD_W_PACKED.
  *   scales   TENSOR: float[1]; ROW: float[rows]; COL: float[cols];
  *            MX32_ROW: uint8[rows][cols/32]; MX32_COL: uint8[cols][rows/32].
  *            (The scale layout does not depend on transpose_out.)
@@ -140,7 +150,9 @@ loka_status loka_quant_fp8(const loka_quant_args* args, void* stream);
  *
  *   X       bf16 [M, K]; quantized inside the kernel per x_mode, e4m3.
  *   qw, sw  the weight, quantized beforehand with loka_quant_fp8 on
- *           W [K, N] with transpose_out = 1 (codes [N, K], e4m3):
+ *           W [K, N] with transpose_out = 1 (codes [N, K], e4m3), or with
+ *           transpose_out = 2 (the packed layout) and flags
+ *           LOKA_FWD_W_PACKED:
  *             x_mode TENSOR   -> W mode TENSOR,  sw float[1]
  *             x_mode ROW      -> W mode COL,     sw float[N]
  *             x_mode MX32_ROW -> W mode MX32_COL, sw uint8[N][K/32]
@@ -154,16 +166,22 @@ loka_status loka_quant_fp8(const loka_quant_args* args, void* stream);
  *   Optional outputs (NULL to skip): z fp32 [M, N]; mean, rstd fp32 [M];
  *   qx_out e4m3 [M, K] and sx_out (float[1] | float[M] | uint8[M][K/32]):
  *   the quantized X, bit-identical to loka_quant_fp8's, for the backward.
- *   workspace: loka_gemm_fp8_ln_workspace_size() bytes (TENSOR needs the
- *   amax partials; 0 otherwise).
+ *   workspace: loka_gemm_fp8_ln_workspace_size() bytes: the TENSOR amax
+ *   partials and, for a row-major qw on the weight-resident shapes (N <=
+ *   512, K <= 1024 / 640 / 512 for N <= 256 / 384 / 512), the weight
+ *   rearranged into the packed layout (one extra pass over qw per call;
+ *   LOKA_FWD_W_PACKED avoids it).  0 when neither applies.
+ *   flags: 0 or LOKA_FWD_W_PACKED (qw in the packed layout; only on the
+ *   weight-resident shapes, LOKA_ERR_UNSUPPORTED otherwise).
  * Requirements: M >= 0; N % 64 == 0 and 64 <= N <= 1024 (else
  * UNSUPPORTED: the row must fit one workgroup); K % 16 == 0 (MX: % 32),
  * 16 <= K <= 2048.
  * ---------------------------------------------------------------------- */
+#define LOKA_FWD_W_PACKED 1 /* qw is in loka_quant_fp8's transpose_out = 2 layout */
 typedef struct {
   int64_t M, N, K;
   int32_t x_mode; /* LOKA_SCALE_TENSOR, LOKA_SCALE_ROW or LOKA_SCALE_MX32_ROW */
-  int32_t flags;  /* reserved, must be 0 */
+  int32_t flags;  /* 0 or LOKA_FWD_W_PACKED */
   float eps;
   const void* x;
   const uint8_t* qw;
@@ -262,15 +280,19 @@ loka_status loka_gemm_fp8_bwd(const loka_bwd_args* args, void* stream);
  *   groups  HOST array of num_groups descriptors; each is one forward with
  *           the same meaning and requirements as loka_fwd_args (x_mode
  *           ROW): x bf16 [M,K], qw [N,K] + sw float[N] from
- *           loka_quant_fp8(COL, transpose_out=1), bias/gamma/beta bf16 [N]
- *           or NULL, y bf16 [M,N], optional z fp32 [M,N].
+ *           loka_quant_fp8(COL, transpose_out=1) (or every group's qw in
+ *           the packed layout of transpose_out=2, with flags
+ *           LOKA_FWD_W_PACKED), bias/gamma/beta bf16 [N] or NULL, y bf16
+ *           [M,N], optional z fp32 [M,N].
  *   workspace device memory of loka_grouped_workspace_size() bytes: the
  *           library copies the descriptors and the tile table into it with
  *           an asynchronous host-to-device copy on `stream`, so it must not
  *           be reused until the launch has completed.
  *   The workspace also receives the launch plan (each group's first tile
- *   and each workgroup's share), computed on the device from the copied
- *   descriptors.  For graph capture the host array must stay valid and
+ *   and each workgroup's share) when it is computed on the device from the
+ *   copied descriptors, and without LOKA_FWD_W_PACKED every group's weight
+ *   rearranged into the packed layout (at a fixed stride: the largest
+ *   group's N * ceil(K/128) * 128 bytes).  For graph capture the host array must stay valid and
  *   unchanged for every replay.
  * Each group's output is bit-identical to a single loka_gemm_fp8_ln call
  * with the same inputs.  Requirements: as loka_gemm_fp8_ln, with
@@ -295,7 +317,7 @@ typedef struct {
   int32_t num_groups;
   int32_t x_mode; /* LOKA_SCALE_ROW */
   float eps;
-  int32_t reserved;
+  int32_t flags;  /* 0 or LOKA_FWD_W_PACKED */
   const loka_group_desc* groups;
   void* workspace;
   size_t workspace_bytes;

@@ -40,6 +40,20 @@ def host(t):
     return t.numpy()
 
 
+def unpack_packed(packed, R, C):
+    """Codes in the fragment-interleaved ("packed") layout -> [R, C] row-major,
+    plus the zero padding check.  The layout, as the header states it: one
+    2 KiB block per 16 rows and 128-column chunk, block (rt, c) at
+    (rt * nch + c) * 2048, byte 256 p + 16 i + b = element [16 rt + i][128 c + 16 p + b]."""
+    nch = (C + 127) // 128
+    flat = np.ascontiguousarray(packed).reshape(-1)
+    assert flat.size == R * nch * 128, (flat.size, R, C)
+    blocks = flat.reshape(R // 16, nch, 8, 16, 16)         # [rt, c, p, i, b]
+    full = blocks.transpose(0, 3, 1, 2, 4).reshape(R, nch * 128)  # [rt, i, c, p, b]
+    assert not full[:, C:].any(), "padding past the last column is not zero"
+    return full[:, :C]
+
+
 def bf16_ulp(v):
     a = np.abs(np.asarray(v, dtype=np.float64))
     _, e = np.frexp(np.where(a == 0, 1.0, a))

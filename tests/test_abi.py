@@ -88,12 +88,16 @@ def _call(lib, fn, a):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(N=100), 2), (dict(N=2048), 2), (dict(N=0), 2), (dict(K=20), 2), (dict(K=4096), 2),
-    (dict(M=-1), 1), (dict(x_mode=2), 1), (dict(x_mode=9), 1), (dict(flags=1), 1),
+    (dict(M=-1), 1), (dict(x_mode=2), 1), (dict(x_mode=9), 1), (dict(flags=2), 1), (dict(flags=3), 1),
+    (dict(flags=1, N=1024), 2),  # the packed weight layout exists only for the weight-resident shapes
+    (dict(flags=1, N=512, K=1024), 2),
     (dict(eps=float("nan")), 1), (dict(eps=-1.0), 1),
     (dict(x=None), 1), (dict(qw=None), 1), (dict(sw=None), 1), (dict(y=None), 1),
     (dict(x=FAKE + 8), 3), (dict(bias=FAKE + 2), 3), (dict(z=FAKE + 4), 3),
     (dict(x_mode=3, K=48), 2),
     (dict(x_mode=0), 4),  # tensor recipe needs the amax workspace
+    (dict(x_mode=1), 4),  # a row-major weight on a resident shape needs the relayout workspace
+    (dict(x_mode=0, flags=1), 4),
 ])
 def test_forward_validation(lib, kw, status):
     a = _fwd(**kw)
@@ -115,7 +119,14 @@ def test_forward_workspace_sizes(lib):
     a.workspace = FAKE + 4
     a.workspace_bytes = need
     assert _call(lib, "loka_gemm_fp8_ln", a) == 3
-    assert lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(_fwd(x_mode=1))) == 0
+    # row recipe: only the packed copy of a row-major weight (N * ceil(K/128) * 128 bytes) ...
+    assert lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(_fwd(x_mode=1))) == 256 * 256
+    assert lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(_fwd(x_mode=1, K=144))) == 256 * 256
+    # ... none when the weight comes packed, or on shapes the resident kernel does not take
+    assert lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(_fwd(x_mode=1, flags=1))) == 0
+    assert lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(_fwd(x_mode=1, N=1024))) == 0
+    packed = lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(_fwd(x_mode=0, flags=1)))
+    assert 0 < packed < need
 
 
 def _quant(**kw):
@@ -128,7 +139,8 @@ def _quant(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(rows=-1), 1), (dict(ld=32), 1), (dict(src_dtype=2), 1), (dict(fmt=3), 1), (dict(mode=5), 1),
-    (dict(transpose_out=2), 1), (dict(cols=40, ld=40), 2), (dict(mode=3, cols=48, ld=48), 2),
+    (dict(transpose_out=3), 1), (dict(transpose_out=-1), 1), (dict(transpose_out=2, rows=40), 2),
+    (dict(cols=40, ld=40), 2), (dict(mode=3, cols=48, ld=48), 2),
     (dict(mode=4, rows=48), 2), (dict(transpose_out=1, rows=40), 2), (dict(ld=68), 3),
     (dict(src=None), 1), (dict(codes=None), 1), (dict(scales=None), 1), (dict(mode=3, amax=FAKE), 1),
     (dict(codes=FAKE + 1), 3), (dict(mode=0), 4), (dict(mode=2), 4),
@@ -178,6 +190,13 @@ def test_grouped_validation(lib):
     assert lib.loka_grouped_gemm_fp8_ln(ctypes.byref(a), None) == 3
     descs[1].y = FAKE
     assert lib.loka_grouped_gemm_fp8_ln(ctypes.byref(a), None) == 4
+    plain = lib.loka_grouped_workspace_size(ctypes.byref(a))
+    a.flags = 1  # packed weights: no relayout copies in the workspace
+    assert lib.loka_grouped_workspace_size(ctypes.byref(a)) == plain - 2 * 128 * 128
+    assert lib.loka_grouped_gemm_fp8_ln(ctypes.byref(a), None) == 4
+    a.flags = 2
+    assert lib.loka_grouped_gemm_fp8_ln(ctypes.byref(a), None) == 1
+    a.flags = 0
     a.x_mode = 0
     assert lib.loka_grouped_gemm_fp8_ln(ctypes.byref(a), None) == 2
     a.x_mode = 1

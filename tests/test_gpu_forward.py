@@ -22,17 +22,29 @@ W_MODE = {"tensor": "tensor", "row": "col", "mx32_row": "mx32_col"}
 RECIPE = {"tensor": "tensor", "row": "row", "mx32_row": "mx32"}
 
 
-def run_gpu(lib, c, x_mode, eps=1e-5, no_bias=False, no_affine=False):
+def run_gpu(lib, c, x_mode, eps=1e-5, no_bias=False, no_affine=False, packed=False):
+    """One forward with every optional output.  packed: the weight in the
+    packed layout (the benchmark's configuration), and a second call without
+    the optional outputs (the kernel variant the benchmark times) whose Y
+    must be bit-identical."""
     x = bf16_dev(c["x"])
     w = bf16_dev(c["w"])
     qw, sw, _ = lib.loka_quant_fp8(w, fmt="e4m3", mode=W_MODE[x_mode], transpose_out=True)
-    out = lib.loka_gemm_fp8_ln(x, qw, sw, bias=None if no_bias else bf16_dev(c["bias"]),
-                               gamma=None if no_affine else bf16_dev(c["gamma"]),
-                               beta=None if no_affine else bf16_dev(c["beta"]), eps=eps, x_mode=x_mode,
-                               want_z=True, want_stats=True, want_qx=True)
+    vec = dict(bias=None if no_bias else bf16_dev(c["bias"]), gamma=None if no_affine else bf16_dev(c["gamma"]),
+               beta=None if no_affine else bf16_dev(c["beta"]), eps=eps, x_mode=x_mode)
+    wq = qw
+    if packed:
+        wq, sw2, _ = lib.loka_quant_fp8(w, fmt="e4m3", mode=W_MODE[x_mode], transpose_out="packed")
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(sw2), host(sw))
+    out = lib.loka_gemm_fp8_ln(x, wq, sw, want_z=True, want_stats=True, want_qx=True, w_packed=packed, **vec)
+    if packed:
+        plain = lib.loka_gemm_fp8_ln(x, wq, sw, w_packed=True, **vec)
     torch.cuda.synchronize()
     res = {k: host(v) for k, v in out.items()}
     res["qw"], res["sw"] = host(qw), host(sw)
+    if packed:
+        np.testing.assert_array_equal(host(plain["y"]), res["y"], err_msg="Y without the optional outputs")
     return res
 
 
@@ -69,14 +81,14 @@ def compare(g, o, rows, x_mode, label):
 
 def test_tensor_recipe_full(lib):
     c = tensor_case()
-    g = run_gpu(lib, c, "tensor")
+    g = run_gpu(lib, c, "tensor", packed=True)
     o = oracle_rows(c, "tensor", None)
     compare(g, o, None, "tensor", "tensor 512x256x256")
 
 
 def test_rowwise_outliers_full_size(lib):
     c = outlier_case()
-    g = run_gpu(lib, c, "row")
+    g = run_gpu(lib, c, "row", packed=True)
     rows = sample_rows(c["M"], 1024)
     o = oracle_rows(c, "row", rows)
     compare(g, o, rows, "row", "row 16384x512x512")
@@ -84,7 +96,7 @@ def test_rowwise_outliers_full_size(lib):
 
 def test_mx_full_size(lib):
     c = mx_case()
-    g = run_gpu(lib, c, "mx32_row")
+    g = run_gpu(lib, c, "mx32_row", packed=True)
     rows = sample_rows(c["M"], 512)
     o = oracle_rows(c, "mx32_row", rows)
     compare(g, o, rows, "mx32_row", "mx 65536x1024x256")
@@ -98,6 +110,26 @@ def test_ragged_shapes(lib, x_mode, M, K, N):
     g = run_gpu(lib, c, x_mode)
     o = oracle_rows(c, x_mode, None)
     compare(g, o, None, x_mode, f"{x_mode} {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("x_mode", ["tensor", "row", "mx32_row"])
+@pytest.mark.parametrize("M,K,N", [(1000, 192, 192), (130, 160, 384), (300, 256, 320), (77, 512, 512),
+                                   (33, 1024, 128), (40, 640, 384), (16, 16, 64)])
+def test_packed_weight_is_bit_identical(lib, x_mode, M, K, N):
+    """The packed weight layout (loka_quant_fp8 transpose_out="packed" with
+    w_packed=True) and the row-major layout (rearranged inside the call)
+    give bit-identical outputs, with and without the optional outputs;
+    N = 320 leaves the last wavefronts with fewer column tiles, K = 16 one
+    partial chunk."""
+    if x_mode == "mx32_row" and K % 32:
+        pytest.skip("MX needs K % 32 == 0")
+    c = forward_case(M, K, N, seed=3 * M + K + N, x_dist="student_t3_outliers", gamma_var=0.1, beta_var=0.1)
+    a = run_gpu(lib, c, x_mode, packed=True)
+    b = run_gpu(lib, c, x_mode, packed=False)
+    for k in ("y", "z", "mean", "rstd", "qx", "sx"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=f"{x_mode} {M}x{K}x{N}: {k}")
+    if M * N <= 200000:
+        compare(a, oracle_rows(c, x_mode, None), None, x_mode, f"packed {x_mode} {M}x{K}x{N}")
 
 
 @pytest.mark.parametrize("x_mode", ["row", "mx32_row"])

@@ -61,6 +61,23 @@ def test_grouped_ragged_and_empty_groups(lib):
         check_y(host(o["y"]), ref["y"], f"group {i}")
 
 
+def test_grouped_packed_weights_bit_identical(lib):
+    """w_packed=True (every group's weight quantized straight into the packed
+    layout) gives the same bits as row-major weights rearranged in the call."""
+    groups = grouped_case(seed=9, groups=12, M=300)
+    dg = prepare(lib, groups)
+    dp = [dict(d, qw=lib.loka_quant_fp8(bf16_dev(g["w"]), mode="col", transpose_out="packed")[0])
+          for d, g in zip(dg, groups)]
+    a = lib.loka_grouped_gemm_fp8_ln(dg, want_z=True)
+    b = lib.loka_grouped_gemm_fp8_ln(dp, want_z=True, w_packed=True)
+    c = lib.loka_grouped_gemm_fp8_ln(dp, w_packed=True)
+    torch.cuda.synchronize()
+    for i in range(len(groups)):
+        np.testing.assert_array_equal(host(a[i]["y"]), host(b[i]["y"]), err_msg=f"group {i}")
+        np.testing.assert_array_equal(host(a[i]["z"]), host(b[i]["z"]), err_msg=f"group {i}")
+        np.testing.assert_array_equal(host(a[i]["y"]), host(c[i]["y"]), err_msg=f"group {i} (no z)")
+
+
 def test_grouped_many_groups_device_plan(lib):
     """More than 256 groups in one shape class: the launch plan is built on
     the device instead of being passed by value.  Every group (empty and

@@ -7,7 +7,7 @@ import torch
 
 from oracle import codec, quant
 from synth.workloads import outlier_case, to_bf16_bits
-from tests.gpu_helpers import bf16_dev, f32_dev, host
+from tests.gpu_helpers import bf16_dev, f32_dev, host, unpack_packed
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,11 @@ def check_quant(lib, x_bits_or_f32, mode, fmt, transpose, src_f32=False, label="
     torch.cuda.synchronize()
     ref_codes, ref_scales = quant.quantize(xv, mode, FMTS[fmt])
     got = host(codes)
-    if transpose:
+    if transpose == "packed":
+        rows, cols = ref_codes.shape
+        assert tuple(codes.shape) == lib.packed_shape(rows, cols)
+        got = unpack_packed(got, cols, rows).T
+    elif transpose:
         got = got.T
     bad = np.nonzero(got != ref_codes)
     assert bad[0].size == 0, (f"{label} {mode}/{fmt}/T={transpose}: {bad[0].size} code mismatches, first at "
@@ -55,6 +59,19 @@ def check_quant(lib, x_bits_or_f32, mode, fmt, transpose, src_f32=False, label="
 @pytest.mark.parametrize("mode", MODES)
 def test_every_bf16_value(lib, mode, fmt, transpose):
     check_quant(lib, all_bf16_matrix(), mode, fmt, transpose, label="all-bf16")
+
+
+@pytest.mark.parametrize("mode", ["tensor", "col", "mx32_col"])
+@pytest.mark.parametrize("rows,cols", [(256, 256), (144, 96), (32, 16), (640, 48)])
+def test_packed_layout(lib, mode, rows, cols):
+    """transpose_out="packed": the codes of src^T in the fragment-interleaved
+    layout (rows not a multiple of 128 are padded with zero codes), the same
+    codes and scales as the plain layouts."""
+    if mode == "mx32_col" and rows % 32:
+        pytest.skip("MX32_COL needs rows % 32 == 0")
+    rng = np.random.default_rng(rows * 7 + cols)
+    x = to_bf16_bits(rng.standard_t(3, size=(rows, cols)))
+    check_quant(lib, x, mode, "e4m3", "packed", label=f"packed {rows}x{cols}")
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
