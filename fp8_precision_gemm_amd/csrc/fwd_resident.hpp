@@ -57,6 +57,11 @@ namespace loka {
 namespace fwd {
 
 constexpr int kResRows = 16;  // rows per tile
+// float2 slots per row of the statistics exchange: the 8 wavefronts' (sum,
+// centred sum of squares) plus 2 of padding, so that the 16 rows of a tile
+// (80 bytes apart) fall on distinct LDS banks when a wavefront writes or
+// reads them all at once
+constexpr int kRedRow = 10;
 
 // Shapes: NT column tiles per wavefront (N <= 128*NT) and KC resident 128-deep
 // K chunks (K <= 128*KC); NT*KC fragments of 8 VGPRs stay within 128
@@ -104,7 +109,7 @@ __host__ __device__ constexpr int res_shape(int nt, int kc) {
 
 // LDS carve-up (bytes, every part 16-byte aligned):
 //   codes [2][16][LDX] u8 | xe8 [2][16][XE] u8 | rs [2][16] f32 |
-//   red [2][16][8] float2 | cvec [4][N] f32 (s_w, bias, gamma, beta) |
+//   red [2][16][kRedRow] float2 | cvec [4][N] f32 (s_w, bias, gamma, beta) |
 //   wmx [3][8] f32 | ystg [8][16][32*NT + 16] (each wavefront's Y block)
 struct ResLds {
   int codes, xe8, rs, red, cvec, wmx, ystg, total;
@@ -117,7 +122,7 @@ __host__ __device__ inline ResLds res_lds(int nt, int kc, int N) {
   l.xe8 = l.codes + 2 * kResRows * ldx;
   l.rs = l.xe8 + ((2 * kResRows * xe + 15) / 16) * 16;
   l.red = l.rs + 2 * kResRows * 4;
-  l.cvec = l.red + 2 * kResRows * 8 * 8;
+  l.cvec = l.red + 2 * kResRows * kRedRow * 8;
   l.wmx = l.cvec + 4 * N * 4;
   l.ystg = l.wmx + 32 * 4;
   l.total = l.ystg + kWaves * kResRows * res_yst(nt);
@@ -347,14 +352,11 @@ struct ResBlock {
     }
   }
 
-  // ---- set-up, part 1: this thread's column vectors and the MX scale
-  // bytes, then the weight slice straight into the fragment registers
-  // (fragment-interleaved W^T: lane l reads bytes 16l of both 1 KiB halves
-  // of each 2 KiB block; chunks in the order the GEMM uses them).  Nothing
-  // here waits for a load; the vectors come first so that staging them does
-  // not wait for the weight.
+  // ---- set-up, part 1: the weight slice straight into the fragment
+  // registers (fragment-interleaved W^T: lane l reads bytes 16l of both
+  // 1 KiB halves of each 2 KiB block; chunks in the order the GEMM uses
+  // them) and the MX scale bytes.  Nothing here waits for a load.
   __device__ __forceinline__ void request_weights() {
-    request_vectors();
     const int64_t nch = (K + 127) >> 7;
     const uint8_t* base = p.qw + (int64_t)(wave * NT) * nch * 2048 + lane * 16;
 #pragma unroll
@@ -373,9 +375,6 @@ struct ResBlock {
         wf[t][c] = f;
       }
     }
-  }
-
-  __device__ __forceinline__ void request_vectors() {
     if (MODE == 3) {
       const uint8_t* sw8 = static_cast<const uint8_t*>(p.sw);
 #pragma unroll
@@ -388,12 +387,21 @@ struct ResBlock {
         }
       }
     }
-    if (tid < N) {
-      cv_sw = MODE == 1 ? static_cast<const float*>(p.sw)[tid] : (MODE == 0 ? static_cast<const float*>(p.sw)[0] : 1.0f);
-      cv_b = p.bias ? p.bias[tid] : (uint16_t)0;
-      cv_g = p.gamma ? p.gamma[tid] : (uint16_t)0x3F80;
-      cv_be = p.beta ? p.beta[tid] : (uint16_t)0;
-    }
+  }
+
+  // ---- this thread's column vectors (column tid; threads past N load
+  // column 0 and never use it).  No branch: a missing vector reads element 0
+  // of X instead and the value is replaced by its default, so no load sits
+  // in a branch that would have to wait for it there.
+  __device__ __forceinline__ void request_vectors() {
+    const int ct = tid < N ? tid : 0;
+    const uint16_t* x0 = p.x;
+    cv_sw = MODE == 1 ? static_cast<const float*>(p.sw)[ct] : (MODE == 0 ? static_cast<const float*>(p.sw)[0] : 1.0f);
+    const uint16_t b = *(p.bias ? p.bias + ct : x0), gm = *(p.gamma ? p.gamma + ct : x0);
+    const uint16_t be = *(p.beta ? p.beta + ct : x0);
+    cv_b = p.bias ? b : (uint16_t)0;
+    cv_g = p.gamma ? gm : (uint16_t)0x3F80;
+    cv_be = p.beta ? be : (uint16_t)0;
   }
 
   // ---- set-up, part 2: MX scale words, column vectors into LDS with their
@@ -535,12 +543,12 @@ struct ResBlock {
           q = fmaf(d, d, q);
         }
     q = sum4(q);
-    red[(buf * kResRows + r) * kWaves + wave] = make_float2(s, q);  // the row's 4 lanes write the same pair
+    red[(buf * kResRows + r) * kRedRow + wave] = make_float2(s, q);  // the row's 4 lanes write the same pair
   }
 
   // ---- epilogue, part 2 (after the barrier): combine the slices, normalize, store
   __device__ __forceinline__ void epilogue_out(int buf, int64_t t, const v4f (&acc)[NT], float cs) {
-    const float4* rw4 = reinterpret_cast<const float4*>(red + (buf * kResRows + r) * kWaves);
+    const float4* rw4 = reinterpret_cast<const float4*>(red + (buf * kResRows + r) * kRedRow);
     float sw_[kWaves], qw_[kWaves];
 #pragma unroll
     for (int i = 0; i < kWaves / 2; ++i) {
@@ -683,14 +691,18 @@ struct ResBlock {
   __device__ __forceinline__ void run() {
     if (tb >= te) return;
     if (OPT && MODE == 0 && p.sx_out != nullptr && tb == 0 && tid == 0) static_cast<float*>(p.sx_out)[0] = p.x_s;
-    // requests first, in the order they are needed (load completions are
-    // counted in issue order): X tile 0 (HBM), the weight slice (L2-resident
-    // after its first reader) and the column vectors, then X tile 1
+    // every request first, in the order they are needed (load completions
+    // are counted in issue order): X tile 0 (HBM), the column vectors, the
+    // weight slice (L2-resident after its first reader), then the next X
+    // tiles; the scheduling barrier keeps the first wait (tile 0's
+    // quantization) from being hoisted above any of them
     load_x<0>(tb);
+    request_vectors();
     request_weights();
     if (D > 1) load_x<(1 % D)>(tb + 1);
     if (D > 2) load_x<(2 % D)>(tb + 2);
     if (D > 3) load_x<(3 % D)>(tb + 3);
+    __builtin_amdgcn_sched_barrier(0);
     quantize<0>(tb, 0);
     load_x<0>(tb + D);
     stage_vectors();
@@ -708,26 +720,29 @@ struct ResBlock {
     epilogue_stats(0, acc0, cs0);
     __syncthreads();
     const int64_t n = te - tb;
-    // step j quantizes tile j+1 from slot (j+1) % D and fills accumulator set j % 2
+    // Step j quantizes tile j+1 from slot (j+1) % D and fills accumulator
+    // set j % 2.  The loop runs whole groups of steps (one period of the
+    // slot and set pattern) with no exit in between, then a tail of the
+    // remaining steps: an exit between the steps of the loop body would give
+    // the loop header a path on which the X loads just issued are the
+    // latest memory operations, and every iteration would then wait for them.
     int64_t j = 1;
     if (D == 2) {
-      while (j < n) {
+      for (int64_t i = (n - 1) >> 1; i > 0; --i, j += 2) {
         step<0, 1>(j);
-        if (++j >= n) break;
-        step<(1 % D), 0>(j);
-        ++j;
+        step<(1 % D), 0>(j + 1);
       }
+      if (j < n) step<0, 1>(j++);
     } else {
-      while (j < n) {
+      for (int64_t i = (n - 1) >> 2; i > 0; --i, j += 4) {
         step<(2 % D), 1>(j);
-        if (++j >= n) break;
-        step<(3 % D), 0>(j);
-        if (++j >= n) break;
-        step<0, 1>(j);
-        if (++j >= n) break;
-        step<(1 % D), 0>(j);
-        ++j;
+        step<(3 % D), 0>(j + 1);
+        step<0, 1>(j + 2);
+        step<(1 % D), 0>(j + 3);
       }
+      if (j < n) step<(2 % D), 1>(j++);
+      if (j < n) step<(3 % D), 0>(j++);
+      if (j < n) step<0, 1>(j++);
     }
     // the last tile's normalization and stores
     const int64_t l = n - 1;
