@@ -142,6 +142,37 @@ __device__ __forceinline__ float wave_max_dpp(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
+// Sum over the 16 lanes of each DPP row (lanes 16g .. 16g+15), returned in
+// all of them: four rotate-and-add steps within the row.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, true));  // row_ror:8
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, true));  // row_ror:4
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, true));  // row_ror:2
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, true));  // row_ror:1
+  return v;
+}
+// Max over the 16 lanes of each DPP row; non-negative values.
+__device__ __forceinline__ float row16_max(float v) {
+  v = dpp_max<0x128>(v);
+  v = dpp_max<0x124>(v);
+  v = dpp_max<0x122>(v);
+  return dpp_max<0x121>(v);
+}
+// Sum / max over the 4 lanes l, l^16, l^32, l^48 (one per DPP row),
+// returned in all four: row swaps by v_permlane16_swap / v_permlane32_swap.
+__device__ __forceinline__ float rows4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float rows4_max(float v) {  // non-negative values
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const uint32_t m = max((uint32_t)a[0], (uint32_t)a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(m, m, false, false);
+  return __uint_as_float(max((uint32_t)b[0], (uint32_t)b[1]));
+}
+
 // Wavefront (64-lane) reductions through LDS permutes.
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -73,19 +73,18 @@ __device__ __forceinline__ void ld4_bf16(const uint16_t* p, float def, float o[4
   o[0] = bf16_lo(u.x); o[1] = bf16_hi(u.x); o[2] = bf16_lo(u.y); o[3] = bf16_hi(u.y);
 }
 
-// Sum / max over the 16 lanes sharing l / 16 (lanes with the same 4 columns).
-__device__ __forceinline__ float col16_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-__device__ __forceinline__ float col16_max(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
+// Sum / max over the 16 lanes sharing l / 16 (lanes with the same 4
+// columns): one DPP row.
+__device__ __forceinline__ float col16_sum(float v) { return row16_sum(v); }
+__device__ __forceinline__ float col16_max(float v) { return row16_max(v); }
 
-template <int NTMAX, int KTMAX, int NO_LN>
+// dY rows staged in LDS for N <= 512 and K <= 512 (the staging area and the
+// X and dZ code rows then fit the LDS together)
+__host__ __device__ constexpr bool bwd_stage_dy(int ntmax, int ktmax) { return ntmax == 8 && ktmax == 8; }
+
+// FULLM: M is a multiple of the 64-row block, so every row exists (no row
+// guards).
+template <int NTMAX, int KTMAX, int NO_LN, bool FULLM>
 __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = p.K, N = p.N;
@@ -99,50 +98,76 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
   float* red0 = reinterpret_cast<float*>(ds + (size_t)kBM * ldn);
   float* red1 = red0 + 4 * kBM;
   float* rsc = red1 + 4 * kBM;                         // dZ row scales [BM]
+  // SDY: the block's dY rows staged in LDS [BM][2N+16] (when the LDS has room)
+  constexpr bool SDY = bwd_stage_dy(NTMAX, KTMAX);
+  const int ldy = 2 * N + 16;
+  uint8_t* dys = reinterpret_cast<uint8_t*>(rsc + kBM);
 
   const int nt = N / 64;
   const int nb = wave * nt * 16;
   v4f acc[NTMAX][kMT];  // holds Z, then dZ
 
+  // per-row constants of this lane's rows m = m0 + 16 i + r, requested first
+  bool rowok[kMT];
+  float mu[kMT], rs[kMT], sxv[kMT];
+#pragma unroll
+  for (int i = 0; i < kMT; ++i) {
+    const int64_t m = m0 + 16 * i + r;
+    rowok[i] = FULLM || m < p.M;
+    mu[i] = (!NO_LN && rowok[i]) ? p.mean[m] : 0.0f;
+    rs[i] = (!NO_LN && rowok[i]) ? p.rstd[m] : 0.0f;
+    sxv[i] = (!NO_LN && rowok[i]) ? p.sx[m] : 0.0f;
+  }
+
   if (!NO_LN) {
-    // stage the forward's X codes in LDS
-    const int k16 = K / 16;
-    for (int u = tid; u < kBM * k16; u += 256) {
-      const int lr = u / k16, c = (u - lr * k16) * 16;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (m0 + lr < p.M) v = *reinterpret_cast<const uint4*>(p.qx + (m0 + lr) * K + c);
-      *reinterpret_cast<uint4*>(xs + lr * ldk + c) = v;
+    // stage the forward's X codes in LDS, and with SDY the block's dY rows
+    // too: all requests go out before the first wait, so one HBM latency
+    // covers both, and the two LayerNorm passes read dY from LDS
+    const int k16 = K / 16, n8 = SDY ? N / 8 : 0;
+    for (int u = tid; u < kBM * (k16 + n8); u += 256) {
+      if (u < kBM * k16) {
+        const int lr = u / k16, c = (u - lr * k16) * 16;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (FULLM || m0 + lr < p.M) v = *reinterpret_cast<const uint4*>(p.qx + (m0 + lr) * K + c);
+        *reinterpret_cast<uint4*>(xs + lr * ldk + c) = v;
+      } else {
+        const int v8 = u - kBM * k16, lr = v8 / n8, c = (v8 - lr * n8) * 8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (FULLM || m0 + lr < p.M) v = *reinterpret_cast<const uint4*>(p.dy + (m0 + lr) * N + c);
+        *reinterpret_cast<uint4*>(dys + lr * ldy + 2 * c) = v;
+      }
     }
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < NTMAX; ++t)
 #pragma unroll
       for (int i = 0; i < kMT; ++i) acc[t][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int kc = 0; kc < K; kc += 128) {
+    // weight fragments double-buffered: chunk c+1 is requested before the
+    // MFMAs of chunk c (one wavefront per SIMD: nothing else hides the L2
+    // latency)
+    const int nchk = (K + 127) >> 7;
+    v8i wa[NTMAX], wb[NTMAX];
+    auto wload = [&](int c, v8i (&w)[NTMAX]) {
+#pragma unroll
+      for (int t = 0; t < NTMAX; ++t)
+        if (t < nt) w[t] = load_frag_ilv(p.qwi, nb / 16 + t, c, nchk, r, g);
+    };
+    auto zchunk = [&](int c, const v8i (&wc)[NTMAX], v8i (&wn)[NTMAX]) {
+      if (c + 1 < nchk) wload(c + 1, wn);
       v8i xf[kMT];
 #pragma unroll
-      for (int i = 0; i < kMT; ++i) xf[i] = load_frag(xs + (16 * i + r) * ldk, g, kc, K);
+      for (int i = 0; i < kMT; ++i) xf[i] = load_frag(xs + (16 * i + r) * ldk, g, 128 * c, K);
 #pragma unroll
-      for (int t = 0; t < NTMAX; ++t) {
-        if (t < nt) {
-          const v8i wf = load_frag_ilv(p.qwi, nb / 16 + t, kc >> 7, (K + 127) >> 7, r, g);
+      for (int t = 0; t < NTMAX; ++t)
+        if (t < nt)
 #pragma unroll
-          for (int i = 0; i < kMT; ++i) acc[t][i] = mfma_fp8<0, 0>(wf, xf[i], acc[t][i]);
-        }
-      }
+          for (int i = 0; i < kMT; ++i) acc[t][i] = mfma_fp8<0, 0>(wc[t], xf[i], acc[t][i]);
+    };
+    wload(0, wa);
+    for (int c = 0; c < nchk; c += 2) {
+      zchunk(c, wa, wb);
+      if (c + 1 < nchk) zchunk(c + 1, wb, wa);
     }
-  }
-
-  // per-row constants of this lane's rows m = m0 + 16 i + r
-  float mu[kMT], rs[kMT], sxv[kMT];
-  bool rowok[kMT];
-#pragma unroll
-  for (int i = 0; i < kMT; ++i) {
-    const int64_t m = m0 + 16 * i + r;
-    rowok[i] = m < p.M;
-    mu[i] = (!NO_LN && rowok[i]) ? p.mean[m] : 0.0f;
-    rs[i] = (!NO_LN && rowok[i]) ? p.rstd[m] : 0.0f;
-    sxv[i] = (!NO_LN && rowok[i]) ? p.sx[m] : 0.0f;
   }
 
   // g = dY * gamma, yhat; row sums of g and g * yhat.  acc <- yhat, dyg[] <- g
@@ -171,7 +196,8 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
       for (int i = 0; i < kMT; ++i) {
         const int64_t m = m0 + 16 * i + r;
         float dyv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (rowok[i]) ld4_bf16(p.dy + m * N + n0, 0.0f, dyv);
+        if (SDY && !NO_LN) ld4_bf16(reinterpret_cast<const uint16_t*>(dys + (16 * i + r) * ldy) + n0, 0.0f, dyv);
+        else if (rowok[i]) ld4_bf16(p.dy + m * N + n0, 0.0f, dyv);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if (NO_LN) {
@@ -194,8 +220,8 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
   if (!NO_LN) {
 #pragma unroll
     for (int i = 0; i < kMT; ++i) {
-      s1[i] = group4_sum(s1[i]);
-      s2[i] = group4_sum(s2[i]);
+      s1[i] = rows4_sum(s1[i]);
+      s2[i] = rows4_sum(s2[i]);
       if (g == 0) {
         red0[wave * kBM + 16 * i + r] = s1[i];
         red1[wave * kBM + 16 * i + r] = s2[i];
@@ -220,7 +246,8 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
         for (int i = 0; i < kMT; ++i) {
           const int64_t m = m0 + 16 * i + r;
           float dyv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-          if (rowok[i]) ld4_bf16(p.dy + m * N + n0, 0.0f, dyv);
+          if (SDY) ld4_bf16(reinterpret_cast<const uint16_t*>(dys + (16 * i + r) * ldy) + n0, 0.0f, dyv);
+          else if (rowok[i]) ld4_bf16(p.dy + m * N + n0, 0.0f, dyv);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float gg = dyv[j] * gm[j];
@@ -245,8 +272,7 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
   __syncthreads();  // red0/red1 reads above are complete before reuse
 #pragma unroll
   for (int i = 0; i < kMT; ++i) {
-    am[i] = fmaxf(am[i], __shfl_xor(am[i], 16, 64));
-    am[i] = fmaxf(am[i], __shfl_xor(am[i], 32, 64));
+    am[i] = rows4_max(am[i]);
     if (g == 0) red0[wave * kBM + 16 * i + r] = am[i];
   }
   __syncthreads();
@@ -315,18 +341,29 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
   for (int t = 0; t < KTMAX; ++t)
 #pragma unroll
     for (int i = 0; i < kMT; ++i) dacc[t][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  for (int nc = 0; nc < N; nc += 128) {
+  // weight fragments double-buffered as in the Z recompute
+  const int nchn = (N + 127) >> 7;
+  v8i ra[KTMAX], rb[KTMAX];
+  auto rload = [&](int c, v8i (&w)[KTMAX]) {
+#pragma unroll
+    for (int t = 0; t < KTMAX; ++t)
+      if (t < kt) w[t] = load_frag_ilv(p.qwri, kb0 / 16 + t, c, nchn, r, g);
+  };
+  auto dchunk = [&](int c, const v8i (&wc)[KTMAX], v8i (&wn)[KTMAX]) {
+    if (c + 1 < nchn) rload(c + 1, wn);
     v8i df[kMT];
 #pragma unroll
-    for (int i = 0; i < kMT; ++i) df[i] = load_frag(ds + (16 * i + r) * ldn, g, nc, N);
+    for (int i = 0; i < kMT; ++i) df[i] = load_frag(ds + (16 * i + r) * ldn, g, 128 * c, N);
 #pragma unroll
-    for (int t = 0; t < KTMAX; ++t) {
-      if (t < kt) {
-        const v8i wf = load_frag_ilv(p.qwri, kb0 / 16 + t, nc >> 7, (N + 127) >> 7, r, g);
+    for (int t = 0; t < KTMAX; ++t)
+      if (t < kt)
 #pragma unroll
-        for (int i = 0; i < kMT; ++i) dacc[t][i] = mfma_fp8<0, 1>(wf, df[i], dacc[t][i]);
-      }
-    }
+        for (int i = 0; i < kMT; ++i) dacc[t][i] = mfma_fp8<0, 1>(wc[t], df[i], dacc[t][i]);
+  };
+  rload(0, ra);
+  for (int c = 0; c < nchn; c += 2) {
+    dchunk(c, ra, rb);
+    if (c + 1 < nchn) dchunk(c + 1, rb, ra);
   }
   float dsv[kMT];
 #pragma unroll
@@ -340,11 +377,13 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
 #pragma unroll
       for (int i = 0; i < kMT; ++i) {
         const int64_t m = m0 + 16 * i + r;
-        if (m < p.M) {
+        if (FULLM || m < p.M) {
           float o[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) o[j] = dacc[t][i][j] * dsv[i] * swr[j];
-          *reinterpret_cast<uint2*>(p.dx + m * K + k0) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+          // dX is not read again here: streaming (non-temporal) stores
+          __builtin_nontemporal_store(pack_bf16x2(o[0], o[1]) | ((uint64_t)pack_bf16x2(o[2], o[3]) << 32),
+                                      reinterpret_cast<uint64_t*>(p.dx + m * K + k0));
         }
       }
     }
@@ -464,8 +503,9 @@ __global__ __launch_bounds__(256) void k_col_vectors(const float* cpart, int nbl
   }
 }
 
-size_t bwd_lds_bytes(int K, int N) {
-  return (size_t)kBM * (K + 16) + (size_t)kBM * (N + 16) + (size_t)(2 * 4 * kBM + kBM) * 4;
+size_t bwd_lds_bytes(int K, int N, bool sdy) {
+  return (size_t)kBM * (K + 16) + (size_t)kBM * (N + 16) + (size_t)(2 * 4 * kBM + kBM) * 4 +
+         (sdy ? (size_t)kBM * (2 * N + 16) : 0);
 }
 
 struct BwdWs {
@@ -500,19 +540,15 @@ BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K) {
 
 template <int NTMAX, int KTMAX>
 hipError_t launch_main_t(const BwdBlock& p, int no_ln, hipStream_t s) {
-  const size_t lds = bwd_lds_bytes(p.K, p.N);
+  const size_t lds = bwd_lds_bytes(p.K, p.N, bwd_stage_dy(NTMAX, KTMAX));
   const dim3 grid((unsigned)p.nblocks);
-  if (no_ln) {
-    auto kern = k_bwd_main<NTMAX, KTMAX, 1>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, p);
-  } else {
-    auto kern = k_bwd_main<NTMAX, KTMAX, 0>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, p);
-  }
+  const bool full = p.M % kBM == 0;
+  auto kern = no_ln ? (full ? k_bwd_main<NTMAX, KTMAX, 1, true> : k_bwd_main<NTMAX, KTMAX, 1, false>)
+                    : (full ? k_bwd_main<NTMAX, KTMAX, 0, true> : k_bwd_main<NTMAX, KTMAX, 0, false>);
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, p);
   return hipGetLastError();
 }
 

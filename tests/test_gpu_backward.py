@@ -126,7 +126,7 @@ def test_literal_reading_full_size(lib):
     print(f"literal: dX err/rms {ex:.2e}  dW err/rms {ew:.2e}")
 
 
-@pytest.mark.parametrize("M,K,N", [(16384, 512, 512), (1040, 192, 320), (64, 64, 64)])
+@pytest.mark.parametrize("M,K,N", [(16384, 512, 512), (1040, 192, 320), (64, 64, 64), (144, 1024, 256), (96, 256, 1024)])
 def test_layernorm_reading(lib, M, K, N):
     if M == 16384:
         c = outlier_case(dy=True)
