@@ -29,10 +29,6 @@
 
 namespace loka {
 
-QuantPlan quant_plan(int64_t rows, int64_t cols, int mode);
-hipError_t launch_cast_col_with_partials(const void* src, int src_dtype, int fmt, int64_t rows, int64_t cols,
-                                         int64_t ld, const float* partials, int64_t np, uint8_t* codes_t,
-                                         float* scales, float* mult, hipStream_t s);
 
 namespace {
 
@@ -448,9 +444,9 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint8_t* dzt, const uint8_t
 
 // dW[k][n] = (sum_s part[s][k][n]) * sxc[k] * sdzc[n].  Fixed summation
 // order => deterministic.
-__global__ __launch_bounds__(256) void k_finalize(const float* wpart, int nsplit, const float* sxc, const float* sdzc,
-                                                  int K, int N, float* dw) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void finalize_body(int64_t blk, const float* wpart, int nsplit, const float* sxc,
+                                              const float* sdzc, int K, int N, float* dw) {
+  const int64_t i = blk * 256 + threadIdx.x;
   const int64_t kn = (int64_t)K * N;
   if (i < kn) {
     float s = 0.0f;
@@ -463,11 +459,11 @@ __global__ __launch_bounds__(256) void k_finalize(const float* wpart, int nsplit
 // dgamma, dbeta, dbias from the per-workgroup column partials: block of 256
 // threads = 16 columns x 16 subsets of the workgroups (strided, 2 in flight),
 // then the subset sums in a fixed order => deterministic.
-__global__ __launch_bounds__(256) void k_col_vectors(const float* cpart, int nblocks, int N, float* dgamma,
-                                                     float* dbeta, float* dbias) {
+__device__ __forceinline__ void col_vectors_body(int blk, const float* cpart, int nblocks, int N, float* dgamma,
+                                                 float* dbeta, float* dbias) {
   __shared__ float red[3][16][16];
   const int cl = threadIdx.x & 15, part = threadIdx.x >> 4;
-  const int n = blockIdx.x * 16 + cl;
+  const int n = blk * 16 + cl;
   const size_t plane = (size_t)nblocks * N;
   float a = 0.0f, b = 0.0f, c = 0.0f;
   if (n < N) {
@@ -501,6 +497,16 @@ __global__ __launch_bounds__(256) void k_col_vectors(const float* cpart, int nbl
     if (dbeta) dbeta[n] = b;
     if (dbias) dbias[n] = c;
   }
+}
+
+// dW (blocks [0, nf)) and, when requested, dgamma / dbeta / dbias (the
+// blocks after them) in one launch: the two reductions are independent.
+__global__ __launch_bounds__(256) void k_finalize_vectors(const float* wpart, int nsplit, const float* sxc,
+                                                          const float* sdzc, int K, int N, float* dw, int nf,
+                                                          const float* cpart, int nblocks, float* dgamma,
+                                                          float* dbeta, float* dbias) {
+  if ((int)blockIdx.x < nf) finalize_body(blockIdx.x, wpart, nsplit, sxc, sdzc, K, N, dw);
+  else col_vectors_body((int)blockIdx.x - nf, cpart, nblocks, N, dgamma, dbeta, dbias);
 }
 
 size_t bwd_lds_bytes(int K, int N, bool sdy) {
@@ -577,10 +583,10 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
   p.qwri = ws + w.qwri;
 
   hipError_t e;
-  {  // both weights into the fragment-interleaved order
-    if (!a.no_ln && (e = launch_relayout(a.qw, a.N, a.K, ws + w.qwi, s)) != hipSuccess) return e;
-    if ((e = launch_relayout(a.qw_row, a.K, a.N, ws + w.qwri, s)) != hipSuccess) return e;
-  }
+  // both weights into the fragment-interleaved order, in one launch
+  if ((e = launch_relayout2(a.no_ln ? nullptr : a.qw, a.N, a.K, ws + w.qwi, a.qw_row, a.K, a.N, ws + w.qwri, s)) !=
+      hipSuccess)
+    return e;
   const int nt = (int)a.N / 64, kt = (int)a.K / 64;
   if (nt <= 8 && kt <= 8) e = launch_main_t<8, 8>(p, a.no_ln, s);
   else if (nt <= 8) e = launch_main_t<8, 16>(p, a.no_ln, s);
@@ -593,15 +599,16 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
   float* sxc = reinterpret_cast<float*>(ws + w.sxc);
   uint8_t* dzt = ws + w.dzt;
   float* sdzc = reinterpret_cast<float*>(ws + w.sdzc);
-  QuantLaunch xq{};
-  xq.src = a.x; xq.rows = a.M; xq.cols = a.K; xq.ld = a.K; xq.src_dtype = 0; xq.fmt = 0; xq.mode = 2;
-  xq.transpose_out = 2; xq.codes = xt; xq.scales = sxc; xq.amax_out = nullptr; xq.workspace = ws + w.xcolp;
-  e = launch_quant(xq, s);
-  if (e != hipSuccess) return e;
+  // X: column maxima (row-chunk partials); then the column scales of X and
+  // of dZ (whose partials the main kernel wrote) in one launch, and both
+  // casts in one launch
+  float* xcolp = reinterpret_cast<float*>(ws + w.xcolp);
+  int64_t xnp = 0;
+  if ((e = launch_col_amax_partials(a.x, 0, a.M, a.K, a.K, xcolp, &xnp, s)) != hipSuccess) return e;
   const float* dzmax = p.part + (size_t)3 * w.nblocks * a.N;
-  e = launch_cast_col_with_partials(p.dz, 1, 1, a.M, a.N, a.N, dzmax, w.nblocks, dzt, sdzc,
-                                    reinterpret_cast<float*>(ws + w.dzmult), s);
-  if (e != hipSuccess) return e;
+  ColQuantJob jx{a.x, 0, 0, a.M, a.K, a.K, xcolp, xnp, xt, sxc, xcolp + xnp * a.K};
+  ColQuantJob jd{p.dz, 1, 1, a.M, a.N, a.N, dzmax, w.nblocks, dzt, sdzc, reinterpret_cast<float*>(ws + w.dzmult)};
+  if ((e = launch_col_quant_pair(jx, jd, s)) != hipSuccess) return e;
 
   float* wpart = reinterpret_cast<float*>(ws + w.wpart);
   dim3 g((unsigned)((a.N + 127) / 128), (unsigned)((a.K + 127) / 128), (unsigned)w.nsplit);
@@ -610,12 +617,10 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t tot = a.K * a.N;
-  hipLaunchKernelGGL(k_finalize, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, wpart, w.nsplit, sxc, sdzc,
-                     (int)a.K, (int)a.N, a.dw);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (a.dgamma || a.dbeta || a.dbias)
-    hipLaunchKernelGGL(k_col_vectors, dim3((unsigned)((a.N + 15) / 16)), dim3(256), 0, s, p.part, w.nblocks, (int)a.N,
-                       a.dgamma, a.dbeta, a.dbias);
+  const int nf = (int)((tot + 255) / 256);
+  const int nv = (a.dgamma || a.dbeta || a.dbias) ? (int)((a.N + 15) / 16) : 0;
+  hipLaunchKernelGGL(k_finalize_vectors, dim3((unsigned)(nf + nv)), dim3(256), 0, s, wpart, w.nsplit, sxc, sdzc,
+                     (int)a.K, (int)a.N, a.dw, nf, p.part, w.nblocks, a.dgamma, a.dbeta, a.dbias);
   return hipGetLastError();
 }
 

@@ -46,6 +46,35 @@ hipError_t launch_relayout(const uint8_t* src, int64_t R, int64_t C, uint8_t* ds
   return hipGetLastError();
 }
 
+namespace {
+// Two [R][C] -> fragment-interleaved rearrangements: blocks [0, n1) the first.
+__global__ __launch_bounds__(256) void k_relayout2(const uint8_t* src1, int64_t R1, int64_t C1, uint8_t* dst1,
+                                                   int64_t n1, const uint8_t* src2, int64_t R2, int64_t C2,
+                                                   uint8_t* dst2) {
+  const bool first = (int64_t)blockIdx.x < n1;
+  const uint8_t* src = first ? src1 : src2;
+  const int64_t R = first ? R1 : R2, C = first ? C1 : C2;
+  uint8_t* dst = first ? dst1 : dst2;
+  const int64_t nch = (C + 127) / 128, pieces = nch * 8;
+  const int64_t u = ((int64_t)blockIdx.x - (first ? 0 : n1)) * 256 + threadIdx.x;
+  if (u >= R * pieces) return;
+  const int64_t row = u / pieces, col = (u - row * pieces) * 16;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (col < C) v = *reinterpret_cast<const uint4*>(src + row * C + col);
+  *reinterpret_cast<uint4*>(dst + ilv_offset(row, col, nch)) = v;
+}
+}  // namespace
+
+hipError_t launch_relayout2(const uint8_t* src1, int64_t R1, int64_t C1, uint8_t* dst1, const uint8_t* src2,
+                            int64_t R2, int64_t C2, uint8_t* dst2, hipStream_t s) {
+  const int64_t b1 = src1 ? (R1 * ((C1 + 127) / 128) * 8 + 255) / 256 : 0;
+  const int64_t b2 = (R2 * ((C2 + 127) / 128) * 8 + 255) / 256;
+  if (b1 + b2 == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_relayout2, dim3((unsigned)(b1 + b2)), dim3(256), 0, s, src1, R1, C1, dst1, b1, src2, R2, C2,
+                     dst2);
+  return hipGetLastError();
+}
+
 size_t fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int x_mode, bool w_packed) {
   size_t b = partial_bytes(M, K, x_mode);
   if (!w_packed && fwd_weight_resident(N, K)) b += ilv_bytes(N, K);

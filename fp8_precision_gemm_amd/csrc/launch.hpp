@@ -26,6 +26,22 @@ struct QuantPlan {
   int64_t ws_floats = 0;  // workspace floats
 };
 QuantPlan quant_plan(int64_t rows, int64_t cols, int mode);
+// One column-scaled quantization whose column maxima are already reduced to
+// row-chunk partials: codes to the fragment-interleaved transposed layout
+// (rows padded to 128 with zero codes), scales and multipliers per column.
+struct ColQuantJob {
+  const void* src;
+  int src_dtype, fmt;
+  int64_t rows, cols, ld;
+  const float* partials;
+  int64_t np;
+  uint8_t* codes_t;
+  float* scales;
+  float* mult;  // cols floats of scratch
+};
+hipError_t launch_col_amax_partials(const void* src, int src_dtype, int64_t rows, int64_t cols, int64_t ld,
+                                   float* partials, int64_t* np, hipStream_t s);
+hipError_t launch_col_quant_pair(const ColQuantJob& a, const ColQuantJob& b, hipStream_t s);
 hipError_t launch_quant(const QuantLaunch& a, hipStream_t s);
 
 // ---- forward -------------------------------------------------------------
@@ -57,6 +73,9 @@ size_t fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int x_mode, bool w_p
 inline size_t ilv_bytes(int64_t R, int64_t C) { return (size_t)R * (size_t)((C + 127) / 128 * 128); }
 // [R][C] row-major codes (R % 16 == 0, C % 16 == 0) -> fragment-interleaved.
 hipError_t launch_relayout(const uint8_t* src, int64_t R, int64_t C, uint8_t* dst, hipStream_t s);
+// Two such rearrangements in one launch (src1 may be NULL to skip the first).
+hipError_t launch_relayout2(const uint8_t* src1, int64_t R1, int64_t C1, uint8_t* dst1, const uint8_t* src2,
+                            int64_t R2, int64_t C2, uint8_t* dst2, hipStream_t s);
 hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s);
 
 // ---- backward ------------------------------------------------------------

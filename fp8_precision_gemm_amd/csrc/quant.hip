@@ -153,11 +153,11 @@ __global__ __launch_bounds__(256) void k_amax_col(const void* src, int64_t rows,
 // in flight each).  Writes the stored scale s, the multiplier r (for the
 // cast) and optionally amax.
 template <int FMT>
-__global__ __launch_bounds__(256) void k_col_scales(const float* partials, int64_t np, int64_t cols, float* scales,
-                                                    float* mult, float* amax_out) {
+__device__ __forceinline__ void col_scales_body(int64_t blk, const float* partials, int64_t np, int64_t cols,
+                                                float* scales, float* mult, float* amax_out) {
   __shared__ float red[16][16];
   const int cl = threadIdx.x & 15, part = threadIdx.x >> 4;
-  const int64_t c = (int64_t)blockIdx.x * 16 + cl;
+  const int64_t c = blk * 16 + cl;
   float m = 0.0f;
   if (c < cols) {
     int64_t k = part;
@@ -179,6 +179,11 @@ __global__ __launch_bounds__(256) void k_col_scales(const float* partials, int64
     if (amax_out) amax_out[c] = m;
   }
 }
+template <int FMT>
+__global__ __launch_bounds__(256) void k_col_scales(const float* partials, int64_t np, int64_t cols, float* scales,
+                                                    float* mult, float* amax_out) {
+  col_scales_body<FMT>(blockIdx.x, partials, np, cols, scales, mult, amax_out);
+}
 
 // ---- pass 2 ---------------------------------------------------------------
 
@@ -195,7 +200,7 @@ struct CastParams {
 // Tile (blockIdx.y, blockIdx.x) covers rows [64 by, +64), cols [64 bx, +64).
 // Thread t: tile row t / 4, tile columns 16 (t % 4) .. +16.
 template <int DT, int FMT, int MODE, int TRANS>
-__global__ __launch_bounds__(256) void k_cast_tile(CastParams p) {
+__device__ __forceinline__ void cast_tile_body(const CastParams& p, int64_t bx, int64_t by) {
   __shared__ float r_col[kTile];             // COL: multiplier per tile column
   __shared__ float red[4];
   __shared__ float colmax[kTile][kTile + 1];  // MX32_COL: |x| staging
@@ -204,8 +209,8 @@ __global__ __launch_bounds__(256) void k_cast_tile(CastParams p) {
 
   const int t = threadIdx.x;
   const int tr = t >> 2, tc = (t & 3) * 16;
-  const int64_t row = (int64_t)blockIdx.y * kTile + tr;
-  const int64_t col0 = (int64_t)blockIdx.x * kTile + tc;
+  const int64_t row = by * kTile + tr;
+  const int64_t col0 = bx * kTile + tc;
   const bool ok = row < p.rows && col0 < p.cols;
 
   float v[16];
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(256) void k_cast_tile(CastParams p) {
     __syncthreads();
     m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     ScalePair sp = scales_from_amax<FMT>(m);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
+    if (bx == 0 && by == 0 && t == 0) {
       static_cast<float*>(p.scales)[0] = sp.s;
       if (p.amax_out) p.amax_out[0] = m;
     }
@@ -229,7 +234,7 @@ __global__ __launch_bounds__(256) void k_cast_tile(CastParams p) {
   } else if (MODE == 1) {  // row
     float a = row < p.rows ? p.amax_in[row] : 0.0f;
     ScalePair sp = scales_from_amax<FMT>(a);
-    if (blockIdx.x == 0 && (t & 3) == 0 && row < p.rows) {
+    if (bx == 0 && (t & 3) == 0 && row < p.rows) {
       static_cast<float*>(p.scales)[row] = sp.s;
       if (p.amax_out) p.amax_out[row] = a;
     }
@@ -237,7 +242,7 @@ __global__ __launch_bounds__(256) void k_cast_tile(CastParams p) {
     for (int i = 0; i < 16; ++i) mult[i] = sp.r;
   } else if (MODE == 2) {  // column: the multipliers from k_col_scales
     if (t < kTile) {
-      const int64_t c = (int64_t)blockIdx.x * kTile + t;
+      const int64_t c = bx * kTile + t;
       r_col[t] = c < p.cols ? p.amax_in[c] : 1.0f;
     }
     __syncthreads();
@@ -266,8 +271,8 @@ __global__ __launch_bounds__(256) void k_cast_tile(CastParams p) {
       for (int i = 0; i < 32; ++i) m = fmaxf(m, colmax[32 * b + i][c]);
       int e8 = e8m0_from_amax<FMT>(m);
       e8_col[b][c] = e8;
-      int64_t gc = (int64_t)blockIdx.x * kTile + c;
-      int64_t grb = (int64_t)blockIdx.y * 2 + b;  // global row block
+      int64_t gc = bx * kTile + c;
+      int64_t grb = by * 2 + b;  // global row block
       if (gc < p.cols && grb * 32 < p.rows) static_cast<uint8_t*>(p.scales)[gc * (p.rows / 32) + grb] = (uint8_t)e8;
     }
     __syncthreads();
@@ -291,8 +296,8 @@ __global__ __launch_bounds__(256) void k_cast_tile(CastParams p) {
     __syncthreads();
     // thread t: tile column t / 4, tile rows 16 (t % 4) .. +16
     const int oc = t >> 2, orow = (t & 3) * 16;
-    const int64_t gc = (int64_t)blockIdx.x * kTile + oc;
-    const int64_t gr = (int64_t)blockIdx.y * kTile + orow;
+    const int64_t gc = bx * kTile + oc;
+    const int64_t gr = by * kTile + orow;
     // TRANS 2: fragment-interleaved [cols][rows padded to 128]; the rows past
     // `rows` (up to the padding) are written as zero codes
     const int64_t nch = (p.rows + 127) / 128;
@@ -306,6 +311,30 @@ __global__ __launch_bounds__(256) void k_cast_tile(CastParams p) {
       *reinterpret_cast<uint4*>(dst) = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
+}
+template <int DT, int FMT, int MODE, int TRANS>
+__global__ __launch_bounds__(256) void k_cast_tile(CastParams p) {
+  cast_tile_body<DT, FMT, MODE, TRANS>(p, blockIdx.x, blockIdx.y);
+}
+
+// Two column-scaled casts to the fragment-interleaved transposed layout in
+// one launch (blocks [0, na) the first, the rest the second; each with its
+// own 2-D tile grid of width gxa / gxb).
+template <int DTA, int FMTA, int DTB, int FMTB>
+__global__ __launch_bounds__(256) void k_cast_col_pair(CastParams a, CastParams b, int64_t na, int64_t gxa,
+                                                       int64_t gxb) {
+  const int64_t blk = blockIdx.x;
+  if (blk < na) cast_tile_body<DTA, FMTA, 2, 2>(a, blk % gxa, blk / gxa);
+  else cast_tile_body<DTB, FMTB, 2, 2>(b, (blk - na) % gxb, (blk - na) / gxb);
+}
+// Two sets of column scales in one launch (blocks [0, na) the first).
+template <int FMTA, int FMTB>
+__global__ __launch_bounds__(256) void k_col_scales_pair(const float* pa, int64_t npa, int64_t ca, float* sa,
+                                                         float* ma, const float* pb, int64_t npb, int64_t cb,
+                                                         float* sb, float* mb, int64_t na) {
+  const int64_t blk = blockIdx.x;
+  if (blk < na) col_scales_body<FMTA>(blk, pa, npa, ca, sa, ma, nullptr);
+  else col_scales_body<FMTB>(blk - na, pb, npb, cb, sb, mb, nullptr);
 }
 
 // trans: 0 plain, 1 transposed row-major, 2 transposed fragment-interleaved
@@ -412,24 +441,35 @@ hipError_t launch_amax_tensor_partials(const void* src, int64_t rows, int64_t co
   return hipGetLastError();
 }
 
-// Column cast with precomputed partial column maxima (np x cols), used by the
-// backward for dZ whose column maxima come out of the fused LN-backward kernel.
-// mult: cols floats of scratch for the multipliers.  Output: codes transposed
-// to [cols][rows] in the fragment-interleaved layout (rows padded to 128).
-hipError_t launch_cast_col_with_partials(const void* src, int src_dtype, int fmt, int64_t rows, int64_t cols,
-                                         int64_t ld, const float* partials, int64_t np, uint8_t* codes_t,
-                                         float* scales, float* mult, hipStream_t s) {
-  dim3 gs((unsigned)((cols + 15) / 16));
-  if (fmt == 0) hipLaunchKernelGGL(k_col_scales<0>, gs, dim3(256), 0, s, partials, np, cols, scales, mult, nullptr);
-  else hipLaunchKernelGGL(k_col_scales<1>, gs, dim3(256), 0, s, partials, np, cols, scales, mult, nullptr);
-  CastParams cp{src, rows, cols, ld, codes_t, scales, nullptr, mult, np};
-  if (src_dtype == 1) {
-    if (fmt == 0) launch_cast<1, 0, 2>(cp, 2, s);
-    else launch_cast<1, 1, 2>(cp, 2, s);
-  } else {
-    if (fmt == 0) launch_cast<0, 0, 2>(cp, 2, s);
-    else launch_cast<0, 1, 2>(cp, 2, s);
-  }
+// Column maxima of a [rows, cols] array as row-chunk partials (np x cols
+// floats at `partials`, np returned); the first pass of the column recipe.
+hipError_t launch_col_amax_partials(const void* src, int src_dtype, int64_t rows, int64_t cols, int64_t ld,
+                                   float* partials, int64_t* np, hipStream_t s) {
+  const QuantPlan q = quant_plan(rows, cols, 2);
+  *np = q.np;
+  dim3 g((unsigned)((cols + 511) / 512), (unsigned)q.np);
+  if (src_dtype == 1) hipLaunchKernelGGL(k_amax_col<1>, g, dim3(256), 0, s, src, rows, cols, ld, q.rpc, partials);
+  else hipLaunchKernelGGL(k_amax_col<0>, g, dim3(256), 0, s, src, rows, cols, ld, q.rpc, partials);
+  return hipGetLastError();
+}
+
+// Two column quantizations from their partial maxima: both sets of scales
+// in one launch, then both casts (to the fragment-interleaved transposed
+// layout, rows padded to 128) in one launch.  The backward's pair: X (bf16,
+// e4m3) and dZ (fp32, e5m2).
+hipError_t launch_col_quant_pair(const ColQuantJob& a, const ColQuantJob& b, hipStream_t s) {
+  if (!(a.src_dtype == 0 && a.fmt == 0 && b.src_dtype == 1 && b.fmt == 1)) return hipErrorInvalidValue;
+  const int64_t sa = (a.cols + 15) / 16, sb = (b.cols + 15) / 16;
+  hipLaunchKernelGGL((k_col_scales_pair<0, 1>), dim3((unsigned)(sa + sb)), dim3(256), 0, s, a.partials, a.np, a.cols,
+                     a.scales, a.mult, b.partials, b.np, b.cols, b.scales, b.mult, sa);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const CastParams ca{a.src, a.rows, a.cols, a.ld, a.codes_t, a.scales, nullptr, a.mult, a.np};
+  const CastParams cb{b.src, b.rows, b.cols, b.ld, b.codes_t, b.scales, nullptr, b.mult, b.np};
+  const int64_t gxa = (a.cols + kTile - 1) / kTile, gya = ((a.rows + 127) / 128 * 128 + kTile - 1) / kTile;
+  const int64_t gxb = (b.cols + kTile - 1) / kTile, gyb = ((b.rows + 127) / 128 * 128 + kTile - 1) / kTile;
+  hipLaunchKernelGGL((k_cast_col_pair<0, 0, 1, 1>), dim3((unsigned)(gxa * gya + gxb * gyb)), dim3(256), 0, s, ca, cb,
+                     gxa * gya, gxa, gxb);
   return hipGetLastError();
 }
 
