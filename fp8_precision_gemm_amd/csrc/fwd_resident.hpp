@@ -148,6 +148,20 @@ __device__ __forceinline__ float sum4(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Sum of n values as a balanced tree (pairs of neighbours first).
+template <int n>
+__device__ __forceinline__ float tree_sum(const float (&v)[n]) {
+  if constexpr (n == 1) {
+    return v[0];
+  } else {
+    constexpr int h = (n + 1) / 2;
+    float a[h];
+#pragma unroll
+    for (int i = 0; i < h; ++i) a[i] = (2 * i + 1 < n) ? v[2 * i] + v[2 * i + 1] : v[2 * i];
+    return tree_sum<h>(a);
+  }
+}
+
 // 8 bf16 (one 16-byte piece) -> fp32
 __device__ __forceinline__ void unpack8(const uint4& u, float v[8]) {
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
@@ -512,89 +526,81 @@ struct ResBlock {
     const float bound = MODE == 3 ? ldexpf(bw, (int)rsv - 127) + bb : sx * bw + bb;
     cs = row_rescale(bound);
     const float* cb = cvec + c0 + 4 * g;
-    float s = 0.0f;
+    // sums as short trees (per tile, then over the tiles) rather than one
+    // long chain: the statistics sit on the step's critical path
+    float st[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
+      st[t] = 0.0f;
       if (tv(t)) {
         const float4 sw4 = *reinterpret_cast<const float4*>(cb + 16 * t);
         const float4 b4 = *reinterpret_cast<const float4*>(cb + N + 16 * t);
         const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float z = MODE == 3 ? acc[t][j] + bv[j] : fmaf(acc[t][j], sx * swv[j], bv[j]);
-          acc[t][j] = z;
-          s += z;
-        }
+        for (int j = 0; j < 4; ++j)
+          acc[t][j] = MODE == 3 ? acc[t][j] + bv[j] : fmaf(acc[t][j], sx * swv[j], bv[j]);
+        st[t] = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
       }
     }
-    s = sum4(s);
+    const float s = sum4(tree_sum<NT>(st));
     const float mw = s * inv_nw;
     // deviations scaled by cs before squaring (rows too large to square in
     // fp32); one fma rounds (z - mw) * cs once, which for cs = 1 is z - mw
     // and otherwise its exact power-of-two scaling: no branch on the rare case
     const float nmc = -mw * cs;
-    float q = 0.0f;
+    float qt[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-      if (tv(t))
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float d = fmaf(acc[t][j], cs, nmc);
-          q = fmaf(d, d, q);
-        }
-    q = sum4(q);
+    for (int t = 0; t < NT; ++t) {
+      qt[t] = 0.0f;
+      if (tv(t)) {
+        const float d0 = fmaf(acc[t][0], cs, nmc), d1 = fmaf(acc[t][1], cs, nmc);
+        const float d2 = fmaf(acc[t][2], cs, nmc), d3 = fmaf(acc[t][3], cs, nmc);
+        qt[t] = fmaf(d1, d1, d0 * d0) + fmaf(d3, d3, d2 * d2);
+      }
+    }
+    const float q = sum4(tree_sum<NT>(qt));
     red[(buf * kResRows + r) * kRedRow + wave] = make_float2(s, q);  // the row's 4 lanes write the same pair
   }
 
   // ---- epilogue, part 2 (after the barrier): combine the slices, normalize, store
   __device__ __forceinline__ void epilogue_out(int buf, int64_t t, const v4f (&acc)[NT], float cs) {
-    const float4* rw4 = reinterpret_cast<const float4*>(red + (buf * kResRows + r) * kRedRow);
-    float sw_[kWaves], qw_[kWaves];
-#pragma unroll
-    for (int i = 0; i < kWaves / 2; ++i) {
-      const float4 u = rw4[i];
-      sw_[2 * i] = u.x; qw_[2 * i] = u.y; sw_[2 * i + 1] = u.z; qw_[2 * i + 1] = u.w;
-    }
-    float S = 0.0f, Q = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      S += sw_[w];
-      Q += qw_[w];
-    }
+    // The 4 lanes of a row (g = 0..3) each take two of the 8 slices (2g and
+    // 2g + 1) and the partial terms are summed across them with permlane
+    // swaps: one LDS read per lane and a quarter of the combine each.
+    const float4 u = reinterpret_cast<const float4*>(red + (buf * kResRows + r) * kRedRow)[g];
+    const float S = sum4(u.x + u.z);
     const float invn = 1.0f / (float)N;
     const float mean = S * invn;
-    // between-slice term: sum_w (s_w - n_w mean)^2 / n_w, with the
-    // deviations scaled by cs like the within-slice sums (cs = 1: unscaled)
-    float B = 0.0f;
+    // within-slice centred sums plus the between-slice term
+    // (s_w - n_w mean)^2 / n_w, the deviations scaled by cs like the
+    // within-slice sums (cs = 1: unscaled)
+    float V;
     if (FULL || N == 128 * NT) {  // every slice has 16*NT columns
       const float ns = (float)(16 * NT);
+      float d0, d1;
       if ((NT & (NT - 1)) == 0) {  // ns and cs powers of two: -ns*mean*cs is exact
         const float nsm = -ns * mean * cs;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float d = fmaf(sw_[w], cs, nsm);
-          B = fmaf(d, d, B);
-        }
+        d0 = fmaf(u.x, cs, nsm);
+        d1 = fmaf(u.z, cs, nsm);
       } else {
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-          const float d = fmaf(-ns, mean, sw_[w]) * cs;
-          B = fmaf(d, d, B);
-        }
+        d0 = fmaf(-ns, mean, u.x) * cs;
+        d1 = fmaf(-ns, mean, u.z) * cs;
       }
-      B *= 1.0f / ns;
+      V = (u.y + u.w) + fmaf(d0, d0, d1 * d1) * (1.0f / ns);
     } else {
+      V = u.y + u.w;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const int nw = 16 * min(max(T16 - w * NT, 0), NT);
+      for (int h = 0; h < 2; ++h) {
+        const int nw = 16 * min(max(T16 - (2 * g + h) * NT, 0), NT);
         if (nw > 0) {
-          const float d = fmaf(-(float)nw, mean, sw_[w]) * cs;
-          B = fmaf(d * (1.0f / (float)nw), d, B);
+          const float d = fmaf(-(float)nw, mean, h ? u.z : u.x) * cs;
+          V = fmaf(d * (1.0f / (float)nw), d, V);
         }
       }
     }
+    V = sum4(V);
     // variance of the scaled deviations is var * cs^2: rstd = cs / sqrt(var cs^2 + eps cs^2)
-    const float rstd = cs * __builtin_amdgcn_rsqf(fmaf(Q + B, invn, p.eps * cs * cs));
+    const float rstd = cs * __builtin_amdgcn_rsqf(fmaf(V, invn, p.eps * cs * cs));
     const int64_t m = t * kResRows + r;
     const bool row_ok = FULL || m < p.M;
     if (OPT && row_ok && wave == 0 && g == 0) {
