@@ -25,6 +25,9 @@ Steps (the plain definition; the GPU kernel is a faster evaluation of it):
   4. mu = mean_n Z, v = mean_n (Z - mu)**2 (population variance, two
      passes), y = gamma * (Z - mu) / sqrt(v + eps) + beta;
   5. Y = RNE-bf16(y).
+The BlockNorm + Hard Swish variant ([LoKA] section III-B2 Fig. 7d and
+section III-B3) replaces step 4 by y = h(Z / sqrt(mean_block Z^2 + eps)) over
+fixed blocks of features, h the Hard Swish.
 """
 
 import numpy as np
@@ -101,6 +104,44 @@ def gemm_ln_forward(x_bits, w_bits, bias_bits=None, gamma_bits=None, beta_bits=N
         "y_bits": f64_to_bf16(y), "y": y, "z": z, "mean": mu, "rstd": rstd,
         "qx": qx, "sx": sx, "qw": qw, "sw": sw,
     }
+
+
+def hard_swish(v):
+    """[LoKA] section III-B3 (Hard Swish): h(v) = v * ReLU6(v + 3) / 6 with
+    ReLU6(u) = min(max(u, 0), 6): zero at and below -3, the identity at and
+    above 3, piecewise quadratic between."""
+    return v * np.minimum(np.maximum(v + 3.0, 0.0), 6.0) / 6.0
+
+
+def block_rmsnorm(z, block, eps):
+    """[LoKA] section III-B2 (BlockNorm, Fig. 7d): root-mean-square
+    normalization over fixed blocks of `block` consecutive features, each
+    block's statistic computed on its own (an unparameterized grouped
+    RMSNorm).  z [M, N] with N a multiple of block; returns (yhat, rinv),
+    yhat = z / sqrt(mean_block(z^2) + eps) and rinv [M, N/block] the
+    blocks' 1 / sqrt(mean(z^2) + eps)."""
+    M, N = z.shape
+    assert N % block == 0
+    zb = z.reshape(M, N // block, block)
+    rinv = 1.0 / np.sqrt((zb * zb).mean(axis=2) + eps)
+    return (zb * rinv[:, :, None]).reshape(M, N), rinv
+
+
+def gemm_blocknorm_hswish_forward(x_bits, w_bits, bias_bits=None, eps=1e-5, recipe="row", block=256):
+    """The BlockNorm + Hard Swish variant of the block ([LoKA] section
+    III-B2 and III-B3, the "LoKA Mods" epilogue): steps 1-3 and the bias as
+    in gemm_ln_forward, then y = h(BlockNorm(Z)) per block of `block`
+    features (no affine parameters), Y = RNE-bf16(y).  Returns y_bits, y,
+    z, rinv and the quantized operands."""
+    x = bf16_to_f64(x_bits)
+    w = bf16_to_f64(w_bits)
+    N = w.shape[1]
+    eps = float(np.float32(eps))
+    z, qx, sx, qw, sw = quantized_product(x, w, recipe)
+    z = z + _vec(bias_bits, N, 0.0)[None, :]
+    yhat, rinv = block_rmsnorm(z, block, eps)
+    y = hard_swish(yhat)
+    return {"y_bits": f64_to_bf16(y), "y": y, "z": z, "rinv": rinv, "qx": qx, "sx": sx, "qw": qw, "sw": sw}
 
 
 def reference_forward(x_bits, w_bits, bias_bits=None, gamma_bits=None, beta_bits=None, eps=1e-5):
