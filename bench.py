@@ -45,7 +45,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-rows", action="store_true", help="skip the other workloads")
     p.add_argument("--only", default=None,
-                   help="comma list of workloads to time (for profiling): fwd,tensor,mx,bwd,grouped,copy")
+                   help="comma list of workloads to time (for profiling): fwd,tensor,mx,blocknorm,bwd,grouped,copy")
     return p.parse_args()
 
 
@@ -109,7 +109,7 @@ def dev_bf16(torch, bits):
     return t.view(torch.bfloat16).cuda()
 
 
-def bench_forward(torch, lk, case, x_mode, steps, warmup, stream, packed=True):
+def bench_forward(torch, lk, case, x_mode, steps, warmup, stream, packed=True, epilogue="layernorm"):
     """Time loka_gemm_fp8_ln over ROTATE buffer sets; returns a dict.  The
     weight is quantized straight into the packed layout the kernel reads
     (packed=False: row-major [N, K] codes, rearranged inside every call)."""
@@ -120,10 +120,13 @@ def bench_forward(torch, lk, case, x_mode, steps, warmup, stream, packed=True):
     qw, sw, _ = lk.loka_quant_fp8(w, mode=wmode, transpose_out=layout, stream=stream)
     x0 = dev_bf16(torch, case["x"])
     vec = [dev_bf16(torch, case[k]) for k in ("bias", "gamma", "beta")]
+    if epilogue != "layernorm":
+        vec = vec[:1] + [None, None]  # BlockNorm has no affine parameters
     launches = []
     for i in range(ROTATE):
         x = x0 if i == 0 else x0.clone()
-        f, _ = lk.loka_gemm_fp8_ln(x, qw, sw, *vec, x_mode=x_mode, stream=stream, prepare=True, w_packed=packed)
+        f, _ = lk.loka_gemm_fp8_ln(x, qw, sw, *vec, x_mode=x_mode, stream=stream, prepare=True, w_packed=packed,
+                                   epilogue=epilogue)
         launches.append(f)
     torch.cuda.synchronize()
     secs, n = timed_graph(torch, launches, steps, warmup, stream)
@@ -257,6 +260,15 @@ def main():
         rows["mx_fwd_65536x1024x256"] = {k: round(v, 3) for k, v in r.items()}
         rows["mx_fwd_65536x1024x256"]["hbm_frac"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
         print(f"[bench] mx forward: {r['us']:.2f} us", file=sys.stderr, flush=True)
+    if not args.no_rows and want("blocknorm"):
+        for nm, c in (("blocknorm_fwd_16384x512x512", case),
+                      ("blocknorm_fwd_4096x512x4096", workloads.forward_case(4096, 512, 4096, seed=7,
+                                                                             x_dist="student_t3_outliers"))):
+            r = bench_forward(torch, lk, c, "row", max(200, args.steps // 4), max(20, args.warmup // 4), stream,
+                              epilogue="blocknorm_hswish")
+            rows[nm] = {k: round(v, 3) for k, v in r.items()}
+            rows[nm]["hbm_frac"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
+            print(f"[bench] {nm}: {r['us']:.2f} us", file=sys.stderr, flush=True)
     if not args.no_rows and want("bwd"):
         r = bench_backward(torch, lk, case, args.steps, args.warmup, stream)
         rows["bwd_16384x512x512"] = {k: round(v, 3) for k, v in r.items()}

@@ -29,6 +29,8 @@ STATUS = {0: "LOKA_OK", 1: "LOKA_ERR_INVALID_ARG", 2: "LOKA_ERR_UNSUPPORTED", 3:
           4: "LOKA_ERR_WORKSPACE", 5: "LOKA_ERR_HIP"}
 BWD_NO_LN = 1
 FWD_W_PACKED = 1
+FWD_BLOCKNORM_HSWISH = 2
+EPILOGUES = {"layernorm": 0, "blocknorm_hswish": FWD_BLOCKNORM_HSWISH}
 
 c_i64, c_i32, c_f32, c_vp, c_sz = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
 
@@ -187,19 +189,24 @@ def loka_quant_fp8(src, fmt="e4m3", mode="row", transpose_out=False, codes=None,
     return codes, scales, amax
 
 
-def _fwd_args(x, qw, sw, bias, gamma, beta, eps, x_mode, y, z, mean, rstd, qx_out, sx_out, w_packed=False):
+def _fwd_args(x, qw, sw, bias, gamma, beta, eps, x_mode, y, z, mean, rstd, qx_out, sx_out, w_packed=False,
+              epilogue="layernorm"):
     M, K = x.shape
     N = qw.shape[0]
-    return FwdArgs(M=M, N=N, K=K, x_mode=MODES[x_mode], flags=FWD_W_PACKED if w_packed else 0, eps=eps, x=_ptr(x), qw=_ptr(qw), sw=_ptr(sw),
+    flags = (FWD_W_PACKED if w_packed else 0) | EPILOGUES[epilogue]
+    return FwdArgs(M=M, N=N, K=K, x_mode=MODES[x_mode], flags=flags, eps=eps, x=_ptr(x), qw=_ptr(qw), sw=_ptr(sw),
                    bias=_ptr(bias), gamma=_ptr(gamma), beta=_ptr(beta), y=_ptr(y), z=_ptr(z), mean=_ptr(mean),
                    rstd=_ptr(rstd), qx_out=_ptr(qx_out), sx_out=_ptr(sx_out))
 
 
 def loka_gemm_fp8_ln(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e-5, x_mode="row", y=None, want_z=False,
-                     want_stats=False, want_qx=False, workspace=None, stream=None, prepare=False, w_packed=False):
+                     want_stats=False, want_qx=False, workspace=None, stream=None, prepare=False, w_packed=False,
+                     epilogue="layernorm"):
     """Y = LayerNorm(dequant(q(X) . q(W)) + bias) for bf16 X [M, K] and the
     pre-quantized weight qw [N, K] (e4m3) with scales sw; with w_packed=True
     qw is in the packed layout (loka_quant_fp8(transpose_out="packed")).
+    epilogue="blocknorm_hswish": Y = HardSwish(BlockNorm_256(Z)) instead
+    (row recipe, no gamma/beta, no mean/rstd).
 
     Returns a dict with y and the requested optional outputs.  With
     prepare=True returns (launch, outputs) where launch() enqueues the call
@@ -227,7 +234,7 @@ def loka_gemm_fp8_ln(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e-5, x_mo
         else:
             out["sx"] = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
     a = _fwd_args(x, qw, sw, bias, gamma, beta, eps, x_mode, out["y"], out.get("z"), out.get("mean"),
-                  out.get("rstd"), out.get("qx"), out.get("sx"), w_packed)
+                  out.get("rstd"), out.get("qx"), out.get("sx"), w_packed, epilogue)
     lib = library()
     nb = lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(a))
     ws = _workspace(nb, dev, workspace)

@@ -135,18 +135,32 @@ loka_status loka_quant_fp8(const loka_quant_args* a, void* stream) {
 // ---------------------------------------------------------------------------
 size_t loka_gemm_fp8_ln_workspace_size(const loka_fwd_args* a) {
   if (a == nullptr || a->M <= 0 || a->K <= 0) return 0;
-  return loka::fwd_workspace_bytes(a->M, a->N, a->K, a->x_mode, (a->flags & LOKA_FWD_W_PACKED) != 0);
+  return loka::fwd_workspace_bytes(a->M, a->N, a->K, a->x_mode, (a->flags & LOKA_FWD_W_PACKED) != 0,
+                                   (a->flags & LOKA_FWD_BLOCKNORM_HSWISH) != 0);
 }
 
 loka_status loka_gemm_fp8_ln(const loka_fwd_args* a, void* stream) {
   REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
   REQUIRE(a->x_mode == LOKA_SCALE_TENSOR || a->x_mode == LOKA_SCALE_ROW || a->x_mode == LOKA_SCALE_MX32_ROW,
           LOKA_ERR_INVALID_ARG, "x_mode must be TENSOR, ROW or MX32_ROW (got %d)", a->x_mode);
-  REQUIRE((a->flags & ~LOKA_FWD_W_PACKED) == 0, LOKA_ERR_INVALID_ARG, "unknown flags %d", a->flags);
+  REQUIRE((a->flags & ~(LOKA_FWD_W_PACKED | LOKA_FWD_BLOCKNORM_HSWISH)) == 0, LOKA_ERR_INVALID_ARG,
+          "unknown flags %d", a->flags);
   const bool packed = (a->flags & LOKA_FWD_W_PACKED) != 0;
-  loka_status st = check_fwd_shape(a->M, a->N, a->K, a->x_mode);
-  if (st != LOKA_OK) return st;
-  REQUIRE(!packed || loka::fwd_weight_resident(a->N, a->K), LOKA_ERR_UNSUPPORTED,
+  const bool blocknorm = (a->flags & LOKA_FWD_BLOCKNORM_HSWISH) != 0;
+  loka_status st;
+  if (blocknorm) {
+    REQUIRE(a->M >= 0 && a->N >= 0 && a->K >= 0, LOKA_ERR_INVALID_ARG, "negative size");
+    REQUIRE(a->x_mode == LOKA_SCALE_ROW, LOKA_ERR_UNSUPPORTED, "the BlockNorm epilogue supports x_mode ROW only");
+    REQUIRE(loka::fwd_blocknorm_fits(a->N, a->K), LOKA_ERR_UNSUPPORTED,
+            "BlockNorm needs N %% 256 == 0, 256 <= N <= 8192, K %% 16 == 0, 16 <= K <= 1024 (got N=%lld K=%lld)",
+            (long long)a->N, (long long)a->K);
+    REQUIRE(a->M <= ((int64_t)1 << 31) - 64, LOKA_ERR_UNSUPPORTED, "M too large");
+    REQUIRE(a->gamma == nullptr && a->beta == nullptr && a->mean == nullptr && a->rstd == nullptr,
+            LOKA_ERR_INVALID_ARG, "the BlockNorm epilogue has no gamma/beta and no mean/rstd outputs");
+  } else {
+    if ((st = check_fwd_shape(a->M, a->N, a->K, a->x_mode)) != LOKA_OK) return st;
+  }
+  REQUIRE(!packed || blocknorm || loka::fwd_weight_resident(a->N, a->K), LOKA_ERR_UNSUPPORTED,
           "LOKA_FWD_W_PACKED needs the weight-resident shapes: N <= 512 and K <= 1024 (N <= 256), 640 (N <= 384) "
           "or 512 (N <= 512); got N=%lld K=%lld",
           (long long)a->N, (long long)a->K);
@@ -163,6 +177,7 @@ loka_status loka_gemm_fp8_ln(const loka_fwd_args* a, void* stream) {
   f.y = a->y; f.z = a->z; f.mean = a->mean; f.rstd = a->rstd; f.qx_out = a->qx_out; f.sx_out = a->sx_out;
   f.workspace = a->workspace;
   f.w_packed = packed;
+  f.blocknorm = blocknorm;
   return hip_status(loka::launch_fwd(f, static_cast<hipStream_t>(stream)), "loka_gemm_fp8_ln");
 }
 

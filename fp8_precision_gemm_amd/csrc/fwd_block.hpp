@@ -57,6 +57,7 @@ struct FwdBlock {
   void* sx_out;
   float eps;
   float x_r, x_s;  // tensor mode: X multiplier and dequantization scale
+  int ldy;         // row stride of y and z in elements (0: N); a column slab's is the full width
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

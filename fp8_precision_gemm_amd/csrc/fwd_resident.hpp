@@ -197,7 +197,12 @@ __device__ __forceinline__ v4f mfma_mx_sel(int sel, const v8i& a, const v8i& b, 
 // FULL: N = 128*NT, K = 256*KQ and M a multiple of 16, so every wavefront
 // owns NT whole column tiles, every lane a whole share of each row and every
 // tile 16 real rows: no partial-shape guards.
-template <int MODE, int NT, int KC, bool OPT, bool FULL>
+// EPI: 0 = LayerNorm over the row (gamma, beta); 1 = BlockNorm over blocks
+// of 256 columns (RMS, no affine parameters) followed by Hard Swish
+// ([LoKA] section III-B2 Fig. 7d and III-B3).  With EPI 1 the block covers
+// one column slab of 128*NT columns (a whole number of 256-blocks).
+constexpr int kBlockNorm = 256;
+template <int MODE, int NT, int KC, bool OPT, bool FULL, int EPI = 0>
 struct ResBlock {
   using R = Res<NT, KC>;
   static constexpr int KQ = R::KQ, D = R::D, LDX = R::LDX, XE = R::XE, KP = R::KP;
@@ -205,7 +210,7 @@ struct ResBlock {
 
   const FwdBlock& p;
   int64_t tb, te;  // tile range [tb, te)
-  int K, N, kcv, kb, T16, nv, c0, tid, lane, wave, r, g, hrow, hl;
+  int K, N, ldy, kcv, kb, T16, nv, c0, tid, lane, wave, r, g, hrow, hl;
   uint8_t* codes;
   uint8_t* xe8;
   float* rs;
@@ -235,6 +240,7 @@ struct ResBlock {
       : p(p_), tb(tb_), te(te_) {
     K = p.K;
     N = p.N;
+    ldy = p.ldy > 0 ? p.ldy : p.N;
     kcv = FULL ? KC : (K + 127) >> 7;
     kb = K >> 5;
     T16 = N >> 4;
@@ -542,6 +548,16 @@ struct ResBlock {
         st[t] = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
       }
     }
+    if constexpr (EPI == 1) {  // BlockNorm: the slice's sum of squares (scaled by cs like the LayerNorm path)
+      float qt[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const float d0 = acc[t][0] * cs, d1 = acc[t][1] * cs, d2 = acc[t][2] * cs, d3 = acc[t][3] * cs;
+        qt[t] = fmaf(d1, d1, d0 * d0) + fmaf(d3, d3, d2 * d2);
+      }
+      red[(buf * kResRows + r) * kRedRow + wave] = make_float2(sum4(tree_sum<NT>(qt)), 0.0f);
+      return;
+    }
     const float s = sum4(tree_sum<NT>(st));
     const float mw = s * inv_nw;
     // deviations scaled by cs before squaring (rows too large to square in
@@ -564,6 +580,10 @@ struct ResBlock {
 
   // ---- epilogue, part 2 (after the barrier): combine the slices, normalize, store
   __device__ __forceinline__ void epilogue_out(int buf, int64_t t, const v4f (&acc)[NT], float cs) {
+    if constexpr (EPI == 1) {
+      blocknorm_out(buf, t, acc, cs);
+      return;
+    }
     // The 4 lanes of a row (g = 0..3) each take two of the 8 slices (2g and
     // 2g + 1) and the partial terms are summed across them with permlane
     // swaps: one LDS read per lane and a quarter of the combine each.
@@ -623,10 +643,55 @@ struct ResBlock {
         *reinterpret_cast<uint2*>(ystg + r * YST + (16 * t2 + 4 * g) * 2) =
             make_uint2(pack_bf16_hw(o[0], o[1]), pack_bf16_hw(o[2], o[3]));
         if (OPT && p.z != nullptr && row_ok)
-          *reinterpret_cast<float4*>(p.z + m * N + cl + 16 * t2) =
+          *reinterpret_cast<float4*>(p.z + m * ldy + cl + 16 * t2) =
               make_float4(acc[t2][0], acc[t2][1], acc[t2][2], acc[t2][3]);
       }
     }
+    store_y(t);
+  }
+
+  // BlockNorm + Hard Swish (after the barrier): the 256-column block of this
+  // wavefront's slice has 256 / (16 NT) slices, whose sums of squares the
+  // row's lanes add (NT = 2: all 8 slices, two per lane; NT = 4: the four
+  // slices of the block, two per lane, paired across g and g^1); then
+  // y = h(z / sqrt(mean z^2 + eps)) with h(t) = t * clamp(t / 6 + 1/2, 0, 1).
+  __device__ __forceinline__ void blocknorm_out(int buf, int64_t t, const v4f (&acc)[NT], float cs) {
+    static_assert(NT == 2 || NT == 4, "BlockNorm slabs are 256 or 512 columns");
+    const float4* rw = reinterpret_cast<const float4*>(red + (buf * kResRows + r) * kRedRow);
+    float V;
+    if (NT == 2) {
+      const float4 u = rw[g];
+      V = sum4(u.x + u.z);
+    } else {
+      const float4 u = rw[2 * (wave >> 2) + (g & 1)];
+      const float v = u.x + u.z;
+      const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+      V = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    }
+    const float rinv = cs * __builtin_amdgcn_rsqf(fmaf(V, 1.0f / (float)kBlockNorm, p.eps * cs * cs));
+    const int64_t m = t * kResRows + r;
+    const bool row_ok = FULL || m < p.M;
+    const int cl = c0 + 4 * g;
+    constexpr int YST = res_yst(NT);
+#pragma unroll
+    for (int t2 = 0; t2 < NT; ++t2) {
+      float o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float v = acc[t2][j] * rinv;
+        o[j] = v * __builtin_amdgcn_fmed3f(fmaf(v, 1.0f / 6.0f, 0.5f), 0.0f, 1.0f);
+      }
+      *reinterpret_cast<uint2*>(ystg + r * YST + (16 * t2 + 4 * g) * 2) =
+          make_uint2(pack_bf16_hw(o[0], o[1]), pack_bf16_hw(o[2], o[3]));
+      if (OPT && p.z != nullptr && row_ok)
+        *reinterpret_cast<float4*>(p.z + m * ldy + cl + 16 * t2) =
+            make_float4(acc[t2][0], acc[t2][1], acc[t2][2], acc[t2][3]);
+    }
+    store_y(t);
+  }
+
+  __device__ __forceinline__ void store_y(int64_t t) {
+    constexpr int YST = res_yst(NT);
     // The wavefront's 16 x 16*NT block of Y goes out from the staging rows in
     // 16-byte pieces, consecutive lanes along a row: each store instruction
     // writes whole 32*NT-byte row segments (for NT = 4, eight 128-byte
@@ -644,7 +709,7 @@ struct ResBlock {
         const uint4 v = *reinterpret_cast<const uint4*>(ystg + row * YST + ch * 16);
         const int64_t mm = t * kResRows + row;
         if (FULL || (mm < p.M && ch < 2 * nv))
-          __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p.y + mm * N + c0 + ch * 8));
+          __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p.y + mm * ldy + c0 + ch * 8));
       }
     }
   }

@@ -13,6 +13,7 @@ namespace fwd {
 hipError_t launch_tensor(const FwdBlock& p, const float* partials, int np, hipStream_t s);
 hipError_t launch_row(const FwdBlock& p, const float* partials, int np, hipStream_t s);
 hipError_t launch_mx(const FwdBlock& p, const float* partials, int np, hipStream_t s);
+hipError_t launch_row_blocknorm(const FwdBlock& p, hipStream_t s);
 }  // namespace fwd
 
 bool fwd_weight_resident(int64_t N, int64_t K) { return N <= 512 && K <= 2048 && fwd::res_fits((int)K, (int)N); }
@@ -75,9 +76,15 @@ hipError_t launch_relayout2(const uint8_t* src1, int64_t R1, int64_t C1, uint8_t
   return hipGetLastError();
 }
 
-size_t fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int x_mode, bool w_packed) {
+// N a multiple of 256 up to 8192; slabs of 512 columns need K <= 512, slabs
+// of 256 columns K <= 1024
+bool fwd_blocknorm_fits(int64_t N, int64_t K) {
+  return N >= 256 && N <= 8192 && N % 256 == 0 && K >= 16 && K % 16 == 0 && K <= 1024;
+}
+
+size_t fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int x_mode, bool w_packed, bool blocknorm) {
   size_t b = partial_bytes(M, K, x_mode);
-  if (!w_packed && fwd_weight_resident(N, K)) b += ilv_bytes(N, K);
+  if (!w_packed && (blocknorm || fwd_weight_resident(N, K))) b += ilv_bytes(N, K);
   return b;
 }
 
@@ -93,13 +100,15 @@ hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s) {
   p.y = static_cast<uint16_t*>(a.y);
   p.z = a.z; p.mean = a.mean; p.rstd = a.rstd; p.qx_out = a.qx_out; p.sx_out = a.sx_out;
   p.eps = a.eps; p.x_r = 1.0f; p.x_s = 1.0f;
-  if (!a.w_packed && fwd_weight_resident(a.N, a.K)) {
+  p.ldy = (int)a.N;
+  if (!a.w_packed && (a.blocknorm || fwd_weight_resident(a.N, a.K))) {
     // the resident kernel reads the weight fragment-interleaved
     uint8_t* wi = static_cast<uint8_t*>(a.workspace) + partial_bytes(a.M, a.K, a.x_mode);
     hipError_t e = launch_relayout(a.qw, a.N, a.K, wi, s);
     if (e != hipSuccess) return e;
     p.qw = wi;
   }
+  if (a.blocknorm) return fwd::launch_row_blocknorm(p, s);
   if (a.x_mode == 0) {
     float* partials = static_cast<float*>(a.workspace);
     const int np = (int)quant_plan(a.M, a.K, 0).np;

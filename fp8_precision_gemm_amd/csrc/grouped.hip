@@ -188,6 +188,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped_res(const GroupDev* groups
     p.M = gd.M; p.N = (int)gd.N; p.K = (int)gd.K;
     p.x = static_cast<const uint16_t*>(gd.x);
     p.qw = group_weight(wsrc, gd, g); p.sw = gd.sw;
+    p.ldy = (int)gd.N;
     p.bias = static_cast<const uint16_t*>(gd.bias);
     p.gamma = static_cast<const uint16_t*>(gd.gamma);
     p.beta = static_cast<const uint16_t*>(gd.beta);
@@ -224,6 +225,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped_res_arg(const GroupDev* gr
     p.M = gd.M; p.N = (int)gd.N; p.K = (int)gd.K;
     p.x = static_cast<const uint16_t*>(gd.x);
     p.qw = group_weight(wsrc, gd, plan.gid[q]); p.sw = gd.sw;
+    p.ldy = (int)gd.N;
     p.bias = static_cast<const uint16_t*>(gd.bias);
     p.gamma = static_cast<const uint16_t*>(gd.gamma);
     p.beta = static_cast<const uint16_t*>(gd.beta);

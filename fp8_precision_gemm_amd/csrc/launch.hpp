@@ -62,12 +62,15 @@ struct FwdLaunch {
   uint8_t* qx_out;
   void* sx_out;
   void* workspace;
-  bool w_packed;  // qw already in the fragment-interleaved layout
+  bool w_packed;   // qw already in the fragment-interleaved layout
+  bool blocknorm;  // BlockNorm(256) + Hard Swish epilogue instead of LayerNorm
 };
 // Workspace of one forward: the tensor recipe's amax partials, then (for
 // the weight-resident kernel with a row-major weight) the weight rearranged
 // into the fragment-interleaved layout.
-size_t fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int x_mode, bool w_packed);
+size_t fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int x_mode, bool w_packed, bool blocknorm);
+// BlockNorm + Hard Swish: can the column-slab resident kernel take (N, K)?
+bool fwd_blocknorm_fits(int64_t N, int64_t K);
 // Bytes of a [R][C] code array in the fragment-interleaved layout (C padded
 // to a multiple of 128).
 inline size_t ilv_bytes(int64_t R, int64_t C) { return (size_t)R * (size_t)((C + 127) / 128 * 128); }

@@ -171,17 +171,29 @@ loka_status loka_quant_fp8(const loka_quant_args* args, void* stream);
  *   512, K <= 1024 / 640 / 512 for N <= 256 / 384 / 512), the weight
  *   rearranged into the packed layout (one extra pass over qw per call;
  *   LOKA_FWD_W_PACKED avoids it).  0 when neither applies.
- *   flags: 0 or LOKA_FWD_W_PACKED (qw in the packed layout; only on the
- *   weight-resident shapes, LOKA_ERR_UNSUPPORTED otherwise).
+ *   flags: LOKA_FWD_W_PACKED (qw in the packed layout; only on the
+ *   weight-resident shapes or with BlockNorm, LOKA_ERR_UNSUPPORTED
+ *   otherwise) and/or LOKA_FWD_BLOCKNORM_HSWISH (below), or 0.
  * Requirements: M >= 0; N % 64 == 0 and 64 <= N <= 1024 (else
  * UNSUPPORTED: the row must fit one workgroup); K % 16 == 0 (MX: % 32),
  * 16 <= K <= 2048.
  * ---------------------------------------------------------------------- */
 #define LOKA_FWD_W_PACKED 1 /* qw is in loka_quant_fp8's transpose_out = 2 layout */
+/* BlockNorm + Hard Swish epilogue instead of LayerNorm: LoKA section III-B2
+ * (Block-wise Normalization, Fig. 7d) and III-B3 (Hard Swish):
+ *   Y = h(Z / sqrt(mean_b Z^2 + eps)) over blocks b of 256 consecutive
+ *   columns, h(t) = t * min(max(t + 3, 0), 6) / 6, Z as above (bias
+ *   optional), no affine parameters, bf16 RNE.
+ * Requirements: x_mode ROW; gamma, beta, mean and rstd NULL; N % 256 == 0,
+ * 256 <= N <= 8192; 16 <= K <= 1024, K % 16 == 0.  The row does not have to
+ * fit one workgroup: N is processed as independent slabs of 512 columns
+ * (N % 512 == 0 and K <= 512) or else 256 columns.  Optional z, qx_out and
+ * sx_out as for LayerNorm. */
+#define LOKA_FWD_BLOCKNORM_HSWISH 2
 typedef struct {
   int64_t M, N, K;
   int32_t x_mode; /* LOKA_SCALE_TENSOR, LOKA_SCALE_ROW or LOKA_SCALE_MX32_ROW */
-  int32_t flags;  /* 0 or LOKA_FWD_W_PACKED */
+  int32_t flags;  /* LOKA_FWD_W_PACKED | LOKA_FWD_BLOCKNORM_HSWISH, or 0 */
   float eps;
   const void* x;
   const uint8_t* qw;

@@ -88,7 +88,11 @@ def _call(lib, fn, a):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(N=100), 2), (dict(N=2048), 2), (dict(N=0), 2), (dict(K=20), 2), (dict(K=4096), 2),
-    (dict(M=-1), 1), (dict(x_mode=2), 1), (dict(x_mode=9), 1), (dict(flags=2), 1), (dict(flags=3), 1),
+    (dict(M=-1), 1), (dict(x_mode=2), 1), (dict(x_mode=9), 1), (dict(flags=4), 1), (dict(flags=7), 1),
+    # BlockNorm + Hard Swish (flag 2): row recipe, N % 256, K <= 1024, no gamma/beta/mean/rstd
+    (dict(flags=2, x_mode=0), 2), (dict(flags=2, x_mode=3), 2), (dict(flags=2, N=320), 2), (dict(flags=2, N=8448), 2),
+    (dict(flags=2, K=1040), 2), (dict(flags=2, gamma=FAKE), 1), (dict(flags=2, rstd=FAKE), 1),
+    (dict(flags=2), 4), (dict(flags=2, N=4096, K=1024), 4),  # valid: stops at the missing relayout workspace
     (dict(flags=1, N=1024), 2),  # the packed weight layout exists only for the weight-resident shapes
     (dict(flags=1, N=512, K=1024), 2),
     (dict(eps=float("nan")), 1), (dict(eps=-1.0), 1),
