@@ -286,6 +286,10 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
   }
 
   const int nblk = blockIdx.x;
+  // dZ (fp32) of the block's 64 rows through one buffer resource: 32-bit
+  // offsets instead of a 64-bit address per store
+  const __amdgpu_buffer_rsrc_t dzr = __builtin_amdgcn_make_buffer_rsrc(
+      p.dz + m0 * N, (short)0, (int)((FULLM ? (int64_t)kBM : min((int64_t)kBM, p.M - m0)) * N * 4), kBufferWord3);
 #pragma unroll
   for (int t = 0; t < NTMAX; ++t) {
     if (t < nt) {
@@ -303,28 +307,31 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
         const uint32_t q = cvt4<1>(acc[t][i][0] * rq[i], acc[t][i][1] * rq[i], acc[t][i][2] * rq[i],
                                    acc[t][i][3] * rq[i]);
         *reinterpret_cast<uint32_t*>(ds + lr * ldn + n0) = q;
-        if (rowok[i]) {
-          *reinterpret_cast<float4*>(p.dz + m * N + n0) =
-              make_float4(acc[t][i][0], acc[t][i][1], acc[t][i][2], acc[t][i][3]);
-          if (p.dz_codes) *reinterpret_cast<uint32_t*>(p.dz_codes + m * N + n0) = q;
-        }
+        // rows past M fall outside the resource: the hardware drops them
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v4u{__float_as_uint(acc[t][i][0]), __float_as_uint(acc[t][i][1]), __float_as_uint(acc[t][i][2]),
+                __float_as_uint(acc[t][i][3])},
+            dzr, (uint32_t)(lr * N + n0) * 4u, 0, 0);
+        if (p.dz_codes && rowok[i]) *reinterpret_cast<uint32_t*>(p.dz_codes + m * N + n0) = q;
       }
-      // reduce over the 16 lanes (rows) sharing these 4 columns
+      // reduce over the 16 lanes (rows) sharing these 4 columns; then lane r
+      // of the group stores quantity r / 4 of column n0 + r % 4, so one store
+      // instruction writes the tile's 4 x 4 partials for all four groups
+      float vq[4][4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float a = col16_sum(colg[t][j]);
-        const float b = col16_sum(colb[t][j]);
-        const float c = col16_sum(cdb[j]);
-        const float d = col16_max(cmx[j]);
-        if (r == 0) {
-          const size_t o = (size_t)nblk * N + n0 + j;
-          const size_t plane = (size_t)p.nblocks * N;
-          p.part[o] = a;
-          p.part[plane + o] = b;
-          p.part[2 * plane + o] = c;
-          p.part[3 * plane + o] = d;
-        }
+        vq[0][j] = col16_sum(colg[t][j]);
+        vq[1][j] = col16_sum(colb[t][j]);
+        vq[2][j] = col16_sum(cdb[j]);
+        vq[3][j] = col16_max(cmx[j]);
       }
+      const int qs = r >> 2, js = r & 3;
+      float vj[4];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        vj[q4] = js == 0 ? vq[q4][0] : (js == 1 ? vq[q4][1] : (js == 2 ? vq[q4][2] : vq[q4][3]));
+      const float v = qs == 0 ? vj[0] : (qs == 1 ? vj[1] : (qs == 2 ? vj[2] : vj[3]));
+      p.part[(size_t)qs * p.nblocks * N + (size_t)nblk * N + n0 + js] = v;
     }
   }
   __syncthreads();
