@@ -76,12 +76,24 @@ __device__ __forceinline__ float col16_max(float v) { return row16_max(v); }
 
 // dY rows staged in LDS for N <= 512 and K <= 512 (the staging area and the
 // X and dZ code rows then fit the LDS together)
-__host__ __device__ constexpr bool bwd_stage_dy(int ntmax, int ktmax) { return ntmax == 8 && ktmax == 8; }
+__host__ __device__ constexpr bool bwd_stage_dy(int ntmax, int ktmax, int waves) {
+  return ntmax * waves <= 32 && ktmax * waves <= 32;
+}
+
+// The 16-column tiles [t0, t0 + n) of T that wavefront w of WAVES owns (T
+// split as evenly as the wavefronts allow)
+template <int WAVES>
+__device__ __forceinline__ void wave_tiles(int T, int w, int& t0, int& n) {
+  t0 = (w * T) / WAVES;
+  n = ((w + 1) * T) / WAVES - t0;
+}
 
 // FULLM: M is a multiple of the 64-row block, so every row exists (no row
-// guards).
-template <int NTMAX, int KTMAX, int NO_LN, bool FULLM>
-__global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
+// guards).  WAVES wavefronts split the columns: eight (two per SIMD) where a
+// wavefront's accumulators and weight fragments fit half the register file
+// (N, K <= 512), else four.
+template <int NTMAX, int KTMAX, int NO_LN, bool FULLM, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = p.K, N = p.N;
   const int ldk = K + 16, ldn = N + 16;
@@ -92,15 +104,16 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
   uint8_t* xs = smem;                                  // qX rows [BM][K+16]
   uint8_t* ds = xs + (size_t)kBM * ldk;                // dZ codes [BM][N+16]
   float* red0 = reinterpret_cast<float*>(ds + (size_t)kBM * ldn);
-  float* red1 = red0 + 4 * kBM;
-  float* rsc = red1 + 4 * kBM;                         // dZ row scales [BM]
+  float* red1 = red0 + WAVES * kBM;
+  float* rsc = red1 + WAVES * kBM;                 // dZ row scales [BM]
   // SDY: the block's dY rows staged in LDS [BM][2N+16] (when the LDS has room)
-  constexpr bool SDY = bwd_stage_dy(NTMAX, KTMAX);
+  constexpr bool SDY = bwd_stage_dy(NTMAX, KTMAX, WAVES);
   const int ldy = 2 * N + 16;
   uint8_t* dys = reinterpret_cast<uint8_t*>(rsc + kBM);
 
-  const int nt = N / 64;
-  const int nb = wave * nt * 16;
+  int nt, nb;
+  wave_tiles<WAVES>(N / 16, wave, nb, nt);
+  nb *= 16;
   v4f acc[NTMAX][kMT];  // holds Z, then dZ
 
   // per-row constants of this lane's rows m = m0 + 16 i + r, requested first
@@ -120,7 +133,7 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
     // too: all requests go out before the first wait, so one HBM latency
     // covers both, and the two LayerNorm passes read dY from LDS
     const int k16 = K / 16, n8 = SDY ? N / 8 : 0;
-    for (int u = tid; u < kBM * (k16 + n8); u += 256) {
+    for (int u = tid; u < kBM * (k16 + n8); u += 64 * WAVES) {
       if (u < kBM * k16) {
         const int lr = u / k16, c = (u - lr * k16) * 16;
         uint4 v = make_uint4(0, 0, 0, 0);
@@ -228,8 +241,14 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
 #pragma unroll
     for (int i = 0; i < kMT; ++i) {
       const int rr = 16 * i + r;
-      s1[i] = (red0[rr] + red0[kBM + rr] + red0[2 * kBM + rr] + red0[3 * kBM + rr]) * invn;  // mean g
-      s2[i] = (red1[rr] + red1[kBM + rr] + red1[2 * kBM + rr] + red1[3 * kBM + rr]) * invn;  // mean g*yhat
+      float a = 0.0f, b = 0.0f;
+#pragma unroll
+      for (int w = 0; w < WAVES; ++w) {
+        a += red0[w * kBM + rr];
+        b += red1[w * kBM + rr];
+      }
+      s1[i] = a * invn;  // mean g
+      s2[i] = b * invn;  // mean g*yhat
     }
     // dZ = rstd * (g - mean g - yhat * mean(g yhat))
 #pragma unroll
@@ -276,7 +295,9 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
 #pragma unroll
   for (int i = 0; i < kMT; ++i) {
     const int rr = 16 * i + r;
-    const float a = fmaxf(fmaxf(red0[rr], red0[kBM + rr]), fmaxf(red0[2 * kBM + rr], red0[3 * kBM + rr]));
+    float a = red0[rr];
+#pragma unroll
+    for (int w = 1; w < WAVES; ++w) a = fmaxf(a, red0[w * kBM + rr]);
     ScalePair sp = scales_from_amax<1>(a);
     rq[i] = sp.r;
     if (wave == 0 && g == 0) {
@@ -336,9 +357,11 @@ __global__ __launch_bounds__(256) void k_bwd_main(BwdBlock p) {
   }
   __syncthreads();
 
-  // dgrad: D[k][m] = sum_n Wr[k][n] dZq[m][n];  wave w owns k columns [w K/4, (w+1) K/4)
-  const int kt = K / 64;
-  const int kb0 = wave * kt * 16;
+  // dgrad: D[k][m] = sum_n Wr[k][n] dZq[m][n]; each wavefront owns a run of
+  // 16-column tiles of k
+  int kt, kb0;
+  wave_tiles<WAVES>(K / 16, wave, kb0, kt);
+  kb0 *= 16;
   v4f dacc[KTMAX][kMT];
 #pragma unroll
   for (int t = 0; t < KTMAX; ++t)
@@ -516,8 +539,8 @@ __global__ __launch_bounds__(256) void k_finalize_vectors(const float* wpart, in
   else col_vectors_body((int)blockIdx.x - nf, cpart, nblocks, N, dgamma, dbeta, dbias);
 }
 
-size_t bwd_lds_bytes(int K, int N, bool sdy) {
-  return (size_t)kBM * (K + 16) + (size_t)kBM * (N + 16) + (size_t)(2 * 4 * kBM + kBM) * 4 +
+size_t bwd_lds_bytes(int K, int N, bool sdy, int waves) {
+  return (size_t)kBM * (K + 16) + (size_t)kBM * (N + 16) + (size_t)(2 * waves * kBM + kBM) * 4 +
          (sdy ? (size_t)kBM * (2 * N + 16) : 0);
 }
 
@@ -551,17 +574,17 @@ BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K) {
   return w;
 }
 
-template <int NTMAX, int KTMAX>
+template <int NTMAX, int KTMAX, int WAVES>
 hipError_t launch_main_t(const BwdBlock& p, int no_ln, hipStream_t s) {
-  const size_t lds = bwd_lds_bytes(p.K, p.N, bwd_stage_dy(NTMAX, KTMAX));
+  const size_t lds = bwd_lds_bytes(p.K, p.N, bwd_stage_dy(NTMAX, KTMAX, WAVES), WAVES);
   const dim3 grid((unsigned)p.nblocks);
   const bool full = p.M % kBM == 0;
-  auto kern = no_ln ? (full ? k_bwd_main<NTMAX, KTMAX, 1, true> : k_bwd_main<NTMAX, KTMAX, 1, false>)
-                    : (full ? k_bwd_main<NTMAX, KTMAX, 0, true> : k_bwd_main<NTMAX, KTMAX, 0, false>);
+  auto kern = no_ln ? (full ? k_bwd_main<NTMAX, KTMAX, 1, true, WAVES> : k_bwd_main<NTMAX, KTMAX, 1, false, WAVES>)
+                    : (full ? k_bwd_main<NTMAX, KTMAX, 0, true, WAVES> : k_bwd_main<NTMAX, KTMAX, 0, false, WAVES>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(256), lds, s, p);
+  hipLaunchKernelGGL(kern, grid, dim3(64 * WAVES), lds, s, p);
   return hipGetLastError();
 }
 
@@ -594,11 +617,12 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
   if ((e = launch_relayout2(a.no_ln ? nullptr : a.qw, a.N, a.K, ws + w.qwi, a.qw_row, a.K, a.N, ws + w.qwri, s)) !=
       hipSuccess)
     return e;
-  const int nt = (int)a.N / 64, kt = (int)a.K / 64;
-  if (nt <= 8 && kt <= 8) e = launch_main_t<8, 8>(p, a.no_ln, s);
-  else if (nt <= 8) e = launch_main_t<8, 16>(p, a.no_ln, s);
-  else if (kt <= 8) e = launch_main_t<16, 8>(p, a.no_ln, s);
-  else e = launch_main_t<16, 16>(p, a.no_ln, s);
+  // N, K <= 512: eight wavefronts of at most four 16-column tiles each;
+  // else four wavefronts of at most eight or sixteen
+  if (a.N <= 512 && a.K <= 512) e = launch_main_t<4, 4, 8>(p, a.no_ln, s);
+  else if (a.N <= 512) e = launch_main_t<8, 16, 4>(p, a.no_ln, s);
+  else if (a.K <= 512) e = launch_main_t<16, 8, 4>(p, a.no_ln, s);
+  else e = launch_main_t<16, 16, 4>(p, a.no_ln, s);
   if (e != hipSuccess) return e;
 
   // column quantization of X (e4m3) and dZ (e5m2), both transposed to [*, M]
