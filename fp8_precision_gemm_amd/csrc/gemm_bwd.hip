@@ -132,7 +132,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
     // stage the forward's X codes in LDS, and with SDY the block's dY rows
     // too: all requests go out before the first wait, so one HBM latency
     // covers both, and the two LayerNorm passes read dY from LDS
-    const int k16 = K / 16, n8 = SDY ? N / 8 : 0;
+    const int k16 = K / 16, n8 = SDY ? N / 8 : 0, n8d = SDY ? n8 : 1;
     for (int u = tid; u < kBM * (k16 + n8); u += 64 * WAVES) {
       if (u < kBM * k16) {
         const int lr = u / k16, c = (u - lr * k16) * 16;
@@ -140,7 +140,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
         if (FULLM || m0 + lr < p.M) v = *reinterpret_cast<const uint4*>(p.qx + (m0 + lr) * K + c);
         *reinterpret_cast<uint4*>(xs + lr * ldk + c) = v;
       } else {
-        const int v8 = u - kBM * k16, lr = v8 / n8, c = (v8 - lr * n8) * 8;
+        const int v8 = u - kBM * k16, lr = v8 / n8d, c = (v8 - lr * n8d) * 8;
         uint4 v = make_uint4(0, 0, 0, 0);
         if (FULLM || m0 + lr < p.M) v = *reinterpret_cast<const uint4*>(p.dy + (m0 + lr) * N + c);
         *reinterpret_cast<uint4*>(dys + lr * ldy + 2 * c) = v;
@@ -394,24 +394,44 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
   float dsv[kMT];
 #pragma unroll
   for (int i = 0; i < kMT; ++i) dsv[i] = rsc[16 * i + r];
+  float swr[KTMAX][4];
+#pragma unroll
+  for (int t = 0; t < KTMAX; ++t) {
+    if (t < kt) {
+      const float4 s4 = *reinterpret_cast<const float4*>(p.sw_row + kb0 + 16 * t + 4 * g);
+      swr[t][0] = s4.x; swr[t][1] = s4.y; swr[t][2] = s4.z; swr[t][3] = s4.w;
+    }
+  }
+  // dX goes out through LDS, so that every store instruction writes whole
+  // row segments: the block's tile [BM][K] (bf16, row stride 2K + 16 bytes)
+  // takes the LDS from its start once every wavefront is past the dgrad
+  // MFMAs (the dZ codes' last reader) and has read its row scales
+  const int ldx = 2 * K + 16;
+  uint8_t* dxs = smem;
+  __syncthreads();
 #pragma unroll
   for (int t = 0; t < KTMAX; ++t) {
     if (t < kt) {
       const int k0 = kb0 + 16 * t + 4 * g;
-      const float4 s4 = *reinterpret_cast<const float4*>(p.sw_row + k0);
-      const float swr[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
       for (int i = 0; i < kMT; ++i) {
-        const int64_t m = m0 + 16 * i + r;
-        if (FULLM || m < p.M) {
-          float o[4];
+        float o[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) o[j] = dacc[t][i][j] * dsv[i] * swr[j];
-          // dX is not read again here: streaming (non-temporal) stores
-          __builtin_nontemporal_store(pack_bf16x2(o[0], o[1]) | ((uint64_t)pack_bf16x2(o[2], o[3]) << 32),
-                                      reinterpret_cast<uint64_t*>(p.dx + m * K + k0));
-        }
+        for (int j = 0; j < 4; ++j) o[j] = dacc[t][i][j] * dsv[i] * swr[t][j];
+        *reinterpret_cast<uint2*>(dxs + (16 * i + r) * ldx + 2 * k0) =
+            make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
       }
+    }
+  }
+  __syncthreads();
+  // 16 bytes per lane, a wavefront's 64 lanes on consecutive bytes of a row;
+  // dX is not read again here: streaming (non-temporal) stores
+  const int c16 = K / 8;
+  for (int u = tid; u < kBM * c16; u += 64 * WAVES) {
+    const int lr = u / c16, c = u - lr * c16;
+    if (FULLM || m0 + lr < p.M) {
+      const uint4 v = *reinterpret_cast<const uint4*>(dxs + lr * ldx + 16 * c);
+      __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p.dx + (m0 + lr) * K) + c);
     }
   }
 }
@@ -540,8 +560,10 @@ __global__ __launch_bounds__(256) void k_finalize_vectors(const float* wpart, in
 }
 
 size_t bwd_lds_bytes(int K, int N, bool sdy, int waves) {
-  return (size_t)kBM * (K + 16) + (size_t)kBM * (N + 16) + (size_t)(2 * waves * kBM + kBM) * 4 +
-         (sdy ? (size_t)kBM * (2 * N + 16) : 0);
+  const size_t main = (size_t)kBM * (K + 16) + (size_t)kBM * (N + 16) + (size_t)(2 * waves * kBM + kBM) * 4 +
+                      (sdy ? (size_t)kBM * (2 * N + 16) : 0);
+  const size_t dx_tile = (size_t)kBM * (2 * K + 16);  // reuses the LDS at the end
+  return main > dx_tile ? main : dx_tile;
 }
 
 struct BwdWs {
