@@ -28,13 +28,23 @@ dZ is rounded to fp32 (the precision the quantizer is defined on) and:
     operands scaled along the contraction;
   * dW stays fp32-or-wider (returned in fp64 here), dX is rounded to bf16.
 The literal reading (dY already is dZ, no LayerNorm) is `no_ln=True`.
+
+Square-block recipe ([GEM] "Low Precision Flash Attention", Block-wise
+Quantization: 32 x 32 blocks make the quantization transpose-invariant, so
+each tensor is quantized once and serves every GEMM that reads it):
+X, W and dZ are each quantized once in 32 x 32 blocks (reading R3b; e4m3 for
+X and W, e5m2 for dZ), the forward with those X and W codes, and
+  * dgrad: dX = dequant(q_sq(dZ)) . dequant(q_sq(W))^T,
+  * wgrad: dW = dequant(q_sq(X))^T . dequant(q_sq(dZ)),
+with the same codes and scales the forward and dgrad used (no requantization
+along the other dimension).
 """
 
 import numpy as np
 
 from .codec import E4M3, E5M2, bf16_to_f64, decode_fp8, f32, f64_to_bf16
 from .forward import gemm_ln_forward, _vec
-from .quant import quantize, ROW, COL
+from .quant import quantize, dequantize, ROW, COL, MX32_SQ
 
 
 def layernorm_backward(dy, z, mu, rstd, gamma):
@@ -90,5 +100,37 @@ def gemm_ln_backward(x_bits, w_bits, dy_bits, bias_bits=None, gamma_bits=None, b
         "dz": dz, "dz32": dz32, "q_dz": q_dz, "s_dz": s_dz, "q_wr": q_wr, "s_wr": s_wr,
         "dx": dx, "dx_bits": f64_to_bf16(dx), "dw": dw,
         "q_xc": q_xc, "s_xc": s_xc, "q_dzc": q_dzc, "s_dzc": s_dzc,
+        "dgamma": dgamma, "dbeta": dbeta, "dbias": dz.sum(axis=0),
+    }
+
+
+def gemm_ln_backward_sq(x_bits, w_bits, dy_bits, bias_bits=None, gamma_bits=None, beta_bits=None,
+                        eps=1e-5, no_ln=False):
+    """Backward of the square-block forward (recipe "mx32_sq") for bf16
+    inputs x[M,K], w[K,N], dy[M,N] (M, K, N multiples of 32).
+
+    Returns a dict with dz (fp64), dz32, the square e5m2 codes/scales of dz32
+    (q_dz [M,N], s_dz [M/32,N/32]), the forward's square codes/scales of X
+    and W, dx (fp64) and dx_bits (bf16), dw (fp64), dgamma, dbeta, dbias."""
+    x = bf16_to_f64(x_bits)
+    w = bf16_to_f64(w_bits)
+    dy = bf16_to_f64(dy_bits)
+    N = w.shape[1]
+    q_x, s_x = quantize(x, MX32_SQ, E4M3)
+    q_w, s_w = quantize(w, MX32_SQ, E4M3)
+    if no_ln:
+        dz, dgamma, dbeta = dy, None, None
+    else:
+        fwd = gemm_ln_forward(x_bits, w_bits, bias_bits, gamma_bits, beta_bits, eps, recipe="mx32_sq")
+        dz, dgamma, dbeta = layernorm_backward(dy, fwd["z"], fwd["mean"], fwd["rstd"],
+                                               _vec(gamma_bits, N, 1.0))
+    dz32 = f32(dz).astype(np.float64)
+    q_dz, s_dz = quantize(dz32, MX32_SQ, E5M2)
+    dzq = dequantize(q_dz, s_dz, MX32_SQ, E5M2)
+    dx = dzq @ dequantize(q_w, s_w, MX32_SQ, E4M3).T
+    dw = dequantize(q_x, s_x, MX32_SQ, E4M3).T @ dzq
+    return {
+        "dz": dz, "dz32": dz32, "q_dz": q_dz, "s_dz": s_dz, "q_x": q_x, "s_x": s_x, "q_w": q_w, "s_w": s_w,
+        "dx": dx, "dx_bits": f64_to_bf16(dx), "dw": dw,
         "dgamma": dgamma, "dbeta": dbeta, "dbias": dz.sum(axis=0),
     }

@@ -13,7 +13,9 @@ Sources:
     equals the standard normalization.  This is that standard
     normalization over the full row.
   * [LoKA] section III-B1 (No Bias): a missing bias is a first-class mode.
-  * [GEM] "Low Precision Flash Attention": block scales along K (MX path).
+  * [GEM] "Low Precision Flash Attention": block scales along K (MX path);
+    its Block-wise Quantization gives the square-block recipe "mx32_sq",
+    X[M,K] and W[K,N] each with one E8M0 scale per 32 x 32 block.
 
 Steps (the plain definition; the GPU kernel is a faster evaluation of it):
   1. quantize X per recipe (tensor / row / mx32 along K) and W per recipe
@@ -33,13 +35,14 @@ fixed blocks of features, h the Hard Swish.
 import numpy as np
 
 from .codec import E4M3, bf16_to_f64, decode_fp8, decode_e8m0, f64_to_bf16
-from .quant import quantize, TENSOR, ROW, COL, MX32_ROW, MX32_COL
+from .quant import quantize, dequantize, TENSOR, ROW, COL, MX32_ROW, MX32_COL, MX32_SQ
 
 RECIPES = {
     # recipe name -> (mode for X[M,K], mode for W[K,N])
     "tensor": (TENSOR, TENSOR),
     "row": (ROW, COL),
     "mx32": (MX32_ROW, MX32_COL),
+    "mx32_sq": (MX32_SQ, MX32_SQ),
 }
 
 
@@ -71,6 +74,8 @@ def quantized_product(x, w, recipe, fmt_x=E4M3, fmt_w=E4M3):
         ex = np.repeat(decode_e8m0(sx), 32, axis=1)          # [M, K]
         ew = np.repeat(decode_e8m0(sw), 32, axis=1).T        # [K, N]
         z = (dx * ex) @ (dw * ew)
+    elif recipe == "mx32_sq":
+        z = dequantize(qx, sx, MX32_SQ, fmt_x) @ dequantize(qw, sw, MX32_SQ, fmt_w)
     else:
         acc = dx @ dw
         sxb = np.float64(sx[0]) if mode_x == TENSOR else np.asarray(sx, np.float64)[:, None]

@@ -25,6 +25,12 @@ Readings taken where the pages are silent (each is stated once here):
       e = clamp(floor(log2 amax) - emax_elem, -127, 127) (the OCP MX v1.0
       rule), stored as e + 127, amax == 0 -> code 0; elements are
       satRNE_fp8(x * 2**-e), where the scaling is exact.
+  R3b MX32 square blocks ([GEM] "Low Precision Flash Attention",
+      Block-wise Quantization: one scale factor per 32 x 32 block, which
+      makes the quantization transpose-invariant so each tensor is quantized
+      once): the block is 32 consecutive rows by 32 consecutive columns; its
+      scale is R3's E8M0 exponent of the block's max-abs, and every element
+      is satRNE_fp8(x * 2**-e).  Scales are stored [R/32][C/32].
 """
 
 import numpy as np
@@ -32,7 +38,8 @@ import numpy as np
 from .codec import encode_fp8, decode_fp8, decode_e8m0, f32
 
 TENSOR, ROW, COL, MX32_ROW, MX32_COL = "tensor", "row", "col", "mx32_row", "mx32_col"
-MODES = (TENSOR, ROW, COL, MX32_ROW, MX32_COL)
+MX32_SQ = "mx32_sq"
+MODES = (TENSOR, ROW, COL, MX32_ROW, MX32_COL, MX32_SQ)
 FLT_MAX = np.float32(np.finfo(np.float32).max)
 
 
@@ -41,7 +48,8 @@ def amax(x, mode):
 
     tensor -> shape (1,); row -> (R,) (over each row); col -> (C,) (down each
     column); mx32_row -> (R, C/32) (32 consecutive elements along a row);
-    mx32_col -> (C, R/32) (32 consecutive elements down a column)."""
+    mx32_col -> (C, R/32) (32 consecutive elements down a column);
+    mx32_sq -> (R/32, C/32) (32 x 32 blocks)."""
     a = np.abs(np.asarray(x, dtype=np.float64))
     R, C = a.shape
     if mode == TENSOR:
@@ -54,6 +62,8 @@ def amax(x, mode):
         return a.reshape(R, C // 32, 32).max(axis=2)
     if mode == MX32_COL:
         return a.T.reshape(C, R // 32, 32).max(axis=2)
+    if mode == MX32_SQ:
+        return a.reshape(R // 32, 32, C // 32, 32).max(axis=(1, 3))
     raise ValueError(mode)
 
 
@@ -94,7 +104,7 @@ def quantize(x, mode, fmt):
 
     Returns (codes[R, C] uint8, scales) where scales are the fp32 dequant
     scales s (tensor (1,), row (R,), col (C,)) or the E8M0 codes (mx32_row
-    (R, C/32), mx32_col (C, R/32))."""
+    (R, C/32), mx32_col (C, R/32), mx32_sq (R/32, C/32))."""
     x = np.asarray(x, dtype=np.float64)
     R, C = x.shape
     am = amax(x, mode)
@@ -111,8 +121,10 @@ def quantize(x, mode, fmt):
     e = e8.astype(np.int64) - 127
     if mode == MX32_ROW:
         sh = np.repeat(-e, 32, axis=1)              # [R, C]
-    else:
+    elif mode == MX32_COL:
         sh = np.repeat(-e, 32, axis=1).T            # [C, R] -> [R, C]
+    else:
+        sh = np.repeat(np.repeat(-e, 32, axis=0), 32, axis=1)  # [R/32, C/32] -> [R, C]
     t = np.ldexp(x, sh)                              # exact power-of-two scaling
     return encode_fp8(t, fmt), e8
 
@@ -132,4 +144,6 @@ def dequantize(codes, scales, mode, fmt):
         return v * np.repeat(sc, 32, axis=1)
     if mode == MX32_COL:
         return v * np.repeat(sc, 32, axis=1).T
+    if mode == MX32_SQ:
+        return v * np.repeat(np.repeat(sc, 32, axis=0), 32, axis=1)
     raise ValueError(mode)
