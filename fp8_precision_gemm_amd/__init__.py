@@ -24,7 +24,7 @@ library_path = os.path.join(_HERE, "liblokafp8.so")
 
 E4M3, E5M2 = 0, 1
 FMTS = {"e4m3": E4M3, "e5m2": E5M2, E4M3: E4M3, E5M2: E5M2}
-MODES = {"tensor": 0, "row": 1, "col": 2, "mx32_row": 3, "mx32_col": 4}
+MODES = {"tensor": 0, "row": 1, "col": 2, "mx32_row": 3, "mx32_col": 4, "mx32_sq": 5}
 STATUS = {0: "LOKA_OK", 1: "LOKA_ERR_INVALID_ARG", 2: "LOKA_ERR_UNSUPPORTED", 3: "LOKA_ERR_ALIGNMENT",
           4: "LOKA_ERR_WORKSPACE", 5: "LOKA_ERR_HIP"}
 BWD_NO_LN = 1
@@ -170,8 +170,10 @@ def loka_quant_fp8(src, fmt="e4m3", mode="row", transpose_out=False, codes=None,
             scales = torch.empty(cols, dtype=torch.float32, device=dev)
         elif m == 3:
             scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
-        else:
+        elif m == 4:
             scales = torch.empty((cols, rows // 32), dtype=torch.uint8, device=dev)
+        else:
+            scales = torch.empty((rows // 32, cols // 32), dtype=torch.uint8, device=dev)
     if want_amax and amax is None and m <= 2:
         amax = torch.empty(scales.shape, dtype=torch.float32, device=dev)
     a = QuantArgs(rows=rows, cols=cols, ld=src.stride(0) if rows > 1 else cols,

@@ -93,7 +93,7 @@ const char* loka_last_error(void) { return g_last_error; }
 
 // ---------------------------------------------------------------------------
 size_t loka_quant_workspace_size(const loka_quant_args* a) {
-  if (a == nullptr || a->rows < 0 || a->cols < 0 || a->mode < 0 || a->mode > 4) return 0;
+  if (a == nullptr || a->rows < 0 || a->cols < 0 || a->mode < 0 || a->mode > LOKA_SCALE_MX32_SQ) return 0;
   if (a->rows == 0 || a->cols == 0) return 0;
   return (size_t)loka::quant_plan(a->rows, a->cols, a->mode).ws_floats * sizeof(float);
 }
@@ -105,14 +105,16 @@ loka_status loka_quant_fp8(const loka_quant_args* a, void* stream) {
   REQUIRE(a->src_dtype == LOKA_DTYPE_BF16 || a->src_dtype == LOKA_DTYPE_F32, LOKA_ERR_INVALID_ARG, "bad src_dtype %d",
           a->src_dtype);
   REQUIRE(a->fmt == LOKA_E4M3 || a->fmt == LOKA_E5M2, LOKA_ERR_INVALID_ARG, "bad fmt %d", a->fmt);
-  REQUIRE(a->mode >= LOKA_SCALE_TENSOR && a->mode <= LOKA_SCALE_MX32_COL, LOKA_ERR_INVALID_ARG, "bad mode %d", a->mode);
+  REQUIRE(a->mode >= LOKA_SCALE_TENSOR && a->mode <= LOKA_SCALE_MX32_SQ, LOKA_ERR_INVALID_ARG, "bad mode %d", a->mode);
   REQUIRE(a->transpose_out >= 0 && a->transpose_out <= 2, LOKA_ERR_INVALID_ARG, "transpose_out must be 0, 1 or 2");
-  const bool mx = a->mode == LOKA_SCALE_MX32_ROW || a->mode == LOKA_SCALE_MX32_COL;
+  const bool mx = a->mode == LOKA_SCALE_MX32_ROW || a->mode == LOKA_SCALE_MX32_COL || a->mode == LOKA_SCALE_MX32_SQ;
   REQUIRE(!(mx && a->amax != nullptr), LOKA_ERR_INVALID_ARG, "amax output is not defined for MX modes");
   REQUIRE(a->cols % 16 == 0, LOKA_ERR_UNSUPPORTED, "cols %% 16 != 0");
   REQUIRE(a->ld % 8 == 0, LOKA_ERR_ALIGNMENT, "ld %% 8 != 0");
   REQUIRE(a->mode != LOKA_SCALE_MX32_ROW || a->cols % 32 == 0, LOKA_ERR_UNSUPPORTED, "MX32_ROW needs cols %% 32 == 0");
   REQUIRE(a->mode != LOKA_SCALE_MX32_COL || a->rows % 32 == 0, LOKA_ERR_UNSUPPORTED, "MX32_COL needs rows %% 32 == 0");
+  REQUIRE(a->mode != LOKA_SCALE_MX32_SQ || (a->rows % 32 == 0 && a->cols % 32 == 0), LOKA_ERR_UNSUPPORTED,
+          "MX32_SQ needs rows %% 32 == 0 and cols %% 32 == 0");
   REQUIRE(!a->transpose_out || a->rows % 16 == 0, LOKA_ERR_UNSUPPORTED, "transpose_out needs rows %% 16 == 0");
   const bool empty = a->rows == 0 || a->cols == 0;
   if (!empty) {

@@ -205,6 +205,7 @@ __device__ __forceinline__ void cast_tile_body(const CastParams& p, int64_t bx, 
   __shared__ float red[4];
   __shared__ float colmax[kTile][kTile + 1];  // MX32_COL: |x| staging
   __shared__ int e8_col[2][kTile];            // MX32_COL: E8M0 per (row block, column)
+  __shared__ float sq_max[4][2];              // MX32_SQ: per wavefront, per 32-column half
   __shared__ uint8_t tcodes[kTile][kTile + 4];  // transposed output staging
 
   const int t = threadIdx.x;
@@ -259,6 +260,29 @@ __device__ __forceinline__ void cast_tile_body(const CastParams& p, int64_t bx, 
       int64_t nb = p.cols / 32;
       static_cast<uint8_t*>(p.scales)[row * nb + col0 / 32] = (uint8_t)e8;
     }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mult[i] = mu;
+  } else if (MODE == 5) {  // MX32 square: the tile's 2 x 2 blocks of 32 x 32
+    // wavefront w holds tile rows 16w .. +16 (block row w / 2); lane bit 1
+    // selects the 32-column half (block column); reduce over the other bits
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(v[i]));
+    m = fmaxf(m, __shfl_xor(m, 1, 64));
+    m = fmaxf(m, __shfl_xor(m, 4, 64));
+    m = fmaxf(m, __shfl_xor(m, 8, 64));
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    const int w = t >> 6, h = (t >> 1) & 1;
+    if ((t & 63) < 4 && (t & 1) == 0) sq_max[w][h] = m;  // lanes 0 and 2
+    __syncthreads();
+    const int b = w >> 1;
+    m = fmaxf(sq_max[2 * b][h], sq_max[2 * b + 1][h]);
+    const int e8 = e8m0_from_amax<FMT>(m);
+    const float mu = e8m0_inv_multiplier(e8);
+    const int64_t grb = by * 2 + b, gcb = bx * 2 + h;
+    if ((t & 127) < 4 && (t & 1) == 0 && grb * 32 < p.rows && gcb * 32 < p.cols)
+      static_cast<uint8_t*>(p.scales)[grb * (p.cols / 32) + gcb] = (uint8_t)e8;
 #pragma unroll
     for (int i = 0; i < 16; ++i) mult[i] = mu;
   } else {  // MX32 down columns: 32-row blocks of each column, via LDS
@@ -358,7 +382,8 @@ void dispatch_cast(const CastParams& cp, int mode, int trans, hipStream_t s) {
     case 1: launch_cast<DT, FMT, 1>(cp, trans, s); break;
     case 2: launch_cast<DT, FMT, 2>(cp, trans, s); break;
     case 3: launch_cast<DT, FMT, 3>(cp, trans, s); break;
-    default: launch_cast<DT, FMT, 4>(cp, trans, s); break;
+    case 4: launch_cast<DT, FMT, 4>(cp, trans, s); break;
+    default: launch_cast<DT, FMT, 5>(cp, trans, s); break;
   }
 }
 

@@ -80,7 +80,8 @@ typedef enum {
   LOKA_SCALE_ROW = 1,     /* one fp32 scale per row (amax along the row)        */
   LOKA_SCALE_COL = 2,     /* one fp32 scale per column (amax down the column)   */
   LOKA_SCALE_MX32_ROW = 3,/* one E8M0 per 32 consecutive elements along a row   */
-  LOKA_SCALE_MX32_COL = 4 /* one E8M0 per 32 consecutive elements down a column */
+  LOKA_SCALE_MX32_COL = 4,/* one E8M0 per 32 consecutive elements down a column */
+  LOKA_SCALE_MX32_SQ = 5  /* one E8M0 per 32 x 32 block (rows and columns)      */
 } loka_scaling;
 
 typedef enum { LOKA_DTYPE_BF16 = 0, LOKA_DTYPE_F32 = 1 } loka_dtype;
@@ -112,14 +113,21 @@ typedef enum { LOKA_DTYPE_BF16 = 0, LOKA_DTYPE_F32 = 1 } loka_dtype;
  *            1 KiB half: the weight layout loka_gemm_fp8_ln and the
  *            grouped launch read with LOKA_FWD_W_PACKED.
  *   scales   TENSOR: float[1]; ROW: float[rows]; COL: float[cols];
- *            MX32_ROW: uint8[rows][cols/32]; MX32_COL: uint8[cols][rows/32].
+ *            MX32_ROW: uint8[rows][cols/32]; MX32_COL: uint8[cols][rows/32];
+ *            MX32_SQ: uint8[rows/32][cols/32], the block (i, j) covering
+ *            rows 32i..32i+31 and columns 32j..32j+31 (GEM "Low Precision
+ *            Flash Attention", Block-wise Quantization: the square block is
+ *            transpose-invariant, so one quantization serves a tensor and its
+ *            transpose; the codes of src^T are transpose_out's bytes and
+ *            the scales of src^T are the transposed grid).
  *            (The scale layout does not depend on transpose_out.)
  *   amax     optional float out, same count as the fp32 scales
  *            (TENSOR/ROW/COL only; must be NULL for MX).
  *   workspace device scratch of loka_quant_workspace_size() bytes
  *            (may be NULL when that size is 0).
  * Requirements: rows, cols >= 0; cols % 16 == 0; MX32_ROW: cols % 32 == 0;
- * MX32_COL: rows % 32 == 0; transpose_out requires rows % 16 == 0.
+ * MX32_COL: rows % 32 == 0; MX32_SQ: rows % 32 == 0 and cols % 32 == 0;
+ * transpose_out requires rows % 16 == 0.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int64_t rows, cols, ld;

@@ -142,10 +142,11 @@ def _quant(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(rows=-1), 1), (dict(ld=32), 1), (dict(src_dtype=2), 1), (dict(fmt=3), 1), (dict(mode=5), 1),
+    (dict(rows=-1), 1), (dict(ld=32), 1), (dict(src_dtype=2), 1), (dict(fmt=3), 1), (dict(mode=6), 1),
     (dict(transpose_out=3), 1), (dict(transpose_out=-1), 1), (dict(transpose_out=2, rows=40), 2),
     (dict(cols=40, ld=40), 2), (dict(mode=3, cols=48, ld=48), 2),
     (dict(mode=4, rows=48), 2), (dict(transpose_out=1, rows=40), 2), (dict(ld=68), 3),
+    (dict(mode=5, rows=48), 2), (dict(mode=5, cols=48, ld=48), 2), (dict(mode=5, amax=FAKE), 1),
     (dict(src=None), 1), (dict(codes=None), 1), (dict(scales=None), 1), (dict(mode=3, amax=FAKE), 1),
     (dict(codes=FAKE + 1), 3), (dict(mode=0), 4), (dict(mode=2), 4),
 ])

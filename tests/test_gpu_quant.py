@@ -11,7 +11,8 @@ from tests.gpu_helpers import bf16_dev, f32_dev, host, unpack_packed
 
 pytestmark = pytest.mark.gpu
 
-MODES = ["tensor", "row", "col", "mx32_row", "mx32_col"]
+MODES = ["tensor", "row", "col", "mx32_row", "mx32_col", "mx32_sq"]
+MX = ("mx32_row", "mx32_col", "mx32_sq")
 FMTS = {"e4m3": codec.E4M3, "e5m2": codec.E5M2}
 
 
@@ -47,7 +48,7 @@ def check_quant(lib, x_bits_or_f32, mode, fmt, transpose, src_f32=False, label="
                               f"{bad[0][0], bad[1][0]}: gpu {got[bad[0][0], bad[1][0]]:#04x} "
                               f"ref {ref_codes[bad[0][0], bad[1][0]]:#04x} x={xv[bad[0][0], bad[1][0]]!r}")
     gs = host(scales)
-    if mode in ("mx32_row", "mx32_col"):
+    if mode in MX:
         np.testing.assert_array_equal(gs, ref_scales)
     else:
         np.testing.assert_array_equal(gs.view(np.uint32), ref_scales.astype(np.float32).view(np.uint32))
@@ -61,14 +62,16 @@ def test_every_bf16_value(lib, mode, fmt, transpose):
     check_quant(lib, all_bf16_matrix(), mode, fmt, transpose, label="all-bf16")
 
 
-@pytest.mark.parametrize("mode", ["tensor", "col", "mx32_col"])
-@pytest.mark.parametrize("rows,cols", [(256, 256), (144, 96), (32, 16), (640, 48)])
+@pytest.mark.parametrize("mode", ["tensor", "col", "mx32_col", "mx32_sq"])
+@pytest.mark.parametrize("rows,cols", [(256, 256), (144, 96), (32, 16), (640, 48), (96, 160)])
 def test_packed_layout(lib, mode, rows, cols):
     """transpose_out="packed": the codes of src^T in the fragment-interleaved
     layout (rows not a multiple of 128 are padded with zero codes), the same
     codes and scales as the plain layouts."""
     if mode == "mx32_col" and rows % 32:
         pytest.skip("MX32_COL needs rows % 32 == 0")
+    if mode == "mx32_sq" and (rows % 32 or cols % 32):
+        pytest.skip("MX32_SQ needs rows and cols % 32 == 0")
     rng = np.random.default_rng(rows * 7 + cols)
     x = to_bf16_bits(rng.standard_t(3, size=(rows, cols)))
     check_quant(lib, x, mode, "e4m3", "packed", label=f"packed {rows}x{cols}")
@@ -81,7 +84,7 @@ def test_fp32_source_with_ragged_edges(lib, mode, fmt):
     tile, heavy tails, zero rows/columns and subnormal-range values."""
     rng = np.random.default_rng(3)
     rows, cols = 96 + 32, 80 + 48  # 128 x 128 for MX; ragged against 64-tiles elsewhere below
-    if mode not in ("mx32_row", "mx32_col"):
+    if mode not in MX:
         rows, cols = 100 + 12, 144
     x = (rng.standard_t(3, size=(rows, cols)) * np.exp(3 * rng.standard_normal((rows, 1)))).astype(np.float32)
     x[5] = 0.0
@@ -118,3 +121,15 @@ def test_deterministic(lib):
     b = [host(t) for t in lib.loka_quant_fp8(xt, fmt="e5m2", mode="col", transpose_out=True)[:2]]
     for u, v in zip(a, b):
         np.testing.assert_array_equal(u, v)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("rows,cols", [(96, 160), (32, 32), (160, 96)])
+def test_square_blocks_partial_tiles(lib, fmt, rows, cols):
+    """MX32_SQ where the 32 x 32 blocks do not fill the 64 x 64 cast tiles,
+    with one block per row band scaled far apart (every block its own scale)."""
+    rng = np.random.default_rng(rows + 3 * cols)
+    x = rng.standard_normal((rows, cols)) * np.exp2(rng.integers(-30, 30, (rows // 32, cols // 32))).repeat(
+        32, axis=0).repeat(32, axis=1)
+    check_quant(lib, to_bf16_bits(x), "mx32_sq", fmt, False, label="square")
+    check_quant(lib, to_bf16_bits(x), "mx32_sq", fmt, True, label="square")
