@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblokafp8.so")
-SOURCES = ["api.cpp", "quant.hip", "gemm_ln_fwd.hip", "fwd_tensor.hip", "fwd_row.hip", "fwd_blocknorm.hip", "fwd_mx.hip",
+SOURCES = ["api.cpp", "quant.hip", "gemm_ln_fwd.hip", "fwd_tensor.hip", "fwd_row.hip", "fwd_blocknorm.hip", "fwd_mx.hip", "fwd_mxsq.hip",
            "grouped.hip", "gemm_bwd.hip"]
 
 FLAGS = [

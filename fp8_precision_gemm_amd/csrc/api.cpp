@@ -60,8 +60,8 @@ loka_status check_fwd_shape(int64_t M, int64_t N, int64_t K, int x_mode) {
           "N=%lld: the fused LayerNorm needs N %% 64 == 0 and 64 <= N <= 1024", (long long)N);
   REQUIRE(K >= 16 && K <= 2048 && K % 16 == 0, LOKA_ERR_UNSUPPORTED, "K=%lld: need K %% 16 == 0, 16 <= K <= 2048",
           (long long)K);
-  REQUIRE(x_mode != LOKA_SCALE_MX32_ROW || K % 32 == 0, LOKA_ERR_UNSUPPORTED, "MX32 needs K %% 32 == 0 (K=%lld)",
-          (long long)K);
+  REQUIRE((x_mode != LOKA_SCALE_MX32_ROW && x_mode != LOKA_SCALE_MX32_SQ) || K % 32 == 0, LOKA_ERR_UNSUPPORTED,
+          "MX32 needs K %% 32 == 0 (K=%lld)", (long long)K);
   REQUIRE(M <= ((int64_t)1 << 31) - 64, LOKA_ERR_UNSUPPORTED, "M=%lld too large", (long long)M);
   return LOKA_OK;
 }
@@ -143,8 +143,9 @@ size_t loka_gemm_fp8_ln_workspace_size(const loka_fwd_args* a) {
 
 loka_status loka_gemm_fp8_ln(const loka_fwd_args* a, void* stream) {
   REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
-  REQUIRE(a->x_mode == LOKA_SCALE_TENSOR || a->x_mode == LOKA_SCALE_ROW || a->x_mode == LOKA_SCALE_MX32_ROW,
-          LOKA_ERR_INVALID_ARG, "x_mode must be TENSOR, ROW or MX32_ROW (got %d)", a->x_mode);
+  REQUIRE(a->x_mode == LOKA_SCALE_TENSOR || a->x_mode == LOKA_SCALE_ROW || a->x_mode == LOKA_SCALE_MX32_ROW ||
+              a->x_mode == LOKA_SCALE_MX32_SQ,
+          LOKA_ERR_INVALID_ARG, "x_mode must be TENSOR, ROW, MX32_ROW or MX32_SQ (got %d)", a->x_mode);
   REQUIRE((a->flags & ~(LOKA_FWD_W_PACKED | LOKA_FWD_BLOCKNORM_HSWISH)) == 0, LOKA_ERR_INVALID_ARG,
           "unknown flags %d", a->flags);
   const bool packed = (a->flags & LOKA_FWD_W_PACKED) != 0;
@@ -166,6 +167,20 @@ loka_status loka_gemm_fp8_ln(const loka_fwd_args* a, void* stream) {
           "LOKA_FWD_W_PACKED needs the weight-resident shapes: N <= 512 and K <= 1024 (N <= 256), 640 (N <= 384) "
           "or 512 (N <= 512); got N=%lld K=%lld",
           (long long)a->N, (long long)a->K);
+  if (a->x_mode == LOKA_SCALE_MX32_SQ) {
+    REQUIRE(!blocknorm, LOKA_ERR_UNSUPPORTED, "the BlockNorm epilogue supports x_mode ROW only");
+    REQUIRE(a->M % 32 == 0 && a->N % 32 == 0, LOKA_ERR_UNSUPPORTED, "MX32_SQ needs M %% 32 == 0 (M=%lld)",
+            (long long)a->M);
+    REQUIRE(loka::fwd_weight_resident(a->N, a->K), LOKA_ERR_UNSUPPORTED,
+            "MX32_SQ runs on the weight-resident shapes: N <= 512 and K <= 1024 (N <= 256), 640 (N <= 384) or 512 "
+            "(N <= 512); got N=%lld K=%lld",
+            (long long)a->N, (long long)a->K);
+    REQUIRE(a->qx_out == nullptr && a->sx_out == nullptr, LOKA_ERR_INVALID_ARG,
+            "MX32_SQ takes X quantized: qx_out and sx_out must be NULL");
+    if (a->M > 0) REQUIRE(a->x_scales != nullptr, LOKA_ERR_INVALID_ARG, "MX32_SQ needs x_scales");
+  } else {
+    REQUIRE(a->x_scales == nullptr, LOKA_ERR_INVALID_ARG, "x_scales is only for x_mode MX32_SQ");
+  }
   if ((st = check_eps(a->eps)) != LOKA_OK) return st;
   if (a->M > 0) REQUIRE(a->x && a->qw && a->sw && a->y, LOKA_ERR_INVALID_ARG, "x, qw, sw and y are required");
   REQUIRE_ALIGNED(a->x); REQUIRE_ALIGNED(a->qw); REQUIRE_ALIGNED(a->sw); REQUIRE_ALIGNED(a->bias);
@@ -178,6 +193,7 @@ loka_status loka_gemm_fp8_ln(const loka_fwd_args* a, void* stream) {
   f.x = a->x; f.qw = a->qw; f.sw = a->sw; f.bias = a->bias; f.gamma = a->gamma; f.beta = a->beta;
   f.y = a->y; f.z = a->z; f.mean = a->mean; f.rstd = a->rstd; f.qx_out = a->qx_out; f.sx_out = a->sx_out;
   f.workspace = a->workspace;
+  f.x_scales = a->x_scales;
   f.w_packed = packed;
   f.blocknorm = blocknorm;
   return hip_status(loka::launch_fwd(f, static_cast<hipStream_t>(stream)), "loka_gemm_fp8_ln");

@@ -58,6 +58,10 @@ struct FwdBlock {
   float eps;
   float x_r, x_s;  // tensor mode: X multiplier and dequantization scale
   int ldy;         // row stride of y and z in elements (0: N); a column slab's is the full width
+  // square-block recipe (MODE 4): X arrives quantized, e4m3 codes [M][K]
+  // and E8M0 scales [M/32][K/32]
+  const uint8_t* xq;
+  const uint8_t* xs;
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

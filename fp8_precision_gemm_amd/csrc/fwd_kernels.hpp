@@ -105,6 +105,9 @@ hipError_t launch_mode(const FwdBlock& p, const float* partials, int np, hipStre
       default: return hipErrorInvalidValue;
     }
   }
+  if constexpr (MODE == 4) {
+    return hipErrorInvalidValue;  // the square-block recipe runs on the resident shapes only
+  } else {
   switch ((p.N + 127) / 128) {  // column tiles per wavefront
 #define LOKA_CASE(V) \
   case V:            \
@@ -112,6 +115,7 @@ hipError_t launch_mode(const FwdBlock& p, const float* partials, int np, hipStre
     LOKA_CASE(1) LOKA_CASE(2) LOKA_CASE(3) LOKA_CASE(4) LOKA_CASE(5) LOKA_CASE(6) LOKA_CASE(7) LOKA_CASE(8)
 #undef LOKA_CASE
     default: return hipErrorInvalidValue;
+  }
   }
 }
 

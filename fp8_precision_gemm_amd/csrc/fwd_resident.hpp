@@ -202,9 +202,13 @@ __device__ __forceinline__ v4f mfma_mx_sel(int sel, const v8i& a, const v8i& b, 
 // ([LoKA] section III-B2 Fig. 7d and III-B3).  With EPI 1 the block covers
 // one column slab of 128*NT columns (a whole number of 256-blocks).
 constexpr int kBlockNorm = 256;
+// MODE: 0 tensor, 1 row, 3 MX32 along K (X quantized here), 4 MX32 square
+// blocks (X given as e4m3 codes with E8M0 scales per 32 x 32 block; the
+// weight's scales per 32 x 32 block of W[K][N]).
 template <int MODE, int NT, int KC, bool OPT, bool FULL, int EPI = 0>
 struct ResBlock {
   using R = Res<NT, KC>;
+  static constexpr bool MX = MODE >= 3;  // E8M0 block scales inside the MFMA
   static constexpr int KQ = R::KQ, D = R::D, LDX = R::LDX, XE = R::XE, KP = R::KP;
   static constexpr bool PIPE = R::PIPE;
 
@@ -224,6 +228,7 @@ struct ResBlock {
   v8i wf[NT][KC];
   uint32_t wsc[NT][KP];
   uint4 xr[D][KQ];
+  uint32_t xq8[D][KQ];  // MODE 4: the E8M0 byte of each loaded piece's block
   // two accumulator sets: the GEMM of tile j fills one while the epilogue
   // of tile j-1 reads the other
   v4f acc0[NT], acc1[NT];
@@ -272,6 +277,28 @@ struct ResBlock {
   // clamped to K-8 (duplicates, never stored either).
   template <int S>
   __device__ __forceinline__ void load_x(int64_t t) {
+    if (MODE == 4) {
+      // codes: 8 bytes per piece, the same elements as the bf16 path; the
+      // scale byte of each piece's 32 x 32 block (rows clamped into M: a
+      // row past M has zero codes, its scale is never used)
+      const int64_t row0 = min(t * kResRows, p.M);
+      const int64_t left = min(min(te * kResRows, p.M) - row0, (int64_t)kResRows);
+      const int bytes = left > 0 ? (int)left * K : 0;
+      const __amdgpu_buffer_rsrc_t rsrc =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(p.xq + row0 * K), (short)0, bytes, kBufferWord3);
+      const uint32_t rb = (uint32_t)hrow * (uint32_t)K;
+      const int64_t mc = min(t * kResRows + hrow, p.M - 1);
+      const uint8_t* srow = p.xs + (mc >> 5) * kb;
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) {
+        int k = q * 256 + hl * 8;
+        if (!FULL) k = k < K ? k : K - 8;
+        const uint2 c = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rsrc, rb + (uint32_t)k, 0, 0));
+        xr[S][q] = make_uint4(c.x, c.y, 0u, 0u);
+        xq8[S][q] = srow[k >> 5];
+      }
+      return;
+    }
     const int64_t row0 = min(t * kResRows, p.M);
     const int64_t left = min(min(te * kResRows, p.M) - row0, (int64_t)kResRows);
     const int bytes = left > 0 ? (int)left * K * 2 : 0;
@@ -299,6 +326,25 @@ struct ResBlock {
     // the optional global outputs (those rows belong to another workgroup)
     const bool out_ok = OPT && t < te && m < p.M;
     uint8_t* crow = codes + (buf * kResRows + hrow) * LDX;
+    if (MODE == 4) {
+      // the codes are the input: into the code buffer, the block scales into
+      // the same LDS slots as MODE 3's (block 8q + hl/4 at (g, c) = ((hl/4)%4, 2q + hl/16))
+      uint8_t* erow = xe8 + (buf * kResRows + hrow) * XE + ((hl >> 2) & 3) * (4 * KP) + (hl >> 4);
+      float emax = 0.0f;
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) {
+        const int k = q * 256 + hl * 8;
+        if (kv(k)) {
+          const uint32_t e8 = xq8[S][q];
+          emax = fmaxf(emax, (float)e8);
+          erow[2 * q] = (uint8_t)e8;
+          *reinterpret_cast<uint2*>(crow + k) = make_uint2(xr[S][q].x, xr[S][q].y);
+        }
+      }
+      emax = half_max(emax);
+      rs[buf * kResRows + hrow] = emax;
+      return;
+    }
     if (MODE == 3) {
       // block of piece q: 8q + hl/4, stored at LDS slot (g = (hl/4)%4, c = 2q + hl/16)
       uint8_t* erow = xe8 + (buf * kResRows + hrow) * XE + ((hl >> 2) & 3) * (4 * KP) + (hl >> 4);
@@ -395,7 +441,9 @@ struct ResBlock {
         wf[t][c] = f;
       }
     }
-    if (MODE == 3) {
+    if (MX) {
+      // MODE 3: W's scales [N][K/32] (32 consecutive k of column col);
+      // MODE 4: [K/32][N/32] (32 x 32 blocks of W[K][N])
       const uint8_t* sw8 = static_cast<const uint8_t*>(p.sw);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
@@ -403,7 +451,8 @@ struct ResBlock {
 #pragma unroll
         for (int c = 0; c < KC; ++c) {
           const int blk = 4 * c + g;
-          wse[t][c] = (tv(t) && (FULL || blk < kb)) ? sw8[(int64_t)col * kb + blk] : (uint8_t)127;
+          const int64_t si = MODE == 4 ? (int64_t)blk * (N >> 5) + (col >> 5) : (int64_t)col * kb + blk;
+          wse[t][c] = (tv(t) && (FULL || blk < kb)) ? sw8[si] : (uint8_t)127;
         }
       }
     }
@@ -415,7 +464,8 @@ struct ResBlock {
   // in a branch that would have to wait for it there.
   __device__ __forceinline__ void request_vectors() {
     const int ct = tid < N ? tid : 0;
-    const uint16_t* x0 = p.x;
+    // a valid address to read in place of a missing vector (MODE 4 has X as codes)
+    const uint16_t* x0 = MODE == 4 ? reinterpret_cast<const uint16_t*>(p.xq) : p.x;
     cv_sw = MODE == 1 ? static_cast<const float*>(p.sw)[ct] : (MODE == 0 ? static_cast<const float*>(p.sw)[0] : 1.0f);
     const uint16_t b = *(p.bias ? p.bias + ct : x0), gm = *(p.gamma ? p.gamma + ct : x0);
     const uint16_t be = *(p.beta ? p.beta + ct : x0);
@@ -428,7 +478,7 @@ struct ResBlock {
   // maxima, LDS padding
   __device__ __forceinline__ void stage_vectors() {
     float msw = 0.0f, mb = 0.0f, ewm = 0.0f;
-    if (MODE == 3) {
+    if (MX) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
 #pragma unroll
@@ -468,7 +518,7 @@ struct ResBlock {
           *reinterpret_cast<uint4*>(codes + row * LDX + o) = make_uint4(0, 0, 0, 0);
         }
       }
-      if (MODE == 3) {
+      if (MX) {
         for (int u = tid; u < 2 * kResRows * XE; u += kThreads) {
           const int sl = u % XE, c = sl % (4 * KP);  // LDS slot (g, c) holds block 4c+g
           if (4 * c + sl / (4 * KP) >= kb) xe8[u] = 127;
@@ -488,7 +538,7 @@ struct ResBlock {
     }
     const float kk = (448.0f * 448.0f) * (float)K;
     // launch constants: kept in scalar registers
-    bw = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(MODE == 3 ? ldexpf(kk, (int)ewm - 127) : kk * msw)));
+    bw = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(MX ? ldexpf(kk, (int)ewm - 127) : kk * msw)));
     bb = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(mb)));
   }
 
@@ -499,7 +549,7 @@ struct ResBlock {
     const uint8_t* brow = codes + (buf * kResRows + r) * LDX + 16 * g;
     const uint32_t* erow = reinterpret_cast<const uint32_t*>(xe8 + (buf * kResRows + r) * XE + g * (4 * KP));
     uint32_t xsw[KP];
-    if (MODE == 3) {
+    if (MX) {
 #pragma unroll
       for (int q = 0; q < KP; ++q) xsw[q] = erow[q];
     }
@@ -513,7 +563,7 @@ struct ResBlock {
       xf[4] = (int)b.x; xf[5] = (int)b.y; xf[6] = (int)b.z; xf[7] = (int)b.w;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        if (MODE == 3)
+        if (MX)
           acc[t] = mfma_mx_sel(c & 3, wf[t][c], xf, acc[t], wsc[t][c >> 2], xsw[c >> 2]);
         else
           acc[t] = mfma_fp8<0, 0>(wf[t][c], xf, acc[t]);
@@ -529,7 +579,7 @@ struct ResBlock {
   __device__ __forceinline__ void epilogue_stats(int buf, v4f (&acc)[NT], float& cs) {
     const float rsv = rs[buf * kResRows + r];
     const float sx = MODE == 1 ? rsv : (MODE == 0 ? p.x_s : 1.0f);
-    const float bound = MODE == 3 ? ldexpf(bw, (int)rsv - 127) + bb : sx * bw + bb;
+    const float bound = MX ? ldexpf(bw, (int)rsv - 127) + bb : sx * bw + bb;
     cs = row_rescale(bound);
     const float* cb = cvec + c0 + 4 * g;
     // sums as short trees (per tile, then over the tiles) rather than one
@@ -544,7 +594,7 @@ struct ResBlock {
         const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          acc[t][j] = MODE == 3 ? acc[t][j] + bv[j] : fmaf(acc[t][j], sx * swv[j], bv[j]);
+          acc[t][j] = MX ? acc[t][j] + bv[j] : fmaf(acc[t][j], sx * swv[j], bv[j]);
         st[t] = (acc[t][0] + acc[t][1]) + (acc[t][2] + acc[t][3]);
       }
     }

@@ -13,6 +13,7 @@ namespace fwd {
 hipError_t launch_tensor(const FwdBlock& p, const float* partials, int np, hipStream_t s);
 hipError_t launch_row(const FwdBlock& p, const float* partials, int np, hipStream_t s);
 hipError_t launch_mx(const FwdBlock& p, const float* partials, int np, hipStream_t s);
+hipError_t launch_mx_square(const FwdBlock& p, hipStream_t s);
 hipError_t launch_row_blocknorm(const FwdBlock& p, hipStream_t s);
 }  // namespace fwd
 
@@ -101,6 +102,12 @@ hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s) {
   p.z = a.z; p.mean = a.mean; p.rstd = a.rstd; p.qx_out = a.qx_out; p.sx_out = a.sx_out;
   p.eps = a.eps; p.x_r = 1.0f; p.x_s = 1.0f;
   p.ldy = (int)a.N;
+  p.xq = nullptr; p.xs = nullptr;
+  if (a.x_mode == 5) {
+    p.xq = static_cast<const uint8_t*>(a.x);
+    p.xs = a.x_scales;
+    p.x = nullptr;
+  }
   if (!a.w_packed && (a.blocknorm || fwd_weight_resident(a.N, a.K))) {
     // the resident kernel reads the weight fragment-interleaved
     uint8_t* wi = static_cast<uint8_t*>(a.workspace) + partial_bytes(a.M, a.K, a.x_mode);
@@ -117,6 +124,7 @@ hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s) {
     return fwd::launch_tensor(p, partials, np, s);
   }
   if (a.x_mode == 1) return fwd::launch_row(p, nullptr, 0, s);
+  if (a.x_mode == 5) return fwd::launch_mx_square(p, s);
   return fwd::launch_mx(p, nullptr, 0, s);
 }
 

@@ -47,7 +47,7 @@ hipError_t launch_quant(const QuantLaunch& a, hipStream_t s);
 // ---- forward -------------------------------------------------------------
 struct FwdLaunch {
   int64_t M, N, K;
-  int x_mode;  // 0 tensor, 1 row, 3 mx32
+  int x_mode;  // 0 tensor, 1 row, 3 mx32, 5 mx32 square blocks (X given as codes)
   float eps;
   const void* x;
   const uint8_t* qw;
@@ -62,6 +62,7 @@ struct FwdLaunch {
   uint8_t* qx_out;
   void* sx_out;
   void* workspace;
+  const uint8_t* x_scales;  // square-block recipe: X's E8M0 scales [M/32][K/32] (x holds its codes)
   bool w_packed;   // qw already in the fragment-interleaved layout
   bool blocknorm;  // BlockNorm(256) + Hard Swish epilogue instead of LayerNorm
 };

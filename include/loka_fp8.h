@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define LOKA_ABI_VERSION 1
+#define LOKA_ABI_VERSION 2
 
 typedef enum {
   LOKA_OK = 0,
@@ -164,6 +164,15 @@ loka_status loka_quant_fp8(const loka_quant_args* args, void* stream);
  *             x_mode TENSOR   -> W mode TENSOR,  sw float[1]
  *             x_mode ROW      -> W mode COL,     sw float[N]
  *             x_mode MX32_ROW -> W mode MX32_COL, sw uint8[N][K/32]
+ *             x_mode MX32_SQ  -> W mode MX32_SQ,  sw uint8[K/32][N/32]
+ *   x_mode MX32_SQ (GEM "Low Precision Flash Attention", Block-wise
+ *           Quantization, with activation quantization fused into the
+ *           producer, GEM "Mixed Ultra-Low-Precision Training"): X arrives
+ *           quantized -- x holds its e4m3 codes [M, K] and x_scales its
+ *           E8M0 scales uint8[M/32][K/32], as loka_quant_fp8 (MX32_SQ,
+ *           transpose_out 0) writes them -- and the same codes serve the
+ *           backward.  Needs M % 32 == 0, the weight-resident shapes and
+ *           qx_out = sx_out = NULL; x_scales must be NULL in other modes.
  *   bias, gamma, beta  bf16 [N] or NULL (NULL = 0, 1, 0; NULL bias is the
  *           No-Bias mode).
  *   Z[m,n]  = acc[m,n] * s_x[m] * s_w[n] + bias[n]   (MX: the E8M0 scales
@@ -200,7 +209,7 @@ loka_status loka_quant_fp8(const loka_quant_args* args, void* stream);
 #define LOKA_FWD_BLOCKNORM_HSWISH 2
 typedef struct {
   int64_t M, N, K;
-  int32_t x_mode; /* LOKA_SCALE_TENSOR, LOKA_SCALE_ROW or LOKA_SCALE_MX32_ROW */
+  int32_t x_mode; /* LOKA_SCALE_TENSOR, LOKA_SCALE_ROW, LOKA_SCALE_MX32_ROW or LOKA_SCALE_MX32_SQ */
   int32_t flags;  /* LOKA_FWD_W_PACKED | LOKA_FWD_BLOCKNORM_HSWISH, or 0 */
   float eps;
   const void* x;
@@ -217,6 +226,7 @@ typedef struct {
   void* sx_out;
   void* workspace;
   size_t workspace_bytes;
+  const uint8_t* x_scales; /* MX32_SQ only: X's E8M0 scales [M/32][K/32] */
 } loka_fwd_args;
 
 size_t loka_gemm_fp8_ln_workspace_size(const loka_fwd_args* args);

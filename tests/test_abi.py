@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_helpers(lib):
-    assert lib.loka_abi_version() == 1
+    assert lib.loka_abi_version() == 2
     for code, name in lk.STATUS.items():
         assert lib.loka_status_string(code).decode() == name
 
