@@ -28,6 +28,7 @@ MODES = {"tensor": 0, "row": 1, "col": 2, "mx32_row": 3, "mx32_col": 4, "mx32_sq
 STATUS = {0: "LOKA_OK", 1: "LOKA_ERR_INVALID_ARG", 2: "LOKA_ERR_UNSUPPORTED", 3: "LOKA_ERR_ALIGNMENT",
           4: "LOKA_ERR_WORKSPACE", 5: "LOKA_ERR_HIP"}
 BWD_NO_LN = 1
+BWD_MX32_SQ = 2
 FWD_W_PACKED = 1
 FWD_BLOCKNORM_HSWISH = 2
 EPILOGUES = {"layernorm": 0, "blocknorm_hswish": FWD_BLOCKNORM_HSWISH}
@@ -266,19 +267,29 @@ def loka_gemm_fp8_ln(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e-5, x_mo
 
 def loka_gemm_fp8_bwd(dy, x, qw_row, sw_row, ctx=None, bias=None, gamma=None, no_ln=False, want_dz=False,
                       want_dz_codes=False, want_dgamma=True, want_dbias=True, workspace=None, stream=None,
-                      prepare=False):
+                      prepare=False, square=False):
     """Backward of loka_gemm_fp8_ln (row recipe).
 
     ctx: dict with qx [M,K] uint8, sx [M], mean [M], rstd [M], qw [N,K], sw [N]
     (the forward's qx/sx outputs, statistics and weight); unused with no_ln.
+    square=True: the backward of the square-block forward (x_mode="mx32_sq";
+    flag LOKA_BWD_MX32_SQ): ctx holds X's codes qx [M,K] and scales sx
+    [M/32,K/32], the weight's qw [N,K] and sw [K/32,N/32] (always required),
+    and mean/rstd unless no_ln; x, qw_row and sw_row are unused (None).
     Returns a dict with dx, dw and the requested outputs."""
     M, N = dy.shape
-    K = x.shape[1]
+    ctx = ctx or {}
+    K = (ctx["qx"] if square else x).shape[1]
     dev = dy.device
     _need(dy, torch.bfloat16, (M, N), "dy")
-    _need(x, torch.bfloat16, (M, K), "x")
-    _need(qw_row, torch.uint8, (K, N), "qw_row")
-    ctx = ctx or {}
+    if square:
+        _need(ctx["qx"], torch.uint8, (M, K), "qx")
+        _need(ctx["sx"], torch.uint8, (M // 32, K // 32), "sx")
+        _need(ctx["qw"], torch.uint8, (N, K), "qw")
+        _need(ctx["sw"], torch.uint8, (K // 32, N // 32), "sw")
+    else:
+        _need(x, torch.bfloat16, (M, K), "x")
+        _need(qw_row, torch.uint8, (K, N), "qw_row")
     out = {"dx": torch.empty((M, K), dtype=torch.bfloat16, device=dev),
            "dw": torch.empty((K, N), dtype=torch.float32, device=dev)}
     if want_dgamma and not no_ln:
@@ -290,8 +301,10 @@ def loka_gemm_fp8_bwd(dy, x, qw_row, sw_row, ctx=None, bias=None, gamma=None, no
         out["dz"] = torch.empty((M, N), dtype=torch.float32, device=dev)
     if want_dz_codes:
         out["dz_codes"] = torch.empty((M, N), dtype=torch.uint8, device=dev)
-        out["dz_scales"] = torch.empty(M, dtype=torch.float32, device=dev)
-    a = BwdArgs(M=M, N=N, K=K, flags=BWD_NO_LN if no_ln else 0, reserved=0, dy=_ptr(dy), qx=_ptr(ctx.get("qx")),
+        out["dz_scales"] = (torch.empty((M // 32, N // 32), dtype=torch.uint8, device=dev) if square
+                            else torch.empty(M, dtype=torch.float32, device=dev))
+    flags = (BWD_NO_LN if no_ln else 0) | (BWD_MX32_SQ if square else 0)
+    a = BwdArgs(M=M, N=N, K=K, flags=flags, reserved=0, dy=_ptr(dy), qx=_ptr(ctx.get("qx")),
                 sx=_ptr(ctx.get("sx")), mean=_ptr(ctx.get("mean")), rstd=_ptr(ctx.get("rstd")),
                 qw=_ptr(ctx.get("qw")), sw=_ptr(ctx.get("sw")), bias=_ptr(bias), gamma=_ptr(gamma), x=_ptr(x),
                 qw_row=_ptr(qw_row), sw_row=_ptr(sw_row), dx=_ptr(out["dx"]), dw=_ptr(out["dw"]),

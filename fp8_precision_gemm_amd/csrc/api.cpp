@@ -202,23 +202,36 @@ loka_status loka_gemm_fp8_ln(const loka_fwd_args* a, void* stream) {
 // ---------------------------------------------------------------------------
 size_t loka_gemm_fp8_bwd_workspace_size(const loka_bwd_args* a) {
   if (a == nullptr || a->M <= 0 || a->N <= 0 || a->K <= 0) return 0;
-  return loka::bwd_workspace_bytes(a->M, a->N, a->K);
+  return loka::bwd_workspace_bytes(a->M, a->N, a->K, (a->flags & LOKA_BWD_MX32_SQ) != 0);
 }
 
 loka_status loka_gemm_fp8_bwd(const loka_bwd_args* a, void* stream) {
   REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
-  REQUIRE(a->flags == 0 || a->flags == LOKA_BWD_NO_LN, LOKA_ERR_INVALID_ARG, "unknown flags %d", a->flags);
-  loka_status st = check_fwd_shape(a->M, a->N, a->K, LOKA_SCALE_ROW);
+  REQUIRE((a->flags & ~(LOKA_BWD_NO_LN | LOKA_BWD_MX32_SQ)) == 0, LOKA_ERR_INVALID_ARG, "unknown flags %d",
+          a->flags);
+  const bool sq = (a->flags & LOKA_BWD_MX32_SQ) != 0;
+  loka_status st = check_fwd_shape(a->M, a->N, a->K, sq ? LOKA_SCALE_MX32_SQ : LOKA_SCALE_ROW);
   if (st != LOKA_OK) return st;
   REQUIRE(a->K % 64 == 0 && a->K <= 1024, LOKA_ERR_UNSUPPORTED, "backward needs K %% 64 == 0 and K <= 1024");
   REQUIRE(a->M % 16 == 0, LOKA_ERR_UNSUPPORTED, "backward needs M %% 16 == 0");
+  if (sq)
+    REQUIRE(a->M % 32 == 0 && a->N <= 512 && a->K <= 512, LOKA_ERR_UNSUPPORTED,
+            "the square-block backward needs M %% 32 == 0, N <= 512 and K <= 512 (got M=%lld N=%lld K=%lld)",
+            (long long)a->M, (long long)a->N, (long long)a->K);
   const bool no_ln = (a->flags & LOKA_BWD_NO_LN) != 0;
   if (a->M > 0) {
-    REQUIRE(a->dy && a->x && a->qw_row && a->sw_row && a->dx && a->dw, LOKA_ERR_INVALID_ARG,
-            "dy, x, qw_row, sw_row, dx and dw are required");
-    if (!no_ln)
-      REQUIRE(a->qx && a->sx && a->mean && a->rstd && a->qw && a->sw, LOKA_ERR_INVALID_ARG,
-              "the forward context (qx, sx, mean, rstd, qw, sw) is required");
+    if (sq) {
+      REQUIRE(a->dy && a->qx && a->sx && a->qw && a->sw && a->dx && a->dw, LOKA_ERR_INVALID_ARG,
+              "dy, qx, sx, qw, sw, dx and dw are required");
+      if (!no_ln)
+        REQUIRE(a->mean && a->rstd, LOKA_ERR_INVALID_ARG, "the forward's mean and rstd are required");
+    } else {
+      REQUIRE(a->dy && a->x && a->qw_row && a->sw_row && a->dx && a->dw, LOKA_ERR_INVALID_ARG,
+              "dy, x, qw_row, sw_row, dx and dw are required");
+      if (!no_ln)
+        REQUIRE(a->qx && a->sx && a->mean && a->rstd && a->qw && a->sw, LOKA_ERR_INVALID_ARG,
+                "the forward context (qx, sx, mean, rstd, qw, sw) is required");
+    }
   }
   REQUIRE(!(no_ln && (a->dgamma || a->dbeta)), LOKA_ERR_INVALID_ARG, "dgamma/dbeta are undefined without LayerNorm");
   REQUIRE_ALIGNED(a->dy); REQUIRE_ALIGNED(a->qx); REQUIRE_ALIGNED(a->sx); REQUIRE_ALIGNED(a->mean);
@@ -230,7 +243,7 @@ loka_status loka_gemm_fp8_bwd(const loka_bwd_args* a, void* stream) {
     return st;
   if (a->M == 0) return LOKA_OK;
   loka::BwdLaunch b{};
-  b.M = a->M; b.N = a->N; b.K = a->K; b.no_ln = no_ln ? 1 : 0;
+  b.M = a->M; b.N = a->N; b.K = a->K; b.no_ln = no_ln ? 1 : 0; b.sq = sq;
   b.dy = a->dy; b.qx = a->qx; b.sx = a->sx; b.mean = a->mean; b.rstd = a->rstd; b.qw = a->qw; b.sw = a->sw;
   b.bias = a->bias; b.gamma = a->gamma; b.x = a->x; b.qw_row = a->qw_row; b.sw_row = a->sw_row;
   b.dx = a->dx; b.dw = a->dw; b.dgamma = a->dgamma; b.dbeta = a->dbeta; b.dbias = a->dbias;

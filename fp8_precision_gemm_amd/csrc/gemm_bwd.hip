@@ -58,7 +58,21 @@ struct BwdBlock {
   float* dz_scales;
   float* part;  // [4][nblocks][N]: dgamma, dbeta, dbias, max|dZ|
   int nblocks;
+  // square-block recipe: X's and W's E8M0 scales ([M/32][K/32], [K/32][N/32]),
+  // dZ's scales out ([M/32][N/32]) and its codes out transposed for the wgrad
+  // (fragment-interleaved [N][M padded to 128], nchm 128-row chunks)
+  const uint8_t* sx8;
+  const uint8_t* sw8;
+  uint8_t* sdz;
+  uint8_t* dzt;
+  int64_t nchm;
 };
+
+// MFMA with both operands' E8M0 scale bytes (the bytes this lane supplies)
+template <int FA, int FB>
+__device__ __forceinline__ v4f mfma_fp8_scaled(const v8i& a, const v8i& b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
+}
 
 __device__ __forceinline__ void ld4_bf16(const uint16_t* p, float def, float o[4]) {
   if (p == nullptr) {
@@ -92,7 +106,10 @@ __device__ __forceinline__ void wave_tiles(int T, int w, int& t0, int& n) {
 // guards).  WAVES wavefronts split the columns: eight (two per SIMD) where a
 // wavefront's accumulators and weight fragments fit half the register file
 // (N, K <= 512), else four.
-template <int NTMAX, int KTMAX, int NO_LN, bool FULLM, int WAVES>
+// SQ: the square-block recipe (X, W and dZ with one E8M0 scale per 32 x 32
+// block; the MFMAs apply the scales, dZ is quantized by blocks and its codes
+// also leave transposed for the wgrad).
+template <int NTMAX, int KTMAX, int NO_LN, bool FULLM, int WAVES, bool SQ = false>
 __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
   extern __shared__ __align__(16) uint8_t smem[];
   const int K = p.K, N = p.N;
@@ -125,7 +142,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
     rowok[i] = FULLM || m < p.M;
     mu[i] = (!NO_LN && rowok[i]) ? p.mean[m] : 0.0f;
     rs[i] = (!NO_LN && rowok[i]) ? p.rstd[m] : 0.0f;
-    sxv[i] = (!NO_LN && rowok[i]) ? p.sx[m] : 0.0f;
+    sxv[i] = (!NO_LN && !SQ && rowok[i]) ? p.sx[m] : 0.0f;
   }
 
   if (!NO_LN) {
@@ -166,11 +183,27 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
       v8i xf[kMT];
 #pragma unroll
       for (int i = 0; i < kMT; ++i) xf[i] = load_frag(xs + (16 * i + r) * ldk, g, 128 * c, K);
+      if constexpr (SQ) {
+        // lane group g supplies the scales of K block 4c + g (clamped past K,
+        // where the codes are zero): W's for its column, X's for its row
+        const int kbk = min(4 * c + g, (K >> 5) - 1);
+        int sa[NTMAX], sb[kMT];
 #pragma unroll
-      for (int t = 0; t < NTMAX; ++t)
-        if (t < nt)
+        for (int t = 0; t < NTMAX; ++t) sa[t] = t < nt ? p.sw8[kbk * (N >> 5) + ((nb + 16 * t + r) >> 5)] : 127;
 #pragma unroll
-          for (int i = 0; i < kMT; ++i) acc[t][i] = mfma_fp8<0, 0>(wc[t], xf[i], acc[t][i]);
+        for (int i = 0; i < kMT; ++i) sb[i] = p.sx8[(min(m0 + 16 * i + r, p.M - 1) >> 5) * (K >> 5) + kbk];
+#pragma unroll
+        for (int t = 0; t < NTMAX; ++t)
+          if (t < nt)
+#pragma unroll
+            for (int i = 0; i < kMT; ++i) acc[t][i] = mfma_fp8_scaled<0, 0>(wc[t], xf[i], acc[t][i], sa[t], sb[i]);
+      } else {
+#pragma unroll
+        for (int t = 0; t < NTMAX; ++t)
+          if (t < nt)
+#pragma unroll
+            for (int i = 0; i < kMT; ++i) acc[t][i] = mfma_fp8<0, 0>(wc[t], xf[i], acc[t][i]);
+      }
     };
     wload(0, wa);
     for (int c = 0; c < nchk; c += 2) {
@@ -194,10 +227,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
   for (int t = 0; t < NTMAX; ++t) {
     if (t < nt) {
       const int n0 = nb + 16 * t + 4 * g;
-      float swv[4], bv[4], gm[4];
+      float swv[4] = {1.0f, 1.0f, 1.0f, 1.0f}, bv[4], gm[4];
       if (!NO_LN) {
-        float4 s4 = *reinterpret_cast<const float4*>(p.sw + n0);
-        swv[0] = s4.x; swv[1] = s4.y; swv[2] = s4.z; swv[3] = s4.w;
+        if (!SQ) {
+          float4 s4 = *reinterpret_cast<const float4*>(p.sw + n0);
+          swv[0] = s4.x; swv[1] = s4.y; swv[2] = s4.z; swv[3] = s4.w;
+        }
         ld4_bf16(p.bias ? p.bias + n0 : nullptr, 0.0f, bv);
         ld4_bf16(p.gamma ? p.gamma + n0 : nullptr, 1.0f, gm);
       }
@@ -212,7 +247,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
           if (NO_LN) {
             acc[t][i][j] = dyv[j];  // dZ = dY
           } else {
-            const float z = acc[t][i][j] * sxv[i] * swv[j] + bv[j];
+            const float z = SQ ? acc[t][i][j] + bv[j] : acc[t][i][j] * sxv[i] * swv[j] + bv[j];
             const float yh = (z - mu[i]) * rs[i];
             const float gg = dyv[j] * gm[j];
             acc[t][i][j] = yh;
@@ -284,25 +319,73 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
       for (int i = 0; i < kMT; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) am[i] = fmaxf(am[i], fabsf(acc[t][i][j]));
-  __syncthreads();  // red0/red1 reads above are complete before reuse
-#pragma unroll
-  for (int i = 0; i < kMT; ++i) {
-    am[i] = rows4_max(am[i]);
-    if (g == 0) red0[wave * kBM + 16 * i + r] = am[i];
-  }
-  __syncthreads();
   float rq[kMT];
+  float mq[NTMAX][2];  // SQ: multiplier of the 32 x 32 block of tile t, row band i / 2
+  int* be8 = reinterpret_cast<int*>(rsc);  // SQ: the block's E8M0 codes [2][N/32]
+  if constexpr (SQ) {
+    // 32 x 32 block maxima of |dZ|: per 16 x 16 tile a DPP max over its rows
+    // and a permlane max over its column groups, two tiles per 32-row band;
+    // the bands' tile maxima go through LDS, since a block may straddle two
+    // wavefronts' column runs
+    const int T16 = N >> 4;
+    float tm[NTMAX][2];
 #pragma unroll
-  for (int i = 0; i < kMT; ++i) {
-    const int rr = 16 * i + r;
-    float a = red0[rr];
+    for (int t = 0; t < NTMAX; ++t)
 #pragma unroll
-    for (int w = 1; w < WAVES; ++w) a = fmaxf(a, red0[w * kBM + rr]);
-    ScalePair sp = scales_from_amax<1>(a);
-    rq[i] = sp.r;
-    if (wave == 0 && g == 0) {
-      rsc[rr] = sp.s;
-      if (p.dz_scales && rowok[i]) p.dz_scales[m0 + rr] = sp.s;
+      for (int rb = 0; rb < 2; ++rb) {
+        float a = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) a = fmaxf(a, fmaxf(fabsf(acc[t][2 * rb][j]), fabsf(acc[t][2 * rb + 1][j])));
+        tm[t][rb] = rows4_max(row16_max(a));
+      }
+    __syncthreads();  // red0/red1 reads above are complete before reuse
+    if (lane == 0) {
+#pragma unroll
+      for (int t = 0; t < NTMAX; ++t)
+        if (t < nt) {
+          red0[(nb >> 4) + t] = tm[t][0];
+          red0[T16 + (nb >> 4) + t] = tm[t][1];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NTMAX; ++t)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        mq[t][rb] = 1.0f;
+        if (t < nt) {
+          const int ct = (nb >> 4) + t, cb = ct >> 1;
+          const float a = fmaxf(red0[rb * T16 + 2 * cb], red0[rb * T16 + 2 * cb + 1]);
+          const int e8 = e8m0_from_amax<1>(a);
+          mq[t][rb] = e8m0_inv_multiplier(e8);
+          // one writer per block: lane 0 of the wavefront owning its even tile
+          if (lane == 0 && (ct & 1) == 0) {
+            be8[rb * (N >> 5) + cb] = e8;
+            const int64_t gb = (m0 >> 5) + rb;
+            if (gb * 32 < p.M) p.sdz[gb * (N >> 5) + cb] = (uint8_t)e8;
+          }
+        }
+      }
+  } else {
+    __syncthreads();  // red0/red1 reads above are complete before reuse
+#pragma unroll
+    for (int i = 0; i < kMT; ++i) {
+      am[i] = rows4_max(am[i]);
+      if (g == 0) red0[wave * kBM + 16 * i + r] = am[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kMT; ++i) {
+      const int rr = 16 * i + r;
+      float a = red0[rr];
+#pragma unroll
+      for (int w = 1; w < WAVES; ++w) a = fmaxf(a, red0[w * kBM + rr]);
+      ScalePair sp = scales_from_amax<1>(a);
+      rq[i] = sp.r;
+      if (wave == 0 && g == 0) {
+        rsc[rr] = sp.s;
+        if (p.dz_scales && rowok[i]) p.dz_scales[m0 + rr] = sp.s;
+      }
     }
   }
 
@@ -325,14 +408,16 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
           cdb[j] += acc[t][i][j];
           cmx[j] = fmaxf(cmx[j], fabsf(acc[t][i][j]));
         }
-        const uint32_t q = cvt4<1>(acc[t][i][0] * rq[i], acc[t][i][1] * rq[i], acc[t][i][2] * rq[i],
-                                   acc[t][i][3] * rq[i]);
+        const float mul = SQ ? mq[t][i >> 1] : rq[i];
+        const uint32_t q = cvt4<1>(acc[t][i][0] * mul, acc[t][i][1] * mul, acc[t][i][2] * mul, acc[t][i][3] * mul);
         *reinterpret_cast<uint32_t*>(ds + lr * ldn + n0) = q;
         // rows past M fall outside the resource: the hardware drops them
-        __builtin_amdgcn_raw_buffer_store_b128(
-            v4u{__float_as_uint(acc[t][i][0]), __float_as_uint(acc[t][i][1]), __float_as_uint(acc[t][i][2]),
-                __float_as_uint(acc[t][i][3])},
-            dzr, (uint32_t)(lr * N + n0) * 4u, 0, 0);
+        // (SQ: fp32 dZ only on request; the wgrad reads the codes)
+        if (!SQ || p.dz != nullptr)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v4u{__float_as_uint(acc[t][i][0]), __float_as_uint(acc[t][i][1]), __float_as_uint(acc[t][i][2]),
+                  __float_as_uint(acc[t][i][3])},
+              dzr, (uint32_t)(lr * N + n0) * 4u, 0, 0);
         if (p.dz_codes && rowok[i]) *reinterpret_cast<uint32_t*>(p.dz_codes + m * N + n0) = q;
       }
       // reduce over the 16 lanes (rows) sharing these 4 columns; then lane r
@@ -356,6 +441,23 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
     }
   }
   __syncthreads();
+  if constexpr (SQ) {
+    // the block's dZ codes, transposed, into the wgrad operand: a thread
+    // gathers 16 rows of column n, one 16-byte piece of the interleaved
+    // [N][M padded to 128] layout; rows past M hold zero codes, and the last
+    // block also writes the zero rows up to the padding
+    const int64_t rows_out = blockIdx.x == gridDim.x - 1 ? p.nchm * 128 - m0 : (int64_t)kBM;
+    const int pieces = (int)(rows_out >> 4) * N;
+    for (int u = tid; u < pieces; u += 64 * WAVES) {
+      const int q = u / N, n = u - q * N;
+      uint32_t w4[4] = {0u, 0u, 0u, 0u};
+      if (q < kMT) {
+#pragma unroll
+        for (int b = 0; b < 16; ++b) w4[b >> 2] |= (uint32_t)ds[(16 * q + b) * ldn + n] << (8 * (b & 3));
+      }
+      *reinterpret_cast<uint4*>(p.dzt + ilv_offset(n, m0 + 16 * q, p.nchm)) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+    }
+  }
 
   // dgrad: D[k][m] = sum_n Wr[k][n] dZq[m][n]; each wavefront owns a run of
   // 16-column tiles of k
@@ -380,11 +482,27 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
     v8i df[kMT];
 #pragma unroll
     for (int i = 0; i < kMT; ++i) df[i] = load_frag(ds + (16 * i + r) * ldn, g, 128 * c, N);
+    if constexpr (SQ) {
+      // lane group g: N block 4c + g (clamped past N, where the codes are
+      // zero); W's scale for row k, dZ's for row band i / 2
+      const int nbk = min(4 * c + g, (N >> 5) - 1);
+      int sa[KTMAX], sb[kMT];
 #pragma unroll
-    for (int t = 0; t < KTMAX; ++t)
-      if (t < kt)
+      for (int t = 0; t < KTMAX; ++t) sa[t] = t < kt ? p.sw8[((kb0 + 16 * t + r) >> 5) * (N >> 5) + nbk] : 127;
 #pragma unroll
-        for (int i = 0; i < kMT; ++i) dacc[t][i] = mfma_fp8<0, 1>(wc[t], df[i], dacc[t][i]);
+      for (int i = 0; i < kMT; ++i) sb[i] = be8[(i >> 1) * (N >> 5) + nbk];
+#pragma unroll
+      for (int t = 0; t < KTMAX; ++t)
+        if (t < kt)
+#pragma unroll
+          for (int i = 0; i < kMT; ++i) dacc[t][i] = mfma_fp8_scaled<0, 1>(wc[t], df[i], dacc[t][i], sa[t], sb[i]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < KTMAX; ++t)
+        if (t < kt)
+#pragma unroll
+          for (int i = 0; i < kMT; ++i) dacc[t][i] = mfma_fp8<0, 1>(wc[t], df[i], dacc[t][i]);
+    }
   };
   rload(0, ra);
   for (int c = 0; c < nchn; c += 2) {
@@ -393,11 +511,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
   }
   float dsv[kMT];
 #pragma unroll
-  for (int i = 0; i < kMT; ++i) dsv[i] = rsc[16 * i + r];
+  for (int i = 0; i < kMT; ++i) dsv[i] = SQ ? 1.0f : rsc[16 * i + r];
   float swr[KTMAX][4];
 #pragma unroll
   for (int t = 0; t < KTMAX; ++t) {
-    if (t < kt) {
+    swr[t][0] = swr[t][1] = swr[t][2] = swr[t][3] = 1.0f;
+    if (!SQ && t < kt) {
       const float4 s4 = *reinterpret_cast<const float4*>(p.sw_row + kb0 + 16 * t + 4 * g);
       swr[t][0] = s4.x; swr[t][1] = s4.y; swr[t][2] = s4.z; swr[t][3] = s4.w;
     }
@@ -442,8 +561,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
 // (e4m3), both fragment-interleaved with M padded to 128 (zero codes), so
 // lane (r, g) holds D[n = 16a + 4g + j][k = 16b + r].  Slice s covers the
 // 128-row chunks [s * chunks_per_split, +chunks_per_split).
+// SQ: both operands carry E8M0 scales per 32 x 32 block (dZ's [M/32][N/32],
+// X's [M/32][K/32]), applied by the MFMA: lane group g of chunk c supplies
+// M block 4c + g (clamped past M, where the codes are zero).
+template <bool SQ>
 __global__ __launch_bounds__(256) void k_wgrad(const uint8_t* dzt, const uint8_t* xt, int64_t M, int N, int K,
-                                               int64_t chunks_per_split, float* part) {
+                                               int64_t chunks_per_split, float* part, const uint8_t* sdz,
+                                               const uint8_t* sx8) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 15, g = lane >> 4;
   const int n0 = blockIdx.x * 128 + (wave & 1) * 64;
@@ -461,24 +585,41 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint8_t* dzt, const uint8_t
   if (nin && kin && cs < ce) {
     // the next 128-row chunk's fragments are requested before this chunk's MFMAs
     v8i af[4], bf[4], an[4], bn[4];
+    int sa[4], sb[4], san[4], sbn[4];
+    const int64_t mbl = M / 32 - 1;
+    auto scales = [&](int64_t c, int (&xa)[4], int (&xb)[4]) {
+      if constexpr (SQ) {
+        const int64_t mb = min(4 * c + g, mbl);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) xa[a] = sdz[mb * (N >> 5) + ((n0 + 16 * a + r) >> 5)];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) xb[b] = sx8[mb * (K >> 5) + ((k0 + 16 * b + r) >> 5)];
+      }
+    };
 #pragma unroll
     for (int a = 0; a < 4; ++a) af[a] = load_frag_ilv(dzt, n0 / 16 + a, cs, nch, r, g);
 #pragma unroll
     for (int b = 0; b < 4; ++b) bf[b] = load_frag_ilv(xt, k0 / 16 + b, cs, nch, r, g);
+    scales(cs, sa, sb);
     for (int64_t c = cs; c < ce; ++c) {
       const int64_t cn = c + 1 < ce ? c + 1 : c;  // past the end: a harmless reload of this chunk
 #pragma unroll
       for (int a = 0; a < 4; ++a) an[a] = load_frag_ilv(dzt, n0 / 16 + a, cn, nch, r, g);
 #pragma unroll
       for (int b = 0; b < 4; ++b) bn[b] = load_frag_ilv(xt, k0 / 16 + b, cn, nch, r, g);
+      scales(cn, san, sbn);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = mfma_fp8<1, 0>(af[a], bf[b], acc[a][b]);
+        for (int b = 0; b < 4; ++b)
+          acc[a][b] = SQ ? mfma_fp8_scaled<1, 0>(af[a], bf[b], acc[a][b], sa[a], sb[b])
+                         : mfma_fp8<1, 0>(af[a], bf[b], acc[a][b]);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         af[a] = an[a];
         bf[a] = bn[a];
+        sa[a] = san[a];
+        sb[a] = sbn[a];
       }
     }
 #pragma unroll
@@ -492,8 +633,9 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint8_t* dzt, const uint8_t
   }
 }
 
-// dW[k][n] = (sum_s part[s][k][n]) * sxc[k] * sdzc[n].  Fixed summation
-// order => deterministic.
+// dW[k][n] = (sum_s part[s][k][n]) * sxc[k] * sdzc[n] (no column scales,
+// sxc == NULL, when the MFMA applied block scales).  Fixed summation order
+// => deterministic.
 __device__ __forceinline__ void finalize_body(int64_t blk, const float* wpart, int nsplit, const float* sxc,
                                               const float* sdzc, int K, int N, float* dw) {
   const int64_t i = blk * 256 + threadIdx.x;
@@ -502,7 +644,7 @@ __device__ __forceinline__ void finalize_body(int64_t blk, const float* wpart, i
     float s = 0.0f;
     for (int sp = 0; sp < nsplit; ++sp) s += wpart[(int64_t)sp * kn + i];
     const int k = (int)(i / N), n = (int)(i - (int64_t)k * N);
-    dw[i] = s * sxc[k] * sdzc[n];
+    dw[i] = sxc != nullptr ? s * sxc[k] * sdzc[n] : s;
   }
 }
 
@@ -559,6 +701,74 @@ __global__ __launch_bounds__(256) void k_finalize_vectors(const float* wpart, in
   else col_vectors_body((int)blockIdx.x - nf, cpart, nblocks, N, dgamma, dbeta, dbias);
 }
 
+// The square-block backward's three MFMA operands in one launch, all
+// fragment-interleaved: job 0 the weight codes qw [N][K] as they are (the Z
+// recompute), job 1 their transpose [K][N] (the dgrad: W's own rows), job 2
+// the X codes' transpose [K][M] (the wgrad).  The transposes go through a
+// 64 x 64 LDS tile; their rows are padded with zero codes up to a multiple
+// of 128 columns.  One quantization per tensor: no code is recomputed.
+struct TJob {
+  const uint8_t* src;
+  int64_t R, C;  // source [R][C], C % 64 == 0
+  uint8_t* dst;  // interleaved [C][R padded to 128]
+  int64_t tiles_c, blocks;
+};
+__global__ __launch_bounds__(256) void k_relayout_sq(const uint8_t* qw, int64_t N, int64_t K, uint8_t* qwi,
+                                                     int64_t b0, TJob j1, TJob j2) {
+  __shared__ uint32_t tile[64][17];  // 64 source rows x 64 bytes, padded
+  const int t = threadIdx.x;
+  int64_t b = blockIdx.x;
+  if (b < b0) {
+    const int64_t nch = (K + 127) / 128, pieces = nch * 8;
+    const int64_t u = b * 256 + t;
+    if (u >= N * pieces) return;
+    const int64_t row = u / pieces, col = (u - row * pieces) * 16;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (col < K) v = *reinterpret_cast<const uint4*>(qw + row * K + col);
+    *reinterpret_cast<uint4*>(qwi + ilv_offset(row, col, nch)) = v;
+    return;
+  }
+  b -= b0;
+  const bool first = b < j1.blocks;
+  const TJob j = first ? j1 : j2;
+  if (!first) b -= j1.blocks;
+  const int64_t tr = b / j.tiles_c, tc = b - tr * j.tiles_c;
+  // source row 64 tr + t/4, bytes 64 tc + 16 (t%4) .. +16 (rows past R: zeros)
+  const int lr = t >> 2, lc = (t & 3) * 4;
+  const int64_t srow = 64 * tr + lr;
+  uint4 v = make_uint4(0, 0, 0, 0);
+  if (srow < j.R) v = *reinterpret_cast<const uint4*>(j.src + srow * j.C + 64 * tc + 4 * lc);
+  tile[lr][lc] = v.x; tile[lr][lc + 1] = v.y; tile[lr][lc + 2] = v.z; tile[lr][lc + 3] = v.w;
+  __syncthreads();
+  // destination row 64 tc + t/4 (a source column), its 16 columns 64 tr + 16 (t%4) .. (source rows)
+  const int oc = t >> 2, orr = (t & 3) * 16;
+  uint32_t w4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const uint32_t word = tile[orr + q][oc >> 2];
+    w4[q >> 2] |= ((word >> (8 * (oc & 3))) & 0xFFu) << (8 * (q & 3));
+  }
+  const int64_t nch = (j.R + 127) / 128;
+  *reinterpret_cast<uint4*>(j.dst + ilv_offset(64 * tc + oc, 64 * tr + orr, nch)) =
+      make_uint4(w4[0], w4[1], w4[2], w4[3]);
+}
+
+hipError_t launch_relayout_sq(const uint8_t* qw, int64_t N, int64_t K, uint8_t* qwi, uint8_t* qwri, const uint8_t* qx,
+                              int64_t M, uint8_t* xt, hipStream_t s) {
+  const int64_t b0 = (N * ((K + 127) / 128) * 8 + 255) / 256;
+  auto job = [](const uint8_t* src, int64_t R, int64_t C, uint8_t* dst) {
+    TJob j;
+    j.src = src; j.R = R; j.C = C; j.dst = dst;
+    j.tiles_c = C / 64;
+    j.blocks = (R + 127) / 128 * 2 * j.tiles_c;  // 64-row tiles up to the 128 padding
+    return j;
+  };
+  const TJob j1 = job(qw, N, K, qwri), j2 = job(qx, M, K, xt);
+  hipLaunchKernelGGL(k_relayout_sq, dim3((unsigned)(b0 + j1.blocks + j2.blocks)), dim3(256), 0, s, qw, N, K, qwi, b0,
+                     j1, j2);
+  return hipGetLastError();
+}
+
 size_t bwd_lds_bytes(int K, int N, bool sdy, int waves) {
   const size_t main = (size_t)kBM * (K + 16) + (size_t)kBM * (N + 16) + (size_t)(2 * waves * kBM + kBM) * 4 +
                       (sdy ? (size_t)kBM * (2 * N + 16) : 0);
@@ -567,11 +777,13 @@ size_t bwd_lds_bytes(int K, int N, bool sdy, int waves) {
 }
 
 struct BwdWs {
-  size_t part, dz, xt, sxc, xcolp, dzt, sdzc, dzmult, qwi, qwri, wpart, total;
+  size_t part, dz, xt, sxc, xcolp, dzt, sdzc, dzmult, qwi, qwri, wpart, sdz, total;
   int nblocks, nsplit;
   int64_t xnp;
 };
-BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K) {
+// sq: the square-block recipe needs no fp32 dZ, no column maxima or scales,
+// only dZ's block scales
+BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K, bool sq) {
   BwdWs w{};
   auto al = [](size_t b) { return (b + 255) / 256 * 256; };
   w.nblocks = (int)((M + kBM - 1) / kBM);
@@ -581,14 +793,20 @@ BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K) {
   w.xnp = xq.np;
   size_t o = 0;
   w.part = o; o += al((size_t)4 * w.nblocks * N * 4);
-  w.dz = o; o += al((size_t)M * N * 4);
+  if (!sq) { w.dz = o; o += al((size_t)M * N * 4); }
   const int64_t mpad = (M + 127) / 128 * 128;
   w.xt = o; o += al((size_t)mpad * K);
-  w.sxc = o; o += al((size_t)K * 4);
-  w.xcolp = o; o += al((size_t)xq.ws_floats * 4);
+  if (!sq) {
+    w.sxc = o; o += al((size_t)K * 4);
+    w.xcolp = o; o += al((size_t)xq.ws_floats * 4);
+  }
   w.dzt = o; o += al((size_t)mpad * N);
-  w.sdzc = o; o += al((size_t)N * 4);
-  w.dzmult = o; o += al((size_t)N * 4);
+  if (!sq) {
+    w.sdzc = o; o += al((size_t)N * 4);
+    w.dzmult = o; o += al((size_t)N * 4);
+  } else {
+    w.sdz = o; o += al((size_t)(M / 32) * (N / 32));
+  }
   w.qwi = o; o += al((size_t)N * ((K + 127) / 128 * 128));
   w.qwri = o; o += al((size_t)K * ((N + 127) / 128 * 128));
   w.wpart = o; o += al((size_t)w.nsplit * K * N * 4);
@@ -596,13 +814,13 @@ BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K) {
   return w;
 }
 
-template <int NTMAX, int KTMAX, int WAVES>
+template <int NTMAX, int KTMAX, int WAVES, bool SQ = false>
 hipError_t launch_main_t(const BwdBlock& p, int no_ln, hipStream_t s) {
   const size_t lds = bwd_lds_bytes(p.K, p.N, bwd_stage_dy(NTMAX, KTMAX, WAVES), WAVES);
   const dim3 grid((unsigned)p.nblocks);
   const bool full = p.M % kBM == 0;
-  auto kern = no_ln ? (full ? k_bwd_main<NTMAX, KTMAX, 1, true, WAVES> : k_bwd_main<NTMAX, KTMAX, 1, false, WAVES>)
-                    : (full ? k_bwd_main<NTMAX, KTMAX, 0, true, WAVES> : k_bwd_main<NTMAX, KTMAX, 0, false, WAVES>);
+  auto kern = no_ln ? (full ? k_bwd_main<NTMAX, KTMAX, 1, true, WAVES, SQ> : k_bwd_main<NTMAX, KTMAX, 1, false, WAVES, SQ>)
+                    : (full ? k_bwd_main<NTMAX, KTMAX, 0, true, WAVES, SQ> : k_bwd_main<NTMAX, KTMAX, 0, false, WAVES, SQ>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)lds);
   if (e != hipSuccess) return e;
@@ -612,29 +830,57 @@ hipError_t launch_main_t(const BwdBlock& p, int no_ln, hipStream_t s) {
 
 }  // namespace
 
-size_t bwd_workspace_bytes(int64_t M, int64_t N, int64_t K) { return bwd_ws_layout(M, N, K).total; }
+size_t bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, bool sq) { return bwd_ws_layout(M, N, K, sq).total; }
 
 hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  const BwdWs w = bwd_ws_layout(a.M, a.N, a.K);
+  const BwdWs w = bwd_ws_layout(a.M, a.N, a.K, a.sq);
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
   BwdBlock p;
   p.M = a.M; p.N = (int)a.N; p.K = (int)a.K;
   p.dy = static_cast<const uint16_t*>(a.dy);
-  p.qx = a.qx; p.sx = a.sx; p.mean = a.mean; p.rstd = a.rstd;
-  p.qw = a.qw; p.sw = a.sw;
+  p.qx = a.qx; p.mean = a.mean; p.rstd = a.rstd;
+  p.qw = a.qw;
+  p.sx = a.sq ? nullptr : static_cast<const float*>(a.sx);
+  p.sw = a.sq ? nullptr : static_cast<const float*>(a.sw);
+  p.sx8 = a.sq ? static_cast<const uint8_t*>(a.sx) : nullptr;
+  p.sw8 = a.sq ? static_cast<const uint8_t*>(a.sw) : nullptr;
   p.bias = static_cast<const uint16_t*>(a.bias);
   p.gamma = static_cast<const uint16_t*>(a.gamma);
   p.qw_row = a.qw_row; p.sw_row = a.sw_row;
   p.dx = static_cast<uint16_t*>(a.dx);
-  p.dz = a.dz ? a.dz : reinterpret_cast<float*>(ws + w.dz);
-  p.dz_codes = a.dz_codes; p.dz_scales = a.dz_scales;
+  p.dz = a.dz ? a.dz : (a.sq ? nullptr : reinterpret_cast<float*>(ws + w.dz));
+  p.dz_codes = a.dz_codes;
+  p.dz_scales = a.sq ? nullptr : static_cast<float*>(a.dz_scales);
   p.part = reinterpret_cast<float*>(ws + w.part);
   p.nblocks = w.nblocks;
   p.qwi = ws + w.qwi;
   p.qwri = ws + w.qwri;
+  p.sdz = a.sq ? (a.dz_scales ? static_cast<uint8_t*>(a.dz_scales) : ws + w.sdz) : nullptr;
+  p.dzt = ws + w.dzt;
+  p.nchm = (a.M + 127) / 128;
 
   hipError_t e;
+  if (a.sq) {
+    // square-block recipe: the forward's codes, rearranged (no requantization),
+    // the main kernel (dZ quantized once, in blocks), the wgrad on the codes
+    // and the final sums; N, K <= 512
+    uint8_t* xt = ws + w.xt;
+    if ((e = launch_relayout_sq(a.qw, a.N, a.K, ws + w.qwi, ws + w.qwri, a.qx, a.M, xt, s)) != hipSuccess) return e;
+    if ((e = launch_main_t<4, 4, 8, true>(p, a.no_ln, s)) != hipSuccess) return e;
+    float* wpart = reinterpret_cast<float*>(ws + w.wpart);
+    dim3 g((unsigned)((a.N + 127) / 128), (unsigned)((a.K + 127) / 128), (unsigned)w.nsplit);
+    hipLaunchKernelGGL(k_wgrad<true>, g, dim3(256), 0, s, p.dzt, xt, a.M, (int)a.N, (int)a.K,
+                       (int64_t)(kWgSplitRows / 128), wpart, p.sdz, p.sx8);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t tot = a.K * a.N;
+    const int nf = (int)((tot + 255) / 256);
+    const int nv = (a.dgamma || a.dbeta || a.dbias) ? (int)((a.N + 15) / 16) : 0;
+    hipLaunchKernelGGL(k_finalize_vectors, dim3((unsigned)(nf + nv)), dim3(256), 0, s, wpart, w.nsplit,
+                       (const float*)nullptr, (const float*)nullptr, (int)a.K, (int)a.N, a.dw, nf, p.part, w.nblocks,
+                       a.dgamma, a.dbeta, a.dbias);
+    return hipGetLastError();
+  }
   // both weights into the fragment-interleaved order, in one launch
   if ((e = launch_relayout2(a.no_ln ? nullptr : a.qw, a.N, a.K, ws + w.qwi, a.qw_row, a.K, a.N, ws + w.qwri, s)) !=
       hipSuccess)
@@ -665,8 +911,8 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
 
   float* wpart = reinterpret_cast<float*>(ws + w.wpart);
   dim3 g((unsigned)((a.N + 127) / 128), (unsigned)((a.K + 127) / 128), (unsigned)w.nsplit);
-  hipLaunchKernelGGL(k_wgrad, g, dim3(256), 0, s, dzt, xt, a.M, (int)a.N, (int)a.K, (int64_t)(kWgSplitRows / 128),
-                     wpart);
+  hipLaunchKernelGGL(k_wgrad<false>, g, dim3(256), 0, s, dzt, xt, a.M, (int)a.N, (int)a.K,
+                     (int64_t)(kWgSplitRows / 128), wpart, (const uint8_t*)nullptr, (const uint8_t*)nullptr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t tot = a.K * a.N;

@@ -86,13 +86,14 @@ hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s);
 struct BwdLaunch {
   int64_t M, N, K;
   int no_ln;
+  bool sq;  // square-block recipe: sx, sw, dz_scales are E8M0 grids of 32 x 32 blocks
   const void* dy;
   const uint8_t* qx;
-  const float* sx;
+  const void* sx;
   const float* mean;
   const float* rstd;
   const uint8_t* qw;
-  const float* sw;
+  const void* sw;
   const void* bias;
   const void* gamma;
   const void* x;
@@ -105,10 +106,10 @@ struct BwdLaunch {
   float* dbias;
   float* dz;
   uint8_t* dz_codes;
-  float* dz_scales;
+  void* dz_scales;
   void* workspace;
 };
-size_t bwd_workspace_bytes(int64_t M, int64_t N, int64_t K);
+size_t bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, bool sq);
 hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s);
 
 // ---- grouped -------------------------------------------------------------

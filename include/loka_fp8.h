@@ -265,8 +265,23 @@ loka_status loka_gemm_fp8_ln(const loka_fwd_args* args, void* stream);
  *   All reductions over M are deterministic (fixed-order two-stage sums).
  * Requirements: as loka_gemm_fp8_ln with x_mode ROW, plus K % 64 == 0,
  *   K <= 1024 and M % 16 == 0.
+ *
+ * With flags & LOKA_BWD_MX32_SQ, the backward of the square-block forward
+ * (x_mode MX32_SQ; GEM "Low Precision Flash Attention", Block-wise
+ * Quantization: 32 x 32 blocks are transpose-invariant, so each tensor is
+ * quantized once and serves every GEMM that reads it):
+ *   qx, sx   X's codes [M, K] and E8M0 scales uint8[M/32][K/32] (the
+ *            forward's input, read transposed by the wgrad);
+ *   qw, sw   W's codes [N, K] (transpose_out 1) and scales uint8[K/32][N/32]
+ *            (read as they are for Z, transposed for the dgrad);
+ *   dZ is quantized once, e5m2 in 32 x 32 blocks:
+ *     dX = dequant(q(dZ)) . dequant(q(W))^T,  dW = dequant(q(X))^T . dequant(q(dZ));
+ *   x, qw_row and sw_row are unused (may be NULL); dz_scales, if given,
+ *   receives dZ's scales uint8[M/32][N/32].  Needs M % 32 == 0, N <= 512
+ *   and K <= 512; mean and rstd unless LOKA_BWD_NO_LN.
  * ---------------------------------------------------------------------- */
 #define LOKA_BWD_NO_LN 1
+#define LOKA_BWD_MX32_SQ 2
 
 typedef struct {
   int64_t M, N, K;
@@ -274,11 +289,11 @@ typedef struct {
   int32_t reserved;
   const void* dy;
   const uint8_t* qx;
-  const float* sx;
+  const void* sx; /* float[M] (ROW) or uint8[M/32][K/32] (MX32_SQ) */
   const float* mean;
   const float* rstd;
   const uint8_t* qw;
-  const float* sw;
+  const void* sw; /* float[N] (ROW) or uint8[K/32][N/32] (MX32_SQ) */
   const void* bias;
   const void* gamma;
   const void* x;
@@ -291,7 +306,7 @@ typedef struct {
   float* dbias;
   float* dz;
   uint8_t* dz_codes;
-  float* dz_scales;
+  void* dz_scales; /* float[M] (ROW) or uint8[M/32][N/32] (MX32_SQ) */
   void* workspace;
   size_t workspace_bytes;
 } loka_bwd_args;

@@ -169,13 +169,24 @@ def _bwd(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(flags=2), 1), (dict(K=96), 2), (dict(K=2048), 2), (dict(M=24), 2), (dict(N=96), 2),
+    (dict(flags=4), 1), (dict(K=96), 2), (dict(K=2048), 2), (dict(M=24), 2), (dict(N=96), 2),
+    # the square-block recipe: N, K <= 512, M % 32 == 0, the codes required, mean/rstd unless NO_LN
+    (dict(flags=2, N=640), 2), (dict(flags=2, K=576), 2), (dict(flags=2, M=48), 2), (dict(flags=2, qx=None), 1),
+    (dict(flags=2, sw=None), 1), (dict(flags=2, rstd=None), 1), (dict(flags=2, x=None, qw_row=None, sw_row=None), 4),
+    (dict(flags=3, mean=None, rstd=None, x=None), 4),
     (dict(dy=None), 1), (dict(dw=None), 1), (dict(mean=None), 1), (dict(qx=None), 1),
     (dict(flags=1, dgamma=FAKE), 1), (dict(dz=FAKE + 4), 3),
     ({}, 4),  # the backward always needs its workspace
 ])
 def test_backward_validation(lib, kw, status):
     assert _call(lib, "loka_gemm_fp8_bwd", _bwd(**kw)) == status
+
+
+def test_square_backward_workspace_is_smaller(lib):
+    # no fp32 dZ and no column maxima or scales: only the codes and block scales
+    row = lib.loka_gemm_fp8_bwd_workspace_size(ctypes.byref(_bwd(M=16384, N=512, K=512)))
+    sq = lib.loka_gemm_fp8_bwd_workspace_size(ctypes.byref(_bwd(M=16384, N=512, K=512, flags=2)))
+    assert row - sq >= 16384 * 512 * 4
 
 
 def test_backward_literal_reading_needs_no_context(lib):

@@ -82,3 +82,134 @@ def test_square_forward_rejects_unsupported(lib):
     with pytest.raises((LokaError, ValueError)):
         lib.loka_gemm_fp8_ln(x, qw, sw, x_mode="mx32_sq", x_scales=torch.zeros((1, 2), dtype=torch.uint8,
                                                                                   device="cuda"))
+
+
+# ---- backward ---------------------------------------------------------------
+# The square-block backward (flag LOKA_BWD_MX32_SQ) takes the forward's codes
+# as they are and quantizes dZ once in 32 x 32 e5m2 blocks.  Literal reading
+# (dY is dZ): the codes and block scales are bit-exact and dX, dW, dbias are
+# checked to the backward tests' tolerances.  LayerNorm reading: the kernel's
+# dZ is fp32 against the oracle's fp64, so a code within that error of an
+# e5m2 midpoint (or a block whose max-abs is that close to a power of two) may
+# round either way; those are masked and bounded as in test_gpu_backward.py.
+
+from oracle import backward, codec  # noqa: E402
+from tests.gpu_helpers import bf16_ulp  # noqa: E402
+from tests.test_gpu_backward import ambiguous, check_colsum  # noqa: E402
+
+TAU = 1e-3
+MFMA_WINDOW = 2.0 ** -14
+E5 = codec.E5M2
+
+
+def run_square_bwd(lib, c, no_ln, fast_check=True):
+    x, w, dy = bf16_dev(c["x"]), bf16_dev(c["w"]), bf16_dev(c["dy"])
+    bias, gamma, beta = bf16_dev(c["bias"]), bf16_dev(c["gamma"]), bf16_dev(c["beta"])
+    qx, sx, _ = lib.loka_quant_fp8(x, fmt="e4m3", mode="mx32_sq")
+    qw, sw, _ = lib.loka_quant_fp8(w, fmt="e4m3", mode="mx32_sq", transpose_out=True)
+    ctx = {"qx": qx, "sx": sx, "qw": qw, "sw": sw}
+    if not no_ln:
+        f = lib.loka_gemm_fp8_ln(qx, qw, sw, bias, gamma, beta, x_mode="mx32_sq", x_scales=sx, want_stats=True)
+        ctx["mean"], ctx["rstd"] = f["mean"], f["rstd"]
+    out = lib.loka_gemm_fp8_bwd(dy, None, None, None, ctx=ctx, bias=bias, gamma=gamma, no_ln=no_ln, want_dz=True,
+                                want_dz_codes=True, square=True)
+    fast = None
+    if fast_check:  # without the optional outputs: the configuration the benchmark times
+        fast = lib.loka_gemm_fp8_bwd(dy, None, None, None, ctx=ctx, bias=bias, gamma=gamma, no_ln=no_ln,
+                                     square=True)
+    torch.cuda.synchronize()
+    res = {k: host(v) for k, v in out.items()}
+    if fast is not None:
+        for k in ("dx", "dw", "dbias"):
+            np.testing.assert_array_equal(host(fast[k]), res[k], err_msg=f"{k} without the optional outputs")
+    return res
+
+
+def _deq(q, s, fmt):
+    return quant.dequantize(q, s, quant.MX32_SQ, fmt)
+
+
+def check_dx_sq(g, o, flip=None):
+    dx = codec.bf16_to_f64(g["dx"])
+    rms = np.sqrt((o["dx"] ** 2).mean(axis=1, keepdims=True))
+    term = MFMA_WINDOW * (np.abs(_deq(o["q_dz"], o["s_dz"], E5)) @ np.abs(_deq(o["q_w"], o["s_w"], E4M3)).T)
+    tol = 2 * bf16_ulp(o["dx"]) + 1e-3 * rms + term + (0 if flip is None else flip)
+    err = np.abs(dx - o["dx"])
+    assert np.all(err <= tol), f"dX: {int((err > tol).sum())} outside tolerance; worst {np.max(err / tol):.3f} x tol"
+    return float(np.max(err / rms))
+
+
+def check_dw_sq(g, o, flip=None):
+    rms = np.sqrt((o["dw"] ** 2).mean())
+    term = MFMA_WINDOW * (np.abs(_deq(o["q_x"], o["s_x"], E4M3)).T @ np.abs(_deq(o["q_dz"], o["s_dz"], E5)))
+    tol = 1e-3 * rms + term + (0 if flip is None else flip)
+    err = np.abs(g["dw"].astype(np.float64) - o["dw"])
+    assert np.all(err <= tol), f"dW: worst {np.max(err / tol):.3f} x tol"
+    return float(err.max() / rms)
+
+
+def test_square_backward_literal_full_size(lib):
+    c = outlier_case(dy=True)
+    g = run_square_bwd(lib, c, no_ln=True)
+    o = backward.gemm_ln_backward_sq(c["x"], c["w"], c["dy"], no_ln=True)
+    np.testing.assert_array_equal(g["dz"], o["dz"].astype(np.float32))
+    np.testing.assert_array_equal(g["dz_codes"], o["q_dz"])
+    np.testing.assert_array_equal(g["dz_scales"], o["s_dz"])
+    ex = check_dx_sq(g, o)
+    ew = check_dw_sq(g, o)
+    check_colsum(g["dbias"], o["dbias"], np.abs(codec.bf16_to_f64(c["dy"])).sum(axis=0), "dbias")
+    print(f"square literal: dX err/rms {ex:.2e}  dW err/rms {ew:.2e}")
+
+
+@pytest.mark.parametrize("M,K,N", [(16384, 512, 512), (1056, 192, 320), (64, 64, 64), (96, 512, 128),
+                                   (160, 256, 448)])
+def test_square_backward_layernorm(lib, M, K, N):
+    if M == 16384:
+        c = outlier_case(dy=True)
+    else:
+        c = forward_case(M, K, N, seed=M + 2 * K + N, x_dist="student_t3_outliers", gamma_var=0.1, beta_var=0.1,
+                         dy_var=1e-3)
+    g = run_square_bwd(lib, c, no_ln=False, fast_check=(M != 16384))
+    o = backward.gemm_ln_backward_sq(c["x"], c["w"], c["dy"], c["bias"], c["gamma"], c["beta"])
+    dz_ref = o["dz"]
+    rms_row = np.sqrt((dz_ref ** 2).mean(axis=1, keepdims=True))
+    dz_tol = TAU * np.maximum(np.abs(dz_ref), rms_row)
+    dz_err = np.abs(g["dz"].astype(np.float64) - dz_ref)
+    assert np.all(dz_err <= dz_tol), f"dZ: worst {np.max(dz_err / dz_tol):.3f} x tol"
+
+    # block scales: unique unless the block max-abs is within the dZ error of a power of two
+    am = quant.amax(dz_ref, quant.MX32_SQ)
+    am_tol = quant.amax(dz_tol, quant.MX32_SQ)
+    lo, hi = np.floor(np.log2(np.maximum(am - am_tol, 1e-300))), np.floor(np.log2(am + am_tol))
+    amb_s = lo != hi
+    sdiff = g["dz_scales"] != o["s_dz"]
+    assert not np.any(sdiff & ~amb_s), f"{int((sdiff & ~amb_s).sum())} block scales differ away from a boundary"
+    assert np.all(np.abs(g["dz_scales"].astype(int) - o["s_dz"].astype(int)) <= 1)
+    # codes: unique away from midpoints within blocks of equal scale
+    e_ref = np.repeat(np.repeat(codec.decode_e8m0(o["s_dz"]), 32, axis=0), 32, axis=1)
+    t_ref = dz_ref / e_ref
+    amb, gap = ambiguous(t_ref, (dz_tol + 2 * TAU * np.abs(dz_ref)) / e_ref)
+    blk_amb = np.repeat(np.repeat(sdiff, 32, axis=0), 32, axis=1)
+    differ = g["dz_codes"] != o["q_dz"]
+    assert not np.any(differ & ~amb & ~blk_amb), f"{int((differ & ~amb & ~blk_amb).sum())} dZ codes differ"
+    # bound of a flipped value (decoded difference), a flipped block: both scales' rounding
+    flip_v = np.where(blk_amb, 0.5 * np.abs(dz_ref) + 2.0 * e_ref * gap, amb * gap * e_ref)
+    wq = np.abs(_deq(o["q_w"], o["s_w"], E4M3))       # [K, N]
+    xq = np.abs(_deq(o["q_x"], o["s_x"], E4M3))       # [M, K]
+    ex = check_dx_sq(g, o, flip_v @ wq.T * (1 + 2 * TAU) + 2 * TAU * np.abs(o["dx"]))
+    ew = check_dw_sq(g, o, xq.T @ flip_v * (1 + 2 * TAU) + 2 * TAU * np.abs(o["dw"]))
+    dy = codec.bf16_to_f64(c["dy"])
+    fwd = forward.gemm_ln_forward(c["x"], c["w"], c["bias"], c["gamma"], c["beta"], recipe="mx32_sq")
+    yhat = (fwd["z"] - fwd["mean"][:, None]) * fwd["rstd"][:, None]
+    check_colsum(g["dgamma"], o["dgamma"], np.abs(dy * yhat).sum(axis=0), "dgamma")
+    check_colsum(g["dbeta"], o["dbeta"], np.abs(dy).sum(axis=0), "dbeta")
+    check_colsum(g["dbias"], o["dbias"], np.abs(dz_ref).sum(axis=0), "dbias")
+    print(f"square LN {M}x{K}x{N}: dZ worst {np.max(dz_err / dz_tol):.3f} x tol, {int(differ.sum())} code flips "
+          f"of {int(amb.sum())} ambiguous, {int(sdiff.sum())} scale flips; dX err/rms {ex:.2e}; dW err/rms {ew:.2e}")
+
+
+def test_square_backward_rejects_unsupported(lib):
+    from fp8_precision_gemm_amd import LokaError
+    c = forward_case(64, 64, 640, seed=1, dy_var=1e-3)
+    with pytest.raises(LokaError):  # N > 512 is outside the square-block backward
+        run_square_bwd(lib, c, no_ln=True, fast_check=False)
