@@ -45,7 +45,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-rows", action="store_true", help="skip the other workloads")
     p.add_argument("--only", default=None,
-                   help="comma list of workloads to time (for profiling): fwd,tensor,mx,blocknorm,bwd,grouped,copy")
+                   help="comma list of workloads to time (for profiling): "
+                        "fwd,tensor,mx,blocknorm,bwd,square,grouped,copy")
     return p.parse_args()
 
 
@@ -172,6 +173,51 @@ def bench_backward(torch, lk, case, steps, warmup, stream):
     return {"us": per * 1e6, "tflops": flops / per / 1e12, "gbs_min_bytes": nbytes / per / 1e9}
 
 
+def bench_square(torch, lk, case, steps, warmup, stream):
+    """The square-block recipe (one E8M0 per 32 x 32 block): the forward on
+    X's codes (quantized once, as its producer would emit them; that
+    quantization is timed on its own as x_quant_us) and the backward on the
+    forward's codes.  Returns (forward row, backward row)."""
+    M, K, N = case["M"], case["K"], case["N"]
+    x, w, dy = dev_bf16(torch, case["x"]), dev_bf16(torch, case["w"]), dev_bf16(torch, case["dy"])
+    bias, gamma, beta = (dev_bf16(torch, case[k]) for k in ("bias", "gamma", "beta"))
+    qw, sw, _ = lk.loka_quant_fp8(w, mode="mx32_sq", transpose_out=True, stream=stream)
+    qwp, _, _ = lk.loka_quant_fp8(w, mode="mx32_sq", transpose_out="packed", stream=stream)
+    qx, sx, _ = lk.loka_quant_fp8(x, mode="mx32_sq", stream=stream)
+    launches, quants = [], []
+    for i in range(ROTATE):
+        qxi = qx if i == 0 else qx.clone()
+        f, _ = lk.loka_gemm_fp8_ln(qxi, qwp, sw, bias, gamma, beta, x_mode="mx32_sq", x_scales=sx, stream=stream,
+                                   prepare=True, w_packed=True)
+        launches.append(f)
+        xi = x if i == 0 else x.clone()
+        ci, si = torch.empty_like(qx), torch.empty_like(sx)
+        quants.append(lambda xi=xi, ci=ci, si=si: lk.loka_quant_fp8(xi, mode="mx32_sq", codes=ci, scales=si,
+                                                                     stream=stream))
+    torch.cuda.synchronize()
+    secs, n = timed_graph(torch, launches, steps, warmup, stream)
+    per = secs / n
+    qsecs, qn = timed_graph(torch, quants, min(steps, 800), min(warmup, 80), stream)
+    nbytes = M * K + (M // 32) * (K // 32) + N * K + (K // 32) * (N // 32) + 3 * 2 * N + 2 * M * N
+    fwd = {"us": per * 1e6, "tflops": 2.0 * M * N * K / per / 1e12, "gbs": nbytes / per / 1e9, "bytes": nbytes,
+           "x_quant_us": qsecs / qn * 1e6}
+    f = lk.loka_gemm_fp8_ln(qx, qw, sw, bias, gamma, beta, x_mode="mx32_sq", x_scales=sx, want_stats=True,
+                            stream=stream)
+    ctx = {"qx": qx, "sx": sx, "qw": qw, "sw": sw, "mean": f["mean"], "rstd": f["rstd"]}
+    launches = []
+    for i in range(4):
+        dyi = dy if i == 0 else dy.clone()
+        fn, _ = lk.loka_gemm_fp8_bwd(dyi, None, None, None, ctx=ctx, bias=bias, gamma=gamma, stream=stream,
+                                     prepare=True, square=True)
+        launches.append(fn)
+    torch.cuda.synchronize()
+    secs, n = timed_graph(torch, launches, max(40, steps // 20), max(8, warmup // 20), stream)
+    per = secs / n
+    nbytes = 2 * M * N + M * K + 2 * M * K + 4 * K * N  # dY, qX, dX, dW (minimum)
+    bwd = {"us": per * 1e6, "tflops": 2.0 * M * N * K * 3 / per / 1e12, "gbs_min_bytes": nbytes / per / 1e9}
+    return fwd, bwd
+
+
 def bench_grouped(torch, lk, groups, steps, warmup, stream):
     dg = []
     flops = 0.0
@@ -273,6 +319,13 @@ def main():
         r = bench_backward(torch, lk, case, args.steps, args.warmup, stream)
         rows["bwd_16384x512x512"] = {k: round(v, 3) for k, v in r.items()}
         print(f"[bench] backward: {r['us']:.2f} us", file=sys.stderr, flush=True)
+    if not args.no_rows and want("square"):
+        f, b = bench_square(torch, lk, case, max(200, args.steps // 4), max(20, args.warmup // 4), stream)
+        rows["square_fwd_16384x512x512"] = {k: round(v, 3) for k, v in f.items()}
+        rows["square_fwd_16384x512x512"]["hbm_frac"] = round(f["gbs"] / PEAK_HBM_GBS, 4)
+        rows["square_bwd_16384x512x512"] = {k: round(v, 3) for k, v in b.items()}
+        print(f"[bench] square forward: {f['us']:.2f} us (X quantization {f['x_quant_us']:.2f} us); "
+              f"square backward: {b['us']:.2f} us", file=sys.stderr, flush=True)
     if not args.no_rows and want("grouped"):
         r = bench_grouped(torch, lk, workloads.grouped_case(), args.steps, args.warmup, stream)
         rows["grouped_64x8192"] = {k: round(v, 3) for k, v in r.items()}
