@@ -25,9 +25,10 @@ Modules:
   backward  LayerNorm backward, e5m2 dZ, dgrad and wgrad in fp64
   grouped   the grouped forward as a list of independent forwards
   mere      mean element-wise relative error report ([LoKA] section II-C)
+  dispatch  the Dispatch runtime's recipe selection rule ([LoKA] section III-C)
 
 Parity unpinned: nothing.  Every function is pinned by tests/test_oracle_*.py
 against hand-worked encodings, closed forms, invariants or brute force.
 """
 
-from . import codec, quant, forward, backward, grouped, mere  # noqa: F401
+from . import codec, quant, forward, backward, grouped, mere, dispatch  # noqa: F401
