@@ -15,7 +15,8 @@ import torch
 __all__ = [
     "LokaError", "library", "library_path", "abi_version",
     "loka_quant_fp8", "loka_gemm_fp8_ln", "loka_gemm_fp8_bwd", "loka_grouped_gemm_fp8_ln",
-    "QuantArgs", "FwdArgs", "BwdArgs", "GroupDesc", "GroupedArgs",
+    "loka_mere_z", "loka_dispatch_select",
+    "QuantArgs", "FwdArgs", "BwdArgs", "GroupDesc", "GroupedArgs", "MereArgs", "DispatchCandidate",
     "E4M3", "E5M2", "MODES", "STATUS",
 ]
 
@@ -67,6 +68,15 @@ class GroupedArgs(ctypes.Structure):
                 ("groups", ctypes.POINTER(GroupDesc)), ("workspace", c_vp), ("workspace_bytes", c_sz)]
 
 
+class MereArgs(ctypes.Structure):
+    _fields_ = [("M", c_i64), ("N", c_i64), ("K", c_i64), ("S", c_i64), ("x", c_vp), ("w", c_vp), ("bias", c_vp),
+                ("z", c_vp), ("rows", c_vp), ("out", c_vp), ("workspace", c_vp), ("workspace_bytes", c_sz)]
+
+
+class DispatchCandidate(ctypes.Structure):
+    _fields_ = [("us", ctypes.c_double), ("mere", ctypes.c_double)]
+
+
 class LokaError(RuntimeError):
     def __init__(self, status, detail):
         self.status = status
@@ -85,12 +95,14 @@ def library():
                                "`python -m fp8_precision_gemm_amd.build` (no fallback exists)")
         lib = ctypes.CDLL(library_path)
         for name, argt in [("loka_quant_fp8", QuantArgs), ("loka_gemm_fp8_ln", FwdArgs),
-                           ("loka_gemm_fp8_bwd", BwdArgs), ("loka_grouped_gemm_fp8_ln", GroupedArgs)]:
+                           ("loka_gemm_fp8_bwd", BwdArgs), ("loka_grouped_gemm_fp8_ln", GroupedArgs),
+                           ("loka_mere_z", MereArgs)]:
             f = getattr(lib, name)
             f.argtypes = [ctypes.POINTER(argt), c_vp]
             f.restype = c_i32
         for name, argt in [("loka_quant_workspace_size", QuantArgs), ("loka_gemm_fp8_ln_workspace_size", FwdArgs),
-                           ("loka_gemm_fp8_bwd_workspace_size", BwdArgs), ("loka_grouped_workspace_size", GroupedArgs)]:
+                           ("loka_gemm_fp8_bwd_workspace_size", BwdArgs), ("loka_grouped_workspace_size", GroupedArgs),
+                           ("loka_mere_workspace_size", MereArgs)]:
             f = getattr(lib, name)
             f.argtypes = [ctypes.POINTER(argt)]
             f.restype = c_sz
@@ -98,6 +110,9 @@ def library():
         lib.loka_status_string.restype = ctypes.c_char_p
         lib.loka_status_string.argtypes = [c_i32]
         lib.loka_abi_version.restype = c_i32
+        lib.loka_dispatch_select.argtypes = [ctypes.POINTER(DispatchCandidate), c_i32, ctypes.c_double,
+                                             ctypes.c_double, ctypes.c_double, ctypes.POINTER(c_i32)]
+        lib.loka_dispatch_select.restype = c_i32
         _lib = lib
     return _lib
 
@@ -371,3 +386,41 @@ def loka_grouped_gemm_fp8_ln(groups, eps=1e-5, want_z=False, workspace=None, str
         return launch, outs
     launch()
     return outs
+
+
+def loka_mere_z(x, w, z, rows, bias=None, stream=None):
+    """MERE of a candidate's Z (fp32 [M, N]) against the fp32 reference X W + b
+    of the unquantized bf16 operands x [M, K] and w [K, N], over the rows in
+    `rows` (int64 CUDA tensor).  Returns (mere, count of nonzero reference
+    entries); synchronizes to read them."""
+    M, K = x.shape
+    N = w.shape[1]
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(w, torch.bfloat16, (K, N), "w")
+    _need(z, torch.float32, (M, N), "z")
+    if rows.dtype != torch.int64 or rows.dim() != 1 or not rows.is_contiguous():
+        raise ValueError("rows must be a contiguous 1-D int64 tensor")
+    out = torch.zeros(3, dtype=torch.float64, device=x.device)
+    a = MereArgs(M=M, N=N, K=K, S=rows.numel(), x=_ptr(x), w=_ptr(w), bias=_ptr(bias), z=_ptr(z), rows=_ptr(rows),
+                 out=_ptr(out))
+    lib = library()
+    nb = lib.loka_mere_workspace_size(ctypes.byref(a))
+    ws = _workspace(nb, x.device, None)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = nb if ws is None else ws.numel()
+    _check(lib.loka_mere_z(ctypes.byref(a), _stream(stream)))
+    o = out.cpu().tolist()
+    if o[2] != 0:
+        raise ValueError(f"{int(o[2])} sampled row indices outside [0, {M})")
+    return o[0], int(o[1])
+
+
+def loka_dispatch_select(candidates, baseline_us, mere_max=0.2, min_speedup=1.05):
+    """Index of the recipe Dispatch chooses among (time_us, mere) pairs, or -1
+    to keep the high-precision path (host only)."""
+    n = len(candidates)
+    arr = (DispatchCandidate * max(1, n))(*[DispatchCandidate(float(u), float(e)) for u, e in candidates])
+    choice = c_i32(-2)
+    _check(library().loka_dispatch_select(arr, n, float(baseline_us), float(mere_max), float(min_speedup),
+                                          ctypes.byref(choice)))
+    return choice.value

@@ -252,6 +252,51 @@ loka_status loka_gemm_fp8_bwd(const loka_bwd_args* a, void* stream) {
 }
 
 // ---------------------------------------------------------------------------
+size_t loka_mere_workspace_size(const loka_mere_args* a) {
+  if (a == nullptr || a->S <= 0) return 0;
+  return loka::mere_workspace_bytes(a->S);
+}
+
+loka_status loka_mere_z(const loka_mere_args* a, void* stream) {
+  REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
+  REQUIRE(a->M >= 1 && a->N >= 1 && a->K >= 1 && a->S >= 1, LOKA_ERR_INVALID_ARG, "M, N, K and S must be >= 1");
+  REQUIRE(a->K <= loka::mere_max_k() && a->N <= 8192, LOKA_ERR_UNSUPPORTED, "MERE needs K <= %d and N <= 8192",
+          loka::mere_max_k());
+  REQUIRE(a->x && a->w && a->z && a->rows && a->out, LOKA_ERR_INVALID_ARG, "x, w, z, rows and out are required");
+  REQUIRE_ALIGNED(a->x); REQUIRE_ALIGNED(a->w); REQUIRE_ALIGNED(a->bias); REQUIRE_ALIGNED(a->z);
+  REQUIRE_ALIGNED(a->rows); REQUIRE_ALIGNED(a->out);
+  loka_status st;
+  if ((st = check_workspace(loka_mere_workspace_size(a), a->workspace, a->workspace_bytes)) != LOKA_OK) return st;
+  loka::MereLaunch m{a->M, a->N, a->K, a->S, a->x, a->w, a->bias, a->z, a->rows, a->out, a->workspace};
+  return hip_status(loka::launch_mere(m, static_cast<hipStream_t>(stream)), "loka_mere_z");
+}
+
+// The pages' rule, step by step: the accuracy filter, the speed filter, then
+// the shortest time among what passes.
+loka_status loka_dispatch_select(const loka_dispatch_candidate* c, int32_t n, double baseline_us, double mere_max,
+                                 double min_speedup, int32_t* choice) {
+  REQUIRE(choice != nullptr, LOKA_ERR_INVALID_ARG, "choice is NULL");
+  REQUIRE(n >= 0 && (n == 0 || c != nullptr), LOKA_ERR_INVALID_ARG, "bad candidate array");
+  REQUIRE(std::isfinite(baseline_us) && baseline_us > 0.0, LOKA_ERR_INVALID_ARG, "baseline_us must be finite, > 0");
+  REQUIRE(std::isfinite(mere_max) && mere_max > 0.0 && std::isfinite(min_speedup) && min_speedup > 0.0,
+          LOKA_ERR_INVALID_ARG, "thresholds must be finite and > 0");
+  int32_t best = -1;
+  double best_us = 0.0;
+  for (int32_t i = 0; i < n; ++i) {
+    const double us = c[i].us, e = c[i].mere;
+    if (!std::isfinite(us) || !std::isfinite(e) || us <= 0.0) continue;
+    if (!(e < mere_max)) continue;                  // accuracy
+    if (!(baseline_us / us > min_speedup)) continue;  // speed
+    if (best < 0 || us < best_us) {
+      best = i;
+      best_us = us;
+    }
+  }
+  *choice = best;
+  return LOKA_OK;
+}
+
+// ---------------------------------------------------------------------------
 static_assert(sizeof(loka_group_desc) == sizeof(loka::GroupDev), "group descriptor layouts differ");
 
 size_t loka_grouped_workspace_size(const loka_grouped_args* a) {

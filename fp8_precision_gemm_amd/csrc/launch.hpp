@@ -112,6 +112,21 @@ struct BwdLaunch {
 size_t bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, bool sq);
 hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s);
 
+// ---- MERE against the fp32 reference of the linear layer ----------------
+struct MereLaunch {
+  int64_t M, N, K, S;
+  const void* x;       // bf16 [M][K]
+  const void* w;       // bf16 [K][N]
+  const void* bias;    // bf16 [N] or null
+  const float* z;      // the candidate's Z, fp32 [M][N]
+  const int64_t* rows; // device [S]
+  double* out;         // device [3]
+  void* workspace;
+};
+size_t mere_workspace_bytes(int64_t S);
+int mere_max_k();
+hipError_t launch_mere(const MereLaunch& a, hipStream_t s);
+
 // ---- grouped -------------------------------------------------------------
 struct GroupDev {  // one group as the device sees it (copied into the workspace)
   int64_t M, N, K;

@@ -372,6 +372,69 @@ size_t loka_grouped_workspace_size(const loka_grouped_args* args);
 loka_status loka_grouped_gemm_fp8_ln(const loka_grouped_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
+ * loka_mere_z: the error of a candidate recipe's linear-layer output against
+ * the high-precision reference, on sampled rows.
+ *
+ * Source: LoKA section II-C ("Error Analysis": the mean element-wise
+ * relative error, MERE, of a low-precision linear layer against a higher
+ * precision) and section III-C ("Library and Recipe Selection": Dispatch
+ * filters candidates by MERE).
+ *
+ *   x     bf16 [M, K], w bf16 [K, N] (the unquantized operands), bias bf16
+ *         [N] or NULL;
+ *   z     the candidate's output Z = dequant(q(X) q(W)) + bias, fp32 [M, N]
+ *         (loka_gemm_fp8_ln's optional z output);
+ *   rows  DEVICE int64 [S]: the sampled row indices;
+ *   out   DEVICE double[3]: MERE = mean over the sampled rows' entries with
+ *         z_ref != 0 of |z - z_ref| / |z_ref|; the count of those entries;
+ *         the count of row indices outside [0, M) (those rows contribute
+ *         nothing: a caller checks out[2] == 0).
+ * z_ref = X W + b is computed here in fp32 (exact bf16 products, summed in
+ * k order).  Sums are in a fixed order: the result is deterministic.
+ * workspace: loka_mere_workspace_size() bytes (24 S).
+ * Requirements: M, N, K >= 1, K <= 2048, N <= 8192, S >= 1.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t M, N, K, S;
+  const void* x;
+  const void* w;
+  const void* bias;
+  const float* z;
+  const int64_t* rows;
+  double* out;
+  void* workspace;
+  size_t workspace_bytes;
+} loka_mere_args;
+
+size_t loka_mere_workspace_size(const loka_mere_args* args);
+loka_status loka_mere_z(const loka_mere_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
+ * loka_dispatch_select: the Dispatch runtime's choice among measured
+ * candidate recipes for one operation (host only; no GPU work).
+ *
+ * Source: LoKA section III-C ("Library and Recipe Selection"): candidates
+ * are filtered by accuracy (MERE below a conservative threshold, typically
+ * 0.2) and by speed (speedup above a minimum factor, typically 1.05x), and
+ * the one with the highest measured throughput is chosen.
+ *
+ *   cands        HOST array of n {time in us, MERE} (n >= 0);
+ *   baseline_us  the high-precision path's time (> 0): speedup = baseline_us / us;
+ *   mere_max, min_speedup  the thresholds (> 0); both tests are strict;
+ *   choice       out: the index of the shortest time among the candidates
+ *                that pass both filters (the earlier one on equal times),
+ *                or -1 when none does (keep the high-precision path).
+ * Candidates with a non-finite MERE or time, or a time <= 0, never pass.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  double us;
+  double mere;
+} loka_dispatch_candidate;
+
+loka_status loka_dispatch_select(const loka_dispatch_candidate* cands, int32_t n, double baseline_us,
+                                 double mere_max, double min_speedup, int32_t* choice);
+
+/* ------------------------------------------------------------------------
  * Helpers.
  * ---------------------------------------------------------------------- */
 const char* loka_status_string(loka_status s); /* static text, never NULL */
