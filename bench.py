@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--no-rows", action="store_true", help="skip the other workloads")
     p.add_argument("--only", default=None,
                    help="comma list of workloads to time (for profiling): "
-                        "fwd,tensor,mx,blocknorm,bwd,square,grouped,copy")
+                        "fwd,tensor,mx,blocknorm,bwd,square,dispatch,grouped,copy")
     return p.parse_args()
 
 
@@ -326,6 +326,19 @@ def main():
         rows["square_bwd_16384x512x512"] = {k: round(v, 3) for k, v in b.items()}
         print(f"[bench] square forward: {f['us']:.2f} us (X quantization {f['x_quant_us']:.2f} us); "
               f"square backward: {b['us']:.2f} us", file=sys.stderr, flush=True)
+    if not args.no_rows and want("dispatch"):
+        from fp8_precision_gemm_amd.dispatch import dispatch
+        x, w = dev_bf16(torch, case["x"]), dev_bf16(torch, case["w"])
+        vec = [dev_bf16(torch, case[k]) for k in ("bias", "gamma", "beta")]
+        with torch.cuda.stream(stream):
+            d = dispatch(x, w, *vec, reps=max(20, args.steps // 20), warmup=5, stream=stream)
+        rows["dispatch_16384x512x512"] = {
+            "choice": d["choice"], "baseline_us": round(d["baseline_us"], 3),
+            "baseline": "bf16 library linear + LayerNorm",
+            "table": {r["recipe"]: {"us": round(r["us"], 3), "mere": round(r["mere"], 5)} for r in d["table"]}}
+        print(f"[bench] dispatch: {d['choice']} (baseline {d['baseline_us']:.1f} us; "
+              + ", ".join(f"{r['recipe']} {r['us']:.1f} us MERE {r['mere']:.3f}" for r in d["table"]) + ")",
+              file=sys.stderr, flush=True)
     if not args.no_rows and want("grouped"):
         r = bench_grouped(torch, lk, workloads.grouped_case(), args.steps, args.warmup, stream)
         rows["grouped_64x8192"] = {k: round(v, 3) for k, v in r.items()}
