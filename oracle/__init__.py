@@ -26,9 +26,10 @@ Modules:
   grouped   the grouped forward as a list of independent forwards
   mere      mean element-wise relative error report ([LoKA] section II-C)
   dispatch  the Dispatch runtime's recipe selection rule ([LoKA] section III-C)
+  probe     the Probe's input/weight statistics and sampler ([LoKA] section III-A1)
 
 Parity unpinned: nothing.  Every function is pinned by tests/test_oracle_*.py
 against hand-worked encodings, closed forms, invariants or brute force.
 """
 
-from . import codec, quant, forward, backward, grouped, mere, dispatch  # noqa: F401
+from . import codec, quant, forward, backward, grouped, mere, dispatch, probe  # noqa: F401
