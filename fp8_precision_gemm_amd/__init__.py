@@ -15,7 +15,8 @@ import torch
 __all__ = [
     "LokaError", "library", "library_path", "abi_version",
     "loka_quant_fp8", "loka_gemm_fp8_ln", "loka_gemm_fp8_bwd", "loka_grouped_gemm_fp8_ln",
-    "loka_mere_z", "loka_dispatch_select",
+    "loka_mere_z", "loka_dispatch_select", "loka_probe_input_update", "loka_probe_weight_update",
+    "loka_probe_sample_input", "loka_probe_sample_weight",
     "QuantArgs", "FwdArgs", "BwdArgs", "GroupDesc", "GroupedArgs", "MereArgs", "DispatchCandidate",
     "E4M3", "E5M2", "MODES", "STATUS",
 ]
@@ -77,6 +78,29 @@ class DispatchCandidate(ctypes.Structure):
     _fields_ = [("us", ctypes.c_double), ("mere", ctypes.c_double)]
 
 
+c_u64 = ctypes.c_uint64
+
+
+class ProbeInputArgs(ctypes.Structure):
+    _fields_ = [("B", c_i64), ("K", c_i64), ("n_old", c_i64), ("T", c_vp), ("mu", c_vp), ("S", c_vp),
+                ("workspace", c_vp), ("workspace_bytes", c_sz)]
+
+
+class ProbeWeightArgs(ctypes.Structure):
+    _fields_ = [("R", c_i64), ("C", c_i64), ("m", c_f32), ("first", c_i32), ("W", c_vp), ("M", c_vp), ("U", c_vp),
+                ("V", c_vp), ("info", c_vp), ("workspace", c_vp), ("workspace_bytes", c_sz)]
+
+
+class ProbeSampleInputArgs(ctypes.Structure):
+    _fields_ = [("B", c_i64), ("K", c_i64), ("n", c_i64), ("mu", c_vp), ("S", c_vp), ("seed", c_u64), ("out", c_vp),
+                ("info", c_vp), ("workspace", c_vp), ("workspace_bytes", c_sz)]
+
+
+class ProbeSampleWeightArgs(ctypes.Structure):
+    _fields_ = [("R", c_i64), ("C", c_i64), ("M", c_vp), ("U", c_vp), ("V", c_vp), ("seed", c_u64), ("out", c_vp),
+                ("info", c_vp), ("workspace", c_vp), ("workspace_bytes", c_sz)]
+
+
 class LokaError(RuntimeError):
     def __init__(self, status, detail):
         self.status = status
@@ -96,13 +120,20 @@ def library():
         lib = ctypes.CDLL(library_path)
         for name, argt in [("loka_quant_fp8", QuantArgs), ("loka_gemm_fp8_ln", FwdArgs),
                            ("loka_gemm_fp8_bwd", BwdArgs), ("loka_grouped_gemm_fp8_ln", GroupedArgs),
-                           ("loka_mere_z", MereArgs)]:
+                           ("loka_mere_z", MereArgs), ("loka_probe_input_update", ProbeInputArgs),
+                           ("loka_probe_weight_update", ProbeWeightArgs),
+                           ("loka_probe_sample_input", ProbeSampleInputArgs),
+                           ("loka_probe_sample_weight", ProbeSampleWeightArgs)]:
             f = getattr(lib, name)
             f.argtypes = [ctypes.POINTER(argt), c_vp]
             f.restype = c_i32
         for name, argt in [("loka_quant_workspace_size", QuantArgs), ("loka_gemm_fp8_ln_workspace_size", FwdArgs),
                            ("loka_gemm_fp8_bwd_workspace_size", BwdArgs), ("loka_grouped_workspace_size", GroupedArgs),
-                           ("loka_mere_workspace_size", MereArgs)]:
+                           ("loka_mere_workspace_size", MereArgs),
+                           ("loka_probe_input_workspace_size", ProbeInputArgs),
+                           ("loka_probe_weight_workspace_size", ProbeWeightArgs),
+                           ("loka_probe_sample_input_workspace_size", ProbeSampleInputArgs),
+                           ("loka_probe_sample_weight_workspace_size", ProbeSampleWeightArgs)]:
             f = getattr(lib, name)
             f.argtypes = [ctypes.POINTER(argt)]
             f.restype = c_sz
@@ -424,3 +455,87 @@ def loka_dispatch_select(candidates, baseline_us, mere_max=0.2, min_speedup=1.05
     _check(library().loka_dispatch_select(arr, n, float(baseline_us), float(mere_max), float(min_speedup),
                                           ctypes.byref(choice)))
     return choice.value
+
+
+# ---- the Probe's statistics ---------------------------------------------------
+
+def _run(fn_name, size_name, a, dev, stream):
+    lib = library()
+    nb = getattr(lib, size_name)(ctypes.byref(a))
+    ws = _workspace(nb, dev, None)
+    a.workspace = _ptr(ws)
+    a.workspace_bytes = nb if ws is None else ws.numel()
+    _check(getattr(lib, fn_name)(ctypes.byref(a), _stream(stream)))
+    return ws
+
+
+def _check_info(info, what):
+    bad = info.cpu().tolist()
+    if any(bad):
+        raise LokaError(2, f"{what}: Cholesky pivot not positive (status {bad})")
+
+
+def loka_probe_input_update(T, state=None, stream=None):
+    """Merge the batch T (bf16 [B, K]) into state {"n", "mu" fp32 [K], "S" fp32
+    [K, K]} (a new state when None); returns the state (updated in place)."""
+    B, K = T.shape
+    _need(T, torch.bfloat16, (B, K), "T")
+    if state is None:
+        state = {"n": 0, "mu": torch.zeros(K, dtype=torch.float32, device=T.device),
+                 "S": torch.zeros((K, K), dtype=torch.float32, device=T.device)}
+    a = ProbeInputArgs(B=B, K=K, n_old=state["n"], T=_ptr(T), mu=_ptr(state["mu"]), S=_ptr(state["S"]))
+    ws = _run("loka_probe_input_update", "loka_probe_input_workspace_size", a, T.device, stream)
+    state["n"] += B
+    state["_keep"] = ws  # the workspace lives until the stream has used it
+    return state
+
+
+def loka_probe_weight_update(W, state=None, m=0.99, stream=None, check=True):
+    """One flip-flop update of state {"M", "U", "V"} (fp32) with W (bf16 [R, C]);
+    the first call (state None) initializes.  check: synchronize and raise if
+    a Cholesky factorization failed."""
+    R, C = W.shape
+    _need(W, torch.bfloat16, (R, C), "W")
+    first = state is None
+    if first:
+        dev = W.device
+        state = {"M": torch.empty((R, C), dtype=torch.float32, device=dev),
+                 "U": torch.empty((R, R), dtype=torch.float32, device=dev),
+                 "V": torch.empty((C, C), dtype=torch.float32, device=dev),
+                 "info": torch.zeros(2, dtype=torch.int32, device=dev)}
+    a = ProbeWeightArgs(R=R, C=C, m=m, first=1 if first else 0, W=_ptr(W), M=_ptr(state["M"]), U=_ptr(state["U"]),
+                        V=_ptr(state["V"]), info=_ptr(state["info"]))
+    state["_keep"] = _run("loka_probe_weight_update", "loka_probe_weight_workspace_size", a, W.device, stream)
+    if check and not first:
+        _check_info(state["info"], "loka_probe_weight_update")
+    return state
+
+
+def loka_probe_sample_input(state, B, seed, stream=None, check=True):
+    """B rows sampled from the tracked input distribution: bf16 [B, K]."""
+    K = state["mu"].numel()
+    dev = state["mu"].device
+    out = torch.empty((B, K), dtype=torch.bfloat16, device=dev)
+    info = torch.zeros(1, dtype=torch.int32, device=dev)
+    a = ProbeSampleInputArgs(B=B, K=K, n=state["n"], mu=_ptr(state["mu"]), S=_ptr(state["S"]), seed=seed,
+                             out=_ptr(out), info=_ptr(info))
+    ws = _run("loka_probe_sample_input", "loka_probe_sample_input_workspace_size", a, dev, stream)
+    if check:
+        _check_info(info, "loka_probe_sample_input")
+    del ws
+    return out
+
+
+def loka_probe_sample_weight(state, seed, stream=None, check=True):
+    """A weight sampled from the tracked matrix-normal: bf16 [R, C]."""
+    R, C = state["M"].shape
+    dev = state["M"].device
+    out = torch.empty((R, C), dtype=torch.bfloat16, device=dev)
+    info = torch.zeros(2, dtype=torch.int32, device=dev)
+    a = ProbeSampleWeightArgs(R=R, C=C, M=_ptr(state["M"]), U=_ptr(state["U"]), V=_ptr(state["V"]), seed=seed,
+                              out=_ptr(out), info=_ptr(info))
+    ws = _run("loka_probe_sample_weight", "loka_probe_sample_weight_workspace_size", a, dev, stream)
+    if check:
+        _check_info(info, "loka_probe_sample_weight")
+    del ws
+    return out

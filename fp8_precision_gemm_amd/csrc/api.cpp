@@ -271,6 +271,82 @@ loka_status loka_mere_z(const loka_mere_args* a, void* stream) {
   return hip_status(loka::launch_mere(m, static_cast<hipStream_t>(stream)), "loka_mere_z");
 }
 
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int64_t kProbeMaxDim = 2048;
+bool probe_dim_ok(int64_t d) { return d >= 1 && d <= kProbeMaxDim; }
+}  // namespace
+
+size_t loka_probe_input_workspace_size(const loka_probe_input_args* a) {
+  if (a == nullptr || a->B < 1 || !probe_dim_ok(a->K)) return 0;
+  return loka::probe_input_ws(a->B, a->K);
+}
+loka_status loka_probe_input_update(const loka_probe_input_args* a, void* stream) {
+  REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
+  REQUIRE(a->B >= 1 && a->n_old >= 0, LOKA_ERR_INVALID_ARG, "B >= 1 and n_old >= 0 are required");
+  REQUIRE(probe_dim_ok(a->K), LOKA_ERR_UNSUPPORTED, "the Probe needs 1 <= K <= %lld", (long long)kProbeMaxDim);
+  REQUIRE(a->T && a->mu && a->S, LOKA_ERR_INVALID_ARG, "T, mu and S are required");
+  REQUIRE_ALIGNED(a->T); REQUIRE_ALIGNED(a->mu); REQUIRE_ALIGNED(a->S);
+  loka_status st;
+  if ((st = check_workspace(loka_probe_input_workspace_size(a), a->workspace, a->workspace_bytes)) != LOKA_OK)
+    return st;
+  loka::ProbeInputLaunch l{a->B, a->K, a->n_old, a->T, a->mu, a->S, a->workspace};
+  return hip_status(loka::probe_input_update(l, static_cast<hipStream_t>(stream)), "loka_probe_input_update");
+}
+
+size_t loka_probe_weight_workspace_size(const loka_probe_weight_args* a) {
+  if (a == nullptr || !probe_dim_ok(a->R) || !probe_dim_ok(a->C) || a->first) return 0;
+  return loka::probe_weight_ws(a->R, a->C);
+}
+loka_status loka_probe_weight_update(const loka_probe_weight_args* a, void* stream) {
+  REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
+  REQUIRE(probe_dim_ok(a->R) && probe_dim_ok(a->C), LOKA_ERR_UNSUPPORTED, "the Probe needs 1 <= R, C <= %lld",
+          (long long)kProbeMaxDim);
+  REQUIRE(std::isfinite(a->m) && a->m >= 0.0f && a->m < 1.0f, LOKA_ERR_INVALID_ARG, "momentum must be in [0, 1)");
+  REQUIRE(a->W && a->M && a->U && a->V && (a->first || a->info), LOKA_ERR_INVALID_ARG,
+          "W, M, U, V (and info unless first) are required");
+  REQUIRE_ALIGNED(a->W); REQUIRE_ALIGNED(a->M); REQUIRE_ALIGNED(a->U); REQUIRE_ALIGNED(a->V);
+  loka_status st;
+  if ((st = check_workspace(loka_probe_weight_workspace_size(a), a->workspace, a->workspace_bytes)) != LOKA_OK)
+    return st;
+  loka::ProbeWeightLaunch l{a->R, a->C, a->m, a->first != 0, a->W, a->M, a->U, a->V, a->info, a->workspace};
+  return hip_status(loka::probe_weight_update(l, static_cast<hipStream_t>(stream)), "loka_probe_weight_update");
+}
+
+size_t loka_probe_sample_input_workspace_size(const loka_probe_sample_input_args* a) {
+  if (a == nullptr || a->B < 1 || !probe_dim_ok(a->K)) return 0;
+  return loka::probe_sample_input_ws(a->B, a->K);
+}
+loka_status loka_probe_sample_input(const loka_probe_sample_input_args* a, void* stream) {
+  REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
+  REQUIRE(a->B >= 1 && a->n >= 2, LOKA_ERR_INVALID_ARG, "B >= 1 and n >= 2 are required");
+  REQUIRE(probe_dim_ok(a->K), LOKA_ERR_UNSUPPORTED, "the Probe needs 1 <= K <= %lld", (long long)kProbeMaxDim);
+  REQUIRE(a->mu && a->S && a->out && a->info, LOKA_ERR_INVALID_ARG, "mu, S, out and info are required");
+  REQUIRE_ALIGNED(a->mu); REQUIRE_ALIGNED(a->S); REQUIRE_ALIGNED(a->out);
+  loka_status st;
+  if ((st = check_workspace(loka_probe_sample_input_workspace_size(a), a->workspace, a->workspace_bytes)) != LOKA_OK)
+    return st;
+  loka::ProbeSampleInputLaunch l{a->B, a->K, a->n, a->mu, a->S, a->seed, a->out, a->info, a->workspace};
+  return hip_status(loka::probe_sample_input(l, static_cast<hipStream_t>(stream)), "loka_probe_sample_input");
+}
+
+size_t loka_probe_sample_weight_workspace_size(const loka_probe_sample_weight_args* a) {
+  if (a == nullptr || !probe_dim_ok(a->R) || !probe_dim_ok(a->C)) return 0;
+  return loka::probe_sample_weight_ws(a->R, a->C);
+}
+loka_status loka_probe_sample_weight(const loka_probe_sample_weight_args* a, void* stream) {
+  REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
+  REQUIRE(probe_dim_ok(a->R) && probe_dim_ok(a->C), LOKA_ERR_UNSUPPORTED, "the Probe needs 1 <= R, C <= %lld",
+          (long long)kProbeMaxDim);
+  REQUIRE(a->M && a->U && a->V && a->out && a->info, LOKA_ERR_INVALID_ARG, "M, U, V, out and info are required");
+  REQUIRE_ALIGNED(a->M); REQUIRE_ALIGNED(a->U); REQUIRE_ALIGNED(a->V); REQUIRE_ALIGNED(a->out);
+  loka_status st;
+  if ((st = check_workspace(loka_probe_sample_weight_workspace_size(a), a->workspace, a->workspace_bytes)) != LOKA_OK)
+    return st;
+  loka::ProbeSampleWeightLaunch l{a->R, a->C, a->M, a->U, a->V, a->seed, a->out, a->info, a->workspace};
+  return hip_status(loka::probe_sample_weight(l, static_cast<hipStream_t>(stream)), "loka_probe_sample_weight");
+}
+
 // The pages' rule, step by step: the accuracy filter, the speed filter, then
 // the shortest time among what passes.
 loka_status loka_dispatch_select(const loka_dispatch_candidate* c, int32_t n, double baseline_us, double mere_max,

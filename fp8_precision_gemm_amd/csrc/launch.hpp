@@ -127,6 +127,49 @@ size_t mere_workspace_bytes(int64_t S);
 int mere_max_k();
 hipError_t launch_mere(const MereLaunch& a, hipStream_t s);
 
+// ---- Probe statistics ------------------------------------------------------
+struct ProbeInputLaunch {
+  int64_t B, K, n_old;
+  const void* T;  // bf16 [B][K]
+  float* mu;      // [K], updated
+  float* S;       // [K][K] scatter, updated
+  void* workspace;
+};
+struct ProbeWeightLaunch {
+  int64_t R, C;
+  float m;
+  bool first;
+  const void* W;  // bf16 [R][C]
+  float *M, *U, *V;
+  int* info;      // device [2]: Cholesky status of V, U
+  void* workspace;
+};
+struct ProbeSampleInputLaunch {
+  int64_t B, K, n;
+  const float* mu;
+  const float* S;
+  uint64_t seed;
+  void* out;  // bf16 [B][K]
+  int* info;
+  void* workspace;
+};
+struct ProbeSampleWeightLaunch {
+  int64_t R, C;
+  const float *M, *U, *V;
+  uint64_t seed;
+  void* out;  // bf16 [R][C]
+  int* info;  // device [2]
+  void* workspace;
+};
+size_t probe_input_ws(int64_t B, int64_t K);
+size_t probe_weight_ws(int64_t R, int64_t C);
+size_t probe_sample_input_ws(int64_t B, int64_t K);
+size_t probe_sample_weight_ws(int64_t R, int64_t C);
+hipError_t probe_input_update(const ProbeInputLaunch& a, hipStream_t s);
+hipError_t probe_weight_update(const ProbeWeightLaunch& a, hipStream_t s);
+hipError_t probe_sample_input(const ProbeSampleInputLaunch& a, hipStream_t s);
+hipError_t probe_sample_weight(const ProbeSampleWeightLaunch& a, hipStream_t s);
+
 // ---- grouped -------------------------------------------------------------
 struct GroupDev {  // one group as the device sees it (copied into the workspace)
   int64_t M, N, K;

@@ -1,0 +1,462 @@
+// The Probe's statistics ([LoKA] section III-A1, "Online Distribution
+// Learning" and "Sampling learned distributions"): the input tracker's
+// batched mean/scatter merge (Chan, Golub and LeVeque's pairwise update,
+// accumulated in fp32 as the pages note), the weight tracker's matrix-normal
+// Kronecker flip-flop with an EMA (Cholesky factors and linear solves, no
+// explicit inverses; trace renormalization) and the two samplers.  All work
+// is fp32 vector arithmetic: the Probe runs every hundred or so steps, off
+// the training step's path, on K x K and R x C problems.
+#include <math.h>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace loka {
+namespace {
+
+constexpr int kPT = 256;     // threads of the element-wise and GEMM kernels
+constexpr int kGT = 64;      // GEMM tile (output rows and columns)
+constexpr int kGK = 16;      // GEMM depth per LDS stage
+constexpr int kChol = 1024;  // threads of the Cholesky workgroup (16 wavefronts)
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ---- element-wise ----------------------------------------------------------
+
+// column sums of a bf16 [B][K] over row chunks: part[chunk][k] (rows in order)
+__global__ __launch_bounds__(kPT) void k_colsum(const uint16_t* T, int64_t B, int K, int64_t rows_per, float* part) {
+  const int k = blockIdx.x * kPT + threadIdx.x;
+  if (k >= K) return;
+  const int64_t b0 = (int64_t)blockIdx.y * rows_per, b1 = min(b0 + rows_per, B);
+  float s = 0.0f;
+  for (int64_t b = b0; b < b1; ++b) s += bf16_lo(T[b * K + k]);
+  part[(int64_t)blockIdx.y * K + k] = s;
+}
+
+// batch mean, its difference to the running mean and the merged mean:
+// mu_b = sum / B, d = mu_b - mu, mu <- mu + (B / n') d
+__global__ __launch_bounds__(kPT) void k_mean_merge(const float* part, int nch, int64_t B, int K, float frac,
+                                                    float* mu, float* mu_b, float* d) {
+  const int k = blockIdx.x * kPT + threadIdx.x;
+  if (k >= K) return;
+  float s = 0.0f;
+  for (int c = 0; c < nch; ++c) s += part[(int64_t)c * K + k];
+  const float mb = s / (float)B;
+  const float dd = mb - mu[k];
+  mu_b[k] = mb;
+  d[k] = dd;
+  mu[k] = mu[k] + frac * dd;
+}
+
+// Tc = T - mu_b (fp32)
+__global__ __launch_bounds__(kPT) void k_center(const uint16_t* T, int64_t n, int K, const float* mu_b, float* Tc) {
+  const int64_t i = (int64_t)blockIdx.x * kPT + threadIdx.x;
+  if (i < n) Tc[i] = bf16_lo(T[i]) - mu_b[i % K];
+}
+
+// weight tracker, first update: M = W, U = I, V = I
+__global__ __launch_bounds__(kPT) void k_weight_init(const uint16_t* W, int64_t RC, int R, int C, float* M, float* U,
+                                                     float* V) {
+  const int64_t i = (int64_t)blockIdx.x * kPT + threadIdx.x;
+  if (i < RC) M[i] = bf16_lo(W[i]);
+  if (i < (int64_t)R * R) U[i] = (i / R == i % R) ? 1.0f : 0.0f;
+  if (i < (int64_t)C * C) V[i] = (i / C == i % C) ? 1.0f : 0.0f;
+}
+
+// M <- m M + (1 - m) W, Wc = W - M
+__global__ __launch_bounds__(kPT) void k_weight_ema(const uint16_t* W, int64_t RC, float m, float* M, float* Wc) {
+  const int64_t i = (int64_t)blockIdx.x * kPT + threadIdx.x;
+  if (i >= RC) return;
+  const float w = bf16_lo(W[i]);
+  const float mm = m * M[i] + (1.0f - m) * w;
+  M[i] = mm;
+  Wc[i] = w - mm;
+}
+
+// s = trace(U) / R (one workgroup), then U /= s, V *= s
+__global__ __launch_bounds__(kPT) void k_trace(const float* U, int R, float* s) {
+  __shared__ float red[kPT / 64];
+  float t = 0.0f;
+  for (int i = threadIdx.x; i < R; i += kPT) t += U[(int64_t)i * R + i];
+  t = wave_sum(t);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
+  __syncthreads();
+  if (threadIdx.x == 0) s[0] = (red[0] + red[1] + red[2] + red[3]) / (float)R;
+}
+__global__ __launch_bounds__(kPT) void k_renorm(const float* s, int64_t RR, int64_t CC, float* U, float* V) {
+  const int64_t i = (int64_t)blockIdx.x * kPT + threadIdx.x;
+  const float sc = s[0];
+  if (i < RR) U[i] = U[i] / sc;
+  if (i < CC) V[i] = V[i] * sc;
+}
+
+// ---- GEMM: P[z] = A B^T over the z-th slice of the contraction ----------------
+// A(i, k) = A[i * a_rs + k * a_cs], B(j, k) = B[j * b_rs + k * b_cs]; a 64 x 64
+// output tile per workgroup, 4 x 4 per thread, 16-deep LDS stages.
+struct GemmJob {
+  int64_t M, N, K, kper;
+  const float* A;
+  int64_t a_rs, a_cs;
+  const float* B;
+  int64_t b_rs, b_cs;
+  float* P;  // [splits][M][N]
+};
+__global__ __launch_bounds__(kPT) void k_gemm_f32(GemmJob g) {
+  __shared__ float As[kGK][kGT + 4], Bs[kGK][kGT + 4];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int64_t i0 = (int64_t)blockIdx.y * kGT, j0 = (int64_t)blockIdx.x * kGT;
+  const int64_t k0 = (int64_t)blockIdx.z * g.kper, k1 = min(k0 + g.kper, g.K);
+  float acc[4][4] = {};
+  for (int64_t kk = k0; kk < k1; kk += kGK) {
+    // stage: 16 x 64 of each operand, 4 elements per thread
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = threadIdx.x + q * kPT;
+      const int r = e & 63, kq = e >> 6;  // tile row r, depth kq
+      const int64_t k = kk + kq;
+      const int64_t ia = i0 + r, jb = j0 + r;
+      As[kq][r] = (k < k1 && ia < g.M) ? g.A[ia * g.a_rs + k * g.a_cs] : 0.0f;
+      Bs[kq][r] = (k < k1 && jb < g.N) ? g.B[jb * g.b_rs + k * g.b_cs] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kq = 0; kq < kGK; ++kq) {
+      float a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        a[u] = As[kq][ty * 4 + u];
+        b[u] = Bs[kq][tx * 4 + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a[u], b[v], acc[u][v]);
+    }
+    __syncthreads();
+  }
+  float* P = g.P + (int64_t)blockIdx.z * g.M * g.N;
+#pragma unroll
+  for (int u = 0; u < 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int64_t i = i0 + ty * 4 + u, j = j0 + tx * 4 + v;
+      if (i < g.M && j < g.N) P[i * g.N + j] = acc[u][v];
+    }
+}
+
+// C = beta C + alpha sum_z P[z] (z in order) + coef d_i d_j + row[j] + mat[i][j];
+// the result as fp32 (C) or bf16 (Cb); absent terms are null.
+struct ReduceJob {
+  int64_t M, N;
+  int splits;
+  const float* P;
+  float alpha, beta, coef;
+  const float* d;
+  const float* row;
+  const float* mat;
+  float* C;
+  uint16_t* Cb;
+};
+__global__ __launch_bounds__(kPT) void k_reduce(ReduceJob r) {
+  const int64_t e = (int64_t)blockIdx.x * kPT + threadIdx.x;
+  if (e >= r.M * r.N) return;
+  const int64_t i = e / r.N, j = e - i * r.N;
+  float s = 0.0f;
+  for (int z = 0; z < r.splits; ++z) s += r.P[(int64_t)z * r.M * r.N + e];
+  float c = r.alpha * s;
+  if (r.beta != 0.0f) c += r.beta * r.C[e];
+  if (r.d != nullptr) c += r.coef * r.d[i] * r.d[j];
+  if (r.row != nullptr) c += r.row[j];
+  if (r.mat != nullptr) c += r.mat[e];
+  if (r.Cb != nullptr) r.Cb[e] = (uint16_t)f32_to_bf16_bits(c);
+  else r.C[e] = c;
+}
+
+// ---- Cholesky: L L^T = a A + eps I, eps = 1e-6 trace(a A) / n ------------------
+// One workgroup, left-looking by columns: row j is staged in LDS, wavefront 0
+// takes the diagonal, then each wavefront takes rows i > j with its 64 lanes
+// on the dot product.  A non-positive pivot sets *info = j + 1 (the factor is
+// then not valid).  L's upper triangle is zero.
+__global__ __launch_bounds__(kChol) void k_cholesky(const float* A, int n, float a, float* L, int* info) {
+  extern __shared__ float rowj[];  // n floats
+  __shared__ float red[kChol / 64];
+  __shared__ float diag;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float t = 0.0f;
+  for (int i = tid; i < n; i += kChol) t += A[(int64_t)i * n + i];
+  t = wave_sum(t);
+  if (lane == 0) red[wave] = t;
+  __syncthreads();
+  float tr = 0.0f;
+  for (int w = 0; w < kChol / 64; ++w) tr += red[w];
+  const float eps = 1e-6f * a * tr / (float)n;
+  if (tid == 0) *info = 0;
+  for (int64_t e = tid; e < (int64_t)n * n; e += kChol) L[e] = 0.0f;
+  __syncthreads();
+  for (int j = 0; j < n; ++j) {
+    for (int k = tid; k < j; k += kChol) rowj[k] = L[(int64_t)j * n + k];
+    __syncthreads();
+    if (wave == 0) {
+      float s = 0.0f;
+      for (int k = lane; k < j; k += 64) s = fmaf(rowj[k], rowj[k], s);
+      s = wave_sum(s);
+      if (lane == 0) {
+        float p = a * A[(int64_t)j * n + j] + eps - s;
+        if (!(p > 0.0f)) {
+          if (*info == 0) *info = j + 1;
+          p = 1e-30f;
+        }
+        diag = sqrtf(p);
+        L[(int64_t)j * n + j] = diag;
+      }
+    }
+    __syncthreads();
+    const float dj = diag;
+    for (int i = j + 1 + wave; i < n; i += kChol / 64) {
+      float s = 0.0f;
+      for (int k = lane; k < j; k += 64) s = fmaf(L[(int64_t)i * n + k], rowj[k], s);
+      s = wave_sum(s);
+      if (lane == 0) L[(int64_t)i * n + j] = (a * A[(int64_t)i * n + j] - s) / dj;
+    }
+    __syncthreads();
+  }
+}
+
+// ---- lower-triangular solves L y = b for many right-hand sides -------------------
+// Right-hand side v has element i at b[v * vs + i * es] (and y likewise);
+// one wavefront per right-hand side, its solution in LDS, forward
+// substitution with the 64 lanes on each dot product.
+__global__ __launch_bounds__(kPT) void k_trsv_lower(const float* L, int n, const float* b, float* y, int64_t count,
+                                                    int64_t vs, int64_t es) {
+  extern __shared__ float xs[];  // (kPT / 64) x n
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t v = (int64_t)blockIdx.x * (kPT / 64) + wave;
+  if (v >= count) return;  // whole wavefronts: no barrier follows
+  float* x = xs + wave * n;
+  for (int i = 0; i < n; ++i) {
+    float s = 0.0f;
+    for (int k = lane; k < i; k += 64) s = fmaf(L[(int64_t)i * n + k], x[k], s);
+    s = wave_sum(s);
+    const float xi = (b[v * vs + i * es] - s) / L[(int64_t)i * n + i];
+    if (lane == 0) x[i] = xi;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    if (lane == 0) y[v * vs + i * es] = xi;
+  }
+}
+
+// ---- standard normals from Philox4x64-10 (Salmon et al., SC'11) ----------------
+// Block i: counter (i, 0, 0, 0), key (seed, 0); its four 64-bit outputs give
+// two uniform pairs u = (w >> 11) 2^-53 and Box-Muller normals
+// sqrt(-2 ln(1 - u1)) (cos 2 pi u2, sin 2 pi u2), stored in order.
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+  const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0; c[1] = lo1; c[2] = n2; c[3] = lo0;
+    k0 += W0;
+    k1 += W1;
+  }
+}
+__global__ __launch_bounds__(kPT) void k_normals(float* z, int64_t count, uint64_t seed) {
+  const int64_t blk = (int64_t)blockIdx.x * kPT + threadIdx.x;
+  if (blk * 4 >= count) return;
+  uint64_t c[4] = {(uint64_t)blk, 0, 0, 0};
+  philox4x64_10(c, seed, 0);
+  const double two_pi = 6.283185307179586476925286766559;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const double u1 = (double)(c[2 * p] >> 11) * 0x1.0p-53, u2 = (double)(c[2 * p + 1] >> 11) * 0x1.0p-53;
+    const double rr = sqrt(-2.0 * log(1.0 - u1)), t = two_pi * u2;
+    const int64_t j = blk * 4 + 2 * p;
+    if (j < count) z[j] = (float)(rr * cos(t));
+    if (j + 1 < count) z[j + 1] = (float)(rr * sin(t));
+  }
+}
+
+// ---- host helpers --------------------------------------------------------------
+
+unsigned blocks(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+constexpr int64_t kSplitDepth = 1024;  // contraction per GEMM slice
+int64_t gemm_splits(int64_t K) { return K <= kSplitDepth ? 1 : (K + kSplitDepth - 1) / kSplitDepth; }
+
+hipError_t gemm(const GemmJob& j0, const ReduceJob& r0, hipStream_t s) {
+  GemmJob j = j0;
+  ReduceJob r = r0;
+  const int64_t sp = gemm_splits(j.K);
+  j.kper = (j.K + sp - 1) / sp;
+  j.kper = (j.kper + kGK - 1) / kGK * kGK;
+  hipLaunchKernelGGL(k_gemm_f32, dim3(blocks(j.N, kGT), blocks(j.M, kGT), (unsigned)sp), dim3(kPT), 0, s, j);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  r.M = j.M; r.N = j.N; r.splits = (int)sp; r.P = j.P;
+  hipLaunchKernelGGL(k_reduce, dim3(blocks(j.M * j.N, kPT)), dim3(kPT), 0, s, r);
+  return hipGetLastError();
+}
+
+hipError_t cholesky(const float* A, int n, float a, float* L, int* info, hipStream_t s) {
+  hipLaunchKernelGGL(k_cholesky, dim3(1), dim3(kChol), (size_t)n * sizeof(float), s, A, n, a, L, info);
+  return hipGetLastError();
+}
+
+hipError_t trsv(const float* L, int n, const float* b, float* y, int64_t count, int64_t vs, int64_t es,
+                hipStream_t s) {
+  hipLaunchKernelGGL(k_trsv_lower, dim3(blocks(count, kPT / 64)), dim3(kPT), (size_t)(kPT / 64) * n * sizeof(float),
+                     s, L, n, b, y, count, vs, es);
+  return hipGetLastError();
+}
+
+hipError_t normals(float* z, int64_t count, uint64_t seed, hipStream_t s) {
+  hipLaunchKernelGGL(k_normals, dim3(blocks((count + 3) / 4, kPT)), dim3(kPT), 0, s, z, count, seed);
+  return hipGetLastError();
+}
+
+size_t al256(size_t b) { return (b + 255) / 256 * 256; }
+
+}  // namespace
+
+// ---- the four operations ---------------------------------------------------------
+
+int64_t probe_colsum_chunks(int64_t B) { return B < 256 ? 1 : min((int64_t)64, B / 256); }
+
+size_t probe_input_ws(int64_t B, int64_t K) {
+  const int64_t nch = probe_colsum_chunks(B);
+  return al256((size_t)nch * K * 4) + 2 * al256((size_t)K * 4) + al256((size_t)B * K * 4) +
+         al256((size_t)gemm_splits(B) * K * K * 4);
+}
+
+hipError_t probe_input_update(const ProbeInputLaunch& a, hipStream_t s) {
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  const int64_t nch = probe_colsum_chunks(a.B), K = a.K;
+  float* part = reinterpret_cast<float*>(ws);
+  float* mu_b = reinterpret_cast<float*>(ws + al256((size_t)nch * K * 4));
+  float* d = mu_b + al256((size_t)K * 4) / 4;
+  float* Tc = d + al256((size_t)K * 4) / 4;
+  float* P = Tc + al256((size_t)a.B * K * 4) / 4;
+  const int64_t rows_per = (a.B + nch - 1) / nch;
+  const uint16_t* T = static_cast<const uint16_t*>(a.T);
+  hipLaunchKernelGGL(k_colsum, dim3(blocks(K, kPT), (unsigned)nch), dim3(kPT), 0, s, T, a.B, (int)K, rows_per, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n_new = a.n_old + a.B;
+  hipLaunchKernelGGL(k_mean_merge, dim3(blocks(K, kPT)), dim3(kPT), 0, s, part, (int)nch, a.B, (int)K,
+                     (float)((double)a.B / (double)n_new), a.mu, mu_b, d);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_center, dim3(blocks(a.B * K, kPT)), dim3(kPT), 0, s, T, a.B * K, (int)K, mu_b, Tc);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // S <- S + Tc^T Tc + (n B / n') d d^T
+  GemmJob g{K, K, a.B, 0, Tc, 1, K, Tc, 1, K, P};
+  ReduceJob r{};
+  r.alpha = 1.0f; r.beta = 1.0f; r.coef = (float)((double)a.n_old * (double)a.B / (double)n_new);
+  r.d = d; r.C = a.S;
+  return gemm(g, r, s);
+}
+
+size_t probe_weight_ws(int64_t R, int64_t C) {
+  const size_t rc = al256((size_t)R * C * 4);
+  return 3 * rc + al256((size_t)R * R * 4) + al256((size_t)C * C * 4) +
+         al256((size_t)max(gemm_splits(C) * R * R, gemm_splits(R) * C * C) * 4) + 256;
+}
+
+hipError_t probe_weight_update(const ProbeWeightLaunch& a, hipStream_t s) {
+  const int64_t R = a.R, C = a.C, RC = R * C;
+  const uint16_t* W = static_cast<const uint16_t*>(a.W);
+  if (a.first) {
+    hipLaunchKernelGGL(k_weight_init, dim3(blocks(max(RC, max(R * R, C * C)), kPT)), dim3(kPT), 0, s, W, RC, (int)R,
+                       (int)C, a.M, a.U, a.V);
+    return hipGetLastError();
+  }
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  const size_t rc = al256((size_t)RC * 4);
+  float* Wc = reinterpret_cast<float*>(ws);
+  float* Wt = reinterpret_cast<float*>(ws + rc);
+  float* Wu = reinterpret_cast<float*>(ws + 2 * rc);
+  float* LU = reinterpret_cast<float*>(ws + 3 * rc);
+  float* LV = reinterpret_cast<float*>(ws + 3 * rc + al256((size_t)R * R * 4));
+  float* P = LV + al256((size_t)C * C * 4) / 4;
+  float* sc = P + al256((size_t)max(gemm_splits(C) * R * R, gemm_splits(R) * C * C) * 4) / 4;
+  hipLaunchKernelGGL(k_weight_ema, dim3(blocks(RC, kPT)), dim3(kPT), 0, s, W, RC, a.m, a.M, Wc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // both factors from the U and V before this update
+  if ((e = cholesky(a.V, (int)C, 1.0f, LV, a.info, s)) != hipSuccess) return e;
+  if ((e = cholesky(a.U, (int)R, 1.0f, LU, a.info + 1, s)) != hipSuccess) return e;
+  // Wt = Wc LV^-T (each row r of Wc: LV x = w_r), Wu = LU^-1 Wc (each column c)
+  if ((e = trsv(LV, (int)C, Wc, Wt, R, C, 1, s)) != hipSuccess) return e;
+  if ((e = trsv(LU, (int)R, Wc, Wu, C, 1, C, s)) != hipSuccess) return e;
+  // U <- m U + (1 - m) Wt Wt^T / C;  V <- m V + (1 - m) Wu^T Wu / R
+  ReduceJob r{};
+  r.beta = a.m;
+  r.alpha = (1.0f - a.m) / (float)C;
+  r.C = a.U;
+  if ((e = gemm(GemmJob{R, R, C, 0, Wt, C, 1, Wt, C, 1, P}, r, s)) != hipSuccess) return e;
+  r.alpha = (1.0f - a.m) / (float)R;
+  r.C = a.V;
+  if ((e = gemm(GemmJob{C, C, R, 0, Wu, 1, C, Wu, 1, C, P}, r, s)) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_trace, dim3(1), dim3(kPT), 0, s, a.U, (int)R, sc);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(k_renorm, dim3(blocks(max(R * R, C * C), kPT)), dim3(kPT), 0, s, sc, R * R, C * C, a.U, a.V);
+  return hipGetLastError();
+}
+
+size_t probe_sample_input_ws(int64_t B, int64_t K) {
+  return al256((size_t)K * K * 4) + al256((size_t)B * K * 4) + al256((size_t)gemm_splits(K) * B * K * 4);
+}
+
+hipError_t probe_sample_input(const ProbeSampleInputLaunch& a, hipStream_t s) {
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  const int64_t K = a.K, B = a.B;
+  float* L = reinterpret_cast<float*>(ws);
+  float* Z = reinterpret_cast<float*>(ws + al256((size_t)K * K * 4));
+  float* P = Z + al256((size_t)B * K * 4) / 4;
+  // L L^T = S / (n - 1) + eps I
+  hipError_t e = cholesky(a.S, (int)K, (float)(1.0 / (double)(a.n - 1)), L, a.info, s);
+  if (e != hipSuccess) return e;
+  if ((e = normals(Z, B * K, a.seed, s)) != hipSuccess) return e;
+  // T' = 1 mu^T + Z L^T, bf16
+  ReduceJob r{};
+  r.alpha = 1.0f;
+  r.row = a.mu;
+  r.Cb = static_cast<uint16_t*>(a.out);
+  return gemm(GemmJob{B, K, K, 0, Z, K, 1, L, K, 1, P}, r, s);
+}
+
+size_t probe_sample_weight_ws(int64_t R, int64_t C) {
+  return al256((size_t)R * R * 4) + al256((size_t)C * C * 4) + 2 * al256((size_t)R * C * 4) +
+         al256((size_t)max(gemm_splits(C), gemm_splits(R)) * R * C * 4);
+}
+
+hipError_t probe_sample_weight(const ProbeSampleWeightLaunch& a, hipStream_t s) {
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  const int64_t R = a.R, C = a.C;
+  float* LU = reinterpret_cast<float*>(ws);
+  float* LV = reinterpret_cast<float*>(ws + al256((size_t)R * R * 4));
+  float* Z = LV + al256((size_t)C * C * 4) / 4;
+  float* Y = Z + al256((size_t)R * C * 4) / 4;
+  float* P = Y + al256((size_t)R * C * 4) / 4;
+  hipError_t e;
+  if ((e = cholesky(a.U, (int)R, 1.0f, LU, a.info, s)) != hipSuccess) return e;
+  if ((e = cholesky(a.V, (int)C, 1.0f, LV, a.info + 1, s)) != hipSuccess) return e;
+  if ((e = normals(Z, R * C, a.seed, s)) != hipSuccess) return e;
+  // Y = Z LV^T, then W' = M + LU Y (bf16)
+  ReduceJob r{};
+  r.alpha = 1.0f;
+  r.C = Y;
+  if ((e = gemm(GemmJob{R, C, C, 0, Z, C, 1, LV, C, 1, P}, r, s)) != hipSuccess) return e;
+  ReduceJob r2{};
+  r2.alpha = 1.0f;
+  r2.mat = a.M;
+  r2.Cb = static_cast<uint16_t*>(a.out);
+  return gemm(GemmJob{R, C, R, 0, LU, R, 1, Y, 1, C, P}, r2, s);
+}
+
+}  // namespace loka

@@ -435,6 +435,95 @@ loka_status loka_dispatch_select(const loka_dispatch_candidate* cands, int32_t n
                                  double mere_max, double min_speedup, int32_t* choice);
 
 /* ------------------------------------------------------------------------
+ * The Probe's statistics (LoKA section III-A1, "Online Distribution
+ * Learning" and "Sampling learned distributions"), on the device.  fp32
+ * throughout; every reduction runs in a fixed order (deterministic).
+ * Shapes: 1 <= K, R, C <= 2048; B >= 1.  All pointers are device pointers
+ * unless marked HOST; workspace as returned by the _workspace_size call.
+ *
+ * loka_probe_input_update: merge a batch T bf16 [B, K] of a layer's input
+ *   into (n_old, mu fp32 [K], S fp32 [K, K]) in place, S the unnormalized
+ *   scatter (Chan, Golub and LeVeque's pairwise update, as the pages give it):
+ *     n' = n_old + B, d = mean(T) - mu, mu += (B / n') d,
+ *     S += (T - mean T)^T (T - mean T) + (n_old B / n') d d^T.
+ *   The caller keeps n (add B after the call); the covariance is S / (n - 1).
+ *
+ * loka_probe_weight_update: the matrix-normal Kronecker flip-flop with an
+ *   EMA of momentum m for W bf16 [R, C] ~ MN(M, U, V), state M fp32 [R, C],
+ *   U fp32 [R, R], V fp32 [C, C] in place.  first != 0 initializes
+ *   (M = W, U = I, V = I).  Otherwise, with eps = 1e-6 trace(A) / dim(A):
+ *     M <- m M + (1 - m) W, Wc = W - M,
+ *     L_V L_V^T = V + eps I, Wt = Wc L_V^-T, U1 = Wt Wt^T / C,
+ *     L_U L_U^T = U + eps I, Wu = L_U^-1 Wc, V1 = Wu^T Wu / R
+ *     (both factors from the state before the update; linear solves, no
+ *     inverses), U <- m U + (1 - m) U1, V <- m V + (1 - m) V1,
+ *     s = trace(U) / R, U <- U / s, V <- s V.
+ *   info: device int[2], the Cholesky status of V and U (0, or the 1-based
+ *   column of a non-positive pivot, after which the state is not valid).
+ *
+ * loka_probe_sample_input: T' = 1 mu^T + Z L^T, L L^T = S / (n - 1) + eps I,
+ *   out bf16 [B, K]; info int[1].
+ * loka_probe_sample_weight: W' = M + L_U Z L_V^T, out bf16 [R, C]; info int[2].
+ *   Z is standard normal: Philox4x64-10 (Salmon et al., SC'11) block i with
+ *   counter (i, 0, 0, 0) and key (seed, 0); each 64-bit output w gives the
+ *   uniform (w >> 11) 2^-53, pairs (u1, u2) the Box-Muller normals
+ *   sqrt(-2 ln(1 - u1)) (cos 2 pi u2, sin 2 pi u2), in row-major order.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int64_t B, K, n_old;
+  const void* T;
+  float* mu;
+  float* S;
+  void* workspace;
+  size_t workspace_bytes;
+} loka_probe_input_args;
+
+typedef struct {
+  int64_t R, C;
+  float m;
+  int32_t first;
+  const void* W;
+  float* M;
+  float* U;
+  float* V;
+  int32_t* info;
+  void* workspace;
+  size_t workspace_bytes;
+} loka_probe_weight_args;
+
+typedef struct {
+  int64_t B, K, n;
+  const float* mu;
+  const float* S;
+  uint64_t seed;
+  void* out;
+  int32_t* info;
+  void* workspace;
+  size_t workspace_bytes;
+} loka_probe_sample_input_args;
+
+typedef struct {
+  int64_t R, C;
+  const float* M;
+  const float* U;
+  const float* V;
+  uint64_t seed;
+  void* out;
+  int32_t* info;
+  void* workspace;
+  size_t workspace_bytes;
+} loka_probe_sample_weight_args;
+
+size_t loka_probe_input_workspace_size(const loka_probe_input_args* args);
+loka_status loka_probe_input_update(const loka_probe_input_args* args, void* stream);
+size_t loka_probe_weight_workspace_size(const loka_probe_weight_args* args);
+loka_status loka_probe_weight_update(const loka_probe_weight_args* args, void* stream);
+size_t loka_probe_sample_input_workspace_size(const loka_probe_sample_input_args* args);
+loka_status loka_probe_sample_input(const loka_probe_sample_input_args* args, void* stream);
+size_t loka_probe_sample_weight_workspace_size(const loka_probe_sample_weight_args* args);
+loka_status loka_probe_sample_weight(const loka_probe_sample_weight_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
  * Helpers.
  * ---------------------------------------------------------------------- */
 const char* loka_status_string(loka_status s); /* static text, never NULL */
