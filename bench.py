@@ -46,7 +46,7 @@ def parse():
     p.add_argument("--no-rows", action="store_true", help="skip the other workloads")
     p.add_argument("--only", default=None,
                    help="comma list of workloads to time (for profiling): "
-                        "fwd,tensor,mx,blocknorm,bwd,square,dispatch,grouped,copy")
+                        "fwd,tensor,mx,blocknorm,bwd,square,dispatch,probe,grouped,copy")
     return p.parse_args()
 
 
@@ -218,6 +218,35 @@ def bench_square(torch, lk, case, steps, warmup, stream):
     return fwd, bwd
 
 
+def bench_probe(torch, lk, case, stream, reps=20):
+    """The Probe's four operations on the benchmark layer: the input update
+    with the 16384 x 512 activations, the weight update and the two samplers
+    (512 x 512 weight; 16384 sampled rows).  Per-call time in us."""
+    x, w = dev_bf16(torch, case["x"]), dev_bf16(torch, case["w"])
+    out = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        e1.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    with torch.cuda.stream(stream):
+        st = lk.loka_probe_input_update(x, stream=stream)
+        out["input_update_us"] = timed(lambda: lk.loka_probe_input_update(x, st, stream=stream))
+        ws = lk.loka_probe_weight_update(w, stream=stream)
+        lk.loka_probe_weight_update(w.clone(), ws, m=0.9, stream=stream)
+        out["weight_update_us"] = timed(lambda: lk.loka_probe_weight_update(w, ws, m=0.9, stream=stream, check=False))
+        out["sample_input_us"] = timed(lambda: lk.loka_probe_sample_input(st, 16384, 1, stream=stream, check=False))
+        out["sample_weight_us"] = timed(lambda: lk.loka_probe_sample_weight(ws, 1, stream=stream, check=False))
+    return out
+
+
 def bench_grouped(torch, lk, groups, steps, warmup, stream):
     dg = []
     flops = 0.0
@@ -339,6 +368,10 @@ def main():
         print(f"[bench] dispatch: {d['choice']} (baseline {d['baseline_us']:.1f} us; "
               + ", ".join(f"{r['recipe']} {r['us']:.1f} us MERE {r['mere']:.3f}" for r in d["table"]) + ")",
               file=sys.stderr, flush=True)
+    if not args.no_rows and want("probe"):
+        r = bench_probe(torch, lk, case, stream)
+        rows["probe_16384x512x512"] = {k: round(v, 2) for k, v in r.items()}
+        print("[bench] probe: " + ", ".join(f"{k} {v:.1f}" for k, v in r.items()), file=sys.stderr, flush=True)
     if not args.no_rows and want("grouped"):
         r = bench_grouped(torch, lk, workloads.grouped_case(), args.steps, args.warmup, stream)
         rows["grouped_64x8192"] = {k: round(v, 3) for k, v in r.items()}
