@@ -17,7 +17,6 @@ namespace {
 constexpr int kPT = 256;     // threads of the element-wise and GEMM kernels
 constexpr int kGT = 64;      // GEMM tile (output rows and columns)
 constexpr int kGK = 16;      // GEMM depth per LDS stage
-constexpr int kChol = 1024;  // threads of the Cholesky workgroup (16 wavefronts)
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -67,14 +66,18 @@ __global__ __launch_bounds__(kPT) void k_weight_init(const uint16_t* W, int64_t 
   if (i < (int64_t)C * C) V[i] = (i / C == i % C) ? 1.0f : 0.0f;
 }
 
-// M <- m M + (1 - m) W, Wc = W - M
-__global__ __launch_bounds__(kPT) void k_weight_ema(const uint16_t* W, int64_t RC, float m, float* M, float* Wc) {
+// M <- m M + (1 - m) W; Wc = W - M [R][C] and its transpose WcT [C][R] (the
+// right-hand sides of the two solves, each solved in place)
+__global__ __launch_bounds__(kPT) void k_weight_ema(const uint16_t* W, int64_t RC, int C, int R, float m, float* M,
+                                                    float* Wc, float* WcT) {
   const int64_t i = (int64_t)blockIdx.x * kPT + threadIdx.x;
   if (i >= RC) return;
   const float w = bf16_lo(W[i]);
   const float mm = m * M[i] + (1.0f - m) * w;
   M[i] = mm;
   Wc[i] = w - mm;
+  const int64_t r = i / C, c = i - r * C;
+  WcT[c * R + r] = w - mm;
 }
 
 // s = trace(U) / R (one workgroup), then U /= s, V *= s
@@ -149,7 +152,8 @@ __global__ __launch_bounds__(kPT) void k_gemm_f32(GemmJob g) {
 }
 
 // C = beta C + alpha sum_z P[z] (z in order) + coef d_i d_j + row[j] + mat[i][j];
-// the result as fp32 (C) or bf16 (Cb); absent terms are null.
+// the result as fp32 (C, row stride ldc; 0 = N) or bf16 (Cb); absent terms
+// are null; lower: only the entries j <= i.
 struct ReduceJob {
   int64_t M, N;
   int splits;
@@ -160,92 +164,126 @@ struct ReduceJob {
   const float* mat;
   float* C;
   uint16_t* Cb;
+  int64_t ldc;
+  int lower;
 };
 __global__ __launch_bounds__(kPT) void k_reduce(ReduceJob r) {
   const int64_t e = (int64_t)blockIdx.x * kPT + threadIdx.x;
   if (e >= r.M * r.N) return;
   const int64_t i = e / r.N, j = e - i * r.N;
+  if (r.lower && j > i) return;
+  const int64_t ce = r.ldc > 0 ? i * r.ldc + j : e;
   float s = 0.0f;
   for (int z = 0; z < r.splits; ++z) s += r.P[(int64_t)z * r.M * r.N + e];
   float c = r.alpha * s;
-  if (r.beta != 0.0f) c += r.beta * r.C[e];
+  if (r.beta != 0.0f) c += r.beta * r.C[ce];
   if (r.d != nullptr) c += r.coef * r.d[i] * r.d[j];
   if (r.row != nullptr) c += r.row[j];
   if (r.mat != nullptr) c += r.mat[e];
   if (r.Cb != nullptr) r.Cb[e] = (uint16_t)f32_to_bf16_bits(c);
-  else r.C[e] = c;
+  else r.C[ce] = c;
 }
 
-// ---- Cholesky: L L^T = a A + eps I, eps = 1e-6 trace(a A) / n ------------------
-// One workgroup, left-looking by columns: row j is staged in LDS, wavefront 0
-// takes the diagonal, then each wavefront takes rows i > j with its 64 lanes
-// on the dot product.  A non-positive pivot sets *info = j + 1 (the factor is
-// then not valid).  L's upper triangle is zero.
-__global__ __launch_bounds__(kChol) void k_cholesky(const float* A, int n, float a, float* L, int* info) {
-  extern __shared__ float rowj[];  // n floats
-  __shared__ float red[kChol / 64];
-  __shared__ float diag;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// ---- Cholesky, blocked right-looking: L L^T = a A + eps I ----------------------
+// eps = 1e-6 trace(a A) / n.  L starts as the lower triangle of a A + eps I;
+// per 64-column panel: the diagonal block is factored in LDS, the rows below
+// solve against it (k_trsm_panel), and the trailing lower triangle takes the
+// panel's product away (GEMM + reduce).  A non-positive pivot sets *info to
+// its 1-based column (the first one met); the factor is then not valid.
+constexpr int kPanel = 64;
+
+__global__ __launch_bounds__(kPT) void k_chol_eps(const float* A, int n, float a, float* eps, int* info) {
+  __shared__ float red[kPT / 64];
   float t = 0.0f;
-  for (int i = tid; i < n; i += kChol) t += A[(int64_t)i * n + i];
+  for (int i = threadIdx.x; i < n; i += kPT) t += A[(int64_t)i * n + i];
   t = wave_sum(t);
-  if (lane == 0) red[wave] = t;
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = t;
   __syncthreads();
-  float tr = 0.0f;
-  for (int w = 0; w < kChol / 64; ++w) tr += red[w];
-  const float eps = 1e-6f * a * tr / (float)n;
-  if (tid == 0) *info = 0;
-  for (int64_t e = tid; e < (int64_t)n * n; e += kChol) L[e] = 0.0f;
+  if (threadIdx.x == 0) {
+    eps[0] = 1e-6f * a * (red[0] + red[1] + red[2] + red[3]) / (float)n;
+    *info = 0;
+  }
+}
+__global__ __launch_bounds__(kPT) void k_chol_init(const float* A, int n, float a, const float* eps, float* L) {
+  const int64_t e = (int64_t)blockIdx.x * kPT + threadIdx.x;
+  if (e >= (int64_t)n * n) return;
+  const int64_t i = e / n, j = e - i * n;
+  L[e] = j > i ? 0.0f : a * A[e] + (i == j ? eps[0] : 0.0f);
+}
+
+// factor the b x b diagonal block at (jb, jb) of L in place (b <= 64)
+__global__ __launch_bounds__(kPT) void k_potrf_block(float* L, int n, int jb, int b, int* info) {
+  __shared__ float Ab[kPanel][kPanel + 1];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < b * b; e += kPT) {
+    const int i = e / b, j = e - i * b;
+    Ab[i][j] = j <= i ? L[(int64_t)(jb + i) * n + jb + j] : 0.0f;
+  }
   __syncthreads();
-  for (int j = 0; j < n; ++j) {
-    for (int k = tid; k < j; k += kChol) rowj[k] = L[(int64_t)j * n + k];
-    __syncthreads();
-    if (wave == 0) {
-      float s = 0.0f;
-      for (int k = lane; k < j; k += 64) s = fmaf(rowj[k], rowj[k], s);
-      s = wave_sum(s);
-      if (lane == 0) {
-        float p = a * A[(int64_t)j * n + j] + eps - s;
-        if (!(p > 0.0f)) {
-          if (*info == 0) *info = j + 1;
-          p = 1e-30f;
-        }
-        diag = sqrtf(p);
-        L[(int64_t)j * n + j] = diag;
+  // thread (tj, ti): column tj, rows ti, ti + 4, ... of the trailing update
+  const int tj = tid & (kPanel - 1), ti = tid >> 6;
+  for (int c = 0; c < b; ++c) {
+    if (tid == 0) {
+      float d = Ab[c][c];
+      if (!(d > 0.0f)) {
+        if (*info == 0) *info = jb + c + 1;
+        d = 1e-30f;
       }
+      Ab[c][c] = sqrtf(d);
     }
     __syncthreads();
-    const float dj = diag;
-    for (int i = j + 1 + wave; i < n; i += kChol / 64) {
-      float s = 0.0f;
-      for (int k = lane; k < j; k += 64) s = fmaf(L[(int64_t)i * n + k], rowj[k], s);
-      s = wave_sum(s);
-      if (lane == 0) L[(int64_t)i * n + j] = (a * A[(int64_t)i * n + j] - s) / dj;
+    if (tid > c && tid < b) Ab[tid][c] /= Ab[c][c];
+    __syncthreads();
+    if (tj > c && tj < b) {
+      const float ljc = Ab[tj][c];
+      for (int i = max(ti, tj - ((tj - ti) & 3)); i < b; i += kPT / kPanel)
+        if (i >= tj) Ab[i][tj] = fmaf(-Ab[i][c], ljc, Ab[i][tj]);
     }
     __syncthreads();
   }
+  for (int e = tid; e < b * b; e += kPT) {
+    const int i = e / b, j = e - i * b;
+    L[(int64_t)(jb + i) * n + jb + j] = j <= i ? Ab[i][j] : 0.0f;
+  }
 }
 
-// ---- lower-triangular solves L y = b for many right-hand sides -------------------
-// Right-hand side v has element i at b[v * vs + i * es] (and y likewise);
-// one wavefront per right-hand side, its solution in LDS, forward
-// substitution with the 64 lanes on each dot product.
-__global__ __launch_bounds__(kPT) void k_trsv_lower(const float* L, int n, const float* b, float* y, int64_t count,
-                                                    int64_t vs, int64_t es) {
-  extern __shared__ float xs[];  // (kPT / 64) x n
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t v = (int64_t)blockIdx.x * (kPT / 64) + wave;
-  if (v >= count) return;  // whole wavefronts: no barrier follows
-  float* x = xs + wave * n;
-  for (int i = 0; i < n; ++i) {
-    float s = 0.0f;
-    for (int k = lane; k < i; k += 64) s = fmaf(L[(int64_t)i * n + k], x[k], s);
-    s = wave_sum(s);
-    const float xi = (b[v * vs + i * es] - s) / L[(int64_t)i * n + i];
-    if (lane == 0) x[i] = xi;
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    if (lane == 0) y[v * vs + i * es] = xi;
+// Rows v of X [count][ldx], columns jb .. jb+b: x <- x L_jj^-T with L_jj the
+// b x b diagonal block of L at (jb, jb) (forward substitution per row; the
+// block and 256 rows are staged in LDS, one row per thread).
+__global__ __launch_bounds__(kPT) void k_trsm_panel(float* X, int64_t count, int64_t ldx, const float* L, int ldl,
+                                                    int jb, int b) {
+  __shared__ float Lj[kPanel][kPanel + 1];
+  __shared__ float xs[kPT][kPanel + 1];
+  const int tid = threadIdx.x;
+  const int64_t v0 = (int64_t)blockIdx.x * kPT;
+  for (int e = tid; e < b * b; e += kPT) {
+    const int i = e / b, j = e - i * b;
+    Lj[i][j] = j <= i ? L[(int64_t)(jb + i) * ldl + jb + j] : 0.0f;
+  }
+  for (int e = tid; e < kPT * b; e += kPT) {
+    const int r = e / b, c = e - r * b;
+    xs[r][c] = v0 + r < count ? X[(v0 + r) * ldx + jb + c] : 0.0f;
+  }
+  __syncthreads();
+  // this thread's row in registers; the block's entries are LDS broadcasts
+  float x[kPanel];
+#pragma unroll
+  for (int c = 0; c < kPanel; ++c) x[c] = xs[tid][c];
+#pragma unroll
+  for (int c = 0; c < kPanel; ++c) {
+    if (c < b) {
+      float t = x[c];
+#pragma unroll
+      for (int k = 0; k < c; ++k) t = fmaf(-x[k], Lj[c][k], t);
+      x[c] = t / Lj[c][c];
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < kPanel; ++c) xs[tid][c] = x[c];
+  __syncthreads();
+  for (int e = tid; e < kPT * b; e += kPT) {
+    const int r = e / b, c = e - r * b;
+    if (v0 + r < count) X[(v0 + r) * ldx + jb + c] = xs[r][c];
   }
 }
 
@@ -303,16 +341,45 @@ hipError_t gemm(const GemmJob& j0, const ReduceJob& r0, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t cholesky(const float* A, int n, float a, float* L, int* info, hipStream_t s) {
-  hipLaunchKernelGGL(k_cholesky, dim3(1), dim3(kChol), (size_t)n * sizeof(float), s, A, n, a, L, info);
-  return hipGetLastError();
+// L L^T = a A + eps I (scal: one float of workspace, P: n*n floats of workspace)
+hipError_t cholesky(const float* A, int n, float a, float* L, int* info, float* scal, float* P, hipStream_t s) {
+  hipLaunchKernelGGL(k_chol_eps, dim3(1), dim3(kPT), 0, s, A, n, a, scal, info);
+  hipLaunchKernelGGL(k_chol_init, dim3(blocks((int64_t)n * n, kPT)), dim3(kPT), 0, s, A, n, a, scal, L);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  for (int jb = 0; jb < n; jb += kPanel) {
+    const int b = min(kPanel, n - jb), r = n - jb - b;
+    hipLaunchKernelGGL(k_potrf_block, dim3(1), dim3(kPT), 0, s, L, n, jb, b, info);
+    if (r > 0) {
+      float* below = L + (int64_t)(jb + b) * n;
+      hipLaunchKernelGGL(k_trsm_panel, dim3(blocks(r, kPT)), dim3(kPT), 0, s, below, (int64_t)r, (int64_t)n, L, n,
+                         jb, b);
+      ReduceJob rj{};
+      rj.alpha = -1.0f; rj.beta = 1.0f; rj.C = below + jb + b; rj.ldc = n; rj.lower = 1;
+      if ((e = gemm(GemmJob{r, r, b, 0, below + jb, n, 1, below + jb, n, 1, P}, rj, s)) != hipSuccess) return e;
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
-hipError_t trsv(const float* L, int n, const float* b, float* y, int64_t count, int64_t vs, int64_t es,
-                hipStream_t s) {
-  hipLaunchKernelGGL(k_trsv_lower, dim3(blocks(count, kPT / 64)), dim3(kPT), (size_t)(kPT / 64) * n * sizeof(float),
-                     s, L, n, b, y, count, vs, es);
-  return hipGetLastError();
+// X [count][n] <- X L^-T in place (each row: L x = row), blocked by panels
+hipError_t trsm_rows(float* X, int64_t count, int n, const float* L, float* P, hipStream_t s) {
+  hipError_t e;
+  for (int jb = 0; jb < n; jb += kPanel) {
+    const int b = min(kPanel, n - jb), r = n - jb - b;
+    hipLaunchKernelGGL(k_trsm_panel, dim3(blocks(count, kPT)), dim3(kPT), 0, s, X, count, (int64_t)n, L, n, jb, b);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (r > 0) {
+      // X[:, jb+b:] -= X[:, jb:jb+b] L[jb+b:, jb:jb+b]^T
+      ReduceJob rj{};
+      rj.alpha = -1.0f; rj.beta = 1.0f; rj.C = X + jb + b; rj.ldc = n;
+      if ((e = gemm(GemmJob{count, r, b, 0, X + jb, n, 1, L + (int64_t)(jb + b) * n + jb, n, 1, P}, rj, s)) !=
+          hipSuccess)
+        return e;
+    }
+  }
+  return hipSuccess;
 }
 
 hipError_t normals(float* z, int64_t count, uint64_t seed, hipStream_t s) {
@@ -361,10 +428,11 @@ hipError_t probe_input_update(const ProbeInputLaunch& a, hipStream_t s) {
   return gemm(g, r, s);
 }
 
+
 size_t probe_weight_ws(int64_t R, int64_t C) {
-  const size_t rc = al256((size_t)R * C * 4);
-  return 3 * rc + al256((size_t)R * R * 4) + al256((size_t)C * C * 4) +
-         al256((size_t)max(gemm_splits(C) * R * R, gemm_splits(R) * C * C) * 4) + 256;
+  const size_t p = max(max((size_t)R * C, (size_t)max(R * R, C * C)),
+                       (size_t)max(gemm_splits(C) * R * R, gemm_splits(R) * C * C));
+  return 2 * al256((size_t)R * C * 4) + al256((size_t)R * R * 4) + al256((size_t)C * C * 4) + al256(p * 4) + 256;
 }
 
 hipError_t probe_weight_update(const ProbeWeightLaunch& a, hipStream_t s) {
@@ -377,22 +445,23 @@ hipError_t probe_weight_update(const ProbeWeightLaunch& a, hipStream_t s) {
   }
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
   const size_t rc = al256((size_t)RC * 4);
-  float* Wc = reinterpret_cast<float*>(ws);
-  float* Wt = reinterpret_cast<float*>(ws + rc);
-  float* Wu = reinterpret_cast<float*>(ws + 2 * rc);
-  float* LU = reinterpret_cast<float*>(ws + 3 * rc);
-  float* LV = reinterpret_cast<float*>(ws + 3 * rc + al256((size_t)R * R * 4));
+  float* Wt = reinterpret_cast<float*>(ws);        // Wc, then Wc LV^-T
+  float* WuT = reinterpret_cast<float*>(ws + rc);  // Wc^T, then (LU^-1 Wc)^T
+  float* LU = reinterpret_cast<float*>(ws + 2 * rc);
+  float* LV = LU + al256((size_t)R * R * 4) / 4;
   float* P = LV + al256((size_t)C * C * 4) / 4;
-  float* sc = P + al256((size_t)max(gemm_splits(C) * R * R, gemm_splits(R) * C * C) * 4) / 4;
-  hipLaunchKernelGGL(k_weight_ema, dim3(blocks(RC, kPT)), dim3(kPT), 0, s, W, RC, a.m, a.M, Wc);
+  const size_t pn = max(max((size_t)R * C, (size_t)max(R * R, C * C)),
+                        (size_t)max(gemm_splits(C) * R * R, gemm_splits(R) * C * C));
+  float* sc = P + al256(pn * 4) / 4;
+  hipLaunchKernelGGL(k_weight_ema, dim3(blocks(RC, kPT)), dim3(kPT), 0, s, W, RC, (int)C, (int)R, a.m, a.M, Wt, WuT);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // both factors from the U and V before this update
-  if ((e = cholesky(a.V, (int)C, 1.0f, LV, a.info, s)) != hipSuccess) return e;
-  if ((e = cholesky(a.U, (int)R, 1.0f, LU, a.info + 1, s)) != hipSuccess) return e;
-  // Wt = Wc LV^-T (each row r of Wc: LV x = w_r), Wu = LU^-1 Wc (each column c)
-  if ((e = trsv(LV, (int)C, Wc, Wt, R, C, 1, s)) != hipSuccess) return e;
-  if ((e = trsv(LU, (int)R, Wc, Wu, C, 1, C, s)) != hipSuccess) return e;
+  if ((e = cholesky(a.V, (int)C, 1.0f, LV, a.info, sc, P, s)) != hipSuccess) return e;
+  if ((e = cholesky(a.U, (int)R, 1.0f, LU, a.info + 1, sc, P, s)) != hipSuccess) return e;
+  // Wt = Wc LV^-T (rows of Wc); WuT = Wc^T LU^-T = (LU^-1 Wc)^T (rows of Wc^T)
+  if ((e = trsm_rows(Wt, R, (int)C, LV, P, s)) != hipSuccess) return e;
+  if ((e = trsm_rows(WuT, C, (int)R, LU, P, s)) != hipSuccess) return e;
   // U <- m U + (1 - m) Wt Wt^T / C;  V <- m V + (1 - m) Wu^T Wu / R
   ReduceJob r{};
   r.beta = a.m;
@@ -401,7 +470,7 @@ hipError_t probe_weight_update(const ProbeWeightLaunch& a, hipStream_t s) {
   if ((e = gemm(GemmJob{R, R, C, 0, Wt, C, 1, Wt, C, 1, P}, r, s)) != hipSuccess) return e;
   r.alpha = (1.0f - a.m) / (float)R;
   r.C = a.V;
-  if ((e = gemm(GemmJob{C, C, R, 0, Wu, 1, C, Wu, 1, C, P}, r, s)) != hipSuccess) return e;
+  if ((e = gemm(GemmJob{C, C, R, 0, WuT, R, 1, WuT, R, 1, P}, r, s)) != hipSuccess) return e;
   hipLaunchKernelGGL(k_trace, dim3(1), dim3(kPT), 0, s, a.U, (int)R, sc);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_renorm, dim3(blocks(max(R * R, C * C), kPT)), dim3(kPT), 0, s, sc, R * R, C * C, a.U, a.V);
@@ -409,7 +478,8 @@ hipError_t probe_weight_update(const ProbeWeightLaunch& a, hipStream_t s) {
 }
 
 size_t probe_sample_input_ws(int64_t B, int64_t K) {
-  return al256((size_t)K * K * 4) + al256((size_t)B * K * 4) + al256((size_t)gemm_splits(K) * B * K * 4);
+  return al256((size_t)K * K * 4) + al256((size_t)B * K * 4) +
+         al256((size_t)max(gemm_splits(K) * B * K, K * K) * 4) + 256;
 }
 
 hipError_t probe_sample_input(const ProbeSampleInputLaunch& a, hipStream_t s) {
@@ -418,8 +488,9 @@ hipError_t probe_sample_input(const ProbeSampleInputLaunch& a, hipStream_t s) {
   float* L = reinterpret_cast<float*>(ws);
   float* Z = reinterpret_cast<float*>(ws + al256((size_t)K * K * 4));
   float* P = Z + al256((size_t)B * K * 4) / 4;
+  float* sc = P + al256((size_t)max(gemm_splits(K) * B * K, K * K) * 4) / 4;
   // L L^T = S / (n - 1) + eps I
-  hipError_t e = cholesky(a.S, (int)K, (float)(1.0 / (double)(a.n - 1)), L, a.info, s);
+  hipError_t e = cholesky(a.S, (int)K, (float)(1.0 / (double)(a.n - 1)), L, a.info, sc, P, s);
   if (e != hipSuccess) return e;
   if ((e = normals(Z, B * K, a.seed, s)) != hipSuccess) return e;
   // T' = 1 mu^T + Z L^T, bf16
@@ -432,7 +503,7 @@ hipError_t probe_sample_input(const ProbeSampleInputLaunch& a, hipStream_t s) {
 
 size_t probe_sample_weight_ws(int64_t R, int64_t C) {
   return al256((size_t)R * R * 4) + al256((size_t)C * C * 4) + 2 * al256((size_t)R * C * 4) +
-         al256((size_t)max(gemm_splits(C), gemm_splits(R)) * R * C * 4);
+         al256((size_t)max(max(gemm_splits(C), gemm_splits(R)) * R * C, max(R * R, C * C)) * 4) + 256;
 }
 
 hipError_t probe_sample_weight(const ProbeSampleWeightLaunch& a, hipStream_t s) {
@@ -443,9 +514,10 @@ hipError_t probe_sample_weight(const ProbeSampleWeightLaunch& a, hipStream_t s) 
   float* Z = LV + al256((size_t)C * C * 4) / 4;
   float* Y = Z + al256((size_t)R * C * 4) / 4;
   float* P = Y + al256((size_t)R * C * 4) / 4;
+  float* sc = P + al256((size_t)max(max(gemm_splits(C), gemm_splits(R)) * R * C, max(R * R, C * C)) * 4) / 4;
   hipError_t e;
-  if ((e = cholesky(a.U, (int)R, 1.0f, LU, a.info, s)) != hipSuccess) return e;
-  if ((e = cholesky(a.V, (int)C, 1.0f, LV, a.info + 1, s)) != hipSuccess) return e;
+  if ((e = cholesky(a.U, (int)R, 1.0f, LU, a.info, sc, P, s)) != hipSuccess) return e;
+  if ((e = cholesky(a.V, (int)C, 1.0f, LV, a.info + 1, sc, P, s)) != hipSuccess) return e;
   if ((e = normals(Z, R * C, a.seed, s)) != hipSuccess) return e;
   // Y = Z LV^T, then W' = M + LU Y (bf16)
   ReduceJob r{};
