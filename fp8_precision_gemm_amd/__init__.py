@@ -48,7 +48,8 @@ class FwdArgs(ctypes.Structure):
     _fields_ = [("M", c_i64), ("N", c_i64), ("K", c_i64), ("x_mode", c_i32), ("flags", c_i32), ("eps", c_f32),
                 ("x", c_vp), ("qw", c_vp), ("sw", c_vp), ("bias", c_vp), ("gamma", c_vp), ("beta", c_vp),
                 ("y", c_vp), ("z", c_vp), ("mean", c_vp), ("rstd", c_vp), ("qx_out", c_vp), ("sx_out", c_vp),
-                ("workspace", c_vp), ("workspace_bytes", c_sz), ("x_scales", c_vp)]
+                ("workspace", c_vp), ("workspace_bytes", c_sz), ("x_scales", c_vp), ("y_codes", c_vp),
+                ("y_scales", c_vp)]
 
 
 class BwdArgs(ctypes.Structure):
@@ -239,18 +240,19 @@ def loka_quant_fp8(src, fmt="e4m3", mode="row", transpose_out=False, codes=None,
 
 
 def _fwd_args(x, qw, sw, bias, gamma, beta, eps, x_mode, y, z, mean, rstd, qx_out, sx_out, w_packed=False,
-              epilogue="layernorm", x_scales=None):
+              epilogue="layernorm", x_scales=None, y_codes=None, y_scales=None):
     M, K = x.shape
     N = qw.shape[0]
     flags = (FWD_W_PACKED if w_packed else 0) | EPILOGUES[epilogue]
     return FwdArgs(M=M, N=N, K=K, x_mode=MODES[x_mode], flags=flags, eps=eps, x=_ptr(x), qw=_ptr(qw), sw=_ptr(sw),
                    bias=_ptr(bias), gamma=_ptr(gamma), beta=_ptr(beta), y=_ptr(y), z=_ptr(z), mean=_ptr(mean),
-                   rstd=_ptr(rstd), qx_out=_ptr(qx_out), sx_out=_ptr(sx_out), x_scales=_ptr(x_scales))
+                   rstd=_ptr(rstd), qx_out=_ptr(qx_out), sx_out=_ptr(sx_out), x_scales=_ptr(x_scales),
+                   y_codes=_ptr(y_codes), y_scales=_ptr(y_scales))
 
 
 def loka_gemm_fp8_ln(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e-5, x_mode="row", y=None, want_z=False,
                      want_stats=False, want_qx=False, workspace=None, stream=None, prepare=False, w_packed=False,
-                     epilogue="layernorm", x_scales=None):
+                     epilogue="layernorm", x_scales=None, want_y_square=False):
     """Y = LayerNorm(dequant(q(X) . q(W)) + bias) for bf16 X [M, K] and the
     pre-quantized weight qw [N, K] (e4m3) with scales sw; with w_packed=True
     qw is in the packed layout (loka_quant_fp8(transpose_out="packed")).
@@ -259,6 +261,9 @@ def loka_gemm_fp8_ln(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e-5, x_mo
     x_mode="mx32_sq": x is X already quantized (uint8 e4m3 codes [M, K] from
     loka_quant_fp8(mode="mx32_sq")) and x_scales its E8M0 scales
     [M/32, K/32]; the weight is quantized with mode="mx32_sq" too.
+    want_y_square: Y also as e4m3 codes [M, N] and E8M0 scales [M/32, N/32]
+    in 32 x 32 blocks (out["y_codes"], out["y_scales"]): the next layer's
+    x_mode="mx32_sq" input.
 
     Returns a dict with y and the requested optional outputs.  With
     prepare=True returns (launch, outputs) where launch() enqueues the call
@@ -289,8 +294,12 @@ def loka_gemm_fp8_ln(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e-5, x_mo
             out["sx"] = torch.empty(M, dtype=torch.float32, device=dev)
         else:
             out["sx"] = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
+    if want_y_square:
+        out["y_codes"] = torch.empty((M, N), dtype=torch.uint8, device=dev)
+        out["y_scales"] = torch.empty((M // 32, N // 32), dtype=torch.uint8, device=dev)
     a = _fwd_args(x, qw, sw, bias, gamma, beta, eps, x_mode, out["y"], out.get("z"), out.get("mean"),
-                  out.get("rstd"), out.get("qx"), out.get("sx"), w_packed, epilogue, x_scales)
+                  out.get("rstd"), out.get("qx"), out.get("sx"), w_packed, epilogue, x_scales, out.get("y_codes"),
+                  out.get("y_scales"))
     lib = library()
     nb = lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(a))
     ws = _workspace(nb, dev, workspace)

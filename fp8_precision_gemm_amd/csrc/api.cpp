@@ -181,6 +181,15 @@ loka_status loka_gemm_fp8_ln(const loka_fwd_args* a, void* stream) {
   } else {
     REQUIRE(a->x_scales == nullptr, LOKA_ERR_INVALID_ARG, "x_scales is only for x_mode MX32_SQ");
   }
+  if (a->y_codes != nullptr || a->y_scales != nullptr) {
+    REQUIRE(a->y_codes != nullptr && a->y_scales != nullptr, LOKA_ERR_INVALID_ARG,
+            "y_codes and y_scales go together");
+    REQUIRE(!blocknorm && (a->N == 256 || a->N == 512) && loka::fwd_weight_resident(a->N, a->K) && a->M % 32 == 0,
+            LOKA_ERR_UNSUPPORTED,
+            "the square-block Y output needs the LayerNorm epilogue, N = 256 or 512, the weight-resident shapes and "
+            "M %% 32 == 0 (got M=%lld N=%lld K=%lld)",
+            (long long)a->M, (long long)a->N, (long long)a->K);
+  }
   if ((st = check_eps(a->eps)) != LOKA_OK) return st;
   if (a->M > 0) REQUIRE(a->x && a->qw && a->sw && a->y, LOKA_ERR_INVALID_ARG, "x, qw, sw and y are required");
   REQUIRE_ALIGNED(a->x); REQUIRE_ALIGNED(a->qw); REQUIRE_ALIGNED(a->sw); REQUIRE_ALIGNED(a->bias);
@@ -194,6 +203,8 @@ loka_status loka_gemm_fp8_ln(const loka_fwd_args* a, void* stream) {
   f.y = a->y; f.z = a->z; f.mean = a->mean; f.rstd = a->rstd; f.qx_out = a->qx_out; f.sx_out = a->sx_out;
   f.workspace = a->workspace;
   f.x_scales = a->x_scales;
+  f.y_codes = a->y_codes;
+  f.y_scales = a->y_scales;
   f.w_packed = packed;
   f.blocknorm = blocknorm;
   return hip_status(loka::launch_fwd(f, static_cast<hipStream_t>(stream)), "loka_gemm_fp8_ln");

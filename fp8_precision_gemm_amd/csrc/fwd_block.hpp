@@ -62,6 +62,9 @@ struct FwdBlock {
   // and E8M0 scales [M/32][K/32]
   const uint8_t* xq;
   const uint8_t* xs;
+  // optional: Y quantized in 32 x 32 blocks (e4m3 [M][N], E8M0 [M/32][N/32])
+  uint8_t* y_codes;
+  uint8_t* y_scales;
 };
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));

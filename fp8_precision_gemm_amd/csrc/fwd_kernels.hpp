@@ -48,9 +48,12 @@ __global__ __launch_bounds__(kThreads) void k_fwd_res(FwdBlock p, const float* p
     p.x_r = sp.r;
     p.x_s = sp.s;
   }
-  // a contiguous, balanced range of 16-row tiles per workgroup
+  // a contiguous, balanced range of 16-row tiles per workgroup (of tile
+  // pairs when Y also leaves in 32 x 32 blocks: a block is two tiles)
   const int64_t T = (p.M + kResRows - 1) / kResRows, G = gridDim.x, b = blockIdx.x;
-  ResBlock<MODE, NT, KC, OPT, FULL> blk(p, b * T / G, (b + 1) * T / G, smem);
+  const bool pairs = OPT && p.y_codes != nullptr;
+  const int64_t tb = pairs ? 2 * (b * (T / 2) / G) : b * T / G, te = pairs ? 2 * ((b + 1) * (T / 2) / G) : (b + 1) * T / G;
+  ResBlock<MODE, NT, KC, OPT, FULL> blk(p, tb, te, smem);
   blk.run();
 }
 
@@ -58,7 +61,7 @@ template <int MODE, int NT, int KC>
 hipError_t launch_res_t(const FwdBlock& p, const float* partials, int np, int grid, hipStream_t s) {
   const size_t lds = (size_t)res_lds(NT, KC, p.N).total;
   const bool opt = p.z != nullptr || p.mean != nullptr || p.rstd != nullptr || p.qx_out != nullptr ||
-                   p.sx_out != nullptr;
+                   p.sx_out != nullptr || p.y_codes != nullptr;
   const bool full = res_full(p.M, p.N, p.K, NT, KC);
   auto kern = opt ? (full ? k_fwd_res<MODE, NT, KC, true, true> : k_fwd_res<MODE, NT, KC, true, false>)
                   : (full ? k_fwd_res<MODE, NT, KC, false, true> : k_fwd_res<MODE, NT, KC, false, false>);

@@ -110,9 +110,11 @@ __host__ __device__ constexpr int res_shape(int nt, int kc) {
 // LDS carve-up (bytes, every part 16-byte aligned):
 //   codes [2][16][LDX] u8 | xe8 [2][16][XE] u8 | rs [2][16] f32 |
 //   red [2][16][kRedRow] float2 | cvec [4][N] f32 (s_w, bias, gamma, beta) |
-//   wmx [3][8] f32 | ystg [8][16][32*NT + 16] (each wavefront's Y block)
+//   wmx [3][8] f32 | ystg [8][16][32*NT + 16] (each wavefront's Y block) |
+//   yprev [8][16][32*NT + 16] (the previous tile's Y block, for the Y output
+//   quantized in 32 x 32 blocks)
 struct ResLds {
-  int codes, xe8, rs, red, cvec, wmx, ystg, total;
+  int codes, xe8, rs, red, cvec, wmx, ystg, yprev, total;
 };
 __host__ __device__ constexpr int res_yst(int nt) { return 32 * nt + 16; }  // Y staging row stride (bytes)
 __host__ __device__ inline ResLds res_lds(int nt, int kc, int N) {
@@ -125,7 +127,8 @@ __host__ __device__ inline ResLds res_lds(int nt, int kc, int N) {
   l.cvec = l.red + 2 * kResRows * kRedRow * 8;
   l.wmx = l.cvec + 4 * N * 4;
   l.ystg = l.wmx + 32 * 4;
-  l.total = l.ystg + kWaves * kResRows * res_yst(nt);
+  l.yprev = l.ystg + kWaves * kResRows * res_yst(nt);
+  l.total = l.yprev + kWaves * kResRows * res_yst(nt);
   return l;
 }
 
@@ -222,6 +225,8 @@ struct ResBlock {
   float* cvec;
   float* wmx;
   uint8_t* ystg;  // this wavefront's Y staging block [16][res_yst(NT)]
+  uint8_t* yprev;  // its copy of the previous (even) tile's block, square-block Y output
+  float sq_prev[NT / 2 > 0 ? NT / 2 : 1];  // that tile's 16 x 32 maxima per 32-column block
   float bw, bb;   // bound on |z|: row factor (tensor/row: 448^2 K max s_w; MX: 448^2 K 2^(ew_max-127)), max |bias|
   float inv_nw;   // 1 / (columns of this wavefront's slice)
 
@@ -267,6 +272,7 @@ struct ResBlock {
     cvec = reinterpret_cast<float*>(smem + l.cvec);
     wmx = reinterpret_cast<float*>(smem + l.wmx);
     ystg = smem + l.ystg + wave * (kResRows * res_yst(NT));
+    yprev = smem + l.yprev + wave * (kResRows * res_yst(NT));
   }
 
   // ---- X row of tile `t` for this lane into register slot S: elements
@@ -698,6 +704,58 @@ struct ResBlock {
       }
     }
     store_y(t);
+    if constexpr (OPT && NT % 2 == 0) {
+      if (p.y_codes != nullptr) square_y(t);
+    }
+  }
+
+  // Y also leaves quantized in 32 x 32 blocks (e4m3 codes and E8M0 scales,
+  // the square-block recipe's input for the next layer: the activation
+  // quantization fused into the normalization that produces it, the GEM
+  // page's PreNorm fusion).  The codes are those of the bf16 Y: the same as
+  // quantizing the stored Y.  A block is two 16-row tiles (the workgroup's
+  // tile range starts on a pair) by two of this wavefront's 16-column tiles;
+  // the even tile keeps its Y block and its maxima, the odd one completes
+  // the block.  N = 128 NT with NT even and M % 32 == 0 (checked by the
+  // entry point), so every tile and row is real.
+  __device__ __forceinline__ void square_y(int64_t t) {
+    constexpr int YST = res_yst(NT), NB = NT / 2;
+    uint2 cur[NT];
+    float bm[NB];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) bm[cb] = 0.0f;
+#pragma unroll
+    for (int t2 = 0; t2 < NT; ++t2) {
+      cur[t2] = *reinterpret_cast<const uint2*>(ystg + r * YST + (16 * t2 + 4 * g) * 2);
+      bm[t2 >> 1] = fmaxf(bm[t2 >> 1], fmaxf(fmaxf(fabsf(bf16_lo(cur[t2].x)), fabsf(bf16_hi(cur[t2].x))),
+                                             fmaxf(fabsf(bf16_lo(cur[t2].y)), fabsf(bf16_hi(cur[t2].y)))));
+    }
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) bm[cb] = rows4_max(row16_max(bm[cb]));
+    if ((t & 1) == 0) {
+#pragma unroll
+      for (int t2 = 0; t2 < NT; ++t2) *reinterpret_cast<uint2*>(yprev + r * YST + (16 * t2 + 4 * g) * 2) = cur[t2];
+#pragma unroll
+      for (int cb = 0; cb < NB; ++cb) sq_prev[cb] = bm[cb];
+      return;
+    }
+    const int64_t m1 = t * kResRows + r, m0 = m1 - kResRows;
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+      const int e8 = e8m0_from_amax<0>(fmaxf(bm[cb], sq_prev[cb]));
+      const float mu = e8m0_inv_multiplier(e8);
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t2 = 2 * cb + h, col = c0 + 16 * t2 + 4 * g;
+        const uint2 pv = *reinterpret_cast<const uint2*>(yprev + r * YST + (16 * t2 + 4 * g) * 2);
+        const uint32_t qp = cvt4<0>(bf16_lo(pv.x) * mu, bf16_hi(pv.x) * mu, bf16_lo(pv.y) * mu, bf16_hi(pv.y) * mu);
+        const uint32_t qc = cvt4<0>(bf16_lo(cur[t2].x) * mu, bf16_hi(cur[t2].x) * mu, bf16_lo(cur[t2].y) * mu,
+                                    bf16_hi(cur[t2].y) * mu);
+        *reinterpret_cast<uint32_t*>(p.y_codes + m0 * N + col) = qp;
+        *reinterpret_cast<uint32_t*>(p.y_codes + m1 * N + col) = qc;
+      }
+      if (lane == 0) p.y_scales[(t >> 1) * (N >> 5) + (c0 >> 5) + cb] = (uint8_t)e8;
+    }
   }
 
   // BlockNorm + Hard Swish (after the barrier): the 256-column block of this

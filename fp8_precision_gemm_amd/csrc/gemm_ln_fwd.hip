@@ -91,7 +91,7 @@ size_t fwd_workspace_bytes(int64_t M, int64_t N, int64_t K, int x_mode, bool w_p
 
 hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s) {
   if (a.M == 0) return hipSuccess;
-  fwd::FwdBlock p;
+  fwd::FwdBlock p{};
   p.M = a.M; p.N = (int)a.N; p.K = (int)a.K;
   p.x = static_cast<const uint16_t*>(a.x);
   p.qw = a.qw; p.sw = a.sw;
@@ -103,6 +103,7 @@ hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s) {
   p.eps = a.eps; p.x_r = 1.0f; p.x_s = 1.0f;
   p.ldy = (int)a.N;
   p.xq = nullptr; p.xs = nullptr;
+  p.y_codes = a.y_codes; p.y_scales = a.y_scales;
   if (a.x_mode == 5) {
     p.xq = static_cast<const uint8_t*>(a.x);
     p.xs = a.x_scales;

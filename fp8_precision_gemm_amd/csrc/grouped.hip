@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped_res(const GroupDev* groups
     while (tile_pre[g + 1] <= t) ++g;  // past finished groups and those of other classes
     const int seg_end = min(tend, tile_pre[g + 1]);
     const GroupDev gd = groups[g];
-    FwdBlock p;
+    FwdBlock p{};
     p.M = gd.M; p.N = (int)gd.N; p.K = (int)gd.K;
     p.x = static_cast<const uint16_t*>(gd.x);
     p.qw = group_weight(wsrc, gd, g); p.sw = gd.sw;
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped_res_arg(const GroupDev* gr
     while (plan.tile_pre[q + 1] <= t) ++q;  // past finished and empty groups
     const int seg_end = min(tend, plan.tile_pre[q + 1]);
     const GroupDev gd = groups[plan.gid[q]];
-    FwdBlock p;
+    FwdBlock p{};
     p.M = gd.M; p.N = (int)gd.N; p.K = (int)gd.K;
     p.x = static_cast<const uint16_t*>(gd.x);
     p.qw = group_weight(wsrc, gd, plan.gid[q]); p.sw = gd.sw;

@@ -63,6 +63,8 @@ struct FwdLaunch {
   void* sx_out;
   void* workspace;
   const uint8_t* x_scales;  // square-block recipe: X's E8M0 scales [M/32][K/32] (x holds its codes)
+  uint8_t* y_codes;         // optional: Y quantized in 32 x 32 blocks, e4m3 [M][N]
+  uint8_t* y_scales;        //   and its E8M0 scales [M/32][N/32]
   bool w_packed;   // qw already in the fragment-interleaved layout
   bool blocknorm;  // BlockNorm(256) + Hard Swish epilogue instead of LayerNorm
 };

@@ -173,6 +173,13 @@ loka_status loka_quant_fp8(const loka_quant_args* args, void* stream);
  *           transpose_out 0) writes them -- and the same codes serve the
  *           backward.  Needs M % 32 == 0, the weight-resident shapes and
  *           qx_out = sx_out = NULL; x_scales must be NULL in other modes.
+ *   y_codes, y_scales (optional, together; LayerNorm epilogue, any x_mode):
+ *           Y also leaves quantized in 32 x 32 blocks -- the next layer's
+ *           MX32_SQ input, with the activation quantization fused into the
+ *           normalization that produces it (GEM "Handling Quantization
+ *           Overhead", PreNorm fusion).  The codes and scales equal
+ *           loka_quant_fp8(Y, e4m3, MX32_SQ) of the bf16 Y.  Needs N = 256 or
+ *           512, the weight-resident shapes and M % 32 == 0.
  *   bias, gamma, beta  bf16 [N] or NULL (NULL = 0, 1, 0; NULL bias is the
  *           No-Bias mode).
  *   Z[m,n]  = acc[m,n] * s_x[m] * s_w[n] + bias[n]   (MX: the E8M0 scales
@@ -227,6 +234,8 @@ typedef struct {
   void* workspace;
   size_t workspace_bytes;
   const uint8_t* x_scales; /* MX32_SQ only: X's E8M0 scales [M/32][K/32] */
+  uint8_t* y_codes;        /* optional (with y_scales): Y in 32 x 32 blocks, e4m3 [M, N] */
+  uint8_t* y_scales;       /* optional (with y_codes): their E8M0 scales [M/32][N/32] */
 } loka_fwd_args;
 
 size_t loka_gemm_fp8_ln_workspace_size(const loka_fwd_args* args);

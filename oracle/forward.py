@@ -149,6 +149,14 @@ def gemm_blocknorm_hswish_forward(x_bits, w_bits, bias_bits=None, eps=1e-5, reci
     return {"y_bits": f64_to_bf16(y), "y": y, "z": z, "rinv": rinv, "qx": qx, "sx": sx, "qw": qw, "sw": sw}
 
 
+def square_quantized_output(y_bits):
+    """The block's output Y quantized in 32 x 32 blocks, e4m3 (reading R16:
+    the next layer's square-block input, its quantization fused into the
+    normalization that produces Y -- [GEM] "Handling Quantization
+    Overhead", PreNorm fusion): the codes and scales of the bf16 Y."""
+    return quantize(bf16_to_f64(y_bits), MX32_SQ, E4M3)
+
+
 def reference_forward(x_bits, w_bits, bias_bits=None, gamma_bits=None, beta_bits=None, eps=1e-5):
     """The unquantized bf16 reference: the same block on the bf16 inputs taken
     exactly in fp64 (what the quantization error is measured against)."""

@@ -213,3 +213,70 @@ def test_square_backward_rejects_unsupported(lib):
     c = forward_case(64, 64, 640, seed=1, dy_var=1e-3)
     with pytest.raises(LokaError):  # N > 512 is outside the square-block backward
         run_square_bwd(lib, c, no_ln=True, fast_check=False)
+
+
+# ---- Y leaving in 32 x 32 blocks (the next layer's square-block input) -------
+# With want_y_square the LayerNorm epilogue also writes Y's e4m3 codes and
+# E8M0 block scales.  They must be bit-identical to quantizing the stored Y
+# with loka_quant_fp8 (the definition of the output), Y itself unchanged, and
+# against the oracle (forward.square_quantized_output of the oracle's Y) the
+# decoded values must agree within Y's tolerance plus one e4m3 spacing.
+
+@pytest.mark.parametrize("x_mode,M,K,N", [("row", 16384, 512, 512), ("row", 96, 160, 256), ("tensor", 224, 256, 512),
+                                          ("mx32_row", 64, 1024, 256), ("mx32_sq", 320, 512, 512)])
+def test_fused_y_square_output(lib, x_mode, M, K, N):
+    c = outlier_case() if M == 16384 else forward_case(M, K, N, seed=M + K, x_dist="student_t3_outliers",
+                                                       gamma_var=0.1, beta_var=0.1)
+    x, w = bf16_dev(c["x"]), bf16_dev(c["w"])
+    wmode = {"row": "col", "tensor": "tensor", "mx32_row": "mx32_col", "mx32_sq": "mx32_sq"}[x_mode]
+    qw, sw, _ = lib.loka_quant_fp8(w, mode=wmode, transpose_out="packed")
+    vec = dict(bias=bf16_dev(c["bias"]), gamma=bf16_dev(c["gamma"]), beta=bf16_dev(c["beta"]), x_mode=x_mode,
+               w_packed=True)
+    xin = x
+    if x_mode == "mx32_sq":
+        xin, sx, _ = lib.loka_quant_fp8(x, mode="mx32_sq")
+        vec["x_scales"] = sx
+    out = lib.loka_gemm_fp8_ln(xin, qw, sw, want_y_square=True, **vec)
+    plain = lib.loka_gemm_fp8_ln(xin, qw, sw, **vec)
+    qy, sy, _ = lib.loka_quant_fp8(out["y"], mode="mx32_sq")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(out["y"]), host(plain["y"]), err_msg="Y changed")
+    np.testing.assert_array_equal(host(out["y_codes"]), host(qy), err_msg="codes differ from quantizing Y")
+    np.testing.assert_array_equal(host(out["y_scales"]), host(sy), err_msg="scales differ from quantizing Y")
+    rows = sample_blocks(M, 24) if M == 16384 else np.arange(M)
+    recipe = {"row": "row", "tensor": "tensor", "mx32_row": "mx32", "mx32_sq": "mx32_sq"}[x_mode]
+    o = forward.gemm_ln_forward(c["x"][rows], c["w"], c["bias"], c["gamma"], c["beta"], recipe=recipe)
+    qo, so = forward.square_quantized_output(o["y_bits"])
+    got = quant.dequantize(host(out["y_codes"])[rows], host(out["y_scales"])[rows[::32] // 32], quant.MX32_SQ, E4M3)
+    want = quant.dequantize(qo, so, quant.MX32_SQ, E4M3)
+    blk = np.repeat(np.repeat(np.exp2(so.astype(np.float64) - 127), 32, axis=0), 32, axis=1)
+    y_err = np.abs(codec.bf16_to_f64(host(out["y"])[rows]) - o["y"])
+    # one e4m3 spacing at the value (relative 2^-3), the subnormal spacing of
+    # the block (2^-9 of its scale) and the Y deviation, doubled for a scale
+    # that may differ by one
+    tol = 2 * (0.125 * np.abs(want) + 2.0 ** -9 * 448 * blk / 256 + y_err) + 1e-30
+    assert np.all(np.abs(got - want) <= tol), f"worst {np.max(np.abs(got - want) / tol):.3f} x tol"
+
+
+def test_fused_y_square_feeds_the_next_layer(lib):
+    c1 = forward_case(256, 256, 512, seed=21, x_dist="student_t3_outliers", gamma_var=0.1, beta_var=0.1)
+    c2 = forward_case(256, 512, 256, seed=22, gamma_var=0.1, beta_var=0.1)
+    qw1, sw1, _ = lib.loka_quant_fp8(bf16_dev(c1["w"]), mode="col", transpose_out="packed")
+    l1 = lib.loka_gemm_fp8_ln(bf16_dev(c1["x"]), qw1, sw1, bf16_dev(c1["bias"]), bf16_dev(c1["gamma"]),
+                              bf16_dev(c1["beta"]), w_packed=True, want_y_square=True)
+    qw2, sw2, _ = lib.loka_quant_fp8(bf16_dev(c2["w"]), mode="mx32_sq", transpose_out="packed")
+    vec2 = dict(bias=bf16_dev(c2["bias"]), gamma=bf16_dev(c2["gamma"]), beta=bf16_dev(c2["beta"]), x_mode="mx32_sq",
+                w_packed=True)
+    fused = lib.loka_gemm_fp8_ln(l1["y_codes"], qw2, sw2, x_scales=l1["y_scales"], **vec2)
+    qy, sy, _ = lib.loka_quant_fp8(l1["y"], mode="mx32_sq")
+    sep = lib.loka_gemm_fp8_ln(qy, qw2, sw2, x_scales=sy, **vec2)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(fused["y"]), host(sep["y"]))
+
+
+def test_fused_y_square_rejects_unsupported(lib):
+    from fp8_precision_gemm_amd import LokaError
+    c = forward_case(64, 128, 384, seed=2)
+    qw, sw, _ = lib.loka_quant_fp8(bf16_dev(c["w"]), mode="col", transpose_out=True)
+    with pytest.raises(LokaError):  # N = 384: not 256 or 512
+        lib.loka_gemm_fp8_ln(bf16_dev(c["x"]), qw, sw, want_y_square=True)
