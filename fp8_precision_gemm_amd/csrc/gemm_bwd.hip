@@ -564,18 +564,33 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
 // SQ: both operands carry E8M0 scales per 32 x 32 block (dZ's [M/32][N/32],
 // X's [M/32][K/32]), applied by the MFMA: lane group g of chunk c supplies
 // M block 4c + g (clamped past M, where the codes are zero).
+// Eight wavefronts: wavefront w owns the 64 x 64 sub-tile w % 4 over one half
+// of the slice's chunks (two wavefronts per SIMD); the second half's sums
+// join the first's through LDS, in a fixed order.
 template <bool SQ>
-__global__ __launch_bounds__(256) void k_wgrad(const uint8_t* dzt, const uint8_t* xt, int64_t M, int N, int K,
+__global__ __launch_bounds__(512) void k_wgrad(const uint8_t* dzt, const uint8_t* xt, int64_t M, int N, int K,
                                                int64_t chunks_per_split, float* part, const uint8_t* sdz,
                                                const uint8_t* sx8) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ v4f wred[4][16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, sub = wave & 3, half = wave >> 2;
   const int r = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * 128 + (wave & 1) * 64;
-  const int k0 = blockIdx.y * 128 + (wave >> 1) * 64;
+  // 1-D grid of (N/128) x (K/128) tiles x slices.  Consecutive workgroups go
+  // to the 8 XCDs in turn, and each XCD has its own L2: when the count is a
+  // multiple of 8, workgroup i is given the (i % 8)-th eighth of the
+  // slice-major order, so the tiles of one slice -- which read the same M
+  // rows of both operands -- share an XCD and its L2.
+  const int nx = (N + 127) / 128, ny = (K + 127) / 128;
+  const int total = (int)gridDim.x, id = (int)blockIdx.x;
+  const int lin = (total & 7) == 0 ? (id & 7) * (total >> 3) + (id >> 3) : id;
+  const int bz = lin / (nx * ny), tl = lin - bz * (nx * ny), by = tl / nx, bx = tl - by * nx;
+  const int n0 = bx * 128 + (sub & 1) * 64;
+  const int k0 = by * 128 + (sub >> 1) * 64;
   const int64_t nch = (M + 127) / 128;
-  const int64_t cs = (int64_t)blockIdx.z * chunks_per_split;
-  int64_t ce = cs + chunks_per_split;
-  if (ce > nch) ce = nch;
+  const int64_t c0s = (int64_t)bz * chunks_per_split;
+  int64_t c0e = c0s + chunks_per_split;
+  if (c0e > nch) c0e = nch;
+  const int64_t mid = c0s + (c0e - c0s + 1) / 2;
+  const int64_t cs = half ? mid : c0s, ce = half ? c0e : mid;
   v4f acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
@@ -622,13 +637,22 @@ __global__ __launch_bounds__(256) void k_wgrad(const uint8_t* dzt, const uint8_t
         sb[a] = sbn[a];
       }
     }
+  }
+  if (half == 1) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) wred[sub][4 * a + b][lane] = acc[a][b];
+  }
+  __syncthreads();
+  if (half == 0 && nin && kin) {
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
+        const v4f o = acc[a][b] + wred[sub][4 * a + b][lane];
         const int n = n0 + 16 * a + 4 * g, k = k0 + 16 * b + r;
-        *reinterpret_cast<float4*>(part + ((int64_t)blockIdx.z * K + k) * N + n) =
-            make_float4(acc[a][b][0], acc[a][b][1], acc[a][b][2], acc[a][b][3]);
+        *reinterpret_cast<float4*>(part + ((int64_t)bz * K + k) * N + n) = make_float4(o[0], o[1], o[2], o[3]);
       }
   }
 }
@@ -869,8 +893,8 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
     if ((e = launch_relayout_sq(a.qw, a.N, a.K, ws + w.qwi, ws + w.qwri, a.qx, a.M, xt, s)) != hipSuccess) return e;
     if ((e = launch_main_t<4, 4, 8, true>(p, a.no_ln, s)) != hipSuccess) return e;
     float* wpart = reinterpret_cast<float*>(ws + w.wpart);
-    dim3 g((unsigned)((a.N + 127) / 128), (unsigned)((a.K + 127) / 128), (unsigned)w.nsplit);
-    hipLaunchKernelGGL(k_wgrad<true>, g, dim3(256), 0, s, p.dzt, xt, a.M, (int)a.N, (int)a.K,
+    dim3 g((unsigned)(((a.N + 127) / 128) * ((a.K + 127) / 128) * w.nsplit));
+    hipLaunchKernelGGL(k_wgrad<true>, g, dim3(512), 0, s, p.dzt, xt, a.M, (int)a.N, (int)a.K,
                        (int64_t)(kWgSplitRows / 128), wpart, p.sdz, p.sx8);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t tot = a.K * a.N;
@@ -910,8 +934,8 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
   if ((e = launch_col_quant_pair(jx, jd, s)) != hipSuccess) return e;
 
   float* wpart = reinterpret_cast<float*>(ws + w.wpart);
-  dim3 g((unsigned)((a.N + 127) / 128), (unsigned)((a.K + 127) / 128), (unsigned)w.nsplit);
-  hipLaunchKernelGGL(k_wgrad<false>, g, dim3(256), 0, s, dzt, xt, a.M, (int)a.N, (int)a.K,
+  dim3 g((unsigned)(((a.N + 127) / 128) * ((a.K + 127) / 128) * w.nsplit));
+  hipLaunchKernelGGL(k_wgrad<false>, g, dim3(512), 0, s, dzt, xt, a.M, (int)a.N, (int)a.K,
                      (int64_t)(kWgSplitRows / 128), wpart, (const uint8_t*)nullptr, (const uint8_t*)nullptr);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
