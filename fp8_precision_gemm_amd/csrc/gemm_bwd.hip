@@ -150,17 +150,47 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
     // too: all requests go out before the first wait, so one HBM latency
     // covers both, and the two LayerNorm passes read dY from LDS
     const int k16 = K / 16, n8 = SDY ? N / 8 : 0, n8d = SDY ? n8 : 1;
-    for (int u = tid; u < kBM * (k16 + n8); u += 64 * WAVES) {
-      if (u < kBM * k16) {
-        const int lr = u / k16, c = (u - lr * k16) * 16;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (FULLM || m0 + lr < p.M) v = *reinterpret_cast<const uint4*>(p.qx + (m0 + lr) * K + c);
-        *reinterpret_cast<uint4*>(xs + lr * ldk + c) = v;
-      } else {
-        const int v8 = u - kBM * k16, lr = v8 / n8d, c = (v8 - lr * n8d) * 8;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (FULLM || m0 + lr < p.M) v = *reinterpret_cast<const uint4*>(p.dy + (m0 + lr) * N + c);
-        *reinterpret_cast<uint4*>(dys + lr * ldy + 2 * c) = v;
+    if constexpr (SDY) {
+      // N, K <= 512: at most 32 / WAVES pieces of X codes and 64 / WAVES of
+      // dY per thread; every load is issued before the first wait, so the
+      // staging costs one memory round trip instead of one per piece
+      constexpr int XP = 32 / WAVES, YP = 64 / WAVES;
+      uint4 xv[XP], yv[YP];
+#pragma unroll
+      for (int q = 0; q < XP; ++q) {
+        const int u = tid + q * 64 * WAVES, lr = u / k16, c = (u - lr * k16) * 16;
+        xv[q] = make_uint4(0, 0, 0, 0);
+        if (u < kBM * k16 && (FULLM || m0 + lr < p.M)) xv[q] = *reinterpret_cast<const uint4*>(p.qx + (m0 + lr) * K + c);
+      }
+#pragma unroll
+      for (int q = 0; q < YP; ++q) {
+        const int u = tid + q * 64 * WAVES, lr = u / n8d, c = (u - lr * n8d) * 8;
+        yv[q] = make_uint4(0, 0, 0, 0);
+        if (u < kBM * n8 && (FULLM || m0 + lr < p.M)) yv[q] = *reinterpret_cast<const uint4*>(p.dy + (m0 + lr) * N + c);
+      }
+#pragma unroll
+      for (int q = 0; q < XP; ++q) {
+        const int u = tid + q * 64 * WAVES, lr = u / k16, c = (u - lr * k16) * 16;
+        if (u < kBM * k16) *reinterpret_cast<uint4*>(xs + lr * ldk + c) = xv[q];
+      }
+#pragma unroll
+      for (int q = 0; q < YP; ++q) {
+        const int u = tid + q * 64 * WAVES, lr = u / n8d, c = (u - lr * n8d) * 8;
+        if (u < kBM * n8) *reinterpret_cast<uint4*>(dys + lr * ldy + 2 * c) = yv[q];
+      }
+    } else {
+      for (int u = tid; u < kBM * (k16 + n8); u += 64 * WAVES) {
+        if (u < kBM * k16) {
+          const int lr = u / k16, c = (u - lr * k16) * 16;
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (FULLM || m0 + lr < p.M) v = *reinterpret_cast<const uint4*>(p.qx + (m0 + lr) * K + c);
+          *reinterpret_cast<uint4*>(xs + lr * ldk + c) = v;
+        } else {
+          const int v8 = u - kBM * k16, lr = v8 / n8d, c = (v8 - lr * n8d) * 8;
+          uint4 v = make_uint4(0, 0, 0, 0);
+          if (FULLM || m0 + lr < p.M) v = *reinterpret_cast<const uint4*>(p.dy + (m0 + lr) * N + c);
+          *reinterpret_cast<uint4*>(dys + lr * ldy + 2 * c) = v;
+        }
       }
     }
     __syncthreads();
