@@ -695,8 +695,17 @@ __device__ __forceinline__ void finalize_body(int64_t blk, const float* wpart, i
   const int64_t i = blk * 256 + threadIdx.x;
   const int64_t kn = (int64_t)K * N;
   if (i < kn) {
+    // eight slices' loads in flight per iteration, added in slice order
     float s = 0.0f;
-    for (int sp = 0; sp < nsplit; ++sp) s += wpart[(int64_t)sp * kn + i];
+    int sp = 0;
+    for (; sp + 8 <= nsplit; sp += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = wpart[(int64_t)(sp + q) * kn + i];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += v[q];
+    }
+    for (; sp < nsplit; ++sp) s += wpart[(int64_t)sp * kn + i];
     const int k = (int)(i / N), n = (int)(i - (int64_t)k * N);
     dw[i] = sxc != nullptr ? s * sxc[k] * sdzc[n] : s;
   }
@@ -714,12 +723,22 @@ __device__ __forceinline__ void col_vectors_body(int blk, const float* cpart, in
   float a = 0.0f, b = 0.0f, c = 0.0f;
   if (n < N) {
     int bl = part;
-    for (; bl + 16 < nblocks; bl += 32) {
-      const size_t o0 = (size_t)bl * N + n, o1 = (size_t)(bl + 16) * N + n;
-      const float a0 = cpart[o0], b0 = cpart[plane + o0], c0 = cpart[2 * plane + o0];
-      const float a1 = cpart[o1], b1 = cpart[plane + o1], c1 = cpart[2 * plane + o1];
-      a += a0; b += b0; c += c0;
-      a += a1; b += b1; c += c1;
+    // eight rows of partials per quantity in flight, added in row order
+    for (; bl + 112 < nblocks; bl += 128) {
+      float va[8], vb[8], vc[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const size_t o = (size_t)(bl + 16 * q) * N + n;
+        va[q] = cpart[o];
+        vb[q] = cpart[plane + o];
+        vc[q] = cpart[2 * plane + o];
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        a += va[q];
+        b += vb[q];
+        c += vc[q];
+      }
     }
     for (; bl < nblocks; bl += 16) {
       const size_t o = (size_t)bl * N + n;
@@ -745,14 +764,17 @@ __device__ __forceinline__ void col_vectors_body(int blk, const float* cpart, in
   }
 }
 
-// dW (blocks [0, nf)) and, when requested, dgamma / dbeta / dbias (the
-// blocks after them) in one launch: the two reductions are independent.
+// dW (the last nf blocks) and, when requested, dgamma / dbeta / dbias (the
+// blocks before them) in one launch: the two reductions are independent.
 __global__ __launch_bounds__(256) void k_finalize_vectors(const float* wpart, int nsplit, const float* sxc,
                                                           const float* sdzc, int K, int N, float* dw, int nf,
                                                           const float* cpart, int nblocks, float* dgamma,
                                                           float* dbeta, float* dbias) {
-  if ((int)blockIdx.x < nf) finalize_body(blockIdx.x, wpart, nsplit, sxc, sdzc, K, N, dw);
-  else col_vectors_body((int)blockIdx.x - nf, cpart, nblocks, N, dgamma, dbeta, dbias);
+  // the few column-vector blocks first: their longer reductions then overlap
+  // the dW blocks instead of trailing them
+  const int nv = (int)gridDim.x - nf;
+  if ((int)blockIdx.x < nv) col_vectors_body((int)blockIdx.x, cpart, nblocks, N, dgamma, dbeta, dbias);
+  else finalize_body((int)blockIdx.x - nv, wpart, nsplit, sxc, sdzc, K, N, dw);
 }
 
 // The square-block backward's three MFMA operands in one launch, all
