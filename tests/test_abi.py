@@ -226,3 +226,48 @@ def test_product_path_refuses_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(lk, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         lk.library()
+
+
+def test_probe_and_mere_validation(lib):
+    """The Probe and MERE entry points check their arguments before any
+    launch (no GPU work happens on these paths)."""
+    a = lk.ProbeInputArgs(B=16, K=0, n_old=0, T=FAKE, mu=FAKE, S=FAKE)
+    assert lib.loka_probe_input_update(ctypes.byref(a), None) == 2          # K out of range
+    a.K = 64
+    a.T = None
+    assert lib.loka_probe_input_update(ctypes.byref(a), None) == 1          # missing input
+    a.T = FAKE
+    assert lib.loka_probe_input_update(ctypes.byref(a), None) == 4          # no workspace
+    w = lk.ProbeWeightArgs(R=64, C=64, m=1.0, first=0, W=FAKE, M=FAKE, U=FAKE, V=FAKE, info=FAKE)
+    assert lib.loka_probe_weight_update(ctypes.byref(w), None) == 1         # momentum must be < 1
+    w.m = 0.9
+    w.C = 4096
+    assert lib.loka_probe_weight_update(ctypes.byref(w), None) == 2
+    w.C = 64
+    assert lib.loka_probe_weight_update(ctypes.byref(w), None) == 4
+    w.first = 1
+    assert lib.loka_probe_weight_workspace_size(ctypes.byref(w)) == 0       # initializing needs none
+    si = lk.ProbeSampleInputArgs(B=8, K=32, n=1, mu=FAKE, S=FAKE, seed=1, out=FAKE, info=FAKE)
+    assert lib.loka_probe_sample_input(ctypes.byref(si), None) == 1         # n >= 2 for a covariance
+    sw = lk.ProbeSampleWeightArgs(R=32, C=32, M=FAKE, U=FAKE, V=FAKE, seed=1, out=FAKE, info=None)
+    assert lib.loka_probe_sample_weight(ctypes.byref(sw), None) == 1
+    m = lk.MereArgs(M=64, N=64, K=4096, S=8, x=FAKE, w=FAKE, z=FAKE, rows=FAKE, out=FAKE)
+    assert lib.loka_mere_z(ctypes.byref(m), None) == 2                      # K > 2048
+    m.K = 64
+    m.S = 0
+    assert lib.loka_mere_z(ctypes.byref(m), None) == 1
+    m.S = 8
+    assert lib.loka_mere_z(ctypes.byref(m), None) == 4
+    assert lib.loka_mere_workspace_size(ctypes.byref(m)) == 8 * 3 * 8
+
+
+def test_fused_y_square_validation(lib):
+    a = _fwd(x_mode=1, N=256, K=256, M=128)
+    a.y_codes = FAKE
+    assert lib.loka_gemm_fp8_ln(ctypes.byref(a), None) == 1                 # y_scales missing
+    a.y_scales = FAKE
+    a.N = 384
+    assert lib.loka_gemm_fp8_ln(ctypes.byref(a), None) == 2                 # N must be 256 or 512
+    a.N = 256
+    a.M = 144
+    assert lib.loka_gemm_fp8_ln(ctypes.byref(a), None) == 2                 # M % 32
