@@ -477,15 +477,34 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
     // [N][M padded to 128] layout; rows past M hold zero codes, and the last
     // block also writes the zero rows up to the padding
     const int64_t rows_out = blockIdx.x == gridDim.x - 1 ? p.nchm * 128 - m0 : (int64_t)kBM;
-    const int pieces = (int)(rows_out >> 4) * N;
-    for (int u = tid; u < pieces; u += 64 * WAVES) {
-      const int q = u / N, n = u - q * N;
-      uint32_t w4[4] = {0u, 0u, 0u, 0u};
-      if (q < kMT) {
+    // a thread takes 16 rows x 4 columns: 16 word reads, each 4 x 4 byte
+    // block transposed with byte permutes (v_perm selects bytes 0-3 from its
+    // second operand, 4-7 from its first), then one piece per column
+    const int n4s = N >> 2;
+    const int groups = (int)(rows_out >> 4) * n4s;
+    for (int u = tid; u < groups; u += 64 * WAVES) {
+      const int q = u / n4s, n = (u - q * n4s) * 4;
+      uint32_t col[4][4];
 #pragma unroll
-        for (int b = 0; b < 16; ++b) w4[b >> 2] |= (uint32_t)ds[(16 * q + b) * ldn + n] << (8 * (b & 3));
+      for (int k = 0; k < 4; ++k) {
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        if (q < kMT) {
+#pragma unroll
+          for (int b = 0; b < 4; ++b) w[b] = *reinterpret_cast<const uint32_t*>(ds + (16 * q + 4 * k + b) * ldn + n);
+        }
+        const uint32_t ab_lo = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // a0 b0 a1 b1
+        const uint32_t ab_hi = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // a2 b2 a3 b3
+        const uint32_t cd_lo = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);  // c0 d0 c1 d1
+        const uint32_t cd_hi = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);  // c2 d2 c3 d3
+        col[0][k] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);           // a0 b0 c0 d0
+        col[1][k] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);           // a1 b1 c1 d1
+        col[2][k] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);
+        col[3][k] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
       }
-      *reinterpret_cast<uint4*>(p.dzt + ilv_offset(n, m0 + 16 * q, p.nchm)) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<uint4*>(p.dzt + ilv_offset(n + j, m0 + 16 * q, p.nchm)) =
+            make_uint4(col[j][0], col[j][1], col[j][2], col[j][3]);
     }
   }
 
