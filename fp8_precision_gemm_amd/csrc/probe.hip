@@ -211,79 +211,103 @@ __global__ __launch_bounds__(kPT) void k_chol_init(const float* A, int n, float 
   L[e] = j > i ? 0.0f : a * A[e] + (i == j ? eps[0] : 0.0f);
 }
 
-// factor the b x b diagonal block at (jb, jb) of L in place (b <= 64)
-__global__ __launch_bounds__(kPT) void k_potrf_block(float* L, int n, int jb, int b, int* info) {
-  __shared__ float Ab[kPanel][kPanel + 1];
-  const int tid = threadIdx.x;
-  for (int e = tid; e < b * b; e += kPT) {
-    const int i = e / b, j = e - i * b;
-    Ab[i][j] = j <= i ? L[(int64_t)(jb + i) * n + jb + j] : 0.0f;
-  }
-  __syncthreads();
-  // thread (tj, ti): column tj, rows ti, ti + 4, ... of the trailing update
-  const int tj = tid & (kPanel - 1), ti = tid >> 6;
-  for (int c = 0; c < b; ++c) {
-    if (tid == 0) {
-      float d = Ab[c][c];
+// factor the b x b diagonal block at (jb, jb) of L in place (b <= 64).  One
+// wavefront, lane i holding row i in registers.  Column c: the pivot comes
+// from lane c, the rows below scale by its reciprocal square root, the column
+// goes through LDS, and each row's later columns take their update (fused
+// multiply-adds in column order, as in the textbook right-looking
+// factorization).  Lanes past b and the entries
+// above the diagonal carry values that are never used or stored.
+__global__ __launch_bounds__(64) void k_potrf_block(float* L, int n, int jb, int b, int* info) {
+  __shared__ __align__(16) float col[kPanel];
+  const int i = threadIdx.x;
+  const float* src = L + (int64_t)(jb + min(i, b - 1)) * n + jb;
+  float a[kPanel];
+#pragma unroll
+  for (int j = 0; j < kPanel; ++j) a[j] = (j <= i && j < b) ? src[j] : 0.0f;
+#pragma unroll
+  for (int c = 0; c < kPanel; ++c) {
+    if (c < b) {
+      float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[c]), c));
       if (!(d > 0.0f)) {
-        if (*info == 0) *info = jb + c + 1;
+        if (i == 0 && *info == 0) *info = jb + c + 1;
         d = 1e-30f;
       }
-      Ab[c][c] = sqrtf(d);
+      // one reciprocal square root on the column's chain: the pivot is
+      // d / sqrt(d) and the rows below scale by 1 / sqrt(d)
+      const float rp = rsqrtf(d);
+      a[c] = i == c ? d * rp : a[c] * rp;
+      col[i] = a[c];
+      // the wavefront's LDS accesses complete in order: the reads below see
+      // every lane's write
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int k = c + 1; k < kPanel; ++k) a[k] = fmaf(-a[c], col[k], a[k]);
+      __builtin_amdgcn_wave_barrier();
     }
-    __syncthreads();
-    if (tid > c && tid < b) Ab[tid][c] /= Ab[c][c];
-    __syncthreads();
-    if (tj > c && tj < b) {
-      const float ljc = Ab[tj][c];
-      for (int i = max(ti, tj - ((tj - ti) & 3)); i < b; i += kPT / kPanel)
-        if (i >= tj) Ab[i][tj] = fmaf(-Ab[i][c], ljc, Ab[i][tj]);
-    }
-    __syncthreads();
   }
-  for (int e = tid; e < b * b; e += kPT) {
-    const int i = e / b, j = e - i * b;
-    L[(int64_t)(jb + i) * n + jb + j] = j <= i ? Ab[i][j] : 0.0f;
+  if (i < b) {
+    float* dst = L + (int64_t)(jb + i) * n + jb;
+#pragma unroll
+    for (int j = 0; j < kPanel; ++j)
+      if (j < b) dst[j] = j <= i ? a[j] : 0.0f;
   }
 }
 
 // Rows v of X [count][ldx], columns jb .. jb+b: x <- x L_jj^-T with L_jj the
-// b x b diagonal block of L at (jb, jb) (forward substitution per row; the
-// block and 256 rows are staged in LDS, one row per thread).
-__global__ __launch_bounds__(kPT) void k_trsm_panel(float* X, int64_t count, int64_t ldx, const float* L, int ldl,
-                                                    int jb, int b) {
-  __shared__ float Lj[kPanel][kPanel + 1];
-  __shared__ float xs[kPT][kPanel + 1];
+// b x b diagonal block of L at (jb, jb): forward substitution per row, one
+// row per thread in registers.  Right-looking: once x_c is final it updates
+// every later x_k with L_kc, so each x_k takes the same fused multiply-adds
+// in the same order as the row-by-row form (c ascending), but the chain of
+// dependent steps is b long instead of b^2 / 2.  x_c is scaled by the
+// diagonal entry's reciprocal (at most one rounding more than a division).  The block is kept in LDS by
+// columns (LT[c][k] = L_kc), read as broadcasts; X rows go straight between
+// HBM and registers.
+constexpr int kTrsmRows = 64;  // rows (threads) per workgroup
+constexpr int kLTS = kPanel + 4;  // LT row stride (floats): 16-byte aligned rows
+// FULL: b == 64, no per-column guards (the compiler then keeps more of the
+// block's reads in flight)
+template <bool FULL>
+__global__ __launch_bounds__(kTrsmRows, 1) void k_trsm_panel(float* X, int64_t count, int64_t ldx, const float* L,
+                                                          int ldl, int jb, int b) {
+  __shared__ __align__(16) float LT[kPanel][kLTS];
+  __shared__ __align__(16) float rdg[kPanel];
+  if (FULL) b = kPanel;
   const int tid = threadIdx.x;
-  const int64_t v0 = (int64_t)blockIdx.x * kPT;
-  for (int e = tid; e < b * b; e += kPT) {
-    const int i = e / b, j = e - i * b;
-    Lj[i][j] = j <= i ? L[(int64_t)(jb + i) * ldl + jb + j] : 0.0f;
+  const int64_t v = (int64_t)blockIdx.x * kTrsmRows + tid;
+  // thread k stages row k of the block as column k of LT; every load in flight
+  {
+    const float* lrow = L + (int64_t)(jb + min(tid, b - 1)) * ldl + jb;
+    float t[kPanel];
+#pragma unroll
+    for (int c = 0; c < kPanel; ++c) t[c] = (c <= tid && c < b && tid < b) ? lrow[c] : 0.0f;
+#pragma unroll
+    for (int c = 0; c < kPanel; ++c) LT[c][tid] = t[c];
   }
-  for (int e = tid; e < kPT * b; e += kPT) {
-    const int r = e / b, c = e - r * b;
-    xs[r][c] = v0 + r < count ? X[(v0 + r) * ldx + jb + c] : 0.0f;
-  }
-  __syncthreads();
-  // this thread's row in registers; the block's entries are LDS broadcasts
+  // the diagonal's reciprocals, off the substitution's dependency chain (a
+  // thread reads back only the entry it wrote itself); the whole-panel
+  // variant keeps them in place of the diagonal
+  if constexpr (FULL) LT[tid][tid] = 1.0f / LT[tid][tid];
+  else rdg[tid] = tid < b ? 1.0f / LT[tid][tid] : 0.0f;
+  // this thread's row straight into registers (rows past count read row 0
+  // and are never stored)
+  float* xrow = X + (v < count ? v : 0) * ldx + jb;
   float x[kPanel];
 #pragma unroll
-  for (int c = 0; c < kPanel; ++c) x[c] = xs[tid][c];
+  for (int c = 0; c < kPanel; ++c) x[c] = c < b ? xrow[c] : 0.0f;
+  __syncthreads();
 #pragma unroll
   for (int c = 0; c < kPanel; ++c) {
-    if (c < b) {
-      float t = x[c];
+    if (FULL || c < b) {
+      x[c] = x[c] * (FULL ? LT[c][c] : rdg[c]);
 #pragma unroll
-      for (int k = 0; k < c; ++k) t = fmaf(-x[k], Lj[c][k], t);
-      x[c] = t / Lj[c][c];
+      for (int k = c + 1; k < kPanel; ++k) x[k] = fmaf(-x[c], LT[c][k], x[k]);
     }
   }
+  if (v < count) {
 #pragma unroll
-  for (int c = 0; c < kPanel; ++c) xs[tid][c] = x[c];
-  __syncthreads();
-  for (int e = tid; e < kPT * b; e += kPT) {
-    const int r = e / b, c = e - r * b;
-    if (v0 + r < count) X[(v0 + r) * ldx + jb + c] = xs[r][c];
+    for (int c = 0; c < kPanel; ++c)
+      if (c < b) xrow[c] = x[c];
   }
 }
 
@@ -327,6 +351,15 @@ unsigned blocks(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
 constexpr int64_t kSplitDepth = 1024;  // contraction per GEMM slice
 int64_t gemm_splits(int64_t K) { return K <= kSplitDepth ? 1 : (K + kSplitDepth - 1) / kSplitDepth; }
 
+void trsm_panel(float* X, int64_t count, int64_t ldx, const float* L, int ldl, int jb, int b, hipStream_t s) {
+  if (b == kPanel)
+    hipLaunchKernelGGL(k_trsm_panel<true>, dim3(blocks(count, kTrsmRows)), dim3(kTrsmRows), 0, s, X, count, ldx, L, ldl,
+                       jb, b);
+  else
+    hipLaunchKernelGGL(k_trsm_panel<false>, dim3(blocks(count, kTrsmRows)), dim3(kTrsmRows), 0, s, X, count, ldx, L,
+                       ldl, jb, b);
+}
+
 hipError_t gemm(const GemmJob& j0, const ReduceJob& r0, hipStream_t s) {
   GemmJob j = j0;
   ReduceJob r = r0;
@@ -349,11 +382,10 @@ hipError_t cholesky(const float* A, int n, float a, float* L, int* info, float* 
   if (e != hipSuccess) return e;
   for (int jb = 0; jb < n; jb += kPanel) {
     const int b = min(kPanel, n - jb), r = n - jb - b;
-    hipLaunchKernelGGL(k_potrf_block, dim3(1), dim3(kPT), 0, s, L, n, jb, b, info);
+    hipLaunchKernelGGL(k_potrf_block, dim3(1), dim3(64), 0, s, L, n, jb, b, info);
     if (r > 0) {
       float* below = L + (int64_t)(jb + b) * n;
-      hipLaunchKernelGGL(k_trsm_panel, dim3(blocks(r, kPT)), dim3(kPT), 0, s, below, (int64_t)r, (int64_t)n, L, n,
-                         jb, b);
+      trsm_panel(below, (int64_t)r, (int64_t)n, L, n, jb, b, s);
       ReduceJob rj{};
       rj.alpha = -1.0f; rj.beta = 1.0f; rj.C = below + jb + b; rj.ldc = n; rj.lower = 1;
       if ((e = gemm(GemmJob{r, r, b, 0, below + jb, n, 1, below + jb, n, 1, P}, rj, s)) != hipSuccess) return e;
@@ -368,7 +400,7 @@ hipError_t trsm_rows(float* X, int64_t count, int n, const float* L, float* P, h
   hipError_t e;
   for (int jb = 0; jb < n; jb += kPanel) {
     const int b = min(kPanel, n - jb), r = n - jb - b;
-    hipLaunchKernelGGL(k_trsm_panel, dim3(blocks(count, kPT)), dim3(kPT), 0, s, X, count, (int64_t)n, L, n, jb, b);
+    trsm_panel(X, count, (int64_t)n, L, n, jb, b, s);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (r > 0) {
       // X[:, jb+b:] -= X[:, jb:jb+b] L[jb+b:, jb:jb+b]^T
