@@ -97,6 +97,44 @@ __global__ __launch_bounds__(kPT) void k_renorm(const float* s, int64_t RR, int6
   if (i < CC) V[i] = V[i] * sc;
 }
 
+// C = beta C + alpha sum_z P[z] (z in order) + coef d_i d_j + row[j] + mat[i][j];
+// the result as fp32 (C, row stride ldc; 0 = N) or bf16 (Cb); absent terms
+// are null; lower: only the entries j <= i.
+struct ReduceJob {
+  int64_t M, N;
+  int splits;
+  const float* P;
+  float alpha, beta, coef;
+  const float* d;
+  const float* row;
+  const float* mat;
+  float* C;
+  uint16_t* Cb;
+  int64_t ldc;
+  int lower;
+};
+// the output element (i, j) from the sum s of its slices
+__device__ __forceinline__ void reduce_out(const ReduceJob& r, int64_t i, int64_t j, float s) {
+  const int64_t e = i * r.N + j;
+  const int64_t ce = r.ldc > 0 ? i * r.ldc + j : e;
+  float c = r.alpha * s;
+  if (r.beta != 0.0f) c += r.beta * r.C[ce];
+  if (r.d != nullptr) c += r.coef * r.d[i] * r.d[j];
+  if (r.row != nullptr) c += r.row[j];
+  if (r.mat != nullptr) c += r.mat[e];
+  if (r.Cb != nullptr) r.Cb[e] = (uint16_t)f32_to_bf16_bits(c);
+  else r.C[ce] = c;
+}
+__global__ __launch_bounds__(kPT) void k_reduce(ReduceJob r) {
+  const int64_t e = (int64_t)blockIdx.x * kPT + threadIdx.x;
+  if (e >= r.M * r.N) return;
+  const int64_t i = e / r.N, j = e - i * r.N;
+  if (r.lower && j > i) return;
+  float s = 0.0f;
+  for (int z = 0; z < r.splits; ++z) s += r.P[(int64_t)z * r.M * r.N + e];
+  reduce_out(r, i, j, s);
+}
+
 // ---- GEMM: P[z] = A B^T over the z-th slice of the contraction ----------------
 // A(i, k) = A[i * a_rs + k * a_cs], B(j, k) = B[j * b_rs + k * b_cs]; a 64 x 64
 // output tile per workgroup, 4 x 4 per thread, 16-deep LDS stages.
@@ -108,7 +146,14 @@ struct GemmJob {
   int64_t b_rs, b_cs;
   float* P;  // [splits][M][N]
 };
-__global__ __launch_bounds__(kPT) void k_gemm_f32(GemmJob g) {
+// One slice (gridDim.z == 1): the reduction's output is written directly.
+// Staging: an operand contiguous along the contraction is read 16 elements
+// per row by consecutive threads, else 64 rows per depth step.
+__device__ __forceinline__ float gemm_ld(const float* X, int64_t rs, int64_t cs, int64_t rows, int64_t r, int64_t k,
+                                         int64_t k1) {
+  return (k < k1 && r < rows) ? X[r * rs + k * cs] : 0.0f;
+}
+__global__ __launch_bounds__(kPT) void k_gemm_f32(GemmJob g, ReduceJob red) {
   __shared__ float As[kGK][kGT + 4], Bs[kGK][kGT + 4];
   const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int64_t i0 = (int64_t)blockIdx.y * kGT, j0 = (int64_t)blockIdx.x * kGT;
@@ -119,11 +164,12 @@ __global__ __launch_bounds__(kPT) void k_gemm_f32(GemmJob g) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int e = threadIdx.x + q * kPT;
-      const int r = e & 63, kq = e >> 6;  // tile row r, depth kq
-      const int64_t k = kk + kq;
-      const int64_t ia = i0 + r, jb = j0 + r;
-      As[kq][r] = (k < k1 && ia < g.M) ? g.A[ia * g.a_rs + k * g.a_cs] : 0.0f;
-      Bs[kq][r] = (k < k1 && jb < g.N) ? g.B[jb * g.b_rs + k * g.b_cs] : 0.0f;
+      const int rr = e & 63, kr = e >> 6;  // rows fastest
+      const int rk = e >> 4, kk16 = e & 15;  // depth fastest
+      if (g.a_cs == 1) As[kk16][rk] = gemm_ld(g.A, g.a_rs, 1, g.M, i0 + rk, kk + kk16, k1);
+      else As[kr][rr] = gemm_ld(g.A, g.a_rs, g.a_cs, g.M, i0 + rr, kk + kr, k1);
+      if (g.b_cs == 1) Bs[kk16][rk] = gemm_ld(g.B, g.b_rs, 1, g.N, j0 + rk, kk + kk16, k1);
+      else Bs[kr][rr] = gemm_ld(g.B, g.b_rs, g.b_cs, g.N, j0 + rr, kk + kr, k1);
     }
     __syncthreads();
 #pragma unroll
@@ -141,6 +187,16 @@ __global__ __launch_bounds__(kPT) void k_gemm_f32(GemmJob g) {
     }
     __syncthreads();
   }
+  if (gridDim.z == 1) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t i = i0 + ty * 4 + u, j = j0 + tx * 4 + v;
+        if (i < g.M && j < g.N && (!red.lower || j <= i)) reduce_out(red, i, j, acc[u][v]);
+      }
+    return;
+  }
   float* P = g.P + (int64_t)blockIdx.z * g.M * g.N;
 #pragma unroll
   for (int u = 0; u < 4; ++u)
@@ -149,39 +205,6 @@ __global__ __launch_bounds__(kPT) void k_gemm_f32(GemmJob g) {
       const int64_t i = i0 + ty * 4 + u, j = j0 + tx * 4 + v;
       if (i < g.M && j < g.N) P[i * g.N + j] = acc[u][v];
     }
-}
-
-// C = beta C + alpha sum_z P[z] (z in order) + coef d_i d_j + row[j] + mat[i][j];
-// the result as fp32 (C, row stride ldc; 0 = N) or bf16 (Cb); absent terms
-// are null; lower: only the entries j <= i.
-struct ReduceJob {
-  int64_t M, N;
-  int splits;
-  const float* P;
-  float alpha, beta, coef;
-  const float* d;
-  const float* row;
-  const float* mat;
-  float* C;
-  uint16_t* Cb;
-  int64_t ldc;
-  int lower;
-};
-__global__ __launch_bounds__(kPT) void k_reduce(ReduceJob r) {
-  const int64_t e = (int64_t)blockIdx.x * kPT + threadIdx.x;
-  if (e >= r.M * r.N) return;
-  const int64_t i = e / r.N, j = e - i * r.N;
-  if (r.lower && j > i) return;
-  const int64_t ce = r.ldc > 0 ? i * r.ldc + j : e;
-  float s = 0.0f;
-  for (int z = 0; z < r.splits; ++z) s += r.P[(int64_t)z * r.M * r.N + e];
-  float c = r.alpha * s;
-  if (r.beta != 0.0f) c += r.beta * r.C[ce];
-  if (r.d != nullptr) c += r.coef * r.d[i] * r.d[j];
-  if (r.row != nullptr) c += r.row[j];
-  if (r.mat != nullptr) c += r.mat[e];
-  if (r.Cb != nullptr) r.Cb[e] = (uint16_t)f32_to_bf16_bits(c);
-  else r.C[ce] = c;
 }
 
 // ---- Cholesky, blocked right-looking: L L^T = a A + eps I ----------------------
@@ -366,10 +389,10 @@ hipError_t gemm(const GemmJob& j0, const ReduceJob& r0, hipStream_t s) {
   const int64_t sp = gemm_splits(j.K);
   j.kper = (j.K + sp - 1) / sp;
   j.kper = (j.kper + kGK - 1) / kGK * kGK;
-  hipLaunchKernelGGL(k_gemm_f32, dim3(blocks(j.N, kGT), blocks(j.M, kGT), (unsigned)sp), dim3(kPT), 0, s, j);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   r.M = j.M; r.N = j.N; r.splits = (int)sp; r.P = j.P;
+  hipLaunchKernelGGL(k_gemm_f32, dim3(blocks(j.N, kGT), blocks(j.M, kGT), (unsigned)sp), dim3(kPT), 0, s, j, r);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || sp == 1) return e;
   hipLaunchKernelGGL(k_reduce, dim3(blocks(j.M * j.N, kPT)), dim3(kPT), 0, s, r);
   return hipGetLastError();
 }
