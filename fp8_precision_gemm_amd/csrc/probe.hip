@@ -209,9 +209,10 @@ __global__ __launch_bounds__(kPT) void k_gemm_f32(GemmJob g, ReduceJob red) {
 
 // ---- Cholesky, blocked right-looking: L L^T = a A + eps I ----------------------
 // eps = 1e-6 trace(a A) / n.  L starts as the lower triangle of a A + eps I;
-// per 64-column panel: the diagonal block is factored in LDS, the rows below
-// solve against it (k_trsm_panel), and the trailing lower triangle takes the
-// panel's product away (GEMM + reduce).  A non-positive pivot sets *info to
+// per 64-column panel: one wavefront factors the diagonal block
+// (k_potrf_block), the rows below solve against it (k_trsm_panel), and the
+// trailing lower triangle takes the panel's product away (the GEMM, with the
+// reduction in its epilogue).  A non-positive pivot sets *info to
 // its 1-based column (the first one met); the factor is then not valid.
 constexpr int kPanel = 64;
 
