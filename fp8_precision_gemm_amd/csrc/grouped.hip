@@ -1,4 +1,7 @@
-// loka_grouped_gemm_fp8_ln: many independent rowwise forwards in one launch.
+// loka_grouped_gemm_fp8_ln: many independent rowwise forwards in one call: one
+// persistent launch when every group has N <= 384, K <= 512 and a guarded
+// shape (k_grouped_mixed), else one persistent launch per register shape
+// class of the groups.
 //
 // Source: LoKA section I (wide ensembles of small layers); GEM "Generalized
 // Dot-Product Attention" (tile lists precomputed instead of discovered by
@@ -167,6 +170,23 @@ __global__ __launch_bounds__(kPlanThreads) void k_grouped_plan(const GroupDev* g
   }
 }
 
+// the resident block's arguments for one group (rowwise X, no optional
+// statistics or context outputs)
+__device__ __forceinline__ FwdBlock group_block(const GroupDev& gd, const uint8_t* qw, float eps) {
+  FwdBlock p{};
+  p.M = gd.M; p.N = (int)gd.N; p.K = (int)gd.K;
+  p.x = static_cast<const uint16_t*>(gd.x);
+  p.qw = qw; p.sw = gd.sw;
+  p.ldy = (int)gd.N;
+  p.bias = static_cast<const uint16_t*>(gd.bias);
+  p.gamma = static_cast<const uint16_t*>(gd.gamma);
+  p.beta = static_cast<const uint16_t*>(gd.beta);
+  p.y = static_cast<uint16_t*>(gd.y);
+  p.z = gd.z;
+  p.eps = eps; p.x_r = 1.0f; p.x_s = 1.0f;
+  return p;
+}
+
 template <bool OPT, int NT, int KC, bool FULL>
 __global__ __launch_bounds__(kThreads) void k_grouped_res(const GroupDev* groups, const int* tile_pre,
                                                           const int* wg_start, int G, float eps, WeightSrc wsrc) {
@@ -183,19 +203,7 @@ __global__ __launch_bounds__(kThreads) void k_grouped_res(const GroupDev* groups
   while (t < tend) {
     while (tile_pre[g + 1] <= t) ++g;  // past finished groups and those of other classes
     const int seg_end = min(tend, tile_pre[g + 1]);
-    const GroupDev gd = groups[g];
-    FwdBlock p{};
-    p.M = gd.M; p.N = (int)gd.N; p.K = (int)gd.K;
-    p.x = static_cast<const uint16_t*>(gd.x);
-    p.qw = group_weight(wsrc, gd, g); p.sw = gd.sw;
-    p.ldy = (int)gd.N;
-    p.bias = static_cast<const uint16_t*>(gd.bias);
-    p.gamma = static_cast<const uint16_t*>(gd.gamma);
-    p.beta = static_cast<const uint16_t*>(gd.beta);
-    p.y = static_cast<uint16_t*>(gd.y);
-    p.z = gd.z;
-    p.mean = nullptr; p.rstd = nullptr; p.qx_out = nullptr; p.sx_out = nullptr;
-    p.eps = eps; p.x_r = 1.0f; p.x_s = 1.0f;
+    const FwdBlock p = group_block(groups[g], group_weight(wsrc, groups[g], g), eps);
     ResBlock<1, NT, KC, OPT, FULL> blk(p, t - tile_pre[g], seg_end - tile_pre[g], smem);
     blk.run();
     __syncthreads();  // the next group's set-up rewrites the LDS
@@ -220,24 +228,63 @@ __global__ __launch_bounds__(kThreads) void k_grouped_res_arg(const GroupDev* gr
   while (t < tend) {
     while (plan.tile_pre[q + 1] <= t) ++q;  // past finished and empty groups
     const int seg_end = min(tend, plan.tile_pre[q + 1]);
-    const GroupDev gd = groups[plan.gid[q]];
-    FwdBlock p{};
-    p.M = gd.M; p.N = (int)gd.N; p.K = (int)gd.K;
-    p.x = static_cast<const uint16_t*>(gd.x);
-    p.qw = group_weight(wsrc, gd, plan.gid[q]); p.sw = gd.sw;
-    p.ldy = (int)gd.N;
-    p.bias = static_cast<const uint16_t*>(gd.bias);
-    p.gamma = static_cast<const uint16_t*>(gd.gamma);
-    p.beta = static_cast<const uint16_t*>(gd.beta);
-    p.y = static_cast<uint16_t*>(gd.y);
-    p.z = gd.z;
-    p.mean = nullptr; p.rstd = nullptr; p.qx_out = nullptr; p.sx_out = nullptr;
-    p.eps = eps; p.x_r = 1.0f; p.x_s = 1.0f;
+    const FwdBlock p = group_block(groups[plan.gid[q]], group_weight(wsrc, groups[plan.gid[q]], plan.gid[q]), eps);
     ResBlock<1, NT, KC, OPT, FULL> blk(p, t - plan.tile_pre[q], seg_end - plan.tile_pre[q], smem);
     blk.run();
     __syncthreads();  // the next group's set-up rewrites the LDS
     t = seg_end;
   }
+}
+
+// Every group in one launch when all have N <= 384, K <= 512 and guarded
+// (not FULL) shapes: the same walk over one plan of all the groups, and each
+// group's segment runs the block variant of its column-tile count
+// (N <= 128 NT).  The variants share the 4-chunk weight footprint, so the
+// kernel's registers are those of the widest (with N = 512 they would
+// spill).
+template <int NT, bool OPT>
+__device__ __forceinline__ void run_group(const FwdBlock& p, int64_t tb, int64_t te, uint8_t* smem) {
+  ResBlock<1, NT, 4, OPT, false> blk(p, tb, te, smem);
+  blk.run();
+}
+template <bool OPT>
+__global__ __launch_bounds__(kThreads) void k_grouped_mixed(const GroupDev* groups, GroupPlan plan, float eps,
+                                                            WeightSrc wsrc) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  int t = plan.wg_start[blockIdx.x];
+  const int tend = plan.wg_start[blockIdx.x + 1];
+  int lo = 0, hi = plan.ngroups - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (plan.tile_pre[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  int q = lo;
+  while (t < tend) {
+    while (plan.tile_pre[q + 1] <= t) ++q;
+    const int seg_end = min(tend, plan.tile_pre[q + 1]);
+    const int gi = plan.gid[q];
+    const FwdBlock p = group_block(groups[gi], group_weight(wsrc, groups[gi], gi), eps);
+    const int64_t tb = t - plan.tile_pre[q], te = seg_end - plan.tile_pre[q];
+    switch (res_nt(p.N)) {
+      case 1: run_group<1, OPT>(p, tb, te, smem); break;
+      case 2: run_group<2, OPT>(p, tb, te, smem); break;
+      default: run_group<3, OPT>(p, tb, te, smem); break;
+    }
+    __syncthreads();  // the next group's set-up rewrites the LDS
+    t = seg_end;
+  }
+}
+
+template <bool OPT>
+hipError_t launch_mixed(const GroupDev* dg, const GroupPlan& plan, size_t lds, float eps, WeightSrc w,
+                        hipStream_t s) {
+  auto kern = k_grouped_mixed<OPT>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)plan.grid), dim3(kThreads), lds, s, dg, plan, eps, w);
+  return hipGetLastError();
 }
 
 template <bool OPT, int NT, int KC, bool FULL>
@@ -282,6 +329,46 @@ size_t plan_bytes(int num_groups) {
   b += ((size_t)fwd::kClasses * (num_groups + 1) * sizeof(int) + 255) / 256 * 256;
   b += ((size_t)fwd::kClasses * (fwd::kMaxGrid + 1) * sizeof(int) + 255) / 256 * 256;
   return b;
+}
+// the plan of the groups `take` selects, in descriptor order: each one's
+// first 16-row tile, and for each of min(tiles, cus) workgroups the first
+// tile whose starting cost reaches its equal share of the total
+template <class Take>
+void host_plan_of(const GroupDev* groups, int G, int cus, Take take, fwd::GroupPlan& plan) {
+  plan.ngroups = 0;
+  int64_t cost_pre[fwd::kPlanGroups + 1];
+  int64_t ccost[fwd::kPlanGroups];
+  int64_t tp = 0, cp = 0;
+  for (int gi = 0; gi < G; ++gi) {
+    const GroupDev& gd = groups[gi];
+    if (!take(gd)) continue;
+    const int q = plan.ngroups++;
+    plan.gid[q] = gi;
+    plan.tile_pre[q] = (int)tp;
+    cost_pre[q] = cp;
+    ccost[q] = fwd::tile_cost(gd.K, gd.N);
+    const int64_t tl = (gd.M + fwd::kResRows - 1) / fwd::kResRows;
+    tp += tl;
+    cp += tl * ccost[q];
+  }
+  const int ng = plan.ngroups;
+  plan.tile_pre[ng] = (int)tp;
+  cost_pre[ng] = cp;
+  const int grid = (int)(tp < cus ? tp : cus);
+  plan.grid = grid;
+  for (int b = 0; b <= grid; ++b) {
+    if (b == grid) {
+      plan.wg_start[b] = (int)tp;
+      continue;
+    }
+    const int64_t x = (cp / grid) * b + ((cp % grid) * b) / grid;
+    int q = 0;
+    while (q + 1 < ng && cost_pre[q + 1] <= x) ++q;
+    const int64_t tq = plan.tile_pre[q + 1] - plan.tile_pre[q];
+    int64_t j = tq == 0 ? 0 : (x - cost_pre[q] + ccost[q] - 1) / ccost[q];
+    if (j > tq) j = tq;
+    plan.wg_start[b] = plan.tile_pre[q] + (int)j;
+  }
 }
 }  // namespace
 
@@ -348,44 +435,31 @@ hipError_t launch_grouped(const GroupedLaunch& a, hipStream_t s) {
   bool host_plan = cus <= fwd::kPlanGroups;
   for (int c = 0; c < fwd::kClasses; ++c) host_plan = host_plan && ngc[c] <= fwd::kPlanGroups;
   if (host_plan) {
+    // one launch for every group when all groups with rows have N <= 384,
+    // K <= 512 and guarded shapes
+    bool mixed = true;
+    int nrows = 0;
+    size_t lmax = 0;
+    for (int gi = 0; gi < G; ++gi) {
+      const GroupDev& gd = a.groups[gi];
+      if (gd.M == 0) continue;
+      ++nrows;
+      const int nt = fwd::res_nt((int)gd.N);
+      if (nt > 3 || fwd::group_kc(nt, (int)gd.K) != 4 || (fwd::group_class(gd.M, gd.N, gd.K) & 1)) mixed = false;
+      const size_t l = (size_t)fwd::res_lds(nt, 4, (int)gd.N).total;
+      if (l > lmax) lmax = l;
+    }
+    if (mixed && nrows <= fwd::kPlanGroups) {
+      fwd::GroupPlan plan;
+      host_plan_of(a.groups, G, cus, [](const GroupDev& gd) { return gd.M > 0; }, plan);
+      return opt ? fwd::launch_mixed<true>(dgroups, plan, lmax, a.eps, wsrc, s)
+                 : fwd::launch_mixed<false>(dgroups, plan, lmax, a.eps, wsrc, s);
+    }
     for (int c = 0; c < fwd::kClasses && e == hipSuccess; ++c) {
       if (tiles[c] == 0) continue;
       fwd::GroupPlan plan;
-      plan.ngroups = 0;
-      int64_t cost_pre[fwd::kPlanGroups + 1];
-      int64_t ccost[fwd::kPlanGroups];
-      int64_t tp = 0, cp = 0;
-      for (int gi = 0; gi < G; ++gi) {
-        const GroupDev& gd = a.groups[gi];
-        if (fwd::group_class(gd.M, gd.N, gd.K) != c) continue;
-        const int q = plan.ngroups++;
-        plan.gid[q] = gi;
-        plan.tile_pre[q] = (int)tp;
-        cost_pre[q] = cp;
-        ccost[q] = fwd::tile_cost(gd.K, gd.N);
-        const int64_t tl = (gd.M + fwd::kResRows - 1) / fwd::kResRows;
-        tp += tl;
-        cp += tl * ccost[q];
-      }
-      const int ng = plan.ngroups;
-      plan.tile_pre[ng] = (int)tp;
-      cost_pre[ng] = cp;
-      const int grid = (int)(tp < cus ? tp : cus);
-      plan.grid = grid;
-      // workgroup b starts at the first tile whose starting cost is >= b*C/grid
-      for (int b = 0; b <= grid; ++b) {
-        if (b == grid) {
-          plan.wg_start[b] = (int)tp;
-          continue;
-        }
-        const int64_t x = (cp / grid) * b + ((cp % grid) * b) / grid;
-        int q = 0;
-        while (q + 1 < ng && cost_pre[q + 1] <= x) ++q;
-        const int64_t tq = plan.tile_pre[q + 1] - plan.tile_pre[q];
-        int64_t j = tq == 0 ? 0 : (x - cost_pre[q] + ccost[q] - 1) / ccost[q];
-        if (j > tq) j = tq;
-        plan.wg_start[b] = plan.tile_pre[q] + (int)j;
-      }
+      host_plan_of(a.groups, G, cus,
+                   [c](const GroupDev& gd) { return fwd::group_class(gd.M, gd.N, gd.K) == c; }, plan);
 #define LOKA_CLASS(S, NT, KC)                                                                     \
   case 2 * S:                                                                                    \
     e = opt ? fwd::launch_class_arg<true, NT, KC, false>(dgroups, plan, lds[c], a.eps, wsrc, s)        \

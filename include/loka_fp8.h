@@ -325,7 +325,9 @@ loka_status loka_gemm_fp8_bwd(const loka_bwd_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
  * loka_grouped_gemm_fp8_ln: many independent loka_gemm_fp8_ln problems
- * (x_mode ROW) in one launch.
+ * (x_mode ROW) in one call: one persistent launch when every group has
+ * N <= 384 and K <= 512 and a guarded shape, else one per register shape
+ * class of the groups (column tiles per wavefront, ceil(N/128), and K depth).
  *
  * Source: LoKA section I (wide ensembles of small layers); GEM
  * "Generalized Dot-Product Attention" (tile lists precomputed on the CPU,
