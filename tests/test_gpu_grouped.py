@@ -8,7 +8,7 @@ import pytest
 import torch
 
 from oracle import forward
-from synth.workloads import forward_case, grouped_case
+from synth.workloads import forward_case, grouped_case, to_bf16_bits
 from tests.gpu_helpers import bf16_dev, check_y, check_z, host, row_sigma, sample_rows
 
 pytestmark = pytest.mark.gpu
@@ -103,3 +103,49 @@ def test_grouped_many_groups_device_plan(lib):
             ref = forward.gemm_ln_forward(g["x"], g["w"], g["bias"], g["gamma"], g["beta"])
             check_z(host(o["z"]), ref["z"], row_sigma(ref["z"]), f"group {i}")
             check_y(host(o["y"]), ref["y"], f"group {i}")
+
+
+def _bitwise_like_single(lib, dg, outs, idx):
+    for i in idx:
+        d = dg[i]
+        s = lib.loka_gemm_fp8_ln(d["x"], d["qw"], d["sw"], d["bias"], d["gamma"], d["beta"])
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(host(s["y"]), host(outs[i]["y"]), err_msg=f"group {i}")
+
+
+def test_grouped_y_only(lib):
+    """Without Z (the launch the benchmark times): Y against the oracle and bit
+    for bit against single calls without Z."""
+    groups = grouped_case(seed=9, groups=12, M=1000)
+    dg = prepare(lib, groups)
+    outs = lib.loka_grouped_gemm_fp8_ln(dg)
+    torch.cuda.synchronize()
+    assert all("z" not in o for o in outs)
+    for i, (g, o) in enumerate(zip(groups, outs)):
+        rows = sample_rows(g["M"], 64, seed=i)
+        ref = forward.gemm_ln_forward(g["x"][rows], g["w"], g["bias"], g["gamma"], g["beta"])
+        check_y(host(o["y"])[rows], ref["y"], f"group {i} (K={g['K']}, N={g['N']})")
+    _bitwise_like_single(lib, dg, outs, range(len(groups)))
+
+
+@pytest.mark.parametrize("want_z", [False, True])
+def test_grouped_with_wide_and_deep_groups(lib, want_z):
+    """Groups with N = 512 or K > 512 in the mix (one launch per register
+    shape class instead of the single launch): the same results."""
+    groups = grouped_case(seed=13, groups=8, M=300)
+    for i, (K, N) in zip((1, 4, 6), ((256, 512), (640, 128), (512, 512))):
+        rng = np.random.default_rng(100 + i)
+        groups[i] = dict(groups[i], K=K, N=N,
+                         x=to_bf16_bits(rng.standard_normal((300, K))),
+                         w=to_bf16_bits(rng.standard_normal((K, N)) / np.sqrt(K)),
+                         bias=to_bf16_bits(0.1 * rng.standard_normal(N)),
+                         gamma=to_bf16_bits(np.ones(N)), beta=to_bf16_bits(np.zeros(N)))
+    dg = prepare(lib, groups)
+    outs = lib.loka_grouped_gemm_fp8_ln(dg, want_z=want_z)
+    torch.cuda.synchronize()
+    for i, (g, o) in enumerate(zip(groups, outs)):
+        ref = forward.gemm_ln_forward(g["x"], g["w"], g["bias"], g["gamma"], g["beta"])
+        if want_z:
+            check_z(host(o["z"]), ref["z"], row_sigma(ref["z"]), f"group {i}")
+        check_y(host(o["y"]), ref["y"], f"group {i} (K={g['K']}, N={g['N']})")
+    _bitwise_like_single(lib, dg, outs, range(len(groups)))
