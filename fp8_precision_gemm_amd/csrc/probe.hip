@@ -32,6 +32,8 @@ __global__ __launch_bounds__(kPT) void k_colsum(const uint16_t* T, int64_t B, in
   if (k >= K) return;
   const int64_t b0 = (int64_t)blockIdx.y * rows_per, b1 = min(b0 + rows_per, B);
   float s = 0.0f;
+  // rows in order; the unrolled loop keeps 16 loads in flight per thread
+#pragma unroll 16
   for (int64_t b = b0; b < b1; ++b) s += bf16_lo(T[b * K + k]);
   part[(int64_t)blockIdx.y * K + k] = s;
 }
@@ -43,6 +45,7 @@ __global__ __launch_bounds__(kPT) void k_mean_merge(const float* part, int nch, 
   const int k = blockIdx.x * kPT + threadIdx.x;
   if (k >= K) return;
   float s = 0.0f;
+#pragma unroll 16
   for (int c = 0; c < nch; ++c) s += part[(int64_t)c * K + k];
   const float mb = s / (float)B;
   const float dd = mb - mu[k];
@@ -237,13 +240,12 @@ __global__ __launch_bounds__(kPT) void k_chol_init(const float* A, int n, float 
 
 // factor the b x b diagonal block at (jb, jb) of L in place (b <= 64).  One
 // wavefront, lane i holding row i in registers.  Column c: the pivot comes
-// from lane c, the rows below scale by its reciprocal square root, the column
-// goes through LDS, and each row's later columns take their update (fused
-// multiply-adds in column order, as in the textbook right-looking
-// factorization).  Lanes past b and the entries
+// from lane c, the rows below scale by its reciprocal square root, the
+// column's entries reach every lane by readlane, and each row's later columns
+// take their update (fused multiply-adds in column order, as in the textbook
+// right-looking factorization).  Lanes past b and the entries
 // above the diagonal carry values that are never used or stored.
 __global__ __launch_bounds__(64) void k_potrf_block(float* L, int n, int jb, int b, int* info) {
-  __shared__ __align__(16) float col[kPanel];
   const int i = threadIdx.x;
   const float* src = L + (int64_t)(jb + min(i, b - 1)) * n + jb;
   float a[kPanel];
@@ -261,13 +263,10 @@ __global__ __launch_bounds__(64) void k_potrf_block(float* L, int n, int jb, int
       // d / sqrt(d) and the rows below scale by 1 / sqrt(d)
       const float rp = rsqrtf(d);
       a[c] = i == c ? d * rp : a[c] * rp;
-      col[i] = a[c];
-      // the wavefront's LDS accesses complete in order: the reads below see
-      // every lane's write
-      __builtin_amdgcn_wave_barrier();
+      // L_kc from lane k as a scalar operand of every lane's update
 #pragma unroll
-      for (int k = c + 1; k < kPanel; ++k) a[k] = fmaf(-a[c], col[k], a[k]);
-      __builtin_amdgcn_wave_barrier();
+      for (int k = c + 1; k < kPanel; ++k)
+        a[k] = fmaf(-a[c], __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[c]), k)), a[k]);
     }
   }
   if (i < b) {
