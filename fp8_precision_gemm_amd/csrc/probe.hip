@@ -16,7 +16,7 @@ namespace {
 
 constexpr int kPT = 256;     // threads of the element-wise and GEMM kernels
 constexpr int kGT = 64;      // GEMM tile (output rows and columns)
-constexpr int kGK = 16;      // GEMM depth per LDS stage
+constexpr int kGK = 64;      // GEMM depth per LDS stage
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -140,7 +140,8 @@ __global__ __launch_bounds__(kPT) void k_reduce(ReduceJob r) {
 
 // ---- GEMM: P[z] = A B^T over the z-th slice of the contraction ----------------
 // A(i, k) = A[i * a_rs + k * a_cs], B(j, k) = B[j * b_rs + k * b_cs]; a 64 x 64
-// output tile per workgroup, 4 x 4 per thread, 16-deep LDS stages.
+// output tile per workgroup, 64-deep LDS stages, fp32 MFMA (fp32 products
+// and sums).
 struct GemmJob {
   int64_t M, N, K, kper;
   const float* A;
@@ -150,64 +151,81 @@ struct GemmJob {
   float* P;  // [splits][M][N]
 };
 // One slice (gridDim.z == 1): the reduction's output is written directly.
-// Staging: an operand contiguous along the contraction is read 16 elements
+// Staging: an operand contiguous along the contraction is read 64 elements
 // per row by consecutive threads, else 64 rows per depth step.
-__device__ __forceinline__ float gemm_ld(const float* X, int64_t rs, int64_t cs, int64_t rows, int64_t r, int64_t k,
-                                         int64_t k1) {
-  return (k < k1 && r < rows) ? X[r * rs + k * cs] : 0.0f;
-}
 __global__ __launch_bounds__(kPT) void k_gemm_f32(GemmJob g, ReduceJob red) {
   __shared__ float As[kGK][kGT + 4], Bs[kGK][kGT + 4];
-  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wavefront (wm, wn) owns the 32 x 32 quarter (rows 32 wm.., columns 32 wn..)
+  // as 2 x 2 tiles of v_mfma_f32_16x16x4_f32: lane l supplies A(i = l % 16,
+  // k = l / 16) and B(k = l / 16, j = l % 16) and holds D(4 (l / 16) + r, l % 16)
+  const int wm = wave >> 1, wn = wave & 1, lr = lane & 15, lg = lane >> 4;
   const int64_t i0 = (int64_t)blockIdx.y * kGT, j0 = (int64_t)blockIdx.x * kGT;
   const int64_t k0 = (int64_t)blockIdx.z * g.kper, k1 = min(k0 + g.kper, g.K);
-  float acc[4][4] = {};
+  v4f acc[2][2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int v = 0; v < 2; ++v) acc[u][v] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
   for (int64_t kk = k0; kk < k1; kk += kGK) {
-    // stage: 16 x 64 of each operand, 4 elements per thread
+    // stage: 64 x 64 of each operand, 16 elements per thread, every load
+    // issued before the LDS writes.  Thread (hi0, lo) takes elements
+    // (hi0 + 4q, lo) of the tile, lo along the operand's contiguous axis.
+    static_assert(kGK == kGT && kGT == 64, "square 64 x 64 stages");
+    const int lo = threadIdx.x & 63, hi0 = threadIdx.x >> 6;
+    const bool ac = g.a_cs == 1, bc = g.b_cs == 1;
+    const float* pa = g.A + (ac ? (i0 + hi0) * g.a_rs + (kk + lo) : (i0 + lo) * g.a_rs + (kk + hi0) * g.a_cs);
+    const float* pb = g.B + (bc ? (j0 + hi0) * g.b_rs + (kk + lo) : (j0 + lo) * g.b_rs + (kk + hi0) * g.b_cs);
+    const int64_t sa = 4 * (ac ? g.a_rs : g.a_cs), sb = 4 * (bc ? g.b_rs : g.b_cs);
+    // bounds: (row, depth) of element q is (i0 + hi0 + 4q, kk + lo) or (i0 + lo, kk + hi0 + 4q)
+    const int64_t ra = ac ? g.M - i0 - hi0 : k1 - kk - hi0, rb = bc ? g.N - j0 - hi0 : k1 - kk - hi0;
+    const bool fa = ac ? kk + lo < k1 : i0 + lo < g.M, fb = bc ? kk + lo < k1 : j0 + lo < g.N;
+    float ta[16], tb[16];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = threadIdx.x + q * kPT;
-      const int rr = e & 63, kr = e >> 6;  // rows fastest
-      const int rk = e >> 4, kk16 = e & 15;  // depth fastest
-      if (g.a_cs == 1) As[kk16][rk] = gemm_ld(g.A, g.a_rs, 1, g.M, i0 + rk, kk + kk16, k1);
-      else As[kr][rr] = gemm_ld(g.A, g.a_rs, g.a_cs, g.M, i0 + rr, kk + kr, k1);
-      if (g.b_cs == 1) Bs[kk16][rk] = gemm_ld(g.B, g.b_rs, 1, g.N, j0 + rk, kk + kk16, k1);
-      else Bs[kr][rr] = gemm_ld(g.B, g.b_rs, g.b_cs, g.N, j0 + rr, kk + kr, k1);
+    for (int q = 0; q < 16; ++q) {
+      ta[q] = (fa && 4 * q < ra) ? pa[q * sa] : 0.0f;
+      tb[q] = (fb && 4 * q < rb) ? pb[q * sb] : 0.0f;
+    }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int hi = hi0 + 4 * q;
+      if (ac) As[lo][hi] = ta[q];
+      else As[hi][lo] = ta[q];
+      if (bc) Bs[lo][hi] = tb[q];
+      else Bs[hi][lo] = tb[q];
     }
     __syncthreads();
+#pragma unroll 2
+    for (int ks = 0; ks < kGK / 4; ++ks) {
+      const int kq = 4 * ks + lg;
+      float a[2], b[2];
 #pragma unroll
-    for (int kq = 0; kq < kGK; ++kq) {
-      float a[4], b[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        a[u] = As[kq][ty * 4 + u];
-        b[u] = Bs[kq][tx * 4 + u];
+      for (int u = 0; u < 2; ++u) {
+        a[u] = As[kq][32 * wm + 16 * u + lr];
+        b[u] = Bs[kq][32 * wn + 16 * u + lr];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 2; ++u)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[u][v] = fmaf(a[u], b[v], acc[u][v]);
+        for (int v = 0; v < 2; ++v) acc[u][v] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], b[v], acc[u][v], 0, 0, 0);
     }
     __syncthreads();
-  }
-  if (gridDim.z == 1) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t i = i0 + ty * 4 + u, j = j0 + tx * 4 + v;
-        if (i < g.M && j < g.N && (!red.lower || j <= i)) reduce_out(red, i, j, acc[u][v]);
-      }
-    return;
   }
   float* P = g.P + (int64_t)blockIdx.z * g.M * g.N;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int64_t i = i0 + ty * 4 + u, j = j0 + tx * 4 + v;
-      if (i < g.M && j < g.N) P[i * g.N + j] = acc[u][v];
-    }
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t i = i0 + 32 * wm + 16 * u + 4 * lg + r, j = j0 + 32 * wn + 16 * v + lr;
+        if (i >= g.M || j >= g.N) continue;
+        if (gridDim.z == 1) {
+          if (!red.lower || j <= i) reduce_out(red, i, j, acc[u][v][r]);
+        } else {
+          P[i * g.N + j] = acc[u][v][r];
+        }
+      }
 }
 
 // ---- Cholesky, blocked right-looking: L L^T = a A + eps I ----------------------
