@@ -552,6 +552,33 @@ __device__ __forceinline__ ScalePair reduce_tensor_scale(const float* partials, 
   return scales_from_amax<FMT>(m);
 }
 
+// The tensor scale straight from a small X (bf16 [M][K] contiguous, 16-byte
+// aligned, M K a multiple of 8): each thread's max-abs over 16-byte pieces,
+// then the workgroup's.  The max of exact values does not depend on the
+// order, so the scale equals the one from the partials pass bit for bit.
+__device__ __forceinline__ ScalePair tensor_scale_self(const FwdBlock& p, float* red8) {
+  const int64_t n8 = p.M * (int64_t)p.K / 8;
+  const uint4* x = reinterpret_cast<const uint4*>(p.x);
+  float m = 0.0f;
+#pragma unroll 4
+  for (int64_t u = threadIdx.x; u < n8; u += kThreads) {
+    const uint4 v = x[u];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m = fmaxf(m, fabsf(__uint_as_float(w[i] << 16)));
+      m = fmaxf(m, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+    }
+  }
+  m = wave_max_dpp(m);
+  if ((threadIdx.x & 63) == 0) red8[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = red8[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) m = fmaxf(m, red8[w]);
+  return scales_from_amax<0>(m);
+}
+
 // Workgroup shape per column count: 64-row tiles up to N = 512 (4 column
 // tiles per wavefront), 32-row tiles above (up to 8 per wavefront).
 template <int NTW>

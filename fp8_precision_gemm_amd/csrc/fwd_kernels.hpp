@@ -18,7 +18,7 @@ __global__ __launch_bounds__(kThreads) void k_fwd(FwdBlock p, const float* parti
   extern __shared__ __align__(16) uint8_t smem[];
   if (MODE == 0) {
     __shared__ float red8[kWaves];
-    ScalePair sp = reduce_tensor_scale<0>(partials, np, red8);
+    ScalePair sp = np < 0 ? tensor_scale_self(p, red8) : reduce_tensor_scale<0>(partials, np, red8);
     p.x_r = sp.r;
     p.x_s = sp.s;
   }
@@ -43,8 +43,9 @@ template <int MODE, int NT, int KC, bool OPT, bool FULL>
 __global__ __launch_bounds__(kThreads) void k_fwd_res(FwdBlock p, const float* partials, int np) {
   extern __shared__ __align__(16) uint8_t smem[];
   if (MODE == 0) {
+    // np < 0: X is small and every workgroup takes its max itself
     __shared__ float red8[kWaves];
-    ScalePair sp = reduce_tensor_scale<0>(partials, np, red8);
+    ScalePair sp = np < 0 ? tensor_scale_self(p, red8) : reduce_tensor_scale<0>(partials, np, red8);
     p.x_r = sp.r;
     p.x_s = sp.s;
   }

@@ -118,6 +118,11 @@ hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s) {
   }
   if (a.blocknorm) return fwd::launch_row_blocknorm(p, s);
   if (a.x_mode == 0) {
+    // small X on the resident kernel: no partials pass, each workgroup reads
+    // all of X (elements x workgroups <= 2^22, 8 MiB of cached reads)
+    const int64_t tiles = (a.M + 15) / 16;
+    if (fwd::res_fits((int)a.K, (int)a.N) && a.M * a.K * (tiles < 256 ? tiles : 256) <= ((int64_t)1 << 22))
+      return fwd::launch_tensor(p, nullptr, -1, s);
     float* partials = static_cast<float*>(a.workspace);
     const int np = (int)quant_plan(a.M, a.K, 0).np;
     hipError_t e = launch_amax_tensor_partials(a.x, a.M, a.K, a.K, partials, s);
