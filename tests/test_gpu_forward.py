@@ -112,6 +112,17 @@ def test_ragged_shapes(lib, x_mode, M, K, N):
     compare(g, o, None, x_mode, f"{x_mode} {M}x{K}x{N}")
 
 
+@pytest.mark.parametrize("M", [256, 272])
+def test_tensor_scale_either_side_of_the_small_x_path(lib, M):
+    """Tensorwise X at 1024 columns: 256 rows (16 workgroups x 2^18 elements =
+    2^22) take the max inside the forward kernel, 272 rows use the partials
+    pass.  Both give the oracle's scale and codes bit for bit."""
+    c = forward_case(M, 1024, 256, seed=M, x_dist="student_t3_outliers", gamma_var=0.1, beta_var=0.1)
+    g = run_gpu(lib, c, "tensor", packed=True)
+    o = oracle_rows(c, "tensor", None)
+    compare(g, o, None, "tensor", f"tensor {M}x1024x256")
+
+
 @pytest.mark.parametrize("x_mode", ["tensor", "row", "mx32_row"])
 @pytest.mark.parametrize("M,K,N", [(1000, 192, 192), (130, 160, 384), (300, 256, 320), (77, 512, 512),
                                    (33, 1024, 128), (40, 640, 384), (16, 16, 64)])
