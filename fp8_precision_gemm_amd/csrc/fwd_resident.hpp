@@ -214,6 +214,10 @@ struct ResBlock {
   static constexpr bool MX = MODE >= 3;  // E8M0 block scales inside the MFMA
   static constexpr int KQ = R::KQ, D = R::D, LDX = R::LDX, XE = R::XE, KP = R::KP;
   static constexpr bool PIPE = R::PIPE;
+  // sequential steps, guard-free shape, LayerNorm, no optional outputs: Y
+  // leaves as whole rows after the next barrier (two staging buffers by tile
+  // parity), so no 128-byte line is written in parts by two wavefronts
+  static constexpr bool COOP = FULL && !OPT && !PIPE && EPI == 0;
 
   const FwdBlock& p;
   int64_t tb, te;  // tile range [tb, te)
@@ -687,6 +691,7 @@ struct ResBlock {
     const int cl = c0 + 4 * g;  // this lane's first column (tile t adds 16t)
     const float* gb = cvec + 2 * N + cl;
     constexpr int YST = res_yst(NT);
+    uint8_t* ys = COOP && (t & 1) ? ystg + kWaves * kResRows * YST : ystg;
 #pragma unroll
     for (int t2 = 0; t2 < NT; ++t2) {
       if (tv(t2)) {
@@ -696,14 +701,14 @@ struct ResBlock {
         float o[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[j] = fmaf(fmaf(acc[t2][j], rstd, nmr), gv[j], bv[j]);
-        *reinterpret_cast<uint2*>(ystg + r * YST + (16 * t2 + 4 * g) * 2) =
+        *reinterpret_cast<uint2*>(ys + r * YST + (16 * t2 + 4 * g) * 2) =
             make_uint2(pack_bf16_hw(o[0], o[1]), pack_bf16_hw(o[2], o[3]));
         if (OPT && p.z != nullptr && row_ok)
           *reinterpret_cast<float4*>(p.z + m * ldy + cl + 16 * t2) =
               make_float4(acc[t2][0], acc[t2][1], acc[t2][2], acc[t2][3]);
       }
     }
-    store_y(t);
+    if constexpr (!COOP) store_y(t);
     if constexpr (OPT && NT % 2 == 0) {
       if (p.y_codes != nullptr) square_y(t);
     }
@@ -853,6 +858,26 @@ struct ResBlock {
     __syncthreads();
   }
 
+  // COOP: the workgroup's 16 x N block of Y of tile t as whole rows, each
+  // 16-byte piece read from the staging buffer (t & 1) of the wavefront that
+  // produced it; called after a barrier that follows every wavefront's
+  // staging writes of tile t
+  __device__ __forceinline__ void coop_store(int64_t t) {
+    constexpr int YST = res_yst(NT), PPR = 16 * NT, TOT = kResRows * PPR;  // pieces per row of N = 128 NT
+    const uint8_t* yb = ystg - wave * (kResRows * YST) + ((t & 1) ? kWaves * kResRows * YST : 0);
+#pragma unroll
+    for (int i = 0; i < (TOT + kThreads - 1) / kThreads; ++i) {
+      const int u = tid + kThreads * i;
+      if (TOT % kThreads == 0 || u < TOT) {
+        const int row = u / PPR, pc = u - row * PPR;
+        const int w = pc / (2 * NT), ch = pc - w * (2 * NT);
+        const uint4 v = *reinterpret_cast<const uint4*>(yb + (w * kResRows + row) * YST + ch * 16);
+        __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w},
+                                    reinterpret_cast<v4u*>(p.y + (t * kResRows + row) * ldy + pc * 8));
+      }
+    }
+  }
+
   // one tile without the pipeline (deep K): GEMM of tile j, quantization of
   // tile j+1 from the single slot, request of tile j+2, statistics, barrier,
   // normalization and stores
@@ -864,6 +889,7 @@ struct ResBlock {
     load_x<0>(t + 2);
     epilogue_stats(buf, acc0, cs0);
     __syncthreads();
+    if (COOP && j > 0) coop_store(t - 1);
     epilogue_out(buf, t, acc0, cs0);
   }
 
@@ -889,6 +915,10 @@ struct ResBlock {
     read_bounds();
     if (!PIPE) {
       for (int64_t j = 0; j < te - tb; ++j) step_seq(j);
+      if (COOP) {
+        __syncthreads();
+        coop_store(te - 1);
+      }
       return;
     }
     // tile 0: GEMM alongside the quantization of tile 1
