@@ -15,7 +15,8 @@ Test infrastructure only (see the package docstring).
     momentum m.  Per update, with Wc = W - M:
         L_V L_V^T = V + eps_V I,  Wt = Wc L_V^-T,  U1 = Wt Wt^T / C,
         L_U L_U^T = U + eps_U I,  Wu = L_U^-1 Wc,  V1 = Wu^T Wu / R,
-        U <- m U + (1 - m) U1,  V <- m V + (1 - m) V1,
+        U'' = m U + (1 - m) U1,  V'' = m V + (1 - m) V1,
+        U <- (U'' + U''^T) / 2 + eps_U I,  V <- (V'' + V''^T) / 2 + eps_V I,
         s = trace(U) / R,  U <- U / s,  V <- s V.
     Linear solves with the Cholesky factors, never explicit inverses.
   * Sampler: T' = 1 mu^T + Z L^T with L L^T = cov + eps I;
@@ -28,7 +29,9 @@ Readings (reading R18), where the extracted text is silent:
   * both per-update estimates use the U and V from before the update
     (a simultaneous, not a sequential, flip-flop);
   * eps = 1e-6 trace(A) / dim(A) for each factor A (the pages give
-    1e-6 trace(U) / M as the example);
+    1e-6 trace(U) / M as the example), with A the matrix being regularized:
+    the factor before the update for the two Cholesky factorizations, and
+    the EMA result U'' or V'' for the symmetrization step;
   * the random draws Z are standard normal from Philox4x64-10 (Salmon,
     Moraes, Dror and Shaw, SC'11), counter (i, 0, 0, 0) for block i and key
     (seed, 0), each 64-bit output u giving the uniform (u >> 11) 2^-53 and
@@ -117,8 +120,12 @@ def weight_update(state, W, m):
     LU = np.linalg.cholesky(U + _eps(U) * np.eye(R))
     Wu = np.linalg.solve(LU, Wc)              # LU^-1 Wc
     V1 = Wu.T @ Wu / R
-    U = m * U + (1 - m) * U1
-    V = m * V + (1 - m) * V1
+    U2 = m * U + (1 - m) * U1
+    V2 = m * V + (1 - m) * V1
+    # symmetrize and regularize the EMA results, then fix the Kronecker
+    # scale by the trace of U
+    U = 0.5 * (U2 + U2.T) + _eps(U2) * np.eye(R)
+    V = 0.5 * (V2 + V2.T) + _eps(V2) * np.eye(C)
     s = np.trace(U) / R
     return M, U / s, V * s
 

@@ -7,8 +7,11 @@ fixes them independently of its code:
   * the batched mean/scatter merge against NumPy's mean and cov of all the
     batches at once, also with a mean far larger than the spread;
   * the flip-flop: trace renormalization, symmetry and definiteness, the
-    Kronecker product unchanged by the renormalization, and convergence to
-    the true row and column covariances on matrix-normal samples;
+    Kronecker product unchanged by the renormalization, convergence to
+    the true row and column covariances on matrix-normal samples, and a
+    zero-residual update (W equal to the tracked mean) worked out by hand,
+    which fixes the EMA, the symmetrization + eps I step and the trace
+    renormalization in closed form;
   * the samplers against the moments of the distributions they sample.
 A dropped merge term, a transposed factor or a wrong solve fails one."""
 
@@ -102,7 +105,55 @@ def test_renormalization_keeps_the_kronecker_product():
     U1 = Wc @ np.linalg.inv(Vo + probe._eps(Vo) * np.eye(C)) @ Wc.T / C
     V1 = Wc.T @ np.linalg.inv(Uo + probe._eps(Uo) * np.eye(R)) @ Wc / R
     Uu, Vu = 0.9 * Uo + 0.1 * U1, 0.9 * Vo + 0.1 * V1
+    Uu = (Uu + Uu.T) / 2 + 1e-6 * np.trace(Uu) / R * np.eye(R)
+    Vu = (Vu + Vu.T) / 2 + 1e-6 * np.trace(Vu) / C * np.eye(C)
     np.testing.assert_allclose(np.kron(V, U), np.kron(Vu, Uu), rtol=1e-9, atol=1e-12)
+
+
+@pytest.mark.parametrize("m", [0.9, 0.99])
+def test_zero_residual_update_closed_form(m):
+    """W equal to the tracked mean: the mean stays, the centred residual and
+    both per-update estimates vanish, so U'' = m U and V'' = m V.  With
+    diagonal U = diag(u), V = diag(v) the pages' steps give by hand, with
+    tu = sum(u), tv = sum(v):
+        U <- m diag(u) + 1e-6 m tu / R I,   V <- m diag(v) + 1e-6 m tv / C I,
+        s = m tu (1 + 1e-6) / R,            U <- U / s,  V <- s V.
+    Dropping the eps I step moves every entry by about 1e-6 (relative); a
+    missing renormalization leaves trace(U) = m R (1 + 1e-6)."""
+    R, C = 5, 3
+    u = np.array([0.5, 1.0, 2.0, 4.0, 0.25])
+    v = np.array([3.0, 0.125, 1.5])
+    W = np.zeros((R, C))     # m W + (1 - m) W == W exactly, so Wc == 0 exactly
+    M, U, V = probe.weight_update((W.copy(), np.diag(u), np.diag(v)), W, m)
+    tu, tv = u.sum(), v.sum()
+    s = m * tu * (1 + 1e-6) / R
+    U_hand = np.diag((m * u + 1e-6 * m * tu / R) / s)
+    V_hand = np.diag((m * v + 1e-6 * m * tv / C) * s)
+    np.testing.assert_array_equal(M, W)
+    np.testing.assert_allclose(U, U_hand, rtol=1e-14, atol=0)
+    np.testing.assert_allclose(V, V_hand, rtol=1e-14, atol=0)
+    # the same without the regularization would be off by ~1e-6
+    assert abs(U[0, 0] / (u[0] / (tu / R)) - 1) > 5e-8
+
+
+def test_zero_residual_update_symmetrizes():
+    """An asymmetric U or V (an EMA of round-off, say) leaves the update as
+    the average of itself and its transpose plus eps I, then renormalized:
+    with W equal to the mean, U <- (m (U + U^T) / 2 + eps I) / s where
+    eps = 1e-6 m trace(U) / R and s = (m trace(U) + R eps) / R."""
+    R, C, m = 3, 2, 0.9
+    U0 = np.array([[2.0, 0.5, 0.0], [0.25, 1.0, 0.125], [0.0, 0.0, 3.0]])
+    V0 = np.array([[1.0, 0.0], [0.5, 2.0]])
+    W = np.zeros((R, C))
+    _, U, V = probe.weight_update((W.copy(), U0, V0), W, m)
+    eu = 1e-6 * m * 6.0 / R
+    ev = 1e-6 * m * 3.0 / C
+    s = (m * 6.0 + R * eu) / R
+    U_hand = (m * np.array([[2.0, 0.375, 0.0], [0.375, 1.0, 0.0625], [0.0, 0.0625, 3.0]]) + eu * np.eye(R)) / s
+    V_hand = (m * np.array([[1.0, 0.25], [0.25, 2.0]]) + ev * np.eye(C)) * s
+    np.testing.assert_allclose(U, U_hand, rtol=1e-14, atol=1e-16)
+    np.testing.assert_allclose(V, V_hand, rtol=1e-14, atol=1e-16)
+    np.testing.assert_array_equal(U, U.T)
 
 
 def test_input_sampler_moments():
