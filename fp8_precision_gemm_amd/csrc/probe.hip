@@ -3,7 +3,8 @@
 // batched mean/scatter merge (Chan, Golub and LeVeque's pairwise update,
 // accumulated in fp32 as the pages note), the weight tracker's matrix-normal
 // Kronecker flip-flop with an EMA (Cholesky factors and linear solves, no
-// explicit inverses; trace renormalization) and the two samplers.  All work
+// explicit inverses; the EMA results symmetrized with eps I added, then
+// the trace renormalization) and the two samplers.  All work
 // is fp32 vector arithmetic: the Probe runs every hundred or so steps, off
 // the training step's path, on K x K and R x C problems.
 #include <math.h>
@@ -81,6 +82,49 @@ __global__ __launch_bounds__(kPT) void k_weight_ema(const uint16_t* W, int64_t R
   Wc[i] = w - mm;
   const int64_t r = i / C, c = i - r * C;
   WcT[c * R + r] = w - mm;
+}
+
+// tr[0] = trace(U), tr[1] = trace(V) (one workgroup, fixed order)
+__global__ __launch_bounds__(kPT) void k_trace_pair(const float* U, int R, const float* V, int C, float* tr) {
+  __shared__ float red[2][kPT / 64];
+  float tu = 0.0f, tv = 0.0f;
+  for (int i = threadIdx.x; i < R; i += kPT) tu += U[(int64_t)i * R + i];
+  for (int i = threadIdx.x; i < C; i += kPT) tv += V[(int64_t)i * C + i];
+  tu = wave_sum(tu);
+  tv = wave_sum(tv);
+  if ((threadIdx.x & 63) == 0) {
+    red[0][threadIdx.x >> 6] = tu;
+    red[1][threadIdx.x >> 6] = tv;
+  }
+  __syncthreads();
+  if (threadIdx.x < 2) tr[threadIdx.x] = red[threadIdx.x][0] + red[threadIdx.x][1] + red[threadIdx.x][2] + red[threadIdx.x][3];
+}
+
+// the EMA results made symmetric and regularized, in place:
+// A <- (A + A^T) / 2 + eps I with eps = 1e-6 trace(A) / n (trace before the
+// step), for U (n = R) and V (n = C).  Thread e handles the pair (i, j),
+// i <= j, of element e = i n + j and writes both entries, so no entry is
+// read after another thread wrote it.
+__global__ __launch_bounds__(kPT) void k_sym_eps(float* U, int R, float* V, int C, const float* tr) {
+  const int64_t e = (int64_t)blockIdx.x * kPT + threadIdx.x;
+  if (e < (int64_t)R * R) {
+    const int64_t i = e / R, j = e - i * R;
+    if (i <= j) {
+      float a = 0.5f * (U[i * R + j] + U[j * R + i]);
+      if (i == j) a += 1e-6f * tr[0] / (float)R;
+      U[i * R + j] = a;
+      U[j * R + i] = a;
+    }
+  }
+  if (e < (int64_t)C * C) {
+    const int64_t i = e / C, j = e - i * C;
+    if (i <= j) {
+      float a = 0.5f * (V[i * C + j] + V[j * C + i]);
+      if (i == j) a += 1e-6f * tr[1] / (float)C;
+      V[i * C + j] = a;
+      V[j * C + i] = a;
+    }
+  }
 }
 
 // s = trace(U) / R (one workgroup), then U /= s, V *= s
@@ -544,6 +588,11 @@ hipError_t probe_weight_update(const ProbeWeightLaunch& a, hipStream_t s) {
   r.alpha = (1.0f - a.m) / (float)R;
   r.C = a.V;
   if ((e = gemm(GemmJob{C, C, R, 0, WuT, R, 1, WuT, R, 1, P}, r, s)) != hipSuccess) return e;
+  // U <- (U'' + U''^T) / 2 + eps I, V likewise, then s = trace(U) / R
+  hipLaunchKernelGGL(k_trace_pair, dim3(1), dim3(kPT), 0, s, a.U, (int)R, a.V, (int)C, sc + 1);
+  hipLaunchKernelGGL(k_sym_eps, dim3(blocks(max(R * R, C * C), kPT)), dim3(kPT), 0, s, a.U, (int)R, a.V, (int)C,
+                     sc + 1);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_trace, dim3(1), dim3(kPT), 0, s, a.U, (int)R, sc);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   hipLaunchKernelGGL(k_renorm, dim3(blocks(max(R * R, C * C), kPT)), dim3(kPT), 0, s, sc, R * R, C * C, a.U, a.V);

@@ -134,7 +134,7 @@ typedef struct {
   int32_t src_dtype;     /* loka_dtype   */
   int32_t fmt;           /* loka_fp8_fmt */
   int32_t mode;          /* loka_scaling */
-  int32_t transpose_out; /* 0 or 1       */
+  int32_t transpose_out; /* 0, 1 or 2    */
   const void* src;
   uint8_t* codes;
   void* scales;
@@ -467,7 +467,9 @@ loka_status loka_dispatch_select(const loka_dispatch_candidate* cands, int32_t n
  *     L_V L_V^T = V + eps I, Wt = Wc L_V^-T, U1 = Wt Wt^T / C,
  *     L_U L_U^T = U + eps I, Wu = L_U^-1 Wc, V1 = Wu^T Wu / R
  *     (both factors from the state before the update; linear solves, no
- *     inverses), U <- m U + (1 - m) U1, V <- m V + (1 - m) V1,
+ *     inverses), U'' = m U + (1 - m) U1, V'' = m V + (1 - m) V1,
+ *     U <- (U'' + U''^T) / 2 + eps'' I, V <- (V'' + V''^T) / 2 + eps'' I
+ *     (eps'' = 1e-6 trace(U'') / R, resp. 1e-6 trace(V'') / C),
  *     s = trace(U) / R, U <- U / s, V <- s V.
  *   info: device int[2], the Cholesky status of V and U (0, or the 1-based
  *   column of a non-positive pivot, after which the state is not valid).

@@ -80,6 +80,39 @@ def test_weight_flip_flop(lib, R, C):
     assert abs(np.trace(host(state["U"])) - R) < 1e-3 * R
 
 
+def test_weight_zero_residual_closed_form(lib):
+    """W equal to the tracked mean (both zero): U'' = m U, V'' = m V, then
+    the symmetrization with eps I and the trace renormalization in closed
+    form.  The diagonal spans four decades, so eps = 1e-6 trace / R moves the
+    smallest entries by about 1e-3 (relative), far above fp32 rounding; the
+    off-diagonal entries of U and V are asymmetric, so their average shows."""
+    R, C, m = 96, 40, 0.9
+    rng = np.random.default_rng(7)
+    u = np.logspace(-2, 2, R)
+    v = np.logspace(-1, 1, C)
+    U0 = np.diag(u) + np.tril(rng.standard_normal((R, R)), -1) * 1e-3
+    V0 = np.diag(v) + np.tril(rng.standard_normal((C, C)), -1) * 1e-3
+    dev = torch.device("cuda")
+    f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+    U0, V0 = U0.astype(np.float32).astype(np.float64), V0.astype(np.float32).astype(np.float64)
+    state = {"M": f32(np.zeros((R, C))), "U": f32(U0), "V": f32(V0),
+             "info": torch.zeros(2, dtype=torch.int32, device=dev)}
+    W = np.zeros((R, C), dtype=np.uint16)           # bf16 zeros
+    state = lk.loka_probe_weight_update(bf16_dev(W), state, m=m)
+    torch.cuda.synchronize()
+    eu, ev = 1e-6 * m * np.trace(U0) / R, 1e-6 * m * np.trace(V0) / C
+    s = (m * np.trace(U0) + R * eu) / R
+    U_hand = (m * (U0 + U0.T) / 2 + eu * np.eye(R)) / s
+    V_hand = (m * (V0 + V0.T) / 2 + ev * np.eye(C)) * s
+    for got, want, nm in ((state["U"], U_hand, "U"), (state["V"], V_hand, "V")):
+        g = host(got).astype(np.float64)
+        np.testing.assert_array_equal(g, g.T)
+        tol = 4e-6 * np.abs(want) + 1e-9 * np.abs(want).max()   # fp32 EMA, average, trace sum
+        err = np.abs(g - want)
+        assert np.all(err <= tol), f"{nm}: worst {np.max(err / tol):.3f} x tol"
+    np.testing.assert_array_equal(host(state["M"]), np.zeros((R, C), np.float32))
+
+
 def _close_bf16(got_bits, want, label):
     g = codec.bf16_to_f64(got_bits)
     scale = np.sqrt((want ** 2).mean(axis=1, keepdims=True))
