@@ -24,7 +24,8 @@ Modules:
   forward   quantize -> fp64 GEMM -> dequant + bias -> LayerNorm -> bf16
   backward  LayerNorm backward, e5m2 dZ, dgrad and wgrad in fp64
   grouped   the grouped forward as a list of independent forwards
-  mere      mean element-wise relative error report ([LoKA] section II-C)
+  mere      mean element-wise relative error ([LoKA] section II-C)
+  report    per-layer MERE of every workload against the bf16 reference
   dispatch  the Dispatch runtime's recipe selection rule ([LoKA] section III-C)
   probe     the Probe's input/weight statistics and sampler ([LoKA] section III-A1)
 
@@ -32,4 +33,4 @@ Parity unpinned: nothing.  Every function is pinned by tests/test_oracle_*.py
 against hand-worked encodings, closed forms, invariants or brute force.
 """
 
-from . import codec, quant, forward, backward, grouped, mere, dispatch, probe  # noqa: F401
+from . import codec, quant, forward, backward, grouped, mere, dispatch, probe, report  # noqa: F401

@@ -43,7 +43,7 @@ along the other dimension).
 import numpy as np
 
 from .codec import E4M3, E5M2, bf16_to_f64, decode_fp8, f32, f64_to_bf16
-from .forward import gemm_ln_forward, _vec
+from .forward import gemm_ln_forward, reference_forward, _vec
 from .quant import quantize, dequantize, ROW, COL, MX32_SQ
 
 
@@ -134,3 +134,17 @@ def gemm_ln_backward_sq(x_bits, w_bits, dy_bits, bias_bits=None, gamma_bits=None
         "dx": dx, "dx_bits": f64_to_bf16(dx), "dw": dw,
         "dgamma": dgamma, "dbeta": dbeta, "dbias": dz.sum(axis=0),
     }
+
+
+def reference_backward(x_bits, w_bits, dy_bits, bias_bits=None, gamma_bits=None, beta_bits=None, eps=1e-5):
+    """The unquantized bf16 reference of the backward: the exact fp64
+    gradients of sum(dY * Y) for Y = LayerNorm(X W + b) on the bf16 inputs
+    taken exactly (what the backward's quantization error is measured
+    against, reading R10).  Returns dz, dx = dZ W^T, dw = X^T dZ."""
+    x = bf16_to_f64(x_bits)
+    w = bf16_to_f64(w_bits)
+    dy = bf16_to_f64(dy_bits)
+    N = w.shape[1]
+    ref = reference_forward(x_bits, w_bits, bias_bits, gamma_bits, beta_bits, eps)
+    dz, _, _ = layernorm_backward(dy, ref["z"], ref["mean"], ref["rstd"], _vec(gamma_bits, N, 1.0))
+    return {"dz": dz, "dx": dz @ w.T, "dw": x.T @ dz}

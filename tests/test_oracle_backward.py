@@ -120,3 +120,40 @@ def test_full_backward_consistency():
     assert np.abs(out["dx"] - dx_plain).max() < 0.2 * np.abs(dx_plain).max()
     assert np.abs(out["dw"] - dw_plain).max() < 0.2 * np.abs(dw_plain).max()
     np.testing.assert_array_equal(out["dx_bits"], codec.f64_to_bf16(out["dx"]))
+
+
+def test_reference_backward_finite_differences():
+    """The unquantized reference backward against central differences of the
+    plain fp64 loss L(X, W, b) = sum(dY * LayerNorm(X W + b)) -- a function
+    written here from the definition, not from the oracle."""
+    rng = np.random.default_rng(21)
+    M, K, N = 3, 4, 5
+    x = rng.standard_normal((M, K))
+    w = rng.standard_normal((K, N))
+    b = rng.standard_normal(N)
+    g = 1 + 0.3 * rng.standard_normal(N)
+    be = rng.standard_normal(N)
+    dy = rng.standard_normal((M, N))
+    xb, wb, bb, gb, beb, dyb = (to_bf16_bits(a) for a in (x, w, b, g, be, dy))
+    x, w, b, g, be, dy = (codec.bf16_to_f64(a) for a in (xb, wb, bb, gb, beb, dyb))
+    eps = float(np.float32(1e-5))
+
+    def loss(xx, ww):
+        z = xx @ ww + b[None, :]
+        mu = z.mean(axis=1, keepdims=True)
+        var = ((z - mu) ** 2).mean(axis=1, keepdims=True)
+        return np.sum(dy * (g * (z - mu) / np.sqrt(var + eps) + be))
+
+    ref = backward.reference_backward(xb, wb, dyb, bb, gb, beb)
+    h = 1e-6
+    for arr, grad in ((x, ref["dx"]), (w, ref["dw"])):
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + h
+            lp = loss(x, w)
+            arr[idx] = old - h
+            lm = loss(x, w)
+            arr[idx] = old
+            fd[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(grad, fd, rtol=1e-6, atol=1e-7)

@@ -224,3 +224,70 @@ def test_reference_forward_quantization_error_is_small():
     sigma = np.sqrt(ref["z"].var(axis=1))
     rel_row = np.abs(out["z"] - ref["z"]) / sigma[:, None]
     assert 1e-4 < rel_row.max() < 0.2
+
+
+def test_reference_forward_exact_rationals():
+    """The unquantized reference against exact rational arithmetic on a tiny
+    problem with bias, gamma and beta: Z = X.W + b entry by entry (the
+    products and sums of these bf16 values are exact in fp64, so Z must
+    match bit for bit), then the mean and population variance exactly, and
+    y = gamma (z - mean) / sqrt(v + eps) + beta with one final square root.
+    A dropped bias, a transposed W (the shape is square and W asymmetric) or
+    a mean over the wrong axis fails."""
+    rng = np.random.default_rng(11)
+    M, K, N = 3, 6, 6
+    x = np.ldexp(rng.integers(-255, 256, size=(M, K)), rng.integers(-6, -3, size=(M, K))).astype(np.float64)
+    w = np.ldexp(rng.integers(-255, 256, size=(K, N)), rng.integers(-9, -6, size=(K, N))).astype(np.float64)
+    assert not np.allclose(w, w.T)
+    b = np.ldexp(rng.integers(-255, 256, size=N), -8).astype(np.float64)
+    g = np.ldexp(rng.integers(64, 256, size=N), -7).astype(np.float64)
+    be = np.ldexp(rng.integers(-128, 128, size=N), -7).astype(np.float64)
+    xb, wb, bb, gb, beb = (to_bf16_bits(a) for a in (x, w, b, g, be))
+    for a, ab in ((x, xb), (w, wb), (b, bb), (g, gb), (be, beb)):
+        assert np.all(codec.bf16_to_f64(ab) == a)
+    ref = forward.reference_forward(xb, wb, bb, gb, beb)
+    eps = Fraction(float(np.float32(1e-5)))
+    for m in range(M):
+        z = [sum(Fraction(x[m, k]) * Fraction(w[k, n]) for k in range(K)) + Fraction(b[n]) for n in range(N)]
+        for n in range(N):
+            assert Fraction(ref["z"][m, n]) == z[n]
+        mu = sum(z) / N
+        v = sum((zz - mu) ** 2 for zz in z) / N
+        rstd = 1.0 / np.sqrt(float(v + eps))
+        assert abs(ref["mean"][m] - float(mu)) <= 1e-15 * max(abs(float(mu)), 1e-30)
+        for n in range(N):
+            y = float(Fraction(g[n]) * (z[n] - mu)) * rstd + be[n]
+            assert abs(ref["y"][m, n] - y) <= 1e-13 * (abs(y) + 1)
+
+
+@pytest.mark.parametrize("recipe", ["tensor", "row", "mx32"])
+def test_reference_equals_quantized_on_lossless_inputs(recipe):
+    """Inputs on the e4m3 grid whose group maxima are 448 * 2**j quantize
+    exactly, so the quantized block and the unquantized reference are the
+    same computation: Z and Y equal bit for bit, and the MERE of both is 0
+    over every nonzero entry."""
+    rng = np.random.default_rng(12)
+    M, K, N = 40, 96, 48
+    x = _grid_values(rng, (M, K), E4)
+    w = _grid_values(rng, (K, N), E4, axis=0)
+    if recipe == "mx32":
+        for blk in range(K // 32):
+            x[:, 32 * blk] = 448.0
+            w[32 * blk, :] = -448.0
+        x = np.ldexp(x, np.repeat(rng.integers(-10, 3, size=(M, K // 32)), 32, axis=1))
+        w = np.ldexp(w, np.repeat(rng.integers(-10, 3, size=(N, K // 32)), 32, axis=1).T)
+    elif recipe == "row":
+        x = np.ldexp(x, rng.integers(-10, 3, size=M)[:, None])
+        w = np.ldexp(w, rng.integers(-10, 3, size=N)[None, :])
+    else:
+        x, w = np.ldexp(x, -2), np.ldexp(w, -6)
+    xb, wb = to_bf16_bits(x), to_bf16_bits(w)
+    assert np.all(codec.bf16_to_f64(xb) == x) and np.all(codec.bf16_to_f64(wb) == w)
+    c = forward_case(M, K, N, seed=13, gamma_var=0.1, beta_var=0.1)
+    out = forward.gemm_ln_forward(xb, wb, c["bias"], c["gamma"], c["beta"], recipe=recipe)
+    ref = forward.reference_forward(xb, wb, c["bias"], c["gamma"], c["beta"])
+    np.testing.assert_array_equal(out["z"], ref["z"])
+    np.testing.assert_array_equal(out["y"], ref["y"])
+    for a, r in ((out["z"], ref["z"]), (out["y"], ref["y"])):
+        v, n = mere.mere(a, r)
+        assert v == 0.0 and n == int((r != 0).sum()) and n > 0
