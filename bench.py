@@ -11,10 +11,18 @@ reported under `rows`.  Inputs are resident in HBM; 16 rotating
 input/output sets (537 MB) keep the 256 MB Infinity Cache from serving them.
 Launches are replayed from a HIP graph so host launch cost does not enter.
 
+Timing: `--warmup` launches untimed, then 5 batches of max(--steps, 100)
+launches (rounded up to whole graph replays), each bracketed by HIP events
+on the launch stream; the per-launch time is the median batch's, and
+`timing` gives the batch count, the launches per batch and in total, and the
+fastest and slowest batch.
+
 Prints one JSON line.  `roofline` is for the fused forward kernel (HBM
 bound: 254 FLOP/B against a ridge of 625); `cpu_baseline` is the NumPy
-oracle on this host's cores.  Other workloads of the block (tensor recipe,
-MX, backward, grouped) are timed the same way and reported under `rows`.
+oracle on this host's cores (and on one thread); `oracle_mere` (and each
+row's) is the oracle's per-layer quantization error against the bf16
+reference.  Other workloads of the block (tensor recipe, MX, backward,
+grouped, ...) are timed the same way and reported under `rows`.
 """
 
 import argparse
@@ -40,9 +48,10 @@ TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_fwd_row_16384x512x512_hbm_co
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=2000)
-    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-oracle-report", action="store_true", help="skip the oracle's MERE report")
     p.add_argument("--no-rows", action="store_true", help="skip the other workloads")
     p.add_argument("--only", default=None,
                    help="comma list of workloads to time (for profiling): "
@@ -77,9 +86,17 @@ def measured_traffic():
     return int(fields["traffic_bytes_per_launch"])
 
 
+BATCHES = 5          # timed batches; the reported time is their median
+MIN_BATCH = 100      # launches per batch, at least
+
+
 def timed_graph(torch, launches, steps, warmup, stream):
-    """Capture `launches` (callables enqueuing on `stream`) into one graph,
-    replay it until `steps` launches ran; returns (seconds, launches run)."""
+    """Capture `launches` (callables enqueuing on `stream`) into one graph and
+    time its replays: `warmup` launches untimed, then BATCHES batches of at
+    least max(steps, MIN_BATCH) launches each (whole replays), each batch
+    bracketed by HIP events on `stream`.  Returns (median seconds per launch,
+    info) with info = {"batches", "launches_per_batch", "timed_launches",
+    "us_min", "us_max"} (per-launch times of the fastest and slowest batch)."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         for f in launches:  # eager warm-up (kernel attribute set-up happens here)
@@ -88,21 +105,27 @@ def timed_graph(torch, launches, steps, warmup, stream):
     with torch.cuda.graph(g, stream=stream):
         for f in launches:
             f()
-    reps_w = max(1, warmup // len(launches))
-    reps = max(1, steps // len(launches))
+    n = len(launches)
+    reps_w = max(1, -(-warmup // n))
+    reps = max(1, -(-max(steps, MIN_BATCH) // n))
     for _ in range(reps_w):
         g.replay()
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        e0.record(stream)
-        for _ in range(reps):
-            g.replay()
-        e1.record(stream)
-    e1.synchronize()
+    per = []
+    for _ in range(BATCHES):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+        e1.synchronize()
+        per.append(e0.elapsed_time(e1) / 1e3 / (reps * n))
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / 1e3, reps * len(launches)
+    info = {"batches": BATCHES, "launches_per_batch": reps * n, "timed_launches": BATCHES * reps * n,
+            "us_min": round(min(per) * 1e6, 3), "us_max": round(max(per) * 1e6, 3)}
+    return float(np.median(per)), info
 
 
 def dev_bf16(torch, bits):
@@ -130,10 +153,9 @@ def bench_forward(torch, lk, case, x_mode, steps, warmup, stream, packed=True, e
                                    epilogue=epilogue)
         launches.append(f)
     torch.cuda.synchronize()
-    secs, n = timed_graph(torch, launches, steps, warmup, stream)
-    per = secs / n
+    per, tinfo = timed_graph(torch, launches, steps, warmup, stream)
     if not packed:
-        return {"us": per * 1e6}
+        return {"us": per * 1e6, "timing": tinfo}
     flops = 2.0 * M * N * K
     nbytes = fwd_bytes(M, K, N, mx=x_mode == "mx32_row")
     # the weight quantization (once per training step), same rotation
@@ -147,9 +169,9 @@ def bench_forward(torch, lk, case, x_mode, steps, warmup, stream, packed=True, e
         qwi, swi = torch.empty_like(qw), torch.empty_like(sw)
         wq.append(lambda wi=wi, qwi=qwi, swi=swi: lk.loka_quant_fp8(
             wi, mode=wmode, transpose_out=layout, codes=qwi, scales=swi, stream=stream, workspace=wsq))
-    wsecs, wn = timed_graph(torch, wq, min(steps, 800), min(warmup, 80), stream)
+    wper, _ = timed_graph(torch, wq, min(steps, 800), min(warmup, 80), stream)
     return {"us": per * 1e6, "tflops": flops / per / 1e12, "gbs": nbytes / per / 1e9, "bytes": nbytes,
-            "flops": flops, "weight_quant_us": wsecs / wn * 1e6}
+            "flops": flops, "weight_quant_us": wper * 1e6, "timing": tinfo}
 
 
 def bench_backward(torch, lk, case, steps, warmup, stream):
@@ -166,11 +188,11 @@ def bench_backward(torch, lk, case, steps, warmup, stream):
         fn, _ = lk.loka_gemm_fp8_bwd(dyi, x, qwr, swr, ctx=ctx, bias=bias, gamma=gamma, stream=stream, prepare=True)
         launches.append(fn)
     torch.cuda.synchronize()
-    secs, n = timed_graph(torch, launches, max(40, steps // 20), max(8, warmup // 20), stream)
-    per = secs / n
+    per, tinfo = timed_graph(torch, launches, steps, warmup, stream)
     flops = 2.0 * M * N * K * 3  # recomputed Z, dgrad, wgrad
     nbytes = 2 * M * N + M * K + 2 * M * K + 2 * M * K + 4 * K * N  # dY, qX, X, dX, dW (minimum)
-    return {"us": per * 1e6, "tflops": flops / per / 1e12, "gbs_min_bytes": nbytes / per / 1e9}
+    return {"us": per * 1e6, "tflops": flops / per / 1e12, "gbs_min_bytes": nbytes / per / 1e9,
+            "min_bytes": nbytes, "timing": tinfo}
 
 
 def bench_square(torch, lk, case, steps, warmup, stream):
@@ -195,12 +217,11 @@ def bench_square(torch, lk, case, steps, warmup, stream):
         quants.append(lambda xi=xi, ci=ci, si=si: lk.loka_quant_fp8(xi, mode="mx32_sq", codes=ci, scales=si,
                                                                      stream=stream))
     torch.cuda.synchronize()
-    secs, n = timed_graph(torch, launches, steps, warmup, stream)
-    per = secs / n
-    qsecs, qn = timed_graph(torch, quants, min(steps, 800), min(warmup, 80), stream)
+    per, tinfo = timed_graph(torch, launches, steps, warmup, stream)
+    qper, _ = timed_graph(torch, quants, min(steps, 800), min(warmup, 80), stream)
     nbytes = M * K + (M // 32) * (K // 32) + N * K + (K // 32) * (N // 32) + 3 * 2 * N + 2 * M * N
     fwd = {"us": per * 1e6, "tflops": 2.0 * M * N * K / per / 1e12, "gbs": nbytes / per / 1e9, "bytes": nbytes,
-           "x_quant_us": qsecs / qn * 1e6}
+           "x_quant_us": qper * 1e6, "timing": tinfo}
     f = lk.loka_gemm_fp8_ln(qx, qw, sw, bias, gamma, beta, x_mode="mx32_sq", x_scales=sx, want_stats=True,
                             stream=stream)
     ctx = {"qx": qx, "sx": sx, "qw": qw, "sw": sw, "mean": f["mean"], "rstd": f["rstd"]}
@@ -211,10 +232,10 @@ def bench_square(torch, lk, case, steps, warmup, stream):
                                      prepare=True, square=True)
         launches.append(fn)
     torch.cuda.synchronize()
-    secs, n = timed_graph(torch, launches, max(40, steps // 20), max(8, warmup // 20), stream)
-    per = secs / n
+    per, tinfo = timed_graph(torch, launches, steps, warmup, stream)
     nbytes = 2 * M * N + M * K + 2 * M * K + 4 * K * N  # dY, qX, dX, dW (minimum)
-    bwd = {"us": per * 1e6, "tflops": 2.0 * M * N * K * 3 / per / 1e12, "gbs_min_bytes": nbytes / per / 1e9}
+    bwd = {"us": per * 1e6, "tflops": 2.0 * M * N * K * 3 / per / 1e12, "gbs_min_bytes": nbytes / per / 1e9,
+           "min_bytes": nbytes, "timing": tinfo}
     return fwd, bwd
 
 
@@ -259,10 +280,9 @@ def bench_grouped(torch, lk, groups, steps, warmup, stream):
         nbytes += fwd_bytes(g["M"], g["K"], g["N"])
     fn, _ = lk.loka_grouped_gemm_fp8_ln(dg, stream=stream, prepare=True, w_packed=True)
     torch.cuda.synchronize()
-    secs, n = timed_graph(torch, [fn], max(20, steps // 40), max(4, warmup // 40), stream)
-    per = secs / n
+    per, tinfo = timed_graph(torch, [fn], steps, warmup, stream)
     return {"us": per * 1e6, "tflops": flops / per / 1e12, "gbs": nbytes / per / 1e9, "bytes": nbytes,
-            "flops": flops}
+            "flops": flops, "timing": tinfo}
 
 
 def bench_copy(torch, steps, warmup, stream):
@@ -273,29 +293,118 @@ def bench_copy(torch, steps, warmup, stream):
     src = [torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_() for _ in range(ROTATE)]
     dst = [torch.empty_like(t) for t in src]
     launches = [lambda a=a, b=b: b.copy_(a) for a, b in zip(src, dst)]
-    secs, n = timed_graph(torch, launches, steps, warmup, stream)
-    per = secs / n
-    return {"us": per * 1e6, "gbs": 2 * nbytes / per / 1e9, "bytes_read": nbytes, "bytes_written": nbytes}
+    per, tinfo = timed_graph(torch, launches, steps, warmup, stream)
+    return {"us": per * 1e6, "gbs": 2 * nbytes / per / 1e9, "bytes_read": nbytes, "bytes_written": nbytes,
+            "timing": tinfo}
 
 
-def cpu_baseline(case):
-    """The NumPy oracle, untuned, on one host thread: the full rowwise
-    forward (quantize X and W, fp64 GEMM, LayerNorm, bf16 rounding)."""
+CPU_SHARE = 16      # host threads a one-GPU job may use
+CHUNK_ROWS = 256    # rows per task of the MERE report's row blocks
+
+
+def host_cpu():
+    """(threads to use, CPU model) of this host."""
+    n = min(len(os.sched_getaffinity(0)), CPU_SHARE)
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return n, model
+
+
+def cpu_baseline(case, threads, model, budget_s=8.0):
+    """The NumPy oracle as it stands (untuned) on the host: full rowwise
+    forwards (quantize X and W, fp64 GEMM, LayerNorm, bf16 rounding) of the
+    headline workload, its rows split into one block per thread (rows are
+    independent in the rowwise recipe; each block quantizes W again), the
+    blocks spread over `threads` host threads (NumPy's own BLAS pinned to one
+    thread each), repeated for about budget_s seconds; then the same blocks
+    on one thread over a sample of the rows.  TFLOP/s counts 2 M N K per
+    forward, as the GPU's value does."""
+    from concurrent.futures import ThreadPoolExecutor
     from threadpoolctl import threadpool_limits
     from oracle import forward
     M, K, N = case["M"], case["K"], case["N"]
-    with threadpool_limits(limits=1):
+    rows = max(256, (M // threads + 31) // 32 * 32)
+    spans = [(lo, min(lo + rows, M)) for lo in range(0, M, rows)]
+
+    def one(span):
+        lo, hi = span
+        forward.gemm_ln_forward(case["x"][lo:hi], case["w"], case["bias"], case["gamma"], case["beta"], recipe="row")
+
+    with threadpool_limits(limits=1), ThreadPoolExecutor(threads) as ex:
         t0 = time.perf_counter()
         reps = 0
-        while True:
-            forward.gemm_ln_forward(case["x"], case["w"], case["bias"], case["gamma"], case["beta"], recipe="row")
+        while reps == 0 or time.perf_counter() - t0 < budget_s:
+            list(ex.map(one, spans))
             reps += 1
-            if time.perf_counter() - t0 > 12.0:
-                break
         dt = (time.perf_counter() - t0) / reps
-    return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full rowwise forward(s) of M={M},K={K},N={N} on one host thread, "
-                      f"{dt:.2f} s each"}
+        t0 = time.perf_counter()
+        done = 0
+        while done < len(spans) and (done < 2 or time.perf_counter() - t0 < budget_s / 2):
+            one(spans[done])
+            done += 1
+        dt1 = (time.perf_counter() - t0) / (sum(hi - lo for lo, hi in spans[:done]) / M)
+    return {"value": 2.0 * M * N * K / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model,
+            "sample": f"{reps} full rowwise forward(s) of M={M},K={K},N={N}, {len(spans)} blocks of {rows} "
+                      f"rows over {threads} host threads, {dt:.3f} s each",
+            "one_thread": {"value": 2.0 * M * N * K / dt1 / 1e12, "unit": "TFLOP/s",
+                           "sample": f"{done} of the {len(spans)} blocks of the same forward on one thread, "
+                                     f"scaled to the full forward: {dt1:.2f} s"}}
+
+
+def oracle_report(cases, threads):
+    """The oracle's per-layer quantization error (MERE of each workload's
+    outputs against the unquantized bf16 reference) for every workload,
+    whole: Z and Y per forward (the MX workload's rows in blocks over the
+    host threads, which gives the same numbers), dZ, dX and dW for the
+    training step, and every group of the grouped workload."""
+    from concurrent.futures import ThreadPoolExecutor
+    from threadpoolctl import threadpool_limits
+    from oracle import report
+    out = {}
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1), ThreadPoolExecutor(threads) as ex:
+        for name, (c, recipe) in cases["forward"].items():
+            r = report.forward_error(c["x"], c["w"], c["bias"], c["gamma"], c["beta"], recipe, pmap=ex.map,
+                                     chunk_rows=CHUNK_ROWS)
+            out[name] = {k: {"mere": round(v["mere"], 6), "count": v["count"]} for k, v in r.items()}
+        if "backward" in cases:
+            name, c = cases["backward"]
+            r = report.backward_error(c["x"], c["w"], c["dy"], c["bias"], c["gamma"], c["beta"])
+            out[name] = {k: {"mere": round(v["mere"], 6), "count": v["count"]} for k, v in r.items()}
+        if "grouped" in cases:
+            name, gs = cases["grouped"]
+            per = report.grouped_error(gs, pmap=ex.map)
+            out[name] = {"per_group": [{k: round(v["mere"], 6) for k, v in p.items()} for p in per],
+                         "summary": report.summarize(per)}
+    out["seconds"] = round(time.perf_counter() - t0, 1)
+    return out
+
+
+def gpu_clock():
+    """The device name and shader clock: the current and highest SCLK levels
+    from the driver's sysfs table (the current level is marked '*'), read
+    right after the timed region."""
+    import glob
+    out = {}
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            levels = [l.strip() for l in open(f) if l.strip()]
+        except OSError:
+            continue
+        cur = [l for l in levels if l.endswith("*")]
+        out[f.split("/")[4]] = {"current": cur[0].rstrip(" *") if cur else None, "levels": levels}
+    return out
+
+
+def _rounded(r):
+    return {k: (round(v, 3) if isinstance(v, float) else v) for k, v in r.items()}
 
 
 def main():
@@ -319,40 +428,43 @@ def main():
     main_res = None
     if want("fwd"):
         main_res = bench_forward(torch, lk, case, "row", args.steps, args.warmup, stream)
-        print(f"[bench] rowwise forward: {main_res['us']:.2f} us/launch", file=sys.stderr, flush=True)
+        clock = gpu_clock()
+        print(f"[bench] rowwise forward: {main_res['us']:.2f} us/launch (median of {main_res['timing']['batches']} "
+              f"batches of {main_res['timing']['launches_per_batch']})", file=sys.stderr, flush=True)
         if not args.no_rows:
             r = bench_forward(torch, lk, case, "row", max(200, args.steps // 4), max(20, args.warmup // 4), stream,
                               packed=False)
-            rows["fwd_16384x512x512_rowmajor_weight"] = {"us": round(r["us"], 3)}
+            rows["fwd_16384x512x512_rowmajor_weight"] = {"us": round(r["us"], 3), "timing": r["timing"]}
             print(f"[bench] rowwise forward, row-major weight: {r['us']:.2f} us", file=sys.stderr, flush=True)
+    tcase = mxcase = gcase = None
     if not args.no_rows and want("tensor"):
-        r = bench_forward(torch, lk, workloads.tensor_case(), "tensor", args.steps, args.warmup, stream)
-        rows["tensor_fwd_512x256x256"] = {k: round(v, 3) for k, v in r.items()}
+        tcase = workloads.tensor_case()
+        r = bench_forward(torch, lk, tcase, "tensor", args.steps, args.warmup, stream)
+        rows["tensor_fwd_512x256x256"] = _rounded(r)
         print(f"[bench] tensor forward: {r['us']:.2f} us", file=sys.stderr, flush=True)
     if not args.no_rows and want("mx"):
-        r = bench_forward(torch, lk, workloads.mx_case(), "mx32_row", max(200, args.steps // 4),
-                          max(20, args.warmup // 4), stream)
-        rows["mx_fwd_65536x1024x256"] = {k: round(v, 3) for k, v in r.items()}
+        mxcase = workloads.mx_case()
+        r = bench_forward(torch, lk, mxcase, "mx32_row", args.steps, args.warmup, stream)
+        rows["mx_fwd_65536x1024x256"] = _rounded(r)
         rows["mx_fwd_65536x1024x256"]["hbm_frac"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
         print(f"[bench] mx forward: {r['us']:.2f} us", file=sys.stderr, flush=True)
     if not args.no_rows and want("blocknorm"):
         for nm, c in (("blocknorm_fwd_16384x512x512", case),
                       ("blocknorm_fwd_4096x512x4096", workloads.forward_case(4096, 512, 4096, seed=7,
                                                                              x_dist="student_t3_outliers"))):
-            r = bench_forward(torch, lk, c, "row", max(200, args.steps // 4), max(20, args.warmup // 4), stream,
-                              epilogue="blocknorm_hswish")
-            rows[nm] = {k: round(v, 3) for k, v in r.items()}
+            r = bench_forward(torch, lk, c, "row", args.steps, args.warmup, stream, epilogue="blocknorm_hswish")
+            rows[nm] = _rounded(r)
             rows[nm]["hbm_frac"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
             print(f"[bench] {nm}: {r['us']:.2f} us", file=sys.stderr, flush=True)
     if not args.no_rows and want("bwd"):
         r = bench_backward(torch, lk, case, args.steps, args.warmup, stream)
-        rows["bwd_16384x512x512"] = {k: round(v, 3) for k, v in r.items()}
+        rows["bwd_16384x512x512"] = _rounded(r)
         print(f"[bench] backward: {r['us']:.2f} us", file=sys.stderr, flush=True)
     if not args.no_rows and want("square"):
-        f, b = bench_square(torch, lk, case, max(200, args.steps // 4), max(20, args.warmup // 4), stream)
-        rows["square_fwd_16384x512x512"] = {k: round(v, 3) for k, v in f.items()}
+        f, b = bench_square(torch, lk, case, args.steps, args.warmup, stream)
+        rows["square_fwd_16384x512x512"] = _rounded(f)
         rows["square_fwd_16384x512x512"]["hbm_frac"] = round(f["gbs"] / PEAK_HBM_GBS, 4)
-        rows["square_bwd_16384x512x512"] = {k: round(v, 3) for k, v in b.items()}
+        rows["square_bwd_16384x512x512"] = _rounded(b)
         print(f"[bench] square forward: {f['us']:.2f} us (X quantization {f['x_quant_us']:.2f} us); "
               f"square backward: {b['us']:.2f} us", file=sys.stderr, flush=True)
     if not args.no_rows and want("dispatch"):
@@ -373,19 +485,38 @@ def main():
         rows["probe_16384x512x512"] = {k: round(v, 2) for k, v in r.items()}
         print("[bench] probe: " + ", ".join(f"{k} {v:.1f}" for k, v in r.items()), file=sys.stderr, flush=True)
     if not args.no_rows and want("grouped"):
-        r = bench_grouped(torch, lk, workloads.grouped_case(), args.steps, args.warmup, stream)
-        rows["grouped_64x8192"] = {k: round(v, 3) for k, v in r.items()}
+        gcase = workloads.grouped_case()
+        r = bench_grouped(torch, lk, gcase, args.steps, args.warmup, stream)
+        rows["grouped_64x8192"] = _rounded(r)
         rows["grouped_64x8192"]["hbm_frac"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
         print(f"[bench] grouped: {r['us']:.2f} us", file=sys.stderr, flush=True)
     if only is not None and "copy" in only:
         r = bench_copy(torch, args.steps, args.warmup, stream)
-        rows["copy_16MiB"] = {k: round(v, 3) for k, v in r.items()}
+        rows["copy_16MiB"] = _rounded(r)
         print(f"[bench] copy 16 MiB: {r['us']:.2f} us", file=sys.stderr, flush=True)
     if main_res is None:
         print(json.dumps({"rows": rows}))
         return
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline(case)
+    threads, model = host_cpu()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(case, threads, model)
+    report = None
+    if not args.no_oracle_report:
+        fwd_cases = {"fwd_16384x512x512": (case, "row")}
+        if tcase is not None:
+            fwd_cases["tensor_fwd_512x256x256"] = (tcase, "tensor")
+        if mxcase is not None:
+            fwd_cases["mx_fwd_65536x1024x256"] = (mxcase, "mx32")
+        rcases = {"forward": fwd_cases}
+        if "bwd_16384x512x512" in rows:
+            rcases["backward"] = ("bwd_16384x512x512", case)
+        if gcase is not None:
+            rcases["grouped"] = ("grouped_64x8192", gcase)
+        report = oracle_report(rcases, threads)
+        for name, r in report.items():
+            if name in rows:
+                rows[name]["oracle_mere"] = r
+        print(f"[bench] oracle MERE report: {report['seconds']} s on {threads} threads", file=sys.stderr, flush=True)
     ms = main_res["us"] / 1e3
     out = {
         "metric": METRIC,
@@ -411,6 +542,11 @@ def main():
                      "kernel": "k_fwd_res<row> (weight-resident fused X quant + FP8 MFMA GEMM + LayerNorm)",
                      "algorithmic_bytes_per_launch": main_res["bytes"],
                      "avg_launch_us": round(main_res["us"], 3)},
+        "timing": main_res["timing"],
+        "gpu": {"name": torch.cuda.get_device_properties(0).name,
+                "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
+                "sclk_after_headline": clock},
+        "oracle_mere": None if report is None else report["fwd_16384x512x512"],
         "weight_quant_us": round(main_res["weight_quant_us"], 3),
         "value_incl_weight_quant": round(main_res["flops"] / ((main_res["us"] + main_res["weight_quant_us"]) * 1e-6)
                                          / 1e12, 2),
