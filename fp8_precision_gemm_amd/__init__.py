@@ -120,6 +120,7 @@ def library():
                                "`python -m fp8_precision_gemm_amd.build` (no fallback exists)")
         lib = ctypes.CDLL(library_path)
         for name, argt in [("loka_quant_fp8", QuantArgs), ("loka_gemm_fp8_ln", FwdArgs),
+                           ("loka_gemm_fp8_ln_noalloc", FwdArgs),
                            ("loka_gemm_fp8_bwd", BwdArgs), ("loka_grouped_gemm_fp8_ln", GroupedArgs),
                            ("loka_mere_z", MereArgs), ("loka_probe_input_update", ProbeInputArgs),
                            ("loka_probe_weight_update", ProbeWeightArgs),
@@ -252,7 +253,7 @@ def _fwd_args(x, qw, sw, bias, gamma, beta, eps, x_mode, y, z, mean, rstd, qx_ou
 
 def loka_gemm_fp8_ln(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e-5, x_mode="row", y=None, want_z=False,
                      want_stats=False, want_qx=False, workspace=None, stream=None, prepare=False, w_packed=False,
-                     epilogue="layernorm", x_scales=None, want_y_square=False):
+                     epilogue="layernorm", x_scales=None, want_y_square=False, _noalloc=False):
     """Y = LayerNorm(dequant(q(X) . q(W)) + bias) for bf16 X [M, K] and the
     pre-quantized weight qw [N, K] (e4m3) with scales sw; with w_packed=True
     qw is in the packed layout (loka_quant_fp8(transpose_out="packed")).
@@ -301,13 +302,17 @@ def loka_gemm_fp8_ln(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e-5, x_mo
                   out.get("rstd"), out.get("qx"), out.get("sx"), w_packed, epilogue, x_scales, out.get("y_codes"),
                   out.get("y_scales"))
     lib = library()
-    nb = lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(a))
-    ws = _workspace(nb, dev, workspace)
-    a.workspace = _ptr(ws)
-    a.workspace_bytes = nb if ws is None else ws.numel()
+    if _noalloc:
+        ws = None
+        a.workspace, a.workspace_bytes = None, 0
+    else:
+        nb = lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(a))
+        ws = _workspace(nb, dev, workspace)
+        a.workspace = _ptr(ws)
+        a.workspace_bytes = nb if ws is None else ws.numel()
     keep = (x, qw, sw, bias, gamma, beta, ws, out, x_scales)
     st = _stream(stream)
-    fn = lib.loka_gemm_fp8_ln
+    fn = lib.loka_gemm_fp8_ln_noalloc if _noalloc else lib.loka_gemm_fp8_ln
     ref = ctypes.byref(a)
 
     def launch():
@@ -318,6 +323,16 @@ def loka_gemm_fp8_ln(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e-5, x_mo
         return launch, out
     launch()
     return out
+
+
+def loka_gemm_fp8_ln_noalloc(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e-5, x_mode="row", y=None,
+                             want_z=False, want_stats=False, want_qx=False, stream=None, prepare=False,
+                             w_packed=False, epilogue="layernorm", x_scales=None, want_y_square=False):
+    """loka_gemm_fp8_ln through the allocation-free entry point: the same
+    arguments and outputs, no workspace (the library's fixed per-GPU device
+    scratch serves instead; calls on one GPU must not overlap)."""
+    return loka_gemm_fp8_ln(x, qw, sw, bias, gamma, beta, eps, x_mode, y, want_z, want_stats, want_qx, None,
+                            stream, prepare, w_packed, epilogue, x_scales, want_y_square, _noalloc=True)
 
 
 def loka_gemm_fp8_bwd(dy, x, qw_row, sw_row, ctx=None, bias=None, gamma=None, no_ln=False, want_dz=False,

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblokafp8.so")
 SOURCES = ["api.cpp", "quant.hip", "gemm_ln_fwd.hip", "fwd_tensor.hip", "fwd_row.hip", "fwd_blocknorm.hip", "fwd_mx.hip", "fwd_mxsq.hip",
-           "grouped.hip", "gemm_bwd.hip", "mere.hip", "probe.hip"]
+           "grouped.hip", "gemm_bwd.hip", "mere.hip", "probe.hip", "fwd_noalloc.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

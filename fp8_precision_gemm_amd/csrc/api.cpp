@@ -141,7 +141,12 @@ size_t loka_gemm_fp8_ln_workspace_size(const loka_fwd_args* a) {
                                    (a->flags & LOKA_FWD_BLOCKNORM_HSWISH) != 0);
 }
 
-loka_status loka_gemm_fp8_ln(const loka_fwd_args* a, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Every check of loka_gemm_fp8_ln except the workspace's.
+loka_status validate_fwd(const loka_fwd_args* a) {
   REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
   REQUIRE(a->x_mode == LOKA_SCALE_TENSOR || a->x_mode == LOKA_SCALE_ROW || a->x_mode == LOKA_SCALE_MX32_ROW ||
               a->x_mode == LOKA_SCALE_MX32_SQ,
@@ -195,19 +200,50 @@ loka_status loka_gemm_fp8_ln(const loka_fwd_args* a, void* stream) {
   REQUIRE_ALIGNED(a->x); REQUIRE_ALIGNED(a->qw); REQUIRE_ALIGNED(a->sw); REQUIRE_ALIGNED(a->bias);
   REQUIRE_ALIGNED(a->gamma); REQUIRE_ALIGNED(a->beta); REQUIRE_ALIGNED(a->y); REQUIRE_ALIGNED(a->z);
   REQUIRE_ALIGNED(a->mean); REQUIRE_ALIGNED(a->rstd); REQUIRE_ALIGNED(a->qx_out); REQUIRE_ALIGNED(a->sx_out);
-  if ((st = check_workspace(loka_gemm_fp8_ln_workspace_size(a), a->workspace, a->workspace_bytes)) != LOKA_OK) return st;
-  if (a->M == 0) return LOKA_OK;
+  return LOKA_OK;
+}
+
+loka::FwdLaunch fwd_launch(const loka_fwd_args* a, void* workspace) {
   loka::FwdLaunch f{};
   f.M = a->M; f.N = a->N; f.K = a->K; f.x_mode = a->x_mode; f.eps = a->eps;
   f.x = a->x; f.qw = a->qw; f.sw = a->sw; f.bias = a->bias; f.gamma = a->gamma; f.beta = a->beta;
   f.y = a->y; f.z = a->z; f.mean = a->mean; f.rstd = a->rstd; f.qx_out = a->qx_out; f.sx_out = a->sx_out;
-  f.workspace = a->workspace;
+  f.workspace = workspace;
   f.x_scales = a->x_scales;
   f.y_codes = a->y_codes;
   f.y_scales = a->y_scales;
-  f.w_packed = packed;
-  f.blocknorm = blocknorm;
-  return hip_status(loka::launch_fwd(f, static_cast<hipStream_t>(stream)), "loka_gemm_fp8_ln");
+  f.w_packed = (a->flags & LOKA_FWD_W_PACKED) != 0;
+  f.blocknorm = (a->flags & LOKA_FWD_BLOCKNORM_HSWISH) != 0;
+  return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+loka_status loka_gemm_fp8_ln(const loka_fwd_args* a, void* stream) {
+  loka_status st = validate_fwd(a);
+  if (st != LOKA_OK) return st;
+  if ((st = check_workspace(loka_gemm_fp8_ln_workspace_size(a), a->workspace, a->workspace_bytes)) != LOKA_OK) return st;
+  if (a->M == 0) return LOKA_OK;
+  return hip_status(loka::launch_fwd(fwd_launch(a, a->workspace), static_cast<hipStream_t>(stream)),
+                    "loka_gemm_fp8_ln");
+}
+
+loka_status loka_gemm_fp8_ln_noalloc(const loka_fwd_args* a, void* stream) {
+  loka_status st = validate_fwd(a);
+  if (st != LOKA_OK) return st;
+  const size_t need = loka_gemm_fp8_ln_workspace_size(a);
+  REQUIRE(need <= loka::noalloc_scratch_bytes(), LOKA_ERR_UNSUPPORTED,
+          "this call needs %zu bytes of scratch; loka_gemm_fp8_ln_noalloc holds %zu (use loka_gemm_fp8_ln with a "
+          "workspace, or LOKA_FWD_W_PACKED)",
+          need, loka::noalloc_scratch_bytes());
+  if (a->M == 0) return LOKA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void* scratch = nullptr;
+  hipError_t e = loka::noalloc_scratch(s, &scratch);
+  if (e != hipSuccess) return hip_status(e, "loka_gemm_fp8_ln_noalloc (device scratch)");
+  return hip_status(loka::launch_fwd(fwd_launch(a, scratch), s), "loka_gemm_fp8_ln_noalloc");
 }
 
 // ---------------------------------------------------------------------------

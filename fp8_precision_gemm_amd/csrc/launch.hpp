@@ -83,6 +83,9 @@ hipError_t launch_relayout(const uint8_t* src, int64_t R, int64_t C, uint8_t* ds
 hipError_t launch_relayout2(const uint8_t* src1, int64_t R1, int64_t C1, uint8_t* dst1, const uint8_t* src2,
                             int64_t R2, int64_t C2, uint8_t* dst2, hipStream_t s);
 hipError_t launch_fwd(const FwdLaunch& a, hipStream_t s);
+// the allocation-free forward's device scratch (fwd_noalloc.hip)
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(hipStream_t s, void** ptr);
 
 // ---- backward ------------------------------------------------------------
 struct BwdLaunch {

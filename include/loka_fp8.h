@@ -242,6 +242,30 @@ size_t loka_gemm_fp8_ln_workspace_size(const loka_fwd_args* args);
 loka_status loka_gemm_fp8_ln(const loka_fwd_args* args, void* stream);
 
 /* ------------------------------------------------------------------------
+ * loka_gemm_fp8_ln_noalloc: loka_gemm_fp8_ln for callers that cannot
+ * allocate device memory -- code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The same arguments and results
+ * (the same kernels, bit-identical outputs), except that `workspace` and
+ * `workspace_bytes` are ignored: the workspace lives in a fixed device
+ * array of LOKA_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ * held until the process ends.  Neither the call nor the library allocates
+ * or frees device memory.
+ *   - A call whose loka_gemm_fp8_ln_workspace_size() exceeds
+ *     LOKA_NOALLOC_SCRATCH_BYTES returns LOKA_ERR_UNSUPPORTED (every
+ *     LayerNorm-epilogue shape fits; a row-major weight for BlockNorm with
+ *     N * K above about 1 MiB does not -- pass LOKA_FWD_W_PACKED).
+ *   - Every call on one GPU shares that GPU's array: calls that overlap in
+ *     time on one GPU (other streams, other host threads) race and must be
+ *     serialized by the caller.  No state carries from one call to the next.
+ *   - The first call on a device looks the array's device address up
+ *     (hipGetSymbolAddress) with that device current; make it before any
+ *     graph capture.  `stream` must belong to the current device
+ *     (LOKA_ERR_HIP otherwise).
+ * ---------------------------------------------------------------------- */
+#define LOKA_NOALLOC_SCRATCH_BYTES (1u << 20)
+loka_status loka_gemm_fp8_ln_noalloc(const loka_fwd_args* args, void* stream);
+
+/* ------------------------------------------------------------------------
  * loka_gemm_fp8_bwd: the backward of loka_gemm_fp8_ln (x_mode ROW).
  *
  * Source: LoKA section III-C (Trainer Integration: a custom autograd

@@ -109,6 +109,31 @@ def test_forward_validation(lib, kw, status):
     assert lib.loka_last_error().decode()
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=100), 2), (dict(M=-1), 1), (dict(x_mode=9), 1), (dict(flags=4), 1), (dict(x=None), 1),
+    (dict(x=FAKE + 8), 3), (dict(eps=float("nan")), 1), (dict(flags=2, gamma=FAKE), 1),
+    # a valid call whose workspace would exceed the fixed scratch: the row-major weight of a
+    # 4096 x 512 BlockNorm needs 2 MiB rearranged
+    (dict(flags=2, N=4096, K=512), 2),
+])
+def test_noalloc_validation(lib, kw, status):
+    """The allocation-free forward validates exactly as loka_gemm_fp8_ln, then
+    refuses calls whose workspace exceeds its fixed scratch (before any HIP
+    call), and ignores the workspace fields."""
+    a = _fwd(**kw)
+    a.workspace, a.workspace_bytes = FAKE, 1 << 30
+    assert _call(lib, "loka_gemm_fp8_ln_noalloc", a) == status
+    msg = lib.loka_last_error().decode()
+    assert msg
+    if kw.get("N") == 4096:
+        assert "scratch" in msg and str(1 << 20) in msg
+        assert lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(a)) > (1 << 20)
+
+
+def test_noalloc_empty_batch_is_a_noop(lib):
+    assert _call(lib, "loka_gemm_fp8_ln_noalloc", _fwd(M=0, x=None, qw=None, sw=None, y=None)) == 0
+
+
 def test_forward_empty_batch_is_a_noop(lib):
     assert _call(lib, "loka_gemm_fp8_ln", _fwd(M=0, x=None, qw=None, sw=None, y=None)) == 0
 
