@@ -58,11 +58,52 @@ __global__ __launch_bounds__(kThreads) void k_fwd_res(FwdBlock p, const float* p
   blk.run();
 }
 
+// The staged weight-resident forward: the workgroup's whole tile range (at
+// most kXlTiles tiles) in one batch (ResBlock::run_xl).
+template <int MODE, int NT, int KC, bool OPT, bool EXACT>
+__global__ __launch_bounds__(kThreads) void k_fwd_xl(FwdBlock p, const float* partials, int np) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  if (MODE == 0) {
+    __shared__ float red8[kWaves];
+    ScalePair sp = np < 0 ? tensor_scale_self(p, red8) : reduce_tensor_scale<0>(partials, np, red8);
+    p.x_r = sp.r;
+    p.x_s = sp.s;
+  }
+  const int64_t T = (p.M + kResRows - 1) / kResRows, G = gridDim.x, b = blockIdx.x;
+  ResBlock<MODE, NT, KC, OPT, true, 0, true> blk(p, b * T / G, (b + 1) * T / G, smem);
+  blk.xl_layout(smem);
+  blk.template run_xl<EXACT>();
+}
+
+// Does the staged variant take this call?  Guard-free shapes (N = 128 NT,
+// K = 256 KQ, M % 16 == 0) of the row-quantizing recipes with K <= 512, at
+// most kXlTiles tiles per workgroup, no square-block Y output, and its LDS
+// layout within the compute unit's 160 KiB.
+inline bool xl_takes(const FwdBlock& p, int mode, int nt, int kc, int grid) {
+  if (mode == 4 || kc > 4 || p.y_codes != nullptr || !res_full(p.M, p.N, p.K, nt, kc)) return false;
+  const int64_t T = (p.M + kResRows - 1) / kResRows;
+  if ((T + grid - 1) / grid > kXlTiles) return false;
+  return xl_lds(nt, kc, p.N, p.K).total <= 160 * 1024;
+}
+
 template <int MODE, int NT, int KC>
 hipError_t launch_res_t(const FwdBlock& p, const float* partials, int np, int grid, hipStream_t s) {
-  const size_t lds = (size_t)res_lds(NT, KC, p.N).total;
   const bool opt = p.z != nullptr || p.mean != nullptr || p.rstd != nullptr || p.qx_out != nullptr ||
                    p.sx_out != nullptr || p.y_codes != nullptr;
+  if constexpr (MODE != 4 && KC <= 4) {
+    if (xl_takes(p, MODE, NT, KC, grid)) {
+      const size_t lds = (size_t)xl_lds(NT, KC, p.N, p.K).total;
+      const bool exact = ((p.M + kResRows - 1) / kResRows) == (int64_t)grid * kXlTiles;
+      auto kern = opt ? (exact ? k_fwd_xl<MODE, NT, KC, true, true> : k_fwd_xl<MODE, NT, KC, true, false>)
+                      : (exact ? k_fwd_xl<MODE, NT, KC, false, true> : k_fwd_xl<MODE, NT, KC, false, false>);
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, s, p, partials, np);
+      return hipGetLastError();
+    }
+  }
+  const size_t lds = (size_t)res_lds(NT, KC, p.N).total;
   const bool full = res_full(p.M, p.N, p.K, NT, KC);
   auto kern = opt ? (full ? k_fwd_res<MODE, NT, KC, true, true> : k_fwd_res<MODE, NT, KC, true, false>)
                   : (full ? k_fwd_res<MODE, NT, KC, false, true> : k_fwd_res<MODE, NT, KC, false, false>);

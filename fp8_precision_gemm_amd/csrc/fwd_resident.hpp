@@ -132,6 +132,30 @@ __host__ __device__ inline ResLds res_lds(int nt, int kc, int N) {
   return l;
 }
 
+// Staged variant (all of a workgroup's tiles at once, at most kXlTiles):
+//   xraw [kXlTiles][16][2K] (the bf16 X rows, as loaded) | codes
+//   [kXlTiles][16][LDX] | xe8 [kXlTiles][16][XE] | rs [kXlTiles][16] f32 |
+//   red [kXlTiles][16][kRedRow] float2 | cvec [4][N] f32 | wmx [32] f32 |
+//   ystg [8][16][32*NT + 16]
+constexpr int kXlTiles = 4;
+struct XlLds {
+  int xraw, codes, xe8, rs, red, cvec, wmx, ystg, total;
+};
+__host__ __device__ inline XlLds xl_lds(int nt, int kc, int N, int K) {
+  const int ldx = kc * 128 + 16, xe = 16 * ((kc + 3) / 4);
+  XlLds l;
+  l.xraw = 0;
+  l.codes = l.xraw + kXlTiles * kResRows * 2 * K;
+  l.xe8 = l.codes + kXlTiles * kResRows * ldx;
+  l.rs = l.xe8 + ((kXlTiles * kResRows * xe + 15) / 16) * 16;
+  l.red = l.rs + kXlTiles * kResRows * 4;
+  l.cvec = l.red + kXlTiles * kResRows * kRedRow * 8;
+  l.wmx = l.cvec + 4 * N * 4;
+  l.ystg = l.wmx + 32 * 4;
+  l.total = l.ystg + kWaves * kResRows * res_yst(nt);
+  return l;
+}
+
 // Max over each 32-lane half of the wavefront, returned in every lane of
 // that half: quads and rows of 16 by DPP, then the two rows of a half
 // exchanged by v_permlane16_swap.  Non-negative values only.
@@ -208,7 +232,10 @@ constexpr int kBlockNorm = 256;
 // MODE: 0 tensor, 1 row, 3 MX32 along K (X quantized here), 4 MX32 square
 // blocks (X given as e4m3 codes with E8M0 scales per 32 x 32 block; the
 // weight's scales per 32 x 32 block of W[K][N]).
-template <int MODE, int NT, int KC, bool OPT, bool FULL, int EPI = 0>
+// XL: the staged run (run_xl): the workgroup's whole tile range (at most
+// kXlTiles tiles, FULL shapes, LayerNorm) is loaded, quantized, multiplied
+// and normalized as one batch.
+template <int MODE, int NT, int KC, bool OPT, bool FULL, int EPI = 0, bool XL = false>
 struct ResBlock {
   using R = Res<NT, KC>;
   static constexpr bool MX = MODE >= 3;  // E8M0 block scales inside the MFMA
@@ -217,7 +244,7 @@ struct ResBlock {
   // sequential steps, guard-free shape, LayerNorm, no optional outputs: Y
   // leaves as whole rows after the next barrier (two staging buffers by tile
   // parity), so no 128-byte line is written in parts by two wavefronts
-  static constexpr bool COOP = FULL && !OPT && !PIPE && EPI == 0;
+  static constexpr bool COOP = FULL && !OPT && !PIPE && EPI == 0 && !XL;
 
   const FwdBlock& p;
   int64_t tb, te;  // tile range [tb, te)
@@ -241,6 +268,8 @@ struct ResBlock {
   // two accumulator sets: the GEMM of tile j fills one while the epilogue
   // of tile j-1 reads the other
   v4f acc0[NT], acc1[NT];
+  // the staged run: the bf16 X rows in LDS
+  uint8_t* xraw;
   float cs0, cs1;   // per set: this lane's row rescale factor (power of two, 1 for ordinary rows)
   // set-up values in flight: this thread's column (tid < N) and the MX scale bytes
   float cv_sw;
@@ -432,11 +461,12 @@ struct ResBlock {
   // registers (fragment-interleaved W^T: lane l reads bytes 16l of both
   // 1 KiB halves of each 2 KiB block; chunks in the order the GEMM uses
   // them) and the MX scale bytes.  Nothing here waits for a load.
+  template <int C0 = 0, int C1 = KC>
   __device__ __forceinline__ void request_weights() {
     const int64_t nch = (K + 127) >> 7;
     const uint8_t* base = p.qw + (int64_t)(wave * NT) * nch * 2048 + lane * 16;
 #pragma unroll
-    for (int c = 0; c < KC; ++c) {
+    for (int c = C0; c < C1; ++c) {
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         uint4 a = make_uint4(0, 0, 0, 0), b = make_uint4(0, 0, 0, 0);
@@ -451,7 +481,7 @@ struct ResBlock {
         wf[t][c] = f;
       }
     }
-    if (MX) {
+    if (MX && C0 == 0) {
       // MODE 3: W's scales [N][K/32] (32 consecutive k of column col);
       // MODE 4: [K/32][N/32] (32 x 32 blocks of W[K][N])
       const uint8_t* sw8 = static_cast<const uint8_t*>(p.sw);
@@ -649,7 +679,8 @@ struct ResBlock {
     // swaps: one LDS read per lane and a quarter of the combine each.
     const float4 u = reinterpret_cast<const float4*>(red + (buf * kResRows + r) * kRedRow)[g];
     const float S = sum4(u.x + u.z);
-    const float invn = 1.0f / (float)N;
+    // guard-free shapes: N = 128 NT, a compile-time reciprocal (exact: a power of two for NT = 1, 2, 4)
+    const float invn = FULL ? 1.0f / (float)(128 * NT) : 1.0f / (float)N;
     const float mean = S * invn;
     // within-slice centred sums plus the between-slice term
     // (s_w - n_w mean)^2 / n_w, the deviations scaled by cs like the
@@ -814,15 +845,16 @@ struct ResBlock {
     // order, so the reads see the writes above and the next tile's writes
     // come after them.
     constexpr int CPR = 2 * NT, TOT = kResRows * CPR;  // 16-byte pieces per row / per block
+    // the tile's first row of Y (wave-uniform); each piece's offset from it fits 32 bits
+    uint16_t* ytile = p.y + t * kResRows * ldy + c0;
 #pragma unroll
     for (int i = 0; i < (TOT + 63) / 64; ++i) {
       const int u = lane + 64 * i;
       if (TOT % 64 == 0 || u < TOT) {
         const int row = u / CPR, ch = u - row * CPR;
         const uint4 v = *reinterpret_cast<const uint4*>(ystg + row * YST + ch * 16);
-        const int64_t mm = t * kResRows + row;
-        if (FULL || (mm < p.M && ch < 2 * nv))
-          __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p.y + mm * ldy + c0 + ch * 8));
+        if (FULL || (t * kResRows + row < p.M && ch < 2 * nv))
+          __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(ytile + (row * ldy + ch * 8)));
       }
     }
   }
@@ -891,6 +923,148 @@ struct ResBlock {
     __syncthreads();
     if (COOP && j > 0) coop_store(t - 1);
     epilogue_out(buf, t, acc0, cs0);
+  }
+
+  // ---- the staged run ----------------------------------------------------
+  // LDS pointers of the staged layout (replacing the constructor's)
+  __device__ __forceinline__ void xl_layout(uint8_t* smem) {
+    const XlLds l = xl_lds(NT, KC, N, K);
+    xraw = smem + l.xraw;
+    codes = smem + l.codes;
+    xe8 = smem + l.xe8;
+    rs = reinterpret_cast<float*>(smem + l.rs);
+    red = reinterpret_cast<float2*>(smem + l.red);
+    cvec = reinterpret_cast<float*>(smem + l.cvec);
+    wmx = reinterpret_cast<float*>(smem + l.wmx);
+    ystg = smem + l.ystg + wave * (kResRows * res_yst(NT));
+  }
+
+  // This wavefront's two rows (2w, 2w+1) of tile slots [I0, I1) of the
+  // batch, straight from HBM into LDS (buffer loads with the LDS destination: lane
+  // l's 16 bytes land at the wave-uniform LDS address + 16 l, so each
+  // instruction moves 1 KiB of contiguous X).  The two rows are 4K
+  // contiguous bytes in X and in LDS (row stride 2K), so a tile takes
+  // K/256 = KQ instructions.  The buffer covers exactly the batch's rows;
+  // slots past the batch read zeros.  Slots are requested with no branch,
+  // so the compiler keeps them where they stand in the issue order (loads
+  // complete in issue order: a tile requested after the weight waits for
+  // it).
+  template <int I0, int I1>
+  __device__ __forceinline__ void xl_request_x() {
+    const int64_t row0 = tb * kResRows;
+    const int bytes = (int)((min(te * kResRows, p.M) - row0) * K * 2);
+    const __amdgpu_buffer_rsrc_t rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x + row0 * K), (short)0, bytes, kBufferWord3);
+#pragma unroll
+    for (int i = I0; i < I1; ++i) {
+#pragma unroll
+      for (int part = 0; part < KQ; ++part) {
+        const uint32_t off = (uint32_t)((i * kResRows + 2 * wave) * 2 * K + part * 1024);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(xraw + off), 16,
+                                                 off + 16u * (uint32_t)lane, 0, 0, 0);
+      }
+    }
+  }
+
+  // this lane's share of its row of tile i, from LDS into register slot 0
+  // (the same elements load_x would fetch: 256q + 8 hl .. +8)
+  __device__ __forceinline__ void xl_fetch(int i) {
+    const uint8_t* row = xraw + (i * kResRows + hrow) * 2 * K;
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) xr[0][q] = *reinterpret_cast<const uint4*>(row + q * 512 + hl * 16);
+  }
+
+  // GEMM of batch tiles I0 and I0+1 into `acc`, K chunk outermost: chunk c of
+  // the weight serves both tiles as soon as it has arrived (its loads were
+  // issued chunk by chunk), so the MFMAs follow the weight as it lands.
+  template <int I0>
+  __device__ __forceinline__ void xl_mma2(v4f (&acc)[2][NT]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[i][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int c = 0; c < KC; ++c) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint8_t* brow = codes + ((I0 + i) * kResRows + r) * LDX + 16 * g + c * 128;
+        const uint4 a = *reinterpret_cast<const uint4*>(brow);
+        const uint4 b = *reinterpret_cast<const uint4*>(brow + 64);
+        v8i xf;
+        xf[0] = (int)a.x; xf[1] = (int)a.y; xf[2] = (int)a.z; xf[3] = (int)a.w;
+        xf[4] = (int)b.x; xf[5] = (int)b.y; xf[6] = (int)b.z; xf[7] = (int)b.w;
+        uint32_t xsw = 0;
+        if (MX) xsw = reinterpret_cast<const uint32_t*>(xe8 + ((I0 + i) * kResRows + r) * XE + g * (4 * KP))[c >> 2];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          if (MX)
+            acc[i][t] = mfma_mx_sel(c & 3, wf[t][c], xf, acc[i][t], wsc[t][c >> 2], xsw);
+          else
+            acc[i][t] = mfma_fp8<0, 0>(wf[t][c], xf, acc[i][t]);
+        }
+      }
+    }
+  }
+
+  // The staged run, in two halves of two tiles.  Order of requests: X tiles
+  // 0-1 (HBM, into LDS), the column vectors, then the weight chunk by chunk
+  // with tile 0's and tile 1's quantization between the chunks (a wavefront
+  // stalls once its memory requests fill the queue, so its quantization work
+  // goes between them), then X tiles 2-3.  One barrier, and tiles 0-1 are
+  // multiplied chunk by chunk as the weight lands; their row statistics; a
+  // barrier; tiles 2-3 quantized alongside the normalization and stores of
+  // tiles 0-1; a barrier; tiles 2-3 multiplied; their statistics; a
+  // barrier; their normalization and stores.
+  // EXACT: every workgroup has exactly kXlTiles tiles (the tile count is a
+  // multiple of the grid), so no tile is guarded and the compiler may
+  // interleave the independent work of two tiles.
+  template <bool EXACT>
+  __device__ __forceinline__ void run_xl() {
+    const int nt = EXACT ? kXlTiles : (int)(te - tb);
+    if (nt <= 0) return;
+    if (OPT && MODE == 0 && p.sx_out != nullptr && tb == 0 && tid == 0) static_cast<float*>(p.sx_out)[0] = p.x_s;
+    static_assert(kXlTiles == 4 && KC >= 2, "the staged run covers four tiles in two halves");
+    constexpr int KH = KC / 2;
+    xl_request_x<0, 2>();
+    request_vectors();
+    request_weights<0, KH>();
+    __builtin_amdgcn_sched_barrier(0);
+    xl_fetch(0);
+    quantize<0>(tb, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    request_weights<KH, KC>();
+    __builtin_amdgcn_sched_barrier(0);
+    xl_fetch(1);
+    quantize<0>(tb + 1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    xl_request_x<2, 4>();
+    stage_vectors();
+    __syncthreads();
+    read_bounds();
+    v4f accA[2][NT], accB[2][NT];
+    float csA[2], csB[2];
+    xl_mma2<0>(accA);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      if (i < nt) epilogue_stats(i, accA[i], csA[i]);
+    __syncthreads();
+    xl_fetch(2);
+    quantize<0>(tb + 2, 2);
+    if (0 < nt) epilogue_out(0, tb, accA[0], csA[0]);
+    xl_fetch(3);
+    quantize<0>(tb + 3, 3);
+    if (1 < nt) epilogue_out(1, tb + 1, accA[1], csA[1]);
+    __syncthreads();
+    if (nt > 2) {
+      xl_mma2<2>(accB);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (2 + i < nt) epilogue_stats(2 + i, accB[i], csB[i]);
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (2 + i < nt) epilogue_out(2 + i, tb + 2 + i, accB[i], csB[i]);
+    }
   }
 
   __device__ __forceinline__ void run() {
