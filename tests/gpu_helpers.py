@@ -96,3 +96,16 @@ def sample_rows(M, n, seed=0):
     tail = np.arange(max(0, M - 64), M)
     mid = rng.choice(M, size=min(n, M), replace=False)
     return np.unique(np.concatenate([head, tail, mid]))
+
+
+def oracle_forward_blocks(forward_fn, x_bits, *args, rows_per_block=4096, **kw):
+    """The oracle forward of every row of X, taken in blocks of rows (rows are
+    independent under the rowwise and MX recipes, so the result is the same
+    as one call on all rows): the per-row outputs concatenated, the weight's
+    codes and scales from the first block."""
+    M = x_bits.shape[0]
+    parts = [forward_fn(x_bits[lo:lo + rows_per_block], *args, **kw) for lo in range(0, M, rows_per_block)]
+    out = dict(parts[0])
+    for k in ("y_bits", "y", "z", "mean", "rstd", "qx", "sx"):
+        out[k] = np.concatenate([p[k] for p in parts])
+    return out

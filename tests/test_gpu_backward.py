@@ -4,12 +4,14 @@
 Literal reading (dY is dZ, no LayerNorm): dZ is an exact input, so the e5m2
 codes and scales are bit-exact and dX, dW, dbias are checked to tolerance.
 
-LayerNorm reading: the kernel computes dZ in fp32 and the oracle in fp64, so
-an e5m2 code whose exact value sits within the fp32 error of a rounding
-midpoint may legitimately round either way.  The check compares what is
-unique -- every code away from a midpoint must match -- and bounds dX and dW
-by the tolerance plus, for each possibly-flipped code, one e5m2 spacing
-times its weight (all bounds computed from oracle data only).
+LayerNorm reading: the kernel computes dZ in fp32 and the oracle in fp64.
+The e5m2 codes and scales must equal, bit for bit, the oracle quantizer run
+on the kernel's own fp32 dZ (which the kernel writes).  Against the fp64 dZ,
+a code whose exact value sits within the fp32 error of a rounding midpoint
+may legitimately round either way: that comparison checks what is unique --
+every code away from a midpoint must match -- and bounds dX and dW by the
+tolerance plus, for each possibly-flipped code, one e5m2 spacing times its
+weight (all bounds computed from oracle data only).
 
 Tolerances:
   dZ (fp32):  |dz - dz_ref| <= TAU * max(|dz_ref|, rms_row(dz_ref)), TAU = 1e-3
@@ -140,7 +142,13 @@ def test_layernorm_reading(lib, M, K, N):
     dz_err = np.abs(g["dz"].astype(np.float64) - dz_ref)
     assert np.all(dz_err <= dz_tol), f"dZ: worst {np.max(dz_err / dz_tol):.3f} x tol"
 
-    # row (dgrad) codes: unique away from midpoints
+    # the dgrad operand is the quantization of the kernel's own fp32 dZ: the
+    # oracle quantizer on that dZ must give the same codes and scales, bit for bit
+    q_own, s_own = quant.quantize(g["dz"].astype(np.float64), quant.ROW, E5)
+    np.testing.assert_array_equal(g["dz_codes"], q_own)
+    np.testing.assert_array_equal(g["dz_scales"].view(np.uint32), s_own.astype(np.float32).view(np.uint32))
+
+    # against the fp64 dZ: codes unique away from midpoints
     s_ref = o["s_dz"].astype(np.float64)
     np.testing.assert_allclose(g["dz_scales"], s_ref, rtol=2 * TAU)
     t_ref = dz_ref / s_ref[:, None]

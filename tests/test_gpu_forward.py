@@ -2,9 +2,10 @@
 
 Full-size cases use the three forward workloads (tensor recipe 512x256x256,
 rowwise 16384x512x512 on outlier activations, MX 65536x1024x256 on
-log-normal rows) in the launch configuration the benchmark times; the
-oracle computes sampled rows there (rows are independent under the row and
-MX recipes; the tensor case is small enough to check whole).  Smaller cases
+log-normal rows) in the launch configuration the benchmark times, and every
+row is checked: X codes and scales bit for bit, Z, Y, mean and rstd (the
+oracle takes the rows in blocks, which changes nothing: rows are independent
+under the row and MX recipes).  Smaller cases
 span several tiles with ragged M, K not a multiple of 128, No-Bias and
 default gamma/beta, and degenerate rows."""
 
@@ -14,7 +15,7 @@ import torch
 
 from oracle import codec, forward, quant
 from synth.workloads import forward_case, mx_case, outlier_case, tensor_case, to_bf16_bits
-from tests.gpu_helpers import bf16_dev, check_y, check_z, host, row_sigma, sample_rows
+from tests.gpu_helpers import bf16_dev, check_y, check_z, host, oracle_forward_blocks, row_sigma
 
 pytestmark = pytest.mark.gpu
 
@@ -89,17 +90,17 @@ def test_tensor_recipe_full(lib):
 def test_rowwise_outliers_full_size(lib):
     c = outlier_case()
     g = run_gpu(lib, c, "row", packed=True)
-    rows = sample_rows(c["M"], 1024)
-    o = oracle_rows(c, "row", rows)
-    compare(g, o, rows, "row", "row 16384x512x512")
+    o = oracle_forward_blocks(forward.gemm_ln_forward, c["x"], c["w"], c["bias"], c["gamma"], c["beta"],
+                              recipe="row")
+    compare(g, o, None, "row", "row 16384x512x512 (every row)")
 
 
 def test_mx_full_size(lib):
     c = mx_case()
     g = run_gpu(lib, c, "mx32_row", packed=True)
-    rows = sample_rows(c["M"], 512)
-    o = oracle_rows(c, "mx32_row", rows)
-    compare(g, o, rows, "mx32_row", "mx 65536x1024x256")
+    o = oracle_forward_blocks(forward.gemm_ln_forward, c["x"], c["w"], c["bias"], c["gamma"], c["beta"],
+                              recipe="mx32")
+    compare(g, o, None, "mx32_row", "mx 65536x1024x256 (every row)")
 
 
 @pytest.mark.parametrize("x_mode", ["tensor", "row", "mx32_row"])

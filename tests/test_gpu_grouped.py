@@ -1,7 +1,9 @@
 """loka_grouped_gemm_fp8_ln on the GPU: the 64-group wide-ensemble workload
-in one launch.  Every group is checked against the oracle on sampled rows,
-and the grouped outputs must equal single loka_gemm_fp8_ln calls bit for
-bit (same kernel body, same arithmetic order)."""
+in one launch.  Every row of every group is checked against the oracle (Z
+and Y), and every group's outputs must equal a single loka_gemm_fp8_ln call
+bit for bit (same kernel body, same arithmetic order), whose X codes and
+scales are checked bit for bit against the oracle's: the grouped entry
+point has no codes output of its own."""
 
 import numpy as np
 import pytest
@@ -9,7 +11,7 @@ import torch
 
 from oracle import forward
 from synth.workloads import forward_case, grouped_case, to_bf16_bits
-from tests.gpu_helpers import bf16_dev, check_y, check_z, host, row_sigma, sample_rows
+from tests.gpu_helpers import bf16_dev, check_y, check_z, host, row_sigma
 
 pytestmark = pytest.mark.gpu
 
@@ -30,19 +32,25 @@ def test_grouped_full_workload(lib):
     torch.cuda.synchronize()
     worst = 0.0
     for i, (g, o) in enumerate(zip(groups, outs)):
-        rows = sample_rows(g["M"], 96, seed=i)
-        ref = forward.gemm_ln_forward(g["x"][rows], g["w"], g["bias"], g["gamma"], g["beta"])
-        ez = check_z(host(o["z"])[rows], ref["z"], row_sigma(ref["z"]), f"group {i} (K={g['K']}, N={g['N']})")
-        check_y(host(o["y"])[rows], ref["y"], f"group {i}")
+        ref = forward.gemm_ln_forward(g["x"], g["w"], g["bias"], g["gamma"], g["beta"])
+        label = f"group {i} (K={g['K']}, N={g['N']})"
+        ez = check_z(host(o["z"]), ref["z"], row_sigma(ref["z"]), label)
+        check_y(host(o["y"]), ref["y"], label)
         worst = max(worst, ez)
-    print(f"grouped: 64 groups, worst Z err {worst:.2e}")
-    # bitwise equal to single calls
-    for i in (0, 1, 17, 63):
+        # the same group as a single call: bitwise equal, and its X codes and scales the oracle's
         d = dg[i]
-        s = lib.loka_gemm_fp8_ln(d["x"], d["qw"], d["sw"], d["bias"], d["gamma"], d["beta"], want_z=True)
+        s = lib.loka_gemm_fp8_ln(d["x"], d["qw"], d["sw"], d["bias"], d["gamma"], d["beta"], want_z=True,
+                                 want_qx=True)
         torch.cuda.synchronize()
-        np.testing.assert_array_equal(host(s["y"]), host(outs[i]["y"]))
-        np.testing.assert_array_equal(host(s["z"]), host(outs[i]["z"]))
+        np.testing.assert_array_equal(host(s["y"]), host(o["y"]), err_msg=label)
+        np.testing.assert_array_equal(host(s["z"]), host(o["z"]), err_msg=label)
+        np.testing.assert_array_equal(host(s["qx"]), ref["qx"], err_msg=f"{label}: X codes")
+        np.testing.assert_array_equal(host(s["sx"]).view(np.uint32), ref["sx"].astype(np.float32).view(np.uint32),
+                                      err_msg=f"{label}: X scales")
+        np.testing.assert_array_equal(host(d["qw"]).T, ref["qw"], err_msg=f"{label}: W codes")
+        np.testing.assert_array_equal(host(d["sw"]).view(np.uint32), ref["sw"].astype(np.float32).view(np.uint32),
+                                      err_msg=f"{label}: W scales")
+    print(f"grouped: 64 groups, every row, worst Z err {worst:.2e}")
 
 
 def test_grouped_ragged_and_empty_groups(lib):
@@ -122,9 +130,8 @@ def test_grouped_y_only(lib):
     torch.cuda.synchronize()
     assert all("z" not in o for o in outs)
     for i, (g, o) in enumerate(zip(groups, outs)):
-        rows = sample_rows(g["M"], 64, seed=i)
-        ref = forward.gemm_ln_forward(g["x"][rows], g["w"], g["bias"], g["gamma"], g["beta"])
-        check_y(host(o["y"])[rows], ref["y"], f"group {i} (K={g['K']}, N={g['N']})")
+        ref = forward.gemm_ln_forward(g["x"], g["w"], g["bias"], g["gamma"], g["beta"])
+        check_y(host(o["y"]), ref["y"], f"group {i} (K={g['K']}, N={g['N']})")
     _bitwise_like_single(lib, dg, outs, range(len(groups)))
 
 

@@ -177,7 +177,14 @@ def test_square_backward_layernorm(lib, M, K, N):
     dz_err = np.abs(g["dz"].astype(np.float64) - dz_ref)
     assert np.all(dz_err <= dz_tol), f"dZ: worst {np.max(dz_err / dz_tol):.3f} x tol"
 
-    # block scales: unique unless the block max-abs is within the dZ error of a power of two
+    # the kernel's own fp32 dZ, quantized by the oracle in 32 x 32 blocks: the
+    # same codes and scales, bit for bit
+    q_own, s_own = quant.quantize(g["dz"].astype(np.float64), quant.MX32_SQ, E5)
+    np.testing.assert_array_equal(g["dz_codes"], q_own)
+    np.testing.assert_array_equal(g["dz_scales"], s_own)
+
+    # against the fp64 dZ: block scales unique unless the block max-abs is
+    # within the dZ error of a power of two
     am = quant.amax(dz_ref, quant.MX32_SQ)
     am_tol = quant.amax(dz_tol, quant.MX32_SQ)
     lo, hi = np.floor(np.log2(np.maximum(am - am_tol, 1e-300))), np.floor(np.log2(am + am_tol))
