@@ -614,14 +614,47 @@ struct ResBlock {
     }
   }
 
+  // This lane's per-column constants (its 4 columns of each of the NT tiles):
+  // s_w and bias for the statistics, gamma and beta for the output.  The
+  // pipelined run reads them from LDS at every tile; the staged run holds
+  // them in the registers the weight leaves free after its GEMM.
+  struct ColSB {
+    float4 sw[NT], b[NT];
+  };
+  struct ColGB {
+    float4 g[NT], be[NT];
+  };
+  __device__ __forceinline__ ColSB col_sb() const {
+    ColSB v;
+    const float* cb = cvec + c0 + 4 * g;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      v.sw[t] = tv(t) ? *reinterpret_cast<const float4*>(cb + 16 * t) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      v.b[t] = tv(t) ? *reinterpret_cast<const float4*>(cb + N + 16 * t) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    return v;
+  }
+  __device__ __forceinline__ ColGB col_gb() const {
+    ColGB v;
+    const float* cb = cvec + 2 * N + c0 + 4 * g;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      v.g[t] = tv(t) ? *reinterpret_cast<const float4*>(cb + 16 * t) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      v.be[t] = tv(t) ? *reinterpret_cast<const float4*>(cb + N + 16 * t) : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+    return v;
+  }
+
   // ---- epilogue, part 1: z = dequant(acc) + b in place; this slice's row
   // sum and centred sum of squares to LDS
   __device__ __forceinline__ void epilogue_stats(int buf, v4f (&acc)[NT], float& cs) {
+    epilogue_stats(buf, acc, cs, col_sb());
+  }
+  __device__ __forceinline__ void epilogue_stats(int buf, v4f (&acc)[NT], float& cs, const ColSB& cv) {
     const float rsv = rs[buf * kResRows + r];
     const float sx = MODE == 1 ? rsv : (MODE == 0 ? p.x_s : 1.0f);
     const float bound = MX ? ldexpf(bw, (int)rsv - 127) + bb : sx * bw + bb;
     cs = row_rescale(bound);
-    const float* cb = cvec + c0 + 4 * g;
     // sums as short trees (per tile, then over the tiles) rather than one
     // long chain: the statistics sit on the step's critical path
     float st[NT];
@@ -629,8 +662,8 @@ struct ResBlock {
     for (int t = 0; t < NT; ++t) {
       st[t] = 0.0f;
       if (tv(t)) {
-        const float4 sw4 = *reinterpret_cast<const float4*>(cb + 16 * t);
-        const float4 b4 = *reinterpret_cast<const float4*>(cb + N + 16 * t);
+        const float4 sw4 = cv.sw[t];
+        const float4 b4 = cv.b[t];
         const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -670,6 +703,13 @@ struct ResBlock {
 
   // ---- epilogue, part 2 (after the barrier): combine the slices, normalize, store
   __device__ __forceinline__ void epilogue_out(int buf, int64_t t, const v4f (&acc)[NT], float cs) {
+    if constexpr (EPI == 1) {
+      blocknorm_out(buf, t, acc, cs);
+      return;
+    }
+    epilogue_out(buf, t, acc, cs, col_gb());
+  }
+  __device__ __forceinline__ void epilogue_out(int buf, int64_t t, const v4f (&acc)[NT], float cs, const ColGB& cv) {
     if constexpr (EPI == 1) {
       blocknorm_out(buf, t, acc, cs);
       return;
@@ -720,14 +760,13 @@ struct ResBlock {
     }
     const float nmr = -mean * rstd;
     const int cl = c0 + 4 * g;  // this lane's first column (tile t adds 16t)
-    const float* gb = cvec + 2 * N + cl;
     constexpr int YST = res_yst(NT);
     uint8_t* ys = COOP && (t & 1) ? ystg + kWaves * kResRows * YST : ystg;
 #pragma unroll
     for (int t2 = 0; t2 < NT; ++t2) {
       if (tv(t2)) {
-        const float4 ga = *reinterpret_cast<const float4*>(gb + 16 * t2);
-        const float4 be = *reinterpret_cast<const float4*>(gb + N + 16 * t2);
+        const float4 ga = cv.g[t2];
+        const float4 be = cv.be[t2];
         const float gv[4] = {ga.x, ga.y, ga.z, ga.w}, bv[4] = {be.x, be.y, be.z, be.w};
         float o[4];
 #pragma unroll
@@ -974,27 +1013,26 @@ struct ResBlock {
     for (int q = 0; q < KQ; ++q) xr[0][q] = *reinterpret_cast<const uint4*>(row + q * 512 + hl * 16);
   }
 
-  // GEMM of batch tiles I0 and I0+1 into `acc`, K chunk outermost: chunk c of
-  // the weight serves both tiles as soon as it has arrived (its loads were
-  // issued chunk by chunk), so the MFMAs follow the weight as it lands.
-  template <int I0>
-  __device__ __forceinline__ void xl_mma2(v4f (&acc)[2][NT]) {
+  // GEMM of the whole batch into `acc`, K chunk outermost: chunk c of the
+  // weight serves every tile as soon as it has arrived (its loads were issued
+  // chunk by chunk), so the MFMAs follow the weight as it lands.
+  __device__ __forceinline__ void xl_mma(v4f (&acc)[kXlTiles][NT]) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kXlTiles; ++i)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[i][t] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int c = 0; c < KC; ++c) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const uint8_t* brow = codes + ((I0 + i) * kResRows + r) * LDX + 16 * g + c * 128;
+      for (int i = 0; i < kXlTiles; ++i) {
+        const uint8_t* brow = codes + (i * kResRows + r) * LDX + 16 * g + c * 128;
         const uint4 a = *reinterpret_cast<const uint4*>(brow);
         const uint4 b = *reinterpret_cast<const uint4*>(brow + 64);
         v8i xf;
         xf[0] = (int)a.x; xf[1] = (int)a.y; xf[2] = (int)a.z; xf[3] = (int)a.w;
         xf[4] = (int)b.x; xf[5] = (int)b.y; xf[6] = (int)b.z; xf[7] = (int)b.w;
         uint32_t xsw = 0;
-        if (MX) xsw = reinterpret_cast<const uint32_t*>(xe8 + ((I0 + i) * kResRows + r) * XE + g * (4 * KP))[c >> 2];
+        if (MX) xsw = reinterpret_cast<const uint32_t*>(xe8 + (i * kResRows + r) * XE + g * (4 * KP))[c >> 2];
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
           if (MX)
@@ -1006,64 +1044,72 @@ struct ResBlock {
     }
   }
 
-  // The staged run, in two halves of two tiles.  Order of requests: X tiles
-  // 0-1 (HBM, into LDS), the column vectors, then the weight chunk by chunk
-  // with tile 0's and tile 1's quantization between the chunks (a wavefront
-  // stalls once its memory requests fill the queue, so its quantization work
-  // goes between them), then X tiles 2-3.  One barrier, and tiles 0-1 are
-  // multiplied chunk by chunk as the weight lands; their row statistics; a
-  // barrier; tiles 2-3 quantized alongside the normalization and stores of
-  // tiles 0-1; a barrier; tiles 2-3 multiplied; their statistics; a
-  // barrier; their normalization and stores.
-  // EXACT: every workgroup has exactly kXlTiles tiles (the tile count is a
-  // multiple of the grid), so no tile is guarded and the compiler may
-  // interleave the independent work of two tiles.
+  // weight chunks [c0, c1) of the KC, requested between the quantization of
+  // tile I and the next (the chunks spread evenly over the four tiles)
+  template <int I>
+  __device__ __forceinline__ void xl_weights_for() {
+    request_weights<(I * KC) / kXlTiles, ((I + 1) * KC) / kXlTiles>();
+  }
+  template <int I>
+  __device__ __forceinline__ void xl_quantize_tile() {
+    xl_fetch(I);
+    quantize<0>(tb + I, I);
+  }
+
+  // The staged run.  Order of requests: the whole batch's X (HBM, into LDS),
+  // then the column vectors, then the weight chunk by chunk with one tile's
+  // quantization after each part (a wavefront stalls once its memory
+  // requests fill the queue, so its quantization work goes between them, and
+  // every X tile was requested ahead of the weight).  One barrier; the GEMM
+  // of the whole batch, chunk by chunk; the row statistics of every tile;
+  // one barrier; normalization and stores.  At two wavefronts per SIMD the
+  // MFMAs and the VALU work take turns on a SIMD, so the phases are ordered
+  // by their dependencies rather than interleaved.
   template <bool EXACT>
   __device__ __forceinline__ void run_xl() {
     const int nt = EXACT ? kXlTiles : (int)(te - tb);
     if (nt <= 0) return;
     if (OPT && MODE == 0 && p.sx_out != nullptr && tb == 0 && tid == 0) static_cast<float*>(p.sx_out)[0] = p.x_s;
-    static_assert(kXlTiles == 4 && KC >= 2, "the staged run covers four tiles in two halves");
-    constexpr int KH = KC / 2;
-    xl_request_x<0, 2>();
+    static_assert(kXlTiles == 4, "the staged run covers four tiles");
+    xl_request_x<0, kXlTiles>();
     request_vectors();
-    request_weights<0, KH>();
     __builtin_amdgcn_sched_barrier(0);
-    xl_fetch(0);
-    quantize<0>(tb, 0);
+    xl_weights_for<0>();
     __builtin_amdgcn_sched_barrier(0);
-    request_weights<KH, KC>();
+    xl_quantize_tile<0>();
     __builtin_amdgcn_sched_barrier(0);
-    xl_fetch(1);
-    quantize<0>(tb + 1, 1);
+    xl_weights_for<1>();
     __builtin_amdgcn_sched_barrier(0);
-    xl_request_x<2, 4>();
+    xl_quantize_tile<1>();
+    __builtin_amdgcn_sched_barrier(0);
+    xl_weights_for<2>();
+    __builtin_amdgcn_sched_barrier(0);
+    xl_quantize_tile<2>();
+    __builtin_amdgcn_sched_barrier(0);
+    xl_weights_for<3>();
+    __builtin_amdgcn_sched_barrier(0);
+    xl_quantize_tile<3>();
     stage_vectors();
     __syncthreads();
     read_bounds();
-    v4f accA[2][NT], accB[2][NT];
-    float csA[2], csB[2];
-    xl_mma2<0>(accA);
+    v4f acc[kXlTiles][NT];
+    float cs[kXlTiles];
+    xl_mma(acc);
+    // the per-column constants once, into the registers the weight held
+    // (reading them from LDS at every tile made the epilogue LDS-bound);
+    // one tile's epilogue at a time
+    const ColSB sb = col_sb();
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      if (i < nt) epilogue_stats(i, accA[i], csA[i]);
+    for (int i = 0; i < kXlTiles; ++i) {
+      if (i < nt) epilogue_stats(i, acc[i], cs[i], sb);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const ColGB gbv = col_gb();
     __syncthreads();
-    xl_fetch(2);
-    quantize<0>(tb + 2, 2);
-    if (0 < nt) epilogue_out(0, tb, accA[0], csA[0]);
-    xl_fetch(3);
-    quantize<0>(tb + 3, 3);
-    if (1 < nt) epilogue_out(1, tb + 1, accA[1], csA[1]);
-    __syncthreads();
-    if (nt > 2) {
-      xl_mma2<2>(accB);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        if (2 + i < nt) epilogue_stats(2 + i, accB[i], csB[i]);
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        if (2 + i < nt) epilogue_out(2 + i, tb + 2 + i, accB[i], csB[i]);
+    for (int i = 0; i < kXlTiles; ++i) {
+      if (i < nt) epilogue_out(i, tb + i, acc[i], cs[i], gbv);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
