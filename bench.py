@@ -49,7 +49,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=500)
-    p.add_argument("--warmup", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=2000)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-oracle-report", action="store_true", help="skip the oracle's MERE report")
     p.add_argument("--no-rows", action="store_true", help="skip the other workloads")
@@ -88,43 +88,101 @@ def measured_traffic():
 
 BATCHES = 5          # timed batches; the reported time is their median
 MIN_BATCH = 100      # launches per batch, at least
+GRAPH_LAUNCHES = 64  # launches per captured graph, at least (a replay boundary costs ~8 us)
 
 
-def timed_graph(torch, launches, steps, warmup, stream):
-    """Capture `launches` (callables enqueuing on `stream`) into one graph and
-    time its replays: `warmup` launches untimed, then BATCHES batches of at
-    least max(steps, MIN_BATCH) launches each (whole replays), each batch
-    bracketed by HIP events on `stream`.  Returns (median seconds per launch,
-    info) with info = {"batches", "launches_per_batch", "timed_launches",
+class ClockSampler:
+    """Samples the current shader clock level from the driver's sysfs table
+    (`pp_dpm_sclk`, current level marked '*') on a background thread while
+    the timed batches run; `summary()` gives the MHz readings' distribution."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        import threading
+        self.files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        for f in self.files:
+            try:
+                for line in open(f):
+                    line = line.strip()
+                    if line.endswith("*"):
+                        mhz = line.split(":", 1)[1].strip(" *").lower().replace("mhz", "")
+                        return float(mhz)
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.files:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        a = np.asarray(self.samples)
+        return {"samples": int(a.size), "mhz_median": float(np.median(a)), "mhz_min": float(a.min()),
+                "mhz_max": float(a.max())}
+
+
+def timed_graph(torch, launches, steps, warmup, stream, clock=None):
+    """Capture `launches` (callables enqueuing on `stream`), repeated to at
+    least GRAPH_LAUNCHES launches, into one graph and time its replays:
+    `warmup` launches untimed, then BATCHES batches of at least
+    max(steps, MIN_BATCH) launches each (whole replays), each batch
+    bracketed by HIP events on `stream` (with `clock`, a ClockSampler, running
+    over the batches).  Returns (median seconds per launch, info) with info =
+    {"batches", "launches_per_batch", "timed_launches", "launches_per_graph",
     "us_min", "us_max"} (per-launch times of the fastest and slowest batch)."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(stream):
         for f in launches:  # eager warm-up (kernel attribute set-up happens here)
             f()
     stream.synchronize()
+    rounds = max(1, -(-GRAPH_LAUNCHES // len(launches)))
     with torch.cuda.graph(g, stream=stream):
-        for f in launches:
-            f()
-    n = len(launches)
+        for _ in range(rounds):
+            for f in launches:
+                f()
+    n = len(launches) * rounds
     reps_w = max(1, -(-warmup // n))
     reps = max(1, -(-max(steps, MIN_BATCH) // n))
     for _ in range(reps_w):
         g.replay()
     torch.cuda.synchronize()
     per = []
-    for _ in range(BATCHES):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        with torch.cuda.stream(stream):
-            e0.record(stream)
-            for _ in range(reps):
-                g.replay()
-            e1.record(stream)
-        e1.synchronize()
-        per.append(e0.elapsed_time(e1) / 1e3 / (reps * n))
+    import contextlib
+    with clock if clock is not None else contextlib.nullcontext():
+        for _ in range(BATCHES):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(stream):
+                e0.record(stream)
+                for _ in range(reps):
+                    g.replay()
+                e1.record(stream)
+            e1.synchronize()
+            per.append(e0.elapsed_time(e1) / 1e3 / (reps * n))
     torch.cuda.synchronize()
     info = {"batches": BATCHES, "launches_per_batch": reps * n, "timed_launches": BATCHES * reps * n,
-            "us_min": round(min(per) * 1e6, 3), "us_max": round(max(per) * 1e6, 3)}
+            "launches_per_graph": n, "us_min": round(min(per) * 1e6, 3), "us_max": round(max(per) * 1e6, 3)}
     return float(np.median(per)), info
 
 
@@ -133,7 +191,7 @@ def dev_bf16(torch, bits):
     return t.view(torch.bfloat16).cuda()
 
 
-def bench_forward(torch, lk, case, x_mode, steps, warmup, stream, packed=True, epilogue="layernorm"):
+def bench_forward(torch, lk, case, x_mode, steps, warmup, stream, packed=True, epilogue="layernorm", clock=None):
     """Time loka_gemm_fp8_ln over ROTATE buffer sets; returns a dict.  The
     weight is quantized straight into the packed layout the kernel reads
     (packed=False: row-major [N, K] codes, rearranged inside every call)."""
@@ -153,7 +211,7 @@ def bench_forward(torch, lk, case, x_mode, steps, warmup, stream, packed=True, e
                                    epilogue=epilogue)
         launches.append(f)
     torch.cuda.synchronize()
-    per, tinfo = timed_graph(torch, launches, steps, warmup, stream)
+    per, tinfo = timed_graph(torch, launches, steps, warmup, stream, clock=clock)
     if not packed:
         return {"us": per * 1e6, "timing": tinfo}
     flops = 2.0 * M * N * K
@@ -427,8 +485,9 @@ def main():
     want = lambda name: only is None or name in only
     main_res = None
     if want("fwd"):
-        main_res = bench_forward(torch, lk, case, "row", args.steps, args.warmup, stream)
-        clock = gpu_clock()
+        sampler = ClockSampler()
+        main_res = bench_forward(torch, lk, case, "row", args.steps, args.warmup, stream, clock=sampler)
+        clock = {"sysfs_levels": gpu_clock(), "during_headline": sampler.summary()}
         print(f"[bench] rowwise forward: {main_res['us']:.2f} us/launch (median of {main_res['timing']['batches']} "
               f"batches of {main_res['timing']['launches_per_batch']})", file=sys.stderr, flush=True)
         if not args.no_rows:
@@ -539,13 +598,13 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(main_res["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(main_res["gbs"] / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
                      "traffic_unit": "bytes/launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-                     "kernel": "k_fwd_res<row> (weight-resident fused X quant + FP8 MFMA GEMM + LayerNorm)",
+                     "kernel": "k_fwd_xl<row> (weight-resident staged X quant + FP8 MFMA GEMM + LayerNorm)",
                      "algorithmic_bytes_per_launch": main_res["bytes"],
                      "avg_launch_us": round(main_res["us"], 3)},
         "timing": main_res["timing"],
         "gpu": {"name": torch.cuda.get_device_properties(0).name,
                 "arch": getattr(torch.cuda.get_device_properties(0), "gcnArchName", None),
-                "sclk_after_headline": clock},
+                "sclk": clock},
         "oracle_mere": None if report is None else report["fwd_16384x512x512"],
         "weight_quant_us": round(main_res["weight_quant_us"], 3),
         "value_incl_weight_quant": round(main_res["flops"] / ((main_res["us"] + main_res["weight_quant_us"]) * 1e-6)
