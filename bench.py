@@ -236,14 +236,18 @@ def bench_backward(torch, lk, case, steps, warmup, stream):
     M, K, N = case["M"], case["K"], case["N"]
     x, w, dy = dev_bf16(torch, case["x"]), dev_bf16(torch, case["w"]), dev_bf16(torch, case["dy"])
     bias, gamma, beta = (dev_bf16(torch, case[k]) for k in ("bias", "gamma", "beta"))
-    qw, sw, _ = lk.loka_quant_fp8(w, mode="col", transpose_out=True, stream=stream)
-    qwr, swr, _ = lk.loka_quant_fp8(w, mode="row", stream=stream)
-    f = lk.loka_gemm_fp8_ln(x, qw, sw, bias, gamma, beta, want_stats=True, want_qx=True, stream=stream)
+    # both weights quantized once per step straight into the layouts the
+    # kernels read (the forward's packed weight serves the Z recompute)
+    qw, sw, _ = lk.loka_quant_fp8(w, mode="col", transpose_out="packed", stream=stream)
+    qwr, swr, _ = lk.loka_quant_fp8(w, mode="row", transpose_out="packed_rows", stream=stream)
+    f = lk.loka_gemm_fp8_ln(x, qw, sw, bias, gamma, beta, want_stats=True, want_qx=True, stream=stream,
+                            w_packed=True)
     ctx = {"qx": f["qx"], "sx": f["sx"], "mean": f["mean"], "rstd": f["rstd"], "qw": qw, "sw": sw}
     launches = []
     for i in range(4):
         dyi = dy if i == 0 else dy.clone()
-        fn, _ = lk.loka_gemm_fp8_bwd(dyi, x, qwr, swr, ctx=ctx, bias=bias, gamma=gamma, stream=stream, prepare=True)
+        fn, _ = lk.loka_gemm_fp8_bwd(dyi, x, qwr, swr, ctx=ctx, bias=bias, gamma=gamma, stream=stream, prepare=True,
+                                     w_packed=True)
         launches.append(fn)
     torch.cuda.synchronize()
     per, tinfo = timed_graph(torch, launches, steps, warmup, stream)

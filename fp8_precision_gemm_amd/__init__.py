@@ -31,6 +31,7 @@ STATUS = {0: "LOKA_OK", 1: "LOKA_ERR_INVALID_ARG", 2: "LOKA_ERR_UNSUPPORTED", 3:
           4: "LOKA_ERR_WORKSPACE", 5: "LOKA_ERR_HIP"}
 BWD_NO_LN = 1
 BWD_MX32_SQ = 2
+BWD_W_PACKED = 4
 FWD_W_PACKED = 1
 FWD_BLOCKNORM_HSWISH = 2
 EPILOGUES = {"layernorm": 0, "blocknorm_hswish": FWD_BLOCKNORM_HSWISH}
@@ -57,7 +58,8 @@ class BwdArgs(ctypes.Structure):
                 ("dy", c_vp), ("qx", c_vp), ("sx", c_vp), ("mean", c_vp), ("rstd", c_vp), ("qw", c_vp),
                 ("sw", c_vp), ("bias", c_vp), ("gamma", c_vp), ("x", c_vp), ("qw_row", c_vp), ("sw_row", c_vp),
                 ("dx", c_vp), ("dw", c_vp), ("dgamma", c_vp), ("dbeta", c_vp), ("dbias", c_vp), ("dz", c_vp),
-                ("dz_codes", c_vp), ("dz_scales", c_vp), ("workspace", c_vp), ("workspace_bytes", c_sz)]
+                ("dz_codes", c_vp), ("dz_scales", c_vp), ("workspace", c_vp), ("workspace_bytes", c_sz),
+                ("xc_codes", c_vp), ("xc_scales", c_vp), ("dzc_codes", c_vp), ("dzc_scales", c_vp)]
 
 
 class GroupDesc(ctypes.Structure):
@@ -198,17 +200,19 @@ def loka_quant_fp8(src, fmt="e4m3", mode="row", transpose_out=False, codes=None,
     """Quantize a 2-D bf16/fp32 CUDA tensor.  Returns (codes, scales, amax).
 
     transpose_out: False (codes [rows, cols]), True (codes of src^T, [cols,
-    rows]) or "packed" (codes of src^T in the fragment-interleaved layout
-    that loka_gemm_fp8_ln(w_packed=True) reads; shape packed_shape(rows, cols))."""
+    rows]), "packed" (codes of src^T in the fragment-interleaved layout
+    that loka_gemm_fp8_ln(w_packed=True) reads; shape packed_shape(rows, cols))
+    or "packed_rows" (codes of src itself in that layout, the dgrad weight
+    of loka_gemm_fp8_bwd(w_packed=True); shape packed_shape(cols, rows))."""
     if src.dim() != 2 or src.stride(1) != 1:
         raise ValueError("src must be 2-D with unit column stride")
     rows, cols = src.shape
     m = MODES[mode]
     f = FMTS[fmt]
     dev = src.device
-    trans = 2 if transpose_out == "packed" else (1 if transpose_out else 0)
+    trans = {"packed": 2, "packed_rows": 3}.get(transpose_out, 1 if transpose_out else 0)
     if codes is None:
-        shape = packed_shape(rows, cols) if trans == 2 else ((cols, rows) if trans else (rows, cols))
+        shape = {2: packed_shape(rows, cols), 3: packed_shape(cols, rows), 1: (cols, rows)}.get(trans, (rows, cols))
         codes = torch.empty(shape, dtype=torch.uint8, device=dev)
     if scales is None:
         if m == 0:
@@ -337,11 +341,18 @@ def loka_gemm_fp8_ln_noalloc(x, qw, sw, bias=None, gamma=None, beta=None, eps=1e
 
 def loka_gemm_fp8_bwd(dy, x, qw_row, sw_row, ctx=None, bias=None, gamma=None, no_ln=False, want_dz=False,
                       want_dz_codes=False, want_dgamma=True, want_dbias=True, workspace=None, stream=None,
-                      prepare=False, square=False):
+                      prepare=False, square=False, w_packed=False, want_col_codes=False):
     """Backward of loka_gemm_fp8_ln (row recipe).
 
     ctx: dict with qx [M,K] uint8, sx [M], mean [M], rstd [M], qw [N,K], sw [N]
     (the forward's qx/sx outputs, statistics and weight); unused with no_ln.
+    w_packed=True (flag LOKA_BWD_W_PACKED): ctx["qw"] is the packed forward
+    weight (packed_shape(K, N)) and qw_row the packed dgrad weight
+    (loka_quant_fp8(w, mode="row", transpose_out="packed_rows"),
+    packed_shape(N, K)).
+    want_col_codes=True adds the wgrad operands: xc_codes (packed_shape(M, K))
+    and xc_scales [K] of X per column (e4m3), dzc_codes (packed_shape(M, N))
+    and dzc_scales [N] of dZ per column (e5m2).
     square=True: the backward of the square-block forward (x_mode="mx32_sq";
     flag LOKA_BWD_MX32_SQ): ctx holds X's codes qx [M,K] and scales sx
     [M/32,K/32], the weight's qw [N,K] and sw [K/32,N/32] (always required),
@@ -359,7 +370,9 @@ def loka_gemm_fp8_bwd(dy, x, qw_row, sw_row, ctx=None, bias=None, gamma=None, no
         _need(ctx["sw"], torch.uint8, (K // 32, N // 32), "sw")
     else:
         _need(x, torch.bfloat16, (M, K), "x")
-        _need(qw_row, torch.uint8, (K, N), "qw_row")
+        _need(qw_row, torch.uint8, packed_shape(N, K) if w_packed else (K, N), "qw_row")
+        if w_packed and ctx.get("qw") is not None:
+            _need(ctx["qw"], torch.uint8, packed_shape(K, N), "qw")
     out = {"dx": torch.empty((M, K), dtype=torch.bfloat16, device=dev),
            "dw": torch.empty((K, N), dtype=torch.float32, device=dev)}
     if want_dgamma and not no_ln:
@@ -373,13 +386,20 @@ def loka_gemm_fp8_bwd(dy, x, qw_row, sw_row, ctx=None, bias=None, gamma=None, no
         out["dz_codes"] = torch.empty((M, N), dtype=torch.uint8, device=dev)
         out["dz_scales"] = (torch.empty((M // 32, N // 32), dtype=torch.uint8, device=dev) if square
                             else torch.empty(M, dtype=torch.float32, device=dev))
-    flags = (BWD_NO_LN if no_ln else 0) | (BWD_MX32_SQ if square else 0)
+    if want_col_codes:
+        out["xc_codes"] = torch.empty(packed_shape(M, K), dtype=torch.uint8, device=dev)
+        out["xc_scales"] = torch.empty(K, dtype=torch.float32, device=dev)
+        out["dzc_codes"] = torch.empty(packed_shape(M, N), dtype=torch.uint8, device=dev)
+        out["dzc_scales"] = torch.empty(N, dtype=torch.float32, device=dev)
+    flags = (BWD_NO_LN if no_ln else 0) | (BWD_MX32_SQ if square else 0) | (BWD_W_PACKED if w_packed else 0)
     a = BwdArgs(M=M, N=N, K=K, flags=flags, reserved=0, dy=_ptr(dy), qx=_ptr(ctx.get("qx")),
                 sx=_ptr(ctx.get("sx")), mean=_ptr(ctx.get("mean")), rstd=_ptr(ctx.get("rstd")),
                 qw=_ptr(ctx.get("qw")), sw=_ptr(ctx.get("sw")), bias=_ptr(bias), gamma=_ptr(gamma), x=_ptr(x),
                 qw_row=_ptr(qw_row), sw_row=_ptr(sw_row), dx=_ptr(out["dx"]), dw=_ptr(out["dw"]),
                 dgamma=_ptr(out.get("dgamma")), dbeta=_ptr(out.get("dbeta")), dbias=_ptr(out.get("dbias")),
-                dz=_ptr(out.get("dz")), dz_codes=_ptr(out.get("dz_codes")), dz_scales=_ptr(out.get("dz_scales")))
+                dz=_ptr(out.get("dz")), dz_codes=_ptr(out.get("dz_codes")), dz_scales=_ptr(out.get("dz_scales")),
+                xc_codes=_ptr(out.get("xc_codes")), xc_scales=_ptr(out.get("xc_scales")),
+                dzc_codes=_ptr(out.get("dzc_codes")), dzc_scales=_ptr(out.get("dzc_scales")))
     lib = library()
     nb = lib.loka_gemm_fp8_bwd_workspace_size(ctypes.byref(a))
     ws = _workspace(nb, dev, workspace)

@@ -106,7 +106,7 @@ loka_status loka_quant_fp8(const loka_quant_args* a, void* stream) {
           a->src_dtype);
   REQUIRE(a->fmt == LOKA_E4M3 || a->fmt == LOKA_E5M2, LOKA_ERR_INVALID_ARG, "bad fmt %d", a->fmt);
   REQUIRE(a->mode >= LOKA_SCALE_TENSOR && a->mode <= LOKA_SCALE_MX32_SQ, LOKA_ERR_INVALID_ARG, "bad mode %d", a->mode);
-  REQUIRE(a->transpose_out >= 0 && a->transpose_out <= 2, LOKA_ERR_INVALID_ARG, "transpose_out must be 0, 1 or 2");
+  REQUIRE(a->transpose_out >= 0 && a->transpose_out <= 3, LOKA_ERR_INVALID_ARG, "transpose_out must be 0, 1, 2 or 3");
   const bool mx = a->mode == LOKA_SCALE_MX32_ROW || a->mode == LOKA_SCALE_MX32_COL || a->mode == LOKA_SCALE_MX32_SQ;
   REQUIRE(!(mx && a->amax != nullptr), LOKA_ERR_INVALID_ARG, "amax output is not defined for MX modes");
   REQUIRE(a->cols % 16 == 0, LOKA_ERR_UNSUPPORTED, "cols %% 16 != 0");
@@ -254,9 +254,13 @@ size_t loka_gemm_fp8_bwd_workspace_size(const loka_bwd_args* a) {
 
 loka_status loka_gemm_fp8_bwd(const loka_bwd_args* a, void* stream) {
   REQUIRE(a != nullptr, LOKA_ERR_INVALID_ARG, "args is NULL");
-  REQUIRE((a->flags & ~(LOKA_BWD_NO_LN | LOKA_BWD_MX32_SQ)) == 0, LOKA_ERR_INVALID_ARG, "unknown flags %d",
-          a->flags);
+  REQUIRE((a->flags & ~(LOKA_BWD_NO_LN | LOKA_BWD_MX32_SQ | LOKA_BWD_W_PACKED)) == 0, LOKA_ERR_INVALID_ARG,
+          "unknown flags %d", a->flags);
   const bool sq = (a->flags & LOKA_BWD_MX32_SQ) != 0;
+  const bool w_packed = (a->flags & LOKA_BWD_W_PACKED) != 0;
+  REQUIRE(!(sq && w_packed), LOKA_ERR_UNSUPPORTED, "LOKA_BWD_W_PACKED is for the ROW recipe");
+  REQUIRE(!sq || (!a->xc_codes && !a->xc_scales && !a->dzc_codes && !a->dzc_scales), LOKA_ERR_INVALID_ARG,
+          "the column-code outputs belong to the ROW recipe");
   loka_status st = check_fwd_shape(a->M, a->N, a->K, sq ? LOKA_SCALE_MX32_SQ : LOKA_SCALE_ROW);
   if (st != LOKA_OK) return st;
   REQUIRE(a->K % 64 == 0 && a->K <= 1024, LOKA_ERR_UNSUPPORTED, "backward needs K %% 64 == 0 and K <= 1024");
@@ -286,6 +290,8 @@ loka_status loka_gemm_fp8_bwd(const loka_bwd_args* a, void* stream) {
   REQUIRE_ALIGNED(a->gamma); REQUIRE_ALIGNED(a->x); REQUIRE_ALIGNED(a->qw_row); REQUIRE_ALIGNED(a->sw_row);
   REQUIRE_ALIGNED(a->dx); REQUIRE_ALIGNED(a->dw); REQUIRE_ALIGNED(a->dgamma); REQUIRE_ALIGNED(a->dbeta);
   REQUIRE_ALIGNED(a->dbias); REQUIRE_ALIGNED(a->dz); REQUIRE_ALIGNED(a->dz_codes); REQUIRE_ALIGNED(a->dz_scales);
+  REQUIRE_ALIGNED(a->xc_codes); REQUIRE_ALIGNED(a->xc_scales); REQUIRE_ALIGNED(a->dzc_codes);
+  REQUIRE_ALIGNED(a->dzc_scales);
   if ((st = check_workspace(loka_gemm_fp8_bwd_workspace_size(a), a->workspace, a->workspace_bytes)) != LOKA_OK)
     return st;
   if (a->M == 0) return LOKA_OK;
@@ -295,6 +301,8 @@ loka_status loka_gemm_fp8_bwd(const loka_bwd_args* a, void* stream) {
   b.bias = a->bias; b.gamma = a->gamma; b.x = a->x; b.qw_row = a->qw_row; b.sw_row = a->sw_row;
   b.dx = a->dx; b.dw = a->dw; b.dgamma = a->dgamma; b.dbeta = a->dbeta; b.dbias = a->dbias;
   b.dz = a->dz; b.dz_codes = a->dz_codes; b.dz_scales = a->dz_scales; b.workspace = a->workspace;
+  b.w_packed = w_packed;
+  b.xc_codes = a->xc_codes; b.xc_scales = a->xc_scales; b.dzc_codes = a->dzc_codes; b.dzc_scales = a->dzc_scales;
   return hip_status(loka::launch_bwd(b, static_cast<hipStream_t>(stream)), "loka_gemm_fp8_bwd");
 }
 

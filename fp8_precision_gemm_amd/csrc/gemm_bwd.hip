@@ -131,7 +131,32 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
   int nt, nb;
   wave_tiles<WAVES>(N / 16, wave, nb, nt);
   nb *= 16;
+  int kt, kb0;
+  wave_tiles<WAVES>(K / 16, wave, kb0, kt);
+  kb0 *= 16;
   v4f acc[NTMAX][kMT];  // holds Z, then dZ
+
+  // Weight fragments of both GEMMs stream from L2 through three rotating
+  // buffers, two 128-deep chunks ahead of the MFMAs: the Z recompute's first
+  // two chunks are requested before the staging below, the dgrad's right
+  // after the Z recompute, so each arrives during the phase before its GEMM.
+  const int nchk = (K + 127) >> 7, nchn = (N + 127) >> 7;
+  constexpr int WB = NTMAX > KTMAX ? NTMAX : KTMAX;
+  v8i w0[WB], w1[WB], w2[WB];
+  auto wload = [&](int c, v8i (&w)[WB]) {
+#pragma unroll
+    for (int t = 0; t < NTMAX; ++t)
+      if (t < nt) w[t] = load_frag_ilv(p.qwi, nb / 16 + t, c, nchk, r, g);
+  };
+  auto rload = [&](int c, v8i (&w)[WB]) {
+#pragma unroll
+    for (int t = 0; t < KTMAX; ++t)
+      if (t < kt) w[t] = load_frag_ilv(p.qwri, kb0 / 16 + t, c, nchn, r, g);
+  };
+  if (!NO_LN) {
+    wload(0, w0);
+    if (nchk > 1) wload(1, w1);
+  }
 
   // per-row constants of this lane's rows m = m0 + 16 i + r, requested first
   bool rowok[kMT];
@@ -198,18 +223,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
     for (int t = 0; t < NTMAX; ++t)
 #pragma unroll
       for (int i = 0; i < kMT; ++i) acc[t][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    // weight fragments double-buffered: chunk c+1 is requested before the
-    // MFMAs of chunk c (one wavefront per SIMD: nothing else hides the L2
-    // latency)
-    const int nchk = (K + 127) >> 7;
-    v8i wa[NTMAX], wb[NTMAX];
-    auto wload = [&](int c, v8i (&w)[NTMAX]) {
-#pragma unroll
-      for (int t = 0; t < NTMAX; ++t)
-        if (t < nt) w[t] = load_frag_ilv(p.qwi, nb / 16 + t, c, nchk, r, g);
-    };
-    auto zchunk = [&](int c, const v8i (&wc)[NTMAX], v8i (&wn)[NTMAX]) {
-      if (c + 1 < nchk) wload(c + 1, wn);
+    // one 128-deep chunk: request chunk c + 2 into the free buffer, then the
+    // MFMAs of chunk c
+    auto zstep = [&](int c, const v8i (&wc)[WB], v8i (&wn)[WB]) {
+      if (c + 2 < nchk) wload(c + 2, wn);
       v8i xf[kMT];
 #pragma unroll
       for (int i = 0; i < kMT; ++i) xf[i] = load_frag(xs + (16 * i + r) * ldk, g, 128 * c, K);
@@ -235,12 +252,15 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
             for (int i = 0; i < kMT; ++i) acc[t][i] = mfma_fp8<0, 0>(wc[t], xf[i], acc[t][i]);
       }
     };
-    wload(0, wa);
-    for (int c = 0; c < nchk; c += 2) {
-      zchunk(c, wa, wb);
-      if (c + 1 < nchk) zchunk(c + 1, wb, wa);
+    for (int c = 0; c < nchk; c += 3) {
+      zstep(c, w0, w2);
+      if (c + 1 < nchk) zstep(c + 1, w1, w0);
+      if (c + 2 < nchk) zstep(c + 2, w2, w1);
     }
   }
+  // the dgrad's first weight chunk, into a buffer the Z recompute no longer
+  // reads (the second follows once the LayerNorm backward is done)
+  rload(0, w0);
 
   // g = dY * gamma, yhat; row sums of g and g * yhat.  acc <- yhat, dyg[] <- g
   // (the dY values are re-read below; they stay in L1/L2)
@@ -419,6 +439,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
     }
   }
 
+  if (nchn > 1) rload(1, w1);
   const int nblk = blockIdx.x;
   // dZ (fp32) of the block's 64 rows through one buffer resource: 32-bit
   // offsets instead of a 64-bit address per store
@@ -510,24 +531,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
 
   // dgrad: D[k][m] = sum_n Wr[k][n] dZq[m][n]; each wavefront owns a run of
   // 16-column tiles of k
-  int kt, kb0;
-  wave_tiles<WAVES>(K / 16, wave, kb0, kt);
-  kb0 *= 16;
   v4f dacc[KTMAX][kMT];
 #pragma unroll
   for (int t = 0; t < KTMAX; ++t)
 #pragma unroll
     for (int i = 0; i < kMT; ++i) dacc[t][i] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-  // weight fragments double-buffered as in the Z recompute
-  const int nchn = (N + 127) >> 7;
-  v8i ra[KTMAX], rb[KTMAX];
-  auto rload = [&](int c, v8i (&w)[KTMAX]) {
-#pragma unroll
-    for (int t = 0; t < KTMAX; ++t)
-      if (t < kt) w[t] = load_frag_ilv(p.qwri, kb0 / 16 + t, c, nchn, r, g);
-  };
-  auto dchunk = [&](int c, const v8i (&wc)[KTMAX], v8i (&wn)[KTMAX]) {
-    if (c + 1 < nchn) rload(c + 1, wn);
+  auto dstep = [&](int c, const v8i (&wc)[WB], v8i (&wn)[WB]) {
+    if (c + 2 < nchn) rload(c + 2, wn);
     v8i df[kMT];
 #pragma unroll
     for (int i = 0; i < kMT; ++i) df[i] = load_frag(ds + (16 * i + r) * ldn, g, 128 * c, N);
@@ -553,10 +563,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
           for (int i = 0; i < kMT; ++i) dacc[t][i] = mfma_fp8<0, 1>(wc[t], df[i], dacc[t][i]);
     }
   };
-  rload(0, ra);
-  for (int c = 0; c < nchn; c += 2) {
-    dchunk(c, ra, rb);
-    if (c + 1 < nchn) dchunk(c + 1, rb, ra);
+  for (int c = 0; c < nchn; c += 3) {
+    dstep(c, w0, w2);
+    if (c + 1 < nchn) dstep(c + 1, w1, w0);
+    if (c + 2 < nchn) dstep(c + 2, w2, w1);
   }
   float dsv[kMT];
 #pragma unroll
@@ -949,8 +959,8 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
   p.dz_scales = a.sq ? nullptr : static_cast<float*>(a.dz_scales);
   p.part = reinterpret_cast<float*>(ws + w.part);
   p.nblocks = w.nblocks;
-  p.qwi = ws + w.qwi;
-  p.qwri = ws + w.qwri;
+  p.qwi = a.w_packed ? a.qw : ws + w.qwi;
+  p.qwri = a.w_packed ? a.qw_row : ws + w.qwri;
   p.sdz = a.sq ? (a.dz_scales ? static_cast<uint8_t*>(a.dz_scales) : ws + w.sdz) : nullptr;
   p.dzt = ws + w.dzt;
   p.nchm = (a.M + 127) / 128;
@@ -976,9 +986,11 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
                        a.dgamma, a.dbeta, a.dbias);
     return hipGetLastError();
   }
-  // both weights into the fragment-interleaved order, in one launch
-  if ((e = launch_relayout2(a.no_ln ? nullptr : a.qw, a.N, a.K, ws + w.qwi, a.qw_row, a.K, a.N, ws + w.qwri, s)) !=
-      hipSuccess)
+  // both weights into the fragment-interleaved order, in one launch (unless
+  // they arrive in it)
+  if (!a.w_packed &&
+      (e = launch_relayout2(a.no_ln ? nullptr : a.qw, a.N, a.K, ws + w.qwi, a.qw_row, a.K, a.N, ws + w.qwri, s)) !=
+          hipSuccess)
     return e;
   // N, K <= 512: eight wavefronts of at most four 16-column tiles each;
   // else four wavefronts of at most eight or sixteen
@@ -989,10 +1001,11 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
   if (e != hipSuccess) return e;
 
   // column quantization of X (e4m3) and dZ (e5m2), both transposed to [*, M]
-  uint8_t* xt = ws + w.xt;
-  float* sxc = reinterpret_cast<float*>(ws + w.sxc);
-  uint8_t* dzt = ws + w.dzt;
-  float* sdzc = reinterpret_cast<float*>(ws + w.sdzc);
+  // (into the caller's buffers when it asks for them)
+  uint8_t* xt = a.xc_codes ? a.xc_codes : ws + w.xt;
+  float* sxc = a.xc_scales ? a.xc_scales : reinterpret_cast<float*>(ws + w.sxc);
+  uint8_t* dzt = a.dzc_codes ? a.dzc_codes : ws + w.dzt;
+  float* sdzc = a.dzc_scales ? a.dzc_scales : reinterpret_cast<float*>(ws + w.sdzc);
   // X: column maxima (row-chunk partials); then the column scales of X and
   // of dZ (whose partials the main kernel wrote) in one launch, and both
   // casts in one launch

@@ -113,6 +113,11 @@ struct BwdLaunch {
   uint8_t* dz_codes;
   void* dz_scales;
   void* workspace;
+  bool w_packed;       // qw, qw_row already fragment-interleaved
+  uint8_t* xc_codes;   // optional: the wgrad operands (else in the workspace)
+  float* xc_scales;
+  uint8_t* dzc_codes;
+  float* dzc_scales;
 };
 size_t bwd_workspace_bytes(int64_t M, int64_t N, int64_t K, bool sq);
 hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s);

@@ -312,6 +312,12 @@ __device__ __forceinline__ void cast_tile_body(const CastParams& p, int64_t bx, 
 
   if (TRANS == 0) {
     if (ok) *reinterpret_cast<uint4*>(p.codes + row * p.cols + col0) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if (TRANS == 3) {
+    // fragment-interleaved [rows][cols padded to 128], not transposed: the
+    // grid covers the padding, whose columns load as zeros (zero codes)
+    const int64_t nchc = (p.cols + 127) / 128;
+    if (row < p.rows && col0 < nchc * 128)
+      *reinterpret_cast<uint4*>(p.codes + ilv_offset(row, col0, nchc)) = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
@@ -362,12 +368,17 @@ __global__ __launch_bounds__(256) void k_col_scales_pair(const float* pa, int64_
 }
 
 // trans: 0 plain, 1 transposed row-major, 2 transposed fragment-interleaved
-// (internal; the row count is covered up to the next multiple of 128)
+// (internal; the row count is covered up to the next multiple of 128),
+// 3 fragment-interleaved without transposing (the column count is covered
+// up to the next multiple of 128)
 template <int DT, int FMT, int MODE>
 void launch_cast(const CastParams& cp, int trans, hipStream_t s) {
   const int64_t rows = trans == 2 ? (cp.rows + 127) / 128 * 128 : cp.rows;
-  dim3 grid((unsigned)((cp.cols + kTile - 1) / kTile), (unsigned)((rows + kTile - 1) / kTile));
-  if (trans == 2)
+  const int64_t cols = trans == 3 ? (cp.cols + 127) / 128 * 128 : cp.cols;
+  dim3 grid((unsigned)((cols + kTile - 1) / kTile), (unsigned)((rows + kTile - 1) / kTile));
+  if (trans == 3)
+    hipLaunchKernelGGL((k_cast_tile<DT, FMT, MODE, 3>), grid, dim3(256), 0, s, cp);
+  else if (trans == 2)
     hipLaunchKernelGGL((k_cast_tile<DT, FMT, MODE, 2>), grid, dim3(256), 0, s, cp);
   else if (trans == 1)
     hipLaunchKernelGGL((k_cast_tile<DT, FMT, MODE, 1>), grid, dim3(256), 0, s, cp);

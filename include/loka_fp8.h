@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define LOKA_ABI_VERSION 2
+#define LOKA_ABI_VERSION 3
 
 typedef enum {
   LOKA_OK = 0,
@@ -111,7 +111,14 @@ typedef enum { LOKA_DTYPE_BF16 = 0, LOKA_DTYPE_F32 = 1 } loka_dtype;
  *            (p = 0..7, i = 0..15, b = 0..15).  Lane l = i + 16 g of a
  *            64-wide MFMA fragment load then reads bytes 16 l of each
  *            1 KiB half: the weight layout loka_gemm_fp8_ln and the
- *            grouped launch read with LOKA_FWD_W_PACKED.
+ *            grouped launch read with LOKA_FWD_W_PACKED;
+ *            transpose_out == 3: the codes of src itself (not transposed)
+ *            in the same layout, rows * ceil(cols/128)*128 bytes: for
+ *            every 16 consecutive rows i0..i0+15 and 128-column chunk c
+ *            (columns past `cols` are zero codes) one 2 KiB block at
+ *            ((i0/16) * ceil(cols/128) + c) * 2048, whose byte
+ *            256 p + 16 i + b is src[i0 + i][128 c + 16 p + b] -- the dgrad
+ *            weight layout loka_gemm_fp8_bwd reads with LOKA_BWD_W_PACKED.
  *   scales   TENSOR: float[1]; ROW: float[rows]; COL: float[cols];
  *            MX32_ROW: uint8[rows][cols/32]; MX32_COL: uint8[cols][rows/32];
  *            MX32_SQ: uint8[rows/32][cols/32], the block (i, j) covering
@@ -127,14 +134,14 @@ typedef enum { LOKA_DTYPE_BF16 = 0, LOKA_DTYPE_F32 = 1 } loka_dtype;
  *            (may be NULL when that size is 0).
  * Requirements: rows, cols >= 0; cols % 16 == 0; MX32_ROW: cols % 32 == 0;
  * MX32_COL: rows % 32 == 0; MX32_SQ: rows % 32 == 0 and cols % 32 == 0;
- * transpose_out requires rows % 16 == 0.
+ * transpose_out 1, 2 and 3 require rows % 16 == 0.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int64_t rows, cols, ld;
   int32_t src_dtype;     /* loka_dtype   */
   int32_t fmt;           /* loka_fp8_fmt */
   int32_t mode;          /* loka_scaling */
-  int32_t transpose_out; /* 0, 1 or 2    */
+  int32_t transpose_out; /* 0, 1, 2 or 3 */
   const void* src;
   uint8_t* codes;
   void* scales;
@@ -312,9 +319,28 @@ loka_status loka_gemm_fp8_ln_noalloc(const loka_fwd_args* args, void* stream);
  *   x, qw_row and sw_row are unused (may be NULL); dz_scales, if given,
  *   receives dZ's scales uint8[M/32][N/32].  Needs M % 32 == 0, N <= 512
  *   and K <= 512; mean and rstd unless LOKA_BWD_NO_LN.
+ *
+ * With flags & LOKA_BWD_W_PACKED (ROW recipe only) both weights arrive in
+ * the fragment-interleaved layout instead of row-major, so no
+ * rearrangement runs inside the call: qw as loka_quant_fp8 (COL,
+ * transpose_out 2) writes it for W [K, N] (the forward's packed weight,
+ * N * ceil(K/128)*128 bytes), qw_row as loka_quant_fp8 (ROW,
+ * transpose_out 3) writes it (K * ceil(N/128)*128 bytes).  The results
+ * are bit-identical to the row-major call.
+ *
+ * Optional outputs of the ROW recipe (each may be NULL; must be NULL with
+ * LOKA_BWD_MX32_SQ): the wgrad's two operands, exactly as
+ * loka_quant_fp8 (COL, transpose_out 2) would write them --
+ *   xc_codes   e4m3 codes of X quantized per column (amax over the M rows),
+ *              packed layout of X^T, K * ceil(M/128)*128 bytes;
+ *   xc_scales  float[K];
+ *   dzc_codes  e5m2 codes of the fp32 dZ quantized per column, packed
+ *              layout of dZ^T, N * ceil(M/128)*128 bytes;
+ *   dzc_scales float[N].
  * ---------------------------------------------------------------------- */
 #define LOKA_BWD_NO_LN 1
 #define LOKA_BWD_MX32_SQ 2
+#define LOKA_BWD_W_PACKED 4
 
 typedef struct {
   int64_t M, N, K;
@@ -342,6 +368,10 @@ typedef struct {
   void* dz_scales; /* float[M] (ROW) or uint8[M/32][N/32] (MX32_SQ) */
   void* workspace;
   size_t workspace_bytes;
+  uint8_t* xc_codes;
+  float* xc_scales;
+  uint8_t* dzc_codes;
+  float* dzc_scales;
 } loka_bwd_args;
 
 size_t loka_gemm_fp8_bwd_workspace_size(const loka_bwd_args* args);

@@ -45,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_helpers(lib):
-    assert lib.loka_abi_version() == 2
+    assert lib.loka_abi_version() == 3
     for code, name in lk.STATUS.items():
         assert lib.loka_status_string(code).decode() == name
 
@@ -168,7 +168,8 @@ def _quant(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(rows=-1), 1), (dict(ld=32), 1), (dict(src_dtype=2), 1), (dict(fmt=3), 1), (dict(mode=6), 1),
-    (dict(transpose_out=3), 1), (dict(transpose_out=-1), 1), (dict(transpose_out=2, rows=40), 2),
+    (dict(transpose_out=4), 1), (dict(transpose_out=-1), 1), (dict(transpose_out=2, rows=40), 2),
+    (dict(transpose_out=3, rows=40), 2),
     (dict(cols=40, ld=40), 2), (dict(mode=3, cols=48, ld=48), 2),
     (dict(mode=4, rows=48), 2), (dict(transpose_out=1, rows=40), 2), (dict(ld=68), 3),
     (dict(mode=5, rows=48), 2), (dict(mode=5, cols=48, ld=48), 2), (dict(mode=5, amax=FAKE), 1),
@@ -194,7 +195,11 @@ def _bwd(**kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(flags=4), 1), (dict(K=96), 2), (dict(K=2048), 2), (dict(M=24), 2), (dict(N=96), 2),
+    (dict(flags=8), 1), (dict(K=96), 2), (dict(K=2048), 2), (dict(M=24), 2), (dict(N=96), 2),
+    # packed weights and the column-code outputs belong to the ROW recipe
+    (dict(flags=6), 2), (dict(flags=2, xc_codes=FAKE), 1), (dict(flags=2, dzc_scales=FAKE), 1),
+    (dict(xc_codes=FAKE + 1), 3), (dict(dzc_scales=FAKE + 2), 3),
+    (dict(flags=4), 4), (dict(xc_codes=FAKE, xc_scales=FAKE, dzc_codes=FAKE, dzc_scales=FAKE), 4),
     # the square-block recipe: N, K <= 512, M % 32 == 0, the codes required, mean/rstd unless NO_LN
     (dict(flags=2, N=640), 2), (dict(flags=2, K=576), 2), (dict(flags=2, M=48), 2), (dict(flags=2, qx=None), 1),
     (dict(flags=2, sw=None), 1), (dict(flags=2, rstd=None), 1), (dict(flags=2, x=None, qw_row=None, sw_row=None), 4),

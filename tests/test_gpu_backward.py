@@ -31,7 +31,7 @@ import torch
 
 from oracle import backward, codec, forward, quant
 from synth.workloads import forward_case, outlier_case
-from tests.gpu_helpers import bf16_dev, bf16_ulp, host
+from tests.gpu_helpers import bf16_dev, bf16_ulp, host, unpack_packed
 
 pytestmark = pytest.mark.gpu
 
@@ -40,19 +40,37 @@ MFMA_WINDOW = 2.0 ** -14
 E5 = codec.E5M2
 
 
-def run_gpu(lib, c, no_ln):
+def run_gpu(lib, c, no_ln, w_packed=False):
+    """One backward call with every optional output; w_packed: both weights
+    quantized straight into the fragment-interleaved layouts."""
     x, w, dy = bf16_dev(c["x"]), bf16_dev(c["w"]), bf16_dev(c["dy"])
     bias, gamma, beta = bf16_dev(c["bias"]), bf16_dev(c["gamma"]), bf16_dev(c["beta"])
     qw, sw, _ = lib.loka_quant_fp8(w, fmt="e4m3", mode="col", transpose_out=True)
-    qwr, swr, _ = lib.loka_quant_fp8(w, fmt="e4m3", mode="row", transpose_out=False)
+    qwr, swr, _ = lib.loka_quant_fp8(w, fmt="e4m3", mode="row", transpose_out="packed_rows" if w_packed else False)
     ctx = None
     if not no_ln:
         f = lib.loka_gemm_fp8_ln(x, qw, sw, bias, gamma, beta, want_stats=True, want_qx=True)
+        if w_packed:  # the backward's copy of the forward weight, packed (any N)
+            qw, _, _ = lib.loka_quant_fp8(w, fmt="e4m3", mode="col", transpose_out="packed")
         ctx = {"qx": f["qx"], "sx": f["sx"], "mean": f["mean"], "rstd": f["rstd"], "qw": qw, "sw": sw}
     out = lib.loka_gemm_fp8_bwd(dy, x, qwr, swr, ctx=ctx, bias=bias, gamma=gamma, no_ln=no_ln, want_dz=True,
-                                want_dz_codes=True)
+                                want_dz_codes=True, w_packed=w_packed, want_col_codes=True)
     torch.cuda.synchronize()
     return {k: host(v) for k, v in out.items()}
+
+
+def check_col_codes(g, x_bits):
+    """The wgrad operands, bit for bit: X's column codes and scales against
+    the oracle quantizer on X; dZ's against the oracle quantizer on the
+    kernel's own fp32 dZ (the precision the quantizer is defined on)."""
+    M, K = x_bits.shape
+    N = g["dz"].shape[1]
+    q_x, s_x = quant.quantize(codec.bf16_to_f64(x_bits), quant.COL, codec.E4M3)
+    np.testing.assert_array_equal(unpack_packed(g["xc_codes"], K, M).T, q_x)
+    np.testing.assert_array_equal(g["xc_scales"].view(np.uint32), s_x.astype(np.float32).view(np.uint32))
+    q_d, s_d = quant.quantize(g["dz"].astype(np.float64), quant.COL, E5)
+    np.testing.assert_array_equal(unpack_packed(g["dzc_codes"], N, M).T, q_d)
+    np.testing.assert_array_equal(g["dzc_scales"].view(np.uint32), s_d.astype(np.float32).view(np.uint32))
 
 
 def spacing_e5m2(t):
@@ -121,6 +139,9 @@ def test_literal_reading_full_size(lib):
     np.testing.assert_array_equal(g["dz"], o["dz"].astype(np.float32))
     np.testing.assert_array_equal(g["dz_codes"], o["q_dz"])
     np.testing.assert_array_equal(g["dz_scales"].view(np.uint32), o["s_dz"].astype(np.float32).view(np.uint32))
+    # dZ = dY exactly: the column codes equal the oracle's wgrad operands too
+    check_col_codes(g, c["x"])
+    np.testing.assert_array_equal(unpack_packed(g["dzc_codes"], c["N"], c["M"]).T, o["q_dzc"])
     ex = check_dx(g, o, o["dz"], None)
     ew = check_dw(g, o)
     dy = codec.bf16_to_f64(c["dy"])
@@ -147,6 +168,7 @@ def test_layernorm_reading(lib, M, K, N):
     q_own, s_own = quant.quantize(g["dz"].astype(np.float64), quant.ROW, E5)
     np.testing.assert_array_equal(g["dz_codes"], q_own)
     np.testing.assert_array_equal(g["dz_scales"].view(np.uint32), s_own.astype(np.float32).view(np.uint32))
+    check_col_codes(g, c["x"])
 
     # against the fp64 dZ: codes unique away from midpoints
     s_ref = o["s_dz"].astype(np.float64)
@@ -182,6 +204,19 @@ def test_layernorm_reading(lib, M, K, N):
     check_colsum(g["dbias"], o["dbias"], np.abs(dz_ref).sum(axis=0), "dbias")
     print(f"LN {M}x{K}x{N}: dZ worst {np.max(dz_err / dz_tol):.3f} x tol, {int(differ.sum())} row-code flips "
           f"of {int(amb.sum())} ambiguous; dX err/rms {ex:.2e}; dW err/rms {ew:.2e}")
+
+
+@pytest.mark.parametrize("M,K,N", [(16384, 512, 512), (1040, 192, 320), (96, 256, 1024)])
+def test_packed_weights_bit_identical(lib, M, K, N):
+    """LOKA_BWD_W_PACKED (both weights quantized straight into the
+    interleaved layouts) gives the same bits as the row-major call."""
+    c = outlier_case(dy=True) if M == 16384 else forward_case(M, K, N, seed=M + N, x_dist="student_t3_outliers",
+                                                               gamma_var=0.1, beta_var=0.1, dy_var=1e-3)
+    a = run_gpu(lib, c, no_ln=False)
+    b = run_gpu(lib, c, no_ln=False, w_packed=True)
+    assert set(a) == set(b)
+    for k in a:
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
 
 
 def test_backward_deterministic(lib):

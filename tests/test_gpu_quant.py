@@ -41,6 +41,10 @@ def check_quant(lib, x_bits_or_f32, mode, fmt, transpose, src_f32=False, label="
         rows, cols = ref_codes.shape
         assert tuple(codes.shape) == lib.packed_shape(rows, cols)
         got = unpack_packed(got, cols, rows).T
+    elif transpose == "packed_rows":
+        rows, cols = ref_codes.shape
+        assert tuple(codes.shape) == lib.packed_shape(cols, rows)
+        got = unpack_packed(got, rows, cols)
     elif transpose:
         got = got.T
     bad = np.nonzero(got != ref_codes)
@@ -75,6 +79,21 @@ def test_packed_layout(lib, mode, rows, cols):
     rng = np.random.default_rng(rows * 7 + cols)
     x = to_bf16_bits(rng.standard_t(3, size=(rows, cols)))
     check_quant(lib, x, mode, "e4m3", "packed", label=f"packed {rows}x{cols}")
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("rows,cols", [(256, 256), (144, 96), (32, 16), (64, 336), (96, 160)])
+def test_packed_rows_layout(lib, mode, rows, cols):
+    """transpose_out="packed_rows": the codes of src itself in the
+    fragment-interleaved layout (columns not a multiple of 128 padded with
+    zero codes), the same codes and scales as the plain layout."""
+    if mode in ("mx32_row", "mx32_sq") and cols % 32:
+        pytest.skip("MX32_ROW and MX32_SQ need cols % 32 == 0")
+    if mode in ("mx32_col", "mx32_sq") and rows % 32:
+        pytest.skip("MX32_COL and MX32_SQ need rows % 32 == 0")
+    rng = np.random.default_rng(rows * 5 + cols)
+    x = to_bf16_bits(rng.standard_t(3, size=(rows, cols)))
+    check_quant(lib, x, mode, "e5m2" if mode == "row" else "e4m3", "packed_rows", label=f"packed_rows {rows}x{cols}")
 
 
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
