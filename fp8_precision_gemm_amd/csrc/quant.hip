@@ -148,31 +148,39 @@ __global__ __launch_bounds__(256) void k_amax_col(const void* src, int64_t rows,
   }
 }
 
-// Column scales from the row-chunk partial maxima, once per column: block of
-// 256 threads = 16 columns x 16 strided subsets of the np partials (4 loads
-// in flight each).  Writes the stored scale s, the multiplier r (for the
-// cast) and optionally amax.
+// Column scales from the row-chunk partial maxima, once per column; writes
+// the stored scale s, the multiplier r (for the cast) and optionally amax.
+// A block of 256 threads takes 4 columns: thread (part, cl) = (t / 4, t % 4)
+// reads partial rows part, part + 64, ... of column 4 blk + cl with all its
+// loads in flight at once (one memory round trip for np <= 256), then the
+// 64 parts meet by lane shuffles within each wavefront and through LDS
+// across the four.  The max is order-free: the result does not depend on
+// the grouping.
 template <int FMT>
 __device__ __forceinline__ void col_scales_body(int64_t blk, const float* partials, int64_t np, int64_t cols,
                                                 float* scales, float* mult, float* amax_out) {
-  __shared__ float red[16][16];
-  const int cl = threadIdx.x & 15, part = threadIdx.x >> 4;
-  const int64_t c = blk * 16 + cl;
+  __shared__ float red[4][4];
+  const int cl = threadIdx.x & 3, part = threadIdx.x >> 2;
+  const int64_t c = blk * 4 + cl;
   float m = 0.0f;
   if (c < cols) {
     int64_t k = part;
-    for (; k + 48 < np; k += 64) {
-      const float a = partials[k * cols + c], b = partials[(k + 16) * cols + c];
-      const float d = partials[(k + 32) * cols + c], e = partials[(k + 48) * cols + c];
+    for (; k + 192 < np; k += 256) {
+      const float a = partials[k * cols + c], b = partials[(k + 64) * cols + c];
+      const float d = partials[(k + 128) * cols + c], e = partials[(k + 192) * cols + c];
       m = fmaxf(m, fmaxf(fmaxf(a, b), fmaxf(d, e)));
     }
-    for (; k < np; k += 16) m = fmaxf(m, partials[k * cols + c]);
+    for (; k < np; k += 64) m = fmaxf(m, partials[k * cols + c]);
   }
-  red[part][cl] = m;
+  m = fmaxf(m, __shfl_xor(m, 4, 64));
+  m = fmaxf(m, __shfl_xor(m, 8, 64));
+  m = fmaxf(m, __shfl_xor(m, 16, 64));
+  m = fmaxf(m, __shfl_xor(m, 32, 64));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) < 4) red[wave][cl] = m;
   __syncthreads();
-  if (part == 0 && c < cols) {
-#pragma unroll
-    for (int i = 1; i < 16; ++i) m = fmaxf(m, red[i][cl]);
+  if (threadIdx.x < 4 && c < cols) {
+    m = fmaxf(fmaxf(red[0][cl], red[1][cl]), fmaxf(red[2][cl], red[3][cl]));
     const ScalePair sp = scales_from_amax<FMT>(m);
     scales[c] = sp.s;
     mult[c] = sp.r;
@@ -444,7 +452,7 @@ hipError_t launch_quant(const QuantLaunch& a, hipStream_t s) {
     if (f32) hipLaunchKernelGGL(k_amax_col<1>, g, dim3(256), 0, s, a.src, a.rows, a.cols, a.ld, q.rpc, ws);
     else hipLaunchKernelGGL(k_amax_col<0>, g, dim3(256), 0, s, a.src, a.rows, a.cols, a.ld, q.rpc, ws);
     float* mult = ws + q.np * a.cols;
-    dim3 gs((unsigned)((a.cols + 15) / 16));
+    dim3 gs((unsigned)((a.cols + 3) / 4));
     if (a.fmt == 0)
       hipLaunchKernelGGL(k_col_scales<0>, gs, dim3(256), 0, s, ws, q.np, a.cols, static_cast<float*>(a.scales), mult,
                          a.amax_out);
@@ -495,7 +503,7 @@ hipError_t launch_col_amax_partials(const void* src, int src_dtype, int64_t rows
 // e4m3) and dZ (fp32, e5m2).
 hipError_t launch_col_quant_pair(const ColQuantJob& a, const ColQuantJob& b, hipStream_t s) {
   if (!(a.src_dtype == 0 && a.fmt == 0 && b.src_dtype == 1 && b.fmt == 1)) return hipErrorInvalidValue;
-  const int64_t sa = (a.cols + 15) / 16, sb = (b.cols + 15) / 16;
+  const int64_t sa = (a.cols + 3) / 4, sb = (b.cols + 3) / 4;
   hipLaunchKernelGGL((k_col_scales_pair<0, 1>), dim3((unsigned)(sa + sb)), dim3(256), 0, s, a.partials, a.np, a.cols,
                      a.scales, a.mult, b.partials, b.np, b.cols, b.scales, b.mult, sa);
   hipError_t e = hipGetLastError();
