@@ -55,7 +55,8 @@ def parse():
     p.add_argument("--no-rows", action="store_true", help="skip the other workloads")
     p.add_argument("--only", default=None,
                    help="comma list of workloads to time (for profiling): "
-                        "fwd,tensor,mx,blocknorm,bwd,square,dispatch,probe,grouped,copy")
+                        "fwd,tensor,mx,blocknorm (or blocknorm_fwd_16384x512x512 / blocknorm_fwd_4096x512x4096 "
+                        "alone),bwd,square,dispatch,probe,grouped,copy")
     return p.parse_args()
 
 
@@ -84,6 +85,59 @@ def measured_traffic():
     if fields.get("kernel_source_sha256_16", "").strip() != h.hexdigest()[:16]:
         return None
     return int(fields["traffic_bytes_per_launch"])
+
+
+ROWS_COUNTERS = os.path.join(ROOT, "profiles", "rows_hbm_mfma_counters.md")
+CLOCK_GHZ = 2.4     # MI355X peak shader clock, for the MFMA-busy fraction
+
+
+def _sources_hash(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "fp8_precision_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def row_counters():
+    """Per-row hardware counters from the committed summary: for each
+    workload, the HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-
+    calibrated) and the MFMA-busy cycles per launch (SQ_VALU_MFMA_BUSY_CYCLES)
+    of all the kernels one launch of the row runs.  A row is returned only
+    while its listed sources hash to the value recorded with its counters."""
+    try:
+        text = open(ROWS_COUNTERS).read()
+    except OSError:
+        return {}
+    out = {}
+    for line in text.splitlines():
+        if not line.startswith("row: "):
+            continue
+        f = dict(kv.split("=", 1) for kv in line[5:].split() if "=" in kv)
+        try:
+            if _sources_hash(f["sources"].split(",")) != f["sha256_16"]:
+                continue
+            out[f["name"]] = {"traffic_bytes": int(f["traffic_bytes"]), "mfma_busy_cycles": int(f["mfma_busy_cycles"])}
+        except (KeyError, ValueError, OSError):
+            continue
+    return out
+
+
+def attach_counters(rows, counters, bytes_of):
+    """Adds the committed counters to each timed row: traffic (bytes per
+    launch, and as a fraction of the row's algorithmic bytes when it has
+    them) and the MFMA-busy fraction over the row's measured launch time
+    (1024 SIMDs at CLOCK_GHZ)."""
+    for name, c in counters.items():
+        r = rows.get(name)
+        if r is None or "us" not in r:
+            continue
+        d = {"traffic_bytes": c["traffic_bytes"],
+             "mfma_busy_frac": round(c["mfma_busy_cycles"] / (1024 * r["us"] * 1e-6 * CLOCK_GHZ * 1e9), 4)}
+        if bytes_of.get(name):
+            d["traffic_over_algorithmic"] = round(c["traffic_bytes"] / bytes_of[name], 3)
+        r["counters"] = d
 
 
 BATCHES = 5          # timed batches; the reported time is their median
@@ -511,10 +565,13 @@ def main():
         rows["mx_fwd_65536x1024x256"] = _rounded(r)
         rows["mx_fwd_65536x1024x256"]["hbm_frac"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
         print(f"[bench] mx forward: {r['us']:.2f} us", file=sys.stderr, flush=True)
-    if not args.no_rows and want("blocknorm"):
+    if not args.no_rows and (want("blocknorm") or want("blocknorm_fwd_16384x512x512")
+                             or want("blocknorm_fwd_4096x512x4096")):
         for nm, c in (("blocknorm_fwd_16384x512x512", case),
                       ("blocknorm_fwd_4096x512x4096", workloads.forward_case(4096, 512, 4096, seed=7,
                                                                              x_dist="student_t3_outliers"))):
+            if not (want("blocknorm") or want(nm)):
+                continue
             r = bench_forward(torch, lk, c, "row", args.steps, args.warmup, stream, epilogue="blocknorm_hswish")
             rows[nm] = _rounded(r)
             rows[nm]["hbm_frac"] = round(r["gbs"] / PEAK_HBM_GBS, 4)
@@ -557,6 +614,8 @@ def main():
         r = bench_copy(torch, args.steps, args.warmup, stream)
         rows["copy_16MiB"] = _rounded(r)
         print(f"[bench] copy 16 MiB: {r['us']:.2f} us", file=sys.stderr, flush=True)
+    counters = row_counters()
+    attach_counters(rows, counters, {k: v.get("bytes") or v.get("min_bytes") for k, v in rows.items()})
     if main_res is None:
         print(json.dumps({"rows": rows}))
         return
@@ -604,6 +663,9 @@ def main():
                      "traffic_unit": "bytes/launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
                      "kernel": "k_fwd_xl<row> (weight-resident staged X quant + FP8 MFMA GEMM + LayerNorm)",
                      "algorithmic_bytes_per_launch": main_res["bytes"],
+                     "mfma_busy_frac": (round(counters["fwd_16384x512x512"]["mfma_busy_cycles"]
+                                              / (1024 * main_res["us"] * 1e-6 * CLOCK_GHZ * 1e9), 4)
+                                        if "fwd_16384x512x512" in counters else None),
                      "avg_launch_us": round(main_res["us"], 3)},
         "timing": main_res["timing"],
         "gpu": {"name": torch.cuda.get_device_properties(0).name,

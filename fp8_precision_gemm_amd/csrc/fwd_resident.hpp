@@ -647,10 +647,18 @@ struct ResBlock {
 
   // ---- epilogue, part 1: z = dequant(acc) + b in place; this slice's row
   // sum and centred sum of squares to LDS
+  // (the pipelined run: the constants from LDS, tile by tile, so they never
+  // occupy registers across the loop)
   __device__ __forceinline__ void epilogue_stats(int buf, v4f (&acc)[NT], float& cs) {
-    epilogue_stats(buf, acc, cs, col_sb());
+    epilogue_stats_t<false>(buf, acc, cs, nullptr);
   }
+  // (the staged run: the constants already in registers)
   __device__ __forceinline__ void epilogue_stats(int buf, v4f (&acc)[NT], float& cs, const ColSB& cv) {
+    epilogue_stats_t<true>(buf, acc, cs, &cv);
+  }
+  template <bool REG>
+  __device__ __forceinline__ void epilogue_stats_t(int buf, v4f (&acc)[NT], float& cs, const ColSB* cv) {
+    const float* cb = cvec + c0 + 4 * g;
     const float rsv = rs[buf * kResRows + r];
     const float sx = MODE == 1 ? rsv : (MODE == 0 ? p.x_s : 1.0f);
     const float bound = MX ? ldexpf(bw, (int)rsv - 127) + bb : sx * bw + bb;
@@ -662,8 +670,14 @@ struct ResBlock {
     for (int t = 0; t < NT; ++t) {
       st[t] = 0.0f;
       if (tv(t)) {
-        const float4 sw4 = cv.sw[t];
-        const float4 b4 = cv.b[t];
+        float4 sw4, b4;
+        if constexpr (REG) {
+          sw4 = cv->sw[t];
+          b4 = cv->b[t];
+        } else {
+          sw4 = *reinterpret_cast<const float4*>(cb + 16 * t);
+          b4 = *reinterpret_cast<const float4*>(cb + N + 16 * t);
+        }
         const float swv[4] = {sw4.x, sw4.y, sw4.z, sw4.w}, bv[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -703,13 +717,13 @@ struct ResBlock {
 
   // ---- epilogue, part 2 (after the barrier): combine the slices, normalize, store
   __device__ __forceinline__ void epilogue_out(int buf, int64_t t, const v4f (&acc)[NT], float cs) {
-    if constexpr (EPI == 1) {
-      blocknorm_out(buf, t, acc, cs);
-      return;
-    }
-    epilogue_out(buf, t, acc, cs, col_gb());
+    epilogue_out_t<false>(buf, t, acc, cs, nullptr);
   }
   __device__ __forceinline__ void epilogue_out(int buf, int64_t t, const v4f (&acc)[NT], float cs, const ColGB& cv) {
+    epilogue_out_t<true>(buf, t, acc, cs, &cv);
+  }
+  template <bool REG>
+  __device__ __forceinline__ void epilogue_out_t(int buf, int64_t t, const v4f (&acc)[NT], float cs, const ColGB* cv) {
     if constexpr (EPI == 1) {
       blocknorm_out(buf, t, acc, cs);
       return;
@@ -760,13 +774,20 @@ struct ResBlock {
     }
     const float nmr = -mean * rstd;
     const int cl = c0 + 4 * g;  // this lane's first column (tile t adds 16t)
+    const float* gb = cvec + 2 * N + cl;
     constexpr int YST = res_yst(NT);
     uint8_t* ys = COOP && (t & 1) ? ystg + kWaves * kResRows * YST : ystg;
 #pragma unroll
     for (int t2 = 0; t2 < NT; ++t2) {
       if (tv(t2)) {
-        const float4 ga = cv.g[t2];
-        const float4 be = cv.be[t2];
+        float4 ga, be;
+        if constexpr (REG) {
+          ga = cv->g[t2];
+          be = cv->be[t2];
+        } else {
+          ga = *reinterpret_cast<const float4*>(gb + 16 * t2);
+          be = *reinterpret_cast<const float4*>(gb + N + 16 * t2);
+        }
         const float gv[4] = {ga.x, ga.y, ga.z, ga.w}, bv[4] = {be.x, be.y, be.z, be.w};
         float o[4];
 #pragma unroll
