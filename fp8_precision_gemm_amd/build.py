@@ -8,6 +8,7 @@ this file.
 
 import concurrent.futures
 import os
+import re
 import shutil
 import subprocess
 
@@ -34,13 +35,49 @@ def hipcc():
 
 
 def _compile(src):
+    """Compiles one source; returns (object path, warnings, resource rows).
+    The compiler's per-kernel resource remarks (registers, spills, LDS,
+    occupancy) are collected rather than printed."""
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + FLAGS + ["-Rpass-analysis=kernel-resource-usage", "-x", "hip", "-c", os.path.join(CSRC, src),
+                               "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
-    err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
+    rows, cur, other = [], None, []
+    for line in r.stderr.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = {"source": src, "kernel": m.group(1)}
+            rows.append(cur)
+            continue
+        m = re.search(r"remark: ([A-Za-z /\[\]]+?): (\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = int(m.group(2))
+            continue
+        if "kernel-resource-usage" in line or "packed-fp32-ops" in line or not line.strip():
+            continue
+        if "remark:" in line or line.lstrip().startswith(("|", "^")) or re.match(r"^\s*\d+ \|", line):
+            continue
+        other.append(line)
+    err = "\n".join(other)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{err}")
-    return obj, err
+    return obj, err, rows
+
+
+RESOURCES = os.path.join(BUILD, "resource_usage.tsv")
+_COLUMNS = ["VGPRs", "AGPRs", "VGPRs Spill", "SGPRs", "SGPRs Spill", "LDS Size [bytes/block]",
+            "Occupancy [waves/SIMD]"]
+
+
+def _demangle(names):
+    try:
+        r = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True, check=True)
+        out = r.stdout.splitlines()
+        if len(out) == len(names):
+            return out
+    except (OSError, subprocess.CalledProcessError):
+        pass
+    return list(names)
 
 
 def build(verbose=False):
@@ -49,11 +86,21 @@ def build(verbose=False):
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         results = list(ex.map(_compile, SOURCES))
     if verbose:
-        for (_, err), src in zip(results, SOURCES):
+        for (_, err, _), src in zip(results, SOURCES):
             if err.strip():
                 print(f"[{src}]\n{err}")
+    # every kernel's registers, spills, LDS and occupancy, for the tests that
+    # guard the benchmarked kernels against spilling
+    rows = [row for _, _, rs in results for row in rs]
+    names = _demangle([row["kernel"] for row in rows])
+    with open(RESOURCES, "w") as f:
+        f.write("\t".join(["source", "kernel"] + _COLUMNS) + "\n")
+        for row, name in zip(rows, names):
+            short = re.sub(r"^void ", "", name.replace("(anonymous namespace)::", ""))
+            short = re.sub(r"\(.*", "", short)
+            f.write("\t".join([row["source"], short] + [str(row.get(c, "")) for c in _COLUMNS]) + "\n")
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _ in results]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + [o for o, _, _ in results]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
