@@ -40,9 +40,6 @@ METRIC = "FP8 quant+GEMM+LayerNorm TFLOP/s and % FP8 MFMA peak (M=16384,K=N=512)
 PEAK_FP8_TFLOPS = 5000.0   # MI355X dense FP8 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 ROTATE = 16
-# The fused rowwise forward's sources and the committed counter summary of its HBM traffic.
-FWD_SOURCES = ["common.hpp", "launch.hpp", "fwd_block.hpp", "fwd_resident.hpp", "fwd_kernels.hpp", "fwd_row.hip"]
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_fwd_row_16384x512x512_hbm_counters.md")
 
 
 def parse():
@@ -65,26 +62,6 @@ def fwd_bytes(M, K, N, mx=False):
     weight codes and scales, bias/gamma/beta; write Y (bf16) once."""
     sw = N * (K // 32) if mx else N * 4
     return 2 * M * K + N * K + sw + 3 * 2 * N + 2 * M * N
-
-
-def measured_traffic():
-    """HBM bytes per launch of the fused rowwise forward, as FETCH_SIZE +
-    WRITE_SIZE (each calibrated against a 16 MiB copy) recorded in the
-    committed counter summary -- or None when the kernel's sources no longer
-    hash to the value recorded with the counters."""
-    import hashlib
-    try:
-        text = open(TRAFFIC_SUMMARY).read()
-    except OSError:
-        return None
-    fields = dict(line.split(": ", 1) for line in text.splitlines() if ": " in line and " " not in line.split(": ")[0])
-    h = hashlib.sha256()
-    for f in FWD_SOURCES:
-        with open(os.path.join(ROOT, "fp8_precision_gemm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    if fields.get("kernel_source_sha256_16", "").strip() != h.hexdigest()[:16]:
-        return None
-    return int(fields["traffic_bytes_per_launch"])
 
 
 ROWS_COUNTERS = os.path.join(ROOT, "profiles", "rows_hbm_mfma_counters.md")
@@ -659,8 +636,9 @@ def main():
                    "w_layout": "packed (fragment-interleaved e4m3 codes from loka_quant_fp8)"},
         "pct_fp8_peak": round(100 * main_res["tflops"] / PEAK_FP8_TFLOPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(main_res["gbs"], 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(main_res["gbs"] / PEAK_HBM_GBS, 4), "traffic": measured_traffic(),
-                     "traffic_unit": "bytes/launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+                     "frac": round(main_res["gbs"] / PEAK_HBM_GBS, 4), "traffic": counters.get("fwd_16384x512x512", {}).get("traffic_bytes"),
+                     "traffic_unit": "bytes/launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated; "
+                                     "profiles/rows_hbm_mfma_counters.md, null once the kernel's sources change)",
                      "kernel": "k_fwd_xl<row> (weight-resident staged X quant + FP8 MFMA GEMM + LayerNorm)",
                      "algorithmic_bytes_per_launch": main_res["bytes"],
                      "mfma_busy_frac": (round(counters["fwd_16384x512x512"]["mfma_busy_cycles"]
