@@ -78,7 +78,11 @@ extern "C" {
 int loka_abi_version(void) { return LOKA_ABI_VERSION; }
 
 const char* loka_status_string(loka_status s) {
-  switch (s) {
+  // a C caller may pass any int: take the value's bytes rather than loading
+  // an out-of-range enumerator (undefined in C++)
+  int v;
+  std::memcpy(&v, &s, sizeof v);
+  switch (v) {
     case LOKA_OK: return "LOKA_OK";
     case LOKA_ERR_INVALID_ARG: return "LOKA_ERR_INVALID_ARG";
     case LOKA_ERR_UNSUPPORTED: return "LOKA_ERR_UNSUPPORTED";

@@ -301,3 +301,55 @@ def test_fused_y_square_validation(lib):
     a.N = 256
     a.M = 144
     assert lib.loka_gemm_fp8_ln(ctypes.byref(a), None) == 2                 # M % 32
+
+
+def test_hip_error_path_without_a_device(lib):
+    """A call that passes validation reaches the HIP runtime; with no device
+    its first runtime call fails, and the entry point reports LOKA_ERR_HIP
+    with the failing call named (nothing is launched: the packed-weight
+    forward's first HIP call asks for the current device)."""
+    import torch
+    if torch.cuda.device_count() != 0:
+        pytest.skip("a device is visible: this path needs a host without one")
+    a = _fwd(x_mode=1, flags=1)  # row recipe, packed weight: no workspace needed
+    assert lib.loka_gemm_fp8_ln_workspace_size(ctypes.byref(a)) == 0
+    assert _call(lib, "loka_gemm_fp8_ln", a) == 5
+    msg = lib.loka_last_error().decode()
+    assert "loka_gemm_fp8_ln" in msg, msg
+    assert lib.loka_status_string(5).decode() != ""
+
+
+def test_validation_under_sanitizers(tmp_path):
+    """api.cpp rebuilt with the address and undefined-behaviour sanitizers
+    (host code only), linked with the library's other objects, and its
+    validation paths driven through the C ABI by tests/abi_sanitized.cpp
+    (also built with the sanitizers).  Any invalid access, overflow or
+    undefined operation on these paths aborts the driver."""
+    import shutil
+    import subprocess
+    from fp8_precision_gemm_amd import build as b
+    objs = [os.path.join(b.BUILD, os.path.splitext(s)[0] + ".o") for s in b.SOURCES if s != "api.cpp"]
+    clang = "/opt/rocm/llvm/bin/clang++"
+    if not all(os.path.exists(o) for o in objs) or not os.path.exists(clang):
+        pytest.skip("needs the built objects and ROCm's clang")
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+    api_o = str(tmp_path / "api_san.o")
+    so = str(tmp_path / "liblokafp8_san.so")
+    exe = str(tmp_path / "abi_sanitized")
+    run = lambda cmd: subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+    r = run([b.hipcc()] + b.FLAGS + san + ["-x", "hip", "-c", os.path.join(b.CSRC, "api.cpp"), "-o", api_o])
+    assert r.returncode == 0, r.stderr[-3000:]
+    r = run([b.hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", so, api_o] + objs + san)
+    assert r.returncode == 0, r.stderr[-3000:]
+    drv = os.path.join(os.path.dirname(__file__), "abi_sanitized.cpp")
+    host_san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+    r = run([clang, "-O1", "-g", "-std=c++17"] + host_san + [drv, "-o", exe, so, f"-Wl,-rpath,{tmp_path}",
+                                                             "-L/opt/rocm/lib", "-lamdhip64"])
+    assert r.returncode == 0, r.stderr[-3000:]
+    import torch
+    args = [exe] + (["nodevice"] if torch.cuda.device_count() == 0 else [])
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1", UBSAN_OPTIONS="print_stacktrace=1")
+    r = subprocess.run(args, capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode == 0, (r.stdout[-3000:], r.stderr[-3000:])
+    assert "0 mismatch(es)" in r.stdout, r.stdout
