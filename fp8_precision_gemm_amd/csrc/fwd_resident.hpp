@@ -49,6 +49,8 @@
 // MX scaling can reach 512*2^e before the cast and keeps the clamp.
 #pragma once
 
+#include <utility>
+
 #include "common.hpp"
 #include "fwd_block.hpp"
 #include "launch.hpp"
@@ -76,8 +78,9 @@ struct Res {
   // flight
   static constexpr bool PIPE = NT * KC <= 12 || (NT == 4 && KC == 4);
   // tiles of X requested ahead: small weights run short steps, so they
-  // keep four tiles in flight (the registers are there)
-  static constexpr int D = !PIPE ? 1 : (NT * KC <= 8 ? 4 : 2);
+  // keep four tiles in flight (the registers are there); a tile of one
+  // 16-byte load per lane (K <= 256: 4-8 KiB per tile) keeps eight
+  static constexpr int D = !PIPE ? 1 : (KQ == 1 ? 8 : (NT * KC <= 8 ? 4 : 2));
   static constexpr int LDX = KC * 128 + 16;                    // LDS code row stride (bytes)
   static constexpr int KP = (KC + 3) / 4;                     // E8M0 words per lane group
   static constexpr int XE = 16 * KP;                           // E8M0 bytes per LDS row ([g][KP words])
@@ -950,6 +953,22 @@ struct ResBlock {
     __syncthreads();
   }
 
+  // the prologue's requests of tiles 1 .. D-1 (tile k into slot k)
+  template <int... I>
+  __device__ __forceinline__ void prologue_loads(std::integer_sequence<int, I...>) {
+    (load_x<I + 1>(tb + I + 1), ...);
+  }
+  // one period of the slot and set pattern: steps j .. j + D - 1
+  template <int... M>
+  __device__ __forceinline__ void step_group(int64_t j, std::integer_sequence<int, M...>) {
+    (step<(M + 2) % D, (M + 1) % 2>(j + M), ...);
+  }
+  // the remaining steps (fewer than D), in the same pattern
+  template <int... M>
+  __device__ __forceinline__ void step_tail(int64_t& j, int64_t n, std::integer_sequence<int, M...>) {
+    ((j < n ? (step<(M + 2) % D, (M + 1) % 2>(j), ++j) : j), ...);
+  }
+
   // COOP: the workgroup's 16 x N block of Y of tile t as whole rows, each
   // 16-byte piece read from the staging buffer (t & 1) of the wavefront that
   // produced it; called after a barrier that follows every wavefront's
@@ -1145,9 +1164,7 @@ struct ResBlock {
     load_x<0>(tb);
     request_vectors();
     request_weights();
-    if (D > 1) load_x<(1 % D)>(tb + 1);
-    if (D > 2) load_x<(2 % D)>(tb + 2);
-    if (D > 3) load_x<(3 % D)>(tb + 3);
+    prologue_loads(std::make_integer_sequence<int, D - 1>{});
     __builtin_amdgcn_sched_barrier(0);
     quantize<0>(tb, 0);
     load_x<0>(tb + D);
@@ -1176,24 +1193,11 @@ struct ResBlock {
     // remaining steps: an exit between the steps of the loop body would give
     // the loop header a path on which the X loads just issued are the
     // latest memory operations, and every iteration would then wait for them.
+    // Step j uses slot (j + 1) % D and set j % 2; a group of D steps starting
+    // at j = 1 + D i runs step m with slot (m + 2) % D and set (m + 1) % 2.
     int64_t j = 1;
-    if (D == 2) {
-      for (int64_t i = (n - 1) >> 1; i > 0; --i, j += 2) {
-        step<0, 1>(j);
-        step<(1 % D), 0>(j + 1);
-      }
-      if (j < n) step<0, 1>(j++);
-    } else {
-      for (int64_t i = (n - 1) >> 2; i > 0; --i, j += 4) {
-        step<(2 % D), 1>(j);
-        step<(3 % D), 0>(j + 1);
-        step<0, 1>(j + 2);
-        step<(1 % D), 0>(j + 3);
-      }
-      if (j < n) step<(2 % D), 1>(j++);
-      if (j < n) step<(3 % D), 0>(j++);
-      if (j < n) step<0, 1>(j++);
-    }
+    for (int64_t i = (n - 1) / D; i > 0; --i, j += D) step_group(j, std::make_integer_sequence<int, D>{});
+    step_tail(j, n, std::make_integer_sequence<int, D - 1>{});
     // the last tile's normalization and stores
     const int64_t l = n - 1;
     if (l & 1) epilogue_out(1, tb + l, acc1, cs1);

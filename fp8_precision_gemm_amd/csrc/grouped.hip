@@ -244,8 +244,16 @@ __global__ __launch_bounds__(kThreads) void k_grouped_res_arg(const GroupDev* gr
 // spill).
 template <int NT, bool OPT>
 __device__ __forceinline__ void run_group(const FwdBlock& p, int64_t tb, int64_t te, uint8_t* smem) {
-  ResBlock<1, NT, 4, OPT, false> blk(p, tb, te, smem);
-  blk.run();
+  // K <= 256: the block of two K chunks (one 16-byte X load per lane per
+  // tile, so eight tiles in flight); its LDS layout fits in the four-chunk
+  // one the launch sizes
+  if (p.K <= 256) {
+    ResBlock<1, NT, 2, OPT, false> blk(p, tb, te, smem);
+    blk.run();
+  } else {
+    ResBlock<1, NT, 4, OPT, false> blk(p, tb, te, smem);
+    blk.run();
+  }
 }
 template <bool OPT>
 __global__ __launch_bounds__(kThreads) void k_grouped_mixed(const GroupDev* groups, GroupPlan plan, float eps,
