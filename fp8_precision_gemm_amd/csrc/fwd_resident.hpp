@@ -110,9 +110,9 @@ __host__ __device__ constexpr int res_shape(int nt, int kc) {
                  : (kc == 2 ? 9 : 10);
 }
 
-// LDS carve-up (bytes, every part 16-byte aligned):
-//   codes [2][16][LDX] u8 | xe8 [2][16][XE] u8 | rs [2][16] f32 |
-//   red [2][16][kRedRow] float2 | cvec [4][N] f32 (s_w, bias, gamma, beta) |
+// LDS carve-up (bytes, every part 16-byte aligned; nb = 2, or 4 for B2):
+//   codes [nb][16][LDX] u8 | xe8 [nb][16][XE] u8 | rs [nb][16] f32 |
+//   red [nb][16][kRedRow] float2 | cvec [4][N] f32 (s_w, bias, gamma, beta) |
 //   wmx [3][8] f32 | ystg [8][16][32*NT + 16] (each wavefront's Y block) |
 //   yprev [8][16][32*NT + 16] (the previous tile's Y block, for the Y output
 //   quantized in 32 x 32 blocks)
@@ -120,14 +120,16 @@ struct ResLds {
   int codes, xe8, rs, red, cvec, wmx, ystg, yprev, total;
 };
 __host__ __device__ constexpr int res_yst(int nt) { return 32 * nt + 16; }  // Y staging row stride (bytes)
-__host__ __device__ inline ResLds res_lds(int nt, int kc, int N) {
+// nb: tiles in flight through the code, scale and statistics buffers (two,
+// or four when a step takes two tiles)
+__host__ __device__ inline ResLds res_lds(int nt, int kc, int N, int nb = 2) {
   const int ldx = kc * 128 + 16, xe = 16 * ((kc + 3) / 4);
   ResLds l;
   l.codes = 0;
-  l.xe8 = l.codes + 2 * kResRows * ldx;
-  l.rs = l.xe8 + ((2 * kResRows * xe + 15) / 16) * 16;
-  l.red = l.rs + 2 * kResRows * 4;
-  l.cvec = l.red + 2 * kResRows * kRedRow * 8;
+  l.xe8 = l.codes + nb * kResRows * ldx;
+  l.rs = l.xe8 + ((nb * kResRows * xe + 15) / 16) * 16;
+  l.red = l.rs + nb * kResRows * 4;
+  l.cvec = l.red + nb * kResRows * kRedRow * 8;
   l.wmx = l.cvec + 4 * N * 4;
   l.ystg = l.wmx + 32 * 4;
   l.yprev = l.ystg + kWaves * kResRows * res_yst(nt);
@@ -238,16 +240,21 @@ constexpr int kBlockNorm = 256;
 // XL: the staged run (run_xl): the workgroup's whole tile range (at most
 // kXlTiles tiles, FULL shapes, LayerNorm) is loaded, quantized, multiplied
 // and normalized as one batch.
-template <int MODE, int NT, int KC, bool OPT, bool FULL, int EPI = 0, bool XL = false>
+template <int MODE, int NT, int KC, bool OPT, bool FULL, int EPI = 0, bool XL = false, bool B2 = false>
 struct ResBlock {
   using R = Res<NT, KC>;
   static constexpr bool MX = MODE >= 3;  // E8M0 block scales inside the MFMA
-  static constexpr int KQ = R::KQ, D = R::D, LDX = R::LDX, XE = R::XE, KP = R::KP;
+  // B2 keeps four tiles (two pairs) of X in flight
+  static constexpr int KQ = R::KQ, D = B2 && R::D > 4 ? 4 : R::D, LDX = R::LDX, XE = R::XE, KP = R::KP;
   static constexpr bool PIPE = R::PIPE;
   // sequential steps, guard-free shape, LayerNorm, no optional outputs: Y
   // leaves as whole rows after the next barrier (two staging buffers by tile
   // parity), so no 128-byte line is written in parts by two wavefronts
   static constexpr bool COOP = FULL && !OPT && !PIPE && EPI == 0 && !XL;
+  // B2: two tiles per step (one barrier, one statistics exchange and one
+  // round of latencies for both), for small weights whose steps are mostly
+  // fixed latency; the pipelined LayerNorm path only
+  static_assert(!B2 || (PIPE && EPI == 0 && !XL && D % 2 == 0), "B2 runs the pipelined LayerNorm steps");
 
   const FwdBlock& p;
   int64_t tb, te;  // tile range [tb, te)
@@ -271,9 +278,11 @@ struct ResBlock {
   // two accumulator sets: the GEMM of tile j fills one while the epilogue
   // of tile j-1 reads the other
   v4f acc0[NT], acc1[NT];
+  v4f acc2[NT], acc3[NT];  // B2: the other pair's tiles
   // the staged run: the bf16 X rows in LDS
   uint8_t* xraw;
   float cs0, cs1;   // per set: this lane's row rescale factor (power of two, 1 for ordinary rows)
+  float cs2, cs3;   // B2: the other pair's
   // set-up values in flight: this thread's column (tid < N) and the MX scale bytes
   float cv_sw;
   uint16_t cv_b, cv_g, cv_be;
@@ -300,7 +309,7 @@ struct ResBlock {
     nv = FULL ? NT : min(max(T16 - wave * NT, 0), NT);
     c0 = 16 * NT * wave;
     inv_nw = nv > 0 ? 1.0f / (float)(16 * nv) : 0.0f;
-    const ResLds l = res_lds(NT, KC, N);
+    const ResLds l = res_lds(NT, KC, N, B2 ? 4 : 2);
     codes = smem + l.codes;
     xe8 = smem + l.xe8;
     rs = reinterpret_cast<float*>(smem + l.rs);
@@ -551,18 +560,20 @@ struct ResBlock {
       wmx[16 + wave] = ewm;
     }
     // zero the code rows past K (up to the last chunk) and give the padded
-    // MX blocks a unit scale, in both buffers
+    // MX blocks a unit scale, in every buffer (two, or four for B2: a stale
+    // NaN code there would turn its zero weight into a NaN)
     if (!FULL) {
+      constexpr int NB = B2 ? 4 : 2;
       const int padb = kcv * 128 - K;  // multiple of 16
       if (padb > 0) {
         const int per = padb >> 4;
-        for (int u = tid; u < 2 * kResRows * per; u += kThreads) {
+        for (int u = tid; u < NB * kResRows * per; u += kThreads) {
           const int row = u / per, o = K + 16 * (u - row * per);
           *reinterpret_cast<uint4*>(codes + row * LDX + o) = make_uint4(0, 0, 0, 0);
         }
       }
       if (MX) {
-        for (int u = tid; u < 2 * kResRows * XE; u += kThreads) {
+        for (int u = tid; u < NB * kResRows * XE; u += kThreads) {
           const int sl = u % XE, c = sl % (4 * KP);  // LDS slot (g, c) holds block 4c+g
           if (4 * c + sl / (4 * KP) >= kb) xe8[u] = 127;
         }
@@ -953,6 +964,85 @@ struct ResBlock {
     __syncthreads();
   }
 
+  // ---- B2: two tiles per step -------------------------------------------
+  // Pair j = tiles tb + 2j, tb + 2j + 1 (LDS buffers 2A, 2A + 1 with A = j & 1,
+  // accumulator sets acc0/acc1 for A = 0 and acc2/acc3 for A = 1; tile t in
+  // register slot (t - tb) % D).  Step j: GEMM of pair j alongside the
+  // normalization and stores of pair j - 1 and the quantization of pair j + 1
+  // (slots S2, S3), whose refills (D tiles on) are then requested; pair j's
+  // statistics; one barrier.  Each tile runs the same functions as in the
+  // one-tile steps, so the results are the same bit for bit.
+  template <int S2, int S3, int A>
+  __device__ __forceinline__ void step2(int64_t j) {
+    const int64_t t = tb + 2 * j;
+    v4f (&ca)[NT] = A ? acc2 : acc0;
+    v4f (&cb)[NT] = A ? acc3 : acc1;
+    v4f (&pa)[NT] = A ? acc0 : acc2;
+    v4f (&pb)[NT] = A ? acc1 : acc3;
+    mma(2 * A, ca);
+    mma(2 * A + 1, cb);
+    epilogue_out(2 * (1 - A), t - 2, pa, A ? cs0 : cs2);
+    epilogue_out(2 * (1 - A) + 1, t - 1, pb, A ? cs1 : cs3);
+    quantize<S2>(t + 2, 2 * (1 - A));
+    quantize<S3>(t + 3, 2 * (1 - A) + 1);
+    load_x<S2>(t + 2 + D);
+    load_x<S3>(t + 3 + D);
+    epilogue_stats(2 * A, ca, A ? cs2 : cs0);
+    epilogue_stats(2 * A + 1, cb, A ? cs3 : cs1);
+    __syncthreads();
+  }
+  // groups of G = max(D / 2, 2) pairs from j = 1 + G i: pair m of the group
+  // quantizes tiles 2j + 2 and 2j + 3 from slots (4 + 2m) % D and (5 + 2m) % D
+  // and fills sets (1 + m) & 1
+  template <int... M>
+  __device__ __forceinline__ void step2_group(int64_t j, std::integer_sequence<int, M...>) {
+    (step2<(4 + 2 * M) % D, (5 + 2 * M) % D, (1 + M) & 1>(j + M), ...);
+  }
+  template <int... M>
+  __device__ __forceinline__ void step2_tail(int64_t& j, int64_t np, std::integer_sequence<int, M...>) {
+    ((j < np ? (step2<(4 + 2 * M) % D, (5 + 2 * M) % D, (1 + M) & 1>(j), ++j) : j), ...);
+  }
+  // the last pair's normalization; its second tile only when it exists
+  template <int A>
+  __device__ __forceinline__ void last_pair_out(int64_t t) {
+    epilogue_out(2 * A, t, A ? acc2 : acc0, A ? cs2 : cs0);
+    if (t + 1 < te) epilogue_out(2 * A + 1, t + 1, A ? acc3 : acc1, A ? cs3 : cs1);
+  }
+  __device__ __forceinline__ void run_b2() {
+    if (tb >= te) return;
+    load_x<0>(tb);
+    request_vectors();
+    request_weights();
+    prologue_loads(std::make_integer_sequence<int, D - 1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    quantize<0>(tb, 0);
+    quantize<1>(tb + 1, 1);
+    load_x<0>(tb + D);
+    load_x<1>(tb + 1 + D);
+    stage_vectors();
+    __syncthreads();
+    read_bounds();
+    // pair 0: GEMM alongside the quantization of pair 1
+    mma(0, acc0);
+    mma(1, acc1);
+    quantize<(2 % D)>(tb + 2, 2);
+    quantize<(3 % D)>(tb + 3, 3);
+    load_x<(2 % D)>(tb + 2 + D);
+    load_x<(3 % D)>(tb + 3 + D);
+    epilogue_stats(0, acc0, cs0);
+    epilogue_stats(1, acc1, cs1);
+    __syncthreads();
+    // whole groups of pairs, then the tail (see run() on why)
+    constexpr int G = D / 2 > 2 ? D / 2 : 2;
+    const int64_t np = (te - tb + 1) / 2;
+    int64_t j = 1;
+    for (int64_t i = (np - 1) / G; i > 0; --i, j += G) step2_group(j, std::make_integer_sequence<int, G>{});
+    step2_tail(j, np, std::make_integer_sequence<int, G - 1>{});
+    const int64_t l = np - 1;
+    if (l & 1) last_pair_out<1>(tb + 2 * l);
+    else last_pair_out<0>(tb + 2 * l);
+  }
+
   // the prologue's requests of tiles 1 .. D-1 (tile k into slot k)
   template <int... I>
   __device__ __forceinline__ void prologue_loads(std::integer_sequence<int, I...>) {
@@ -1154,6 +1244,11 @@ struct ResBlock {
   }
 
   __device__ __forceinline__ void run() {
+    if constexpr (B2) {
+      static_assert(MODE == 1, "B2 serves the rowwise recipe");
+      run_b2();
+      return;
+    }
     if (tb >= te) return;
     if (OPT && MODE == 0 && p.sx_out != nullptr && tb == 0 && tid == 0) static_cast<float*>(p.sx_out)[0] = p.x_s;
     // every request first, in the order they are needed (load completions

@@ -245,13 +245,14 @@ __global__ __launch_bounds__(kThreads) void k_grouped_res_arg(const GroupDev* gr
 template <int NT, bool OPT>
 __device__ __forceinline__ void run_group(const FwdBlock& p, int64_t tb, int64_t te, uint8_t* smem) {
   // K <= 256: the block of two K chunks (one 16-byte X load per lane per
-  // tile, so eight tiles in flight); its LDS layout fits in the four-chunk
-  // one the launch sizes
+  // tile, so eight tiles in flight), two tiles per step (its four-buffer LDS
+  // layout is part of the launch's size)
   if (p.K <= 256) {
-    ResBlock<1, NT, 2, OPT, false> blk(p, tb, te, smem);
+    ResBlock<1, NT, 2, OPT, false, 0, false, true> blk(p, tb, te, smem);
     blk.run();
   } else {
-    ResBlock<1, NT, 4, OPT, false> blk(p, tb, te, smem);
+    // four K chunks: two tiles per step too where the registers allow
+    ResBlock<1, NT, 4, OPT, false, 0, false, (NT <= 2)> blk(p, tb, te, smem);
     blk.run();
   }
 }
@@ -454,7 +455,9 @@ hipError_t launch_grouped(const GroupedLaunch& a, hipStream_t s) {
       ++nrows;
       const int nt = fwd::res_nt((int)gd.N);
       if (nt > 3 || fwd::group_kc(nt, (int)gd.K) != 4 || (fwd::group_class(gd.M, gd.N, gd.K) & 1)) mixed = false;
-      const size_t l = (size_t)fwd::res_lds(nt, 4, (int)gd.N).total;
+      // the layout run_group uses: two K chunks and four buffers for K <= 256
+      const size_t l =
+          (size_t)(gd.K <= 256 ? fwd::res_lds(nt, 2, (int)gd.N, 4) : fwd::res_lds(nt, 4, (int)gd.N, nt <= 2 ? 4 : 2)).total;
       if (l > lmax) lmax = l;
     }
     if (mixed && nrows <= fwd::kPlanGroups) {

@@ -135,6 +135,29 @@ def test_grouped_y_only(lib):
     _bitwise_like_single(lib, dg, outs, range(len(groups)))
 
 
+def test_grouped_k_padding_after_nan_codes(lib):
+    """Regression: code rows past K must hold zero codes in every code buffer
+    of the launch.  A first launch with K = 256 and X all NaN leaves NaN codes
+    in every byte of the code rows (each workgroup runs several tiles, so all
+    of its buffers are used); a second launch with K = 192, whose rows are
+    padded from byte 192 on, must then still equal the oracle and single
+    calls (a stale NaN code times a zero weight would be NaN)."""
+    poison = grouped_case(seed=21, groups=12, M=2048, dims=(256,))
+    nan_bf16 = np.full_like(poison[0]["x"], 0x7FC0)
+    for g in poison:
+        g["x"] = nan_bf16
+    lib.loka_grouped_gemm_fp8_ln(prepare(lib, poison))
+    torch.cuda.synchronize()
+    groups = grouped_case(seed=22, groups=12, M=2048, dims=(192,))
+    dg = prepare(lib, groups)
+    outs = lib.loka_grouped_gemm_fp8_ln(dg)
+    torch.cuda.synchronize()
+    for i, (g, o) in enumerate(zip(groups, outs)):
+        ref = forward.gemm_ln_forward(g["x"], g["w"], g["bias"], g["gamma"], g["beta"])
+        check_y(host(o["y"]), ref["y"], f"group {i} (K={g['K']}, N={g['N']})")
+    _bitwise_like_single(lib, dg, outs, range(0, len(groups), 3))
+
+
 @pytest.mark.parametrize("want_z", [False, True])
 def test_grouped_with_wide_and_deep_groups(lib, want_z):
     """Groups with N = 512 or K > 512 in the mix (one launch per register
