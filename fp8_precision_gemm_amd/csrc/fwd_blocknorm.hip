@@ -21,13 +21,11 @@ namespace loka {
 namespace fwd {
 namespace {
 
-template <int NT, int KC, bool OPT, bool FULL>
-__global__ __launch_bounds__(kThreads) void k_fwd_bn(FwdBlock p, int slabs) {
-  extern __shared__ __align__(16) uint8_t smem[];
+// this workgroup's slab (s) and its block arguments: the slab's weight rows,
+// scales, bias and its column range of Y and Z
+template <int NT>
+__device__ __forceinline__ int slab_block(FwdBlock& p, int slabs) {
   const int s = (int)(blockIdx.x % (unsigned)slabs);
-  const int64_t b = blockIdx.x / (unsigned)slabs;
-  const int64_t G = (gridDim.x - s + slabs - 1) / slabs;  // workgroups serving slab s
-  const int64_t T = (p.M + kResRows - 1) / kResRows;
   constexpr int WS = 128 * NT;
   p.qw += (int64_t)s * (WS / 16) * ((p.K + 127) / 128) * 2048;
   p.sw = static_cast<const float*>(p.sw) + (int64_t)s * WS;
@@ -38,15 +36,58 @@ __global__ __launch_bounds__(kThreads) void k_fwd_bn(FwdBlock p, int slabs) {
     p.qx_out = nullptr;
     p.sx_out = nullptr;
   }
+  return s;
+}
+
+template <int NT, int KC, bool OPT, bool FULL>
+__global__ __launch_bounds__(kThreads) void k_fwd_bn(FwdBlock p, int slabs) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int s = slab_block<NT>(p, slabs);
+  const int64_t b = blockIdx.x / (unsigned)slabs;
+  const int64_t G = (gridDim.x - s + slabs - 1) / slabs;  // workgroups serving slab s
+  const int64_t T = (p.M + kResRows - 1) / kResRows;
   ResBlock<1, NT, KC, OPT, FULL, 1> blk(p, b * T / G, (b + 1) * T / G, smem);
   blk.run();
 }
 
+// The staged run (ResBlock::run_xl, as the LayerNorm forward's k_fwd_xl)
+// when every workgroup has at most kXlTiles tiles of its slab: the whole
+// batch quantized, multiplied and normalized together.  Each tile's
+// arithmetic is the same as k_fwd_bn's.
+template <int NT, int KC, bool OPT, bool EXACT>
+__global__ __launch_bounds__(kThreads) void k_fwd_bn_xl(FwdBlock p, int slabs) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int s = slab_block<NT>(p, slabs);
+  const int64_t b = blockIdx.x / (unsigned)slabs;
+  const int64_t G = (gridDim.x - s + slabs - 1) / slabs;
+  const int64_t T = (p.M + kResRows - 1) / kResRows;
+  ResBlock<1, NT, KC, OPT, true, 1, true> blk(p, b * T / G, (b + 1) * T / G, smem);
+  blk.xl_layout(smem);
+  blk.template run_xl<EXACT>();
+}
+
 template <int NT, int KC>
 hipError_t launch_bn_t(const FwdBlock& p, int slabs, int grid, hipStream_t s) {
-  const size_t lds = (size_t)res_lds(NT, KC, p.N).total;
   const bool opt = p.z != nullptr || p.qx_out != nullptr || p.sx_out != nullptr;
   const bool full = res_full(p.M, p.N, p.K, NT, KC);
+  // staged: guard-free shapes with at most kXlTiles tiles for every workgroup
+  // of every slab (the slab with the fewest workgroups has grid / slabs)
+  const int64_t T = (p.M + kResRows - 1) / kResRows;
+  const int64_t gmin = grid / slabs;
+  if constexpr (KC <= 4) {
+    if (full && gmin > 0 && (T + gmin - 1) / gmin <= kXlTiles && xl_lds(NT, KC, p.N, p.K).total <= 160 * 1024) {
+      const size_t lds = (size_t)xl_lds(NT, KC, p.N, p.K).total;
+      const bool exact = grid % slabs == 0 && T == gmin * kXlTiles;
+      auto kern = opt ? (exact ? k_fwd_bn_xl<NT, KC, true, true> : k_fwd_bn_xl<NT, KC, true, false>)
+                      : (exact ? k_fwd_bn_xl<NT, KC, false, true> : k_fwd_bn_xl<NT, KC, false, false>);
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), lds, s, p, slabs);
+      return hipGetLastError();
+    }
+  }
+  const size_t lds = (size_t)res_lds(NT, KC, p.N).total;
   auto kern = opt ? (full ? k_fwd_bn<NT, KC, true, true> : k_fwd_bn<NT, KC, true, false>)
                   : (full ? k_fwd_bn<NT, KC, false, true> : k_fwd_bn<NT, KC, false, false>);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,

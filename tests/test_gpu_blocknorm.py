@@ -46,8 +46,12 @@ def compare(g, o, rows, label):
     print(f"{label}: Z err {err:.2e}  Y max abs err {ey:.2e}")
 
 
+# (512, 256, 768) and (8192, 256, 1024) take the staged run (guard-free, at
+# most four tiles per workgroup of each slab): 256-column slabs, and two
+# 512-column slabs with exactly four tiles per workgroup
 @pytest.mark.parametrize("M,K,N", [(1000, 192, 256), (130, 512, 512), (64, 1024, 256), (300, 256, 768),
-                                   (77, 512, 1024), (33, 160, 2048), (48, 640, 1024), (16, 1024, 4096)])
+                                   (77, 512, 1024), (33, 160, 2048), (48, 640, 1024), (16, 1024, 4096),
+                                   (512, 256, 768), (8192, 256, 1024)])
 def test_blocknorm_shapes(lib, M, K, N):
     c = forward_case(M, K, N, seed=M + 3 * K + N, x_dist="student_t3_outliers")
     g = run(lib, c, packed=True)
