@@ -80,7 +80,8 @@ __global__ __launch_bounds__(kThreads) void k_fwd_xl(FwdBlock p, const float* pa
 // most kXlTiles tiles per workgroup, no square-block Y output, and its LDS
 // layout within the compute unit's 160 KiB.
 inline bool xl_takes(const FwdBlock& p, int mode, int nt, int kc, int grid) {
-  if (mode == 4 || kc > 4 || p.y_codes != nullptr || !res_full(p.M, p.N, p.K, nt, kc)) return false;
+  if (kc > 4 || p.y_codes != nullptr || !res_full(p.M, p.N, p.K, nt, kc)) return false;
+  if (mode == 4 && p.K != 512) return false;  // code input: two rows are one 1 KiB load
   const int64_t T = (p.M + kResRows - 1) / kResRows;
   if ((T + grid - 1) / grid > kXlTiles) return false;
   return xl_lds(nt, kc, p.N, p.K).total <= 160 * 1024;
@@ -90,7 +91,7 @@ template <int MODE, int NT, int KC>
 hipError_t launch_res_t(const FwdBlock& p, const float* partials, int np, int grid, hipStream_t s) {
   const bool opt = p.z != nullptr || p.mean != nullptr || p.rstd != nullptr || p.qx_out != nullptr ||
                    p.sx_out != nullptr || p.y_codes != nullptr;
-  if constexpr (MODE != 4 && KC <= 4) {
+  if constexpr (KC == 4 || (MODE != 4 && KC <= 4)) {
     if (xl_takes(p, MODE, NT, KC, grid)) {
       const size_t lds = (size_t)xl_lds(NT, KC, p.N, p.K).total;
       const bool exact = ((p.M + kResRows - 1) / kResRows) == (int64_t)grid * kXlTiles;

@@ -275,6 +275,7 @@ struct ResBlock {
   uint32_t wsc[NT][KP];
   uint4 xr[D][KQ];
   uint32_t xq8[D][KQ];  // MODE 4: the E8M0 byte of each loaded piece's block
+  uint32_t xl_e8[kXlTiles][KQ];  // MODE 4, staged run: those bytes for each tile of the batch
   // two accumulator sets: the GEMM of tile j fills one while the epilogue
   // of tile j-1 reads the other
   v4f acc0[NT], acc1[NT];
@@ -1118,10 +1119,34 @@ struct ResBlock {
   // so the compiler keeps them where they stand in the issue order (loads
   // complete in issue order: a tile requested after the weight waits for
   // it).
+  // MODE 4 (X given as e4m3 codes, K = 512): the two rows are 2K = 1 KiB of
+  // codes, one instruction per tile, at row stride K in LDS; the E8M0 byte of
+  // each of this lane's pieces (block (m/32, k/32), rows clamped into M: a row
+  // past M has zero codes, its scale is never used) with byte loads.
   template <int I0, int I1>
   __device__ __forceinline__ void xl_request_x() {
     const int64_t row0 = tb * kResRows;
-    const int bytes = (int)((min(te * kResRows, p.M) - row0) * K * 2);
+    const int64_t rows = min(te * kResRows, p.M) - row0;
+    if constexpr (MODE == 4) {
+      static_assert(KQ == 2, "staged code input: K = 512");
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(p.xq + row0 * K), (short)0, (int)(rows * K), kBufferWord3);
+#pragma unroll
+      for (int i = I0; i < I1; ++i) {
+        const uint32_t off = (uint32_t)((i * kResRows + 2 * wave) * K);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(xraw + off), 16,
+                                                 off + 16u * (uint32_t)lane, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = I0; i < I1; ++i) {
+        const int64_t mc = min((tb + i) * kResRows + hrow, p.M - 1);
+        const uint8_t* srow = p.xs + (mc >> 5) * kb;
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) xl_e8[i][q] = srow[(q * 256 + hl * 8) >> 5];
+      }
+      return;
+    }
+    const int bytes = (int)(rows * K * 2);
     const __amdgpu_buffer_rsrc_t rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x + row0 * K), (short)0, bytes, kBufferWord3);
 #pragma unroll
@@ -1138,6 +1163,16 @@ struct ResBlock {
   // this lane's share of its row of tile i, from LDS into register slot 0
   // (the same elements load_x would fetch: 256q + 8 hl .. +8)
   __device__ __forceinline__ void xl_fetch(int i) {
+    if constexpr (MODE == 4) {  // 8 codes per piece (the same elements) and the piece's block scale
+      const uint8_t* row = xraw + (i * kResRows + hrow) * K;
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) {
+        const uint2 c = *reinterpret_cast<const uint2*>(row + q * 256 + hl * 8);
+        xr[0][q] = make_uint4(c.x, c.y, 0u, 0u);
+        xq8[0][q] = xl_e8[i][q];
+      }
+      return;
+    }
     const uint8_t* row = xraw + (i * kResRows + hrow) * 2 * K;
 #pragma unroll
     for (int q = 0; q < KQ; ++q) xr[0][q] = *reinterpret_cast<const uint4*>(row + q * 512 + hl * 16);

@@ -66,8 +66,11 @@ def test_square_forward_full_size(lib):
 
 
 @pytest.mark.parametrize("packed", [True, False])
+# K = 512 with M % 16 == 0 takes the staged run (codes straight into LDS):
+# (1024, 512, 512) one tile per workgroup, (2048, 512, 256) 256 columns,
+# (12288, 512, 512) three tiles per workgroup
 @pytest.mark.parametrize("M,K,N", [(96, 160, 192), (64, 1024, 128), (32, 64, 64), (320, 640, 384),
-                                   (1024, 512, 512), (224, 96, 256)])
+                                   (1024, 512, 512), (224, 96, 256), (2048, 512, 256), (12288, 512, 512)])
 def test_square_forward_shapes(lib, M, K, N, packed):
     c = forward_case(M, K, N, seed=M + 3 * K + N, x_dist="student_t3_outliers", gamma_var=0.1, beta_var=0.1)
     g = run_square(lib, c, packed=packed, no_bias=(M == 96))
