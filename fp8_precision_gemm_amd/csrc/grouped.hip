@@ -19,7 +19,7 @@
 //     (exclusive prefix sums of ceil(M_g/16), other classes counting as
 //     empty) and the first tile of every persistent workgroup, chosen so
 //     that each workgroup gets an equal share of the estimated cost (bytes
-//     moved per tile, 32(K_g+N_g), plus a fixed per-tile term).
+//     moved per tile, 32(K_g+N_g), plus a fixed per-tile term, tile_cost).
 //  2. without packed weights, k_relayout_groups rearranges every group's
 //     row-major weight into the fragment-interleaved layout the resident
 //     block reads (group g at g * stride in the workspace);
@@ -64,8 +64,13 @@ __global__ __launch_bounds__(256) void k_relayout_groups(const GroupDev* groups,
 }
 
 // estimated cost of one 16-row tile: bytes of X read and Y written, plus a
-// fixed term for the per-tile reductions and synchronization
-__host__ __device__ inline int64_t tile_cost(int64_t K, int64_t N) { return 32 * (K + N) + 2048; }
+// fixed term for the per-tile reductions, synchronization and latencies.  The
+// fixed term was fitted on the 64-group workload (K and N in 128..384): its
+// steps cost about 1.1 us at K = N = 128 and 2 us at K = N = 384, so most of a
+// small tile's cost is fixed.  With 12288 the launch took 183 us, with 2048
+// 209 us (the workgroups holding small groups finished last), and with
+// 20480 or 32768, 189 and 197 us.
+__host__ __device__ inline int64_t tile_cost(int64_t K, int64_t N) { return 32 * (K + N) + 12288; }
 
 constexpr int kClasses = 2 * kResShapes;  // (NT, KC) shape x FULL or not
 constexpr int kMaxGrid = 1024;    // workgroups per class launch
