@@ -556,18 +556,30 @@ __device__ __forceinline__ ScalePair reduce_tensor_scale(const float* partials, 
 // aligned, M K a multiple of 8): each thread's max-abs over 16-byte pieces,
 // then the workgroup's.  The max of exact values does not depend on the
 // order, so the scale equals the one from the partials pass bit for bit.
+// X is read through a bounds-checked buffer, so pieces past its end read as
+// zeros (which never raise a max) and a round's 16 loads per thread go out
+// with no branch before its first wait: two round trips for 512 x 256 where
+// four loads in flight took eight.  The caller keeps M K 2 below 2^31 bytes.
 __device__ __forceinline__ ScalePair tensor_scale_self(const FwdBlock& p, float* red8) {
   const int64_t n8 = p.M * (int64_t)p.K / 8;
-  const uint4* x = reinterpret_cast<const uint4*>(p.x);
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x), (short)0,
+                                                                        (int)(n8 * 16), kBufferWord3);
+  constexpr int R = 16;
   float m = 0.0f;
-#pragma unroll 4
-  for (int64_t u = threadIdx.x; u < n8; u += kThreads) {
-    const uint4 v = x[u];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int64_t base = threadIdx.x; base < n8; base += (int64_t)R * kThreads) {
+    uint4 v[R];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m = fmaxf(m, fabsf(__uint_as_float(w[i] << 16)));
-      m = fmaxf(m, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+    for (int q = 0; q < R; ++q)
+      v[q] = __builtin_bit_cast(
+          uint4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (uint32_t)((base + q * kThreads) * 16), 0, 0));
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      const uint32_t w[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m = fmaxf(m, fabsf(__uint_as_float(w[i] << 16)));
+        m = fmaxf(m, fabsf(__uint_as_float(w[i] & 0xFFFF0000u)));
+      }
     }
   }
   m = wave_max_dpp(m);
