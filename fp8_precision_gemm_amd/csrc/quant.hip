@@ -207,8 +207,11 @@ struct CastParams {
 
 // Tile (blockIdx.y, blockIdx.x) covers rows [64 by, +64), cols [64 bx, +64).
 // Thread t: tile row t / 4, tile columns 16 (t % 4) .. +16.
+// mult_local (COL only, optional): the tile's 64 column multipliers in LDS,
+// in place of p.amax_in
 template <int DT, int FMT, int MODE, int TRANS>
-__device__ __forceinline__ void cast_tile_body(const CastParams& p, int64_t bx, int64_t by) {
+__device__ __forceinline__ void cast_tile_body(const CastParams& p, int64_t bx, int64_t by,
+                                               const float* mult_local = nullptr) {
   __shared__ float r_col[kTile];             // COL: multiplier per tile column
   __shared__ float red[4];
   __shared__ float colmax[kTile][kTile + 1];  // MX32_COL: |x| staging
@@ -252,7 +255,7 @@ __device__ __forceinline__ void cast_tile_body(const CastParams& p, int64_t bx, 
   } else if (MODE == 2) {  // column: the multipliers from k_col_scales
     if (t < kTile) {
       const int64_t c = bx * kTile + t;
-      r_col[t] = c < p.cols ? p.amax_in[c] : 1.0f;
+      r_col[t] = c < p.cols ? (mult_local != nullptr ? mult_local[t] : p.amax_in[c]) : 1.0f;
     }
     __syncthreads();
 #pragma unroll
@@ -355,6 +358,61 @@ __global__ __launch_bounds__(256) void k_cast_tile(CastParams p) {
   cast_tile_body<DT, FMT, MODE, TRANS>(p, blockIdx.x, blockIdx.y);
 }
 
+// Column scaling of a short bf16 array (rows <= kStripRows) in one launch
+// instead of three: workgroup (x, y) casts tile (x, y) of 64 x 64 (columns
+// covered as the two-pass path covers them, TRANS 3 padding them to 128),
+// after taking the column maxima of its whole 64-column strip over all rows
+// itself (the strip's workgroups read the same 64 KiB, from L2 after the
+// first), so no workgroup waits for another.  The workgroups of tile row 0
+// write the scales.  A max does not depend on the order of its operands, and
+// the tile body is the two-pass path's, so scales and codes are the same bit
+// for bit.  Thread t: columns 8 (t % 8) .. +8 of the strip, rows t / 8,
+// t / 8 + 32, ...; eight rows' loads are issued before their maxima.
+constexpr int64_t kStripRows = 1024;
+template <int FMT, int TRANS>
+__global__ __launch_bounds__(256) void k_quant_col_strip(CastParams p) {
+  __shared__ float cm[32][kTile + 1];
+  __shared__ float mult[kTile];
+  const int t = threadIdx.x, c8 = t & 7, ph = t >> 3;
+  const int64_t col = (int64_t)blockIdx.x * kTile + c8 * 8;
+  float m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (col < p.cols) {
+    int64_t r = ph;
+    for (; r + 7 * 32 < p.rows; r += 8 * 32) {
+      float v[8][8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) load8<0>(p.src, (r + 32 * u) * p.ld + col, v[u]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[u][i]));
+    }
+    for (; r < p.rows; r += 32) {
+      float v[8];
+      load8<0>(p.src, r * p.ld + col, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m[i] = fmaxf(m[i], fabsf(v[i]));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) cm[ph][c8 * 8 + i] = m[i];
+  __syncthreads();
+  if (t < kTile) {
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) a = fmaxf(a, cm[j][t]);
+    const int64_t c = (int64_t)blockIdx.x * kTile + t;
+    const ScalePair sp = scales_from_amax<FMT>(a);
+    mult[t] = sp.r;
+    if (blockIdx.y == 0 && c < p.cols) {
+      static_cast<float*>(p.scales)[c] = sp.s;
+      if (p.amax_out) p.amax_out[c] = a;
+    }
+  }
+  __syncthreads();
+  cast_tile_body<0, FMT, 2, TRANS>(p, blockIdx.x, blockIdx.y, mult);
+}
+
 // Two column-scaled casts to the fragment-interleaved transposed layout in
 // one launch (blocks [0, na) the first, the rest the second; each with its
 // own 2-D tile grid of width gxa / gxb).
@@ -447,6 +505,24 @@ hipError_t launch_quant(const QuantLaunch& a, hipStream_t s) {
     dim3 g((unsigned)((a.rows + 3) / 4));
     if (f32) hipLaunchKernelGGL(k_amax_row<1>, g, dim3(256), 0, s, a.src, a.rows, a.cols, a.ld, ws);
     else hipLaunchKernelGGL(k_amax_row<0>, g, dim3(256), 0, s, a.src, a.rows, a.cols, a.ld, ws);
+  } else if (a.mode == 2 && !f32 && a.rows <= kStripRows) {
+    // one launch: every 64 x 64 tile's workgroup takes its strip's maxima
+    const int tr = a.transpose_out;
+    const int64_t rows_cov = tr == 2 ? (a.rows + 127) / 128 * 128 : a.rows;
+    const int64_t cols_cov = tr == 3 ? (a.cols + 127) / 128 * 128 : a.cols;
+    const dim3 g((unsigned)((cols_cov + kTile - 1) / kTile), (unsigned)((rows_cov + kTile - 1) / kTile));
+    if (a.fmt == 0) {
+      if (tr == 3) hipLaunchKernelGGL((k_quant_col_strip<0, 3>), g, dim3(256), 0, s, cp);
+      else if (tr == 2) hipLaunchKernelGGL((k_quant_col_strip<0, 2>), g, dim3(256), 0, s, cp);
+      else if (tr == 1) hipLaunchKernelGGL((k_quant_col_strip<0, 1>), g, dim3(256), 0, s, cp);
+      else hipLaunchKernelGGL((k_quant_col_strip<0, 0>), g, dim3(256), 0, s, cp);
+    } else {
+      if (tr == 3) hipLaunchKernelGGL((k_quant_col_strip<1, 3>), g, dim3(256), 0, s, cp);
+      else if (tr == 2) hipLaunchKernelGGL((k_quant_col_strip<1, 2>), g, dim3(256), 0, s, cp);
+      else if (tr == 1) hipLaunchKernelGGL((k_quant_col_strip<1, 1>), g, dim3(256), 0, s, cp);
+      else hipLaunchKernelGGL((k_quant_col_strip<1, 0>), g, dim3(256), 0, s, cp);
+    }
+    return hipGetLastError();
   } else if (a.mode == 2) {
     dim3 g((unsigned)((a.cols + 511) / 512), (unsigned)q.np);
     if (f32) hipLaunchKernelGGL(k_amax_col<1>, g, dim3(256), 0, s, a.src, a.rows, a.cols, a.ld, q.rpc, ws);

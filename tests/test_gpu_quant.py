@@ -133,6 +133,20 @@ def test_tiny_and_degenerate(lib):
         check_quant(lib, z, mode, "e4m3", True, label="zeros")
 
 
+@pytest.mark.parametrize("rows", [1024, 1040])
+@pytest.mark.parametrize("transpose", [False, True, "packed", "packed_rows"])
+def test_column_scales_both_paths(lib, rows, transpose):
+    """Column scaling of bf16 takes one launch per 64-column strip up to 1024
+    rows and the partial-maxima pass beyond: both against the oracle, with
+    a column that is all zeros and a column whose maximum sits in the last
+    row."""
+    rng = np.random.default_rng(rows)
+    x = rng.standard_t(3, size=(rows, 208)) * np.exp(2 * rng.standard_normal((1, 208)))
+    x[:, 17] = 0.0
+    x[-1, 40] = 1e6
+    check_quant(lib, to_bf16_bits(x), "col", "e4m3", transpose, label=f"col {rows}x208")
+
+
 def test_deterministic(lib):
     c = outlier_case(M=2048)
     xt = bf16_dev(c["x"])
