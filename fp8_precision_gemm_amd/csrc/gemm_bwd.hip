@@ -66,6 +66,11 @@ struct BwdBlock {
   uint8_t* sdz;
   uint8_t* dzt;
   int64_t nchm;
+  // optional, eight-wavefront kernel only: bf16 X [M][K] and the per-block
+  // column maxima of |X| out ([nblocks][K]), the first pass of the wgrad
+  // operand's column scales
+  const uint16_t* xb;
+  float* xpart;
 };
 
 // MFMA with both operands' E8M0 scale bytes (the bytes this lane supplies)
@@ -580,6 +585,26 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
       swr[t][0] = s4.x; swr[t][1] = s4.y; swr[t][2] = s4.z; swr[t][3] = s4.w;
     }
   }
+  // Column maxima of |X| over the block's rows, requested here, where the
+  // registers are free, so that they arrive while dX goes into LDS.
+  // Wavefront w takes columns 64 w .. 64 w + 63 (K <= 512); lane l loads 8
+  // columns from 8 (l % 8) of rows l / 8 + 8 j: one 16-byte piece per row.
+  // Rows past M fall outside the resource and read as zero.
+  constexpr bool XMAX = WAVES == 8 && !SQ;
+  const bool xmax = XMAX && p.xpart != nullptr && 64 * wave < K;
+  v4u xr[8];
+  if constexpr (XMAX) {
+    if (xmax) {
+      const int64_t rows_here = FULLM ? (int64_t)kBM : min((int64_t)kBM, p.M - m0);
+      const __amdgpu_buffer_rsrc_t xrs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.xb) + m0 * K, (short)0, (int)(rows_here * K * 2),
+                                            kBufferWord3);
+      const int c0 = 64 * wave + 8 * (lane & 7);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        xr[j] = __builtin_amdgcn_raw_buffer_load_b128(xrs, (uint32_t)(((lane >> 3) + 8 * j) * K + c0) * 2u, 0, 0);
+    }
+  }
   // dX goes out through LDS, so that every store instruction writes whole
   // row segments: the block's tile [BM][K] (bf16, row stride 2K + 16 bytes)
   // takes the LDS from its start once every wavefront is past the dgrad
@@ -602,6 +627,31 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
     }
   }
   __syncthreads();
+  if constexpr (XMAX) {
+    if (xmax) {
+      // per lane over its 8 rows (fmaxf drops NaN, as the column quantizer's
+      // own maxima do), then over the 8 lanes sharing l % 8: l ^ 8 by a DPP
+      // row rotation, l ^ 16 and l ^ 32 by row swaps
+      float cm[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cm[e] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t wv = xr[j][e];
+          cm[2 * e] = fmaxf(cm[2 * e], fabsf(__uint_as_float(wv << 16)));
+          cm[2 * e + 1] = fmaxf(cm[2 * e + 1], fabsf(__uint_as_float(wv & 0xFFFF0000u)));
+        }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) cm[e] = rows4_max(dpp_max<0x128>(cm[e]));
+      if (lane < 8) {
+        float4* dst = reinterpret_cast<float4*>(p.xpart + (size_t)blockIdx.x * K + 64 * wave + 8 * lane);
+        dst[0] = make_float4(cm[0], cm[1], cm[2], cm[3]);
+        dst[1] = make_float4(cm[4], cm[5], cm[6], cm[7]);
+      }
+    }
+  }
   // 16 bytes per lane, a wavefront's 64 lanes on consecutive bytes of a row;
   // dX is not read again here: streaming (non-temporal) stores
   const int c16 = K / 8;
@@ -903,7 +953,10 @@ BwdWs bwd_ws_layout(int64_t M, int64_t N, int64_t K, bool sq) {
   w.xt = o; o += al((size_t)mpad * K);
   if (!sq) {
     w.sxc = o; o += al((size_t)K * 4);
-    w.xcolp = o; o += al((size_t)xq.ws_floats * 4);
+    // the main kernel's per-block partials (N, K <= 512) or the column
+    // quantizer's row-chunk partials, then the column multipliers
+    const size_t xfl = (size_t)(w.nblocks + 1) * K;
+    w.xcolp = o; o += al((xfl > (size_t)xq.ws_floats ? xfl : (size_t)xq.ws_floats) * 4);
   }
   w.dzt = o; o += al((size_t)mpad * N);
   if (!sq) {
@@ -964,6 +1017,11 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
   p.sdz = a.sq ? (a.dz_scales ? static_cast<uint8_t*>(a.dz_scales) : ws + w.sdz) : nullptr;
   p.dzt = ws + w.dzt;
   p.nchm = (a.M + 127) / 128;
+  // N, K <= 512 (eight wavefronts): the main kernel also takes X's column
+  // maxima per block, in place of the column quantizer's first pass
+  const bool xmax_fused = !a.sq && a.N <= 512 && a.K <= 512;
+  p.xb = static_cast<const uint16_t*>(a.x);
+  p.xpart = xmax_fused ? reinterpret_cast<float*>(ws + w.xcolp) : nullptr;
 
   hipError_t e;
   if (a.sq) {
@@ -1006,12 +1064,12 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
   float* sxc = a.xc_scales ? a.xc_scales : reinterpret_cast<float*>(ws + w.sxc);
   uint8_t* dzt = a.dzc_codes ? a.dzc_codes : ws + w.dzt;
   float* sdzc = a.dzc_scales ? a.dzc_scales : reinterpret_cast<float*>(ws + w.sdzc);
-  // X: column maxima (row-chunk partials); then the column scales of X and
-  // of dZ (whose partials the main kernel wrote) in one launch, and both
-  // casts in one launch
+  // X: column maxima (per-block partials from the main kernel, or row-chunk
+  // partials); then the column scales of X and of dZ (whose partials the
+  // main kernel wrote) in one launch, and both casts in one launch
   float* xcolp = reinterpret_cast<float*>(ws + w.xcolp);
-  int64_t xnp = 0;
-  if ((e = launch_col_amax_partials(a.x, 0, a.M, a.K, a.K, xcolp, &xnp, s)) != hipSuccess) return e;
+  int64_t xnp = w.nblocks;
+  if (!xmax_fused && (e = launch_col_amax_partials(a.x, 0, a.M, a.K, a.K, xcolp, &xnp, s)) != hipSuccess) return e;
   const float* dzmax = p.part + (size_t)3 * w.nblocks * a.N;
   ColQuantJob jx{a.x, 0, 0, a.M, a.K, a.K, xcolp, xnp, xt, sxc, xcolp + xnp * a.K};
   ColQuantJob jd{p.dz, 1, 1, a.M, a.N, a.N, dzmax, w.nblocks, dzt, sdzc, reinterpret_cast<float*>(ws + w.dzmult)};
