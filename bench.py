@@ -317,12 +317,15 @@ def bench_square(torch, lk, case, steps, warmup, stream):
            "x_quant_us": qper * 1e6, "timing": tinfo}
     f = lk.loka_gemm_fp8_ln(qx, qw, sw, bias, gamma, beta, x_mode="mx32_sq", x_scales=sx, want_stats=True,
                             stream=stream)
-    ctx = {"qx": qx, "sx": sx, "qw": qw, "sw": sw, "mean": f["mean"], "rstd": f["rstd"]}
+    # both weights quantized straight into the packed layouts, as the rowwise
+    # backward's row takes them (the forward's qwp, and W^T's for the dgrad)
+    qwr, _, _ = lk.loka_quant_fp8(w, mode="mx32_sq", transpose_out="packed_rows", stream=stream)
+    ctx = {"qx": qx, "sx": sx, "qw": qwp, "sw": sw, "mean": f["mean"], "rstd": f["rstd"]}
     launches = []
     for i in range(4):
         dyi = dy if i == 0 else dy.clone()
-        fn, _ = lk.loka_gemm_fp8_bwd(dyi, None, None, None, ctx=ctx, bias=bias, gamma=gamma, stream=stream,
-                                     prepare=True, square=True)
+        fn, _ = lk.loka_gemm_fp8_bwd(dyi, None, qwr, None, ctx=ctx, bias=bias, gamma=gamma, stream=stream,
+                                     prepare=True, square=True, w_packed=True)
         launches.append(fn)
     torch.cuda.synchronize()
     per, tinfo = timed_graph(torch, launches, steps, warmup, stream)

@@ -357,6 +357,9 @@ def loka_gemm_fp8_bwd(dy, x, qw_row, sw_row, ctx=None, bias=None, gamma=None, no
     flag LOKA_BWD_MX32_SQ): ctx holds X's codes qx [M,K] and scales sx
     [M/32,K/32], the weight's qw [N,K] and sw [K/32,N/32] (always required),
     and mean/rstd unless no_ln; x, qw_row and sw_row are unused (None).
+    With square=True and w_packed=True, ctx["qw"] is
+    loka_quant_fp8(w, mode="mx32_sq", transpose_out="packed") and qw_row is
+    the same quantization with transpose_out="packed_rows".
     Returns a dict with dx, dw and the requested outputs."""
     M, N = dy.shape
     ctx = ctx or {}
@@ -366,8 +369,10 @@ def loka_gemm_fp8_bwd(dy, x, qw_row, sw_row, ctx=None, bias=None, gamma=None, no
     if square:
         _need(ctx["qx"], torch.uint8, (M, K), "qx")
         _need(ctx["sx"], torch.uint8, (M // 32, K // 32), "sx")
-        _need(ctx["qw"], torch.uint8, (N, K), "qw")
+        _need(ctx["qw"], torch.uint8, packed_shape(K, N) if w_packed else (N, K), "qw")
         _need(ctx["sw"], torch.uint8, (K // 32, N // 32), "sw")
+        if w_packed:
+            _need(qw_row, torch.uint8, packed_shape(N, K), "qw_row")
     else:
         _need(x, torch.bfloat16, (M, K), "x")
         _need(qw_row, torch.uint8, packed_shape(N, K) if w_packed else (K, N), "qw_row")

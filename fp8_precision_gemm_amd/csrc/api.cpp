@@ -262,7 +262,8 @@ loka_status loka_gemm_fp8_bwd(const loka_bwd_args* a, void* stream) {
           "unknown flags %d", a->flags);
   const bool sq = (a->flags & LOKA_BWD_MX32_SQ) != 0;
   const bool w_packed = (a->flags & LOKA_BWD_W_PACKED) != 0;
-  REQUIRE(!(sq && w_packed), LOKA_ERR_UNSUPPORTED, "LOKA_BWD_W_PACKED is for the ROW recipe");
+  REQUIRE(!(sq && w_packed && a->M > 0 && !a->qw_row), LOKA_ERR_INVALID_ARG,
+          "LOKA_BWD_MX32_SQ with LOKA_BWD_W_PACKED needs qw_row (the packed dgrad weight)");
   REQUIRE(!sq || (!a->xc_codes && !a->xc_scales && !a->dzc_codes && !a->dzc_scales), LOKA_ERR_INVALID_ARG,
           "the column-code outputs belong to the ROW recipe");
   loka_status st = check_fwd_shape(a->M, a->N, a->K, sq ? LOKA_SCALE_MX32_SQ : LOKA_SCALE_ROW);

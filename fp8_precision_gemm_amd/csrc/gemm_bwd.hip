@@ -66,6 +66,9 @@ struct BwdBlock {
   uint8_t* sdz;
   uint8_t* dzt;
   int64_t nchm;
+  // square-block recipe with the LayerNorm (X's codes staged for Z): X's
+  // codes out transposed too, in the same layout as dzt ([K][M padded])
+  uint8_t* xt;
   // optional, eight-wavefront kernel only: bf16 X [M][K] and the per-block
   // column maxima of |X| out ([nblocks][K]), the first pass of the wgrad
   // operand's column scales
@@ -113,7 +116,7 @@ __device__ __forceinline__ void wave_tiles(int T, int w, int& t0, int& n) {
 // (N, K <= 512), else four.
 // SQ: the square-block recipe (X, W and dZ with one E8M0 scale per 32 x 32
 // block; the MFMAs apply the scales, dZ is quantized by blocks and its codes
-// also leave transposed for the wgrad).
+// also leave transposed for the wgrad, as do X's staged codes).
 template <int NTMAX, int KTMAX, int NO_LN, bool FULLM, int WAVES, bool SQ = false>
 __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
   extern __shared__ __align__(16) uint8_t smem[];
@@ -506,32 +509,38 @@ __global__ __launch_bounds__(64 * WAVES) void k_bwd_main(BwdBlock p) {
     // a thread takes 16 rows x 4 columns: 16 word reads, each 4 x 4 byte
     // block transposed with byte permutes (v_perm selects bytes 0-3 from its
     // second operand, 4-7 from its first), then one piece per column
-    const int n4s = N >> 2;
-    const int groups = (int)(rows_out >> 4) * n4s;
-    for (int u = tid; u < groups; u += 64 * WAVES) {
-      const int q = u / n4s, n = (u - q * n4s) * 4;
-      uint32_t col[4][4];
+    // The same for X's codes (staged in LDS for the Z recompute, still
+    // intact): the wgrad's other operand, with no pass of its own.
+    auto codes_t = [&](const uint8_t* src, int ld, int C, uint8_t* dst) {
+      const int n4s = C >> 2;
+      const int groups = (int)(rows_out >> 4) * n4s;
+      for (int u = tid; u < groups; u += 64 * WAVES) {
+        const int q = u / n4s, n = (u - q * n4s) * 4;
+        uint32_t col[4][4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-        if (q < kMT) {
+        for (int k = 0; k < 4; ++k) {
+          uint32_t w[4] = {0u, 0u, 0u, 0u};
+          if (q < kMT) {
 #pragma unroll
-          for (int b = 0; b < 4; ++b) w[b] = *reinterpret_cast<const uint32_t*>(ds + (16 * q + 4 * k + b) * ldn + n);
+            for (int b = 0; b < 4; ++b) w[b] = *reinterpret_cast<const uint32_t*>(src + (16 * q + 4 * k + b) * ld + n);
+          }
+          const uint32_t ab_lo = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // a0 b0 a1 b1
+          const uint32_t ab_hi = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // a2 b2 a3 b3
+          const uint32_t cd_lo = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);  // c0 d0 c1 d1
+          const uint32_t cd_hi = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);  // c2 d2 c3 d3
+          col[0][k] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);           // a0 b0 c0 d0
+          col[1][k] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);           // a1 b1 c1 d1
+          col[2][k] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);
+          col[3][k] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
         }
-        const uint32_t ab_lo = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);  // a0 b0 a1 b1
-        const uint32_t ab_hi = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);  // a2 b2 a3 b3
-        const uint32_t cd_lo = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);  // c0 d0 c1 d1
-        const uint32_t cd_hi = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);  // c2 d2 c3 d3
-        col[0][k] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);           // a0 b0 c0 d0
-        col[1][k] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);           // a1 b1 c1 d1
-        col[2][k] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);
-        col[3][k] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
-      }
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<uint4*>(p.dzt + ilv_offset(n + j, m0 + 16 * q, p.nchm)) =
-            make_uint4(col[j][0], col[j][1], col[j][2], col[j][3]);
-    }
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<uint4*>(dst + ilv_offset(n + j, m0 + 16 * q, p.nchm)) =
+              make_uint4(col[j][0], col[j][1], col[j][2], col[j][3]);
+      }
+    };
+    codes_t(ds, ldn, N, p.dzt);
+    if constexpr (!NO_LN) codes_t(xs, ldk, K, p.xt);
   }
 
   // dgrad: D[k][m] = sum_n Wr[k][n] dZq[m][n]; each wavefront owns a run of
@@ -908,9 +917,11 @@ __global__ __launch_bounds__(256) void k_relayout_sq(const uint8_t* qw, int64_t 
       make_uint4(w4[0], w4[1], w4[2], w4[3]);
 }
 
-hipError_t launch_relayout_sq(const uint8_t* qw, int64_t N, int64_t K, uint8_t* qwi, uint8_t* qwri, const uint8_t* qx,
-                              int64_t M, uint8_t* xt, hipStream_t s) {
-  const int64_t b0 = (N * ((K + 127) / 128) * 8 + 255) / 256;
+// The weight's two layouts unless they arrive packed (do_w false), and X's
+// transposed codes for M > 0; no launch when neither is needed.
+hipError_t launch_relayout_sq(const uint8_t* qw, int64_t N, int64_t K, uint8_t* qwi, uint8_t* qwri, bool do_w,
+                              const uint8_t* qx, int64_t M, uint8_t* xt, hipStream_t s) {
+  const int64_t b0 = do_w ? (N * ((K + 127) / 128) * 8 + 255) / 256 : 0;
   auto job = [](const uint8_t* src, int64_t R, int64_t C, uint8_t* dst) {
     TJob j;
     j.src = src; j.R = R; j.C = C; j.dst = dst;
@@ -918,7 +929,8 @@ hipError_t launch_relayout_sq(const uint8_t* qw, int64_t N, int64_t K, uint8_t* 
     j.blocks = (R + 127) / 128 * 2 * j.tiles_c;  // 64-row tiles up to the 128 padding
     return j;
   };
-  const TJob j1 = job(qw, N, K, qwri), j2 = job(qx, M, K, xt);
+  const TJob j1 = job(qw, do_w ? N : 0, K, qwri), j2 = job(qx, M, K, xt);
+  if (b0 + j1.blocks + j2.blocks == 0) return hipSuccess;
   hipLaunchKernelGGL(k_relayout_sq, dim3((unsigned)(b0 + j1.blocks + j2.blocks)), dim3(256), 0, s, qw, N, K, qwi, b0,
                      j1, j2);
   return hipGetLastError();
@@ -1017,6 +1029,7 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
   p.sdz = a.sq ? (a.dz_scales ? static_cast<uint8_t*>(a.dz_scales) : ws + w.sdz) : nullptr;
   p.dzt = ws + w.dzt;
   p.nchm = (a.M + 127) / 128;
+  p.xt = nullptr;
   // N, K <= 512 (eight wavefronts): the main kernel also takes X's column
   // maxima per block, in place of the column quantizer's first pass
   const bool xmax_fused = !a.sq && a.N <= 512 && a.K <= 512;
@@ -1028,8 +1041,14 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
     // square-block recipe: the forward's codes, rearranged (no requantization),
     // the main kernel (dZ quantized once, in blocks), the wgrad on the codes
     // and the final sums; N, K <= 512
+    // (with the LayerNorm the main kernel writes X's transposed codes from
+    // its staged copy; the literal reading stages no X, so the relayout
+    // transposes them; packed weights need no rearrangement)
     uint8_t* xt = ws + w.xt;
-    if ((e = launch_relayout_sq(a.qw, a.N, a.K, ws + w.qwi, ws + w.qwri, a.qx, a.M, xt, s)) != hipSuccess) return e;
+    p.xt = xt;
+    if ((e = launch_relayout_sq(a.qw, a.N, a.K, ws + w.qwi, ws + w.qwri, !a.w_packed, a.qx, a.no_ln ? a.M : 0, xt,
+                                s)) != hipSuccess)
+      return e;
     if ((e = launch_main_t<4, 4, 8, true>(p, a.no_ln, s)) != hipSuccess) return e;
     float* wpart = reinterpret_cast<float*>(ws + w.wpart);
     dim3 g((unsigned)(((a.N + 127) / 128) * ((a.K + 127) / 128) * w.nsplit));

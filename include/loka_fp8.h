@@ -320,13 +320,16 @@ loka_status loka_gemm_fp8_ln_noalloc(const loka_fwd_args* args, void* stream);
  *   receives dZ's scales uint8[M/32][N/32].  Needs M % 32 == 0, N <= 512
  *   and K <= 512; mean and rstd unless LOKA_BWD_NO_LN.
  *
- * With flags & LOKA_BWD_W_PACKED (ROW recipe only) both weights arrive in
- * the fragment-interleaved layout instead of row-major, so no
- * rearrangement runs inside the call: qw as loka_quant_fp8 (COL,
- * transpose_out 2) writes it for W [K, N] (the forward's packed weight,
- * N * ceil(K/128)*128 bytes), qw_row as loka_quant_fp8 (ROW,
- * transpose_out 3) writes it (K * ceil(N/128)*128 bytes).  The results
- * are bit-identical to the row-major call.
+ * With flags & LOKA_BWD_W_PACKED both weights arrive in the
+ * fragment-interleaved layout instead of row-major, so no rearrangement
+ * runs inside the call: qw as loka_quant_fp8 (COL, transpose_out 2) writes
+ * it for W [K, N] (the forward's packed weight, N * ceil(K/128)*128
+ * bytes), qw_row as loka_quant_fp8 (ROW, transpose_out 3) writes it
+ * (K * ceil(N/128)*128 bytes).  With LOKA_BWD_MX32_SQ the same two layouts
+ * come from MX32_SQ quantizations of W (transpose_out 2 for qw, 3 for
+ * qw_row, which is then required); sw stays the [K/32][N/32] block grid,
+ * and sw_row is unused.  The results are bit-identical to the row-major
+ * call.
  *
  * Optional outputs of the ROW recipe (each may be NULL; must be NULL with
  * LOKA_BWD_MX32_SQ): the wgrad's two operands, exactly as

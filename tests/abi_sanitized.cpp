@@ -93,8 +93,8 @@ void backward_cases() {
   loka_bwd_args a;
   a = bwd(); a.flags = 16; expect("bwd flags=16", loka_gemm_fp8_bwd(&a, nullptr), LOKA_ERR_INVALID_ARG);
   a = bwd(); a.K = 96; expect("bwd K=96", loka_gemm_fp8_bwd(&a, nullptr), LOKA_ERR_UNSUPPORTED);
-  a = bwd(); a.flags = LOKA_BWD_MX32_SQ | LOKA_BWD_W_PACKED;
-  expect("bwd sq+packed", loka_gemm_fp8_bwd(&a, nullptr), LOKA_ERR_UNSUPPORTED);
+  a = bwd(); a.flags = LOKA_BWD_MX32_SQ | LOKA_BWD_W_PACKED; a.qw_row = nullptr;
+  expect("bwd sq+packed without qw_row", loka_gemm_fp8_bwd(&a, nullptr), LOKA_ERR_INVALID_ARG);
   a = bwd(); a.flags = LOKA_BWD_MX32_SQ; a.xc_codes = fk<uint8_t>();
   expect("bwd sq+col outputs", loka_gemm_fp8_bwd(&a, nullptr), LOKA_ERR_INVALID_ARG);
   a = bwd(); a.dz = fk<float>(4); expect("bwd dz misaligned", loka_gemm_fp8_bwd(&a, nullptr), LOKA_ERR_ALIGNMENT);

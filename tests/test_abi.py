@@ -196,8 +196,10 @@ def _bwd(**kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(flags=8), 1), (dict(K=96), 2), (dict(K=2048), 2), (dict(M=24), 2), (dict(N=96), 2),
-    # packed weights and the column-code outputs belong to the ROW recipe
-    (dict(flags=6), 2), (dict(flags=2, xc_codes=FAKE), 1), (dict(flags=2, dzc_scales=FAKE), 1),
+    # the column-code outputs belong to the ROW recipe; the square-block
+    # recipe's packed weights need qw_row (the packed dgrad weight)
+    (dict(flags=6), 4), (dict(flags=6, qw_row=None), 1), (dict(flags=2, xc_codes=FAKE), 1),
+    (dict(flags=2, dzc_scales=FAKE), 1),
     (dict(xc_codes=FAKE + 1), 3), (dict(dzc_scales=FAKE + 2), 3),
     (dict(flags=4), 4), (dict(xc_codes=FAKE, xc_scales=FAKE, dzc_codes=FAKE, dzc_scales=FAKE), 4),
     # the square-block recipe: N, K <= 512, M % 32 == 0, the codes required, mean/rstd unless NO_LN

@@ -120,11 +120,20 @@ def run_square_bwd(lib, c, no_ln, fast_check=True):
     if fast_check:  # without the optional outputs: the configuration the benchmark times
         fast = lib.loka_gemm_fp8_bwd(dy, None, None, None, ctx=ctx, bias=bias, gamma=gamma, no_ln=no_ln,
                                      square=True)
+    packed = None
+    if fast_check:  # the weights quantized straight into the packed layouts: no rearrangement in the call
+        qwp, _, _ = lib.loka_quant_fp8(w, fmt="e4m3", mode="mx32_sq", transpose_out="packed")
+        qwr, _, _ = lib.loka_quant_fp8(w, fmt="e4m3", mode="mx32_sq", transpose_out="packed_rows")
+        packed = lib.loka_gemm_fp8_bwd(dy, None, qwr, None, ctx=dict(ctx, qw=qwp), bias=bias, gamma=gamma,
+                                       no_ln=no_ln, square=True, w_packed=True)
     torch.cuda.synchronize()
     res = {k: host(v) for k, v in out.items()}
     if fast is not None:
         for k in ("dx", "dw", "dbias"):
             np.testing.assert_array_equal(host(fast[k]), res[k], err_msg=f"{k} without the optional outputs")
+    if packed is not None:
+        for k in packed:
+            np.testing.assert_array_equal(host(packed[k]), res[k], err_msg=f"{k} with packed weights")
     return res
 
 
