@@ -12,20 +12,38 @@
 // is an independent weight-resident forward over its columns (the resident
 // block of fwd_resident.hpp with EPI = 1 and NT = 4 or 2): its weight
 // rows are one contiguous run of the packed weight, its outputs a column
-// range of Y with the full row stride.  The persistent grid interleaves the
-// slabs (workgroup b serves slab b % S), so the workgroups reading the same
-// X rows run side by side and the repeated X reads mostly hit the caches.
+// range of Y with the full row stride.  The workgroups of one row group's
+// slabs run side by side on one XCD (see slab_of), so the row group's X
+// comes into that XCD's L2 once and the other slabs read it from there.
 #include "fwd_resident.hpp"
 
 namespace loka {
 namespace fwd {
 namespace {
 
-// this workgroup's slab (s) and its block arguments: the slab's weight rows,
-// scales, bias and its column range of Y and Z
+// This workgroup's slab s, its row group b and the number G of row groups
+// of slab s.  Workgroups go to the eight XCDs round-robin (w % 8).  When the
+// grid is a multiple of 8 x slabs, workgroup w = x + 8 j (XCD x) serves slab
+// j % slabs of row group x + 8 (j / slabs): the slabs of a row group share
+// an XCD and its L2.  Otherwise slab w % slabs of row group w / slabs.
+__device__ __forceinline__ void slab_of(int slabs, int& s, int64_t& b, int64_t& G) {
+  const unsigned w = blockIdx.x, n = gridDim.x, S = (unsigned)slabs;
+  if (n % (8u * S) == 0) {
+    const unsigned j = w >> 3;
+    s = (int)(j % S);
+    b = (int64_t)(w & 7u) + 8 * (int64_t)(j / S);
+    G = n / S;
+  } else {
+    s = (int)(w % S);
+    b = w / S;
+    G = (n - (unsigned)s + S - 1) / S;
+  }
+}
+
+// the block arguments of slab s: the slab's weight rows, scales, bias and
+// its column range of Y and Z
 template <int NT>
-__device__ __forceinline__ int slab_block(FwdBlock& p, int slabs) {
-  const int s = (int)(blockIdx.x % (unsigned)slabs);
+__device__ __forceinline__ void slab_block(FwdBlock& p, int s) {
   constexpr int WS = 128 * NT;
   p.qw += (int64_t)s * (WS / 16) * ((p.K + 127) / 128) * 2048;
   p.sw = static_cast<const float*>(p.sw) + (int64_t)s * WS;
@@ -36,15 +54,15 @@ __device__ __forceinline__ int slab_block(FwdBlock& p, int slabs) {
     p.qx_out = nullptr;
     p.sx_out = nullptr;
   }
-  return s;
 }
 
 template <int NT, int KC, bool OPT, bool FULL>
 __global__ __launch_bounds__(kThreads) void k_fwd_bn(FwdBlock p, int slabs) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int s = slab_block<NT>(p, slabs);
-  const int64_t b = blockIdx.x / (unsigned)slabs;
-  const int64_t G = (gridDim.x - s + slabs - 1) / slabs;  // workgroups serving slab s
+  int s;
+  int64_t b, G;
+  slab_of(slabs, s, b, G);
+  slab_block<NT>(p, s);
   const int64_t T = (p.M + kResRows - 1) / kResRows;
   ResBlock<1, NT, KC, OPT, FULL, 1> blk(p, b * T / G, (b + 1) * T / G, smem);
   blk.run();
@@ -57,9 +75,10 @@ __global__ __launch_bounds__(kThreads) void k_fwd_bn(FwdBlock p, int slabs) {
 template <int NT, int KC, bool OPT, bool EXACT>
 __global__ __launch_bounds__(kThreads) void k_fwd_bn_xl(FwdBlock p, int slabs) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int s = slab_block<NT>(p, slabs);
-  const int64_t b = blockIdx.x / (unsigned)slabs;
-  const int64_t G = (gridDim.x - s + slabs - 1) / slabs;
+  int s;
+  int64_t b, G;
+  slab_of(slabs, s, b, G);
+  slab_block<NT>(p, s);
   const int64_t T = (p.M + kResRows - 1) / kResRows;
   ResBlock<1, NT, KC, OPT, true, 1, true> blk(p, b * T / G, (b + 1) * T / G, smem);
   blk.xl_layout(smem);

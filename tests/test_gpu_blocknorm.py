@@ -51,7 +51,10 @@ def compare(g, o, rows, label):
 # 512-column slabs with exactly four tiles per workgroup
 @pytest.mark.parametrize("M,K,N", [(1000, 192, 256), (130, 512, 512), (64, 1024, 256), (300, 256, 768),
                                    (77, 512, 1024), (33, 160, 2048), (48, 640, 1024), (16, 1024, 4096),
-                                   (512, 256, 768), (8192, 256, 1024)])
+                                   (512, 256, 768), (8192, 256, 1024),
+                                   # a full grid of 8 x slabs workgroups (each row group's slabs on one
+                                   # XCD) with a ragged last tile: staged, staged, per-tile
+                                   (4100, 256, 1024), (2000, 512, 4096), (4100, 512, 2048)])
 def test_blocknorm_shapes(lib, M, K, N):
     c = forward_case(M, K, N, seed=M + 3 * K + N, x_dist="student_t3_outliers")
     g = run(lib, c, packed=True)
