@@ -86,6 +86,12 @@ __host__ __device__ inline int group_class(int64_t M, int64_t N, int64_t K) {
   return 2 * res_shape(nt, kc) + (res_full(M, (int)N, (int)K, nt, kc) ? 1 : 0);
 }
 
+// The plan's tile range a workgroup walks.  Workgroups go to the eight XCDs
+// round-robin (w % 8); with n % 8 == 0, workgroup w takes range
+// (w % 8) n/8 + w / 8, so consecutive ranges (mostly tiles of the same
+// groups) run on one XCD and each group's weight is fetched into one L2.
+__device__ __forceinline__ int plan_range(int w, int n) { return (n & 7) == 0 ? (w & 7) * (n >> 3) + (w >> 3) : w; }
+
 // The plan of one class as a kernel argument (by value, so a captured graph
 // replays it without any host copy): the class's groups, their exclusive
 // prefix of 16-row tiles, and each workgroup's first tile.
@@ -196,8 +202,9 @@ template <bool OPT, int NT, int KC, bool FULL>
 __global__ __launch_bounds__(kThreads) void k_grouped_res(const GroupDev* groups, const int* tile_pre,
                                                           const int* wg_start, int G, float eps, WeightSrc wsrc) {
   extern __shared__ __align__(16) uint8_t smem[];
-  int t = wg_start[blockIdx.x];
-  const int tend = wg_start[blockIdx.x + 1];
+  const int wr = plan_range((int)blockIdx.x, (int)gridDim.x);
+  int t = wg_start[wr];
+  const int tend = wg_start[wr + 1];
   int lo = 0, hi = G - 1;  // last group with tile_pre[g] <= t
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -221,8 +228,9 @@ template <bool OPT, int NT, int KC, bool FULL>
 __global__ __launch_bounds__(kThreads) void k_grouped_res_arg(const GroupDev* groups, GroupPlan plan, float eps,
                                                               WeightSrc wsrc) {
   extern __shared__ __align__(16) uint8_t smem[];
-  int t = plan.wg_start[blockIdx.x];
-  const int tend = plan.wg_start[blockIdx.x + 1];
+  const int wr = plan_range((int)blockIdx.x, (int)gridDim.x);
+  int t = plan.wg_start[wr];
+  const int tend = plan.wg_start[wr + 1];
   int lo = 0, hi = plan.ngroups - 1;  // last class group with tile_pre <= t
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -265,8 +273,9 @@ template <bool OPT>
 __global__ __launch_bounds__(kThreads) void k_grouped_mixed(const GroupDev* groups, GroupPlan plan, float eps,
                                                             WeightSrc wsrc) {
   extern __shared__ __align__(16) uint8_t smem[];
-  int t = plan.wg_start[blockIdx.x];
-  const int tend = plan.wg_start[blockIdx.x + 1];
+  const int wr = plan_range((int)blockIdx.x, (int)gridDim.x);
+  int t = plan.wg_start[wr];
+  const int tend = plan.wg_start[wr + 1];
   int lo = 0, hi = plan.ngroups - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
