@@ -780,23 +780,41 @@ __global__ __launch_bounds__(512) void k_wgrad(const uint8_t* dzt, const uint8_t
 // => deterministic.
 __device__ __forceinline__ void finalize_body(int64_t blk, const float* wpart, int nsplit, const float* sxc,
                                               const float* sdzc, int K, int N, float* dw) {
-  const int64_t i = blk * 256 + threadIdx.x;
+  // four consecutive elements of a row of dW per thread (N % 4 == 0); up to
+  // sixteen slices' 16-byte loads in flight at once, added in slice order
+  const int64_t i = (blk * 256 + threadIdx.x) * 4;
   const int64_t kn = (int64_t)K * N;
-  if (i < kn) {
-    // eight slices' loads in flight per iteration, added in slice order
-    float s = 0.0f;
-    int sp = 0;
-    for (; sp + 8 <= nsplit; sp += 8) {
-      float v[8];
+  if (i >= kn) return;
+  float4 s = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  auto add = [&](const float4& v) {
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  };
+  int sp = 0;
+  for (; sp + 16 <= nsplit; sp += 16) {
+    float4 v[16];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = wpart[(int64_t)(sp + q) * kn + i];
+    for (int q = 0; q < 16; ++q) v[q] = *reinterpret_cast<const float4*>(wpart + (int64_t)(sp + q) * kn + i);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) s += v[q];
-    }
-    for (; sp < nsplit; ++sp) s += wpart[(int64_t)sp * kn + i];
-    const int k = (int)(i / N), n = (int)(i - (int64_t)k * N);
-    dw[i] = sxc != nullptr ? s * sxc[k] * sdzc[n] : s;
+    for (int q = 0; q < 16; ++q) add(v[q]);
   }
+  for (; sp + 4 <= nsplit; sp += 4) {
+    float4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const float4*>(wpart + (int64_t)(sp + q) * kn + i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) add(v[q]);
+  }
+  for (; sp < nsplit; ++sp) add(*reinterpret_cast<const float4*>(wpart + (int64_t)sp * kn + i));
+  if (sxc != nullptr) {
+    const int k = (int)(i / N), n = (int)(i - (int64_t)k * N);
+    const float sk = sxc[k];
+    const float4 sn = *reinterpret_cast<const float4*>(sdzc + n);
+    s = make_float4(s.x * sk * sn.x, s.y * sk * sn.y, s.z * sk * sn.z, s.w * sk * sn.w);
+  }
+  *reinterpret_cast<float4*>(dw + i) = s;
 }
 
 // dgamma, dbeta, dbias from the per-workgroup column partials: block of 256
@@ -1056,7 +1074,7 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
                        (int64_t)(kWgSplitRows / 128), wpart, p.sdz, p.sx8);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t tot = a.K * a.N;
-    const int nf = (int)((tot + 255) / 256);
+    const int nf = (int)((tot + 1023) / 1024);
     const int nv = (a.dgamma || a.dbeta || a.dbias) ? (int)((a.N + 15) / 16) : 0;
     hipLaunchKernelGGL(k_finalize_vectors, dim3((unsigned)(nf + nv)), dim3(256), 0, s, wpart, w.nsplit,
                        (const float*)nullptr, (const float*)nullptr, (int)a.K, (int)a.N, a.dw, nf, p.part, w.nblocks,
@@ -1101,7 +1119,7 @@ hipError_t launch_bwd(const BwdLaunch& a, hipStream_t s) {
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t tot = a.K * a.N;
-  const int nf = (int)((tot + 255) / 256);
+  const int nf = (int)((tot + 1023) / 1024);  // four elements per thread
   const int nv = (a.dgamma || a.dbeta || a.dbias) ? (int)((a.N + 15) / 16) : 0;
   hipLaunchKernelGGL(k_finalize_vectors, dim3((unsigned)(nf + nv)), dim3(256), 0, s, wpart, w.nsplit, sxc, sdzc,
                      (int)a.K, (int)a.N, a.dw, nf, p.part, w.nblocks, a.dgamma, a.dbeta, a.dbias);
