@@ -24,14 +24,15 @@ namespace {
 // This workgroup's slab s, its row group b and the number G of row groups
 // of slab s.  Workgroups go to the eight XCDs round-robin (w % 8).  When the
 // grid is a multiple of 8 x slabs, workgroup w = x + 8 j (XCD x) serves slab
-// j % slabs of row group x + 8 (j / slabs): the slabs of a row group share
-// an XCD and its L2.  Otherwise slab w % slabs of row group w / slabs.
+// j % slabs of row group x n/(8 slabs) + j / slabs: the slabs of a row group
+// share an XCD and its L2, and each XCD streams a contiguous eighth of the
+// rows.  Otherwise slab w % slabs of row group w / slabs.
 __device__ __forceinline__ void slab_of(int slabs, int& s, int64_t& b, int64_t& G) {
   const unsigned w = blockIdx.x, n = gridDim.x, S = (unsigned)slabs;
   if (n % (8u * S) == 0) {
     const unsigned j = w >> 3;
     s = (int)(j % S);
-    b = (int64_t)(w & 7u) + 8 * (int64_t)(j / S);
+    b = (int64_t)(w & 7u) * (n / (8u * S)) + (int64_t)(j / S);
     G = n / S;
   } else {
     s = (int)(w % S);
