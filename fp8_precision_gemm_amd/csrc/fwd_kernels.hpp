@@ -50,8 +50,10 @@ __global__ __launch_bounds__(kThreads) void k_fwd_res(FwdBlock p, const float* p
     p.x_s = sp.s;
   }
   // a contiguous, balanced range of 16-row tiles per workgroup (of tile
-  // pairs when Y also leaves in 32 x 32 blocks: a block is two tiles)
-  const int64_t T = (p.M + kResRows - 1) / kResRows, G = gridDim.x, b = blockIdx.x;
+  // pairs when Y also leaves in 32 x 32 blocks: a block is two tiles); the
+  // ranges in XCD order as in k_fwd_xl
+  const int64_t T = (p.M + kResRows - 1) / kResRows, G = gridDim.x;
+  const int64_t b = (G & 7) == 0 ? (int64_t)(blockIdx.x & 7u) * (G >> 3) + (blockIdx.x >> 3) : (int64_t)blockIdx.x;
   const bool pairs = OPT && p.y_codes != nullptr;
   const int64_t tb = pairs ? 2 * (b * (T / 2) / G) : b * T / G, te = pairs ? 2 * ((b + 1) * (T / 2) / G) : (b + 1) * T / G;
   ResBlock<MODE, NT, KC, OPT, FULL> blk(p, tb, te, smem);
